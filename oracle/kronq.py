@@ -1,0 +1,510 @@
+"""KronQ per-layer quantization written out plainly in float64: the oracle.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+execute this module. The test suite, the smoke check of the build entry
+point and the CPU-baseline leg of the benchmark are its only users. It shares
+no code with the GPU library; its inputs come from ``kq_synth`` alone.
+
+Every step is the plain definition or the plain algorithm, in float64, with
+library primitives (matmul, inverse, Cholesky, the Sylvester Hadamard matrix)
+as steps and no blocking or fusion beyond what the algorithm states.
+
+Sources (cited by page title and section):
+  [KQ-en]   "KronQ: LLM Quantization via Kronecker-Factored Hessian",
+            gptget.net English summary: Methodology, Technical Contribution, Abstract.
+  [KQ-zh]   gptget.net Chinese summary of the same paper: 方法论 (methodology).
+  [KQ-news] "KronQ: Kronecker Hessians break GPTQ's 2-bit wall", aimodeling.com news item.
+  [KQ-art]  wmrh.cn popular article on KronQ: sections 二 (the Kronecker split),
+            三 (BiIP and the trace score), 四 (H_G cancels from the column update),
+            六 (mixed precision), 七 (cost), 八 (ablations, diagonal scaling), Q&A.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * s_j = H_jj^(1/4) per side, 1 where H_jj <= 0 (the pages name only "the
+    diagonal elements" of H_X and H_G as the basis of the scaling). Parity of
+    this exponent against the pages: unpinned.
+  * U = (Q_m kron H_p / sqrt(p)) diag(sigma) for d = m * 2^k, m odd.
+  * damping: lambda * mean(diag) added to the post-BiIP H_X, no dead-column rule.
+  * natural column order; asymmetric min-max grid with the scale stored as
+    float32 and the zero point rounded half-to-even and clamped to [0, 2^b-1].
+  * group parameters come from the fully error-fed weights when the sweep
+    reaches the group's first column; per-row grids come from W'' before the sweep.
+  * bit allocation: greedy by score (descending, ties by index) under an
+    integer, parameter-weighted budget. Parity against the pages: unpinned.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Iterable, List, Optional, Sequence
+
+import numpy as np
+import scipy.linalg
+
+import kq_synth
+
+__all__ = [
+    "as_f64", "covariance", "syrk_update", "sensitivity", "hadamard", "rotation_matrix",
+    "rotation_rows", "rotate_rows", "unrotate_rows", "biip_scales", "biip_forward",
+    "biip_inverse", "damped", "chol_inv_upper", "grid", "obs_quantize", "obs_quantize_blocked",
+    "obq_reference", "rtn_quantize", "kron_loss", "allocate_bits", "quantize_layer",
+    "ObsResult", "INFEASIBLE",
+]
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or real arrays -> float64, exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return kq_synth.bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# step 1: covariances  ([KQ-art] 二; [KQ-news]; [KQ-en] Methodology)
+# ---------------------------------------------------------------------------
+def covariance(chunks: Iterable[np.ndarray]) -> np.ndarray:
+    """H = A^T A / N over all token rows of A.
+
+    With A = X this is the activation covariance H_X that GPTQ already uses as
+    the Hessian proxy; with A = G (output gradients from one backward pass) it
+    is the gradient covariance H_G. The Kronecker-factored Hessian is
+    H_X kron H_G ([KQ-art] 二, [KQ-news]).
+    """
+    h = None
+    n = 0
+    for c in chunks:
+        a = as_f64(c)
+        p = a.T @ a
+        h = p if h is None else h + p
+        n += a.shape[0]
+    if n == 0:
+        raise ValueError("covariance of zero tokens is undefined")
+    return h / n
+
+
+def syrk_update(h: Optional[np.ndarray], a: np.ndarray, alpha: float, beta: float) -> np.ndarray:
+    """alpha * A^T A + beta * H (the chunked form of ``covariance``)."""
+    a = as_f64(a)
+    out = alpha * (a.T @ a)
+    if beta != 0.0:
+        out = out + beta * np.asarray(h, np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# step 5a: sensitivity score  ([KQ-news]; [KQ-art] 三, 六)
+# ---------------------------------------------------------------------------
+def sensitivity(h_x: np.ndarray, h_g: np.ndarray, mode: str = "kronq") -> float:
+    """tr(H_G) * tr(H_X) on the raw covariances; ``hx_only`` gives tr(H_X) alone.
+
+    The trace product is the sub-layer score of [KQ-news] and [KQ-art] 三. The
+    H_X-only score is the prior practice that cannot separate q/k/v, which
+    share H_X ([KQ-art] 三, 六).
+    """
+    tx = float(np.trace(np.asarray(h_x, np.float64)))
+    if mode == "hx_only":
+        return tx
+    if mode != "kronq":
+        raise ValueError(mode)
+    return float(np.trace(np.asarray(h_g, np.float64))) * tx
+
+
+# ---------------------------------------------------------------------------
+# step 2: bidirectional incoherence processing  ([KQ-art] 三, 七, 八, Q&A)
+# ---------------------------------------------------------------------------
+def hadamard(p: int) -> np.ndarray:
+    """Sylvester-ordered Hadamard matrix of order p (a power of two), entries +-1."""
+    return scipy.linalg.hadamard(p).astype(np.float64)
+
+
+def rotation_matrix(spec: kq_synth.RotSpec) -> np.ndarray:
+    """Dense U = (Q_m kron H_p / sqrt(p)) diag(sigma). For small n only."""
+    hp = hadamard(spec.p) / np.sqrt(spec.p)
+    return np.kron(np.asarray(spec.q, np.float64), hp) * spec.signs.astype(np.float64)[None, :]
+
+
+def rotation_rows(spec: kq_synth.RotSpec, rows: Sequence[int]) -> np.ndarray:
+    """Selected rows of U, built entry by entry from the definition (any n)."""
+    rows = np.asarray(rows, np.int64)
+    a, b = rows // spec.p, rows % spec.p
+    cols = np.arange(spec.n, dtype=np.int64)
+    a2, b2 = cols // spec.p, cols % spec.p
+    bits = np.bitwise_and(b[:, None], b2[None, :])
+    par = np.zeros(bits.shape, np.int64)
+    x = bits.copy()
+    while np.any(x):
+        par ^= (x & 1)
+        x >>= 1
+    h = np.where(par == 1, -1.0, 1.0) / np.sqrt(spec.p)
+    return np.asarray(spec.q, np.float64)[a[:, None], a2[None, :]] * h * spec.signs.astype(np.float64)[None, :]
+
+
+def rotate_rows(v: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
+    """Apply x -> U x to every row of v (returns v U^T), via the Kronecker reshape."""
+    v = np.asarray(v, np.float64)
+    k, n = v.shape
+    if n != spec.n:
+        raise ValueError("rotation size mismatch")
+    hp = hadamard(spec.p) / np.sqrt(spec.p)
+    r = (v * spec.signs.astype(np.float64)[None, :]).reshape(k, spec.m, spec.p)
+    r = r @ hp
+    r = np.einsum("ab,kbp->kap", np.asarray(spec.q, np.float64), r)
+    return r.reshape(k, n)
+
+
+def unrotate_rows(v: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
+    """Apply x -> U^T x to every row of v (returns v U)."""
+    v = np.asarray(v, np.float64)
+    k, n = v.shape
+    if n != spec.n:
+        raise ValueError("rotation size mismatch")
+    hp = hadamard(spec.p) / np.sqrt(spec.p)
+    r = v.reshape(k, spec.m, spec.p)
+    r = np.einsum("ba,kbp->kap", np.asarray(spec.q, np.float64), r)
+    r = r @ hp
+    return r.reshape(k, n) * spec.signs.astype(np.float64)[None, :]
+
+
+def biip_scales(h: np.ndarray) -> np.ndarray:
+    """Diagonal scaling of one side: s_j = H_jj^(1/4), 1 where H_jj <= 0.
+
+    [KQ-art] 八: the weights are rescaled from the diagonals of H_X and H_G
+    (S_X and S_G) before the rotation. The exponent 1/4 is a reading.
+    """
+    d = np.diag(np.asarray(h, np.float64)).copy()
+    s = np.ones_like(d)
+    pos = d > 0
+    s[pos] = d[pos] ** 0.25
+    return s
+
+
+def _two_sided(h: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
+    """U H U^T."""
+    return rotate_rows(rotate_rows(h, spec).T, spec).T
+
+
+def biip_forward(w: np.ndarray, h_x: np.ndarray, h_g: np.ndarray, rot_in: kq_synth.RotSpec,
+                 rot_out: kq_synth.RotSpec, *, inp: bool = True, out: bool = True, scale: bool = True):
+    """W'' = U_G S_G W S_X U_X^T, H_X'' = U_X S_X^-1 H_X S_X^-1 U_X^T, H_G'' likewise.
+
+    The input side is processed with H_X and the output side with H_G
+    ([KQ-art] 三); scaling precedes the rotation ([KQ-art] 八); the rotation is a
+    randomised Hadamard transform ([KQ-art] 七, Q&A; [KQ-zh] 方法论).
+    Returns (W'', H_X'', H_G'', s_x, s_g). Disabled sides use s = 1 and U = I.
+    """
+    w = as_f64(w)
+    dout, din = w.shape
+    s_x = biip_scales(h_x) if (inp and scale) else np.ones(din)
+    s_g = biip_scales(h_g) if (out and scale) else np.ones(dout)
+    w1 = s_g[:, None] * w * s_x[None, :]
+    hx1 = np.asarray(h_x, np.float64) / s_x[:, None] / s_x[None, :]
+    hg1 = None if h_g is None else np.asarray(h_g, np.float64) / s_g[:, None] / s_g[None, :]
+    if inp:
+        w1 = rotate_rows(w1, rot_in)
+        hx1 = _two_sided(hx1, rot_in)
+    if out:
+        w1 = rotate_rows(w1.T, rot_out).T
+        hg1 = _two_sided(hg1, rot_out)
+    return w1, hx1, hg1, s_x, s_g
+
+
+def biip_inverse(w2: np.ndarray, rot_in: kq_synth.RotSpec, rot_out: kq_synth.RotSpec,
+                 s_x: np.ndarray, s_g: np.ndarray, *, inp: bool = True, out: bool = True) -> np.ndarray:
+    """W = S_G^-1 U_G^T W'' U_X S_X^-1 (undo ``biip_forward`` on the weights)."""
+    w = np.asarray(w2, np.float64)
+    if out:
+        w = unrotate_rows(w.T, rot_out).T
+    if inp:
+        w = unrotate_rows(w, rot_in)
+    return w / np.asarray(s_g, np.float64)[:, None] / np.asarray(s_x, np.float64)[None, :]
+
+
+# ---------------------------------------------------------------------------
+# step 3: damping and the Cholesky factor of the inverse
+# ---------------------------------------------------------------------------
+def damped(h: np.ndarray, lam: float) -> np.ndarray:
+    """H + lam * mean(diag H) * I."""
+    h = np.array(h, np.float64, copy=True)
+    h[np.diag_indices_from(h)] += lam * float(np.mean(np.diag(h)))
+    return h
+
+
+def chol_inv_upper(h: np.ndarray, lam: float) -> np.ndarray:
+    """Upper-triangular R with R^T R = (H + lam*mean(diag H)*I)^-1, by the plain route:
+    explicit inverse, then the lower Cholesky factor L of it, R = L^T."""
+    hinv = np.linalg.inv(damped(h, lam))
+    hinv = 0.5 * (hinv + hinv.T)
+    return np.linalg.cholesky(hinv).T
+
+
+# ---------------------------------------------------------------------------
+# step 4: GPTQ-style column-wise OBS  ([KQ-en] Methodology; [KQ-zh] 方法论; [KQ-art] 四)
+# ---------------------------------------------------------------------------
+def grid(wmin: np.ndarray, wmax: np.ndarray, bits: int):
+    """Asymmetric b-bit min-max grid per row: returns (scale, zero), float64 arrays.
+
+    The range always contains 0; an all-zero range becomes [-1, 1]. The scale
+    is stored as float32, so the grid in use is that float32 value. The zero
+    point is the half-to-even rounding of -xmin/s, clamped to [0, 2^b - 1].
+    """
+    maxq = (1 << bits) - 1
+    xmin = np.minimum(np.asarray(wmin, np.float64), 0.0)
+    xmax = np.maximum(np.asarray(wmax, np.float64), 0.0)
+    flat = (xmin == 0.0) & (xmax == 0.0)
+    xmin = np.where(flat, -1.0, xmin)
+    xmax = np.where(flat, 1.0, xmax)
+    s = ((xmax - xmin) / maxq).astype(np.float32).astype(np.float64)
+    z = np.clip(np.rint(-xmin / s), 0, maxq)
+    return s, z
+
+
+def _tie(u: np.ndarray, window: float) -> np.ndarray:
+    """True where u lies within ``window`` of a rounding midpoint (k + 1/2)."""
+    return np.abs(u - np.floor(u) - 0.5) <= window
+
+
+@dataclass
+class ObsResult:
+    codes: np.ndarray        # uint8 [dout, din]
+    scales: np.ndarray       # float64 [dout, ngroups] (values representable in float32)
+    zeros: np.ndarray        # uint8 [dout, ngroups]
+    what: np.ndarray         # dequantised W'' (float64)
+    t: np.ndarray            # argument of the rounding, w / s, per entry
+    adopted_codes: int = 0   # tie-window entries where the other side's code was taken
+    adopted_zeros: int = 0
+    mismatches: int = 0      # entries where the other side differs outside the rules
+
+
+class _Adopt:
+    """Teacher-forced replay: inside a tie window take the other side's choice."""
+
+    def __init__(self, codes, zeros, window):
+        self.codes = np.asarray(codes)
+        self.zeros = np.asarray(zeros)
+        self.window = window
+        self.codes_n = 0
+        self.zeros_n = 0
+        self.bad = 0
+
+    def pick(self, own, other, u, offset, maxq):
+        other = other.astype(np.float64)
+        differ = other != own
+        if not np.any(differ):
+            return own, 0
+        lo = np.clip(np.floor(u) + offset, 0, maxq)
+        hi = np.clip(np.floor(u) + 1 + offset, 0, maxq)
+        ok = differ & _tie(u, self.window) & ((other == lo) | (other == hi))
+        self.bad += int(np.sum(differ & ~ok))
+        return np.where(ok, other, own), int(np.sum(ok))
+
+
+def _params(wg, bits, adopt, gi):
+    s, z = grid(wg.min(axis=1), wg.max(axis=1), bits)
+    if adopt is not None:
+        xmin = np.minimum(wg.min(axis=1), 0.0)
+        xmax = np.maximum(wg.max(axis=1), 0.0)
+        flat = (xmin == 0.0) & (xmax == 0.0)
+        u = np.where(flat, 1.0, -xmin) / s
+        z, n = adopt.pick(z, adopt.zeros[:, gi], u, 0, (1 << bits) - 1)
+        adopt.zeros_n += n
+    return s, z
+
+
+def obs_quantize(w2: np.ndarray, r: np.ndarray, bits: int, group: int, *, adopt_codes=None,
+                 adopt_zeros=None, window: float = 1e-5) -> ObsResult:
+    """Column-by-column OBS with the upper Cholesky factor R of the damped H_X''^-1.
+
+    For each column j in natural order: quantise w_j to the row's (or group's)
+    grid, take the scaled error e = (w_j - w^_j) / R_jj and remove e * R[j, k]
+    from every later column k. H_G does not appear: under the Kronecker
+    Hessian the optimal compensation of the remaining columns is independent
+    of H_G ([KQ-art] 四), so the update is the GPTQ one.
+
+    ``adopt_codes`` / ``adopt_zeros`` (optional) run the teacher-forced replay
+    used for parity: where the rounding argument lies within ``window`` of a
+    midpoint and the other side chose the neighbouring value, that value is
+    taken so that one legal tie-break does not cascade.
+    """
+    w = as_f64(w2).copy()
+    r = np.asarray(r, np.float64)
+    dout, din = w.shape
+    maxq = (1 << bits) - 1
+    ng = din // group if group else 1
+    codes = np.zeros((dout, din), np.uint8)
+    scales = np.zeros((dout, ng))
+    zeros = np.zeros((dout, ng), np.uint8)
+    what = np.zeros((dout, din))
+    tt = np.zeros((dout, din))
+    adopt = None if adopt_codes is None else _Adopt(adopt_codes, adopt_zeros, window)
+    if not group:
+        s, z = _params(w, bits, adopt, 0)
+        scales[:, 0], zeros[:, 0] = s, z
+    for j in range(din):
+        if group and j % group == 0:
+            s, z = _params(w[:, j:j + group], bits, adopt, j // group)
+            scales[:, j // group], zeros[:, j // group] = s, z
+        t = w[:, j] / s
+        q = np.clip(np.rint(t) + z, 0, maxq)
+        if adopt is not None:
+            q, n = adopt.pick(q, adopt.codes[:, j], t, z, maxq)
+            adopt.codes_n += n
+        wq = s * (q - z)
+        codes[:, j], what[:, j], tt[:, j] = q, wq, t
+        e = (w[:, j] - wq) / r[j, j]
+        w[:, j + 1:] -= np.outer(e, r[j, j + 1:])
+    out = ObsResult(codes, scales, zeros, what, tt)
+    if adopt is not None:
+        out.adopted_codes, out.adopted_zeros, out.mismatches = adopt.codes_n, adopt.zeros_n, adopt.bad
+    return out
+
+
+def obs_quantize_blocked(w2: np.ndarray, r: np.ndarray, bits: int, group: int, block: int) -> ObsResult:
+    """The same sweep with lazy batching: in-block feedback column by column, then
+    one trailing product W[:, end:] -= E R[blk, end:] per block of ``block`` columns.
+
+    Equal to ``obs_quantize`` in exact arithmetic when every group lies inside one
+    block (block % group == 0) or group == 0.
+    """
+    w = as_f64(w2).copy()
+    r = np.asarray(r, np.float64)
+    dout, din = w.shape
+    if din % block or (group and block % group):
+        raise ValueError("block must divide din and be a multiple of group")
+    maxq = (1 << bits) - 1
+    ng = din // group if group else 1
+    codes = np.zeros((dout, din), np.uint8)
+    scales = np.zeros((dout, ng))
+    zeros = np.zeros((dout, ng), np.uint8)
+    what = np.zeros((dout, din))
+    tt = np.zeros((dout, din))
+    if not group:
+        s, z = grid(w.min(axis=1), w.max(axis=1), bits)
+        scales[:, 0], zeros[:, 0] = s, z
+    for b0 in range(0, din, block):
+        b1 = b0 + block
+        e_blk = np.zeros((dout, block))
+        for j in range(b0, b1):
+            if group and j % group == 0:
+                s, z = grid(w[:, j:j + group].min(axis=1), w[:, j:j + group].max(axis=1), bits)
+                scales[:, j // group], zeros[:, j // group] = s, z
+            t = w[:, j] / s
+            q = np.clip(np.rint(t) + z, 0, maxq)
+            wq = s * (q - z)
+            codes[:, j], what[:, j], tt[:, j] = q, wq, t
+            e = (w[:, j] - wq) / r[j, j]
+            e_blk[:, j - b0] = e
+            w[:, j + 1:b1] -= np.outer(e, r[j, j + 1:b1])
+        w[:, b1:] -= e_blk @ r[b0:b1, b1:]
+    return ObsResult(codes, scales, zeros, what, tt)
+
+
+def obq_reference(w2: np.ndarray, h_damped: np.ndarray, bits: int, group: int) -> ObsResult:
+    """OBS written with the explicit inverse and a Schur downdate after each column.
+
+    After column j is fixed, its row and column are eliminated from H^-1; the
+    remaining columns move by -(w_j - w^_j) H^-1[j, k] / H^-1[j, j]. This is the
+    textbook optimal-brain-surgeon step, independent of the Cholesky route.
+    """
+    w = as_f64(w2).copy()
+    hinv = np.linalg.inv(np.asarray(h_damped, np.float64))
+    dout, din = w.shape
+    maxq = (1 << bits) - 1
+    ng = din // group if group else 1
+    codes = np.zeros((dout, din), np.uint8)
+    scales = np.zeros((dout, ng))
+    zeros = np.zeros((dout, ng), np.uint8)
+    what = np.zeros((dout, din))
+    tt = np.zeros((dout, din))
+    if not group:
+        s, z = grid(w.min(axis=1), w.max(axis=1), bits)
+        scales[:, 0], zeros[:, 0] = s, z
+    for j in range(din):
+        if group and j % group == 0:
+            s, z = grid(w[:, j:j + group].min(axis=1), w[:, j:j + group].max(axis=1), bits)
+            scales[:, j // group], zeros[:, j // group] = s, z
+        t = w[:, j] / s
+        q = np.clip(np.rint(t) + z, 0, maxq)
+        wq = s * (q - z)
+        codes[:, j], what[:, j], tt[:, j] = q, wq, t
+        err = w[:, j] - wq
+        w[:, j + 1:] -= np.outer(err / hinv[j, j], hinv[j, j + 1:])
+        hinv = hinv - np.outer(hinv[:, j], hinv[j, :]) / hinv[j, j]
+    return ObsResult(codes, scales, zeros, what, tt)
+
+
+def rtn_quantize(w2: np.ndarray, bits: int, group: int) -> ObsResult:
+    """Round-to-nearest on the same grid, all entries at once, no error feedback."""
+    w = as_f64(w2)
+    dout, din = w.shape
+    maxq = (1 << bits) - 1
+    g = group or din
+    wg = w.reshape(dout, din // g, g)
+    s, z = grid(wg.min(axis=2), wg.max(axis=2), bits)
+    t = wg / s[..., None]
+    q = np.clip(np.rint(t) + z[..., None], 0, maxq)
+    what = s[..., None] * (q - z[..., None])
+    return ObsResult(q.reshape(dout, din).astype(np.uint8), s, z.astype(np.uint8),
+                     what.reshape(dout, din), t.reshape(dout, din))
+
+
+# ---------------------------------------------------------------------------
+# validation: the Kronecker layer loss  ([KQ-en] Abstract; [KQ-news])
+# ---------------------------------------------------------------------------
+def kron_loss(dw: np.ndarray, h_x: np.ndarray, h_g: np.ndarray) -> float:
+    """tr(dW H_X dW^T H_G), which equals vec(dW)^T (H_X kron H_G) vec(dW) for
+    the column-major vec."""
+    dw = np.asarray(dw, np.float64)
+    return float(np.trace(dw @ np.asarray(h_x, np.float64) @ dw.T @ np.asarray(h_g, np.float64)))
+
+
+# ---------------------------------------------------------------------------
+# step 5b: mixed-precision allocation  ([KQ-art] 六; [KQ-zh] 方法论)
+# ---------------------------------------------------------------------------
+INFEASIBLE = "infeasible"
+
+
+def allocate_bits(scores: Sequence[float], n_params: Sequence[int], choices: Sequence[int],
+                  target_millibits: int):
+    """Greedy upgrade of the most sensitive sub-layers under a fixed average.
+
+    Budget (integer bits) = floor(target_millibits * sum(n) / 1000). Every
+    sub-layer starts at min(choices). Visiting sub-layers by score (highest
+    first, ties by lower index), each is raised to the largest choice that
+    keeps sum(n_l * b_l) within the budget. [KQ-art] 六 upgrades the most
+    sensitive class first at a fixed average bit count; the exact greedy rule
+    is a reading. Returns the list of bits, or INFEASIBLE.
+    """
+    n = [int(v) for v in n_params]
+    ch = sorted(set(int(c) for c in choices))
+    if not n or not ch:
+        raise ValueError("empty allocation problem")
+    total = sum(n)
+    budget = (int(target_millibits) * total) // 1000
+    bits = [ch[0]] * len(n)
+    used = ch[0] * total
+    if used > budget:
+        return INFEASIBLE
+    order = sorted(range(len(n)), key=lambda i: (-float(scores[i]), i))
+    for i in order:
+        for c in reversed(ch):
+            if c <= bits[i]:
+                break
+            if used + n[i] * (c - bits[i]) <= budget:
+                used += n[i] * (c - bits[i])
+                bits[i] = c
+                break
+    return bits
+
+
+# ---------------------------------------------------------------------------
+# the whole per-layer path
+# ---------------------------------------------------------------------------
+def quantize_layer(w, h_x, h_g, rot_in, rot_out, *, bits: int, group: int, damp: float,
+                   inp: bool = True, out: bool = True, scale: bool = True) -> Dict[str, object]:
+    """BiIP, damped Cholesky factor of the inverse, OBS sweep, un-rotation, loss."""
+    w64 = as_f64(w)
+    w2, hx2, hg2, s_x, s_g = biip_forward(w64, h_x, h_g, rot_in, rot_out, inp=inp, out=out, scale=scale)
+    r = chol_inv_upper(hx2, damp)
+    res = obs_quantize(w2, r, bits, group)
+    w_hat = biip_inverse(res.what, rot_in, rot_out, s_x, s_g, inp=inp, out=out)
+    return {"w2": w2, "hx2": hx2, "hg2": hg2, "s_x": s_x, "s_g": s_g, "r": r, "obs": res,
+            "w_hat": w_hat, "loss": kron_loss(w_hat - w64, h_x, h_g)}

@@ -1,0 +1,240 @@
+/*
+ * kq.h -- KronQ per-layer quantization on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Every argument is a plain pointer or
+ * a size; no framework types cross this boundary.
+ *
+ * Sources cited below (page title, then section):
+ *   [KQ-en]   "KronQ: LLM Quantization via Kronecker-Factored Hessian",
+ *             gptget.net English summary: Methodology, Technical Contribution.
+ *   [KQ-zh]   gptget.net Chinese summary of the paper: 方法论 (methodology).
+ *   [KQ-news] "KronQ: Kronecker Hessians break GPTQ's 2-bit wall", aimodeling.com.
+ *   [KQ-art]  wmrh.cn article on KronQ, sections 二, 三, 四, 六, 七, 八 and the Q&A.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless a comment says "host". The caller
+ *     owns every buffer; the library allocates no device memory. Scratch space
+ *     is passed in as `ws` / `ws_bytes` after a kq_workspace_size() query.
+ *   - Matrices are row-major. Covariances are float32, d x d, leading
+ *     dimension d, and both triangles are valid.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work on
+ *     it and return; nothing is synchronised unless stated.
+ *   - Argument errors are reported synchronously, before anything is enqueued,
+ *     as KQ_EINVAL / KQ_EUNSUPPORTED; kq_last_error() then holds a message.
+ *     A failed launch returns KQ_EDEVICE. Numerical failure inside a kernel is
+ *     reported through a device `info` word (0 = success).
+ *   - Buffers passed to one call must not overlap unless stated ("in place").
+ */
+#ifndef KQ_H_
+#define KQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KQ_OK = 0,
+  KQ_EINVAL = 1,        /* bad argument (shape, pointer, flag, precondition) */
+  KQ_ENOTPD = 2,        /* reported by the host-side helpers when info != 0 */
+  KQ_EINFEASIBLE = 3,   /* bit budget below min(choices) for every sub-layer */
+  KQ_EDEVICE = 4,       /* HIP runtime error while enqueueing */
+  KQ_EUNSUPPORTED = 5   /* valid request outside what the kernels implement */
+} kq_status;
+
+/* Element types of the weight input of kq_biip_rotate. */
+enum { KQ_BF16 = 0, KQ_F32 = 1, KQ_F64 = 2 };
+
+/* kq_biip_rotate flags. */
+enum {
+  KQ_BIIP_INPUT = 1,    /* process the input side (columns of W) with H_X */
+  KQ_BIIP_OUTPUT = 2,   /* process the output side (rows of W) with H_G */
+  KQ_BIIP_SCALE = 4,    /* diagonal rescale of each processed side before its rotation */
+  KQ_BIIP_INVERSE = 8   /* map a rotated weight back: W = S_G^-1 U_G^T W'' U_X S_X^-1 */
+};
+
+/* kq_sensitivity modes. */
+enum { KQ_SCORE_KRONQ = 0, KQ_SCORE_HX_ONLY = 1 };
+
+/* kq_workspace_size operations. */
+enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS = 3 };
+
+#define KQ_MAX_ODD 63         /* largest odd factor m of a rotated dimension */
+#define KQ_MAX_ROT_DIM 32768  /* largest rotated dimension n = m * 2^k */
+
+/*
+ * Rotation of one side: U = (Q_m kron H_p / sqrt(p)) diag(sigma), n = m * p,
+ * p = 2^log2p, m odd. H_p is the Sylvester Hadamard matrix,
+ * H_p[b][b'] = (-1)^popcount(b & b'); index i = a * p + b (a < m, b < p).
+ * [KQ-art] 七 and Q&A: the incoherence rotation is a Hadamard transform of
+ * O(d log d) cost; [KQ-zh] 方法论: a random orthogonal transform. The random
+ * draw (sigma, Q_m) is an input, made by the caller.
+ */
+typedef struct {
+  int64_t n;              /* dimension of this side */
+  int32_t m;              /* odd factor, 1 <= m <= KQ_MAX_ODD */
+  int32_t log2p;          /* n = m << log2p */
+  const int8_t* signs;    /* device [n], each +1 or -1 */
+  const double* q;        /* device [m * m], row-major orthogonal matrix Q_m */
+} kq_rot;
+
+/* Library version string (host, static storage). */
+const char* kq_version(void);
+/* Text of a status code (host, static storage). */
+const char* kq_status_string(kq_status s);
+/* Message of the last error raised on the calling thread (host, thread-local). */
+const char* kq_last_error(void);
+
+/*
+ * Bytes of scratch space an operation needs (0 = none).
+ *   KQ_OP_ACCUMULATE_COV: d0 = rows, d1 = d
+ *   KQ_OP_BIIP:           d0 = dout, d1 = din
+ *   KQ_OP_CHOLESKY:       d0 = d
+ *   KQ_OP_OBS:            d0 = dout, d1 = din, d2 = block
+ * Returns (size_t)-1 for invalid sizes.
+ */
+size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
+
+/*
+ * kq_accumulate_cov -- H <- alpha * A^T A + beta * H   (symmetric rank-k update)
+ *
+ * With A = X (calibration activations) and alpha = 1/N this forms H_X, the
+ * activation covariance GPTQ uses as its Hessian proxy; with A = G (gradients
+ * of the layer output from one backward pass) it forms H_G. The weight
+ * Hessian is approximated by H_X kron H_G ([KQ-art] 二; [KQ-news];
+ * [KQ-en] Methodology). Call once per token chunk with beta = 0 and then 1.
+ *
+ *   a      device, bf16 bit patterns, [rows, d] with row pitch lda elements (lda >= d)
+ *   rows   number of token rows, >= 0 (0: H <- beta * H)
+ *   h      device float32 [d, d]; read only when beta != 0; both triangles written
+ *   ws     scratch of kq_workspace_size(KQ_OP_ACCUMULATE_COV, rows, d, 0) bytes
+ * bf16 products are exact; sums run in float32 within token slices of 8192
+ * rows and in float64 across slices; the result is rounded once to float32.
+ */
+kq_status kq_accumulate_cov(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha,
+                            float beta, float* h, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kq_sensitivity -- score = tr(H_G) * tr(H_X), or tr(H_X) alone
+ *
+ * The sub-layer sensitivity of [KQ-news] and [KQ-art] 三/六, computed on the
+ * raw (pre-BiIP, undamped) covariances. KQ_SCORE_HX_ONLY gives the H_X-only
+ * ranking, which ties for sub-layers sharing an input (q/k/v).
+ *   h_x    device float32 [din, din]
+ *   h_g    device float32 [dout, dout]; may be NULL with KQ_SCORE_HX_ONLY
+ *   score  device float64 [1], written
+ * Diagonals are summed in float64 in a fixed order (deterministic).
+ */
+kq_status kq_sensitivity(const float* h_x, int64_t din, const float* h_g, int64_t dout, int32_t mode,
+                         double* score, void* stream);
+
+/*
+ * kq_allocate_bits -- mixed-precision bit widths from sensitivity scores (HOST)
+ *
+ * [KQ-art] 六: the most sensitive sub-layers are upgraded first at a fixed
+ * average bit count. Rule: budget = floor(target_millibits * sum(n) / 1000)
+ * bits, in 64-bit integers; every sub-layer starts at min(choices); visiting
+ * sub-layers by score (highest first, ties by lower index), each is raised to
+ * the largest choice that keeps sum(n_l * b_l) within the budget.
+ *   score       host float64 [n_layers]
+ *   n_params    host int64 [n_layers], each > 0
+ *   choices     host int32 [n_choices], each in [2, 8]
+ *   bits_out    host int32 [n_layers], written on KQ_OK
+ * Returns KQ_EINFEASIBLE when min(choices) * sum(n) exceeds the budget.
+ * Runs entirely on the host and needs no device.
+ */
+kq_status kq_allocate_bits(const double* score, const int64_t* n_params, int32_t n_layers,
+                           const int32_t* choices, int32_t n_choices, int64_t target_millibits,
+                           int32_t* bits_out);
+
+/*
+ * kq_biip_rotate -- bidirectional incoherence processing (BiIP)
+ *
+ * Forward (flags without KQ_BIIP_INVERSE):
+ *   s_x = diag(H_X)^(1/4) (1 where the diagonal is <= 0), s_g likewise from H_G,
+ *   W''   = U_G S_G W S_X U_X^T
+ *   H_X'' = U_X S_X^-1 H_X S_X^-1 U_X^T      (in place)
+ *   H_G'' = U_G S_G^-1 H_G S_G^-1 U_G^T      (in place)
+ * The input side is processed with H_X, the output side with H_G ([KQ-art]
+ * 三); the diagonal rescale precedes the rotation ([KQ-art] 八). A side
+ * without its flag uses s = 1 and U = I; KQ_BIIP_SCALE off keeps the rotation
+ * but sets s = 1. The map preserves tr(dW H_X dW^T H_G). H_G is not needed
+ * after this call: the column sweep never reads it ([KQ-art] 四, 七).
+ *
+ * Inverse (KQ_BIIP_INVERSE): w_out = S_G^-1 U_G^T w U_X S_X^-1 with the s_x,
+ * s_g of the forward call as inputs; h_x and h_g are not used (may be NULL).
+ *
+ *   w        device [dout, din] of type w_dtype (forward: any; inverse: KQ_F64)
+ *   w_out    device float64 [dout, din]
+ *   h_x      device float32 [din, din], in place (forward with KQ_BIIP_INPUT)
+ *   h_g      device float32 [dout, dout], in place (forward with KQ_BIIP_OUTPUT)
+ *   rot_in   HOST pointer to the input-side spec (n = din); used with KQ_BIIP_INPUT
+ *   rot_out  HOST pointer to the output-side spec (n = dout); used with KQ_BIIP_OUTPUT
+ *   s_x, s_g device float64 [din], [dout]; written (forward) or read (inverse)
+ *   ws       scratch of kq_workspace_size(KQ_OP_BIIP, dout, din, 0) bytes
+ * Butterflies run in float32 on chip; scales and the final values in float64.
+ */
+kq_status kq_biip_rotate(const void* w, int32_t w_dtype, int64_t dout, int64_t din, double* w_out,
+                         float* h_x, float* h_g, const kq_rot* rot_in, const kq_rot* rot_out,
+                         uint32_t flags, double* s_x, double* s_g, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * kq_cholesky_inv -- R upper triangular with R^T R = (H + damp * mean(diag H) * I)^-1
+ *
+ * The GPTQ route to the column sweep: damping of 1% of the mean diagonal,
+ * then the upper Cholesky factor of the inverse of the damped H_X''. It is
+ * formed without an explicit inverse: H~ = V V^T with V upper (the Cholesky
+ * factor of the index-reversed matrix), then R = V^-1.
+ *   h      device float32 [d, d]; in: H (full symmetric); out: R (upper
+ *          triangle), the strict lower triangle set to 0
+ *   damp   >= 0
+ *   info   device int32 [1]: 0 on success, else j + 1 where j is the first
+ *          index (in elimination order, from d-1 down to 0) whose pivot was not
+ *          positive or not finite; R is then undefined
+ *   ws     scratch of kq_workspace_size(KQ_OP_CHOLESKY, d, 0, 0) bytes
+ * Arithmetic is float32 with float64 diagonal blocks.
+ */
+kq_status kq_cholesky_inv(float* h, int64_t d, float damp, int32_t* info, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * kq_obs_quantize -- GPTQ-style column-wise OBS on the rotated weight
+ *
+ * For each column j in natural order: at the first column of a group, the
+ * asymmetric b-bit min-max grid of each row is taken from the current
+ * (error-fed) weights of that group (group == 0: one grid per row from the
+ * input weights); the scale is stored as float32 and the grid uses that
+ * value; zero = round_half_even(-xmin / s) clamped to [0, 2^b - 1]; then
+ *   code = clamp(round_half_even(w / s) + zero, 0, 2^b - 1),  w^ = s (code - zero)
+ *   e = (w - w^) / R_jj,  w_k -= e R[j][k] for every later column k.
+ * Columns inside a block of `block` columns receive the error at once; later
+ * columns receive the block's errors in one product (lazy batch). H_G does
+ * not appear: it cancels from the per-column update ([KQ-art] 四), so this is
+ * the GPTQ update ([KQ-en] Methodology; [KQ-zh] 方法论).
+ *
+ *   w        device float64 [dout, din]; in: W''; out: dequantised W^'' (in place)
+ *   r        device float32 [din, din], upper triangular R from kq_cholesky_inv
+ *   bits     2..8
+ *   group    0 (one grid per row) or a divisor of block
+ *   block    32, 64 or 128, dividing din
+ *   codes    device uint8 [dout, din]
+ *   scales   device float32 [dout, ngroups], ngroups = group ? din / group : 1
+ *   zeros    device uint8 [dout, ngroups]
+ *   preround device float64 [dout, din] or NULL: w / s of each entry (the
+ *            argument of the rounding), for diagnostics
+ *   ws       scratch of kq_workspace_size(KQ_OP_OBS, dout, din, block) bytes
+ * Arithmetic is float64 throughout (float64 MFMA for the lazy-batch product).
+ */
+kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, int32_t bits,
+                          int32_t group, int32_t block, uint8_t* codes, float* scales,
+                          uint8_t* zeros, double* preround, void* ws, size_t ws_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H_ */

@@ -1,0 +1,213 @@
+"""KronQ per-layer quantization on AMD Instinct MI355X (gfx950).
+
+Python binding of ``libkq.so``: one function per C entry point of
+``include/kq.h``, with the same names and argument order. The binding only
+marshals arguments (device pointers of torch tensors, the current HIP stream,
+scratch buffers); every step of the path runs in the library's HIP kernels.
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "KQError", "KQ_OK", "KQ_EINVAL", "KQ_ENOTPD", "KQ_EINFEASIBLE", "KQ_EDEVICE", "KQ_EUNSUPPORTED",
+    "KQ_BF16", "KQ_F32", "KQ_F64", "KQ_BIIP_INPUT", "KQ_BIIP_OUTPUT", "KQ_BIIP_SCALE", "KQ_BIIP_INVERSE",
+    "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
+    "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
+    "biip_rotate", "cholesky_inv", "obs_quantize", "Rot",
+]
+
+KQ_OK, KQ_EINVAL, KQ_ENOTPD, KQ_EINFEASIBLE, KQ_EDEVICE, KQ_EUNSUPPORTED = range(6)
+KQ_BF16, KQ_F32, KQ_F64 = 0, 1, 2
+KQ_BIIP_INPUT, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_BIIP_INVERSE = 1, 2, 4, 8
+KQ_SCORE_KRONQ, KQ_SCORE_HX_ONLY = 0, 1
+KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.environ.get("KQ_LIB", os.path.join(_HERE, "libkq.so"))
+
+
+class KQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Rot(ctypes.Structure):
+    """kq_rot: one side's rotation U = (Q_m kron H_p / sqrt(p)) diag(sigma)."""
+
+    _fields_ = [("n", ctypes.c_int64), ("m", ctypes.c_int32), ("log2p", ctypes.c_int32),
+                ("signs", ctypes.c_void_p), ("q", ctypes.c_void_p)]
+
+
+_LIB = None
+_VP, _I64, _I32, _U32, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                                    ctypes.c_float, ctypes.c_size_t)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise KQError(KQ_EDEVICE, f"libkq.so not found at {path}; build it with "
+                                  f"`python -m post_quantization_04_amd.build`")
+    L = ctypes.CDLL(path)
+    L.kq_version.restype = ctypes.c_char_p
+    L.kq_status_string.restype = ctypes.c_char_p
+    L.kq_status_string.argtypes = [ctypes.c_int]
+    L.kq_last_error.restype = ctypes.c_char_p
+    L.kq_workspace_size.restype = _SZ
+    L.kq_workspace_size.argtypes = [_I32, _I64, _I64, _I64]
+    L.kq_accumulate_cov.argtypes = [_VP, _I64, _I64, _I64, _F32, _F32, _VP, _VP, _SZ, _VP]
+    L.kq_sensitivity.argtypes = [_VP, _I64, _VP, _I64, _I32, _VP, _VP]
+    L.kq_allocate_bits.argtypes = [_VP, _VP, _I32, _VP, _I32, _I64, _VP]
+    L.kq_biip_rotate.argtypes = [_VP, _I32, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(Rot),
+                                 ctypes.POINTER(Rot), _U32, _VP, _VP, _VP, _SZ, _VP]
+    L.kq_cholesky_inv.argtypes = [_VP, _I64, _F32, _VP, _VP, _SZ, _VP]
+    L.kq_obs_quantize.argtypes = [_VP, _VP, _I64, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]
+    for name in ("kq_accumulate_cov", "kq_sensitivity", "kq_allocate_bits", "kq_biip_rotate",
+                 "kq_cholesky_inv", "kq_obs_quantize"):
+        getattr(L, name).restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def version() -> str:
+    return lib().kq_version().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != KQ_OK:
+        L = lib()
+        raise KQError(status, f"{what}: {L.kq_status_string(status).decode()}: {L.kq_last_error().decode()}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _scratch(nbytes: int, device):
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise KQError(KQ_EINVAL, msg)
+
+
+def workspace_size(op: int, d0: int, d1: int = 0, d2: int = 0) -> int:
+    n = lib().kq_workspace_size(op, d0, d1, d2)
+    if n == ctypes.c_size_t(-1).value:
+        raise KQError(KQ_EINVAL, f"kq_workspace_size: invalid sizes for op {op}")
+    return n
+
+
+def accumulate_cov(a, h, alpha: float, beta: float, *, ws=None, stream=None) -> None:
+    """h <- alpha * a^T a + beta * h; a: [rows, d] torch.bfloat16 (or int16/uint16 bits), h: [d, d] float32."""
+    import torch
+    _need(a.dim() == 2 and h.dim() == 2 and h.shape[0] == h.shape[1] == a.shape[1], "accumulate_cov: shapes")
+    _need(a.dtype in (torch.bfloat16, torch.int16, torch.uint16) and h.dtype == torch.float32,
+          "accumulate_cov: dtypes")
+    _need(a.stride(1) == 1 and h.is_contiguous(), "accumulate_cov: layout")
+    rows, d = a.shape
+    need = workspace_size(KQ_OP_ACCUMULATE_COV, rows, d)
+    if ws is None:
+        ws = _scratch(need, h.device)
+    _check(lib().kq_accumulate_cov(_ptr(a), rows, d, a.stride(0), alpha, beta, _ptr(h), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)), "kq_accumulate_cov")
+
+
+def sensitivity(h_x, h_g, score, mode: int = KQ_SCORE_KRONQ, *, stream=None) -> None:
+    """score[0] <- tr(h_g) * tr(h_x) (or tr(h_x)); score: float64 device tensor of one element."""
+    import torch
+    _need(score.dtype == torch.float64 and score.numel() >= 1, "sensitivity: score must be float64")
+    dout = 0 if h_g is None else h_g.shape[0]
+    _check(lib().kq_sensitivity(_ptr(h_x), h_x.shape[0], _ptr(h_g), dout, mode, _ptr(score), _stream(stream)),
+           "kq_sensitivity")
+
+
+def allocate_bits(score: Sequence[float], n_params: Sequence[int], choices: Sequence[int],
+                  target_millibits: int) -> list:
+    """Host-side bit allocation; returns the list of bit widths."""
+    s = np.ascontiguousarray(score, dtype=np.float64)
+    n = np.ascontiguousarray(n_params, dtype=np.int64)
+    c = np.ascontiguousarray(choices, dtype=np.int32)
+    out = np.zeros(len(s), dtype=np.int32)
+    _need(len(s) == len(n), "allocate_bits: score and n_params differ in length")
+    _check(lib().kq_allocate_bits(s.ctypes.data, n.ctypes.data, len(s), c.ctypes.data, len(c),
+                                  int(target_millibits), out.ctypes.data), "kq_allocate_bits")
+    return out.tolist()
+
+
+def make_rot(signs, q) -> Rot:
+    """kq_rot from device tensors: signs int8 [n], q float64 [m, m]."""
+    n = signs.numel()
+    m = q.shape[0]
+    k = (n // m).bit_length() - 1
+    return Rot(n=n, m=m, log2p=k, signs=_ptr(signs), q=_ptr(q))
+
+
+def biip_rotate(w, w_out, h_x, h_g, rot_in: Optional[Rot], rot_out: Optional[Rot], flags: int, s_x, s_g, *,
+                ws=None, stream=None) -> None:
+    """Forward: w_out = U_G S_G w S_X U_X^T, h_x / h_g transformed in place. Inverse with KQ_BIIP_INVERSE."""
+    import torch
+    dtypes = {torch.bfloat16: KQ_BF16, torch.int16: KQ_BF16, torch.uint16: KQ_BF16,
+              torch.float32: KQ_F32, torch.float64: KQ_F64}
+    _need(w.dtype in dtypes and w.is_contiguous() and w_out.dtype == torch.float64 and w_out.is_contiguous(),
+          "biip_rotate: w / w_out dtype or layout")
+    _need(s_x.dtype == torch.float64 and s_g.dtype == torch.float64, "biip_rotate: scales must be float64")
+    dout, din = w.shape
+    need = workspace_size(KQ_OP_BIIP, dout, din)
+    if ws is None:
+        ws = _scratch(need, w.device)
+    _check(lib().kq_biip_rotate(_ptr(w), dtypes[w.dtype], dout, din, _ptr(w_out), _ptr(h_x), _ptr(h_g),
+                                None if rot_in is None else ctypes.byref(rot_in),
+                                None if rot_out is None else ctypes.byref(rot_out), flags, _ptr(s_x), _ptr(s_g),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "kq_biip_rotate")
+
+
+def cholesky_inv(h, damp: float, info, *, ws=None, stream=None) -> None:
+    """h (float32 [d, d]) <- upper R with R^T R = (h + damp * mean(diag h) * I)^-1; info int32 device [1]."""
+    import torch
+    _need(h.dtype == torch.float32 and h.is_contiguous() and info.dtype == torch.int32, "cholesky_inv: dtypes")
+    d = h.shape[0]
+    need = workspace_size(KQ_OP_CHOLESKY, d)
+    if ws is None:
+        ws = _scratch(need, h.device)
+    _check(lib().kq_cholesky_inv(_ptr(h), d, damp, _ptr(info), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)), "kq_cholesky_inv")
+
+
+def obs_quantize(w, r, bits: int, group: int, block: int, codes, scales, zeros, preround=None, *, ws=None,
+                 stream=None) -> None:
+    """Column-wise OBS: w (float64 [dout, din]) in W'', out dequantised; codes/scales/zeros written."""
+    import torch
+    _need(w.dtype == torch.float64 and r.dtype == torch.float32 and codes.dtype == torch.uint8
+          and scales.dtype == torch.float32 and zeros.dtype == torch.uint8, "obs_quantize: dtypes")
+    dout, din = w.shape
+    need = workspace_size(KQ_OP_OBS, dout, din, block)
+    if ws is None:
+        ws = _scratch(need, w.device)
+    _check(lib().kq_obs_quantize(_ptr(w), _ptr(r), dout, din, bits, group, block, _ptr(codes), _ptr(scales),
+                                 _ptr(zeros), _ptr(preround), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)), "kq_obs_quantize")

@@ -1,0 +1,218 @@
+// C ABI of libkq: argument validation, error reporting and dispatch.
+//
+// Every check here runs on the host before anything is enqueued, so invalid
+// calls fail the same way with or without a GPU present.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+namespace {
+thread_local char g_error[512] = "";
+}
+
+kq_status fail(kq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kq_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return KQ_OK;
+}
+
+}  // namespace kq
+
+using kq::fail;
+
+namespace {
+
+constexpr int64_t kMaxDim = 65536;
+
+bool rot_ok(const kq_rot* r, int64_t n, const char* side) {
+  if (!r) {
+    fail(KQ_EINVAL, "%s rotation spec is NULL", side);
+    return false;
+  }
+  if (r->n != n) {
+    fail(KQ_EINVAL, "%s rotation has n = %lld, expected %lld", side, (long long)r->n, (long long)n);
+    return false;
+  }
+  if (r->m < 1 || r->m > KQ_MAX_ODD || (r->m % 2) == 0 || r->log2p < 0 || r->log2p > 15 ||
+      (int64_t(r->m) << r->log2p) != n) {
+    fail(KQ_EINVAL, "%s rotation: n = %lld is not m * 2^log2p with odd m <= %d (m = %d, log2p = %d)", side,
+         (long long)n, KQ_MAX_ODD, r->m, r->log2p);
+    return false;
+  }
+  if (!r->signs || !r->q) {
+    fail(KQ_EINVAL, "%s rotation: signs or q is NULL", side);
+    return false;
+  }
+  return true;
+}
+
+bool ws_ok(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return true;
+  if (!ws || ws_bytes < need) {
+    fail(KQ_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws ? ws_bytes : size_t(0), need);
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kq_version(void) { return "kq 0.1.0 (gfx950)"; }
+
+const char* kq_status_string(kq_status s) {
+  switch (s) {
+    case KQ_OK: return "ok";
+    case KQ_EINVAL: return "invalid argument";
+    case KQ_ENOTPD: return "matrix not positive definite";
+    case KQ_EINFEASIBLE: return "bit budget infeasible";
+    case KQ_EDEVICE: return "device error";
+    case KQ_EUNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* kq_last_error(void) { return kq::g_error; }
+
+size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2) {
+  const size_t bad = static_cast<size_t>(-1);
+  switch (op) {
+    case KQ_OP_ACCUMULATE_COV:
+      if (d0 < 0 || d1 < 1 || d1 > kMaxDim) return bad;
+      return kq::syrk_workspace(d0, d1);
+    case KQ_OP_BIIP:
+      if (d0 < 1 || d1 < 1 || d0 > KQ_MAX_ROT_DIM || d1 > KQ_MAX_ROT_DIM) return bad;
+      return kq::biip_workspace(d0, d1);
+    case KQ_OP_CHOLESKY:
+      if (d0 < 1 || d0 > kMaxDim) return bad;
+      return kq::chol_workspace(d0);
+    case KQ_OP_OBS:
+      if (d0 < 1 || d1 < 1 || d2 < 1 || d1 > kMaxDim) return bad;
+      return kq::obs_workspace(d0, d1, static_cast<int>(d2));
+    default:
+      return bad;
+  }
+}
+
+kq_status kq_accumulate_cov(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha, float beta,
+                            float* h, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0 || d < 1 || d > kMaxDim) return fail(KQ_EINVAL, "kq_accumulate_cov: bad shape rows=%lld d=%lld",
+                                                    (long long)rows, (long long)d);
+  if (lda < d) return fail(KQ_EINVAL, "kq_accumulate_cov: lda %lld < d %lld", (long long)lda, (long long)d);
+  if (!h || (rows > 0 && !a)) return fail(KQ_EINVAL, "kq_accumulate_cov: NULL pointer");
+  if (!ws_ok(ws, ws_bytes, kq::syrk_workspace(rows, d))) return KQ_EINVAL;
+  return kq::syrk_run(a, rows, d, lda, alpha, beta, h, ws, kq::as_stream(stream));
+}
+
+kq_status kq_sensitivity(const float* h_x, int64_t din, const float* h_g, int64_t dout, int32_t mode,
+                         double* score, void* stream) {
+  if (mode != KQ_SCORE_KRONQ && mode != KQ_SCORE_HX_ONLY) return fail(KQ_EINVAL, "kq_sensitivity: mode %d", mode);
+  if (!h_x || !score || din < 1) return fail(KQ_EINVAL, "kq_sensitivity: NULL pointer or din < 1");
+  if (mode == KQ_SCORE_KRONQ && (!h_g || dout < 1)) return fail(KQ_EINVAL, "kq_sensitivity: H_G missing");
+  return kq::score_run(h_x, din, h_g, dout, mode, score, kq::as_stream(stream));
+}
+
+kq_status kq_allocate_bits(const double* score, const int64_t* n_params, int32_t n_layers, const int32_t* choices,
+                           int32_t n_choices, int64_t target_millibits, int32_t* bits_out) {
+  if (!score || !n_params || !choices || !bits_out) return fail(KQ_EINVAL, "kq_allocate_bits: NULL pointer");
+  if (n_layers < 1 || n_choices < 1) return fail(KQ_EINVAL, "kq_allocate_bits: empty problem");
+  if (target_millibits < 0) return fail(KQ_EINVAL, "kq_allocate_bits: negative target");
+  std::vector<int32_t> ch(choices, choices + n_choices);
+  for (int32_t c : ch)
+    if (c < 2 || c > 8) return fail(KQ_EINVAL, "kq_allocate_bits: choice %d outside [2, 8]", c);
+  std::sort(ch.begin(), ch.end());
+  ch.erase(std::unique(ch.begin(), ch.end()), ch.end());
+  __int128 total = 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (n_params[l] <= 0) return fail(KQ_EINVAL, "kq_allocate_bits: n_params[%d] <= 0", l);
+    total += n_params[l];
+  }
+  if (total > (__int128(1) << 56)) return fail(KQ_EINVAL, "kq_allocate_bits: parameter count too large");
+  const __int128 budget = (__int128(target_millibits) * total) / 1000;
+  std::vector<int32_t> bits(n_layers, ch.front());
+  __int128 used = __int128(ch.front()) * total;
+  if (used > budget) return fail(KQ_EINFEASIBLE, "kq_allocate_bits: budget below min(choices) for all layers");
+  std::vector<int32_t> order(n_layers);
+  for (int32_t l = 0; l < n_layers; ++l) order[l] = l;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    if (score[x] != score[y]) return score[x] > score[y];
+    return x < y;
+  });
+  for (int32_t l : order) {
+    for (auto it = ch.rbegin(); it != ch.rend() && *it > bits[l]; ++it) {
+      const __int128 extra = __int128(n_params[l]) * (*it - bits[l]);
+      if (used + extra <= budget) {
+        used += extra;
+        bits[l] = *it;
+        break;
+      }
+    }
+  }
+  std::memcpy(bits_out, bits.data(), sizeof(int32_t) * n_layers);
+  return KQ_OK;
+}
+
+kq_status kq_biip_rotate(const void* w, int32_t w_dtype, int64_t dout, int64_t din, double* w_out, float* h_x,
+                         float* h_g, const kq_rot* rot_in, const kq_rot* rot_out, uint32_t flags, double* s_x,
+                         double* s_g, void* ws, size_t ws_bytes, void* stream) {
+  if (flags & ~uint32_t(KQ_BIIP_INPUT | KQ_BIIP_OUTPUT | KQ_BIIP_SCALE | KQ_BIIP_INVERSE))
+    return fail(KQ_EINVAL, "kq_biip_rotate: unknown flags 0x%x", flags);
+  if (dout < 1 || din < 1 || dout > KQ_MAX_ROT_DIM || din > KQ_MAX_ROT_DIM)
+    return fail(KQ_EINVAL, "kq_biip_rotate: shape %lld x %lld outside [1, %d]", (long long)dout, (long long)din,
+                KQ_MAX_ROT_DIM);
+  if (w_dtype != KQ_BF16 && w_dtype != KQ_F32 && w_dtype != KQ_F64)
+    return fail(KQ_EINVAL, "kq_biip_rotate: w_dtype %d", w_dtype);
+  if (!w || !w_out || !s_x || !s_g) return fail(KQ_EINVAL, "kq_biip_rotate: NULL pointer");
+  const bool inp = flags & KQ_BIIP_INPUT, out = flags & KQ_BIIP_OUTPUT, inverse = flags & KQ_BIIP_INVERSE;
+  if (inverse && w_dtype != KQ_F64) return fail(KQ_EINVAL, "kq_biip_rotate: the inverse takes a float64 weight");
+  if (inp && !rot_ok(rot_in, din, "input")) return KQ_EINVAL;
+  if (out && !rot_ok(rot_out, dout, "output")) return KQ_EINVAL;
+  if (!inverse && ((inp && !h_x) || (out && !h_g)))
+    return fail(KQ_EINVAL, "kq_biip_rotate: the processed side needs its covariance");
+  if (w_out == w) return fail(KQ_EINVAL, "kq_biip_rotate: w_out must not alias w");
+  if (!ws_ok(ws, ws_bytes, kq::biip_workspace(dout, din))) return KQ_EINVAL;
+  return kq::biip_run(w, w_dtype, dout, din, w_out, h_x, h_g, rot_in, rot_out, flags, s_x, s_g, ws,
+                      kq::as_stream(stream));
+}
+
+kq_status kq_cholesky_inv(float* h, int64_t d, float damp, int32_t* info, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!h || !info) return fail(KQ_EINVAL, "kq_cholesky_inv: NULL pointer");
+  if (d < 1 || d > kMaxDim) return fail(KQ_EINVAL, "kq_cholesky_inv: d = %lld", (long long)d);
+  if (!(damp >= 0.0f) || damp > 1e30f) return fail(KQ_EINVAL, "kq_cholesky_inv: damp must be finite and >= 0");
+  if (!ws_ok(ws, ws_bytes, kq::chol_workspace(d))) return KQ_EINVAL;
+  return kq::chol_run(h, d, damp, info, ws, kq::as_stream(stream));
+}
+
+kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, int32_t bits, int32_t group,
+                          int32_t block, uint8_t* codes, float* scales, uint8_t* zeros, double* preround, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!w || !r || !codes || !scales || !zeros) return fail(KQ_EINVAL, "kq_obs_quantize: NULL pointer");
+  if (dout < 1 || din < 1 || din > kMaxDim) return fail(KQ_EINVAL, "kq_obs_quantize: bad shape");
+  if (bits < 2 || bits > 8) return fail(KQ_EINVAL, "kq_obs_quantize: bits = %d outside [2, 8]", bits);
+  if (block < 1 || din % block != 0)
+    return fail(KQ_EINVAL, "kq_obs_quantize: block %d must divide din %lld", block, (long long)din);
+  if (group < 0 || (group > 0 && block % group != 0))
+    return fail(KQ_EINVAL, "kq_obs_quantize: group %d must be 0 or divide block %d", group, block);
+  if (block != 32 && block != 64 && block != 128)
+    return fail(KQ_EUNSUPPORTED, "kq_obs_quantize: block %d (supported: 32, 64, 128)", block);
+  if (!ws_ok(ws, ws_bytes, kq::obs_workspace(dout, din, block))) return KQ_EINVAL;
+  return kq::obs_run(w, r, dout, din, bits, group, block, codes, scales, zeros, preround, ws, kq::as_stream(stream));
+}
+
+}  // extern "C"

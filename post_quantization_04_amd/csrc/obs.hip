@@ -1,0 +1,283 @@
+// GPTQ-style column-wise OBS on the rotated weight, in float64.
+//
+// The sweep is sequential in the column index and independent across rows,
+// given R. Per block of B columns:
+//   * sweep kernel: 16 lanes own one row; lane l keeps columns l, l + 16, ...
+//     of the block in registers (B / 16 values). For column j the owning
+//     lane quantises, forms the scaled error e = (w - w^) / R_jj and the
+//     error is broadcast to the row's 16 lanes with one DPP row_newbcast;
+//     every lane then removes e * R[j][k] from its columns k. The block of R
+//     sits in LDS, laid out so each lane reads its B / 16 entries of row j
+//     with two 16-byte loads; entries on and below the diagonal are stored as
+//     zero, so the update is branch free. Group minima and maxima are
+//     16-lane shuffle reductions.
+//   * trailing kernel (lazy batch): W[:, end:] -= E R[blk, end:] on float64
+//     MFMA (v_mfma_f64_16x16x4f64), E being the block's scaled errors.
+// Float64 keeps the rounding argument w / s of every entry within about
+// 1e-6 grid units of the float64 oracle across thousands of columns, where a
+// float32 sweep drifts past 1e-5.
+#include "kq_internal.h"
+
+namespace kq {
+namespace {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSweepThreads = 256;  // 16 rows per workgroup
+constexpr int kRowsPerWg = kSweepThreads / 16;
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_bcast(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Value of lane `src` of this lane's group of 16 (row_newbcast), src uniform.
+__device__ __forceinline__ double bcast16(double v, int src) {
+  switch (src) {
+    case 0: return dpp_bcast<0x150>(v);
+    case 1: return dpp_bcast<0x151>(v);
+    case 2: return dpp_bcast<0x152>(v);
+    case 3: return dpp_bcast<0x153>(v);
+    case 4: return dpp_bcast<0x154>(v);
+    case 5: return dpp_bcast<0x155>(v);
+    case 6: return dpp_bcast<0x156>(v);
+    case 7: return dpp_bcast<0x157>(v);
+    case 8: return dpp_bcast<0x158>(v);
+    case 9: return dpp_bcast<0x159>(v);
+    case 10: return dpp_bcast<0x15A>(v);
+    case 11: return dpp_bcast<0x15B>(v);
+    case 12: return dpp_bcast<0x15C>(v);
+    case 13: return dpp_bcast<0x15D>(v);
+    case 14: return dpp_bcast<0x15E>(v);
+    default: return dpp_bcast<0x15F>(v);
+  }
+}
+
+// Asymmetric min-max grid; the scale is rounded to float32 (its stored form).
+__device__ __forceinline__ void make_grid(double mn, double mx, int maxq, double& s, double& z) {
+  double xmin = fmin(mn, 0.0), xmax = fmax(mx, 0.0);
+  if (xmin == 0.0 && xmax == 0.0) {
+    xmin = -1.0;
+    xmax = 1.0;
+  }
+  s = static_cast<double>(static_cast<float>((xmax - xmin) / static_cast<double>(maxq)));
+  z = fmin(fmax(rint(-xmin / s), 0.0), static_cast<double>(maxq));
+}
+
+// One grid per row (group == 0), from the weights before the sweep. One wave per row.
+__global__ __launch_bounds__(256) void row_grid_kernel(const double* __restrict__ w, int64_t dout, int64_t din,
+                                                       int bits, float* __restrict__ scales,
+                                                       uint8_t* __restrict__ zeros) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= dout) return;
+  const int lane = threadIdx.x & 63;
+  double mn = INFINITY, mx = -INFINITY;
+  for (int64_t j = lane; j < din; j += 64) {
+    const double v = w[row * din + j];
+    mn = fmin(mn, v);
+    mx = fmax(mx, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fmin(mn, __shfl_xor(mn, o, 64));
+    mx = fmax(mx, __shfl_xor(mx, o, 64));
+  }
+  if (lane == 0) {
+    double s, z;
+    make_grid(mn, mx, (1 << bits) - 1, s, z);
+    scales[row] = static_cast<float>(s);
+    zeros[row] = static_cast<uint8_t>(z);
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(kSweepThreads) void sweep_kernel(
+    double* __restrict__ w, const float* __restrict__ r, int64_t dout, int64_t din, int64_t c0, int bits, int group,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, uint8_t* __restrict__ zeros,
+    double* __restrict__ preround, double* __restrict__ e_out) {
+  constexpr int EPL = B / 16;
+  __shared__ float rl[B][B];  // rl[j][l * EPL + e] = R[c0 + j][c0 + l + 16 e] above the diagonal, else 0
+  __shared__ double rinv[B];
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < B * B; idx += kSweepThreads) {
+    const int j = idx / B, k = idx % B;
+    const float v = r[(c0 + j) * din + c0 + k];
+    rl[j][(k & 15) * EPL + (k >> 4)] = (k > j) ? v : 0.0f;
+    if (k == j) rinv[j] = 1.0 / static_cast<double>(v);
+  }
+  __syncthreads();
+
+  const int l16 = tid & 15;
+  const int64_t row = int64_t(blockIdx.x) * kRowsPerWg + (tid >> 4);
+  const bool valid = row < dout;
+  const int maxq = (1 << bits) - 1;
+  const int64_t ngroups = group ? din / group : 1;
+
+  double x[EPL], tq[EPL], es[EPL];
+  int cq[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    x[e] = valid ? w[row * din + c0 + l16 + 16 * e] : 0.0;
+    tq[e] = 0.0;
+    es[e] = 0.0;
+    cq[e] = 0;
+  }
+  double s = 1.0, z = 0.0;
+  if (group == 0 && valid) {
+    s = static_cast<double>(scales[row]);
+    z = static_cast<double>(zeros[row]);
+  }
+
+#pragma unroll EPL
+  for (int eo = 0; eo < EPL; ++eo)
+#pragma unroll 16
+  for (int lo = 0; lo < 16; ++lo) {
+    const int j = eo * 16 + lo;
+    if (group > 0 && ((c0 + j) % group) == 0) {
+      double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int col = l16 + 16 * e;
+        if (col >= j && col < j + group) {
+          mn = fmin(mn, x[e]);
+          mx = fmax(mx, x[e]);
+        }
+      }
+      for (int o = 8; o > 0; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o, 16));
+        mx = fmax(mx, __shfl_xor(mx, o, 16));
+      }
+      make_grid(mn, mx, maxq, s, z);
+      if (l16 == 0 && valid) {
+        scales[row * ngroups + (c0 + j) / group] = static_cast<float>(s);
+        zeros[row * ngroups + (c0 + j) / group] = static_cast<uint8_t>(z);
+      }
+    }
+    const double wv = x[eo];
+    const double t = wv / s;
+    const double q = fmin(fmax(rint(t) + z, 0.0), static_cast<double>(maxq));
+    const double wq = s * (q - z);
+    const double err = (wv - wq) * rinv[j];
+    if (l16 == lo) {
+      x[eo] = wq;
+      cq[eo] = static_cast<int>(q);
+      tq[eo] = t;
+      es[eo] = err;
+    }
+    const double eb = bcast16(err, lo);
+    const float* rr = &rl[j][l16 * EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = fma(-eb, static_cast<double>(rr[e]), x[e]);
+  }
+
+  if (!valid) return;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int64_t col = c0 + l16 + 16 * e;
+    w[row * din + col] = x[e];
+    codes[row * din + col] = static_cast<uint8_t>(cq[e]);
+    if (preround) preround[row * din + col] = tq[e];
+    e_out[row * B + l16 + 16 * e] = es[e];
+  }
+}
+
+// W[:, c1:] -= E R[c0:c0+B, c1:], c1 = c0 + B. 64 x 64 output tile per workgroup,
+// 4 waves of 32 x 32 (2 x 2 float64 MFMA 16 x 16 blocks).
+__global__ __launch_bounds__(256) void trailing_kernel(double* __restrict__ w, const float* __restrict__ r,
+                                                       const double* __restrict__ e, int64_t dout, int64_t din,
+                                                       int64_t c0, int B) {
+  __shared__ double as[64][17];
+  __shared__ double bs[16][65];
+  const int64_t c1 = c0 + B;
+  const int64_t i0 = int64_t(blockIdx.y) * 64;
+  const int64_t j0 = c1 + int64_t(blockIdx.x) * 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{};
+  for (int kc = 0; kc < B; kc += 16) {
+    for (int q = tid; q < 64 * 16; q += 256) {
+      const int i = q >> 4, k = q & 15;
+      as[i][k] = (i0 + i < dout) ? e[(i0 + i) * B + kc + k] : 0.0;
+      const int kb = q >> 6, jb = q & 63;
+      bs[kb][jb] = (j0 + jb < din) ? static_cast<double>(r[(c0 + kc + kb) * din + j0 + jb]) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      double fa[2], fb[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) fa[x] = as[wi * 32 + x * 16 + (lane & 15)][4 * kk + (lane >> 4)];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) fb[y] = bs[4 * kk + (lane >> 4)][wj * 32 + y * 16 + (lane & 15)];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // D[i][j] of a 16 x 16 float64 block: lane l, register q -> i = 4 q + l / 16, j = l % 16
+  // (measured on gfx950; the operands are A[i][k] at lane i + 16 k and B[k][j] at lane j + 16 k)
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = i0 + wi * 32 + x * 16 + 4 * q + (lane >> 4);
+        const int64_t j = j0 + wj * 32 + y * 16 + (lane & 15);
+        if (i < dout && j < din) w[i * din + j] -= acc[x][y][q];
+      }
+}
+
+template <int B>
+kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int bits, int group, uint8_t* codes,
+                     float* scales, uint8_t* zeros, double* preround, double* e, hipStream_t st) {
+  const unsigned rows_grid = static_cast<unsigned>((dout + kRowsPerWg - 1) / kRowsPerWg);
+  for (int64_t c0 = 0; c0 < din; c0 += B) {
+    hipLaunchKernelGGL(sweep_kernel<B>, dim3(rows_grid), dim3(kSweepThreads), 0, st, w, r, dout, din, c0, bits,
+                       group, codes, scales, zeros, preround, e);
+    kq_status s = check_launch("sweep_kernel");
+    if (s != KQ_OK) return s;
+    const int64_t rest = din - c0 - B;
+    if (rest <= 0) break;
+    hipLaunchKernelGGL(trailing_kernel, dim3(static_cast<unsigned>((rest + 63) / 64),
+                                             static_cast<unsigned>((dout + 63) / 64)),
+                       dim3(256), 0, st, w, r, e, dout, din, c0, B);
+    s = check_launch("trailing_kernel");
+    if (s != KQ_OK) return s;
+  }
+  return KQ_OK;
+}
+
+}  // namespace
+
+size_t obs_workspace(int64_t dout, int64_t din, int block) {
+  (void)din;
+  return align_up(size_t(dout) * block * sizeof(double), 256);
+}
+
+kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits, int group, int block,
+                  uint8_t* codes, float* scales, uint8_t* zeros, double* preround, void* ws, hipStream_t st) {
+  double* e = static_cast<double*>(ws);
+  if (group == 0) {
+    hipLaunchKernelGGL(row_grid_kernel, dim3(static_cast<unsigned>((dout + 3) / 4)), dim3(256), 0, st, w, dout, din,
+                       bits, scales, zeros);
+    kq_status s = check_launch("row_grid_kernel");
+    if (s != KQ_OK) return s;
+  }
+  switch (block) {
+    case 32: return run_blocks<32>(w, r, dout, din, bits, group, codes, scales, zeros, preround, e, st);
+    case 64: return run_blocks<64>(w, r, dout, din, bits, group, codes, scales, zeros, preround, e, st);
+    case 128: return run_blocks<128>(w, r, dout, din, bits, group, codes, scales, zeros, preround, e, st);
+    default: return fail(KQ_EUNSUPPORTED, "block %d", block);
+  }
+}
+
+}  // namespace kq

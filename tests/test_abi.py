@@ -1,0 +1,166 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, rejects bad arguments before launching anything, and runs the host-only
+bit allocation."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kq_synth
+import oracle
+import post_quantization_04_amd as kq
+from conftest import ROOT, golden_rows
+
+HEADER = os.path.join(ROOT, "include", "kq.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kq.lib_path()):
+        pytest.skip("libkq.so not built")
+    return kq.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_six_entry_points():
+    syms = declared_symbols()
+    for name in ("kq_accumulate_cov", "kq_biip_rotate", "kq_cholesky_inv", "kq_obs_quantize",
+                 "kq_sensitivity", "kq_allocate_bits"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strings(L):
+    assert "gfx950" in kq.version()
+    assert L.kq_status_string(kq.KQ_EINVAL) == b"invalid argument"
+
+
+def _status(call):
+    return call
+
+
+def test_accumulate_cov_validation(L):
+    assert L.kq_accumulate_cov(FAKE, 10, 8, 4, 1.0, 0.0, FAKE, None, 0, None) == kq.KQ_EINVAL  # lda < d
+    assert b"lda" in L.kq_last_error()
+    assert L.kq_accumulate_cov(FAKE, -1, 8, 8, 1.0, 0.0, FAKE, None, 0, None) == kq.KQ_EINVAL
+    assert L.kq_accumulate_cov(None, 10, 8, 8, 1.0, 0.0, FAKE, None, 0, None) == kq.KQ_EINVAL
+    assert L.kq_accumulate_cov(FAKE, 10, 8, 8, 1.0, 0.0, None, None, 0, None) == kq.KQ_EINVAL
+    need = L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 10, 8, 0)
+    assert need > 0
+    assert L.kq_accumulate_cov(FAKE, 10, 8, 8, 1.0, 0.0, FAKE, FAKE, need - 1, None) == kq.KQ_EINVAL
+    assert b"workspace" in L.kq_last_error()
+
+
+def test_obs_validation(L):
+    def call(bits=4, group=128, block=128, din=256, ws=1 << 30):
+        return L.kq_obs_quantize(FAKE, FAKE, 4, din, bits, group, block, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert call(bits=1) == kq.KQ_EINVAL
+    assert call(bits=9) == kq.KQ_EINVAL
+    assert call(din=200) == kq.KQ_EINVAL            # block does not divide din
+    assert call(group=48) == kq.KQ_EINVAL           # group does not divide block
+    assert call(group=-1) == kq.KQ_EINVAL
+    assert call(block=256, group=0, din=512) == kq.KQ_EUNSUPPORTED
+    assert call(ws=0) == kq.KQ_EINVAL
+
+
+def test_biip_validation(L):
+    good = kq.Rot(n=128, m=1, log2p=7, signs=0x1000, q=0x1000)
+    bad_n = kq.Rot(n=96, m=1, log2p=7, signs=0x1000, q=0x1000)
+    even_m = kq.Rot(n=128, m=2, log2p=6, signs=0x1000, q=0x1000)
+    big = 1 << 40
+
+    def call(rin, rout, flags, dtype=kq.KQ_BF16, dout=64, din=128, hx=FAKE, hg=FAKE):
+        return L.kq_biip_rotate(FAKE, dtype, dout, din, ctypes.c_void_p(0x2000), hx, hg,
+                                None if rin is None else ctypes.byref(rin),
+                                None if rout is None else ctypes.byref(rout), flags, FAKE, FAKE, FAKE, big, None)
+    assert call(bad_n, None, kq.KQ_BIIP_INPUT) == kq.KQ_EINVAL
+    assert call(even_m, None, kq.KQ_BIIP_INPUT) == kq.KQ_EINVAL
+    assert call(None, None, kq.KQ_BIIP_INPUT) == kq.KQ_EINVAL
+    assert call(good, None, 0x40) == kq.KQ_EINVAL                               # unknown flag
+    assert call(good, None, kq.KQ_BIIP_INPUT, hx=None) == kq.KQ_EINVAL          # side needs H_X
+    assert call(good, None, kq.KQ_BIIP_INPUT | kq.KQ_BIIP_INVERSE) == kq.KQ_EINVAL  # inverse needs f64
+    assert call(good, None, kq.KQ_BIIP_INPUT, dtype=7) == kq.KQ_EINVAL
+    assert call(good, None, kq.KQ_BIIP_INPUT, din=40000) == kq.KQ_EINVAL
+
+
+def test_cholesky_and_score_validation(L):
+    assert L.kq_cholesky_inv(FAKE, 0, 0.01, FAKE, FAKE, 1 << 30, None) == kq.KQ_EINVAL
+    assert L.kq_cholesky_inv(FAKE, 16, -1.0, FAKE, FAKE, 1 << 30, None) == kq.KQ_EINVAL
+    assert L.kq_cholesky_inv(FAKE, 16, float("nan"), FAKE, FAKE, 1 << 30, None) == kq.KQ_EINVAL
+    assert L.kq_cholesky_inv(None, 16, 0.01, FAKE, FAKE, 1 << 30, None) == kq.KQ_EINVAL
+    assert L.kq_cholesky_inv(FAKE, 16, 0.01, FAKE, FAKE, 0, None) == kq.KQ_EINVAL
+    assert L.kq_sensitivity(FAKE, 8, None, 8, kq.KQ_SCORE_KRONQ, FAKE, None) == kq.KQ_EINVAL
+    assert L.kq_sensitivity(FAKE, 8, FAKE, 8, 5, FAKE, None) == kq.KQ_EINVAL
+
+
+def test_workspace_sizes(L):
+    inv = ctypes.c_size_t(-1).value
+    assert L.kq_workspace_size(99, 1, 1, 1) == inv
+    assert L.kq_workspace_size(kq.KQ_OP_BIIP, 0, 8, 0) == inv
+    assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 0, 64, 0) == 0
+    # float32 partials of all lower-triangle 256 x 256 tiles of one slice group
+    assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8192, 512, 0) >= 3 * 256 * 256 * 4
+    assert L.kq_workspace_size(kq.KQ_OP_OBS, 100, 256, 128) >= 100 * 128 * 8
+    assert L.kq_workspace_size(kq.KQ_OP_CHOLESKY, 100, 0, 0) >= 3 * 128 * 128 * 4
+
+
+def test_allocate_bits_matches_oracle_and_golden(L):
+    for scores, n, choices, target, want in golden_rows("allocation_examples.txt"):
+        args = ([float(x) for x in scores.split()], [int(x) for x in n.split()],
+                [int(x) for x in choices.split()], int(target))
+        if want == "infeasible":
+            with pytest.raises(kq.KQError) as ei:
+                kq.allocate_bits(*args)
+            assert ei.value.status == kq.KQ_EINFEASIBLE
+        else:
+            assert kq.allocate_bits(*args) == [int(x) for x in want.split()]
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        n_l = int(rng.integers(1, 12))
+        scores = rng.uniform(0, 5, n_l)
+        if n_l > 2:
+            scores[2] = scores[0]
+        n = rng.integers(1, 10 ** 8, n_l)
+        target = int(rng.integers(1500, 5000))
+        want = oracle.allocate_bits(scores, n, [2, 3, 4], target)
+        if want == oracle.INFEASIBLE:
+            with pytest.raises(kq.KQError):
+                kq.allocate_bits(scores, n, [2, 3, 4], target)
+        else:
+            assert kq.allocate_bits(scores, n, [4, 2, 3, 3], target) == want
+
+
+def test_allocate_bits_config5_budget(L):
+    cfg = kq_synth.config(5)
+    n = [s.dout * s.din for s in cfg.subs]
+    scores = np.arange(len(n), dtype=np.float64)[::-1]
+    bits = kq.allocate_bits(scores, n, cfg.alloc_choices, cfg.alloc_target_millibits)
+    assert bits == oracle.allocate_bits(scores, n, cfg.alloc_choices, cfg.alloc_target_millibits)
+    assert sum(b * k for b, k in zip(bits, n)) <= 3 * sum(n)
+
+
+def test_allocate_bits_validation(L):
+    with pytest.raises(kq.KQError):
+        kq.allocate_bits([1.0], [10], [1], 3000)
+    with pytest.raises(kq.KQError):
+        kq.allocate_bits([1.0], [0], [2], 3000)
+    with pytest.raises(kq.KQError):
+        kq.allocate_bits([1.0], [10], [2], -5)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setenv("KQ_LIB", "/nonexistent/libkq.so")
+    monkeypatch.setattr(kq, "_LIB", None)
+    with pytest.raises(kq.KQError):
+        kq.lib()

@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Throughput of the KronQ per-layer quantization path on one MI355X.
+
+One step is one pass of the whole path over one layer whose inputs are
+already resident in HBM:
+  1. H_X = X^T X / N and H_G = G^T G / N (bf16-MFMA symmetric rank-k updates
+     over all N tokens),
+  2. the trace score tr(H_G) tr(H_X) and the bit allocation from it,
+  3. BiIP (diagonal rescale + randomised Hadamard rotation on both sides of W,
+     with H_X and H_G transformed alongside),
+  4. the damped Cholesky factor of H_X''^-1,
+  5. the column-wise OBS sweep with its lazy-batch trailing products.
+Workload: LLaMA-2-7B q_proj shapes (W 4096 x 4096 bf16; X and G 262144 x 4096
+bf16, 128 sequences of 2048 tokens), 2-bit, group 128, block 128, damping
+0.01, seeded synthetic inputs.
+
+value = weights quantised per second, end to end including the covariance
+accumulation. The roofline object covers the dominant kernel, the bf16 MFMA
+SYRK (syrk_partial): algorithmic flops N d (d + 1) per covariance over the
+summed durations of its launches, timed with HIP events that the library
+records around each launch on its stream. The CPU baseline is the float64
+oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--bits", type=int, default=2, choices=(2, 4))
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
+    p.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's covariance sample")
+    p.add_argument("--cpu-rows", type=int, default=64, help="weight rows in the oracle's sweep sample")
+    return p.parse_args()
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:  # noqa: BLE001
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, cfg, sub, bits, tokens, rows):
+    """The float64 oracle on a bounded sample, scaled to one full layer."""
+    import numpy as np
+    import oracle
+
+    n_tok = cfg.n_tokens
+    t0 = time.perf_counter()
+    hx = oracle.covariance([wl.x("attn_in")[:tokens]])
+    hg = oracle.covariance([wl.g(sub.name)[:tokens]])
+    t_cov = (time.perf_counter() - t0) * (n_tok / tokens)
+    t0 = time.perf_counter()
+    s = oracle.sensitivity(hx, hg)
+    oracle.allocate_bits([s], [sub.dout * sub.din], [bits], bits * 1000)
+    t_score = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    w2, hx2, _, _, _ = oracle.biip_forward(wl.weight_f64(sub.name), hx, hg, wl.rot_in("attn_in"),
+                                           wl.rot_out(sub.name))
+    t_biip = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r = oracle.chol_inv_upper(hx2, cfg.damp)
+    t_chol = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.obs_quantize(w2[:rows], r, bits, cfg.group)
+    t_obs = (time.perf_counter() - t0) * (sub.dout / rows)
+    total = t_cov + t_score + t_biip + t_chol + t_obs
+    return {
+        "value": round(sub.dout * sub.din / total / 1e6, 4),
+        "unit": "Mweights/s",
+        "cores": cpu_threads(),
+        "kind": "oracle",
+        "sample": (f"float64 oracle: covariances over {tokens} of {n_tok} tokens (x{n_tok / tokens:g}), "
+                   f"OBS sweep on {rows} of {sub.dout} rows (x{sub.dout / rows:g}), BiIP, Cholesky and score "
+                   f"at full size; seconds per layer {total:.1f}"),
+        "seconds_per_layer": round(total, 2),
+    }
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU; the path's multi-GPU sharding is design only, "
+                                   "so --gpus must be 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kq_synth
+    import post_quantization_04_amd as kq
+    from post_quantization_04_amd import pipeline
+
+    dev = torch.device("cuda:0")
+    cfg = kq_synth.config(2)
+    sub = cfg.subs[0]
+    dout, din, n_tok = sub.dout, sub.din, cfg.n_tokens
+    wl = kq_synth.Workload(cfg)
+
+    log(f"libkq {kq.version()}; generating {cfg.name} inputs")
+    t0 = time.perf_counter()
+    x = wl.x("attn_in")
+    g = wl.g(sub.name)
+    w = wl.weight(sub.name)
+    si, so = wl.rot_in("attn_in"), wl.rot_out(sub.name)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    gd = torch.from_numpy(g.view(np.int16)).to(dev)
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    ri, ro = pipeline.upload_rot(si.signs, si.q, dev), pipeline.upload_rot(so.signs, so.q, dev)
+
+    f32, f64 = torch.float32, torch.float64
+    hx = torch.empty((din, din), dtype=f32, device=dev)
+    hg = torch.empty((dout, dout), dtype=f32, device=dev)
+    score = torch.empty(1, dtype=f64, device=dev)
+    w2 = torch.empty((dout, din), dtype=f64, device=dev)
+    s_x = torch.empty(din, dtype=f64, device=dev)
+    s_g = torch.empty(dout, dtype=f64, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    codes = torch.empty((dout, din), dtype=torch.uint8, device=dev)
+    ng = din // cfg.group
+    scales = torch.empty((dout, ng), dtype=f32, device=dev)
+    zeros = torch.empty((dout, ng), dtype=torch.uint8, device=dev)
+
+    def scratch(n):
+        return torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
+
+    ws_cov = scratch(max(kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, din),
+                         kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, dout)))
+    ws_biip = scratch(kq.workspace_size(kq.KQ_OP_BIIP, dout, din))
+    ws_chol = scratch(kq.workspace_size(kq.KQ_OP_CHOLESKY, din))
+    ws_obs = scratch(kq.workspace_size(kq.KQ_OP_OBS, dout, din, cfg.block))
+    flags = pipeline.ALL_SIDES
+    stages = ["cov_x", "cov_g", "score_alloc", "biip", "cholesky", "obs"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        kq.accumulate_cov(xd, hx, 1.0 / n_tok, 0.0, ws=ws_cov)
+        mark(1)
+        kq.accumulate_cov(gd, hg, 1.0 / n_tok, 0.0, ws=ws_cov)
+        mark(2)
+        kq.sensitivity(hx, hg, score)
+        bits = kq.allocate_bits([float(score.item())], [dout * din], [args.bits], args.bits * 1000)[0]
+        mark(3)
+        kq.biip_rotate(wd, w2, hx, hg, ri.rot, ro.rot, flags, s_x, s_g, ws=ws_biip)
+        mark(4)
+        kq.cholesky_inv(hx, cfg.damp, info, ws=ws_chol)
+        mark(5)
+        kq.obs_quantize(w2, hx, bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
+        mark(6)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise RuntimeError(f"Cholesky reported info = {int(info.item())}")
+
+    log(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    kq.timing_enable("syrk_partial")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launches, syrk_ms = kq.timing_query("syrk_partial")
+    kq.timing_enable(None)
+
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {s: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, s in enumerate(stages)}
+    flops_cov = n_tok * din * (din + 1) + n_tok * dout * (dout + 1)
+    t_accum = (stage_ms["cov_x"] + stage_ms["cov_g"]) / 1e3
+    t_quant = sum(stage_ms[s] for s in ("score_alloc", "biip", "cholesky", "obs")) / 1e3
+    syrk_tflops = flops_cov * args.steps / (syrk_ms / 1e3) / 1e12 if syrk_ms > 0 else 0.0
+    value = dout * din / (ms_step / 1e3) / 1e6
+    log(f"{ms_step:.2f} ms/step; stages {json.dumps({k: round(v, 3) for k, v in stage_ms.items()})}")
+    log(f"syrk_partial: {launches} launches, {syrk_ms / max(launches, 1):.3f} ms avg, {syrk_tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": "layer quantize throughput (Mweights/s) + H_X/H_G accumulate TFLOP/s",
+        "value": round(value, 3),
+        "unit": "Mweights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16/f32/f64",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: W {dout}x{din} bf16, X and G {n_tok}x{din} bf16, W{args.bits} "
+                         f"group {cfg.group} block {cfg.block} damp {cfg.damp}, BiIP both sides"),
+            "bits": args.bits,
+            "tokens": n_tok,
+            "weights": dout * din,
+        },
+        "accumulate_tflops": round(flops_cov / t_accum / 1e12, 2),
+        "quantize_mweights_per_s": round(dout * din / t_quant / 1e6, 2),
+        "seconds_per_layer": round(ms_step / 1e3, 5),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": {
+            "kernel": "syrk_partial",
+            "bound": "mfma",
+            "achieved": round(syrk_tflops, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(syrk_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "launches": launches,
+            "avg_launch_ms": round(syrk_ms / max(launches, 1), 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, cfg, sub, args.bits, args.cpu_tokens, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -88,6 +88,18 @@ const char* kq_status_string(kq_status s);
 const char* kq_last_error(void);
 
 /*
+ * Kernel timing (diagnostics, host calls). kq_timing_enable(filter) clears the
+ * record and, while enabled, brackets every launch of a kernel whose name
+ * contains `filter` ("" = all kernels) with HIP events on that launch's
+ * stream; NULL disables. kq_timing_query(name, ...) waits for the recorded
+ * events of kernels whose name contains `name` and returns the number of
+ * launches and their summed duration in milliseconds. Not thread safe
+ * against concurrent launches from other host threads.
+ */
+kq_status kq_timing_enable(const char* filter);
+kq_status kq_timing_query(const char* name, int64_t* launches, double* total_ms);
+
+/*
  * Bytes of scratch space an operation needs (0 = none).
  *   KQ_OP_ACCUMULATE_COV: d0 = rows, d1 = d
  *   KQ_OP_BIIP:           d0 = dout, d1 = din

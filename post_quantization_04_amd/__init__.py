@@ -19,7 +19,7 @@ __all__ = [
     "KQ_BF16", "KQ_F32", "KQ_F64", "KQ_BIIP_INPUT", "KQ_BIIP_OUTPUT", "KQ_BIIP_SCALE", "KQ_BIIP_INVERSE",
     "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
     "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
-    "biip_rotate", "cholesky_inv", "obs_quantize", "Rot",
+    "biip_rotate", "cholesky_inv", "obs_quantize", "Rot", "timing_enable", "timing_query",
 ]
 
 KQ_OK, KQ_EINVAL, KQ_ENOTPD, KQ_EINFEASIBLE, KQ_EDEVICE, KQ_EUNSUPPORTED = range(6)
@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.kq_status_string.restype = ctypes.c_char_p
     L.kq_status_string.argtypes = [ctypes.c_int]
     L.kq_last_error.restype = ctypes.c_char_p
+    L.kq_timing_enable.argtypes = [ctypes.c_char_p]
+    L.kq_timing_enable.restype = ctypes.c_int
+    L.kq_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    L.kq_timing_query.restype = ctypes.c_int
     L.kq_workspace_size.restype = _SZ
     L.kq_workspace_size.argtypes = [_I32, _I64, _I64, _I64]
     L.kq_accumulate_cov.argtypes = [_VP, _I64, _I64, _I64, _F32, _F32, _VP, _VP, _SZ, _VP]
@@ -85,6 +89,19 @@ def lib() -> ctypes.CDLL:
 
 def version() -> str:
     return lib().kq_version().decode()
+
+
+def timing_enable(filter: Optional[str] = "") -> None:
+    """Bracket launches of kernels whose name contains ``filter`` with HIP events (None: off)."""
+    _check(lib().kq_timing_enable(None if filter is None else filter.encode()), "kq_timing_enable")
+
+
+def timing_query(name: str):
+    """(launches, total milliseconds) of the recorded kernels whose name contains ``name``."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().kq_timing_query(name.encode(), ctypes.byref(n), ctypes.byref(ms)), "kq_timing_query")
+    return int(n.value), float(ms.value)
 
 
 def _check(status: int, what: str) -> None:

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ["kq_api.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip"]
+SOURCES = ["kq_api.hip", "timing.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip"]
 ARCH = "gfx950"
 
 

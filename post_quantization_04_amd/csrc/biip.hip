@@ -263,13 +263,19 @@ kq_status launch_rows(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot
   if (fits<double>(n, rot)) {
     kq_status r = allow_lds<double>(&rot_rows<double, Src, Dst>, "rot_rows");
     if (r != KQ_OK) return r;
-    hipLaunchKernelGGL((rot_rows<double, Src, Dst>), dim3(static_cast<unsigned>(rows)), dim3(kRowThreads),
-                       lds_bytes<double>(n, rot), st, src, n, dst, rot, sc);
+    {
+      LaunchTimer timer("rot_rows", st);
+      hipLaunchKernelGGL((rot_rows<double, Src, Dst>), dim3(static_cast<unsigned>(rows)), dim3(kRowThreads),
+                         lds_bytes<double>(n, rot), st, src, n, dst, rot, sc);
+    }
   } else {
     kq_status r = allow_lds<float>(&rot_rows<float, Src, Dst>, "rot_rows");
     if (r != KQ_OK) return r;
-    hipLaunchKernelGGL((rot_rows<float, Src, Dst>), dim3(static_cast<unsigned>(rows)), dim3(kRowThreads),
-                       lds_bytes<float>(n, rot), st, src, n, dst, rot, sc);
+    {
+      LaunchTimer timer("rot_rows", st);
+      hipLaunchKernelGGL((rot_rows<float, Src, Dst>), dim3(static_cast<unsigned>(rows)), dim3(kRowThreads),
+                         lds_bytes<float>(n, rot), st, src, n, dst, rot, sc);
+    }
   }
   return check_launch("rot_rows");
 }
@@ -282,8 +288,11 @@ kq_status launch_cols_t(const Src* src, int64_t n_rows, int64_t n_cols, Dst* dst
   if (r != KQ_OK) return r;
   const int npanel = static_cast<int>((n_cols + (1 << log2c) - 1) >> log2c);
   const int per_xcd = (npanel + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((rot_cols<T, Src, Dst>), dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kColThreads),
-                     lds_bytes<T>(n_rows << log2c, rot), st, src, n_rows, n_cols, dst, log2c, per_xcd, rot, sc);
+  {
+    LaunchTimer timer("rot_cols", st);
+    hipLaunchKernelGGL((rot_cols<T, Src, Dst>), dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kColThreads),
+                       lds_bytes<T>(n_rows << log2c, rot), st, src, n_rows, n_cols, dst, log2c, per_xcd, rot, sc);
+  }
   return check_launch("rot_cols");
 }
 
@@ -345,15 +354,24 @@ kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double
     return launch_rows<double, double>(w2, dout, din, w_out, ri, Scales{s_g, s_x, 1, 1}, st);
   }
   // scales come from the raw diagonals, before H_X and H_G are transformed in place
-  hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((din + 255) / 256)), dim3(256), 0, st, h_x, din,
-                     (inp && scale) ? 1 : 0, s_x);
+  {
+    LaunchTimer timer("scales_kernel", st);
+    hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((din + 255) / 256)), dim3(256), 0, st, h_x, din,
+                       (inp && scale) ? 1 : 0, s_x);
+  }
   if ((r = check_launch("scales_kernel")) != KQ_OK) return r;
   if (h_g || (out && scale)) {
-    hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st, h_g,
-                       dout, (out && scale) ? 1 : 0, s_g);
+    {
+      LaunchTimer timer("scales_kernel", st);
+      hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st, h_g,
+                         dout, (out && scale) ? 1 : 0, s_g);
+    }
   } else {
-    hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const float*>(nullptr), dout, 0, s_g);
+    {
+      LaunchTimer timer("scales_kernel", st);
+      hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st,
+                         static_cast<const float*>(nullptr), dout, 0, s_g);
+    }
   }
   if ((r = check_launch("scales_kernel")) != KQ_OK) return r;
   const Rot ri = make_rot(rot_in, inp, false), ro = make_rot(rot_out, out, false);

@@ -264,22 +264,37 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
   const int nb = static_cast<int>(dp / kB);
   kq_status r;
 
-  hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, h, d, damp, delta, info);
+  {
+    LaunchTimer timer("damp_kernel", st);
+    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, h, d, damp, delta, info);
+  }
   if ((r = check_launch("damp_kernel")) != KQ_OK) return r;
   // M is never read above its diagonal 64 x 64 blocks, so it needs no clearing.
-  hipLaunchKernelGGL(reverse_kernel, dim3(static_cast<unsigned>((dp + 255) / 256), static_cast<unsigned>(dp)),
-                     dim3(256), 0, st, h, d, dp, delta, a);
+  {
+    LaunchTimer timer("reverse_kernel", st);
+    hipLaunchKernelGGL(reverse_kernel, dim3(static_cast<unsigned>((dp + 255) / 256), static_cast<unsigned>(dp)),
+                       dim3(256), 0, st, h, d, dp, delta, a);
+  }
   if ((r = check_launch("reverse_kernel")) != KQ_OK) return r;
 
   for (int kb = 0; kb < nb; ++kb) {
-    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(256), 0, st, a, m, dp, kb, d, info);
+    {
+      LaunchTimer timer("diag_kernel", st);
+      hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(256), 0, st, a, m, dp, kb, d, info);
+    }
     if ((r = check_launch("diag_kernel")) != KQ_OK) return r;
     const int rest = nb - kb - 1;
     if (rest == 0) break;
-    hipLaunchKernelGGL(panel_kernel, dim3(static_cast<unsigned>(rest)), dim3(256), 0, st, a, m, dp, kb, info);
+    {
+      LaunchTimer timer("panel_kernel", st);
+      hipLaunchKernelGGL(panel_kernel, dim3(static_cast<unsigned>(rest)), dim3(256), 0, st, a, m, dp, kb, info);
+    }
     if ((r = check_launch("panel_kernel")) != KQ_OK) return r;
-    hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(rest * (rest + 1) / 2)), dim3(256), 0, st, a, dp,
-                       kb, info);
+    {
+      LaunchTimer timer("update_kernel", st);
+      hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(rest * (rest + 1) / 2)), dim3(256), 0, st, a, dp,
+                         kb, info);
+    }
     if ((r = check_launch("update_kernel")) != KQ_OK) return r;
   }
 
@@ -288,13 +303,19 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
     const int tiles_side = static_cast<int>(s / kB);
     const unsigned grid = static_cast<unsigned>(pairs * tiles_side * tiles_side);
     for (int stage = 0; stage < 2; ++stage) {
-      hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, stage, info);
+      {
+        LaunchTimer timer("merge_kernel", st);
+        hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, stage, info);
+      }
       if ((r = check_launch("merge_kernel")) != KQ_OK) return r;
     }
   }
 
-  hipLaunchKernelGGL(output_kernel, dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(d)),
-                     dim3(256), 0, st, m, d, dp, h);
+  {
+    LaunchTimer timer("output_kernel", st);
+    hipLaunchKernelGGL(output_kernel, dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(d)),
+                       dim3(256), 0, st, m, d, dp, h);
+  }
   return check_launch("output_kernel");
 }
 

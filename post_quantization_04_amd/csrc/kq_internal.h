@@ -20,6 +20,21 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // Turns a launch error into KQ_EDEVICE with the kernel's name.
 kq_status check_launch(const char* what);
 
+// Brackets one kernel launch with HIP events when kernel timing is enabled
+// for this kernel name (kq_timing_enable); otherwise does nothing.
+class LaunchTimer {
+ public:
+  LaunchTimer(const char* name, hipStream_t st);
+  ~LaunchTimer();
+  LaunchTimer(const LaunchTimer&) = delete;
+  LaunchTimer& operator=(const LaunchTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t begin_ = nullptr;
+};
+
 // Number of XCDs on MI355X; workgroups are dispatched to them round robin.
 constexpr int kXcds = 8;
 

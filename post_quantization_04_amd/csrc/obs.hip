@@ -241,15 +241,21 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
                      float* scales, uint8_t* zeros, double* preround, double* e, hipStream_t st) {
   const unsigned rows_grid = static_cast<unsigned>((dout + kRowsPerWg - 1) / kRowsPerWg);
   for (int64_t c0 = 0; c0 < din; c0 += B) {
-    hipLaunchKernelGGL(sweep_kernel<B>, dim3(rows_grid), dim3(kSweepThreads), 0, st, w, r, dout, din, c0, bits,
-                       group, codes, scales, zeros, preround, e);
+    {
+      LaunchTimer timer("sweep_kernel", st);
+      hipLaunchKernelGGL(sweep_kernel<B>, dim3(rows_grid), dim3(kSweepThreads), 0, st, w, r, dout, din, c0, bits,
+                         group, codes, scales, zeros, preround, e);
+    }
     kq_status s = check_launch("sweep_kernel");
     if (s != KQ_OK) return s;
     const int64_t rest = din - c0 - B;
     if (rest <= 0) break;
-    hipLaunchKernelGGL(trailing_kernel, dim3(static_cast<unsigned>((rest + 63) / 64),
-                                             static_cast<unsigned>((dout + 63) / 64)),
-                       dim3(256), 0, st, w, r, e, dout, din, c0, B);
+    {
+      LaunchTimer timer("trailing_kernel", st);
+      hipLaunchKernelGGL(trailing_kernel, dim3(static_cast<unsigned>((rest + 63) / 64),
+                                               static_cast<unsigned>((dout + 63) / 64)),
+                         dim3(256), 0, st, w, r, e, dout, din, c0, B);
+    }
     s = check_launch("trailing_kernel");
     if (s != KQ_OK) return s;
   }
@@ -267,8 +273,11 @@ kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits
                   uint8_t* codes, float* scales, uint8_t* zeros, double* preround, void* ws, hipStream_t st) {
   double* e = static_cast<double*>(ws);
   if (group == 0) {
-    hipLaunchKernelGGL(row_grid_kernel, dim3(static_cast<unsigned>((dout + 3) / 4)), dim3(256), 0, st, w, dout, din,
-                       bits, scales, zeros);
+    {
+      LaunchTimer timer("row_grid_kernel", st);
+      hipLaunchKernelGGL(row_grid_kernel, dim3(static_cast<unsigned>((dout + 3) / 4)), dim3(256), 0, st, w, dout, din,
+                         bits, scales, zeros);
+    }
     kq_status s = check_launch("row_grid_kernel");
     if (s != KQ_OK) return s;
   }

@@ -41,7 +41,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const float* __restrict
 
 kq_status score_run(const float* h_x, int64_t din, const float* h_g, int64_t dout, int mode, double* score,
                     hipStream_t st) {
-  hipLaunchKernelGGL(score_kernel, dim3(1), dim3(kThreads), 0, st, h_x, din, h_g, dout, mode, score);
+  {
+    LaunchTimer timer("score_kernel", st);
+    hipLaunchKernelGGL(score_kernel, dim3(1), dim3(kThreads), 0, st, h_x, din, h_g, dout, mode, score);
+  }
   return check_launch("score_kernel");
 }
 

@@ -266,8 +266,11 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
                    float* h, void* ws, hipStream_t st) {
   if (rows == 0) {
     const int64_t n = d * d;
-    hipLaunchKernelGGL(scale_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, h, n,
-                       beta);
+    {
+      LaunchTimer timer("scale_kernel", st);
+      hipLaunchKernelGGL(scale_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, h, n,
+                         beta);
+    }
     return check_launch("scale_kernel");
   }
   const Plan p = plan(rows, d);
@@ -279,12 +282,18 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
     const int nsl = (s0 + p.group <= p.nslices) ? p.group : p.nslices - s0;
     const int items = p.ntiles * nsl;
     const int per_xcd = (items + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL(syrk_partial, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a,
-                       lda, d, rows, p.ntiles, s0, nsl, per_xcd, vec_ok, part);
+    {
+      LaunchTimer timer("syrk_partial", st);
+      hipLaunchKernelGGL(syrk_partial, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a,
+                         lda, d, rows, p.ntiles, s0, nsl, per_xcd, vec_ok, part);
+    }
     kq_status s = check_launch("syrk_partial");
     if (s != KQ_OK) return s;
-    hipLaunchKernelGGL(syrk_reduce, dim3(static_cast<unsigned>(p.ntiles * 16)), dim3(256), 0, st, part, nsl,
-                       p.ntiles, d, acc, g == 0 ? 1 : 0, g == p.ngroups - 1 ? 1 : 0, alpha, beta, h);
+    {
+      LaunchTimer timer("syrk_reduce", st);
+      hipLaunchKernelGGL(syrk_reduce, dim3(static_cast<unsigned>(p.ntiles * 16)), dim3(256), 0, st, part, nsl,
+                         p.ntiles, d, acc, g == 0 ? 1 : 0, g == p.ngroups - 1 ? 1 : 0, alpha, beta, h);
+    }
     s = check_launch("syrk_reduce");
     if (s != KQ_OK) return s;
   }

@@ -117,71 +117,209 @@ __global__ void reverse_kernel(const float* __restrict__ h, int64_t d, int64_t d
   a[i * dp + j] = v;
 }
 
-// Factor the diagonal block kb in float64, write L_kk to A and L_kk^-1 to M.
-__global__ __launch_bounds__(256) void diag_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp,
-                                                   int kb, int64_t d, int32_t* __restrict__ info) {
-  __shared__ double l[kB][kB + 1];
-  __shared__ double x[kB][kB + 1];
+// ---------------------------------------------------------------------------
+// Diagonal block factorization in float64 with 16 x 16 sub-blocks.
+//   * base cases (16 x 16 Cholesky and its inverse) run on one wave, lanes
+//     0..15 owning one row each in registers, columns broadcast through LDS;
+//   * sub-panel, trailing and inverse products are float64 MFMA 16 x 16 x 4
+//     (operands A[i][k] at lane i + 16 k, B[k][j] at lane j + 16 k; result
+//     row 4 q + lane / 16, column lane % 16 in register q).
+// ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kP = kB + 1;  // LDS row pitch (doubles)
+
+// acc += A16 * B16 (or A16 * B16^T) for 16 x 16 tiles in LDS with pitch kP; one wave.
+template <bool BT>
+__device__ __forceinline__ f64x4 mm16(const double* a, const double* b, f64x4 acc) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const double fa = a[r * kP + 4 * kk + c];
+    const double fb = BT ? b[r * kP + 4 * kk + c] : b[(4 * kk + c) * kP + r];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void store16(double* c, f64x4 v, double scale) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[(4 * q + (lane >> 4)) * kP + (lane & 15)] = scale * v[q];
+}
+
+__device__ __forceinline__ f64x4 load16(const double* c) {
+  const int lane = threadIdx.x & 63;
+  f64x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = c[(4 * q + (lane >> 4)) * kP + (lane & 15)];
+  return v;
+}
+
+// 16 x 16 Cholesky (lower) of the sub-block at l + o * (kP + 1) and its inverse
+// into x + o * (kP + 1); wave 0 only (lanes >= 16 idle). Returns the local index
+// of the first bad pivot, or -1.
+__device__ int base16(double* l, double* x, int o, double* col) {
+  const int lane = threadIdx.x & 63;
+  const bool act = lane < 16;
+  double* L = l + o * (kP + 1);
+  double* X = x + o * (kP + 1);
+  double r[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) r[j] = act ? L[lane * kP + j] : 0.0;
+  int bad = -1;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const double piv = __shfl(r[k], k, 64);
+    if (!(piv > 0.0) || !isfinite(piv)) { bad = k; break; }
+    const double dk = sqrt(piv);
+    const double lik = (lane == k) ? dk : r[k] / dk;
+    r[k] = (lane >= k) ? lik : 0.0;
+    if (act) col[lane] = r[k];
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = k + 1; j < 16; ++j)
+      if (lane >= j) r[j] -= lik * col[j];
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (bad >= 0) return bad;
+  // inverse by forward elimination of [L | I]; lane i owns row i of X
+  double xr[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) xr[j] = (lane == j) ? 1.0 : 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const double lkk = __shfl(r[k], k, 64);
+    if (lane == k) {
+#pragma unroll
+      for (int j = 0; j <= k; ++j) xr[j] /= lkk;
+    }
+    if (lane == k) {
+#pragma unroll
+      for (int j = 0; j <= k; ++j) col[j] = xr[j];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const double lik = r[k];
+#pragma unroll
+    for (int j = 0; j <= k; ++j)
+      if (lane > k) xr[j] -= lik * col[j];
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (act) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      L[lane * kP + j] = (j <= lane) ? r[j] : 0.0;
+      X[lane * kP + j] = (j <= lane) ? xr[j] : 0.0;
+    }
+  }
+  return -1;
+}
+
+// Factor the 64 x 64 diagonal block kb (float64), invert its factor, and solve
+// one 64-row block of the panel below it: workgroup 0 writes L_kk to A and
+// L_kk^-1 to M; workgroup b >= 1 writes L[kb + b, kb] = A[kb + b, kb] L_kk^-T.
+// Every workgroup factors the (small) diagonal block itself.
+__global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp,
+                                                         int kb, int64_t d, int32_t* __restrict__ info) {
+  __shared__ double l[kB * kP];
+  __shared__ double x[kB * kP];
+  __shared__ double col[64];
   __shared__ int bad;
   if (*info) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t o = int64_t(kb) * kB;
   for (int e = tid; e < kB * kB; e += 256) {
     const int i = e >> 6, j = e & 63;
-    l[i][j] = (j <= i) ? static_cast<double>(a[(o + i) * dp + o + j]) : 0.0;
+    l[i * kP + j] = (j <= i) ? static_cast<double>(a[(o + i) * dp + o + j]) : 0.0;
+    x[i * kP + j] = 0.0;
   }
-  if (tid == 0) bad = 0;
+  if (tid == 0) bad = -1;
   __syncthreads();
-  for (int k = 0; k < kB; ++k) {
-    if (tid == 0) {
-      const double piv = l[k][k];
-      if (!(piv > 0.0) || !isfinite(piv)) {
-        bad = 1;
-        const int64_t ir = o + k;
-        const int64_t orig = (ir < d) ? d - 1 - ir : ir;
-        atomicCAS(info, 0, static_cast<int32_t>(orig + 1));
-      } else {
-        l[k][k] = sqrt(piv);
+  for (int s = 0; s < 4; ++s) {
+    if (wave == 0) {
+      const int b = base16(l, x, 16 * s, col);
+      if (lane == 0 && b >= 0) bad = 16 * s + b;
+    }
+    __syncthreads();
+    if (bad >= 0) {
+      if (tid == 0 && blockIdx.x == 0) {
+        const int64_t ir = o + bad;
+        atomicCAS(info, 0, static_cast<int32_t>(((ir < d) ? d - 1 - ir : ir) + 1));
+      }
+      return;
+    }
+    // sub-panel: L[t][s] = A[t][s] inv(L_ss)^T for t > s (one tile per wave)
+    const int t = s + 1 + wave;
+    f64x4 v = f64x4{};
+    if (t < 4) v = mm16<true>(l + 16 * t * kP + 16 * s, x + 16 * s * kP + 16 * s, v);
+    __syncthreads();
+    if (t < 4) store16(l + 16 * t * kP + 16 * s, v, 1.0);
+    __syncthreads();
+    // trailing: A[t][u] -= L[t][s] L[u][s]^T for s < u <= t (at most 6 tiles)
+    for (int q = wave; q < 6; q += 4) {
+      int tt = 0, uu = 0, n = 0;
+      for (int ti = s + 1; ti < 4; ++ti)
+        for (int ui = s + 1; ui <= ti; ++ui, ++n)
+          if (n == q) { tt = ti; uu = ui; }
+      if (q < n) {
+        f64x4 c = load16(l + 16 * tt * kP + 16 * uu);
+        f64x4 p = mm16<true>(l + 16 * tt * kP + 16 * s, l + 16 * uu * kP + 16 * s, f64x4{});
+        store16(l + 16 * tt * kP + 16 * uu, c - p, 1.0);
       }
     }
     __syncthreads();
-    if (bad) return;
-    for (int i = k + 1 + tid; i < kB; i += 256) l[i][k] /= l[k][k];
-    __syncthreads();
-    const int n = kB - 1 - k;
-    for (int e = tid; e < n * n; e += 256) {
-      const int i = k + 1 + e / n, j = k + 1 + e % n;
-      if (j <= i) l[i][j] -= l[i][k] * l[j][k];
+  }
+  // inverse: M[t][s] = -inv(L_tt) sum_{u = s}^{t - 1} L[t][u] M[u][s], row block by row block
+  for (int t = 1; t < 4; ++t) {
+    const int s = wave;  // one column block per wave
+    f64x4 acc = f64x4{};
+    if (s < t) {
+      for (int u = s; u < t; ++u) acc = mm16<false>(l + 16 * t * kP + 16 * u, x + 16 * u * kP + 16 * s, acc);
     }
+    __syncthreads();
+    if (s < t) store16(x + 16 * t * kP + 16 * s, acc, 1.0);  // temporary: T = sum L M
+    __syncthreads();
+    f64x4 mv = f64x4{};
+    if (s < t) mv = mm16<false>(x + 16 * t * kP + 16 * t, x + 16 * t * kP + 16 * s, f64x4{});
+    __syncthreads();
+    if (s < t) store16(x + 16 * t * kP + 16 * s, mv, -1.0);
     __syncthreads();
   }
-  // inverse of the lower factor, one column per thread (forward substitution)
-  if (tid < kB) {
-    const int j = tid;
-    for (int i = 0; i < j; ++i) x[i][j] = 0.0;
-    x[j][j] = 1.0 / l[j][j];
-    for (int i = j + 1; i < kB; ++i) {
-      double s = 0.0;
-      for (int k = j; k < i; ++k) s += l[i][k] * x[k][j];
-      x[i][j] = -s / l[i][i];
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < kB * kB; e += 256) {
+      const int i = e >> 6, j = e & 63;
+      if (j <= i) a[(o + i) * dp + o + j] = static_cast<float>(l[i * kP + j]);
+      m[(o + i) * dp + o + j] = static_cast<float>(x[i * kP + j]);
     }
+    return;
+  }
+  // panel block: P = A[r0.., kb] L_kk^-T, 64 x 64 x 64 in float64 MFMA (4 x 4 tiles of 16, 4 per wave)
+  const int64_t r0 = o + int64_t(blockIdx.x) * kB;
+  __syncthreads();
+  for (int e = tid; e < kB * kB; e += 256) {  // reuse l for the panel block
+    const int i = e >> 6, j = e & 63;
+    l[i * kP + j] = static_cast<double>(a[(r0 + i) * dp + o + j]);
   }
   __syncthreads();
-  for (int e = tid; e < kB * kB; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    if (j <= i) a[(o + i) * dp + o + j] = static_cast<float>(l[i][j]);
-    m[(o + i) * dp + o + j] = static_cast<float>(x[i][j]);
+  f64x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ti = wave, tj = q;
+    f64x4 c = f64x4{};
+    for (int u = 0; u <= tj; ++u)  // (L_kk^-T)[u][tj] = M[tj][u], zero for u > tj
+      c = mm16<true>(l + 16 * ti * kP + 16 * u, x + 16 * tj * kP + 16 * u, c);
+    acc[q] = c;
   }
-}
-
-// L[i, kb] = A[i, kb] L_kk^-T for every block row i > kb (in place).
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ a, const float* __restrict__ m, int64_t dp,
-                                                    int kb, const int32_t* __restrict__ info) {
-  if (*info) return;
-  const int64_t o = int64_t(kb) * kB;
-  const int64_t r0 = o + kB + int64_t(blockIdx.x) * kB;
-  float* blk = a + r0 * dp + o;
-  gemm_tile<false, true>(blk, dp, m + o * dp + o, dp, blk, dp, kB, kB, 0, kB, 1.0f, 0.0f);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = 16 * wave + 4 * w + (lane >> 4), j = 16 * q + (lane & 15);
+      a[(r0 + i) * dp + o + j] = static_cast<float>(acc[q][w]);
+    }
+  }
 }
 
 // A[i, j] -= L[i, kb] L[j, kb]^T for kb < j <= i.
@@ -278,18 +416,14 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
   if ((r = check_launch("reverse_kernel")) != KQ_OK) return r;
 
   for (int kb = 0; kb < nb; ++kb) {
-    {
-      LaunchTimer timer("diag_kernel", st);
-      hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(256), 0, st, a, m, dp, kb, d, info);
-    }
-    if ((r = check_launch("diag_kernel")) != KQ_OK) return r;
     const int rest = nb - kb - 1;
-    if (rest == 0) break;
     {
-      LaunchTimer timer("panel_kernel", st);
-      hipLaunchKernelGGL(panel_kernel, dim3(static_cast<unsigned>(rest)), dim3(256), 0, st, a, m, dp, kb, info);
+      LaunchTimer timer("diag_panel_kernel", st);
+      hipLaunchKernelGGL(diag_panel_kernel, dim3(static_cast<unsigned>(1 + rest)), dim3(256), 0, st, a, m, dp, kb,
+                         d, info);
     }
-    if ((r = check_launch("panel_kernel")) != KQ_OK) return r;
+    if ((r = check_launch("diag_panel_kernel")) != KQ_OK) return r;
+    if (rest == 0) break;
     {
       LaunchTimer timer("update_kernel", st);
       hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(rest * (rest + 1) / 2)), dim3(256), 0, st, a, dp,

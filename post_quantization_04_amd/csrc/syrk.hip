@@ -1,26 +1,33 @@
 // H = alpha * A^T A + beta * H for token-major bf16 A on gfx950 bf16 MFMA.
 //
 // A is [rows, d]: tokens by channels, channels contiguous. The contraction
-// runs over tokens, so each MFMA operand needs eight consecutive tokens of one
-// channel per lane. A thread loads an 8 token x 8 channel block with eight
-// 16-byte global loads (coalesced along channels), transposes it in registers
-// with 16-bit shuffles and writes eight channel-major 16-byte packs to LDS.
-// MFMA fragments are then single ds_read_b128 loads. LDS rows are 128 bytes
-// (64 tokens) and the 16-byte chunks of a row are XOR-swizzled with the row
-// index so that both the transposing writes and the fragment reads are free of
-// bank conflicts.
+// runs over tokens, so each MFMA operand needs consecutive tokens of one
+// channel per lane. Panels of 64 tokens x 256 channels are copied straight
+// from global memory into LDS in their natural token-major layout
+// (global_load_lds_dwordx4, no register staging), and the MFMA fragments are
+// read with the gfx950 transposing LDS load ds_read_b64_tr_b16: in each group
+// of 16 lanes, four lanes per token supply 16 consecutive channels and lane j
+// receives channel j at the four tokens. Two such loads give the eight tokens
+// of a v_mfma_f32_32x32x16_bf16 operand. The 16-byte chunks of each 512-byte
+// token row are XOR-swizzled with the token index so that both the DMA writes
+// and the transposing reads run at the LDS bank minimum.
+//
+// LDS holds two stages (2 x 2 panels x 32 KB); the loads of stage s + 1 are in
+// flight while the MFMAs of stage s run, with one barrier per stage. A final
+// partial stage (fewer than 64 tokens) or a misaligned row pitch takes a
+// register path that zero-fills missing tokens.
 //
 // Work item = (lower-triangle 256 x 256 output tile, token slice of 8192
-// rows). Each workgroup sums one slice in float32 MFMA accumulators
-// (v_mfma_f32_32x32x16_bf16; bf16 products are exact) and writes the float32
-// partial tile. A second kernel adds the slices of a tile in float64, applies
-// alpha and beta, rounds once to float32 and writes both triangles. Short
-// float32 runs keep the accumulated rounding near 1e-7 relative, which the
-// downstream column sweep needs.
+// rows). Each workgroup sums one slice in float32 MFMA accumulators (bf16
+// products are exact) and writes the float32 partial tile. A second kernel
+// adds the slices of a tile in float64, applies alpha and beta, rounds once to
+// float32 and writes both triangles. Short float32 runs keep the accumulated
+// rounding near 1e-7 relative, which the downstream column sweep needs.
 //
 // Workgroups are dispatched round robin over the 8 XCDs; work items are
-// renumbered so that each XCD takes a contiguous run of tiles of one slice,
-// which share their channel panels in that XCD's L2.
+// renumbered so that each XCD runs a contiguous run of a blocked tile order
+// (4 tile rows x 8 tile columns), whose 32 concurrent workgroups share about
+// 12 channel panels in that XCD's L2.
 #include "kq_internal.h"
 
 namespace kq {
@@ -36,14 +43,14 @@ constexpr int kTargetItems = 2048;  // work items per launch before slices are s
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// 16-byte unit index of (channel row, token chunk) in a panel.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 8 + (chunk ^ ((row & 7) ^ ((row >> 3) & 7)));
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
+#define KQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define KQ_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
+
+// 16-byte slot of (token t, channel chunk cc) in a panel stage: 32 chunks per
+// token row, chunk position XOR 4 * (t mod 4) inside each half row.
+__device__ __forceinline__ int slot(int t, int cc) { return t * 32 + ((cc & 16) | ((cc & 15) ^ ((t & 3) << 2))); }
 
 // Triangular tile numbering: t = I (I + 1) / 2 + J with J <= I.
 __device__ __forceinline__ void tri(int t, int& I, int& J) {
@@ -54,17 +61,35 @@ __device__ __forceinline__ void tri(int t, int& I, int& J) {
   J = t - i * (i + 1) / 2;
 }
 
-// Global loads of one 8 x 8 block of the thread: rows tok0 + 8 tg + r, channels c0 + 8 cg ...
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ a, int64_t lda, int64_t d,
-                                           int64_t c0, int64_t tok0, int64_t tok_end, bool vec_ok,
-                                           uint4 (&v)[8]) {
-  const int tid = threadIdx.x;
-  const int64_t ch = c0 + (tid & 31) * 8;
-  const int64_t tb = tok0 + (tid >> 5) * 8;
+// Full stage, aligned rows (lda and d multiples of 8): each wave copies 512
+// slots with 8 DMA loads. Lane l of load i fills slot (wave * 512 + i * 64 + l);
+// its global chunk is the un-swizzled position. Chunks past channel d re-read
+// the row's last 8 channels (their outputs are discarded); every token exists.
+__device__ __forceinline__ void load_stage_dma(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
+                                               int64_t t0, uint4* __restrict__ panel) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int i = 0; i < 8; ++i) {
+    const int sl = wave * 512 + i * 64 + lane;
+    const int t = sl >> 5, cs = sl & 31;
+    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
+    int64_t ch = c0 + int64_t(cc) * 8;
+    if (ch > d - 8) ch = d - 8;
+    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(a + (t0 + t) * lda + ch), KQ_LDS(panel + wave * 512 + i * 64), 16, 0, 0);
+  }
+}
+
+// Any stage: register loads with zero fill for tokens >= tok_end and channels >= d.
+__device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
+                                                int64_t t0, int64_t tok_end, bool vec_ok, uint4* __restrict__ panel) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int sl = i * 256 + static_cast<int>(threadIdx.x);
+    const int t = sl >> 5, cs = sl & 31;
+    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
+    const int64_t ch = c0 + int64_t(cc) * 8;
+    const int64_t tok = t0 + t;
     uint4 val = make_uint4(0, 0, 0, 0);
-    const int64_t tok = tb + r;
     if (tok < tok_end && ch < d) {
       const uint16_t* p = a + tok * lda + ch;
       if (vec_ok && ch + 8 <= d) {
@@ -79,41 +104,54 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ a, int64
         val.w = e[6] | (uint32_t(e[7]) << 16);
       }
     }
-    v[r] = val;
+    panel[sl] = val;
   }
 }
 
-// Transpose the 8 x 8 block (tokens x channels) and store channel-major packs.
-__device__ __forceinline__ void store_block(uint4* __restrict__ panel, const uint4 (&v)[8]) {
-  const int tid = threadIdx.x;
-  const int cg = tid & 31, tg = tid >> 5;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t out[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = word(v[2 * k], c >> 1);
-      const uint32_t hi = word(v[2 * k + 1], c >> 1);
-      out[k] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    panel[swz(cg * 8 + c, tg)] = make_uint4(out[0], out[1], out[2], out[3]);
-  }
+__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
+                                           int64_t t0, int64_t tok_end, bool vec_ok, uint4* __restrict__ panel) {
+  if (vec_ok && t0 + kKT <= tok_end) load_stage_dma(a, lda, d, c0, t0, panel);
+  else load_stage_regs(a, lda, d, c0, t0, tok_end, vec_ok, panel);
 }
 
-__device__ __forceinline__ bf16x8 frag(const uint4* __restrict__ panel, int row, int chunk) {
-  return __builtin_bit_cast(bf16x8, panel[swz(row, chunk)]);
+// MFMA operand: 8 tokens (kk * 16 + 8 (lane / 32) + 0..7) of channel ch0 + lane % 32.
+__device__ __forceinline__ bf16x8 frag_tr(const uint4* __restrict__ panel, int ch0, int kk) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int ch = ch0 + 16 * (g & 1) + 4 * (j & 3);
+  const int cc = ch >> 3, half = (ch >> 2) & 1;
+  const int tb = kk * 16 + 8 * (g >> 1) + (j >> 2);
+  const char* base = reinterpret_cast<const char*>(panel) + half * 8;
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)KQ_LDS(base + slot(tb, cc) * 16));
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)KQ_LDS(base + slot(tb + 4, cc) * 16));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 r = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Lower-triangle tiles in blocks of 4 tile rows x 8 tile columns (row-major
+// inside a block): 32 consecutive work items share about 12 channel panels.
+__global__ void tile_order_kernel(int nt, int* __restrict__ order) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  int r = 0;
+  for (int bi = 0; bi < nt; bi += 4)
+    for (int bj = 0; bj <= bi + 3 && bj < nt; bj += 8)
+      for (int i = bi; i < bi + 4 && i < nt; ++i)
+        for (int j = bj; j < bj + 8 && j <= i; ++j) order[r++] = i * (i + 1) / 2 + j;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
     const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
-    int nsl, int per_xcd, int vec_ok, float* __restrict__ part) {
-  __shared__ uint4 lds[2][kPanelUnits];  // panel I, panel J (64 KB)
+    int nsl, int per_xcd, int vec_ok, const int* __restrict__ order, float* __restrict__ part) {
+  __shared__ uint4 lds[2][2][kPanelUnits];  // [stage buffer][panel I, panel J] (128 KB)
 
   // XCD-aware renumbering: XCD x = blockIdx % 8 takes items [x * per_xcd, (x + 1) * per_xcd).
   const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (item >= ntiles * nsl) return;
   const int sl = item / ntiles;
-  const int tile = item - sl * ntiles;
+  const int tile = order[item - sl * ntiles];
   int I, J;
   tri(tile, I, J);
   const bool diag = (I == J);
@@ -125,8 +163,6 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wi = wave >> 1, wj = wave & 1;
-  const uint4* pa = lds[0];
-  const uint4* pb = diag ? lds[0] : lds[1];
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -134,33 +170,34 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
 
-  uint4 va[8], vb[8];
-  load_block(a, lda, d, cI, tok_begin, tok_end, vec_ok, va);
-  if (!diag) load_block(a, lda, d, cJ, tok_begin, tok_end, vec_ok, vb);
+  load_stage(a, lda, d, cI, tok_begin, tok_end, vec_ok, lds[0][0]);
+  if (!diag) load_stage(a, lda, d, cJ, tok_begin, tok_end, vec_ok, lds[0][1]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   for (int s = 0; s < nstage; ++s) {
-    store_block(lds[0], va);
-    if (!diag) store_block(lds[1], vb);
-    __syncthreads();
+    const int cur = s & 1;
     if (s + 1 < nstage) {
       const int64_t t0 = tok_begin + int64_t(s + 1) * kKT;
-      load_block(a, lda, d, cI, t0, tok_end, vec_ok, va);
-      if (!diag) load_block(a, lda, d, cJ, t0, tok_end, vec_ok, vb);
+      load_stage(a, lda, d, cI, t0, tok_end, vec_ok, lds[cur ^ 1][0]);
+      if (!diag) load_stage(a, lda, d, cJ, t0, tok_end, vec_ok, lds[cur ^ 1][1]);
     }
+    const uint4* pa = lds[cur][0];
+    const uint4* pb = diag ? lds[cur][0] : lds[cur][1];
 #pragma unroll
     for (int kk = 0; kk < kKT / 16; ++kk) {
-      const int chunk = 2 * kk + (lane >> 5);
       bf16x8 fa[4], fb[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) fa[x] = frag(pa, wi * 128 + x * 32 + (lane & 31), chunk);
+      for (int x = 0; x < 4; ++x) fa[x] = frag_tr(pa, wi * 128 + x * 32, kk);
 #pragma unroll
-      for (int y = 0; y < 4; ++y) fb[y] = frag(pb, wj * 128 + y * 32 + (lane & 31), chunk);
+      for (int y = 0; y < 4; ++y) fb[y] = frag_tr(pb, wj * 128 + y * 32, kk);
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -236,7 +273,7 @@ __global__ void scale_kernel(float* __restrict__ h, int64_t n, float beta) {
 
 struct Plan {
   int nt, ntiles, nslices, group, ngroups;
-  size_t part_bytes, acc_bytes;
+  size_t part_bytes, acc_bytes, order_bytes;
 };
 
 Plan plan(int64_t rows, int64_t d) {
@@ -251,6 +288,7 @@ Plan plan(int64_t rows, int64_t d) {
   p.ngroups = p.nslices ? (p.nslices + g - 1) / g : 0;
   p.part_bytes = align_up(size_t(g) * p.ntiles * kT * kT * sizeof(float), 256);
   p.acc_bytes = p.ngroups > 1 ? align_up(size_t(p.ntiles) * kT * kT * sizeof(double), 256) : 0;
+  p.order_bytes = align_up(size_t(p.ntiles) * sizeof(int), 256);
   return p;
 }
 
@@ -259,7 +297,7 @@ Plan plan(int64_t rows, int64_t d) {
 size_t syrk_workspace(int64_t rows, int64_t d) {
   if (rows <= 0) return 0;
   const Plan p = plan(rows, d);
-  return p.part_bytes + p.acc_bytes;
+  return p.part_bytes + p.acc_bytes + p.order_bytes;
 }
 
 kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha, float beta,
@@ -276,7 +314,15 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   const Plan p = plan(rows, d);
   float* part = static_cast<float*>(ws);
   double* acc = reinterpret_cast<double*>(static_cast<char*>(ws) + p.part_bytes);
-  const int vec_ok = (lda % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0);
+  int* order = reinterpret_cast<int*>(static_cast<char*>(ws) + p.part_bytes + p.acc_bytes);
+  // 16-byte loads need aligned rows; the DMA path also needs whole 8-channel chunks
+  const int vec_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0);
+  {
+    LaunchTimer timer("tile_order_kernel", st);
+    hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(64), 0, st, p.nt, order);
+  }
+  kq_status s0 = check_launch("tile_order_kernel");
+  if (s0 != KQ_OK) return s0;
   for (int g = 0; g < p.ngroups; ++g) {
     const int s0 = g * p.group;
     const int nsl = (s0 + p.group <= p.nslices) ? p.group : p.nslices - s0;
@@ -285,7 +331,7 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
     {
       LaunchTimer timer("syrk_partial", st);
       hipLaunchKernelGGL(syrk_partial, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a,
-                         lda, d, rows, p.ntiles, s0, nsl, per_xcd, vec_ok, part);
+                         lda, d, rows, p.ntiles, s0, nsl, per_xcd, vec_ok, order, part);
     }
     kq_status s = check_launch("syrk_partial");
     if (s != KQ_OK) return s;

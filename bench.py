@@ -41,6 +41,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's covariance sample")
     p.add_argument("--cpu-rows", type=int, default=64, help="weight rows in the oracle's sweep sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after timing, copy 1 GiB device-to-device (a reference kernel for HBM byte counters)")
     return p.parse_args()
 
 
@@ -238,6 +240,14 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, cfg, sub, args.bits, args.cpu_tokens, args.cpu_rows)

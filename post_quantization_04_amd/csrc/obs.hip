@@ -113,72 +113,76 @@ __global__ __launch_bounds__(kSweepThreads) void sweep_kernel(
   const bool valid = row < dout;
   const int maxq = (1 << bits) - 1;
   const int64_t ngroups = group ? din / group : 1;
+  const int gmask = group - 1;  // group is a power of two dividing B
 
-  double x[EPL], tq[EPL], es[EPL];
-  int cq[EPL];
+  // x[e] holds column l16 + 16 (eo + e) of this lane's row: the slice being
+  // swept is always x[0]; registers rotate down after each slice of 16 columns.
+  double x[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    x[e] = valid ? w[row * din + c0 + l16 + 16 * e] : 0.0;
-    tq[e] = 0.0;
-    es[e] = 0.0;
-    cq[e] = 0;
-  }
+  for (int e = 0; e < EPL; ++e) x[e] = valid ? w[row * din + c0 + l16 + 16 * e] : 0.0;
   double s = 1.0, z = 0.0;
   if (group == 0 && valid) {
     s = static_cast<double>(scales[row]);
     z = static_cast<double>(zeros[row]);
   }
+  double inv_s = 1.0 / s;
 
-#pragma unroll EPL
-  for (int eo = 0; eo < EPL; ++eo)
-#pragma unroll 16
-  for (int lo = 0; lo < 16; ++lo) {
-    const int j = eo * 16 + lo;
-    if (group > 0 && ((c0 + j) % group) == 0) {
-      double mn = INFINITY, mx = -INFINITY;
+  for (int eo = 0; eo < EPL; ++eo) {
+    double tcur = 0.0, ecur = 0.0;
+    int ccur = 0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int col = l16 + 16 * e;
-        if (col >= j && col < j + group) {
-          mn = fmin(mn, x[e]);
-          mx = fmax(mx, x[e]);
+    for (int lo = 0; lo < 16; ++lo) {
+      const int j = eo * 16 + lo;
+      if (group > 0 && (j & gmask) == 0) {
+        double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const int col = l16 + 16 * (eo + e);
+          if (col >= j && col < j + group) {
+            mn = fmin(mn, x[e]);
+            mx = fmax(mx, x[e]);
+          }
+        }
+        for (int o = 8; o > 0; o >>= 1) {
+          mn = fmin(mn, __shfl_xor(mn, o, 16));
+          mx = fmax(mx, __shfl_xor(mx, o, 16));
+        }
+        make_grid(mn, mx, maxq, s, z);
+        inv_s = 1.0 / s;
+        if (l16 == 0 && valid) {
+          scales[row * ngroups + (c0 + j) / group] = static_cast<float>(s);
+          zeros[row * ngroups + (c0 + j) / group] = static_cast<uint8_t>(z);
         }
       }
-      for (int o = 8; o > 0; o >>= 1) {
-        mn = fmin(mn, __shfl_xor(mn, o, 16));
-        mx = fmax(mx, __shfl_xor(mx, o, 16));
+      // the rounding argument w * (1/s) is within two ulps of w / s
+      const double wv = x[0];
+      const double t = wv * inv_s;
+      const double q = fmin(fmax(rint(t) + z, 0.0), static_cast<double>(maxq));
+      const double wq = s * (q - z);
+      const double err = (wv - wq) * rinv[j];
+      if (l16 == lo) {
+        x[0] = wq;
+        tcur = t;
+        ecur = err;
+        ccur = static_cast<int>(q);
       }
-      make_grid(mn, mx, maxq, s, z);
-      if (l16 == 0 && valid) {
-        scales[row * ngroups + (c0 + j) / group] = static_cast<float>(s);
-        zeros[row * ngroups + (c0 + j) / group] = static_cast<uint8_t>(z);
+      const double eb = bcast16(err, lo);
+      const float* rr = &rl[j][l16 * EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int idx = eo + e < EPL ? eo + e : EPL - 1;  // registers past the block are never stored
+        x[e] = fma(-eb, static_cast<double>(rr[idx]), x[e]);
       }
     }
-    const double wv = x[eo];
-    const double t = wv / s;
-    const double q = fmin(fmax(rint(t) + z, 0.0), static_cast<double>(maxq));
-    const double wq = s * (q - z);
-    const double err = (wv - wq) * rinv[j];
-    if (l16 == lo) {
-      x[eo] = wq;
-      cq[eo] = static_cast<int>(q);
-      tq[eo] = t;
-      es[eo] = err;
+    if (valid) {
+      const int64_t col = c0 + l16 + 16 * eo;
+      w[row * din + col] = x[0];
+      codes[row * din + col] = static_cast<uint8_t>(ccur);
+      if (preround) preround[row * din + col] = tcur;
+      e_out[row * B + l16 + 16 * eo] = ecur;
     }
-    const double eb = bcast16(err, lo);
-    const float* rr = &rl[j][l16 * EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = fma(-eb, static_cast<double>(rr[e]), x[e]);
-  }
-
-  if (!valid) return;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int64_t col = c0 + l16 + 16 * e;
-    w[row * din + col] = x[e];
-    codes[row * din + col] = static_cast<uint8_t>(cq[e]);
-    if (preround) preround[row * din + col] = tq[e];
-    e_out[row * B + l16 + 16 * e] = es[e];
+    for (int e = 0; e + 1 < EPL; ++e) x[e] = x[e + 1];
   }
 }
 

@@ -24,10 +24,12 @@
 // float32 and writes both triangles. Short float32 runs keep the accumulated
 // rounding near 1e-7 relative, which the downstream column sweep needs.
 //
-// Workgroups are dispatched round robin over the 8 XCDs; work items are
-// renumbered so that each XCD runs a contiguous run of a blocked tile order
-// (4 tile rows x 8 tile columns), whose 32 concurrent workgroups share about
-// 12 channel panels in that XCD's L2.
+// Workgroups are dispatched round robin over the 8 XCDs. The tiles of a slice
+// are listed in a blocked order (4 tile rows x 8 tile columns) and cut into 8
+// contiguous groups; XCD x runs group x of slice 0, then of slice 1, ... So
+// all XCDs walk the token slices together (one or two 8192-token slices are
+// live at a time, which the Infinity Cache holds) and each XCD's L2 serves
+// the dozen channel panels of its tile group.
 #include "kq_internal.h"
 
 namespace kq {
@@ -38,7 +40,7 @@ constexpr int kKT = 64;          // tokens per LDS stage
 constexpr int kSlice = 8192;     // tokens per float32 partial sum
 constexpr int kThreads = 256;    // 4 waves in a 2 x 2 grid, 128 x 128 outputs each
 constexpr int kPanelUnits = kT * kKT * 2 / 16;  // 16-byte units per LDS panel (2048)
-constexpr int kTargetItems = 2048;  // work items per launch before slices are split into groups
+constexpr int kTargetItems = 8192;  // work items per launch before slices are split into groups
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -61,25 +63,7 @@ __device__ __forceinline__ void tri(int t, int& I, int& J) {
   J = t - i * (i + 1) / 2;
 }
 
-// Full stage, aligned rows (lda and d multiples of 8): each wave copies 512
-// slots with 8 DMA loads. Lane l of load i fills slot (wave * 512 + i * 64 + l);
-// its global chunk is the un-swizzled position. Chunks past channel d re-read
-// the row's last 8 channels (their outputs are discarded); every token exists.
-__device__ __forceinline__ void load_stage_dma(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
-                                               int64_t t0, uint4* __restrict__ panel) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int sl = wave * 512 + i * 64 + lane;
-    const int t = sl >> 5, cs = sl & 31;
-    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
-    int64_t ch = c0 + int64_t(cc) * 8;
-    if (ch > d - 8) ch = d - 8;
-    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(a + (t0 + t) * lda + ch), KQ_LDS(panel + wave * 512 + i * 64), 16, 0, 0);
-  }
-}
-
-// Any stage: register loads with zero fill for tokens >= tok_end and channels >= d.
+// Register path for any stage: zero fill for tokens >= tok_end and channels >= d.
 __device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
                                                 int64_t t0, int64_t tok_end, bool vec_ok, uint4* __restrict__ panel) {
 #pragma unroll
@@ -108,27 +92,68 @@ __device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, 
   }
 }
 
-__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
-                                           int64_t t0, int64_t tok_end, bool vec_ok, uint4* __restrict__ panel) {
-  if (vec_ok && t0 + kKT <= tok_end) load_stage_dma(a, lda, d, c0, t0, panel);
-  else load_stage_regs(a, lda, d, c0, t0, tok_end, vec_ok, panel);
+// Per-lane element offsets (from the stage origin a + t0 * lda) of the 8
+// chunks this lane copies into a panel: load i of wave w fills slot
+// w * 512 + i * 64 + lane, whose chunk is the un-swizzled position. Chunks past
+// channel d re-read the row's last 8 channels (their outputs are discarded).
+__device__ __forceinline__ void dma_offsets(int64_t lda, int64_t d, int64_t c0, int32_t (&off)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int sl = wave * 512 + i * 64 + lane;
+    const int t = sl >> 5, cs = sl & 31;
+    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
+    int64_t ch = c0 + int64_t(cc) * 8;
+    if (ch > d - 8) ch = d - 8;
+    off[i] = static_cast<int32_t>(int64_t(t) * lda + ch);
+  }
 }
 
-// MFMA operand: 8 tokens (kk * 16 + 8 (lane / 32) + 0..7) of channel ch0 + lane % 32.
-__device__ __forceinline__ bf16x8 frag_tr(const uint4* __restrict__ panel, int ch0, int kk) {
+// One full stage of one panel straight into LDS (8 DMA loads per lane).
+__device__ __forceinline__ void dma_stage(const uint16_t* __restrict__ stage_origin, const int32_t (&off)[8],
+                                          uint4* __restrict__ panel) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(stage_origin + off[i]), KQ_LDS(panel + wave * 512 + i * 64), 16, 0, 0);
+}
+
+// Byte offset (inside a panel) of this lane's first transposing read for the
+// operand block starting at channel ch0; kk adds 8192 bytes, the second read
+// of a pair (+4 tokens) adds 2048.
+__device__ __forceinline__ int32_t tr_offset(int ch0) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
   const int ch = ch0 + 16 * (g & 1) + 4 * (j & 3);
   const int cc = ch >> 3, half = (ch >> 2) & 1;
-  const int tb = kk * 16 + 8 * (g >> 1) + (j >> 2);
-  const char* base = reinterpret_cast<const char*>(panel) + half * 8;
-  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)KQ_LDS(base + slot(tb, cc) * 16));
-  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)KQ_LDS(base + slot(tb + 4, cc) * 16));
+  const int tb = 8 * (g >> 1) + (j >> 2);
+  return slot(tb, cc) * 16 + half * 8;
+}
+
+__device__ __forceinline__ bf16x8 frag_at(const char* p) {
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)KQ_LDS(p));
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)KQ_LDS(p + 2048));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 r = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// The 64 MFMAs of one stage (4 k-steps of 16 tokens) from panels pa, pb.
+__device__ __forceinline__ void mfma_stage(const char* pa, const char* pb, const int32_t (&oa)[4],
+                                           const int32_t (&ob)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int kk = 0; kk < kKT / 16; ++kk) {
+    bf16x8 fa[4], fb[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) fa[x] = frag_at(pa + oa[x] + kk * 8192);
+#pragma unroll
+    for (int y = 0; y < 4; ++y) fb[y] = frag_at(pb + ob[y] + kk * 8192);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+  }
 }
 
 // Lower-triangle tiles in blocks of 4 tile rows x 8 tile columns (row-major
@@ -144,25 +169,33 @@ __global__ void tile_order_kernel(int nt, int* __restrict__ order) {
 
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
     const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
-    int nsl, int per_xcd, int vec_ok, const int* __restrict__ order, float* __restrict__ part) {
+    int nsl, int gsz, int vec_ok, const int* __restrict__ order, float* __restrict__ part) {
   __shared__ uint4 lds[2][2][kPanelUnits];  // [stage buffer][panel I, panel J] (128 KB)
 
-  // XCD-aware renumbering: XCD x = blockIdx % 8 takes items [x * per_xcd, (x + 1) * per_xcd).
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= ntiles * nsl) return;
-  const int sl = item / ntiles;
-  const int tile = order[item - sl * ntiles];
+  // XCD x = blockIdx % 8 runs tile group x (gsz tiles of the blocked order) of each slice in turn.
+  const int local = blockIdx.x / kXcds;
+  const int sl = local / gsz;
+  const int rank = (blockIdx.x % kXcds) * gsz + local % gsz;
+  if (sl >= nsl || rank >= ntiles) return;
+  const int tile = order[rank];
   int I, J;
   tri(tile, I, J);
   const bool diag = (I == J);
   const int64_t cI = int64_t(I) * kT, cJ = int64_t(J) * kT;
   const int64_t tok_begin = int64_t(slice0 + sl) * kSlice;
   const int64_t tok_end = tok_begin + kSlice < rows ? tok_begin + kSlice : rows;
-  const int nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wi = wave >> 1, wj = wave & 1;
+  int32_t oa[4], ob[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    oa[x] = tr_offset(wi * 128 + x * 32);
+    ob[x] = tr_offset(wj * 128 + x * 32) + (diag ? 0 : kPanelUnits * 16);
+  }
+  const char* buf0 = reinterpret_cast<const char*>(lds[0][0]);
+  const char* buf1 = reinterpret_cast<const char*>(lds[1][0]);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -170,33 +203,32 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
 
-  load_stage(a, lda, d, cI, tok_begin, tok_end, vec_ok, lds[0][0]);
-  if (!diag) load_stage(a, lda, d, cJ, tok_begin, tok_end, vec_ok, lds[0][1]);
+  // Stage s lives in buffer s % 2. Full stages of aligned rows are copied by
+  // DMA (issued one stage ahead); a partial last stage, or every stage of
+  // misaligned rows, goes through registers with zero fill.
+  const int nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
+  int32_t da[8], db[8];
+  dma_offsets(lda, d, cI, da);
+  dma_offsets(lda, d, cJ, db);
+  const uint16_t* origin = a + tok_begin * lda;
+  const int64_t step = int64_t(kKT) * lda;
+  auto load = [&](int st, int buf) {
+    const int64_t t0 = tok_begin + int64_t(st) * kKT;
+    if (vec_ok && t0 + kKT <= tok_end) {
+      dma_stage(origin + st * step, da, lds[buf][0]);
+      if (!diag) dma_stage(origin + st * step, db, lds[buf][1]);
+    } else {
+      load_stage_regs(a, lda, d, cI, t0, tok_end, vec_ok, lds[buf][0]);
+      if (!diag) load_stage_regs(a, lda, d, cJ, t0, tok_end, vec_ok, lds[buf][1]);
+    }
+  };
+  load(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
   for (int s = 0; s < nstage; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nstage) {
-      const int64_t t0 = tok_begin + int64_t(s + 1) * kKT;
-      load_stage(a, lda, d, cI, t0, tok_end, vec_ok, lds[cur ^ 1][0]);
-      if (!diag) load_stage(a, lda, d, cJ, t0, tok_end, vec_ok, lds[cur ^ 1][1]);
-    }
-    const uint4* pa = lds[cur][0];
-    const uint4* pb = diag ? lds[cur][0] : lds[cur][1];
-#pragma unroll
-    for (int kk = 0; kk < kKT / 16; ++kk) {
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) fa[x] = frag_tr(pa, wi * 128 + x * 32, kk);
-#pragma unroll
-      for (int y = 0; y < 4; ++y) fb[y] = frag_tr(pb, wj * 128 + y * 32, kk);
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-    }
+    if (s + 1 < nstage) load(s + 1, (s + 1) & 1);
+    const char* cur = (s & 1) ? buf1 : buf0;
+    mfma_stage(cur, cur, oa, ob, acc);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -216,7 +248,9 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
 }
 
 // Sums the float32 partials of a tile in float64; at the last slice group
-// writes H = alpha * S + beta * H to both triangles (64 x 64 sub-blocks).
+// writes H = alpha * S + beta * H to both triangles. One workgroup per 64 x 64
+// sub-block; a thread owns 4 columns x 4 rows (16-byte loads), slices summed
+// four at a time.
 __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ part, int nsl, int ntiles,
                                                    int64_t d, double* __restrict__ acc, int first,
                                                    int last, float alpha, float beta,
@@ -229,19 +263,53 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
   const bool dsub = (I == J) && (si == sj);  // sub-block on the diagonal of H
   if (I == J && sj > si) return;              // mirror of another sub-block
   const int64_t r0 = int64_t(I) * kT + si * 64, c0 = int64_t(J) * kT + sj * 64;
-  const int jl = threadIdx.x & 63;
-  const int ib = (threadIdx.x >> 6) * 16;
-#pragma unroll 4
-  for (int k = 0; k < 16; ++k) {
-    const int il = ib + k;
-    const int64_t e = int64_t(si * 64 + il) * kT + sj * 64 + jl;
-    double s = first ? 0.0 : acc[int64_t(tile) * kT * kT + e];
-    for (int q = 0; q < nsl; ++q) s += static_cast<double>(part[(int64_t(q) * ntiles + tile) * kT * kT + e]);
+  const int cq = (threadIdx.x & 15) * 4;      // first of this thread's 4 columns
+  const int rb = threadIdx.x >> 4;            // rows rb, rb + 16, rb + 32, rb + 48
+  const int64_t tile_off = int64_t(tile) * kT * kT;
+  const int64_t slice_stride = int64_t(ntiles) * kT * kT;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int il = rb + 16 * k;
+    const int64_t e = int64_t(si * 64 + il) * kT + sj * 64 + cq;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    if (!first) {
+      s0 = acc[tile_off + e];
+      s1 = acc[tile_off + e + 1];
+      s2 = acc[tile_off + e + 2];
+      s3 = acc[tile_off + e + 3];
+    }
+    const float* pp = part + tile_off + e;
+    int q = 0;
+    for (; q + 4 <= nsl; q += 4) {
+      const float4 v0 = *reinterpret_cast<const float4*>(pp + (q + 0) * slice_stride);
+      const float4 v1 = *reinterpret_cast<const float4*>(pp + (q + 1) * slice_stride);
+      const float4 v2 = *reinterpret_cast<const float4*>(pp + (q + 2) * slice_stride);
+      const float4 v3 = *reinterpret_cast<const float4*>(pp + (q + 3) * slice_stride);
+      s0 += (double(v0.x) + double(v1.x)) + (double(v2.x) + double(v3.x));
+      s1 += (double(v0.y) + double(v1.y)) + (double(v2.y) + double(v3.y));
+      s2 += (double(v0.z) + double(v1.z)) + (double(v2.z) + double(v3.z));
+      s3 += (double(v0.w) + double(v1.w)) + (double(v2.w) + double(v3.w));
+    }
+    for (; q < nsl; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(pp + q * slice_stride);
+      s0 += v.x;
+      s1 += v.y;
+      s2 += v.z;
+      s3 += v.w;
+    }
     if (!last) {
-      acc[int64_t(tile) * kT * kT + e] = s;
-    } else {
+      acc[tile_off + e] = s0;
+      acc[tile_off + e + 1] = s1;
+      acc[tile_off + e + 2] = s2;
+      acc[tile_off + e + 3] = s3;
+      continue;
+    }
+    const double sv[4] = {s0, s1, s2, s3};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int jl = cq + c;
       const int64_t gi = r0 + il, gj = c0 + jl;
-      double v = static_cast<double>(alpha) * s;
+      double v = static_cast<double>(alpha) * sv[c];
       if (beta != 0.0f && gi < d && gj < d && (!dsub || il >= jl))
         v += static_cast<double>(beta) * static_cast<double>(h[gi * d + gj]);
       tr[il][jl] = static_cast<float>(v);
@@ -249,6 +317,8 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
   }
   if (!last) return;
   __syncthreads();
+  const int jl = threadIdx.x & 63;
+  const int ib = (threadIdx.x >> 6) * 16;
   // lower-triangle position (row-major, coalesced along j)
 #pragma unroll 4
   for (int k = 0; k < 16; ++k) {
@@ -259,8 +329,8 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
   // mirrored position: H[c0 + a][r0 + b] = S[b][a]
 #pragma unroll 4
   for (int k = 0; k < 16; ++k) {
-    const int al = ib + k;  // row offset in the mirror block (from the column side)
-    const int bl = jl;      // column offset (from the row side)
+    const int al = ib + k;
+    const int bl = jl;
     const int64_t gi = c0 + al, gj = r0 + bl;
     if (gi < d && gj < d && (!dsub || bl > al)) h[gi * d + gj] = tr[bl][al];
   }
@@ -326,12 +396,12 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   for (int g = 0; g < p.ngroups; ++g) {
     const int s0 = g * p.group;
     const int nsl = (s0 + p.group <= p.nslices) ? p.group : p.nslices - s0;
-    const int items = p.ntiles * nsl;
-    const int per_xcd = (items + kXcds - 1) / kXcds;
+    const int gsz = (p.ntiles + kXcds - 1) / kXcds;  // tiles per XCD group
+    const int per_xcd = gsz * nsl;
     {
       LaunchTimer timer("syrk_partial", st);
       hipLaunchKernelGGL(syrk_partial, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a,
-                         lda, d, rows, p.ntiles, s0, nsl, per_xcd, vec_ok, order, part);
+                         lda, d, rows, p.ntiles, s0, nsl, gsz, vec_ok, order, part);
     }
     kq_status s = check_launch("syrk_partial");
     if (s != KQ_OK) return s;

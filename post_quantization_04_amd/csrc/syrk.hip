@@ -2,7 +2,7 @@
 //
 // A is [rows, d]: tokens by channels, channels contiguous. The contraction
 // runs over tokens, so each MFMA operand needs consecutive tokens of one
-// channel per lane. Panels of 64 tokens x 256 channels are copied straight
+// channel per lane. Panels of 32 tokens x 256 channels are copied straight
 // from global memory into LDS in their natural token-major layout
 // (global_load_lds_dwordx4, no register staging), and the MFMA fragments are
 // read with the gfx950 transposing LDS load ds_read_b64_tr_b16: in each group
@@ -12,12 +12,26 @@
 // token row are XOR-swizzled with the token index so that both the DMA writes
 // and the transposing reads run at the LDS bank minimum.
 //
-// LDS holds two stages (2 x 2 panels x 32 KB); the loads of stage s + 1 are in
-// flight while the MFMAs of stage s run, with one barrier per stage. A final
-// partial stage (fewer than 64 tokens) or a misaligned row pitch takes a
-// register path that zero-fills missing tokens.
+// Pipeline: five 32 KB stage buffers (both panels of 32 tokens; a diagonal
+// tile loads its one panel twice) form a ring that fills all 160 KB of LDS.
+// Loads run four stages ahead, so up to 128 KB per CU are in flight while the
+// MFMAs consume the current stage. Each buffer
+// is its own __shared__ object and the ring is unrolled, so the compiler can
+// tell the buffer being read from the ones being filled and does not drain
+// the DMA queue before each LDS read. Before the one barrier per stage, each
+// wave waits (vmcnt) only for its own loads of the next stage. Fragments are
+// double buffered in registers: the reads of the next k-step are interleaved
+// with the MFMAs of the current one, and the first reads of the next stage
+// are issued right after the barrier, in the middle of the last k-step.
 //
-// Work item = (lower-triangle 256 x 256 output tile, token slice of 8192
+// A final partial stage is loaded from the last 32 tokens of the slice and
+// the rows already counted by the previous stage are zeroed in LDS; the stage
+// count is padded to whole rings with zeroed stages (a full slice is exactly
+// 51 rings). Rows that
+// are not 16-byte aligned, or fewer than 32 rows in all, take a plain
+// register-staged kernel.
+//
+// Work item = (lower-triangle 256 x 256 output tile, token slice of 8160
 // rows). Each workgroup sums one slice in float32 MFMA accumulators (bf16
 // products are exact) and writes the float32 partial tile. A second kernel
 // adds the slices of a tile in float64, applies alpha and beta, rounds once to
@@ -27,7 +41,7 @@
 // Workgroups are dispatched round robin over the 8 XCDs. The tiles of a slice
 // are listed in a blocked order (4 tile rows x 8 tile columns) and cut into 8
 // contiguous groups; XCD x runs group x of slice 0, then of slice 1, ... So
-// all XCDs walk the token slices together (one or two 8192-token slices are
+// all XCDs walk the token slices together (one or two 8160-token slices are
 // live at a time, which the Infinity Cache holds) and each XCD's L2 serves
 // the dozen channel panels of its tile group.
 #include "kq_internal.h"
@@ -36,19 +50,38 @@ namespace kq {
 namespace {
 
 constexpr int kT = 256;          // output tile edge (channels)
-constexpr int kKT = 64;          // tokens per LDS stage
-constexpr int kSlice = 8192;     // tokens per float32 partial sum
+constexpr int kKT = 32;          // tokens per LDS stage
+constexpr int kNB = 5;           // stage buffers in the ring
+constexpr int kSlice = 8160;     // tokens per float32 partial sum (255 stages = 51 rings)
 constexpr int kThreads = 256;    // 4 waves in a 2 x 2 grid, 128 x 128 outputs each
-constexpr int kPanelUnits = kT * kKT * 2 / 16;  // 16-byte units per LDS panel (2048)
+constexpr int kPanelUnits = kT * kKT * 2 / 16;  // 16-byte units per LDS panel (1024)
+constexpr int kPanelBytes = kPanelUnits * 16;
+constexpr int kUnitsPerLane = kPanelUnits / kThreads;  // DMA loads per lane per panel (4)
 constexpr int kTargetItems = 8192;  // work items per launch before slices are split into groups
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 #define KQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define KQ_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
+
+// The ring: one __shared__ object per stage buffer, panel I then panel J.
+__shared__ uint4 ring0[2 * kPanelUnits];
+__shared__ uint4 ring1[2 * kPanelUnits];
+__shared__ uint4 ring2[2 * kPanelUnits];
+__shared__ uint4 ring3[2 * kPanelUnits];
+__shared__ uint4 ring4[2 * kPanelUnits];
+
+template <int K>
+__device__ __forceinline__ uint4* ring() {
+  static_assert(K >= 0 && K < kNB, "ring index");
+  if constexpr (K == 0) return ring0;
+  else if constexpr (K == 1) return ring1;
+  else if constexpr (K == 2) return ring2;
+  else if constexpr (K == 3) return ring3;
+  else return ring4;
+}
 
 // 16-byte slot of (token t, channel chunk cc) in a panel stage: 32 chunks per
 // token row, chunk position XOR 4 * (t mod 4) inside each half row.
@@ -63,64 +96,9 @@ __device__ __forceinline__ void tri(int t, int& I, int& J) {
   J = t - i * (i + 1) / 2;
 }
 
-// Register path for any stage: zero fill for tokens >= tok_end and channels >= d.
-__device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
-                                                int64_t t0, int64_t tok_end, bool vec_ok, uint4* __restrict__ panel) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int sl = i * 256 + static_cast<int>(threadIdx.x);
-    const int t = sl >> 5, cs = sl & 31;
-    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
-    const int64_t ch = c0 + int64_t(cc) * 8;
-    const int64_t tok = t0 + t;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (tok < tok_end && ch < d) {
-      const uint16_t* p = a + tok * lda + ch;
-      if (vec_ok && ch + 8 <= d) {
-        val = *reinterpret_cast<const uint4*>(p);
-      } else {
-        uint16_t e[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) e[k] = (ch + k < d) ? p[k] : uint16_t(0);
-        val.x = e[0] | (uint32_t(e[1]) << 16);
-        val.y = e[2] | (uint32_t(e[3]) << 16);
-        val.z = e[4] | (uint32_t(e[5]) << 16);
-        val.w = e[6] | (uint32_t(e[7]) << 16);
-      }
-    }
-    panel[sl] = val;
-  }
-}
-
-// Per-lane element offsets (from the stage origin a + t0 * lda) of the 8
-// chunks this lane copies into a panel: load i of wave w fills slot
-// w * 512 + i * 64 + lane, whose chunk is the un-swizzled position. Chunks past
-// channel d re-read the row's last 8 channels (their outputs are discarded).
-__device__ __forceinline__ void dma_offsets(int64_t lda, int64_t d, int64_t c0, int32_t (&off)[8]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int sl = wave * 512 + i * 64 + lane;
-    const int t = sl >> 5, cs = sl & 31;
-    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
-    int64_t ch = c0 + int64_t(cc) * 8;
-    if (ch > d - 8) ch = d - 8;
-    off[i] = static_cast<int32_t>(int64_t(t) * lda + ch);
-  }
-}
-
-// One full stage of one panel straight into LDS (8 DMA loads per lane).
-__device__ __forceinline__ void dma_stage(const uint16_t* __restrict__ stage_origin, const int32_t (&off)[8],
-                                          uint4* __restrict__ panel) {
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(stage_origin + off[i]), KQ_LDS(panel + wave * 512 + i * 64), 16, 0, 0);
-}
-
 // Byte offset (inside a panel) of this lane's first transposing read for the
-// operand block starting at channel ch0; kk adds 8192 bytes, the second read
-// of a pair (+4 tokens) adds 2048.
+// operand block starting at channel ch0; k-step kk adds 8192 bytes, the second
+// read of a pair (+4 tokens) adds 2048.
 __device__ __forceinline__ int32_t tr_offset(int ch0) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
@@ -138,22 +116,168 @@ __device__ __forceinline__ bf16x8 frag_at(const char* p) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// The 64 MFMAs of one stage (4 k-steps of 16 tokens) from panels pa, pb.
-__device__ __forceinline__ void mfma_stage(const char* pa, const char* pb, const int32_t (&oa)[4],
-                                           const int32_t (&ob)[4], f32x16 (&acc)[4][4]) {
+// Operand fragments of one 16-token k-step: 4 row blocks of the wave's I
+// range, 4 column blocks of its J range.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(const char* buf, int kk, const int32_t (&oa)[4], const int32_t (&ob)[4],
+                                           Frags& f) {
 #pragma unroll
-  for (int kk = 0; kk < kKT / 16; ++kk) {
-    bf16x8 fa[4], fb[4];
+  for (int x = 0; x < 4; ++x) f.a[x] = frag_at(buf + oa[x] + kk * 8192);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) fa[x] = frag_at(pa + oa[x] + kk * 8192);
+  for (int y = 0; y < 4; ++y) f.b[y] = frag_at(buf + ob[y] + kk * 8192);
+}
+
+// MFMAs of row blocks x0 .. x1 - 1 against all 4 column blocks.
+__device__ __forceinline__ void mfma_rows(const Frags& f, int x0, int x1, f32x16 (&acc)[4][4]) {
 #pragma unroll
-    for (int y = 0; y < 4; ++y) fb[y] = frag_at(pb + ob[y] + kk * 8192);
+  for (int x = x0; x < x1; ++x)
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int y = 0; y < 4; ++y)
+      acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
+}
+
+// Per-lane byte offsets (from a stage origin a + t0 * lda) of the chunks this
+// lane copies into a panel: load i of wave w fills slot w * 256 + i * 64 +
+// lane, whose chunk is the un-swizzled position. Chunks past channel d re-read
+// the row's last 8 channels (their outputs are discarded).
+__device__ __forceinline__ void dma_offsets(int64_t lda, int64_t d, int64_t c0, uint32_t (&off)[kUnitsPerLane]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-      for (int y = 0; y < 4; ++y)
-        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+  for (int i = 0; i < kUnitsPerLane; ++i) {
+    const int sl = wave * (kUnitsPerLane * 64) + i * 64 + lane;
+    const int t = sl >> 5, cs = sl & 31;
+    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
+    int64_t ch = c0 + int64_t(cc) * 8;
+    if (ch > d - 8) ch = d - 8;
+    off[i] = static_cast<uint32_t>((int64_t(t) * lda + ch) * 2);
   }
+}
+
+// Issues the DMA copies of one stage (both panels) into ring buffer K.
+template <int K>
+__device__ __forceinline__ void dma_stage(const char* origin, const uint32_t (&da)[kUnitsPerLane],
+                                          const uint32_t (&db)[kUnitsPerLane], int wave) {
+  uint4* dst = ring<K>() + wave * (kUnitsPerLane * 64);
+#pragma unroll
+  for (int i = 0; i < kUnitsPerLane; ++i)
+    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(origin + da[i]), KQ_LDS(dst + i * 64), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kUnitsPerLane; ++i)
+    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(origin + db[i]), KQ_LDS(dst + kPanelUnits + i * 64), 16, 0, 0);
+}
+
+// Workgroup barrier without the full memory drain of __syncthreads (which
+// would also wait for the loads of the stages still in flight).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Uniform per-workgroup state of the ring kernel.
+struct Ring {
+  const char* a;        // A as bytes
+  int64_t lda2;         // row pitch in bytes
+  int64_t tok_begin, tok_end;
+  int nstage;
+  int wave;
+  uint32_t da[kUnitsPerLane], db[kUnitsPerLane];
+  int32_t oa[4], ob[4];
+
+  // First token copied for stage q: a partial last stage is shifted back to
+  // end at tok_end, and stages past the end (which pad the count to whole
+  // rings and keep the number of copies in flight constant) repeat the last
+  // stage and are zeroed once landed.
+  __device__ __forceinline__ int64_t origin_token(int q) const {
+    const int qq = q < nstage ? q : nstage - 1;
+    const int64_t t0 = tok_begin + int64_t(qq) * kKT;
+    return t0 + kKT <= tok_end ? t0 : tok_end - kKT;
+  }
+  template <int K>
+  __device__ __forceinline__ void issue(int q) const {
+    dma_stage<K>(a + origin_token(q) * lda2, da, db, wave);
+  }
+  // Makes stage q (in ring buffer K) visible to all waves, with the copies of
+  // the three following stages still in flight. The rows of a partial stage
+  // that precede its first token, and all rows of a stage past the end, are
+  // zeroed by the lanes that copied them.
+  template <int K>
+  __device__ __forceinline__ void land(int q) const {
+    // s_waitcnt vmcnt(3 stages x 8 copies) lgkmcnt(0): fields vmcnt[3:0],
+    // expcnt[6:4] (7 = no wait), lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt(0x4078);
+    const int dup = q < nstage ? static_cast<int>(tok_begin + int64_t(q) * kKT - origin_token(q)) : kKT;
+    const int lane = threadIdx.x & 63;
+    uint4* dst = ring<K>() + wave * (kUnitsPerLane * 64);
+#pragma unroll
+    for (int i = 0; i < kUnitsPerLane; ++i) {
+      if (((wave * (kUnitsPerLane * 64) + i * 64 + lane) >> 5) < dup) {
+        dst[i * 64 + lane] = make_uint4(0, 0, 0, 0);
+        dst[kPanelUnits + i * 64 + lane] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+    barrier();
+  }
+};
+
+// One stage of the ring kernel: stage s in buffer K, its first k-step's
+// fragments already in f0. Straight-line code: the refill, the barrier and
+// the next stage's first reads run even past the last stage (on zeroed
+// copies), so that the MFMA sequence has no branches.
+template <int K>
+__device__ __forceinline__ void ring_step(const Ring& r, int s, Frags& f0, Frags& f1, f32x16 (&acc)[4][4]) {
+  constexpr int KN = (K + 1) % kNB;
+  read_frags(reinterpret_cast<const char*>(ring<K>()), 1, r.oa, r.ob, f1);
+  mfma_rows(f0, 0, 4, acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  mfma_rows(f1, 0, 2, acc);
+  // keep the wait and barrier after all MFMAs that precede them
+  __builtin_amdgcn_sched_barrier(0);
+  r.land<KN>(s + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // every wave is past its reads of stage s: refill its buffer with stage s + 5
+  r.issue<K>(s + kNB);
+  read_frags(reinterpret_cast<const char*>(ring<KN>()), 0, r.oa, r.ob, f0);
+  mfma_rows(f1, 2, 4, acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+}
+
+// Writes a wave's 128 x 128 float32 accumulators into the partial tile.
+// D[i][j] of a 32 x 32 block: lane l, register r -> i = 8 (r / 4) + 4 (l / 32) + r % 4, j = l % 32.
+__device__ __forceinline__ void store_acc(const f32x16 (&acc)[4][4], float* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = wi * 128 + x * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int j = wj * 128 + y * 32 + (lane & 31);
+        out[i * kT + j] = acc[x][y][r];
+      }
+}
+
+// Work item of blockIdx.x: XCD x = blockIdx % 8 runs tile group x (gsz tiles
+// of the blocked order) of each slice in turn. Returns false past the end.
+__device__ __forceinline__ bool work_item(int ntiles, int nsl, int gsz, const int* __restrict__ order, int& sl,
+                                          int& tile) {
+  const int local = blockIdx.x / kXcds;
+  sl = local / gsz;
+  const int rank = (blockIdx.x % kXcds) * gsz + local % gsz;
+  if (sl >= nsl || rank >= ntiles) return false;
+  tile = order[rank];
+  return true;
 }
 
 // Lower-triangle tiles in blocks of 4 tile rows x 8 tile columns (row-major
@@ -167,35 +291,30 @@ __global__ void tile_order_kernel(int nt, int* __restrict__ order) {
         for (int j = bj; j < bj + 8 && j <= i; ++j) order[r++] = i * (i + 1) / 2 + j;
 }
 
+// Ring kernel: needs 16-byte aligned rows (lda, d multiples of 8, A aligned)
+// and rows >= 32.
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
     const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
-    int nsl, int gsz, int vec_ok, const int* __restrict__ order, float* __restrict__ part) {
-  __shared__ uint4 lds[2][2][kPanelUnits];  // [stage buffer][panel I, panel J] (128 KB)
-
-  // XCD x = blockIdx % 8 runs tile group x (gsz tiles of the blocked order) of each slice in turn.
-  const int local = blockIdx.x / kXcds;
-  const int sl = local / gsz;
-  const int rank = (blockIdx.x % kXcds) * gsz + local % gsz;
-  if (sl >= nsl || rank >= ntiles) return;
-  const int tile = order[rank];
+    int nsl, int gsz, const int* __restrict__ order, float* __restrict__ part) {
+  int sl, tile;
+  if (!work_item(ntiles, nsl, gsz, order, sl, tile)) return;
   int I, J;
   tri(tile, I, J);
-  const bool diag = (I == J);
-  const int64_t cI = int64_t(I) * kT, cJ = int64_t(J) * kT;
-  const int64_t tok_begin = int64_t(slice0 + sl) * kSlice;
-  const int64_t tok_end = tok_begin + kSlice < rows ? tok_begin + kSlice : rows;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wi = wave >> 1, wj = wave & 1;
-  int32_t oa[4], ob[4];
+  Ring r;
+  r.a = reinterpret_cast<const char*>(a);
+  r.lda2 = lda * 2;
+  r.tok_begin = int64_t(slice0 + sl) * kSlice;
+  r.tok_end = r.tok_begin + kSlice < rows ? r.tok_begin + kSlice : rows;
+  r.nstage = static_cast<int>((r.tok_end - r.tok_begin + kKT - 1) / kKT);
+  r.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wi = r.wave >> 1, wj = r.wave & 1;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    oa[x] = tr_offset(wi * 128 + x * 32);
-    ob[x] = tr_offset(wj * 128 + x * 32) + (diag ? 0 : kPanelUnits * 16);
+    r.oa[x] = tr_offset(wi * 128 + x * 32);
+    r.ob[x] = tr_offset(wj * 128 + x * 32) + kPanelBytes;
   }
-  const char* buf0 = reinterpret_cast<const char*>(lds[0][0]);
-  const char* buf1 = reinterpret_cast<const char*>(lds[1][0]);
+  dma_offsets(lda, d, int64_t(I) * kT, r.da);
+  dma_offsets(lda, d, int64_t(J) * kT, r.db);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -203,48 +322,88 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
 
-  // Stage s lives in buffer s % 2. Full stages of aligned rows are copied by
-  // DMA (issued one stage ahead); a partial last stage, or every stage of
-  // misaligned rows, goes through registers with zero fill.
-  const int nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
-  int32_t da[8], db[8];
-  dma_offsets(lda, d, cI, da);
-  dma_offsets(lda, d, cJ, db);
-  const uint16_t* origin = a + tok_begin * lda;
-  const int64_t step = int64_t(kKT) * lda;
-  auto load = [&](int st, int buf) {
-    const int64_t t0 = tok_begin + int64_t(st) * kKT;
-    if (vec_ok && t0 + kKT <= tok_end) {
-      dma_stage(origin + st * step, da, lds[buf][0]);
-      if (!diag) dma_stage(origin + st * step, db, lds[buf][1]);
-    } else {
-      load_stage_regs(a, lda, d, cI, t0, tok_end, vec_ok, lds[buf][0]);
-      if (!diag) load_stage_regs(a, lda, d, cJ, t0, tok_end, vec_ok, lds[buf][1]);
-    }
-  };
-  load(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
-    if (s + 1 < nstage) load(s + 1, (s + 1) & 1);
-    const char* cur = (s & 1) ? buf1 : buf0;
-    mfma_stage(cur, cur, oa, ob, acc);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  // prologue: stages 0 .. 4 issued, stage 0 landed, its first fragments read
+  r.issue<0>(0);
+  r.issue<1>(1);
+  r.issue<2>(2);
+  r.issue<3>(3);
+  r.land<0>(0);
+  r.issue<4>(4);
+  Frags f0, f1;
+  read_frags(reinterpret_cast<const char*>(ring<0>()), 0, r.oa, r.ob, f0);
 
-  // D[i][j] of a 32 x 32 block: lane l, register r -> i = 8 (r / 4) + 4 (l / 32) + r % 4, j = l % 32.
-  float* out = part + (int64_t(sl) * ntiles + tile) * (kT * kT);
+  // whole rings only: stages past nstage are zero and add nothing
+  for (int s = 0; s < r.nstage; s += kNB) {
+    ring_step<0>(r, s, f0, f1, acc);
+    ring_step<1>(r, s + 1, f0, f1, acc);
+    ring_step<2>(r, s + 2, f0, f1, acc);
+    ring_step<3>(r, s + 3, f0, f1, acc);
+    ring_step<4>(r, s + 4, f0, f1, acc);
+  }
+  // no copy may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+  store_acc(acc, part + (int64_t(sl) * ntiles + tile) * (kT * kT));
+}
+
+// Register-staged copy of one panel stage with zero fill for tokens >=
+// tok_end and channels >= d (any alignment).
+__device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t c0,
+                                                int64_t t0, int64_t tok_end, uint4* __restrict__ panel) {
+#pragma unroll
+  for (int i = 0; i < kUnitsPerLane; ++i) {
+    const int sl = i * kThreads + static_cast<int>(threadIdx.x);
+    const int t = sl >> 5, cs = sl & 31;
+    const int cc = (cs & 16) | ((cs & 15) ^ ((t & 3) << 2));
+    const int64_t ch = c0 + int64_t(cc) * 8;
+    const int64_t tok = t0 + t;
+    uint32_t e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = (tok < tok_end && ch + k < d) ? a[tok * lda + ch + k] : 0u;
+    panel[sl] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+  }
+}
+
+// Fallback for unaligned rows or fewer than 32 rows: two register-staged
+// buffers, one full barrier per stage.
+__global__ __launch_bounds__(kThreads, 1) void syrk_partial_regs(
+    const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
+    int nsl, int gsz, const int* __restrict__ order, float* __restrict__ part) {
+  __shared__ uint4 lds[2][2 * kPanelUnits];
+  int sl, tile;
+  if (!work_item(ntiles, nsl, gsz, order, sl, tile)) return;
+  int I, J;
+  tri(tile, I, J);
+  const bool two = (I != J);
+  const int64_t tok_begin = int64_t(slice0 + sl) * kSlice;
+  const int64_t tok_end = tok_begin + kSlice < rows ? tok_begin + kSlice : rows;
+  const int nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
+  const int wave = threadIdx.x >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  int32_t oa[4], ob[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    oa[x] = tr_offset(wi * 128 + x * 32);
+    ob[x] = tr_offset(wj * 128 + x * 32) + (two ? kPanelBytes : 0);
+  }
+  f32x16 acc[4][4];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y)
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
+  for (int s = 0; s < nstage; ++s) {
+    uint4* buf = lds[s & 1];
+    const int64_t t0 = tok_begin + int64_t(s) * kKT;
+    load_stage_regs(a, lda, d, int64_t(I) * kT, t0, tok_end, buf);
+    if (two) load_stage_regs(a, lda, d, int64_t(J) * kT, t0, tok_end, buf + kPanelUnits);
+    __syncthreads();
+    Frags f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = wi * 128 + x * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int j = wj * 128 + y * 32 + (lane & 31);
-        out[i * kT + j] = acc[x][y][r];
-      }
+    for (int kk = 0; kk < kKT / 16; ++kk) {
+      read_frags(reinterpret_cast<const char*>(buf), kk, oa, ob, f);
+      mfma_rows(f, 0, 4, acc);
+    }
+  }
+  store_acc(acc, part + (int64_t(sl) * ntiles + tile) * (kT * kT));
 }
 
 // Sums the float32 partials of a tile in float64; at the last slice group
@@ -385,8 +544,11 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   float* part = static_cast<float*>(ws);
   double* acc = reinterpret_cast<double*>(static_cast<char*>(ws) + p.part_bytes);
   int* order = reinterpret_cast<int*>(static_cast<char*>(ws) + p.part_bytes + p.acc_bytes);
-  // 16-byte loads need aligned rows; the DMA path also needs whole 8-channel chunks
-  const int vec_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0);
+  // The DMA ring copies whole 16-byte chunks of aligned rows, addresses a
+  // stage with 32-bit byte offsets, and shifts a partial last stage back
+  // inside A (needs 32 rows).
+  const bool ring_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
+                       rows >= kKT && int64_t(kKT) * lda * 2 < (int64_t(1) << 31);
   {
     LaunchTimer timer("tile_order_kernel", st);
     hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(64), 0, st, p.nt, order);
@@ -398,12 +560,13 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
     const int nsl = (s0 + p.group <= p.nslices) ? p.group : p.nslices - s0;
     const int gsz = (p.ntiles + kXcds - 1) / kXcds;  // tiles per XCD group
     const int per_xcd = gsz * nsl;
+    const char* kname = ring_ok ? "syrk_partial" : "syrk_partial_regs";
     {
-      LaunchTimer timer("syrk_partial", st);
-      hipLaunchKernelGGL(syrk_partial, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a,
-                         lda, d, rows, p.ntiles, s0, nsl, gsz, vec_ok, order, part);
+      LaunchTimer timer(kname, st);
+      hipLaunchKernelGGL(ring_ok ? syrk_partial : syrk_partial_regs, dim3(static_cast<unsigned>(per_xcd * kXcds)),
+                         dim3(kThreads), 0, st, a, lda, d, rows, p.ntiles, s0, nsl, gsz, order, part);
     }
-    kq_status s = check_launch("syrk_partial");
+    kq_status s = check_launch(kname);
     if (s != KQ_OK) return s;
     {
       LaunchTimer timer("syrk_reduce", st);

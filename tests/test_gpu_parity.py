@@ -35,7 +35,8 @@ def _workload(cfg_id, n_tokens, dims, **kw):
 # ---------------------------------------------------------------------------
 # step 1: covariance
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("n_tokens,d", [(512, 128), (20000, 384), (3001, 100), (9000, 520), (1, 8), (8192, 256)])
+@pytest.mark.parametrize("n_tokens,d", [(512, 128), (20000, 384), (3001, 100), (9000, 520), (1, 8), (8192, 256),
+                                        (8170, 136), (40, 64), (31, 64)])
 def test_covariance(n_tokens, d):
     import torch
     kq, pipeline = _kq()
@@ -78,16 +79,18 @@ def test_covariance_chunks_alpha_beta_and_empty():
     np.testing.assert_array_equal(host(hd), 2.0 * prior)
 
 
-def test_covariance_strided_rows():
-    # lda > d (a column slice of a wider activation matrix) takes the element path
+@pytest.mark.parametrize("width,c0", [(300, 20), (320, 16)])
+def test_covariance_strided_rows(width, c0):
+    # lda > d (a column slice of a wider activation matrix): an unaligned pitch
+    # takes the register-staged kernel, an aligned one the DMA ring
     kq, pipeline = _kq()
-    wl = _workload(2, 4000, {"q_proj": (64, 300)})
+    wl = _workload(2, 4000, {"q_proj": (64, width)})
     x = wl.x("attn_in")
-    xd = bits_to_dev(x)[:, 20:276]
+    xd = bits_to_dev(x)[:, c0:c0 + 256]
     import torch
     h = torch.empty((256, 256), dtype=torch.float32, device=DEV)
     kq.accumulate_cov(xd, h, 1.0 / 4000, 0.0)
-    assert rel_fro(host(h), oracle.covariance([x[:, 20:276]])) <= 2e-6
+    assert rel_fro(host(h), oracle.covariance([x[:, c0:c0 + 256]])) <= 2e-6
 
 
 # ---------------------------------------------------------------------------

@@ -12,38 +12,40 @@
 // token row are XOR-swizzled with the token index so that both the DMA writes
 // and the transposing reads run at the LDS bank minimum.
 //
-// Pipeline: five 32 KB stage buffers (both panels of 32 tokens; a diagonal
-// tile loads its one panel twice) form a ring that fills all 160 KB of LDS.
-// Loads run four stages ahead, so up to 128 KB per CU are in flight while the
-// MFMAs consume the current stage. Each buffer
-// is its own __shared__ object and the ring is unrolled, so the compiler can
-// tell the buffer being read from the ones being filled and does not drain
-// the DMA queue before each LDS read. Before the one barrier per stage, each
-// wave waits (vmcnt) only for its own loads of the next stage. Fragments are
-// double buffered in registers: the reads of the next k-step are interleaved
-// with the MFMAs of the current one, and the first reads of the next stage
-// are issued right after the barrier, in the middle of the last k-step.
+// Pipeline: four 32 KB stage buffers (both panels of 32 tokens; a diagonal
+// tile loads its one panel twice) form a ring in LDS. Loads run three stages
+// ahead (two stages in flight when a stage is awaited; a deeper ring measured
+// no faster). Each buffer is its own __shared__ object and the ring is
+// unrolled, so the compiler can tell the buffer being read from the ones
+// being filled and does not drain the DMA queue before each LDS read. Before
+// the one barrier per stage, each wave waits (vmcnt) only for its own loads
+// of the next stage. Fragments are double buffered in registers: the reads of
+// the next k-step are interleaved with the MFMAs of the current one, and the
+// first reads of the next stage are issued right after the barrier, in the
+// middle of the last k-step, together with the refill of the buffer just
+// consumed.
 //
 // A final partial stage is loaded from the last 32 tokens of the slice and
 // the rows already counted by the previous stage are zeroed in LDS; the stage
-// count is padded to whole rings with zeroed stages (a full slice is exactly
-// 51 rings). Rows that
-// are not 16-byte aligned, or fewer than 32 rows in all, take a plain
-// register-staged kernel.
+// count is padded to whole rings with zeroed stages (a full 8192-token slice
+// is exactly 64 rings). Rows that are not 16-byte aligned, or fewer than 32
+// rows in all, take a plain register-staged kernel.
 //
-// Work item = (lower-triangle 256 x 256 output tile, token slice of 8160
+// Work item = (lower-triangle 256 x 256 output tile, token slice of 8192
 // rows). Each workgroup sums one slice in float32 MFMA accumulators (bf16
 // products are exact) and writes the float32 partial tile. A second kernel
 // adds the slices of a tile in float64, applies alpha and beta, rounds once to
 // float32 and writes both triangles. Short float32 runs keep the accumulated
 // rounding near 1e-7 relative, which the downstream column sweep needs.
 //
-// Workgroups are dispatched round robin over the 8 XCDs. The tiles of a slice
-// are listed in a blocked order (4 tile rows x 8 tile columns) and cut into 8
-// contiguous groups; XCD x runs group x of slice 0, then of slice 1, ... So
-// all XCDs walk the token slices together (one or two 8160-token slices are
-// live at a time, which the Infinity Cache holds) and each XCD's L2 serves
-// the dozen channel panels of its tile group.
+// Workgroups are dispatched round robin over the 8 XCDs. With at least 8
+// slices, XCD x runs every tile of slices x, x + 8, ..., tiles in a blocked
+// order (4 tile rows x 8 tile columns, so the 32 workgroups of an XCD share
+// about 12 channel panels) and each token slice streams through one L2 only.
+// With fewer slices, the blocked tile list is cut into 8 groups and XCD x
+// runs group x of every slice.
+#include <utility>
+
 #include "kq_internal.h"
 
 namespace kq {
@@ -51,8 +53,9 @@ namespace {
 
 constexpr int kT = 256;          // output tile edge (channels)
 constexpr int kKT = 32;          // tokens per LDS stage
-constexpr int kNB = 5;           // stage buffers in the ring
-constexpr int kSlice = 8160;     // tokens per float32 partial sum (255 stages = 51 rings)
+constexpr int kNB = 4;           // stage buffers in the ring (2..8)
+// tokens per float32 partial sum: whole rings, at most 8192 tokens
+constexpr int kSlice = 8192 / (kNB * kKT) * (kNB * kKT);
 constexpr int kThreads = 256;    // 4 waves in a 2 x 2 grid, 128 x 128 outputs each
 constexpr int kPanelUnits = kT * kKT * 2 / 16;  // 16-byte units per LDS panel (1024)
 constexpr int kPanelBytes = kPanelUnits * 16;
@@ -66,12 +69,17 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define KQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define KQ_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 
-// The ring: one __shared__ object per stage buffer, panel I then panel J.
-__shared__ uint4 ring0[2 * kPanelUnits];
-__shared__ uint4 ring1[2 * kPanelUnits];
-__shared__ uint4 ring2[2 * kPanelUnits];
-__shared__ uint4 ring3[2 * kPanelUnits];
-__shared__ uint4 ring4[2 * kPanelUnits];
+// The ring: one __shared__ object per stage buffer, panel I then panel J
+// (only the first kNB are referenced, and only those are allocated).
+[[maybe_unused]] __shared__ uint4 ring0[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring1[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring2[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring3[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring4[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring5[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring6[2 * kPanelUnits];
+[[maybe_unused]] __shared__ uint4 ring7[2 * kPanelUnits];
+static_assert(kNB >= 2 && kNB <= 8 && kNB * 2 * kPanelUnits * 16 <= 160 * 1024, "ring must fit in LDS");
 
 template <int K>
 __device__ __forceinline__ uint4* ring() {
@@ -80,7 +88,10 @@ __device__ __forceinline__ uint4* ring() {
   else if constexpr (K == 1) return ring1;
   else if constexpr (K == 2) return ring2;
   else if constexpr (K == 3) return ring3;
-  else return ring4;
+  else if constexpr (K == 4) return ring4;
+  else if constexpr (K == 5) return ring5;
+  else if constexpr (K == 6) return ring6;
+  else return ring7;
 }
 
 // 16-byte slot of (token t, channel chunk cc) in a panel stage: 32 chunks per
@@ -197,14 +208,16 @@ struct Ring {
     dma_stage<K>(a + origin_token(q) * lda2, da, db, wave);
   }
   // Makes stage q (in ring buffer K) visible to all waves, with the copies of
-  // the three following stages still in flight. The rows of a partial stage
+  // the kNB - 2 following stages still in flight. The rows of a partial stage
   // that precede its first token, and all rows of a stage past the end, are
   // zeroed by the lanes that copied them.
   template <int K>
   __device__ __forceinline__ void land(int q) const {
-    // s_waitcnt vmcnt(3 stages x 8 copies) lgkmcnt(0): fields vmcnt[3:0],
-    // expcnt[6:4] (7 = no wait), lgkmcnt[11:8], vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt(0x4078);
+    // s_waitcnt vmcnt((kNB - 2) stages x 8 copies) lgkmcnt(0): fields
+    // vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+    constexpr int vm = (kNB - 2) * 2 * kUnitsPerLane;
+    static_assert(vm < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | 0x70);
     const int dup = q < nstage ? static_cast<int>(tok_begin + int64_t(q) * kKT - origin_token(q)) : kKT;
     const int lane = threadIdx.x & 63;
     uint4* dst = ring<K>() + wave * (kUnitsPerLane * 64);
@@ -240,7 +253,7 @@ __device__ __forceinline__ void ring_step(const Ring& r, int s, Frags& f0, Frags
   __builtin_amdgcn_sched_barrier(0);
   r.land<KN>(s + 1);
   __builtin_amdgcn_sched_barrier(0);
-  // every wave is past its reads of stage s: refill its buffer with stage s + 5
+  // every wave is past its reads of stage s: refill its buffer with stage s + kNB
   r.issue<K>(s + kNB);
   read_frags(reinterpret_cast<const char*>(ring<KN>()), 0, r.oa, r.ob, f0);
   mfma_rows(f1, 2, 4, acc);
@@ -249,6 +262,18 @@ __device__ __forceinline__ void ring_step(const Ring& r, int s, Frags& f0, Frags
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
+}
+
+// The kNB stages of one trip around the ring.
+template <int... K>
+__device__ __forceinline__ void ring_round(const Ring& r, int s, Frags& f0, Frags& f1, f32x16 (&acc)[4][4],
+                                           std::integer_sequence<int, K...>) {
+  (ring_step<K>(r, s + K, f0, f1, acc), ...);
+}
+
+template <int... K>
+__device__ __forceinline__ void issue_first(const Ring& r, std::integer_sequence<int, K...>) {
+  (r.issue<K>(K), ...);
 }
 
 // Writes a wave's 128 x 128 float32 accumulators into the partial tile.
@@ -268,13 +293,22 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[4][4], float* __re
       }
 }
 
-// Work item of blockIdx.x: XCD x = blockIdx % 8 runs tile group x (gsz tiles
-// of the blocked order) of each slice in turn. Returns false past the end.
+// Work item of blockIdx.x; workgroups are dispatched round robin over the
+// 8 XCDs, XCD x = blockIdx % 8. With gsz == 0 (at least 8 slices), XCD x runs
+// every tile of slices x, x + 8, ... in turn, so each slice streams through
+// one L2 only. Otherwise XCD x runs tile group x (gsz tiles of the blocked
+// order) of each slice in turn. Returns false past the end.
 __device__ __forceinline__ bool work_item(int ntiles, int nsl, int gsz, const int* __restrict__ order, int& sl,
                                           int& tile) {
-  const int local = blockIdx.x / kXcds;
-  sl = local / gsz;
-  const int rank = (blockIdx.x % kXcds) * gsz + local % gsz;
+  const int local = blockIdx.x / kXcds, xcd = blockIdx.x % kXcds;
+  int rank;
+  if (gsz == 0) {
+    sl = xcd + kXcds * (local / ntiles);
+    rank = local % ntiles;
+  } else {
+    sl = local / gsz;
+    rank = xcd * gsz + local % gsz;
+  }
   if (sl >= nsl || rank >= ntiles) return false;
   tile = order[rank];
   return true;
@@ -322,24 +356,15 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
 
-  // prologue: stages 0 .. 4 issued, stage 0 landed, its first fragments read
-  r.issue<0>(0);
-  r.issue<1>(1);
-  r.issue<2>(2);
-  r.issue<3>(3);
+  // prologue: stages 0 .. kNB - 1 issued, stage 0 landed, its first fragments read
+  issue_first(r, std::make_integer_sequence<int, kNB - 1>{});
   r.land<0>(0);
-  r.issue<4>(4);
+  r.issue<kNB - 1>(kNB - 1);
   Frags f0, f1;
   read_frags(reinterpret_cast<const char*>(ring<0>()), 0, r.oa, r.ob, f0);
 
   // whole rings only: stages past nstage are zero and add nothing
-  for (int s = 0; s < r.nstage; s += kNB) {
-    ring_step<0>(r, s, f0, f1, acc);
-    ring_step<1>(r, s + 1, f0, f1, acc);
-    ring_step<2>(r, s + 2, f0, f1, acc);
-    ring_step<3>(r, s + 3, f0, f1, acc);
-    ring_step<4>(r, s + 4, f0, f1, acc);
-  }
+  for (int s = 0; s < r.nstage; s += kNB) ring_round(r, s, f0, f1, acc, std::make_integer_sequence<int, kNB>{});
   // no copy may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
   store_acc(acc, part + (int64_t(sl) * ntiles + tile) * (kT * kT));
@@ -558,8 +583,9 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   for (int g = 0; g < p.ngroups; ++g) {
     const int s0 = g * p.group;
     const int nsl = (s0 + p.group <= p.nslices) ? p.group : p.nslices - s0;
-    const int gsz = (p.ntiles + kXcds - 1) / kXcds;  // tiles per XCD group
-    const int per_xcd = gsz * nsl;
+    // whole slices per XCD when there are enough of them, else tile groups
+    const int gsz = nsl >= kXcds ? 0 : (p.ntiles + kXcds - 1) / kXcds;
+    const int per_xcd = gsz == 0 ? p.ntiles * ((nsl + kXcds - 1) / kXcds) : gsz * nsl;
     const char* kname = ring_ok ? "syrk_partial" : "syrk_partial_regs";
     {
       LaunchTimer timer(kname, st);

@@ -36,7 +36,7 @@ def _workload(cfg_id, n_tokens, dims, **kw):
 # step 1: covariance
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n_tokens,d", [(512, 128), (20000, 384), (3001, 100), (9000, 520), (1, 8), (8192, 256),
-                                        (8170, 136), (40, 64), (31, 64)])
+                                        (8170, 136), (40, 64), (31, 64), (65636, 64), (73000, 264)])
 def test_covariance(n_tokens, d):
     import torch
     kq, pipeline = _kq()

@@ -156,56 +156,64 @@ __device__ __forceinline__ f64x4 load16(const double* c) {
   return v;
 }
 
+// Value of v in lane `src` (a compile-time lane), for every lane.
+__device__ __forceinline__ double bcast(double v, int src) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b), src));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), src));
+  return __builtin_bit_cast(double, (static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// 1 / sqrt(p) for finite p > 0: the hardware estimate refined by two Newton
+// steps y <- y + y (1 - p y^2) / 2, which brings it to float64 rounding.
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  double y = __builtin_amdgcn_rsq(p);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = fma(-p * y, y, 1.0);
+    y = fma(0.5 * y, e, y);
+  }
+  return y;
+}
+
 // 16 x 16 Cholesky (lower) of the sub-block at l + o * (kP + 1) and its inverse
-// into x + o * (kP + 1); wave 0 only (lanes >= 16 idle). Returns the local index
-// of the first bad pivot, or -1.
-__device__ int base16(double* l, double* x, int o, double* col) {
+// into x + o * (kP + 1); wave 0 only. Lane i < 16 holds row i in registers;
+// columns are broadcast with readlane and pivots use 1 / sqrt(p), so the
+// column chain has no division, square root or LDS round trip. Returns the
+// local index of the first bad pivot, or -1.
+__device__ int base16(double* l, double* x, int o) {
   const int lane = threadIdx.x & 63;
   const bool act = lane < 16;
   double* L = l + o * (kP + 1);
   double* X = x + o * (kP + 1);
-  double r[16];
+  double r[16], y[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) r[j] = act ? L[lane * kP + j] : 0.0;
-  int bad = -1;
+  // Factor: after step k, lanes i >= k hold l_ik in r[k]. Lanes i < j also
+  // update their (upper) r[j]; those values are never broadcast and are
+  // cleared when their column comes up.
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const double piv = __shfl(r[k], k, 64);
-    if (!(piv > 0.0) || !isfinite(piv)) { bad = k; break; }
-    const double dk = sqrt(piv);
-    const double lik = (lane == k) ? dk : r[k] / dk;
+    const double p = bcast(r[k], k);
+    if (!(p > 0.0) || !(p < __builtin_huge_val())) return k;  // uniform
+    y[k] = rsqrt_f64(p);
+    const double lik = (lane == k) ? p * y[k] : r[k] * y[k];
     r[k] = (lane >= k) ? lik : 0.0;
-    if (act) col[lane] = r[k];
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = k + 1; j < 16; ++j)
-      if (lane >= j) r[j] -= lik * col[j];
-    __builtin_amdgcn_wave_barrier();
+    for (int j = k + 1; j < 16; ++j) r[j] = fma(-lik, bcast(lik, j), r[j]);
   }
-  if (bad >= 0) return bad;
-  // inverse by forward elimination of [L | I]; lane i owns row i of X
+  // Inverse by forward substitution: lane i holds row i of X = L^-1. At step
+  // k row k is scaled by 1 / l_kk = y_k, then removed from the rows below.
   double xr[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) xr[j] = (lane == j) ? 1.0 : 0.0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const double lkk = __shfl(r[k], k, 64);
-    if (lane == k) {
 #pragma unroll
-      for (int j = 0; j <= k; ++j) xr[j] /= lkk;
-    }
-    if (lane == k) {
+    for (int j = 0; j <= k; ++j) xr[j] = (lane == k) ? xr[j] * y[k] : xr[j];
+    const double lik = (lane > k) ? r[k] : 0.0;
 #pragma unroll
-      for (int j = 0; j <= k; ++j) col[j] = xr[j];
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    const double lik = r[k];
-#pragma unroll
-    for (int j = 0; j <= k; ++j)
-      if (lane > k) xr[j] -= lik * col[j];
-    __builtin_amdgcn_wave_barrier();
+    for (int j = 0; j <= k; ++j) xr[j] = fma(-lik, bcast(xr[j], k), xr[j]);
   }
   if (act) {
 #pragma unroll
@@ -225,7 +233,6 @@ __global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, 
                                                          int kb, int64_t d, int32_t* __restrict__ info) {
   __shared__ double l[kB * kP];
   __shared__ double x[kB * kP];
-  __shared__ double col[64];
   __shared__ int bad;
   if (*info) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, 
   __syncthreads();
   for (int s = 0; s < 4; ++s) {
     if (wave == 0) {
-      const int b = base16(l, x, 16 * s, col);
+      const int b = base16(l, x, 16 * s);
       if (lane == 0 && b >= 0) bad = 16 * s + b;
     }
     __syncthreads();

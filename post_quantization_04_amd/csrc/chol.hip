@@ -6,15 +6,18 @@
 //   1. damping: delta = damp * mean(diag H) in float64;
 //   2. reversal copy A = J H J + delta I into scratch, padded to a multiple of
 //      64 with an identity block;
-//   3. blocked right-looking Cholesky of A with 64 x 64 blocks: the diagonal
-//      block is factored (and inverted) in float64 in LDS by one workgroup,
-//      the panel below it is multiplied by the inverse block, and the
-//      trailing lower triangle receives the rank-64 update, both on float32
-//      MFMA (v_mfma_f32_32x32x2f32);
+//   3. blocked right-looking Cholesky of A with 64 x 64 blocks, one launch
+//      per step: the diagonal role brings block column kb up to date with the
+//      previous panel (float64 MFMA), factors and inverts the diagonal block
+//      in float64 in LDS (every workgroup of the role does this itself), and
+//      each workgroup multiplies one 64-row block of the panel by the inverse;
+//      in the same launch the update role applies the previous panel's
+//      rank-64 update to the block columns beyond kb in 128 x 128 tiles on
+//      float32 MFMA (v_mfma_f32_32x32x2f32);
 //   4. M = L^-1 by recursive doubling: diagonal blocks are already inverted;
 //      at each level, neighbouring blocks (B1, B2) merge with
-//      M21 = -M22 (L21 M11), two batched MFMA products that skip the zero
-//      triangles of M11 and M22;
+//      M21 = -M22 (L21 M11), two batched 128 x 128-tile MFMA products that
+//      skip the zero triangles of M11 and M22;
 //   5. R = J M J written over H (strict lower triangle zeroed).
 // A pivot that is not positive and finite stops the chain: `info` takes the
 // original index + 1 and every later kernel returns at once.
@@ -28,51 +31,151 @@ constexpr int kB = 64;  // block edge
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // --------------------------------------------------------------------------
-// 64 x 64 float32 MFMA tile product: C = alpha * A B + beta * C over k in [k0, k1)
-//   A element (i, k) at a[i * lda + k] (TA: a[k * lda + i])
+// 128 x 128 float32 MFMA tile product: C = alpha * A B + beta * C over k in [k0, k1)
+//   A element (i, k) at a[i * lda + k]
 //   B element (k, j) at b[k * ldb + j] (TB: b[j * ldb + k])
-// C may alias A (the panel step): every load of A precedes the first store.
-// m_valid / n_valid bound the tile; k beyond k1 reads as zero.
-// 256 threads: 4 waves in a 2 x 2 grid of 32 x 32 blocks.
+// k0 and k1 are multiples of 16, pointers and pitches 16-byte aligned;
+// m_valid and n_valid are multiples of 64 (rows i >= m_valid of A and
+// columns j >= n_valid of B read as zero and are not stored), so every
+// validity test is uniform across a wave. 256 threads: 4 waves in a 2 x 2
+// grid of 64 x 64, each a 2 x 2 grid of v_mfma_f32_32x32x2f32 blocks. k
+// advances in chunks of 16 through two LDS buffers held k-major ([k][i],
+// padded rows); the next chunk is loaded into registers while the current one
+// is multiplied.
 // --------------------------------------------------------------------------
-template <bool TA, bool TB>
-__device__ void gemm_tile(const float* a, int64_t lda, const float* b, int64_t ldb, float* c, int64_t ldc, int m_valid, int n_valid, int k0, int k1,
-                          float alpha, float beta) {
-  __shared__ float as[32][kB + 4];
-  __shared__ float bs[32][kB + 4];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wi = wave >> 1, wj = wave & 1;
-  f32x16 acc = f32x16{};
-  for (int kc = k0; kc < k1; kc += 32) {
-    // stage A (64 x 32) and B (32 x 64)
-    for (int e = tid; e < kB * 32; e += 256) {
-      int i, k;
-      if (TA) { i = e & 63; k = e >> 6; } else { k = e & 31; i = e >> 5; }
-      const int kg = kc + k;
-      as[k][i] = (i < m_valid && kg < k1) ? (TA ? a[int64_t(kg) * lda + i] : a[int64_t(i) * lda + kg]) : 0.0f;
-      int j, k2;
-      if (TB) { k2 = e & 31; j = e >> 5; } else { j = e & 63; k2 = e >> 6; }
-      const int kg2 = kc + k2;
-      bs[k2][j] = (j < n_valid && kg2 < k1) ? (TB ? b[int64_t(j) * ldb + kg2] : b[int64_t(kg2) * ldb + j]) : 0.0f;
-    }
-    __syncthreads();
+constexpr int kG = 128;       // tile edge
+constexpr int kGK = 16;       // k chunk
+constexpr int kGP = kG + 4;   // LDS row pitch (floats)
+
+struct GemmLds {
+  float a[2][kGK][kGP];
+  float b[2][kGK][kGP];
+};
+
+// Thread's share of a 128 x 16 chunk with rows along the contiguous axis of
+// memory transposed into LDS: rows t / 4 and t / 4 + 64, k quad t % 4.
+__device__ __forceinline__ void load_rows(const float* p, int64_t ld, int valid, int kc, float4 (&v)[2]) {
+  const int t = threadIdx.x;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float fa = as[2 * kk + (lane >> 5)][wi * 32 + (lane & 31)];
-      const float fb = bs[2 * kk + (lane >> 5)][wj * 32 + (lane & 31)];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, fb, acc, 0, 0, 0);
+  for (int h = 0; h < 2; ++h) {
+    const int i = (t >> 2) + 64 * h;
+    v[h] = (64 * h < valid) ? *reinterpret_cast<const float4*>(p + int64_t(i) * ld + kc + 4 * (t & 3))
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+__device__ __forceinline__ void store_rows(float (*lds)[kGP], const float4 (&v)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = (t >> 2) + 64 * h, k = 4 * (t & 3);
+    lds[k][i] = v[h].x;
+    lds[k + 1][i] = v[h].y;
+    lds[k + 2][i] = v[h].z;
+    lds[k + 3][i] = v[h].w;
+  }
+}
+// 16 x 128 chunk with columns along the contiguous axis: k rows t / 32 and
+// t / 32 + 8, column quad t % 32.
+__device__ __forceinline__ void load_cols(const float* p, int64_t ld, int valid, int kc, float4 (&v)[2]) {
+  const int t = threadIdx.x;
+  const int j = 4 * (t & 31);  // a wave covers 64 columns of one k row pair
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = (t >> 5) + 8 * h;
+    v[h] = ((j & ~63) < valid) ? *reinterpret_cast<const float4*>(p + int64_t(kc + k) * ld + j)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+__device__ __forceinline__ void store_cols(float (*lds)[kGP], const float4 (&v)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) *reinterpret_cast<float4*>(&lds[(t >> 5) + 8 * h][4 * (t & 31)]) = v[h];
+}
+
+template <bool TB>
+__device__ __forceinline__ void gemm128(GemmLds& sm, const float* a, int64_t lda, const float* b, int64_t ldb, float* c, int64_t ldc,
+                        int m_valid, int n_valid, int k0, int k1, float alpha, float beta) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  const int nchunk = (k1 - k0) / kGK;
+  float4 va[2], vb[2];
+  auto load = [&](int kc) {
+    load_rows(a, lda, m_valid, kc, va);
+    if (TB) load_rows(b, ldb, n_valid, kc, vb);
+    else load_cols(b, ldb, n_valid, kc, vb);
+  };
+  auto store = [&](int buf) {
+    store_rows(sm.a[buf], va);
+    if (TB) store_rows(sm.b[buf], vb);
+    else store_cols(sm.b[buf], vb);
+  };
+  if (nchunk > 0) {
+    load(k0);
+    store(0);
+  }
+  __syncthreads();
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunk) load(k0 + (ch + 1) * kGK);
+#pragma unroll
+    for (int kk = 0; kk < kGK / 2; ++kk) {
+      const int kr = 2 * kk + (lane >> 5);
+      float fa[2], fb[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) fa[x] = sm.a[buf][kr][wi * 64 + x * 32 + (lane & 31)];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) fb[y] = sm.b[buf][kr][wj * 64 + y * 32 + (lane & 31)];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
+    if (ch + 1 < nchunk) store(buf ^ 1);
     __syncthreads();
   }
+  // D of a 32 x 32 block: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+  // Blocks are wholly valid or not; the C reads of all blocks are issued before any use.
+  const bool rows_ok[2] = {wi * 64 < m_valid, wi * 64 + 32 < m_valid};
+  const bool cols_ok[2] = {wj * 64 < n_valid, wj * 64 + 32 < n_valid};
+  float* cp[2][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = wi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const int j = wj * 32 + (lane & 31);
-    if (i < m_valid && j < n_valid) {
-      float* p = c + int64_t(i) * ldc + j;
-      *p = (beta == 0.0f) ? alpha * acc[r] : alpha * acc[r] + beta * *p;
-    }
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+      cp[x][y] = c + int64_t(wi * 64 + x * 32 + 4 * (lane >> 5)) * ldc + wj * 64 + y * 32 + (lane & 31);
+  if (beta != 0.0f) {
+    f32x16 old[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) old[x][y][r] = cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc];
+        }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc] = alpha * acc[x][y][r] + beta * old[x][y][r];
+        }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc] = alpha * acc[x][y][r];
+        }
   }
 }
 
@@ -139,6 +242,17 @@ __device__ __forceinline__ f64x4 mm16(const double* a, const double* b, f64x4 ac
     const double fb = BT ? b[r * kP + 4 * kk + c] : b[(4 * kk + c) * kP + r];
     acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fa, fb, acc, 0, 0, 0);
   }
+  return acc;
+}
+
+// acc += A16 * B16^T with A16 float32 in LDS (pitch kP floats), B16 float64 (pitch kP).
+__device__ __forceinline__ f64x4 mm16f(const float* a, const double* b, f64x4 acc) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(a[r * kP + 4 * kk + c]), b[r * kP + 4 * kk + c],
+                                               acc, 0, 0, 0);
   return acc;
 }
 
@@ -225,34 +339,104 @@ __device__ int base16(double* l, double* x, int o) {
   return -1;
 }
 
-// Factor the 64 x 64 diagonal block kb (float64), invert its factor, and solve
-// one 64-row block of the panel below it: workgroup 0 writes L_kk to A and
-// L_kk^-1 to M; workgroup b >= 1 writes L[kb + b, kb] = A[kb + b, kb] L_kk^-T.
-// Every workgroup factors the (small) diagonal block itself.
-__global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp,
-                                                         int kb, int64_t d, int32_t* __restrict__ info) {
-  __shared__ double l[kB * kP];
-  __shared__ double x[kB * kP];
-  __shared__ int bad;
-  if (*info) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t o = int64_t(kb) * kB;
-  for (int e = tid; e < kB * kB; e += 256) {
+// Shared memory of the diagonal role: the diagonal block, its inverse, the
+// previous panel's rows of this block, and this workgroup's panel block with
+// its previous-panel rows (float32).
+struct DiagLds {
+  double l[kB * kP];
+  double x[kB * kP];
+  double lp[kB * kP];
+  double pb[kB * kP];
+  float lb[kB * kP];
+  int bad;
+};
+
+union StepLds {
+  DiagLds dg;
+  GemmLds gm;
+};
+
+// Copies the 64 x 64 float32 block at src (pitch dp) into dst as float64;
+// lower = true zeroes the strict upper triangle.
+__device__ __forceinline__ void load_block(double* dst, const float* src, int64_t dp, bool lower) {
+  for (int e = threadIdx.x; e < kB * kB; e += 256) {
     const int i = e >> 6, j = e & 63;
-    l[i * kP + j] = (j <= i) ? static_cast<double>(a[(o + i) * dp + o + j]) : 0.0;
-    x[i * kP + j] = 0.0;
+    dst[i * kP + j] = (!lower || j <= i) ? static_cast<double>(src[int64_t(i) * dp + j]) : 0.0;
   }
-  if (tid == 0) bad = -1;
+}
+
+// Diagonal role of step kb, workgroup b in [0, 1 + rest): brings block
+// column kb up to date with the previous step's rank-64 update (L[:, kb-1],
+// in float64 MFMA), factors the diagonal block and inverts its factor (every
+// workgroup does this itself), then workgroup 0 writes L_kk to A and L_kk^-1
+// to M, and workgroup b >= 1 writes L[kb + b, kb] = A[kb + b, kb] L_kk^-T.
+// All global reads are issued up front; the panel block's own update runs on
+// waves 1..3 while wave 0 factors the first 16 columns.
+__device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb, int64_t d,
+                          int32_t* __restrict__ info, int b) {
+  double* l = sm.l;
+  double* x = sm.x;
+  double* lp = sm.lp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t o = int64_t(kb) * kB, op = o - kB;
+  const int64_t r0 = o + int64_t(b) * kB;
+  const bool panel = b > 0, prev = kb > 0;
+  // this thread's 16 elements e = tid + 256 q of the panel block and its previous-panel rows
+  float ab[16], lb[16];
+  if (panel) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      ab[q] = a[(r0 + (e >> 6)) * dp + o + (e & 63)];
+      lb[q] = prev ? a[(r0 + (e >> 6)) * dp + op + (e & 63)] : 0.0f;
+    }
+  }
+  load_block(l, a + o * dp + o, dp, true);
+  for (int e = tid; e < kB * kB; e += 256) x[(e >> 6) * kP + (e & 63)] = 0.0;
+  if (prev) load_block(lp, a + o * dp + op, dp, false);
+  if (panel) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      sm.pb[(e >> 6) * kP + (e & 63)] = static_cast<double>(ab[q]);
+      sm.lb[(e >> 6) * kP + (e & 63)] = lb[q];
+    }
+  }
+  if (tid == 0) sm.bad = -1;
   __syncthreads();
-  for (int s = 0; s < 4; ++s) {
-    if (wave == 0) {
-      const int b = base16(l, x, 16 * s);
-      if (lane == 0 && b >= 0) bad = 16 * s + b;
+  if (prev) {
+    // A_kk -= L[kb, kb-1] L[kb, kb-1]^T on the 10 lower 16 x 16 tiles
+    for (int q = wave; q < 10; q += 4) {
+      int tt = 0, uu = 0, n = 0;
+      for (int ti = 0; ti < 4; ++ti)
+        for (int ui = 0; ui <= ti; ++ui, ++n)
+          if (n == q) { tt = ti; uu = ui; }
+      f64x4 acc = f64x4{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mm16<true>(lp + 16 * tt * kP + 16 * ks, lp + 16 * uu * kP + 16 * ks, acc);
+      const f64x4 c = load16(l + 16 * tt * kP + 16 * uu);
+      store16(l + 16 * tt * kP + 16 * uu, c - acc, 1.0);
     }
     __syncthreads();
-    if (bad >= 0) {
-      if (tid == 0 && blockIdx.x == 0) {
-        const int64_t ir = o + bad;
+  }
+  for (int s = 0; s < 4; ++s) {
+    if (wave == 0) {
+      const int bb = base16(l, x, 16 * s);
+      if (lane == 0 && bb >= 0) sm.bad = 16 * s + bb;
+    } else if (s == 0 && panel && prev) {
+      // panel block -= L[r0.., kb-1] L[kb, kb-1]^T (16 tiles over waves 1..3)
+      for (int q = wave - 1; q < 16; q += 3) {
+        const int ti = q >> 2, tj = q & 3;
+        f64x4 acc = f64x4{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mm16f(sm.lb + 16 * ti * kP + 16 * ks, lp + 16 * tj * kP + 16 * ks, acc);
+        store16(sm.pb + 16 * ti * kP + 16 * tj, load16(sm.pb + 16 * ti * kP + 16 * tj) - acc, 1.0);
+      }
+    }
+    __syncthreads();
+    if (sm.bad >= 0) {
+      if (tid == 0 && b == 0) {
+        const int64_t ir = o + sm.bad;
         atomicCAS(info, 0, static_cast<int32_t>(((ir < d) ? d - 1 - ir : ir) + 1));
       }
       return;
@@ -272,8 +456,8 @@ __global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, 
           if (n == q) { tt = ti; uu = ui; }
       if (q < n) {
         f64x4 c = load16(l + 16 * tt * kP + 16 * uu);
-        f64x4 p = mm16<true>(l + 16 * tt * kP + 16 * s, l + 16 * uu * kP + 16 * s, f64x4{});
-        store16(l + 16 * tt * kP + 16 * uu, c - p, 1.0);
+        f64x4 pp = mm16<true>(l + 16 * tt * kP + 16 * s, l + 16 * uu * kP + 16 * s, f64x4{});
+        store16(l + 16 * tt * kP + 16 * uu, c - pp, 1.0);
       }
     }
     __syncthreads();
@@ -294,29 +478,26 @@ __global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, 
     if (s < t) store16(x + 16 * t * kP + 16 * s, mv, -1.0);
     __syncthreads();
   }
-  if (blockIdx.x == 0) {
+  if (!panel) {
+    // L_kk into A, L_kk^-1 into M, zeros into the M block to its right (read
+    // as the zero upper triangle by the 128-wide merge tiles)
+    const bool right = o + kB < dp;
     for (int e = tid; e < kB * kB; e += 256) {
       const int i = e >> 6, j = e & 63;
       if (j <= i) a[(o + i) * dp + o + j] = static_cast<float>(l[i * kP + j]);
       m[(o + i) * dp + o + j] = static_cast<float>(x[i * kP + j]);
+      if (right) m[(o + i) * dp + o + kB + j] = 0.0f;
     }
     return;
   }
-  // panel block: P = A[r0.., kb] L_kk^-T, 64 x 64 x 64 in float64 MFMA (4 x 4 tiles of 16, 4 per wave)
-  const int64_t r0 = o + int64_t(blockIdx.x) * kB;
-  __syncthreads();
-  for (int e = tid; e < kB * kB; e += 256) {  // reuse l for the panel block
-    const int i = e >> 6, j = e & 63;
-    l[i * kP + j] = static_cast<double>(a[(r0 + i) * dp + o + j]);
-  }
-  __syncthreads();
+  // P = A[r0.., kb] L_kk^-T, 64 x 64 x 64 in float64 MFMA (4 x 4 tiles of 16, wave w owns tile row w)
   f64x4 acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int ti = wave, tj = q;
     f64x4 c = f64x4{};
     for (int u = 0; u <= tj; ++u)  // (L_kk^-T)[u][tj] = M[tj][u], zero for u > tj
-      c = mm16<true>(l + 16 * ti * kP + 16 * u, x + 16 * tj * kP + 16 * u, c);
+      c = mm16<true>(sm.pb + 16 * ti * kP + 16 * u, x + 16 * tj * kP + 16 * u, c);
     acc[q] = c;
   }
 #pragma unroll
@@ -329,24 +510,42 @@ __global__ __launch_bounds__(256) void diag_panel_kernel(float* __restrict__ a, 
   }
 }
 
-// A[i, j] -= L[i, kb] L[j, kb]^T for kb < j <= i.
-__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ a, int64_t dp, int kb,
-                                                     const int32_t* __restrict__ info) {
-  if (*info) return;
+// Update role of step kb >= 1, tile u: A[i, j] -= L[i, kb-1] L[j, kb-1]^T for
+// block columns kb + 1 <= j <= i (128 x 128 tiles; a diagonal tile also
+// rewrites the upper half of its 64 x 64 diagonal blocks, which is never read).
+// Block column kb receives the same update in the diagonal role.
+__device__ void update_role(GemmLds& sm, float* __restrict__ a, int64_t dp, int kb, int u) {
   int I, J;
-  tri(blockIdx.x, I, J);
-  const int64_t o = int64_t(kb) * kB;
-  const int64_t ri = o + kB + int64_t(I) * kB, rj = o + kB + int64_t(J) * kB;
-  gemm_tile<false, true>(a + ri * dp + o, dp, a + rj * dp + o, dp, a + ri * dp + rj, dp, kB, kB, 0, kB, -1.0f,
-                         1.0f);
+  tri(u, I, J);
+  const int64_t op = int64_t(kb - 1) * kB, c0 = int64_t(kb + 1) * kB;
+  const int64_t ri = c0 + int64_t(I) * kG, rj = c0 + int64_t(J) * kG;
+  const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
+  const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
+  gemm128<true>(sm, a + ri * dp + op, dp, a + rj * dp + op, dp, a + ri * dp + rj, dp, mv, nv, 0, kB, -1.0f, 1.0f);
+}
+
+// Step kb of the blocked factorization: workgroups [0, n_diag) take the
+// diagonal role, the rest the update role of the previous step's panel. The
+// two roles write disjoint block columns (kb, and kb + 1 onwards), so one
+// launch per step suffices.
+__global__ __launch_bounds__(256) void step_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb,
+                                                   int64_t d, int n_diag, int32_t* __restrict__ info) {
+  __shared__ StepLds sm;
+  if (*info) return;
+  if (static_cast<int>(blockIdx.x) < n_diag) diag_role(sm.dg, a, m, dp, kb, d, info, blockIdx.x);
+  else update_role(sm.gm, a, dp, kb, blockIdx.x - n_diag);
 }
 
 // Merge level with block size s: pair p joins B1 = [2ps, 2ps+s) and B2 = [2ps+s, min(2ps+2s, dp)).
 // stage 0: T[B2, B1] = L[B2, B1] M[B1, B1]      (M11 lower: k >= column tile start)
-// stage 1: M[B2, B1] = -M[B2, B2] T[B2, B1]     (M22 lower: k <= row tile end)
+// stage 1: M[B2, B1] = -M[B2, B2] T[B2, B1]     (M22 lower: k < row tile end)
+// 128 x 128 output tiles; a tile reaches at most into the 64 x 64 block just
+// above a diagonal block of M, which the diagonal step zeroes.
+template <int kStage>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ a, float* __restrict__ m,
                                                     float* __restrict__ t, int64_t dp, int64_t s, int tiles_side,
-                                                    int stage, const int32_t* __restrict__ info) {
+                                                    const int32_t* __restrict__ info) {
+  __shared__ GemmLds sm;
   if (*info) return;
   const int tiles_pair = tiles_side * tiles_side;
   const int64_t p = blockIdx.x / tiles_pair;
@@ -355,17 +554,18 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ a,
   const int64_t b1 = 2 * p * s, b2 = b1 + s;
   if (b2 >= dp) return;
   const int64_t n2 = (b2 + s <= dp) ? s : dp - b2;
-  const int64_t i0 = int64_t(ti) * kB, j0 = int64_t(tj) * kB;
+  const int64_t i0 = int64_t(ti) * kG, j0 = int64_t(tj) * kG;
   if (i0 >= n2) return;
-  const int mv = static_cast<int>(n2 - i0 < kB ? n2 - i0 : kB);
-  if (stage == 0) {
+  const int mv = static_cast<int>(n2 - i0 < kG ? n2 - i0 : kG);
+  const int nv = static_cast<int>(s - j0 < kG ? s - j0 : kG);
+  if (kStage == 0) {
     // rows of B2, columns of B1, k over B1 from j0
-    gemm_tile<false, false>(a + (b2 + i0) * dp + b1, dp, m + b1 * dp + b1 + j0, dp, t + (b2 + i0) * dp + b1 + j0,
-                            dp, mv, kB, static_cast<int>(j0), static_cast<int>(s), 1.0f, 0.0f);
+    gemm128<false>(sm, a + (b2 + i0) * dp + b1, dp, m + b1 * dp + b1 + j0, dp, t + (b2 + i0) * dp + b1 + j0, dp,
+                   mv, nv, static_cast<int>(j0), static_cast<int>(s), 1.0f, 0.0f);
   } else {
-    const int kend = static_cast<int>(i0 + kB < n2 ? i0 + kB : n2);
-    gemm_tile<false, false>(m + (b2 + i0) * dp + b2, dp, t + b2 * dp + b1 + j0, dp, m + (b2 + i0) * dp + b1 + j0,
-                            dp, mv, kB, 0, kend, -1.0f, 0.0f);
+    const int kend = static_cast<int>(i0 + kG < n2 ? i0 + kG : n2);
+    gemm128<false>(sm, m + (b2 + i0) * dp + b2, dp, t + b2 * dp + b1 + j0, dp, m + (b2 + i0) * dp + b1 + j0, dp,
+                   mv, nv, 0, kend, -1.0f, 0.0f);
   }
 }
 
@@ -424,32 +624,29 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
 
   for (int kb = 0; kb < nb; ++kb) {
     const int rest = nb - kb - 1;
+    const int ntu = (kb >= 1) ? (rest + 1) / 2 : 0;  // 128-wide tiles over block columns kb + 1 ..
+    const unsigned grid = static_cast<unsigned>(1 + rest + ntu * (ntu + 1) / 2);
     {
-      LaunchTimer timer("diag_panel_kernel", st);
-      hipLaunchKernelGGL(diag_panel_kernel, dim3(static_cast<unsigned>(1 + rest)), dim3(256), 0, st, a, m, dp, kb,
-                         d, info);
+      LaunchTimer timer("step_kernel", st);
+      hipLaunchKernelGGL(step_kernel, dim3(grid), dim3(256), 0, st, a, m, dp, kb, d, 1 + rest, info);
     }
-    if ((r = check_launch("diag_panel_kernel")) != KQ_OK) return r;
-    if (rest == 0) break;
-    {
-      LaunchTimer timer("update_kernel", st);
-      hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(rest * (rest + 1) / 2)), dim3(256), 0, st, a, dp,
-                         kb, info);
-    }
-    if ((r = check_launch("update_kernel")) != KQ_OK) return r;
+    if ((r = check_launch("step_kernel")) != KQ_OK) return r;
   }
 
   for (int64_t s = kB; s < dp; s *= 2) {
     const int64_t pairs = (dp + 2 * s - 1) / (2 * s);
-    const int tiles_side = static_cast<int>(s / kB);
+    const int tiles_side = static_cast<int>((s + kG - 1) / kG);
     const unsigned grid = static_cast<unsigned>(pairs * tiles_side * tiles_side);
-    for (int stage = 0; stage < 2; ++stage) {
-      {
-        LaunchTimer timer("merge_kernel", st);
-        hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, stage, info);
-      }
-      if ((r = check_launch("merge_kernel")) != KQ_OK) return r;
+    {
+      LaunchTimer timer("merge_kernel", st);
+      hipLaunchKernelGGL(merge_kernel<0>, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, info);
     }
+    if ((r = check_launch("merge_kernel")) != KQ_OK) return r;
+    {
+      LaunchTimer timer("merge_kernel", st);
+      hipLaunchKernelGGL(merge_kernel<1>, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, info);
+    }
+    if ((r = check_launch("merge_kernel")) != KQ_OK) return r;
   }
 
   {

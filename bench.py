@@ -43,6 +43,9 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=64, help="weight rows in the oracle's sweep sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, copy 1 GiB device-to-device (a reference kernel for HBM byte counters)")
+    p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                   help="no run: turn two rocprofv3 --pmc runs of '--copy-calibration' (FETCH_SIZE, then "
+                        "WRITE_SIZE) into the per-launch HBM bytes of the roofline kernel")
     return p.parse_args()
 
 
@@ -98,8 +101,82 @@ def cpu_baseline(wl, cfg, sub, bits, tokens, rows):
     }
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ROOFLINE_KERNEL = "syrk_partial"
+ROOFLINE_SOURCE = os.path.join(ROOT, "post_quantization_04_amd", "csrc", "syrk.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_partial_llama2-7b_q_proj_hbm_traffic.json")
+COPY_BYTES = 1 << 30
+
+
+def source_hash(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pmc_dispatches(run_dir: str, counter: str):
+    """[(dispatch id, kernel name, counter value)] from a rocprofv3 --pmc csv run, in dispatch order."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    vals, names = {}, {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                k = int(row["Dispatch_Id"])
+                vals[k] = vals.get(k, 0.0) + float(row["Counter_Value"])
+                names[k] = row["Kernel_Name"]
+    return [(k, names[k], vals[k]) for k in sorted(vals)]
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, out_json: str) -> int:
+    """HBM bytes per launch of the roofline kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for the final 1 GiB device-to-device copy."""
+    out = {"kernel": ROOFLINE_KERNEL, "source": os.path.relpath(ROOFLINE_SOURCE, ROOT),
+           "source_sha256": source_hash(ROOFLINE_SOURCE), "copy_bytes": COPY_BYTES}
+    for key, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = pmc_dispatches(run_dir, counter)
+        copy = rows[-1]  # the calibration copy is the last dispatch of the run
+        if "syrk" in copy[1] or copy[2] <= 0:
+            raise RuntimeError(f"{counter}: last dispatch {copy[1]!r} is not the calibration copy")
+        mine = [v for _, n, v in rows if f"::{ROOFLINE_KERNEL}(" in n or n.startswith(f"{ROOFLINE_KERNEL}(")]
+        if not mine:
+            raise RuntimeError(f"{counter}: no {ROOFLINE_KERNEL} dispatch")
+        scale = COPY_BYTES / (copy[2] * 1024.0)
+        out[f"{key}_kib_per_launch"] = sum(mine) / len(mine)
+        out[f"{key}_launches"] = len(mine)
+        out[f"copy_{key}_kib"] = copy[2]
+        out[f"{key}_scale"] = scale
+        out[f"{key}_bytes_per_launch"] = out[f"{key}_kib_per_launch"] * 1024.0 * scale
+    out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def stored_traffic():
+    """Per-launch HBM bytes of the roofline kernel from the committed counter summary, or None when the
+    summary is missing or was taken on a different version of the kernel's source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("source_sha256") != source_hash(ROOFLINE_SOURCE):
+            return None
+        return int(round(rec["traffic_bytes_per_launch"]))
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def main() -> int:
     args = parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU; the path's multi-GPU sharding is design only, "
@@ -234,7 +311,9 @@ def main() -> int:
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(syrk_tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": 2 * n_tok * din + 4 * din * din,
             "launches": launches,
             "avg_launch_ms": round(syrk_ms / max(launches, 1), 4),
         },

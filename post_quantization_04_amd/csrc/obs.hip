@@ -186,58 +186,113 @@ __global__ __launch_bounds__(kSweepThreads) void sweep_kernel(
   }
 }
 
-// W[:, c1:] -= E R[c0:c0+B, c1:], c1 = c0 + B. 64 x 64 output tile per workgroup,
-// 4 waves of 32 x 32 (2 x 2 float64 MFMA 16 x 16 blocks).
+// W[:, c1:] -= E R[c0:c0+B, c1:], c1 = c0 + B, on float64 MFMA
+// (v_mfma_f64_16x16x4f64). 128 x 128 output tile per workgroup, 4 waves of
+// 64 x 64 (4 x 4 blocks of 16 x 16). The accumulators start as the W tile
+// (read at entry, under the first chunk's loads) and -E goes into LDS, so
+// the MFMAs produce W - E R directly and the exit only stores. k advances in
+// chunks of 16 through two LDS buffers held k-major ([k][row], [k][column]);
+// the next chunk is loaded into registers (R converted to float64 on its way
+// into LDS) while the current one is multiplied. B and the column extent are
+// multiples of 32; rows past dout read as zero and are not written.
+constexpr int kTT = 128;      // tile edge
+constexpr int kTK = 16;       // k chunk
+constexpr int kTP = kTT + 1;  // LDS row pitch (doubles)
+
+template <int B>
 __global__ __launch_bounds__(256) void trailing_kernel(double* __restrict__ w, const float* __restrict__ r,
                                                        const double* __restrict__ e, int64_t dout, int64_t din,
-                                                       int64_t c0, int B) {
-  __shared__ double as[64][17];
-  __shared__ double bs[16][65];
+                                                       int64_t c0) {
+  __shared__ double as[2][kTK][kTP];
+  __shared__ double bs[2][kTK][kTP];
   const int64_t c1 = c0 + B;
-  const int64_t i0 = int64_t(blockIdx.y) * 64;
-  const int64_t j0 = c1 + int64_t(blockIdx.x) * 64;
+  const int64_t i0 = int64_t(blockIdx.y) * kTT;
+  const int64_t j0 = c1 + int64_t(blockIdx.x) * kTT;
+  const int mv = static_cast<int>(dout - i0 < kTT ? dout - i0 : kTT);
+  const int nv = static_cast<int>(din - j0 < kTT ? din - j0 : kTT);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
-  f64x4 acc[2][2];
+  // this thread's loads: E row ar, k half ak (8 doubles); R row bk, columns bc .. bc + 7
+  const int ar = tid >> 1, ak = (tid & 1) * 8;
+  const int bk = tid >> 4, bc = (tid & 15) * 8;
+  const bool a_ok = ar < mv, b_ok = bc < nv;
+  const double* ap = e + (i0 + (a_ok ? ar : 0)) * B + ak;
+  const float* bp = r + (c0 + bk) * din + j0 + (b_ok ? bc : 0);
+  double2 va[4];
+  float4 vb[2];
+  auto load = [&](int kc) {
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int q = 0; q < 4; ++q) va[q] = a_ok ? *reinterpret_cast<const double2*>(ap + kc + 2 * q) : double2{0.0, 0.0};
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{};
-  for (int kc = 0; kc < B; kc += 16) {
-    for (int q = tid; q < 64 * 16; q += 256) {
-      const int i = q >> 4, k = q & 15;
-      as[i][k] = (i0 + i < dout) ? e[(i0 + i) * B + kc + k] : 0.0;
-      const int kb = q >> 6, jb = q & 63;
-      bs[kb][jb] = (j0 + jb < din) ? static_cast<double>(r[(c0 + kc + kb) * din + j0 + jb]) : 0.0;
+    for (int q = 0; q < 2; ++q)
+      vb[q] = b_ok ? *reinterpret_cast<const float4*>(bp + int64_t(kc) * din + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      as[buf][ak + 2 * q][ar] = -va[q].x;
+      as[buf][ak + 2 * q + 1][ar] = -va[q].y;
     }
-    __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      double fa[2], fb[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) fa[x] = as[wi * 32 + x * 16 + (lane & 15)][4 * kk + (lane >> 4)];
-#pragma unroll
-      for (int y = 0; y < 2; ++y) fb[y] = bs[4 * kk + (lane >> 4)][wj * 32 + y * 16 + (lane & 15)];
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      bs[buf][bk][bc + 4 * q] = vb[q].x;
+      bs[buf][bk][bc + 4 * q + 1] = vb[q].y;
+      bs[buf][bk][bc + 4 * q + 2] = vb[q].z;
+      bs[buf][bk][bc + 4 * q + 3] = vb[q].w;
     }
-    __syncthreads();
-  }
+  };
   // D[i][j] of a 16 x 16 float64 block: lane l, register q -> i = 4 q + l / 16, j = l % 16
   // (measured on gfx950; the operands are A[i][k] at lane i + 16 k and B[k][j] at lane j + 16 k)
+  const int jl = lane & 15, il = lane >> 4;
+  f64x4 acc[4][4];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int q = 0; q < 4; ++q) {
+      const int i = wi * 64 + x * 16 + 4 * q + il;
+      const double* wr = w + (i0 + (i < mv ? i : 0)) * din + j0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t i = i0 + wi * 32 + x * 16 + 4 * q + (lane >> 4);
-        const int64_t j = j0 + wj * 32 + y * 16 + (lane & 15);
-        if (i < dout && j < din) w[i * din + j] -= acc[x][y][q];
+      for (int y = 0; y < 4; ++y) {
+        const int j = wj * 64 + y * 16 + jl;
+        acc[x][y][q] = wr[j < nv ? j : 0];
       }
+    }
+  constexpr int nchunk = B / kTK;
+  load(0);
+  store(0);
+  __syncthreads();
+#pragma unroll
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunk) load((ch + 1) * kTK);
+#pragma unroll
+    for (int kk = 0; kk < kTK / 4; ++kk) {
+      const int kr = 4 * kk + (lane >> 4);
+      double fa[4], fb[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) fa[x] = as[buf][kr][wi * 64 + x * 16 + (lane & 15)];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) fb[y] = bs[buf][kr][wj * 64 + y * 16 + (lane & 15)];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    if (ch + 1 < nchunk) store(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = wi * 64 + x * 16 + 4 * q + il;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int j = wj * 64 + y * 16 + jl;
+        if (i < mv && j < nv) w[(i0 + i) * din + j0 + j] = acc[x][y][q];
+      }
+    }
 }
 
 template <int B>
@@ -256,9 +311,9 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
     if (rest <= 0) break;
     {
       LaunchTimer timer("trailing_kernel", st);
-      hipLaunchKernelGGL(trailing_kernel, dim3(static_cast<unsigned>((rest + 63) / 64),
-                                               static_cast<unsigned>((dout + 63) / 64)),
-                         dim3(256), 0, st, w, r, e, dout, din, c0, B);
+      hipLaunchKernelGGL(trailing_kernel<B>, dim3(static_cast<unsigned>((rest + kTT - 1) / kTT),
+                                                  static_cast<unsigned>((dout + kTT - 1) / kTT)),
+                         dim3(256), 0, st, w, r, e, dout, din, c0);
     }
     s = check_launch("trailing_kernel");
     if (s != KQ_OK) return s;

@@ -1,18 +1,25 @@
 // GPTQ-style column-wise OBS on the rotated weight, in float64.
 //
 // The sweep is sequential in the column index and independent across rows,
-// given R. Per block of B columns:
-//   * sweep kernel: 16 lanes own one row; lane l keeps columns l, l + 16, ...
-//     of the block in registers (B / 16 values). For column j the owning
-//     lane quantises, forms the scaled error e = (w - w^) / R_jj and the
-//     error is broadcast to the row's 16 lanes with one DPP row_newbcast;
-//     every lane then removes e * R[j][k] from its columns k. The block of R
-//     sits in LDS, laid out so each lane reads its B / 16 entries of row j
-//     with two 16-byte loads; entries on and below the diagonal are stored as
-//     zero, so the update is branch free. Group minima and maxima are
-//     16-lane shuffle reductions.
-//   * trailing kernel (lazy batch): W[:, end:] -= E R[blk, end:] on float64
-//     MFMA (v_mfma_f64_16x16x4f64), E being the block's scaled errors.
+// given R. Per block k of B columns [c0, c0 + B):
+//   * near kernel (k > 0): the block's columns receive the previous block's
+//     errors, W[:, c0:c0+B] -= E_{k-1} R[c0-B:c0, c0:c0+B] (float64 MFMA,
+//     32-row tiles);
+//   * step kernel, two roles in one launch:
+//     - sweep (16 rows per workgroup): 16 lanes own one row; lane l keeps
+//       columns l, l + 16, ... of the block in registers (B / 16 values). For
+//       column j the owning lane quantises, forms the scaled error
+//       e = (w - w^) / R_jj and the error is broadcast to the row's 16 lanes
+//       with one DPP row_newbcast; every lane then removes e * R[j][k] from
+//       its columns k. The block of R sits in LDS, laid out so each lane reads
+//       its B / 16 entries of row j; entries on and below the diagonal are
+//       stored as zero, so the update is branch free. Group minima and maxima
+//       are 16-lane shuffle reductions. The block's errors go to E_k.
+//     - far update (lazy batch): W[:, c0+B:] -= E_{k-1} R[c0-B:c0, c0+B:] on
+//       float64 MFMA (v_mfma_f64_16x16x4f64) in 128 x 128 tiles.
+//     The roles touch disjoint columns and E is double buffered, so the
+//     latency-bound sweep (one wave per SIMD) shares the GPU with the
+//     MFMA-bound update instead of alternating with it.
 // Float64 keeps the rounding argument w / s of every entry within about
 // 1e-6 grid units of the float64 oracle across thousands of columns, where a
 // float32 sweep drifts past 1e-5.
@@ -91,14 +98,24 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const double* __restrict_
   }
 }
 
+// Shared memory of the sweep: rl[j][l * EPL + e] = R[c0 + j][c0 + l + 16 e]
+// above the diagonal, else 0; rinv[j] = 1 / R[c0 + j][c0 + j].
 template <int B>
-__global__ __launch_bounds__(kSweepThreads) void sweep_kernel(
-    double* __restrict__ w, const float* __restrict__ r, int64_t dout, int64_t din, int64_t c0, int bits, int group,
-    uint8_t* __restrict__ codes, float* __restrict__ scales, uint8_t* __restrict__ zeros,
-    double* __restrict__ preround, double* __restrict__ e_out) {
+struct SweepLds {
+  float rl[B][B];
+  double rinv[B];
+};
+
+// Sweep of block [c0, c0 + B) for rows [16 wg, 16 wg + 16); writes the scaled
+// errors of the block to e_out [dout, B].
+template <int B>
+__device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, const float* __restrict__ r,
+                           int64_t dout, int64_t din, int64_t c0, int bits, int group, uint8_t* __restrict__ codes,
+                           float* __restrict__ scales, uint8_t* __restrict__ zeros, double* __restrict__ preround,
+                           double* __restrict__ e_out) {
   constexpr int EPL = B / 16;
-  __shared__ float rl[B][B];  // rl[j][l * EPL + e] = R[c0 + j][c0 + l + 16 e] above the diagonal, else 0
-  __shared__ double rinv[B];
+  auto& rl = sm.rl;
+  auto& rinv = sm.rinv;
   const int tid = threadIdx.x;
   for (int idx = tid; idx < B * B; idx += kSweepThreads) {
     const int j = idx / B, k = idx % B;
@@ -109,7 +126,7 @@ __global__ __launch_bounds__(kSweepThreads) void sweep_kernel(
   __syncthreads();
 
   const int l16 = tid & 15;
-  const int64_t row = int64_t(blockIdx.x) * kRowsPerWg + (tid >> 4);
+  const int64_t row = int64_t(wg) * kRowsPerWg + (tid >> 4);
   const bool valid = row < dout;
   const int maxq = (1 << bits) - 1;
   const int64_t ngroups = group ? din / group : 1;
@@ -186,75 +203,77 @@ __global__ __launch_bounds__(kSweepThreads) void sweep_kernel(
   }
 }
 
-// W[:, c1:] -= E R[c0:c0+B, c1:], c1 = c0 + B, on float64 MFMA
-// (v_mfma_f64_16x16x4f64). 128 x 128 output tile per workgroup, 4 waves of
-// 64 x 64 (4 x 4 blocks of 16 x 16). The accumulators start as the W tile
-// (read at entry, under the first chunk's loads) and -E goes into LDS, so
-// the MFMAs produce W - E R directly and the exit only stores. k advances in
-// chunks of 16 through two LDS buffers held k-major ([k][row], [k][column]);
+// Tile of W[rows, cols] -= E R[k0 .. k0 + B, cols] on float64 MFMA
+// (v_mfma_f64_16x16x4f64): TM x TN output tile at (i0, j0), 4 waves in a
+// WR x WC grid, each a grid of 16 x 16 blocks. The accumulators start as the
+// W tile (read at entry, under the first chunk's loads) and -E goes into LDS,
+// so the MFMAs produce W - E R directly and the exit only stores. k advances
+// in chunks of 16 through two LDS buffers held k-major ([k][row], [k][column]);
 // the next chunk is loaded into registers (R converted to float64 on its way
-// into LDS) while the current one is multiplied. B and the column extent are
-// multiples of 32; rows past dout read as zero and are not written.
-constexpr int kTT = 128;      // tile edge
-constexpr int kTK = 16;       // k chunk
-constexpr int kTP = kTT + 1;  // LDS row pitch (doubles)
+// into LDS) while the current one is multiplied. E is [dout, B]; the column
+// extent is a multiple of 32; rows past dout read as zero and are not written.
+constexpr int kTK = 16;  // k chunk
 
-template <int B>
-__global__ __launch_bounds__(256) void trailing_kernel(double* __restrict__ w, const float* __restrict__ r,
-                                                       const double* __restrict__ e, int64_t dout, int64_t din,
-                                                       int64_t c0) {
-  __shared__ double as[2][kTK][kTP];
-  __shared__ double bs[2][kTK][kTP];
-  const int64_t c1 = c0 + B;
-  const int64_t i0 = int64_t(blockIdx.y) * kTT;
-  const int64_t j0 = c1 + int64_t(blockIdx.x) * kTT;
-  const int mv = static_cast<int>(dout - i0 < kTT ? dout - i0 : kTT);
-  const int nv = static_cast<int>(din - j0 < kTT ? din - j0 : kTT);
+template <int TM, int TN>
+struct TileLds {
+  double as[2][kTK][TM + 1];
+  double bs[2][kTK][TN + 1];
+};
+
+template <int B, int TM, int TN, int WR, int WC>
+__device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restrict__ w, const float* __restrict__ r,
+                                          const double* __restrict__ e, int64_t dout, int64_t din, int64_t k0,
+                                          int64_t i0, int64_t j0) {
+  static_assert(WR * WC == 4 && TM % (16 * WR) == 0 && TN % (16 * WC) == 0, "tile shape");
+  constexpr int BM = TM / WR / 16, BN = TN / WC / 16;  // 16 x 16 blocks per wave
+  constexpr int DA = TM / 16, DB = TN / 16;            // doubles of E, floats of R per thread per chunk
+  static_assert(DA % 2 == 0 && DB % 2 == 0, "vector loads");
+  const int mv = static_cast<int>(dout - i0 < TM ? dout - i0 : TM);
+  const int nv = static_cast<int>(din - j0 < TN ? din - j0 : TN);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wi = wave >> 1, wj = wave & 1;
-  // this thread's loads: E row ar, k half ak (8 doubles); R row bk, columns bc .. bc + 7
-  const int ar = tid >> 1, ak = (tid & 1) * 8;
-  const int bk = tid >> 4, bc = (tid & 15) * 8;
+  const int wi = wave / WC, wj = wave % WC;
+  // this thread's loads: E row ar, k offset ak (DA doubles); R row bk, columns bc .. bc + DB - 1
+  const int ar = tid / (kTK / DA), ak = (tid % (kTK / DA)) * DA;
+  const int bk = tid / (TN / DB), bc = (tid % (TN / DB)) * DB;
   const bool a_ok = ar < mv, b_ok = bc < nv;
   const double* ap = e + (i0 + (a_ok ? ar : 0)) * B + ak;
-  const float* bp = r + (c0 + bk) * din + j0 + (b_ok ? bc : 0);
-  double2 va[4];
-  float4 vb[2];
+  const float* bp = r + (k0 + bk) * din + j0 + (b_ok ? bc : 0);
+  double2 va[DA / 2];
+  float2 vb[DB / 2];
   auto load = [&](int kc) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) va[q] = a_ok ? *reinterpret_cast<const double2*>(ap + kc + 2 * q) : double2{0.0, 0.0};
+    for (int q = 0; q < DA / 2; ++q)
+      va[q] = a_ok ? *reinterpret_cast<const double2*>(ap + kc + 2 * q) : double2{0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      vb[q] = b_ok ? *reinterpret_cast<const float4*>(bp + int64_t(kc) * din + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < DB / 2; ++q)
+      vb[q] = b_ok ? *reinterpret_cast<const float2*>(bp + int64_t(kc) * din + 2 * q) : make_float2(0.f, 0.f);
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      as[buf][ak + 2 * q][ar] = -va[q].x;
-      as[buf][ak + 2 * q + 1][ar] = -va[q].y;
+    for (int q = 0; q < DA / 2; ++q) {
+      sm.as[buf][ak + 2 * q][ar] = -va[q].x;
+      sm.as[buf][ak + 2 * q + 1][ar] = -va[q].y;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      bs[buf][bk][bc + 4 * q] = vb[q].x;
-      bs[buf][bk][bc + 4 * q + 1] = vb[q].y;
-      bs[buf][bk][bc + 4 * q + 2] = vb[q].z;
-      bs[buf][bk][bc + 4 * q + 3] = vb[q].w;
+    for (int q = 0; q < DB / 2; ++q) {
+      sm.bs[buf][bk][bc + 2 * q] = vb[q].x;
+      sm.bs[buf][bk][bc + 2 * q + 1] = vb[q].y;
     }
   };
   // D[i][j] of a 16 x 16 float64 block: lane l, register q -> i = 4 q + l / 16, j = l % 16
   // (measured on gfx950; the operands are A[i][k] at lane i + 16 k and B[k][j] at lane j + 16 k)
   const int jl = lane & 15, il = lane >> 4;
-  f64x4 acc[4][4];
+  f64x4 acc[BM][BN];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < BM; ++x)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int i = wi * 64 + x * 16 + 4 * q + il;
+      const int i = wi * (TM / WR) + x * 16 + 4 * q + il;
       const double* wr = w + (i0 + (i < mv ? i : 0)) * din + j0;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = wj * 64 + y * 16 + jl;
+      for (int y = 0; y < BN; ++y) {
+        const int j = wj * (TN / WC) + y * 16 + jl;
         acc[x][y][q] = wr[j < nv ? j : 0];
       }
     }
@@ -268,55 +287,107 @@ __global__ __launch_bounds__(256) void trailing_kernel(double* __restrict__ w, c
     if (ch + 1 < nchunk) load((ch + 1) * kTK);
 #pragma unroll
     for (int kk = 0; kk < kTK / 4; ++kk) {
-      const int kr = 4 * kk + (lane >> 4);
-      double fa[4], fb[4];
+      const int kr = 4 * kk + il;
+      double fa[BM], fb[BN];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) fa[x] = as[buf][kr][wi * 64 + x * 16 + (lane & 15)];
+      for (int x = 0; x < BM; ++x) fa[x] = sm.as[buf][kr][wi * (TM / WR) + x * 16 + jl];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) fb[y] = bs[buf][kr][wj * 64 + y * 16 + (lane & 15)];
+      for (int y = 0; y < BN; ++y) fb[y] = sm.bs[buf][kr][wj * (TN / WC) + y * 16 + jl];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < BM; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
+        for (int y = 0; y < BN; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
     if (ch + 1 < nchunk) store(buf ^ 1);
     __syncthreads();
   }
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < BM; ++x)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int i = wi * 64 + x * 16 + 4 * q + il;
+      const int i = wi * (TM / WR) + x * 16 + 4 * q + il;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = wj * 64 + y * 16 + jl;
+      for (int y = 0; y < BN; ++y) {
+        const int j = wj * (TN / WC) + y * 16 + jl;
         if (i < mv && j < nv) w[(i0 + i) * din + j0 + j] = acc[x][y][q];
       }
     }
 }
 
+// Near update before the sweep of block [c0, c0 + B): its columns receive the
+// previous block's errors, W[:, c0:c0+B] -= E_prev R[c0-B:c0, c0:c0+B], in
+// 32-row tiles (many workgroups for a narrow update).
+template <int B>
+struct NearShape {
+  static constexpr int TM = 32, TN = B, WR = (B >= 64 ? 1 : 2), WC = 4 / WR;
+};
+
+template <int B>
+__global__ __launch_bounds__(256) void near_kernel(double* __restrict__ w, const float* __restrict__ r,
+                                                   const double* __restrict__ e_prev, int64_t dout, int64_t din,
+                                                   int64_t c0) {
+  using S = NearShape<B>;
+  __shared__ TileLds<S::TM, S::TN> sm;
+  tile_role<B, S::TM, S::TN, S::WR, S::WC>(sm, w, r, e_prev, dout, din, c0 - B, int64_t(blockIdx.x) * S::TM, c0);
+}
+
+// One step of the sweep: workgroups [0, n_sweep) sweep block [c0, c0 + B)
+// (errors to e_cur), the others apply the previous block's errors e_prev to
+// every column from c0 + B on in 128 x 128 tiles. The two roles touch
+// disjoint columns, so the latency-bound sweep and the MFMA-bound update
+// share the GPU.
+constexpr int kFT = 128;  // far tile edge
+
+template <int B>
+union StepLds {
+  SweepLds<B> sw;
+  TileLds<kFT, kFT> tl;
+};
+
+template <int B>
+__global__ __launch_bounds__(256) void step_kernel(double* __restrict__ w, const float* __restrict__ r,
+                                                   int64_t dout, int64_t din, int64_t c0, int bits, int group,
+                                                   uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                   uint8_t* __restrict__ zeros, double* __restrict__ preround,
+                                                   const double* __restrict__ e_prev, double* __restrict__ e_cur,
+                                                   int n_sweep, int far_cols) {
+  __shared__ StepLds<B> sm;
+  const int b = blockIdx.x;
+  if (b < n_sweep) {
+    sweep_role<B>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_cur);
+    return;
+  }
+  const int t = b - n_sweep;
+  const int64_t c1 = c0 + B;
+  tile_role<B, kFT, kFT, 2, 2>(sm.tl, w, r, e_prev, dout, din, c0 - B, int64_t(t / far_cols) * kFT,
+                               c1 + int64_t(t % far_cols) * kFT);
+}
+
 template <int B>
 kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int bits, int group, uint8_t* codes,
                      float* scales, uint8_t* zeros, double* preround, double* e, hipStream_t st) {
-  const unsigned rows_grid = static_cast<unsigned>((dout + kRowsPerWg - 1) / kRowsPerWg);
-  for (int64_t c0 = 0; c0 < din; c0 += B) {
-    {
-      LaunchTimer timer("sweep_kernel", st);
-      hipLaunchKernelGGL(sweep_kernel<B>, dim3(rows_grid), dim3(kSweepThreads), 0, st, w, r, dout, din, c0, bits,
-                         group, codes, scales, zeros, preround, e);
+  const int n_sweep = static_cast<int>((dout + kRowsPerWg - 1) / kRowsPerWg);
+  const int far_rows = static_cast<int>((dout + kFT - 1) / kFT);
+  double* ebuf[2] = {e, e + dout * B};
+  kq_status s;
+  for (int64_t c0 = 0, k = 0; c0 < din; c0 += B, ++k) {
+    double* e_prev = ebuf[(k + 1) & 1];
+    if (k > 0) {
+      LaunchTimer timer("near_kernel", st);
+      hipLaunchKernelGGL(near_kernel<B>, dim3(static_cast<unsigned>((dout + NearShape<B>::TM - 1) / NearShape<B>::TM)),
+                         dim3(256), 0, st, w, r, e_prev, dout, din, c0);
     }
-    kq_status s = check_launch("sweep_kernel");
-    if (s != KQ_OK) return s;
-    const int64_t rest = din - c0 - B;
-    if (rest <= 0) break;
+    if (k > 0 && (s = check_launch("near_kernel")) != KQ_OK) return s;
+    const int64_t rest = din - c0 - B;  // columns beyond this block
+    const int far_cols = (k > 0 && rest > 0) ? static_cast<int>((rest + kFT - 1) / kFT) : 0;
     {
-      LaunchTimer timer("trailing_kernel", st);
-      hipLaunchKernelGGL(trailing_kernel<B>, dim3(static_cast<unsigned>((rest + kTT - 1) / kTT),
-                                                  static_cast<unsigned>((dout + kTT - 1) / kTT)),
-                         dim3(256), 0, st, w, r, e, dout, din, c0);
+      LaunchTimer timer("step_kernel", st);
+      hipLaunchKernelGGL(step_kernel<B>, dim3(static_cast<unsigned>(n_sweep + far_cols * far_rows)), dim3(256), 0,
+                         st, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_prev, ebuf[k & 1],
+                         n_sweep, far_cols);
     }
-    s = check_launch("trailing_kernel");
-    if (s != KQ_OK) return s;
+    if ((s = check_launch("step_kernel")) != KQ_OK) return s;
   }
   return KQ_OK;
 }
@@ -325,7 +396,7 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
 
 size_t obs_workspace(int64_t dout, int64_t din, int block) {
   (void)din;
-  return align_up(size_t(dout) * block * sizeof(double), 256);
+  return align_up(2 * size_t(dout) * block * sizeof(double), 256);  // errors of two consecutive blocks
 }
 
 kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits, int group, int block,

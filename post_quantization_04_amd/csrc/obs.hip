@@ -106,9 +106,40 @@ struct SweepLds {
   double rinv[B];
 };
 
+// Group start at column j of the block: grid of columns [j, j + group) from
+// this row's current values (16-lane min / max reduction), stored by lane 0.
+template <int EPL>
+__device__ __forceinline__ void group_start(const double (&x)[EPL], int eo, int j, int l16, int group, int log2g,
+                                            int maxq, bool valid, int64_t row, int64_t ngroups, int64_t c0,
+                                            float* __restrict__ scales, uint8_t* __restrict__ zeros, double& s,
+                                            double& z, double& inv_s) {
+  double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int col = l16 + 16 * (eo + e);
+    if (col >= j && col < j + group) {
+      mn = fmin(mn, x[e]);
+      mx = fmax(mx, x[e]);
+    }
+  }
+  for (int o = 8; o > 0; o >>= 1) {
+    mn = fmin(mn, __shfl_xor(mn, o, 16));
+    mx = fmax(mx, __shfl_xor(mx, o, 16));
+  }
+  make_grid(mn, mx, maxq, s, z);
+  inv_s = 1.0 / s;
+  if (l16 == 0 && valid) {
+    const int64_t gi = row * ngroups + ((c0 + j) >> log2g);
+    scales[gi] = static_cast<float>(s);
+    zeros[gi] = static_cast<uint8_t>(z);
+  }
+}
+
 // Sweep of block [c0, c0 + B) for rows [16 wg, 16 wg + 16); writes the scaled
-// errors of the block to e_out [dout, B].
-template <int B>
+// errors of the block to e_out [dout, B]. Groups are powers of two dividing B:
+// with SG false (no group, or group >= 16) a group can start only at a
+// 16-column slice, so the grid code sits outside the unrolled column loop.
+template <int B, bool SG>
 __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, const float* __restrict__ r,
                            int64_t dout, int64_t din, int64_t c0, int bits, int group, uint8_t* __restrict__ codes,
                            float* __restrict__ scales, uint8_t* __restrict__ zeros, double* __restrict__ preround,
@@ -130,7 +161,8 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   const bool valid = row < dout;
   const int maxq = (1 << bits) - 1;
   const int64_t ngroups = group ? din / group : 1;
-  const int gmask = group - 1;  // group is a power of two dividing B
+  const int gmask = group - 1;
+  const int log2g = group ? __builtin_ctz(static_cast<unsigned>(group)) : 0;
 
   // x[e] holds column l16 + 16 (eo + e) of this lane's row: the slice being
   // swept is always x[0]; registers rotate down after each slice of 16 columns.
@@ -145,32 +177,15 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   double inv_s = 1.0 / s;
 
   for (int eo = 0; eo < EPL; ++eo) {
+    if (!SG && group > 0 && ((eo * 16) & gmask) == 0)
+      group_start<EPL>(x, eo, eo * 16, l16, group, log2g, maxq, valid, row, ngroups, c0, scales, zeros, s, z, inv_s);
     double tcur = 0.0, ecur = 0.0;
     int ccur = 0;
 #pragma unroll
     for (int lo = 0; lo < 16; ++lo) {
       const int j = eo * 16 + lo;
-      if (group > 0 && (j & gmask) == 0) {
-        double mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const int col = l16 + 16 * (eo + e);
-          if (col >= j && col < j + group) {
-            mn = fmin(mn, x[e]);
-            mx = fmax(mx, x[e]);
-          }
-        }
-        for (int o = 8; o > 0; o >>= 1) {
-          mn = fmin(mn, __shfl_xor(mn, o, 16));
-          mx = fmax(mx, __shfl_xor(mx, o, 16));
-        }
-        make_grid(mn, mx, maxq, s, z);
-        inv_s = 1.0 / s;
-        if (l16 == 0 && valid) {
-          scales[row * ngroups + (c0 + j) / group] = static_cast<float>(s);
-          zeros[row * ngroups + (c0 + j) / group] = static_cast<uint8_t>(z);
-        }
-      }
+      if (SG && (j & gmask) == 0)
+        group_start<EPL>(x, eo, j, l16, group, log2g, maxq, valid, row, ngroups, c0, scales, zeros, s, z, inv_s);
       // the rounding argument w * (1/s) is within two ulps of w / s
       const double wv = x[0];
       const double t = wv * inv_s;
@@ -345,8 +360,9 @@ union StepLds {
   TileLds<kFT, kFT> tl;
 };
 
-template <int B>
-__global__ __launch_bounds__(256) void step_kernel(double* __restrict__ w, const float* __restrict__ r,
+// Two waves per SIMD: a sweep workgroup and a far-update workgroup share each CU.
+template <int B, bool SG>
+__global__ __launch_bounds__(256, 2) void step_kernel(double* __restrict__ w, const float* __restrict__ r,
                                                    int64_t dout, int64_t din, int64_t c0, int bits, int group,
                                                    uint8_t* __restrict__ codes, float* __restrict__ scales,
                                                    uint8_t* __restrict__ zeros, double* __restrict__ preround,
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(256) void step_kernel(double* __restrict__ w, const
   __shared__ StepLds<B> sm;
   const int b = blockIdx.x;
   if (b < n_sweep) {
-    sweep_role<B>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_cur);
+    sweep_role<B, SG>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_cur);
     return;
   }
   const int t = b - n_sweep;
@@ -383,9 +399,10 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
     const int far_cols = (k > 0 && rest > 0) ? static_cast<int>((rest + kFT - 1) / kFT) : 0;
     {
       LaunchTimer timer("step_kernel", st);
-      hipLaunchKernelGGL(step_kernel<B>, dim3(static_cast<unsigned>(n_sweep + far_cols * far_rows)), dim3(256), 0,
-                         st, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_prev, ebuf[k & 1],
-                         n_sweep, far_cols);
+      const bool small_group = group > 0 && group < 16;  // groups that start inside a 16-column slice
+      auto kern = small_group ? step_kernel<B, true> : step_kernel<B, false>;
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_sweep + far_cols * far_rows)), dim3(256), 0, st, w, r, dout,
+                         din, c0, bits, group, codes, scales, zeros, preround, e_prev, ebuf[k & 1], n_sweep, far_cols);
     }
     if ((s = check_launch("step_kernel")) != KQ_OK) return s;
   }

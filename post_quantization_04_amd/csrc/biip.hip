@@ -7,18 +7,21 @@
 // factors act on different index parts, so their order does not matter; the
 // inverse applies Q_m^T and puts the sign flip last.
 //
-// A two-sided transform U_L M U_R^T needs every element of M on both sides,
-// so it takes two passes over HBM:
-//   * row pass: one workgroup per row, the whole row in LDS (up to 32768
-//     float32 values), transform along the row;
-//   * column pass: one workgroup per panel of C adjacent columns, the whole
-//     panel (n x C) in LDS, transform along the columns. Panels are handed
-//     to XCDs in contiguous runs so that neighbouring panels, which share
-//     cache lines, are read by the same L2.
-// Butterflies and mixes run in float64 in LDS whenever the vector (or panel)
-// fits (n <= 16384), else in float32; the intermediate between the passes is
-// float64; scales are applied in float64 at load or store, and outputs are
-// written in the destination precision.
+// A two-sided transform U_L M U_R^T needs every element of M on both sides:
+//   * row pass (the contiguous direction): one workgroup per row, the whole
+//     row in LDS (float64 up to 20480 values, float32 beyond), butterflies
+//     along the row and the odd-factor mix across its chunks;
+//   * column direction, two coalesced "digit" passes over tiles of 64 (or 32)
+//     contiguous columns: pass A takes the 64 rows that differ in the low six
+//     bits of the row index and applies that part of the Walsh-Hadamard
+//     transform; pass B takes the rows that differ in the remaining bits and
+//     in the odd factor (stride 64) and applies the rest of the transform and
+//     the mix. The Hadamard factors and the mix act on different index bits,
+//     so they commute; signs go first (forward) or last (inverse), scales at
+//     the first load or the last store. Each pass reads and writes whole tiles
+//     of 256 or 512 contiguous bytes per row, in place when possible.
+// Butterflies and mixes run in float64; the intermediate between passes is
+// float64; outputs are written in the destination precision.
 #include "kq_internal.h"
 
 namespace kq {
@@ -27,7 +30,8 @@ namespace {
 constexpr int kRowThreads = 512;
 constexpr int kColThreads = 256;
 constexpr size_t kLdsBudget = 160 * 1024;  // bytes of LDS a pass may use (all of a gfx950 CU)
-constexpr int kMaxOdd = 64;                // register array size for the odd-factor mix
+// Register array sizes for the odd-factor mix: instantiations for m = 1 (no
+// mix), m <= 7 and m <= 63 keep the common no-mix case light.
 
 struct Rot {
   const int8_t* signs;  // nullptr: no rotation on this axis
@@ -41,7 +45,6 @@ struct Rot {
 struct Scales {
   const double* row;    // per-row factor (nullable)
   const double* col;    // per-column factor (nullable)
-  int divide;           // use 1/s instead of s
   int at_store;         // apply when storing instead of when loading
 };
 
@@ -75,7 +78,7 @@ __device__ __forceinline__ double scale_factor(const Scales& sc, int64_t i, int6
   double f = 1.0;
   if (sc.row) f *= sc.row[i];
   if (sc.col) f *= sc.col[j];
-  return sc.divide ? 1.0 / f : f;
+  return f;
 }
 
 // Length-p Walsh-Hadamard butterflies on every chunk; element t of vector c at buf[t * C + c].
@@ -99,53 +102,53 @@ __device__ void fwht_lds(T* buf, int n, int log2c, int log2p) {
 }
 
 // y[a] = sum_k Q[a][k] v[k] (or Q[k][a]) across the m chunks, at each offset b and vector c.
-template <typename T>
-__device__ void mix_lds(T* buf, int log2c, int m, int log2p, const double* qs, int transpose) {
+// A thread holds one (b, c) column of m values in registers and writes the m
+// outputs back in place; Q is read from global memory at wave-uniform
+// addresses (scalar loads). The register array has the bucket size MB >= m.
+template <typename T, int MB>
+__device__ __forceinline__ void mix_column(T* base, int stride, int m, const double* __restrict__ q,
+                                           int transpose) {
+  T v[MB];
+#pragma unroll
+  for (int k = 0; k < MB; ++k) v[k] = (k < m) ? base[k * stride] : T(0);
+  const int qs_a = transpose ? 1 : m, qs_k = transpose ? m : 1;
+  for (int a = 0; a < m; ++a) {
+    const double* qa = q + a * qs_a;
+    double acc = 0.0;
+    // k >= m: v[k] is zero and the Q index is clamped inside the row, so the term adds zero
+#pragma unroll
+    for (int k = 0; k < MB; ++k) acc = fma(qa[(k < m ? k : m - 1) * qs_k], static_cast<double>(v[k]), acc);
+    base[a * stride] = static_cast<T>(acc);
+  }
+}
+
+template <typename T, int MB>
+__device__ void mix_lds(T* buf, int log2c, int m, int log2p, const double* q, int transpose) {
   const int C = 1 << log2c;
   const int p = 1 << log2p;
   const int total = p << log2c;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int c = idx & (C - 1);
     const int b = idx >> log2c;
-    T v[kMaxOdd];
-#pragma unroll
-    for (int a = 0; a < kMaxOdd; ++a) v[a] = (a < m) ? buf[((a * p + b) << log2c) + c] : T(0);
-    for (int a = 0; a < m; ++a) {
-      T acc = T(0);
-#pragma unroll
-      for (int k = 0; k < kMaxOdd; ++k) {
-        if (k < m) acc += static_cast<T>(transpose ? qs[k * m + a] : qs[a * m + k]) * v[k];
-      }
-      buf[((a * p + b) << log2c) + c] = acc;
-    }
+    mix_column<T, MB>(buf + (b << log2c) + c, p << log2c, m, q, transpose);
   }
   __syncthreads();
 }
 
-// float64 slots reserved for Q_m at the start of LDS.
-__host__ __device__ inline int q_slots(const Rot& rot) { return rot.signs ? rot.m * rot.m : 0; }
-
-__device__ void load_q(double* qs, const Rot& rot) {
-  if (!rot.signs || rot.m == 1) return;
-  for (int i = threadIdx.x; i < rot.m * rot.m; i += blockDim.x) qs[i] = rot.q[i];
-}
-
-template <typename T>
-__device__ void transform_lds(T* buf, int n, int log2c, const Rot& rot, const double* qs) {
+template <typename T, int MB>
+__device__ void transform_lds(T* buf, int n, int log2c, const Rot& rot) {
   if (!rot.signs) return;
   fwht_lds(buf, n, log2c, rot.log2p);
-  if (rot.m > 1) mix_lds(buf, log2c, rot.m, rot.log2p, qs, rot.inverse);
+  if (MB > 1 && rot.m > 1) mix_lds<T, MB>(buf, log2c, rot.m, rot.log2p, rot.q, rot.inverse);
 }
 
 // One row per workgroup; the transform runs along the row (length n).
-template <typename T, typename Src, typename Dst>
+template <typename T, typename Src, typename Dst, int MB>
 __global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ src, int64_t n,
                                                         Dst* __restrict__ dst, Rot rot, Scales sc) {
   extern __shared__ double smem[];
-  double* qs = smem;
-  T* buf = reinterpret_cast<T*>(smem + q_slots(rot));
+  T* buf = reinterpret_cast<T*>(smem);
   const int64_t row = blockIdx.x;
-  load_q(qs, rot);
   const Src* s = src + row * n;
   for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
     double v = load_elem<Src>(s + j);
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ 
     buf[j] = static_cast<T>(v);
   }
   __syncthreads();
-  transform_lds<T>(buf, static_cast<int>(n), 0, rot, qs);
+  transform_lds<T, MB>(buf, static_cast<int>(n), 0, rot);
   Dst* o = dst + row * n;
   const double os = rot.signs ? rot.out_scale : 1.0;
   for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
@@ -165,50 +168,199 @@ __global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ 
   }
 }
 
-// One panel of 2^log2c adjacent columns per workgroup; the transform runs
-// along the columns (length n_rows). Matrix is [n_rows, n_cols] row-major.
-template <typename T, typename Src, typename Dst>
-__global__ __launch_bounds__(kColThreads) void rot_cols(const Src* __restrict__ src, int64_t n_rows,
-                                                        int64_t n_cols, Dst* __restrict__ dst, int log2c,
-                                                        int per_xcd, Rot rot, Scales sc) {
+// One digit pass of the column direction on a [n_rows, n_cols] row-major
+// matrix, in LDS (used for odd factors above 31). Workgroup g x column tile
+// ct transforms the tile of rows r(a, i) = base(g) + a * sa + i * si
+// (a < mt, i < 2^lp) and columns
+// [ct * TC, ct * TC + TC): Walsh-Hadamard butterflies over i, then the odd
+// mix over a. Elementwise steps (sign, scales, 1 / sqrt(p)) are applied at
+// load or at store as the pass's position in the transform requires.
+struct ColPass {
+  int64_t n_rows, n_cols;
+  int lo, hishift;             // base row of group g: (g mod 2^lo) + (g / 2^lo) * 2^hishift
+  int64_t si, sa;
+  int lp, mt;
+  const double* q;             // mt x mt, row-major (mt > 1)
+  int transpose;               // apply Q^T
+  // elementwise factors (passes with OPS): value *= rl[r] * cl[j] at load and rs[r] * cs[j] at store
+  const double* rl;
+  const double* cl;
+  const double* rs;
+  const double* cs;
+};
+
+__device__ __forceinline__ int64_t group_base(const ColPass& cp, int64_t g) {
+  return (g & ((int64_t(1) << cp.lo) - 1)) + ((g >> cp.lo) << cp.hishift);
+}
+
+template <int TC>
+__device__ __forceinline__ int64_t tile_row(const ColPass& cp, int64_t base, int li) {
+  const int a = li >> cp.lp, i = li & ((1 << cp.lp) - 1);
+  return base + a * cp.sa + i * cp.si;
+}
+
+template <typename Src, typename Dst, int MB, int TC>
+__global__ __launch_bounds__(kColThreads) void col_pass(const Src* __restrict__ src, Dst* __restrict__ dst,
+                                                        ColPass cp) {
   extern __shared__ double smem[];
-  double* qs = smem;
-  T* buf = reinterpret_cast<T*>(smem + q_slots(rot));
-  const int C = 1 << log2c;
-  const int npanel = static_cast<int>((n_cols + C - 1) >> log2c);
-  const int panel = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (panel >= npanel) return;
-  const int64_t col0 = int64_t(panel) << log2c;
-  load_q(qs, rot);
-  const int64_t total = n_rows << log2c;
-  for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int c = static_cast<int>(idx & (C - 1));
-    const int64_t i = idx >> log2c;
-    const int64_t j = col0 + c;
+  constexpr int P = TC + 1;  // LDS row pitch (doubles)
+  double* tile = smem;
+  const int pt = 1 << cp.lp;
+  const int L = cp.mt << cp.lp;
+  const int nct = static_cast<int>((cp.n_cols + TC - 1) / TC);
+  const int64_t g = blockIdx.x / nct;
+  const int64_t c0 = int64_t(blockIdx.x % nct) * TC;
+  const int64_t base = group_base(cp, g);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < L * TC; e += kColThreads) {
+    const int c = e % TC, li = e / TC;
+    const int64_t r = tile_row<TC>(cp, base, li);
+    const int64_t j = c0 + c;
     double v = 0.0;
-    if (j < n_cols) {
-      v = load_elem<Src>(src + i * n_cols + j);
-      if (!sc.at_store) v *= scale_factor(sc, i, j);
-      if (rot.signs && !rot.inverse) v *= static_cast<double>(rot.signs[i]);
-    }
-    buf[idx] = static_cast<T>(v);
+    if (j < cp.n_cols) v = load_elem<Src>(src + r * cp.n_cols + j) * (cp.rl[r] * cp.cl[j]);
+    tile[li * P + c] = v;
   }
   __syncthreads();
-  transform_lds<T>(buf, static_cast<int>(n_rows), log2c, rot, qs);
-  const double os = rot.signs ? rot.out_scale : 1.0;
-  for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int c = static_cast<int>(idx & (C - 1));
-    const int64_t i = idx >> log2c;
-    const int64_t j = col0 + c;
-    if (j >= n_cols) continue;
-    double v = static_cast<double>(buf[idx]) * os;
-    if (rot.signs && rot.inverse) v *= static_cast<double>(rot.signs[i]);
-    if (sc.at_store) v *= scale_factor(sc, i, j);
-    store_elem<Dst>(dst + i * n_cols + j, v);
+  // butterflies over i for every (a, column)
+  const int half = (L * TC) >> 1;
+  for (int s = 0; s < cp.lp; ++s) {
+    const int h = 1 << s;
+    for (int idx = tid; idx < half; idx += kColThreads) {
+      const int c = idx % TC, pr = idx / TC;
+      const int a = pr >> (cp.lp - 1), ip = pr & ((pt >> 1) - 1);
+      const int i = ((ip >> s) << (s + 1)) + (ip & (h - 1));
+      double* x0 = tile + (a * pt + i) * P + c;
+      double* x1 = x0 + h * P;
+      const double u = *x0, w = *x1;
+      *x0 = u + w;
+      *x1 = u - w;
+    }
+    __syncthreads();
+  }
+  if (MB > 1 && cp.mt > 1) {
+    for (int idx = tid; idx < pt * TC; idx += kColThreads) {
+      const int c = idx % TC, i = idx / TC;
+      mix_column<double, MB>(tile + i * P + c, pt * P, cp.mt, cp.q, cp.transpose);
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < L * TC; e += kColThreads) {
+    const int c = e % TC, li = e / TC;
+    const int64_t r = tile_row<TC>(cp, base, li);
+    const int64_t j = c0 + c;
+    if (j >= cp.n_cols) continue;
+    store_elem<Dst>(dst + r * cp.n_cols + j, tile[li * P + c] * (cp.rs[r] * cp.cs[j]));
   }
 }
 
-__global__ void scales_kernel(const float* __restrict__ h, int64_t n, int enabled, double* __restrict__ s) {
+// Elementwise factors of a column transform: rows (r < n_rows) and columns
+// (j < n_cols) at load and at store. Load side: sigma_r (forward) and the
+// load-side scales; store side: 1 / sqrt(p), sigma_r (inverse) and the
+// store-side scales. Unused factors are ones.
+__global__ void factors_kernel(int64_t n_rows, int64_t n_cols, const int8_t* __restrict__ signs, int inverse,
+                               double out_scale, Scales sc, double* __restrict__ rl, double* __restrict__ cl,
+                               double* __restrict__ rs, double* __restrict__ cs) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n_rows) {
+    const double sg = signs ? static_cast<double>(signs[i]) : 1.0;
+    const double row = sc.row ? sc.row[i] : 1.0;
+    rl[i] = (signs && !inverse ? sg : 1.0) * (sc.at_store ? 1.0 : row);
+    rs[i] = out_scale * (signs && inverse ? sg : 1.0) * (sc.at_store ? row : 1.0);
+  }
+  if (i < n_cols) {
+    const double col = sc.col ? sc.col[i] : 1.0;
+    cl[i] = sc.at_store ? 1.0 : col;
+    cs[i] = sc.at_store ? col : 1.0;
+  }
+}
+
+// Column-direction passes in registers: one thread per column, 256
+// consecutive columns per workgroup (each wave reads 512 contiguous bytes
+// per row), the L rows of the thread's group held in registers; no LDS and
+// no barriers. col_fwht applies 2^LP-point butterflies over rows
+// base(g) + i * si; col_mix applies the odd mix over rows base(g) + a * sa.
+
+template <typename Src, typename Dst, int LP, bool OPS>
+__global__ __launch_bounds__(kColThreads) void col_fwht(const Src* __restrict__ src, Dst* __restrict__ dst,
+                                                        ColPass cp) {
+  constexpr int L = 1 << LP;
+  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
+  const int64_t g = blockIdx.x / ncb;
+  const int64_t j0 = (blockIdx.x % ncb) * kColThreads;  // uniform
+  const uint32_t lane = threadIdx.x;
+  const int64_t j = j0 + lane;
+  if (j >= cp.n_cols) return;
+  const int64_t base = group_base(cp, g);
+  const Src* s0 = src + j0;  // row r of this block: s0 + r * n_cols (uniform) + lane
+  Dst* d0 = dst + j0;
+  const double cl = OPS ? cp.cl[j] : 1.0, cs = OPS ? cp.cs[j] : 1.0;
+  double v[L];
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    const int64_t r = base + t * cp.si;
+    v[t] = load_elem<Src>(s0 + r * cp.n_cols + lane);
+    if (OPS) v[t] *= cp.rl[r] * cl;
+  }
+#pragma unroll
+  for (int st = 0; st < LP; ++st) {
+    const int h = 1 << st;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+      if (t & h) continue;
+      const double a = v[t], b = v[t + h];
+      v[t] = a + b;
+      v[t + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    const int64_t r = base + t * cp.si;
+    store_elem<Dst>(d0 + r * cp.n_cols + lane, OPS ? v[t] * (cp.rs[r] * cs) : v[t]);
+  }
+}
+
+template <typename Src, typename Dst, int MB, bool OPS>
+__global__ __launch_bounds__(kColThreads) void col_mix(const Src* __restrict__ src, Dst* __restrict__ dst,
+                                                       ColPass cp) {
+  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
+  const int64_t g = blockIdx.x / ncb;
+  const int64_t j0 = (blockIdx.x % ncb) * kColThreads;  // uniform
+  const uint32_t lane = threadIdx.x;
+  const int64_t j = j0 + lane;
+  if (j >= cp.n_cols) return;
+  const int64_t base = group_base(cp, g);
+  const Src* s0 = src + j0;
+  Dst* d0 = dst + j0;
+  const int m = cp.mt;
+  const double cl = OPS ? cp.cl[j] : 1.0, cs = OPS ? cp.cs[j] : 1.0;
+  double v[MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a) {
+    const int64_t r = base + a * cp.sa;
+    v[a] = 0.0;
+    if (a < m) {
+      v[a] = load_elem<Src>(s0 + r * cp.n_cols + lane);
+      if (OPS) v[a] *= cp.rl[r] * cl;
+    }
+  }
+  const int qs_a = cp.transpose ? 1 : m, qs_k = cp.transpose ? m : 1;
+#pragma unroll
+  for (int a = 0; a < MB; ++a) {
+    if (a < m) {
+      const double* qa = cp.q + a * qs_a;
+      double acc = 0.0;
+      // k >= m: v[k] is zero and the Q index is clamped inside the row, so the term adds zero
+#pragma unroll
+      for (int k = 0; k < MB; ++k) acc = fma(qa[(k < m ? k : m - 1) * qs_k], v[k], acc);
+      const int64_t r = base + a * cp.sa;
+      store_elem<Dst>(d0 + r * cp.n_cols + lane, OPS ? acc * (cp.rs[r] * cs) : acc);
+    }
+  }
+}
+
+// s_i = H_ii^(1/4) (1 where H_ii <= 0 or the side is off) and its reciprocal.
+__global__ void scales_kernel(const float* __restrict__ h, int64_t n, int enabled, double* __restrict__ s,
+                              double* __restrict__ inv) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   double v = 1.0;
@@ -217,6 +369,12 @@ __global__ void scales_kernel(const float* __restrict__ h, int64_t n, int enable
     if (d > 0.0) v = sqrt(sqrt(d));
   }
   s[i] = v;
+  inv[i] = 1.0 / v;
+}
+
+__global__ void recip_kernel(const double* __restrict__ s, int64_t n, double* __restrict__ inv) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) inv[i] = 1.0 / s[i];
 }
 
 Rot make_rot(const kq_rot* r, bool on, bool inverse) {
@@ -231,107 +389,239 @@ Rot make_rot(const kq_rot* r, bool on, bool inverse) {
   return o;
 }
 
-// Bytes of LDS for n elements of type T behind the Q_m slots.
+// Bytes of LDS for a row of n elements of type T.
 template <typename T>
-size_t lds_bytes(int64_t n, const Rot& rot) { return size_t(q_slots(rot)) * sizeof(double) + size_t(n) * sizeof(T); }
+size_t lds_bytes(int64_t n, const Rot&) { return size_t(n) * sizeof(T); }
 
 template <typename T>
 bool fits(int64_t n, const Rot& rot) { return lds_bytes<T>(n, rot) <= kLdsBudget; }
 
-// Widest power-of-two panel (<= 64 columns) whose n_rows x C block fits.
-template <typename T>
-int col_log2c(int64_t n_rows, const Rot& rot) {
-  int l = 0;
-  while (l < 6 && fits<T>(n_rows << (l + 1), rot)) ++l;
-  return l;
-}
-
-template <typename T, typename K>
+template <typename K>
 kq_status allow_lds(K kernel, const char* name) {
-  static bool done = false;
-  if (!done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(kLdsBudget)) != hipSuccess)
-      return fail(KQ_EDEVICE, "%s: cannot raise the LDS limit to %zu bytes", name, kLdsBudget);
-    done = true;
-  }
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(kLdsBudget)) != hipSuccess)
+    return fail(KQ_EDEVICE, "%s: cannot raise the LDS limit to %zu bytes", name, kLdsBudget);
   return KQ_OK;
 }
 
-template <typename Src, typename Dst>
-kq_status launch_rows(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
-  if (fits<double>(n, rot)) {
-    kq_status r = allow_lds<double>(&rot_rows<double, Src, Dst>, "rot_rows");
-    if (r != KQ_OK) return r;
-    {
-      LaunchTimer timer("rot_rows", st);
-      hipLaunchKernelGGL((rot_rows<double, Src, Dst>), dim3(static_cast<unsigned>(rows)), dim3(kRowThreads),
-                         lds_bytes<double>(n, rot), st, src, n, dst, rot, sc);
-    }
-  } else {
-    kq_status r = allow_lds<float>(&rot_rows<float, Src, Dst>, "rot_rows");
-    if (r != KQ_OK) return r;
-    {
-      LaunchTimer timer("rot_rows", st);
-      hipLaunchKernelGGL((rot_rows<float, Src, Dst>), dim3(static_cast<unsigned>(rows)), dim3(kRowThreads),
-                         lds_bytes<float>(n, rot), st, src, n, dst, rot, sc);
-    }
+// Mix bucket of an odd factor: 1 (none), 8 (m <= 7), 32 (m <= 31) or 64 (m <= 63).
+inline int mix_bucket(int m) { return m == 1 ? 1 : (m <= 7 ? 8 : (m <= 31 ? 32 : 64)); }
+
+template <typename T, typename Src, typename Dst, int MB>
+kq_status launch_rows_mb(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
+  auto kern = rot_rows<T, Src, Dst, MB>;
+  kq_status r = allow_lds(kern, "rot_rows");
+  if (r != KQ_OK) return r;
+  {
+    LaunchTimer timer("rot_rows", st);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds_bytes<T>(n, rot), st, src, n,
+                       dst, rot, sc);
   }
   return check_launch("rot_rows");
 }
 
 template <typename T, typename Src, typename Dst>
-kq_status launch_cols_t(const Src* src, int64_t n_rows, int64_t n_cols, Dst* dst, Rot rot, Scales sc,
-                        hipStream_t st) {
-  const int log2c = col_log2c<T>(n_rows, rot);
-  kq_status r = allow_lds<T>(&rot_cols<T, Src, Dst>, "rot_cols");
-  if (r != KQ_OK) return r;
-  const int npanel = static_cast<int>((n_cols + (1 << log2c) - 1) >> log2c);
-  const int per_xcd = (npanel + kXcds - 1) / kXcds;
-  {
-    LaunchTimer timer("rot_cols", st);
-    hipLaunchKernelGGL((rot_cols<T, Src, Dst>), dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kColThreads),
-                       lds_bytes<T>(n_rows << log2c, rot), st, src, n_rows, n_cols, dst, log2c, per_xcd, rot, sc);
+kq_status launch_rows_t(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
+  switch (mix_bucket(rot.signs ? rot.m : 1)) {
+    case 1: return launch_rows_mb<T, Src, Dst, 1>(src, rows, n, dst, rot, sc, st);
+    case 8: return launch_rows_mb<T, Src, Dst, 8>(src, rows, n, dst, rot, sc, st);
+    case 32: return launch_rows_mb<T, Src, Dst, 32>(src, rows, n, dst, rot, sc, st);
+    default: return launch_rows_mb<T, Src, Dst, 64>(src, rows, n, dst, rot, sc, st);
   }
-  return check_launch("rot_cols");
 }
 
 template <typename Src, typename Dst>
-kq_status launch_cols(const Src* src, int64_t n_rows, int64_t n_cols, Dst* dst, Rot rot, Scales sc,
-                      hipStream_t st) {
-  if (fits<double>(n_rows, rot)) return launch_cols_t<double>(src, n_rows, n_cols, dst, rot, sc, st);
-  return launch_cols_t<float>(src, n_rows, n_cols, dst, rot, sc, st);
+kq_status launch_rows(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
+  if (fits<double>(n, rot)) return launch_rows_t<double>(src, rows, n, dst, rot, sc, st);
+  return launch_rows_t<float>(src, rows, n, dst, rot, sc, st);
 }
 
-// U M U^T of a symmetric d x d float32 matrix, in place, through a float64 scratch copy.
-kq_status two_sided(float* h, int64_t d, const Rot& rot, const double* s, double* tmp, hipStream_t st) {
-  Scales in{s, s, 1, 0};
-  kq_status r = launch_rows<float, double>(h, d, d, tmp, rot, in, st);
+template <typename Src, typename Dst, int MB, int TC>
+kq_status launch_col_pass(const Src* src, Dst* dst, const ColPass& cp, int64_t groups, hipStream_t st) {
+  auto kern = col_pass<Src, Dst, MB, TC>;
+  kq_status r = allow_lds(kern, "col_pass");
   if (r != KQ_OK) return r;
-  return launch_cols<double, float>(tmp, d, d, h, rot, Scales{nullptr, nullptr, 0, 0}, st);
+  const int64_t L = int64_t(cp.mt) << cp.lp;
+  const size_t lds = size_t(L * (TC + 1)) * sizeof(double);
+  const int64_t nct = (cp.n_cols + TC - 1) / TC;
+  {
+    LaunchTimer timer("col_pass", st);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(groups * nct)), dim3(kColThreads), lds, st, src, dst, cp);
+  }
+  return check_launch("col_pass");
+}
+
+template <typename Src, typename Dst>
+kq_status col_pass_any(const Src* src, Dst* dst, const ColPass& cp, int64_t groups, hipStream_t st) {
+  const int64_t L = int64_t(cp.mt) << cp.lp;
+  const bool wide = L <= 128;  // 64-column tiles while the tile stays small, else 32
+  const int mb = mix_bucket(cp.mt);
+  if (wide) {
+    if (mb == 1) return launch_col_pass<Src, Dst, 1, 64>(src, dst, cp, groups, st);
+    if (mb == 8) return launch_col_pass<Src, Dst, 8, 64>(src, dst, cp, groups, st);
+    if (mb == 32) return launch_col_pass<Src, Dst, 32, 64>(src, dst, cp, groups, st);
+    return launch_col_pass<Src, Dst, 64, 64>(src, dst, cp, groups, st);
+  }
+  if (mb == 1) return launch_col_pass<Src, Dst, 1, 32>(src, dst, cp, groups, st);
+  if (mb == 8) return launch_col_pass<Src, Dst, 8, 32>(src, dst, cp, groups, st);
+  if (mb == 32) return launch_col_pass<Src, Dst, 32, 32>(src, dst, cp, groups, st);
+  return launch_col_pass<Src, Dst, 64, 32>(src, dst, cp, groups, st);
+}
+
+template <typename Src, typename Dst, int LP>
+kq_status launch_fwht(const Src* src, Dst* dst, const ColPass& cp, bool ops, hipStream_t st) {
+  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
+  const dim3 grid(static_cast<unsigned>((cp.n_rows >> LP) * ncb));
+  {
+    LaunchTimer timer("col_fwht", st);
+    if (ops) hipLaunchKernelGGL((col_fwht<Src, Dst, LP, true>), grid, dim3(kColThreads), 0, st, src, dst, cp);
+    else hipLaunchKernelGGL((col_fwht<Src, Dst, LP, false>), grid, dim3(kColThreads), 0, st, src, dst, cp);
+  }
+  return check_launch("col_fwht");
+}
+
+template <typename Src, typename Dst, int MB>
+kq_status launch_mix(const Src* src, Dst* dst, const ColPass& cp, bool ops, hipStream_t st) {
+  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
+  const dim3 grid(static_cast<unsigned>((cp.n_rows / cp.mt) * ncb));
+  {
+    LaunchTimer timer("col_mix", st);
+    if (ops) hipLaunchKernelGGL((col_mix<Src, Dst, MB, true>), grid, dim3(kColThreads), 0, st, src, dst, cp);
+    else hipLaunchKernelGGL((col_mix<Src, Dst, MB, false>), grid, dim3(kColThreads), 0, st, src, dst, cp);
+  }
+  return check_launch("col_mix");
+}
+
+// One pass; ops: apply the pass's factor arrays (cp.rl .. cp.cs point at ones where unused).
+template <typename Src, typename Dst>
+kq_status col_step(const Src* src, Dst* dst, const ColPass& cp, bool ops, hipStream_t st) {
+  if (cp.mt == 1) {
+    switch (cp.lp) {
+      case 0: return launch_fwht<Src, Dst, 0>(src, dst, cp, ops, st);
+      case 1: return launch_fwht<Src, Dst, 1>(src, dst, cp, ops, st);
+      case 2: return launch_fwht<Src, Dst, 2>(src, dst, cp, ops, st);
+      case 3: return launch_fwht<Src, Dst, 3>(src, dst, cp, ops, st);
+      case 4: return launch_fwht<Src, Dst, 4>(src, dst, cp, ops, st);
+      case 5: return launch_fwht<Src, Dst, 5>(src, dst, cp, ops, st);
+      default: return launch_fwht<Src, Dst, 6>(src, dst, cp, ops, st);
+    }
+  }
+  if (cp.mt <= 7) return launch_mix<Src, Dst, 8>(src, dst, cp, ops, st);
+  if (cp.mt <= 31) return launch_mix<Src, Dst, 32>(src, dst, cp, ops, st);
+  return col_pass_any<Src, Dst>(src, dst, cp, cp.n_rows / cp.mt, st);  // m in 33 .. 63: LDS tile (always applies)
+}
+
+// Column direction of U_rot applied to a [n_rows, n_cols] matrix (n_rows = n of the rotation):
+// butterfly passes over 6-bit chunks of the row index, then the odd mix, src -> mid -> ... -> dst
+// with mid a float64 buffer (it may equal src or dst when those are float64; every pass works
+// in place on its own elements). Signs and load-side scales go with the first pass; the
+// 1 / sqrt(p) factor, inverse signs and store-side scales with the last. fac holds
+// 2 n_rows + 2 n_cols doubles for the factor arrays; ones_ has max(n_rows, n_cols) ones.
+template <typename Src, typename Dst>
+kq_status launch_cols(const Src* src, int64_t n_rows, int64_t n_cols, Dst* dst, double* mid, const Rot& rot,
+                      Scales sc, double* fac, const double* ones, hipStream_t st) {
+  const int k = rot.signs ? rot.log2p : 0;
+  const int m = rot.signs ? rot.m : 1;
+  ColPass passes[4];
+  int np = 0;
+  for (int lo = 0; lo < k; lo += 6) {
+    ColPass cp{};
+    cp.lp = (k - lo < 6) ? k - lo : 6;
+    cp.lo = lo;
+    cp.hishift = lo + cp.lp;
+    cp.si = int64_t(1) << lo;
+    cp.mt = 1;
+    passes[np++] = cp;
+  }
+  if (m > 1) {
+    ColPass cp{};
+    cp.lp = 0;
+    cp.lo = k;  // groups enumerate the offset b inside a chunk
+    cp.hishift = k;
+    cp.si = 0;
+    cp.sa = int64_t(1) << k;
+    cp.mt = m;
+    cp.q = rot.q;
+    cp.transpose = rot.inverse;
+    passes[np++] = cp;
+  }
+  if (np == 0) {  // no rotation on this axis: one elementwise pass
+    ColPass cp{};
+    cp.mt = 1;
+    passes[np++] = cp;
+  }
+  double* rl = fac;
+  double* rs = fac + n_rows;
+  double* cl = fac + 2 * n_rows;
+  double* cs = cl + n_cols;
+  {
+    const int64_t n = n_rows > n_cols ? n_rows : n_cols;
+    LaunchTimer timer("factors_kernel", st);
+    hipLaunchKernelGGL(factors_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, n_rows,
+                       n_cols, rot.signs, rot.inverse, rot.signs ? rot.out_scale : 1.0, sc, rl, cl, rs, cs);
+  }
+  kq_status r = check_launch("factors_kernel");
+  if (r != KQ_OK) return r;
+  for (int i = 0; i < np; ++i) {
+    passes[i].n_rows = n_rows;
+    passes[i].n_cols = n_cols;
+    passes[i].rl = i == 0 ? rl : ones;
+    passes[i].cl = i == 0 ? cl : ones;
+    passes[i].rs = i == np - 1 ? rs : ones;
+    passes[i].cs = i == np - 1 ? cs : ones;
+  }
+  if (np == 1) return col_step<Src, Dst>(src, dst, passes[0], true, st);
+  r = col_step<Src, double>(src, mid, passes[0], true, st);
+  for (int i = 1; i + 1 < np && r == KQ_OK; ++i) r = col_step<double, double>(mid, mid, passes[i], false, st);
+  if (r != KQ_OK) return r;
+  return col_step<double, Dst>(mid, dst, passes[np - 1], true, st);
+}
+
+// U S^-1 M S^-1 U^T of a symmetric d x d float32 matrix, in place, through a float64 scratch copy.
+kq_status two_sided(float* h, int64_t d, const Rot& rot, const double* inv_s, double* tmp, double* fac,
+                    const double* ones, hipStream_t st) {
+  kq_status r = launch_rows<float, double>(h, d, d, tmp, rot, Scales{inv_s, inv_s, 0}, st);
+  if (r != KQ_OK) return r;
+  return launch_cols<double, float>(tmp, d, d, h, tmp, rot, Scales{nullptr, nullptr, 0}, fac, ones, st);
 }
 
 template <typename Src>
 kq_status forward_w(const Src* w, int64_t dout, int64_t din, double* w_out, const Rot& ri, const Rot& ro,
-                    const double* s_x, const double* s_g, double* tmp, hipStream_t st) {
-  const Scales ld{s_g, s_x, 0, 0};
-  const Scales none{nullptr, nullptr, 0, 0};
+                    const double* s_x, const double* s_g, double* tmp, double* fac, const double* ones,
+                    hipStream_t st) {
+  const Scales ld{s_g, s_x, 0};
+  const Scales none{nullptr, nullptr, 0};
   if (ri.signs && ro.signs) {
     kq_status r = launch_rows<Src, double>(w, dout, din, tmp, ri, ld, st);
     if (r != KQ_OK) return r;
-    return launch_cols<double, double>(tmp, dout, din, w_out, ro, none, st);
+    return launch_cols<double, double>(tmp, dout, din, w_out, tmp, ro, none, fac, ones, st);
   }
-  if (ro.signs) return launch_cols<Src, double>(w, dout, din, w_out, ro, ld, st);
+  if (ro.signs) return launch_cols<Src, double>(w, dout, din, w_out, w_out, ro, ld, fac, ones, st);
   return launch_rows<Src, double>(w, dout, din, w_out, ri, ld, st);  // ri may be "no rotation"
 }
 
 }  // namespace
 
-size_t biip_workspace(int64_t dout, int64_t din) {
+// Workspace layout: float64 intermediate (the largest matrix), 1 / s_x, 1 / s_g, ...
+static size_t biip_tmp_bytes(int64_t dout, int64_t din) {
   int64_t n = dout * din;
   if (din * din > n) n = din * din;
   if (dout * dout > n) n = dout * dout;
   return align_up(size_t(n) * sizeof(double), 256);
+}
+
+// ... then the factor arrays of a column transform (4 max(dout, din)) and max(dout, din) ones.
+static size_t biip_vec_bytes(int64_t n) { return align_up(size_t(n) * sizeof(double), 256); }
+
+size_t biip_workspace(int64_t dout, int64_t din) {
+  const int64_t nmax = dout > din ? dout : din;
+  return biip_tmp_bytes(dout, din) + biip_vec_bytes(din) + biip_vec_bytes(dout) + biip_vec_bytes(4 * nmax) +
+         biip_vec_bytes(nmax);
+}
+
+__global__ void ones_kernel(double* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 1.0;
 }
 
 kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double* w_out, float* h_x, float* h_g,
@@ -339,56 +629,79 @@ kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double
                    void* ws, hipStream_t st) {
   const bool inp = flags & KQ_BIIP_INPUT, out = flags & KQ_BIIP_OUTPUT;
   const bool scale = flags & KQ_BIIP_SCALE, inverse = flags & KQ_BIIP_INVERSE;
-  double* tmp = static_cast<double*>(ws);
+  const int64_t nmax = dout > din ? dout : din;
+  char* p = static_cast<char*>(ws);
+  double* tmp = reinterpret_cast<double*>(p);
+  p += biip_tmp_bytes(dout, din);
+  double* inv_x = reinterpret_cast<double*>(p);
+  p += biip_vec_bytes(din);
+  double* inv_g = reinterpret_cast<double*>(p);
+  p += biip_vec_bytes(dout);
+  double* fac = reinterpret_cast<double*>(p);
+  p += biip_vec_bytes(4 * nmax);
+  double* ones = reinterpret_cast<double*>(p);
   kq_status r;
+  {
+    LaunchTimer timer("ones_kernel", st);
+    hipLaunchKernelGGL(ones_kernel, dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, st, ones, nmax);
+  }
+  if ((r = check_launch("ones_kernel")) != KQ_OK) return r;
   if (inverse) {
+    {
+      LaunchTimer timer("recip_kernel", st);
+      hipLaunchKernelGGL(recip_kernel, dim3(static_cast<unsigned>((din + 255) / 256)), dim3(256), 0, st, s_x, din,
+                         inv_x);
+      hipLaunchKernelGGL(recip_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st, s_g, dout,
+                         inv_g);
+    }
+    if ((r = check_launch("recip_kernel")) != KQ_OK) return r;
     // W = S_G^-1 U_G^T W'' U_X S_X^-1: input-side rows first, then output-side columns;
     // the row scale must follow the output-side rotation, which mixes rows.
     const Rot ri = make_rot(rot_in, inp, true), ro = make_rot(rot_out, out, true);
     const double* w2 = static_cast<const double*>(w);
     if (out) {
-      r = launch_rows<double, double>(w2, dout, din, tmp, ri, Scales{nullptr, s_x, 1, 1}, st);
+      r = launch_rows<double, double>(w2, dout, din, tmp, ri, Scales{nullptr, inv_x, 1}, st);
       if (r != KQ_OK) return r;
-      return launch_cols<double, double>(tmp, dout, din, w_out, ro, Scales{s_g, nullptr, 1, 1}, st);
+      return launch_cols<double, double>(tmp, dout, din, w_out, tmp, ro, Scales{inv_g, nullptr, 1}, fac, ones, st);
     }
-    return launch_rows<double, double>(w2, dout, din, w_out, ri, Scales{s_g, s_x, 1, 1}, st);
+    return launch_rows<double, double>(w2, dout, din, w_out, ri, Scales{inv_g, inv_x, 1}, st);
   }
   // scales come from the raw diagonals, before H_X and H_G are transformed in place
   {
     LaunchTimer timer("scales_kernel", st);
     hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((din + 255) / 256)), dim3(256), 0, st, h_x, din,
-                       (inp && scale) ? 1 : 0, s_x);
+                       (inp && scale) ? 1 : 0, s_x, inv_x);
   }
   if ((r = check_launch("scales_kernel")) != KQ_OK) return r;
   if (h_g || (out && scale)) {
     {
       LaunchTimer timer("scales_kernel", st);
       hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st, h_g,
-                         dout, (out && scale) ? 1 : 0, s_g);
+                         dout, (out && scale) ? 1 : 0, s_g, inv_g);
     }
   } else {
     {
       LaunchTimer timer("scales_kernel", st);
       hipLaunchKernelGGL(scales_kernel, dim3(static_cast<unsigned>((dout + 255) / 256)), dim3(256), 0, st,
-                         static_cast<const float*>(nullptr), dout, 0, s_g);
+                         static_cast<const float*>(nullptr), dout, 0, s_g, inv_g);
     }
   }
   if ((r = check_launch("scales_kernel")) != KQ_OK) return r;
   const Rot ri = make_rot(rot_in, inp, false), ro = make_rot(rot_out, out, false);
   switch (w_dtype) {
     case KQ_BF16:
-      r = forward_w(static_cast<const uint16_t*>(w), dout, din, w_out, ri, ro, s_x, s_g, tmp, st);
+      r = forward_w(static_cast<const uint16_t*>(w), dout, din, w_out, ri, ro, s_x, s_g, tmp, fac, ones, st);
       break;
     case KQ_F32:
-      r = forward_w(static_cast<const float*>(w), dout, din, w_out, ri, ro, s_x, s_g, tmp, st);
+      r = forward_w(static_cast<const float*>(w), dout, din, w_out, ri, ro, s_x, s_g, tmp, fac, ones, st);
       break;
     default:
-      r = forward_w(static_cast<const double*>(w), dout, din, w_out, ri, ro, s_x, s_g, tmp, st);
+      r = forward_w(static_cast<const double*>(w), dout, din, w_out, ri, ro, s_x, s_g, tmp, fac, ones, st);
       break;
   }
   if (r != KQ_OK) return r;
-  if (inp && (r = two_sided(h_x, din, ri, s_x, tmp, st)) != KQ_OK) return r;
-  if (out && (r = two_sided(h_g, dout, ro, s_g, tmp, st)) != KQ_OK) return r;
+  if (inp && (r = two_sided(h_x, din, ri, inv_x, tmp, fac, ones, st)) != KQ_OK) return r;
+  if (out && (r = two_sided(h_g, dout, ro, inv_g, tmp, fac, ones, st)) != KQ_OK) return r;
   return KQ_OK;
 }
 

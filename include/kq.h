@@ -186,7 +186,9 @@ kq_status kq_allocate_bits(const double* score, const int64_t* n_params, int32_t
  *   rot_out  HOST pointer to the output-side spec (n = dout); used with KQ_BIIP_OUTPUT
  *   s_x, s_g device float64 [din], [dout]; written (forward) or read (inverse)
  *   ws       scratch of kq_workspace_size(KQ_OP_BIIP, dout, din, 0) bytes
- * Butterflies run in float32 on chip; scales and the final values in float64.
+ * Butterflies, mixes and scales run in float64 on chip; values between the
+ * passes of the transform are stored in float32 (relative error near 1e-7 in
+ * W'', the precision the column sweep needs); w_out is written in float64.
  */
 kq_status kq_biip_rotate(const void* w, int32_t w_dtype, int64_t dout, int64_t din, double* w_out,
                          float* h_x, float* h_g, const kq_rot* rot_in, const kq_rot* rot_out,

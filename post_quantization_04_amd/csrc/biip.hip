@@ -8,27 +8,33 @@
 // inverse applies Q_m^T and puts the sign flip last.
 //
 // A two-sided transform U_L M U_R^T needs every element of M on both sides:
-//   * row pass (the contiguous direction): one workgroup per row, the whole
-//     row in LDS (float64 up to 20480 values, float32 beyond), butterflies
-//     along the row and the odd-factor mix across its chunks;
-//   * column direction, two coalesced "digit" passes over tiles of 64 (or 32)
-//     contiguous columns: pass A takes the 64 rows that differ in the low six
-//     bits of the row index and applies that part of the Walsh-Hadamard
-//     transform; pass B takes the rows that differ in the remaining bits and
-//     in the odd factor (stride 64) and applies the rest of the transform and
-//     the mix. The Hadamard factors and the mix act on different index bits,
-//     so they commute; signs go first (forward) or last (inverse), scales at
-//     the first load or the last store. Each pass reads and writes whole tiles
-//     of 256 or 512 contiguous bytes per row, in place when possible.
-// Butterflies and mixes run in float64; the intermediate between passes is
-// float64; outputs are written in the destination precision.
+//   * column direction: "digit" passes, one thread per column and 256
+//     consecutive columns per workgroup; a pass holds the 2^6 rows that differ
+//     in six bits of the row index in registers and applies that part of the
+//     Walsh-Hadamard transform, a last pass applies the odd-factor mix across
+//     the rows at stride p. The Hadamard factors and the mix act on different
+//     index bits, so they commute. Per-row and per-column factors cost one
+//     uniform and one per-thread load here, so these passes carry the
+//     diagonal scales of both sides;
+//   * row direction (contiguous): one workgroup per row; radix-16 butterflies
+//     in registers over windows of four index bits, the row staged in LDS
+//     between windows (two exchanges for a 4096-long row), the odd mix on the
+//     staged row. This pass carries only the signs of its side.
+// Forward: column passes first (signs and scales at their first load), then
+// the row pass (signs at load, 1 / sqrt(p) at store). Inverse: row pass first
+// (signs at store), then the column passes (signs and scales at the last store).
+// Butterflies and mixes run in float64 registers; values between passes are
+// float32 (the precision of H and of the rotated weight the sweep needs); the
+// final W'' is written in float64.
 #include "kq_internal.h"
 
 namespace kq {
 namespace {
 
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 512;   // rot_rows (general row kernel)
+constexpr int kFwThreads = 256;    // row_fwht
 constexpr int kColThreads = 256;
+constexpr size_t kRowLdsF64 = 64 * 1024;  // row_fwht keeps float64 in LDS up to this size
 constexpr size_t kLdsBudget = 160 * 1024;  // bytes of LDS a pass may use (all of a gfx950 CU)
 // Register array sizes for the odd-factor mix: instantiations for m = 1 (no
 // mix), m <= 7 and m <= 63 keep the common no-mix case light.
@@ -72,6 +78,69 @@ __device__ __forceinline__ void store_elem<float>(float* p, double v) {
 template <>
 __device__ __forceinline__ void store_elem<double>(double* p, double v) {
   *p = v;
+}
+
+// Buffer-resource access: a uniform base (SGPRs) plus a 32-bit per-lane and a
+// 32-bit uniform byte offset, so that a thread's many row accesses share one
+// address register. Reads at or past num_records return 0 and writes there are
+// dropped.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(n),
+                                           0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ double bload(Rsrc r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ double bload<uint16_t>(Rsrc r, uint32_t voff, uint32_t soff) {
+  return static_cast<double>(
+      __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16));
+}
+template <>
+__device__ __forceinline__ double bload<float>(Rsrc r, uint32_t voff, uint32_t soff) {
+  return static_cast<double>(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0)));
+}
+template <>
+__device__ __forceinline__ double bload<double>(Rsrc r, uint32_t voff, uint32_t soff) {
+  const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return __hiloint2double(static_cast<int>(u[1]), static_cast<int>(u[0]));
+}
+
+template <typename T>
+__device__ __forceinline__ T bload_raw(Rsrc r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ uint16_t bload_raw<uint16_t>(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ float bload_raw<float>(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ double bload_raw<double>(Rsrc r, uint32_t voff, uint32_t soff) {
+  return bload<double>(r, voff, soff);
+}
+__device__ __forceinline__ double widen(uint16_t x) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(x) << 16));
+}
+__device__ __forceinline__ double widen(float x) { return static_cast<double>(x); }
+__device__ __forceinline__ double widen(double x) { return x; }
+
+template <typename T>
+__device__ __forceinline__ void bstore(Rsrc r, uint32_t voff, uint32_t soff, double v);
+template <>
+__device__ __forceinline__ void bstore<float>(Rsrc r, uint32_t voff, uint32_t soff, double v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(static_cast<float>(v)), r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ void bstore<double>(Rsrc r, uint32_t voff, uint32_t soff, double v) {
+  using u2 = unsigned int __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+  u2 u;
+  u[0] = static_cast<unsigned>(__double2loint(v));
+  u[1] = static_cast<unsigned>(__double2hiint(v));
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, 0);
 }
 
 __device__ __forceinline__ double scale_factor(const Scales& sc, int64_t i, int64_t j) {
@@ -144,12 +213,12 @@ __device__ void transform_lds(T* buf, int n, int log2c, const Rot& rot) {
 
 // One row per workgroup; the transform runs along the row (length n).
 template <typename T, typename Src, typename Dst, int MB>
-__global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ src, int64_t n,
-                                                        Dst* __restrict__ dst, Rot rot, Scales sc) {
+__global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ src, int64_t lds, int64_t n,
+                                                        Dst* __restrict__ dst, int64_t ldd, Rot rot, Scales sc) {
   extern __shared__ double smem[];
   T* buf = reinterpret_cast<T*>(smem);
   const int64_t row = blockIdx.x;
-  const Src* s = src + row * n;
+  const Src* s = src + row * lds;
   for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
     double v = load_elem<Src>(s + j);
     if (!sc.at_store) v *= scale_factor(sc, row, j);
@@ -158,13 +227,171 @@ __global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ 
   }
   __syncthreads();
   transform_lds<T, MB>(buf, static_cast<int>(n), 0, rot);
-  Dst* o = dst + row * n;
+  Dst* o = dst + row * ldd;
   const double os = rot.signs ? rot.out_scale : 1.0;
   for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
     double v = static_cast<double>(buf[j]) * os;
     if (rot.signs && rot.inverse) v *= static_cast<double>(rot.signs[j]);
     if (sc.at_store) v *= scale_factor(sc, row, j);
     store_elem<Dst>(o + j, v);
+  }
+}
+
+// Row direction for rows of n = m * 2^k values with k >= 8 (every chunk holds
+// whole groups of 16). Window w covers index bits [lo, lo + 4) of the offset
+// inside a chunk; a thread takes a group of the 16 offsets that differ only in
+// those bits and applies the four radix-2 stages in registers. Window 0 reads
+// 16 contiguous values straight from global memory, the last window writes
+// straight to global memory (consecutive threads, consecutive offsets); the
+// row is staged in LDS in between, with one pad slot per 16 values so that
+// strided groups spread over the banks. When k is not a multiple of 4 the
+// last window is moved down to [k - 4, k) and skips the stages already done.
+struct RowFw {
+  int k;                 // log2 p
+  int m;                 // odd factor
+  const double* q;       // m x m, row-major (m > 1)
+  int transpose;         // apply Q^T
+  const int8_t* signs;   // [n], along the row
+  int inverse;           // signs (and factors) at store instead of at load
+  double out_scale;      // 1 / sqrt(p)
+  const double* rowf;    // per-row factor (nullable), same side as the signs
+  const double* colf;    // per-column factor (nullable), same side as the signs
+};
+
+__device__ __forceinline__ int lpad(int e) { return e + (e >> 4); }
+
+template <typename Src>
+__device__ __forceinline__ void load16(const Src* p, double v[16]);
+template <>
+__device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, double v[16]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  const uint4 a = q[0], b = q[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = static_cast<double>(__uint_as_float(w[i] << 16));
+    v[2 * i + 1] = static_cast<double>(__uint_as_float(w[i] & 0xffff0000u));
+  }
+}
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, double v[16]) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = q[i];
+    v[4 * i] = f.x;
+    v[4 * i + 1] = f.y;
+    v[4 * i + 2] = f.z;
+    v[4 * i + 3] = f.w;
+  }
+}
+template <>
+__device__ __forceinline__ void load16<double>(const double* p, double v[16]) {
+  const double2* q = reinterpret_cast<const double2*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double2 f = q[i];
+    v[2 * i] = f.x;
+    v[2 * i + 1] = f.y;
+  }
+}
+
+// Bit i set: sign i of the 16 at p is negative (each sign byte is +1 or -1).
+__device__ __forceinline__ uint32_t neg_mask16(const int8_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m |= ((w[i >> 2] >> (8 * (i & 3) + 7)) & 1u) << i;
+  return m;
+}
+
+// x with its sign flipped when bit b of m is set.
+__device__ __forceinline__ double flip(double x, uint32_t m, int b) {
+  const int hi = __double2hiint(x) ^ static_cast<int>(((m >> b) & 1u) << 31);
+  return __hiloint2double(hi, __double2loint(x));
+}
+
+// Radix-2 stages j = first .. 3 on a group of 16 (element t differs from t + 2^j in bit j).
+__device__ __forceinline__ void bfly16(double v[16], int first) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j >= first) {
+      const int h = 1 << j;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (t & h) continue;
+        const double a = v[t], b = v[t + h];
+        v[t] = a + b;
+        v[t + h] = a - b;
+      }
+    }
+  }
+}
+
+template <typename T, typename Src, typename Dst, int MB>
+__global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict__ src, int64_t lds, int64_t n,
+                                                       Dst* __restrict__ dst, int64_t ldd, RowFw rf) {
+  extern __shared__ double smem[];
+  T* buf = reinterpret_cast<T*>(smem);
+  const int64_t row = blockIdx.x;
+  const int k = rf.k, kg = k - 4;
+  const int ng = static_cast<int>(n >> 4);
+  const Src* s = src + row * lds;
+  Dst* o = dst + row * ldd;
+  const double rowf = rf.rowf ? rf.rowf[row] : 1.0;
+  for (int g = threadIdx.x; g < ng; g += kFwThreads) {
+    const int e0 = g << 4;
+    double v[16];
+    load16<Src>(s + e0, v);
+    if (!rf.inverse) {
+      const uint32_t neg = neg_mask16(rf.signs + e0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = flip(v[i] * (rf.colf ? rowf * rf.colf[e0 + i] : rowf), neg, i);
+    }
+    bfly16(v, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[lpad(e0 + i)] = static_cast<T>(v[i]);
+  }
+  __syncthreads();
+  if (MB > 1 && rf.m > 1) {
+    const int p = 1 << k;
+    for (int b = threadIdx.x; b < p; b += kFwThreads)
+      mix_column<T, MB>(buf + lpad(b), p + (p >> 4), rf.m, rf.q, rf.transpose);
+    __syncthreads();
+  }
+  const Rsrc ro = make_rsrc(o, uint64_t(n) * sizeof(Dst));
+  for (int lo = 4; lo < k; lo += 4) {
+    const bool last = lo + 4 >= k;
+    const int wlo = last ? k - 4 : lo;   // >= 4: a group's LDS slots are a0 + i * lstep
+    const int first = lo - wlo;
+    const int lstep = (1 << wlo) + (1 << (wlo - 4));
+    const uint32_t gstep = uint32_t(sizeof(Dst)) << wlo;
+    for (int g = threadIdx.x; g < ng; g += kFwThreads) {
+      const int a = g >> kg, idx = g & ((1 << kg) - 1);
+      const int e0 = (a << k) + (idx & ((1 << wlo) - 1)) + ((idx >> wlo) << (wlo + 4));
+      T* b0 = buf + lpad(e0);
+      double v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = static_cast<double>(b0[i * lstep]);
+      bfly16(v, first);
+      if (!last) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b0[i * lstep] = static_cast<T>(v[i]);
+      } else {
+        const uint32_t vo = uint32_t(e0) * uint32_t(sizeof(Dst));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          double x = v[i] * rf.out_scale;
+          if (rf.inverse) {
+            const int e = e0 + (i << wlo);
+            x *= static_cast<double>(rf.signs[e]) * (rf.colf ? rowf * rf.colf[e] : rowf);
+          }
+          bstore<Dst>(ro, vo, i * gstep, x);
+        }
+      }
+    }
+    if (!last) __syncthreads();
   }
 }
 
@@ -177,6 +404,7 @@ __global__ __launch_bounds__(kRowThreads) void rot_rows(const Src* __restrict__ 
 // load or at store as the pass's position in the transform requires.
 struct ColPass {
   int64_t n_rows, n_cols;
+  int64_t lds, ldd;            // row pitch (elements) of the source and of the destination
   int lo, hishift;             // base row of group g: (g mod 2^lo) + (g / 2^lo) * 2^hishift
   int64_t si, sa;
   int lp, mt;
@@ -217,7 +445,7 @@ __global__ __launch_bounds__(kColThreads) void col_pass(const Src* __restrict__ 
     const int64_t r = tile_row<TC>(cp, base, li);
     const int64_t j = c0 + c;
     double v = 0.0;
-    if (j < cp.n_cols) v = load_elem<Src>(src + r * cp.n_cols + j) * (cp.rl[r] * cp.cl[j]);
+    if (j < cp.n_cols) v = load_elem<Src>(src + r * cp.lds + j) * (cp.rl[r] * cp.cl[j]);
     tile[li * P + c] = v;
   }
   __syncthreads();
@@ -249,7 +477,7 @@ __global__ __launch_bounds__(kColThreads) void col_pass(const Src* __restrict__ 
     const int64_t r = tile_row<TC>(cp, base, li);
     const int64_t j = c0 + c;
     if (j >= cp.n_cols) continue;
-    store_elem<Dst>(dst + r * cp.n_cols + j, tile[li * P + c] * (cp.rs[r] * cp.cs[j]));
+    store_elem<Dst>(dst + r * cp.ldd + j, tile[li * P + c] * (cp.rs[r] * cp.cs[j]));
   }
 }
 
@@ -280,42 +508,80 @@ __global__ void factors_kernel(int64_t n_rows, int64_t n_cols, const int8_t* __r
 // no barriers. col_fwht applies 2^LP-point butterflies over rows
 // base(g) + i * si; col_mix applies the odd mix over rows base(g) + a * sa.
 
-template <typename Src, typename Dst, int LP, bool OPS>
+// Value of x in lane l of the wave.
+__device__ __forceinline__ double lane_value(double x, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), l);
+  return __hiloint2double(hi, lo);
+}
+
+// Launches cover column blocks [cb0, cb0 + ncb) of every group. PARTIAL: the
+// one block that runs past the last column; its extra lanes leave at once.
+template <typename Src, typename Dst, int LP, bool OPS, bool PARTIAL>
 __global__ __launch_bounds__(kColThreads) void col_fwht(const Src* __restrict__ src, Dst* __restrict__ dst,
-                                                        ColPass cp) {
+                                                        ColPass cp, int64_t cb0, int64_t ncb) {
   constexpr int L = 1 << LP;
-  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
   const int64_t g = blockIdx.x / ncb;
-  const int64_t j0 = (blockIdx.x % ncb) * kColThreads;  // uniform
+  const int64_t j0 = (cb0 + blockIdx.x % ncb) * kColThreads;  // uniform
   const uint32_t lane = threadIdx.x;
-  const int64_t j = j0 + lane;
-  if (j >= cp.n_cols) return;
+  if (PARTIAL && j0 + lane >= cp.n_cols) return;
   const int64_t base = group_base(cp, g);
-  const Src* s0 = src + j0;  // row r of this block: s0 + r * n_cols (uniform) + lane
-  Dst* d0 = dst + j0;
-  const double cl = OPS ? cp.cl[j] : 1.0, cs = OPS ? cp.cs[j] : 1.0;
-  double v[L];
-#pragma unroll
-  for (int t = 0; t < L; ++t) {
-    const int64_t r = base + t * cp.si;
-    v[t] = load_elem<Src>(s0 + r * cp.n_cols + lane);
-    if (OPS) v[t] *= cp.rl[r] * cl;
+  // rows base + t * si of this block: buffer bases at row base, byte offsets t * step + lane * element size
+  const Rsrc rs_src = make_rsrc(src + base * cp.lds + j0, uint64_t((L - 1) * cp.si * cp.lds + kColThreads) * sizeof(Src));
+  const Rsrc rs_dst = make_rsrc(dst + base * cp.ldd + j0, uint64_t((L - 1) * cp.si * cp.ldd + kColThreads) * sizeof(Dst));
+  const uint32_t sstep = static_cast<uint32_t>(cp.si * cp.lds * int64_t(sizeof(Src)));
+  const uint32_t dstep = static_cast<uint32_t>(cp.si * cp.ldd * int64_t(sizeof(Dst)));
+  const uint32_t lo_s = lane * uint32_t(sizeof(Src)), lo_d = lane * uint32_t(sizeof(Dst));
+  // per-row factors: in full blocks lane t of each wave holds row t's, broadcast with readlane
+  const int wl = static_cast<int>(lane & 63);
+  double rl = 1.0, rs = 1.0, cl = 1.0, cs = 1.0;
+  if (OPS) {
+    if (!PARTIAL && wl < L) {
+      rl = cp.rl[base + wl * cp.si];
+      rs = cp.rs[base + wl * cp.si];
+    }
+    cl = cp.cl[j0 + lane];
+    cs = cp.cs[j0 + lane];
   }
+  // loads land as raw values (one register each for 16/32-bit types); each half of the
+  // rows is then widened and transformed on its own before the last stage joins them
+  Src raw[L];
 #pragma unroll
-  for (int st = 0; st < LP; ++st) {
-    const int h = 1 << st;
+  for (int t = 0; t < L; ++t) raw[t] = bload_raw<Src>(rs_src, lo_s, t * sstep);
+  double v[L];
+  constexpr int H = L > 1 ? L / 2 : 1;
 #pragma unroll
-    for (int t = 0; t < L; ++t) {
-      if (t & h) continue;
-      const double a = v[t], b = v[t + h];
+  for (int half = 0; half < (L > 1 ? 2 : 1); ++half) {
+#pragma unroll
+    for (int t = half * H; t < half * H + H; ++t) {
+      v[t] = widen(raw[t]);
+      if (OPS) v[t] *= (PARTIAL ? cp.rl[base + t * cp.si] : lane_value(rl, t)) * cl;
+    }
+#pragma unroll
+    for (int st = 0; st + 1 < LP; ++st) {
+      const int h = 1 << st;
+#pragma unroll
+      for (int t = half * H; t < half * H + H; ++t) {
+        if (t & h) continue;
+        const double a = v[t], b = v[t + h];
+        v[t] = a + b;
+        v[t + h] = a - b;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (LP > 0) {
+#pragma unroll
+    for (int t = 0; t < H; ++t) {
+      const double a = v[t], b = v[t + H];
       v[t] = a + b;
-      v[t + h] = a - b;
+      v[t + H] = a - b;
     }
   }
 #pragma unroll
   for (int t = 0; t < L; ++t) {
-    const int64_t r = base + t * cp.si;
-    store_elem<Dst>(d0 + r * cp.n_cols + lane, OPS ? v[t] * (cp.rs[r] * cs) : v[t]);
+    const double f = OPS ? (PARTIAL ? cp.rs[base + t * cp.si] : lane_value(rs, t)) * cs : 1.0;
+    bstore<Dst>(rs_dst, lo_d, t * dstep, OPS ? v[t] * f : v[t]);
   }
 }
 
@@ -339,7 +605,7 @@ __global__ __launch_bounds__(kColThreads) void col_mix(const Src* __restrict__ s
     const int64_t r = base + a * cp.sa;
     v[a] = 0.0;
     if (a < m) {
-      v[a] = load_elem<Src>(s0 + r * cp.n_cols + lane);
+      v[a] = load_elem<Src>(s0 + r * cp.lds + lane);
       if (OPS) v[a] *= cp.rl[r] * cl;
     }
   }
@@ -353,7 +619,7 @@ __global__ __launch_bounds__(kColThreads) void col_mix(const Src* __restrict__ s
 #pragma unroll
       for (int k = 0; k < MB; ++k) acc = fma(qa[(k < m ? k : m - 1) * qs_k], v[k], acc);
       const int64_t r = base + a * cp.sa;
-      store_elem<Dst>(d0 + r * cp.n_cols + lane, OPS ? acc * (cp.rs[r] * cs) : acc);
+      store_elem<Dst>(d0 + r * cp.ldd + lane, OPS ? acc * (cp.rs[r] * cs) : acc);
     }
   }
 }
@@ -408,32 +674,77 @@ kq_status allow_lds(K kernel, const char* name) {
 inline int mix_bucket(int m) { return m == 1 ? 1 : (m <= 7 ? 8 : (m <= 31 ? 32 : 64)); }
 
 template <typename T, typename Src, typename Dst, int MB>
-kq_status launch_rows_mb(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
+kq_status launch_rows_mb(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, Rot rot,
+                         Scales sc, hipStream_t st) {
   auto kern = rot_rows<T, Src, Dst, MB>;
   kq_status r = allow_lds(kern, "rot_rows");
   if (r != KQ_OK) return r;
   {
     LaunchTimer timer("rot_rows", st);
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds_bytes<T>(n, rot), st, src, n,
-                       dst, rot, sc);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds_bytes<T>(n, rot), st, src, lds,
+                       n, dst, ldd, rot, sc);
   }
   return check_launch("rot_rows");
 }
 
 template <typename T, typename Src, typename Dst>
-kq_status launch_rows_t(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
+kq_status launch_rows_t(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, Rot rot,
+                        Scales sc, hipStream_t st) {
   switch (mix_bucket(rot.signs ? rot.m : 1)) {
-    case 1: return launch_rows_mb<T, Src, Dst, 1>(src, rows, n, dst, rot, sc, st);
-    case 8: return launch_rows_mb<T, Src, Dst, 8>(src, rows, n, dst, rot, sc, st);
-    case 32: return launch_rows_mb<T, Src, Dst, 32>(src, rows, n, dst, rot, sc, st);
-    default: return launch_rows_mb<T, Src, Dst, 64>(src, rows, n, dst, rot, sc, st);
+    case 1: return launch_rows_mb<T, Src, Dst, 1>(src, lds, rows, n, dst, ldd, rot, sc, st);
+    case 8: return launch_rows_mb<T, Src, Dst, 8>(src, lds, rows, n, dst, ldd, rot, sc, st);
+    case 32: return launch_rows_mb<T, Src, Dst, 32>(src, lds, rows, n, dst, ldd, rot, sc, st);
+    default: return launch_rows_mb<T, Src, Dst, 64>(src, lds, rows, n, dst, ldd, rot, sc, st);
   }
 }
 
+template <typename T, typename Src, typename Dst, int MB>
+kq_status launch_fw_mb(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, const RowFw& rf,
+                       size_t lds_bytes, hipStream_t st) {
+  auto kern = row_fwht<T, Src, Dst, MB>;
+  kq_status r = allow_lds(kern, "row_fwht");
+  if (r != KQ_OK) return r;
+  {
+    LaunchTimer timer("row_fwht", st);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kFwThreads), lds_bytes, st, src, lds, n, dst,
+                       ldd, rf);
+  }
+  return check_launch("row_fwht");
+}
+
+template <typename T, typename Src, typename Dst>
+kq_status launch_fw_t(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, const RowFw& rf,
+                      hipStream_t st) {
+  const size_t bytes = size_t(n + (n >> 4)) * sizeof(T);
+  switch (mix_bucket(rf.m)) {
+    case 1: return launch_fw_mb<T, Src, Dst, 1>(src, lds, rows, n, dst, ldd, rf, bytes, st);
+    case 8: return launch_fw_mb<T, Src, Dst, 8>(src, lds, rows, n, dst, ldd, rf, bytes, st);
+    default: return launch_fw_mb<T, Src, Dst, 32>(src, lds, rows, n, dst, ldd, rf, bytes, st);
+  }
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Row direction of rot on each of the rows (pitches lds, ldd elements), with
+// the diagonal factors of sc. The register-butterfly kernel takes chunks of at
+// least 256, odd factors up to 31, 16-byte aligned rows and factors on the
+// signs' side; anything else takes the LDS kernel.
 template <typename Src, typename Dst>
-kq_status launch_rows(const Src* src, int64_t rows, int64_t n, Dst* dst, Rot rot, Scales sc, hipStream_t st) {
-  if (fits<double>(n, rot)) return launch_rows_t<double>(src, rows, n, dst, rot, sc, st);
-  return launch_rows_t<float>(src, rows, n, dst, rot, sc, st);
+kq_status launch_rows(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, Rot rot,
+                      Scales sc, hipStream_t st) {
+  const bool side_ok = (!sc.row && !sc.col) || (sc.at_store != 0) == (rot.inverse != 0);
+  const bool rows_aligned = aligned16(src) && (lds * int64_t(sizeof(Src))) % 16 == 0;
+  if (rot.signs && rot.log2p >= 8 && rot.m <= 31 && side_ok && rows_aligned && aligned16(rot.signs)) {
+    const RowFw rf{rot.log2p, rot.m, rot.q, rot.inverse, rot.signs, rot.inverse, rot.out_scale, sc.row, sc.col};
+    // float64 staging for float64 output while a row stays small; float32 staging (one
+    // rounding per window, below the float32 output's own) keeps more rows per CU
+    if (sizeof(Dst) == sizeof(double) && size_t(n + (n >> 4)) * sizeof(double) <= kRowLdsF64)
+      return launch_fw_t<double>(src, lds, rows, n, dst, ldd, rf, st);
+    if (size_t(n + (n >> 4)) * sizeof(float) <= kLdsBudget)
+      return launch_fw_t<float>(src, lds, rows, n, dst, ldd, rf, st);
+  }
+  if (fits<double>(n, rot)) return launch_rows_t<double>(src, lds, rows, n, dst, ldd, rot, sc, st);
+  return launch_rows_t<float>(src, lds, rows, n, dst, ldd, rot, sc, st);
 }
 
 template <typename Src, typename Dst, int MB, int TC>
@@ -470,12 +781,24 @@ kq_status col_pass_any(const Src* src, Dst* dst, const ColPass& cp, int64_t grou
 
 template <typename Src, typename Dst, int LP>
 kq_status launch_fwht(const Src* src, Dst* dst, const ColPass& cp, bool ops, hipStream_t st) {
-  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
-  const dim3 grid(static_cast<unsigned>((cp.n_rows >> LP) * ncb));
+  const int64_t groups = cp.n_rows >> LP;
+  const int64_t nfull = cp.n_cols / kColThreads;
   {
     LaunchTimer timer("col_fwht", st);
-    if (ops) hipLaunchKernelGGL((col_fwht<Src, Dst, LP, true>), grid, dim3(kColThreads), 0, st, src, dst, cp);
-    else hipLaunchKernelGGL((col_fwht<Src, Dst, LP, false>), grid, dim3(kColThreads), 0, st, src, dst, cp);
+    if (nfull > 0) {
+      const dim3 grid(static_cast<unsigned>(groups * nfull));
+      if (ops) hipLaunchKernelGGL((col_fwht<Src, Dst, LP, true, false>), grid, dim3(kColThreads), 0, st, src, dst, cp,
+                                  int64_t(0), nfull);
+      else hipLaunchKernelGGL((col_fwht<Src, Dst, LP, false, false>), grid, dim3(kColThreads), 0, st, src, dst, cp,
+                              int64_t(0), nfull);
+    }
+    if (cp.n_cols % kColThreads) {
+      const dim3 grid(static_cast<unsigned>(groups));
+      if (ops) hipLaunchKernelGGL((col_fwht<Src, Dst, LP, true, true>), grid, dim3(kColThreads), 0, st, src, dst, cp,
+                                  nfull, int64_t(1));
+      else hipLaunchKernelGGL((col_fwht<Src, Dst, LP, false, true>), grid, dim3(kColThreads), 0, st, src, dst, cp,
+                              nfull, int64_t(1));
+    }
   }
   return check_launch("col_fwht");
 }
@@ -513,13 +836,13 @@ kq_status col_step(const Src* src, Dst* dst, const ColPass& cp, bool ops, hipStr
 
 // Column direction of U_rot applied to a [n_rows, n_cols] matrix (n_rows = n of the rotation):
 // butterfly passes over 6-bit chunks of the row index, then the odd mix, src -> mid -> ... -> dst
-// with mid a float64 buffer (it may equal src or dst when those are float64; every pass works
-// in place on its own elements). Signs and load-side scales go with the first pass; the
-// 1 / sqrt(p) factor, inverse signs and store-side scales with the last. fac holds
-// 2 n_rows + 2 n_cols doubles for the factor arrays; ones_ has max(n_rows, n_cols) ones.
+// with mid a float32 buffer (it may equal src when that is float32; every pass works in place
+// on its own elements). Signs and load-side scales go with the first pass; the 1 / sqrt(p)
+// factor, inverse signs and store-side scales with the last. fac holds 2 n_rows + 2 n_cols
+// doubles for the factor arrays; ones has max(n_rows, n_cols) ones.
 template <typename Src, typename Dst>
-kq_status launch_cols(const Src* src, int64_t n_rows, int64_t n_cols, Dst* dst, double* mid, const Rot& rot,
-                      Scales sc, double* fac, const double* ones, hipStream_t st) {
+kq_status launch_cols(const Src* src, int64_t lds, int64_t n_rows, int64_t n_cols, Dst* dst, int64_t ldd, float* mid,
+                      int64_t ldm, const Rot& rot, Scales sc, double* fac, const double* ones, hipStream_t st) {
   const int k = rot.signs ? rot.log2p : 0;
   const int m = rot.signs ? rot.m : 1;
   ColPass passes[4];
@@ -565,49 +888,62 @@ kq_status launch_cols(const Src* src, int64_t n_rows, int64_t n_cols, Dst* dst, 
   for (int i = 0; i < np; ++i) {
     passes[i].n_rows = n_rows;
     passes[i].n_cols = n_cols;
+    passes[i].lds = i == 0 ? lds : ldm;
+    passes[i].ldd = i == np - 1 ? ldd : ldm;
     passes[i].rl = i == 0 ? rl : ones;
     passes[i].cl = i == 0 ? cl : ones;
     passes[i].rs = i == np - 1 ? rs : ones;
     passes[i].cs = i == np - 1 ? cs : ones;
   }
   if (np == 1) return col_step<Src, Dst>(src, dst, passes[0], true, st);
-  r = col_step<Src, double>(src, mid, passes[0], true, st);
-  for (int i = 1; i + 1 < np && r == KQ_OK; ++i) r = col_step<double, double>(mid, mid, passes[i], false, st);
+  r = col_step<Src, float>(src, mid, passes[0], true, st);
+  for (int i = 1; i + 1 < np && r == KQ_OK; ++i) r = col_step<float, float>(mid, mid, passes[i], false, st);
   if (r != KQ_OK) return r;
-  return col_step<double, Dst>(mid, dst, passes[np - 1], true, st);
+  return col_step<float, Dst>(mid, dst, passes[np - 1], true, st);
 }
 
-// U S^-1 M S^-1 U^T of a symmetric d x d float32 matrix, in place, through a float64 scratch copy.
-kq_status two_sided(float* h, int64_t d, const Rot& rot, const double* inv_s, double* tmp, double* fac,
+// Row pitch of the float32 intermediate for rows of n values: a multiple of 64
+// values, moved off multiples of 1024 so that rows at power-of-two distances
+// (the column passes step over 2^6 rows at a time) do not share memory channels.
+int64_t mid_pitch(int64_t n) {
+  const int64_t r = (n + 63) / 64 * 64;
+  return r % 1024 == 0 ? r + 64 : r;
+}
+
+// U S^-1 M S^-1 U^T of a symmetric d x d float32 matrix, in place, through a float32 scratch copy:
+// column passes (with both scales) h -> tmp, then the row pass tmp -> h.
+kq_status two_sided(float* h, int64_t d, const Rot& rot, const double* inv_s, float* tmp, double* fac,
                     const double* ones, hipStream_t st) {
-  kq_status r = launch_rows<float, double>(h, d, d, tmp, rot, Scales{inv_s, inv_s, 0}, st);
+  const int64_t pm = mid_pitch(d);
+  kq_status r = launch_cols<float, float>(h, d, d, d, tmp, pm, tmp, pm, rot, Scales{inv_s, inv_s, 0}, fac, ones, st);
   if (r != KQ_OK) return r;
-  return launch_cols<double, float>(tmp, d, d, h, tmp, rot, Scales{nullptr, nullptr, 0}, fac, ones, st);
+  return launch_rows<float, float>(tmp, pm, d, d, h, d, rot, Scales{nullptr, nullptr, 0}, st);
 }
 
 template <typename Src>
 kq_status forward_w(const Src* w, int64_t dout, int64_t din, double* w_out, const Rot& ri, const Rot& ro,
-                    const double* s_x, const double* s_g, double* tmp, double* fac, const double* ones,
+                    const double* s_x, const double* s_g, float* tmp, double* fac, const double* ones,
                     hipStream_t st) {
   const Scales ld{s_g, s_x, 0};
   const Scales none{nullptr, nullptr, 0};
+  const int64_t pm = mid_pitch(din);
   if (ri.signs && ro.signs) {
-    kq_status r = launch_rows<Src, double>(w, dout, din, tmp, ri, ld, st);
+    kq_status r = launch_cols<Src, float>(w, din, dout, din, tmp, pm, tmp, pm, ro, ld, fac, ones, st);
     if (r != KQ_OK) return r;
-    return launch_cols<double, double>(tmp, dout, din, w_out, tmp, ro, none, fac, ones, st);
+    return launch_rows<float, double>(tmp, pm, dout, din, w_out, din, ri, none, st);
   }
-  if (ro.signs) return launch_cols<Src, double>(w, dout, din, w_out, w_out, ro, ld, fac, ones, st);
-  return launch_rows<Src, double>(w, dout, din, w_out, ri, ld, st);  // ri may be "no rotation"
+  if (ro.signs) return launch_cols<Src, double>(w, din, dout, din, w_out, din, tmp, pm, ro, ld, fac, ones, st);
+  return launch_rows<Src, double>(w, din, dout, din, w_out, din, ri, ld, st);  // ri may be "no rotation"
 }
 
 }  // namespace
 
-// Workspace layout: float64 intermediate (the largest matrix), 1 / s_x, 1 / s_g, ...
+// Workspace layout: float32 intermediate (the largest matrix), 1 / s_x, 1 / s_g, ...
 static size_t biip_tmp_bytes(int64_t dout, int64_t din) {
-  int64_t n = dout * din;
-  if (din * din > n) n = din * din;
-  if (dout * dout > n) n = dout * dout;
-  return align_up(size_t(n) * sizeof(double), 256);
+  int64_t n = dout * mid_pitch(din);
+  if (din * mid_pitch(din) > n) n = din * mid_pitch(din);
+  if (dout * mid_pitch(dout) > n) n = dout * mid_pitch(dout);
+  return align_up(size_t(n) * sizeof(float), 256);
 }
 
 // ... then the factor arrays of a column transform (4 max(dout, din)) and max(dout, din) ones.
@@ -631,7 +967,7 @@ kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double
   const bool scale = flags & KQ_BIIP_SCALE, inverse = flags & KQ_BIIP_INVERSE;
   const int64_t nmax = dout > din ? dout : din;
   char* p = static_cast<char*>(ws);
-  double* tmp = reinterpret_cast<double*>(p);
+  float* tmp = reinterpret_cast<float*>(p);
   p += biip_tmp_bytes(dout, din);
   double* inv_x = reinterpret_cast<double*>(p);
   p += biip_vec_bytes(din);
@@ -655,16 +991,19 @@ kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double
                          inv_g);
     }
     if ((r = check_launch("recip_kernel")) != KQ_OK) return r;
-    // W = S_G^-1 U_G^T W'' U_X S_X^-1: input-side rows first, then output-side columns;
-    // the row scale must follow the output-side rotation, which mixes rows.
+    // W = S_G^-1 U_G^T W'' U_X S_X^-1: input-side rows first, then output-side columns
+    // with both scales at their last store (each scale follows the rotation of its index).
     const Rot ri = make_rot(rot_in, inp, true), ro = make_rot(rot_out, out, true);
     const double* w2 = static_cast<const double*>(w);
-    if (out) {
-      r = launch_rows<double, double>(w2, dout, din, tmp, ri, Scales{nullptr, inv_x, 1}, st);
+    const Scales at_store{inv_g, inv_x, 1};
+    const int64_t pm = mid_pitch(din);
+    if (out && inp) {
+      r = launch_rows<double, float>(w2, din, dout, din, tmp, pm, ri, Scales{nullptr, nullptr, 1}, st);
       if (r != KQ_OK) return r;
-      return launch_cols<double, double>(tmp, dout, din, w_out, tmp, ro, Scales{inv_g, nullptr, 1}, fac, ones, st);
+      return launch_cols<float, double>(tmp, pm, dout, din, w_out, din, tmp, pm, ro, at_store, fac, ones, st);
     }
-    return launch_rows<double, double>(w2, dout, din, w_out, ri, Scales{inv_g, inv_x, 1}, st);
+    if (out) return launch_cols<double, double>(w2, din, dout, din, w_out, din, tmp, pm, ro, at_store, fac, ones, st);
+    return launch_rows<double, double>(w2, din, dout, din, w_out, din, ri, at_store, st);
   }
   // scales come from the raw diagonals, before H_X and H_G are transformed in place
   {

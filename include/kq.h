@@ -230,7 +230,8 @@ kq_status kq_cholesky_inv(float* h, int64_t d, float damp, int32_t* info, void* 
  * the GPTQ update ([KQ-en] Methodology; [KQ-zh] 方法论).
  *
  *   w        device float64 [dout, din]; in: W''; out: dequantised W^'' (in place)
- *   r        device float32 [din, din], upper triangular R from kq_cholesky_inv
+ *   r        device float32 [din, din], upper triangular R from kq_cholesky_inv;
+ *            16-byte aligned (KQ_EINVAL otherwise)
  *   bits     2..8
  *   group    0 (one grid per row) or a divisor of block
  *   block    32, 64 or 128, dividing din

@@ -203,6 +203,7 @@ kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, 
                           int32_t block, uint8_t* codes, float* scales, uint8_t* zeros, double* preround, void* ws,
                           size_t ws_bytes, void* stream) {
   if (!w || !r || !codes || !scales || !zeros) return fail(KQ_EINVAL, "kq_obs_quantize: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(r) % 16 != 0) return fail(KQ_EINVAL, "kq_obs_quantize: r must be 16-byte aligned");
   if (dout < 1 || din < 1 || din > kMaxDim) return fail(KQ_EINVAL, "kq_obs_quantize: bad shape");
   if (bits < 2 || bits > 8) return fail(KQ_EINVAL, "kq_obs_quantize: bits = %d outside [2, 8]", bits);
   if (block < 1 || din % block != 0)

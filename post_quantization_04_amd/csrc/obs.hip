@@ -1,13 +1,12 @@
 // GPTQ-style column-wise OBS on the rotated weight, in float64.
 //
 // The sweep is sequential in the column index and independent across rows,
-// given R. Per block k of B columns [c0, c0 + B):
-//   * near kernel (k > 0): the block's columns receive the previous block's
-//     errors, W[:, c0:c0+B] -= E_{k-1} R[c0-B:c0, c0:c0+B] (float64 MFMA,
-//     32-row tiles);
-//   * step kernel, two roles in one launch:
+// given R. Per block k of B columns [c0, c0 + B), one launch with two roles:
 //     - sweep (16 rows per workgroup): 16 lanes own one row; lane l keeps
-//       columns l, l + 16, ... of the block in registers (B / 16 values). For
+//       columns l, l + 16, ... of the block in registers (B / 16 values).
+//       First (k > 0) the registers receive the previous block's errors of
+//       the same rows, W[r, c0:c0+B] -= E_{k-1}[r] R[c0-B:c0, c0:c0+B]; the
+//       workgroup wrote those errors itself one launch earlier. For
 //       column j the owning lane quantises, forms the scaled error
 //       e = (w - w^) / R_jj and the error is broadcast to the row's 16 lanes
 //       with one DPP row_newbcast; every lane then removes e * R[j][k] from
@@ -135,6 +134,34 @@ __device__ __forceinline__ void group_start(const double (&x)[EPL], int eo, int 
   }
 }
 
+// rl[j][l * EPL + e] = R[row0 + j][col0 + l + 16 e] for the B x B block (upper: entries on
+// and below the diagonal stored as 0, rinv[j] = 1 / R[row0 + j][col0 + j]). Every thread
+// issues all of its 16-byte loads before writing LDS.
+template <int B, bool UPPER>
+__device__ __forceinline__ void stage_r(float (&rl)[B][B], double* rinv, const float* __restrict__ r, int64_t din,
+                                        int64_t row0, int64_t col0) {
+  constexpr int EPL = B / 16, V = B / 4, N = B * V / kSweepThreads;
+  static_assert(N >= 1 && B * V % kSweepThreads == 0, "block shape");
+  const int tid = threadIdx.x;
+  float4 v[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const int idx = tid + q * kSweepThreads, j = idx / V, k4 = (idx % V) * 4;
+    v[q] = *reinterpret_cast<const float4*>(r + (row0 + j) * din + col0 + k4);
+  }
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const int idx = tid + q * kSweepThreads, j = idx / V, k4 = (idx % V) * 4;
+    const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = k4 + t;
+      rl[j][(k & 15) * EPL + (k >> 4)] = (!UPPER || k > j) ? f[t] : 0.0f;
+      if (UPPER && k == j) rinv[j] = 1.0 / static_cast<double>(f[t]);
+    }
+  }
+}
+
 // Sweep of block [c0, c0 + B) for rows [16 wg, 16 wg + 16); writes the scaled
 // errors of the block to e_out [dout, B]. Groups are powers of two dividing B:
 // with SG false (no group, or group >= 16) a group can start only at a
@@ -143,19 +170,11 @@ template <int B, bool SG>
 __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, const float* __restrict__ r,
                            int64_t dout, int64_t din, int64_t c0, int bits, int group, uint8_t* __restrict__ codes,
                            float* __restrict__ scales, uint8_t* __restrict__ zeros, double* __restrict__ preround,
-                           double* __restrict__ e_out) {
+                           const double* __restrict__ e_prev, double* __restrict__ e_out) {
   constexpr int EPL = B / 16;
   auto& rl = sm.rl;
   auto& rinv = sm.rinv;
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < B * B; idx += kSweepThreads) {
-    const int j = idx / B, k = idx % B;
-    const float v = r[(c0 + j) * din + c0 + k];
-    rl[j][(k & 15) * EPL + (k >> 4)] = (k > j) ? v : 0.0f;
-    if (k == j) rinv[j] = 1.0 / static_cast<double>(v);
-  }
-  __syncthreads();
-
   const int l16 = tid & 15;
   const int64_t row = int64_t(wg) * kRowsPerWg + (tid >> 4);
   const bool valid = row < dout;
@@ -169,6 +188,31 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   double x[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) x[e] = valid ? w[row * din + c0 + l16 + 16 * e] : 0.0;
+  if (c0 > 0) {
+    // previous block's errors of these rows: x -= E_prev[row] R[c0-B:c0, c0:c0+B],
+    // R staged in the sweep's LDS layout (all entries)
+    stage_r<B, false>(rl, nullptr, r, din, c0 - B, c0);
+    __syncthreads();
+    // E_prev[row][j] is loaded once by lane j / EPL of the row (slot j % EPL) and broadcast
+    double ev[EPL];
+    const double* ep = e_prev + (valid ? row : 0) * B + l16 * EPL;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) ev[i] = ep[i];
+    const int lane0 = (tid & 63) & ~15;  // first lane of this row's 16 in the wave
+#pragma unroll 1
+    for (int src = 0; src < 16; ++src) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const double eb = __shfl(ev[i], lane0 + src, 64);
+        const float* rr = &rl[src * EPL + i][l16 * EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = fma(-eb, static_cast<double>(rr[e]), x[e]);
+      }
+    }
+    __syncthreads();
+  }
+  stage_r<B, true>(rl, rinv, r, din, c0, c0);
+  __syncthreads();
   double s = 1.0, z = 0.0;
   if (group == 0 && valid) {
     s = static_cast<double>(scales[row]);
@@ -176,45 +220,51 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   }
   double inv_s = 1.0 / s;
 
+  // Fully unrolled: x[e] is column l16 + 16 e throughout. Within slice eo only x[eo] is on
+  // the dependent chain (quantise, broadcast, one FMA per column, with the slice's 16 R
+  // entries loaded up front); the updates of the later slices x[e > eo] follow as one batch
+  // at the end of the slice, in the same per-element order as column by column.
+#pragma unroll
   for (int eo = 0; eo < EPL; ++eo) {
     if (!SG && group > 0 && ((eo * 16) & gmask) == 0)
-      group_start<EPL>(x, eo, eo * 16, l16, group, log2g, maxq, valid, row, ngroups, c0, scales, zeros, s, z, inv_s);
-    double tcur = 0.0, ecur = 0.0;
-    int ccur = 0;
+      group_start<EPL>(x, 0, eo * 16, l16, group, log2g, maxq, valid, row, ngroups, c0, scales, zeros, s, z, inv_s);
+    const double rcur = rinv[eo * 16 + l16];  // 1 / R_jj of this lane's column of the slice
+    float rd[16];                              // R[eo 16 + lo][this lane's column of the slice]
+#pragma unroll
+    for (int lo = 0; lo < 16; ++lo) rd[lo] = rl[eo * 16 + lo][l16 * EPL + eo];
+    double eb[16];
+    double tcur = 0.0, ecur = 0.0, qcur = 0.0;
 #pragma unroll
     for (int lo = 0; lo < 16; ++lo) {
       const int j = eo * 16 + lo;
       if (SG && (j & gmask) == 0)
-        group_start<EPL>(x, eo, j, l16, group, log2g, maxq, valid, row, ngroups, c0, scales, zeros, s, z, inv_s);
+        group_start<EPL>(x, 0, j, l16, group, log2g, maxq, valid, row, ngroups, c0, scales, zeros, s, z, inv_s);
       // the rounding argument w * (1/s) is within two ulps of w / s
-      const double wv = x[0];
+      const double wv = x[eo];
       const double t = wv * inv_s;
       const double q = fmin(fmax(rint(t) + z, 0.0), static_cast<double>(maxq));
       const double wq = s * (q - z);
-      const double err = (wv - wq) * rinv[j];
-      if (l16 == lo) {
-        x[0] = wq;
-        tcur = t;
-        ecur = err;
-        ccur = static_cast<int>(q);
-      }
-      const double eb = bcast16(err, lo);
-      const float* rr = &rl[j][l16 * EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int idx = eo + e < EPL ? eo + e : EPL - 1;  // registers past the block are never stored
-        x[e] = fma(-eb, static_cast<double>(rr[idx]), x[e]);
-      }
+      const double err = (wv - wq) * rcur;
+      const bool own = l16 == lo;
+      tcur = own ? t : tcur;
+      ecur = own ? err : ecur;
+      qcur = own ? q : qcur;
+      eb[lo] = bcast16(err, lo);
+      // R[j][own column] and R[j][earlier columns] are stored as 0: those lanes keep their value
+      x[eo] = fma(-eb[lo], static_cast<double>(rd[lo]), own ? wq : wv);
     }
     if (valid) {
       const int64_t col = c0 + l16 + 16 * eo;
-      w[row * din + col] = x[0];
-      codes[row * din + col] = static_cast<uint8_t>(ccur);
+      w[row * din + col] = x[eo];
+      codes[row * din + col] = static_cast<uint8_t>(qcur);
       if (preround) preround[row * din + col] = tcur;
       e_out[row * B + l16 + 16 * eo] = ecur;
     }
 #pragma unroll
-    for (int e = 0; e + 1 < EPL; ++e) x[e] = x[e + 1];
+    for (int e = eo + 1; e < EPL; ++e)
+#pragma unroll
+      for (int lo = 0; lo < 16; ++lo)
+        x[e] = fma(-eb[lo], static_cast<double>(rl[eo * 16 + lo][l16 * EPL + e]), x[e]);
   }
 }
 
@@ -330,23 +380,6 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
     }
 }
 
-// Near update before the sweep of block [c0, c0 + B): its columns receive the
-// previous block's errors, W[:, c0:c0+B] -= E_prev R[c0-B:c0, c0:c0+B], in
-// 32-row tiles (many workgroups for a narrow update).
-template <int B>
-struct NearShape {
-  static constexpr int TM = 32, TN = B, WR = (B >= 64 ? 1 : 2), WC = 4 / WR;
-};
-
-template <int B>
-__global__ __launch_bounds__(256) void near_kernel(double* __restrict__ w, const float* __restrict__ r,
-                                                   const double* __restrict__ e_prev, int64_t dout, int64_t din,
-                                                   int64_t c0) {
-  using S = NearShape<B>;
-  __shared__ TileLds<S::TM, S::TN> sm;
-  tile_role<B, S::TM, S::TN, S::WR, S::WC>(sm, w, r, e_prev, dout, din, c0 - B, int64_t(blockIdx.x) * S::TM, c0);
-}
-
 // One step of the sweep: workgroups [0, n_sweep) sweep block [c0, c0 + B)
 // (errors to e_cur), the others apply the previous block's errors e_prev to
 // every column from c0 + B on in 128 x 128 tiles. The two roles touch
@@ -371,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void step_kernel(double* __restrict__ w, co
   __shared__ StepLds<B> sm;
   const int b = blockIdx.x;
   if (b < n_sweep) {
-    sweep_role<B, SG>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_cur);
+    sweep_role<B, SG>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_prev, e_cur);
     return;
   }
   const int t = b - n_sweep;
@@ -389,12 +422,6 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
   kq_status s;
   for (int64_t c0 = 0, k = 0; c0 < din; c0 += B, ++k) {
     double* e_prev = ebuf[(k + 1) & 1];
-    if (k > 0) {
-      LaunchTimer timer("near_kernel", st);
-      hipLaunchKernelGGL(near_kernel<B>, dim3(static_cast<unsigned>((dout + NearShape<B>::TM - 1) / NearShape<B>::TM)),
-                         dim3(256), 0, st, w, r, e_prev, dout, din, c0);
-    }
-    if (k > 0 && (s = check_launch("near_kernel")) != KQ_OK) return s;
     const int64_t rest = din - c0 - B;  // columns beyond this block
     const int far_cols = (k > 0 && rest > 0) ? static_cast<int>((rest + kFT - 1) / kFT) : 0;
     {

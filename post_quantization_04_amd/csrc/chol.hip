@@ -270,12 +270,34 @@ __device__ __forceinline__ f64x4 load16(const double* c) {
   return v;
 }
 
-// Value of v in lane `src` (a compile-time lane), for every lane.
-__device__ __forceinline__ double bcast(double v, int src) {
-  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
-  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b), src));
-  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), src));
-  return __builtin_bit_cast(double, (static_cast<unsigned long long>(hi) << 32) | lo);
+// Value of v in lane `src` of this lane's row of 16 (DPP row_newbcast; src a compile-time lane).
+template <int CTRL>
+__device__ __forceinline__ double dpp_row(double v) {
+  // every lane reads a valid source under row_newbcast, so no "old" value is needed
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double bcast_row(double v, int src) {
+  switch (src) {
+    case 0: return dpp_row<0x150>(v);
+    case 1: return dpp_row<0x151>(v);
+    case 2: return dpp_row<0x152>(v);
+    case 3: return dpp_row<0x153>(v);
+    case 4: return dpp_row<0x154>(v);
+    case 5: return dpp_row<0x155>(v);
+    case 6: return dpp_row<0x156>(v);
+    case 7: return dpp_row<0x157>(v);
+    case 8: return dpp_row<0x158>(v);
+    case 9: return dpp_row<0x159>(v);
+    case 10: return dpp_row<0x15A>(v);
+    case 11: return dpp_row<0x15B>(v);
+    case 12: return dpp_row<0x15C>(v);
+    case 13: return dpp_row<0x15D>(v);
+    case 14: return dpp_row<0x15E>(v);
+    default: return dpp_row<0x15F>(v);
+  }
 }
 
 // 1 / sqrt(p) for finite p > 0: the hardware estimate refined by two Newton
@@ -291,50 +313,58 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 }
 
 // 16 x 16 Cholesky (lower) of the sub-block at l + o * (kP + 1) and its inverse
-// into x + o * (kP + 1); wave 0 only. Lane i < 16 holds row i in registers;
-// columns are broadcast with readlane and pivots use 1 / sqrt(p), so the
-// column chain has no division, square root or LDS round trip. Returns the
-// local index of the first bad pivot, or -1.
+// into x + o * (kP + 1); wave 0 only. Each of the wave's four rows of 16
+// lanes factors the block (lane i of a row holds row i in registers; columns
+// are broadcast across the 16 lanes with DPP row_newbcast; pivots use
+// 1 / sqrt(p), so the column chain has no division, square root, scalar round
+// trip or LDS access); row q then forms the columns j = q mod 4 of the inverse.
+// Returns the local index of the first bad pivot, or -1 (the chain runs to the
+// end either way; a bad pivot only poisons values the caller then discards).
 __device__ int base16(double* l, double* x, int o) {
   const int lane = threadIdx.x & 63;
-  const bool act = lane < 16;
+  const int i = lane & 15, q = lane >> 4;
   double* L = l + o * (kP + 1);
   double* X = x + o * (kP + 1);
   double r[16], y[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) r[j] = act ? L[lane * kP + j] : 0.0;
+  for (int j = 0; j < 16; ++j) r[j] = L[i * kP + j];
   // Factor: after step k, lanes i >= k hold l_ik in r[k]. Lanes i < j also
   // update their (upper) r[j]; those values are never broadcast and are
   // cleared when their column comes up.
+  int bad = -1;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const double p = bcast(r[k], k);
-    if (!(p > 0.0) || !(p < __builtin_huge_val())) return k;  // uniform
+    const double p = bcast_row(r[k], k);
+    bad = (bad < 0 && !(p > 0.0 && p < __builtin_huge_val())) ? k : bad;
     y[k] = rsqrt_f64(p);
-    const double lik = (lane == k) ? p * y[k] : r[k] * y[k];
-    r[k] = (lane >= k) ? lik : 0.0;
+    const double lik = (i == k) ? p * y[k] : r[k] * y[k];
+    r[k] = (i >= k) ? lik : 0.0;
 #pragma unroll
-    for (int j = k + 1; j < 16; ++j) r[j] = fma(-lik, bcast(lik, j), r[j]);
+    for (int j = k + 1; j < 16; ++j) r[j] = fma(-lik, bcast_row(lik, j), r[j]);
   }
-  // Inverse by forward substitution: lane i holds row i of X = L^-1. At step
-  // k row k is scaled by 1 / l_kk = y_k, then removed from the rows below.
-  double xr[16];
+  bad = __builtin_amdgcn_readfirstlane(bad);
+  if (bad >= 0) return bad;
+  // Inverse by forward substitution, columns j = 4 c + q of X = L^-1 in row q:
+  // xr[c] = X[i][4 c + q]. At step k row k of X is scaled by 1 / l_kk = y_k,
+  // then removed from the rows below (columns beyond k are still zero).
+  double xr[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) xr[j] = (lane == j) ? 1.0 : 0.0;
+  for (int c = 0; c < 4; ++c) xr[c] = (i == 4 * c + q) ? 1.0 : 0.0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
+    constexpr int kc = 4;
+    const int nc = (k >> 2) + 1 < kc ? (k >> 2) + 1 : kc;  // columns 4 c + q <= k need c <= k / 4
 #pragma unroll
-    for (int j = 0; j <= k; ++j) xr[j] = (lane == k) ? xr[j] * y[k] : xr[j];
-    const double lik = (lane > k) ? r[k] : 0.0;
+    for (int c = 0; c < nc; ++c) xr[c] = (i == k) ? xr[c] * y[k] : xr[c];
+    const double lik = (i > k) ? r[k] : 0.0;
 #pragma unroll
-    for (int j = 0; j <= k; ++j) xr[j] = fma(-lik, bcast(xr[j], k), xr[j]);
+    for (int c = 0; c < nc; ++c) xr[c] = fma(-lik, bcast_row(xr[c], k), xr[c]);
   }
-  if (act) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      L[lane * kP + j] = (j <= lane) ? r[j] : 0.0;
-      X[lane * kP + j] = (j <= lane) ? xr[j] : 0.0;
-    }
+  for (int c = 0; c < 4; ++c) {
+    const int j = 4 * c + q;
+    L[i * kP + j] = (j <= i) ? r[j] : 0.0;
+    X[i * kP + j] = (j <= i) ? xr[c] : 0.0;
   }
   return -1;
 }
@@ -356,15 +386,6 @@ union StepLds {
   GemmLds gm;
 };
 
-// Copies the 64 x 64 float32 block at src (pitch dp) into dst as float64;
-// lower = true zeroes the strict upper triangle.
-__device__ __forceinline__ void load_block(double* dst, const float* src, int64_t dp, bool lower) {
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    dst[i * kP + j] = (!lower || j <= i) ? static_cast<double>(src[int64_t(i) * dp + j]) : 0.0;
-  }
-}
-
 // Diagonal role of step kb, workgroup b in [0, 1 + rest): brings block
 // column kb up to date with the previous step's rank-64 update (L[:, kb-1],
 // in float64 MFMA), factors the diagonal block and inverts its factor (every
@@ -381,8 +402,16 @@ __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict_
   const int64_t o = int64_t(kb) * kB, op = o - kB;
   const int64_t r0 = o + int64_t(b) * kB;
   const bool panel = b > 0, prev = kb > 0;
-  // this thread's 16 elements e = tid + 256 q of the panel block and its previous-panel rows
-  float ab[16], lb[16];
+  // this thread's 16 elements e = tid + 256 q of the diagonal block, its previous-panel
+  // rows, the panel block and its previous-panel rows: every load is issued before the
+  // first LDS write, so the inputs written by the previous launch arrive in one round trip
+  float dg[16], dq[16], ab[16], lb[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    dg[q] = a[(o + (e >> 6)) * dp + o + (e & 63)];
+    dq[q] = prev ? a[(o + (e >> 6)) * dp + op + (e & 63)] : 0.0f;
+  }
   if (panel) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -391,9 +420,13 @@ __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict_
       lb[q] = prev ? a[(r0 + (e >> 6)) * dp + op + (e & 63)] : 0.0f;
     }
   }
-  load_block(l, a + o * dp + o, dp, true);
-  for (int e = tid; e < kB * kB; e += 256) x[(e >> 6) * kP + (e & 63)] = 0.0;
-  if (prev) load_block(lp, a + o * dp + op, dp, false);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, i = e >> 6, j = e & 63;
+    l[i * kP + j] = j <= i ? static_cast<double>(dg[q]) : 0.0;
+    x[i * kP + j] = 0.0;
+    if (prev) lp[i * kP + j] = static_cast<double>(dq[q]);
+  }
   if (panel) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {

@@ -389,10 +389,12 @@ union StepLds {
 // Diagonal role of step kb, workgroup b in [0, 1 + rest): brings block
 // column kb up to date with the previous step's rank-64 update (L[:, kb-1],
 // in float64 MFMA), factors the diagonal block and inverts its factor (every
-// workgroup does this itself), then workgroup 0 writes L_kk to A and L_kk^-1
-// to M, and workgroup b >= 1 writes L[kb + b, kb] = A[kb + b, kb] L_kk^-T.
-// All global reads are issued up front; the panel block's own update runs on
-// waves 1..3 while wave 0 factors the first 16 columns.
+// workgroup does this itself), then workgroup 0 writes L_kk^-1 to M, and
+// workgroup b >= 1 writes L[kb + b, kb] = A[kb + b, kb] L_kk^-T. No workgroup
+// writes a block another one of the launch reads, so the result does not
+// depend on when each workgroup starts. All global reads are issued up front;
+// the panel block's own update runs on waves 1..3 while wave 0 factors the
+// first 16 columns.
 __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb, int64_t d,
                           int32_t* __restrict__ info, int b) {
   double* l = sm.l;
@@ -512,12 +514,13 @@ __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict_
     __syncthreads();
   }
   if (!panel) {
-    // L_kk into A, L_kk^-1 into M, zeros into the M block to its right (read
-    // as the zero upper triangle by the 128-wide merge tiles)
+    // L_kk^-1 into M, zeros into the M block to its right (read as the zero
+    // upper triangle by the 128-wide merge tiles). L_kk itself stays out of A:
+    // no later kernel reads a diagonal block of L, and every workgroup of this
+    // launch reads A_kk from A, possibly after this one has finished.
     const bool right = o + kB < dp;
     for (int e = tid; e < kB * kB; e += 256) {
       const int i = e >> 6, j = e & 63;
-      if (j <= i) a[(o + i) * dp + o + j] = static_cast<float>(l[i * kP + j]);
       m[(o + i) * dp + o + j] = static_cast<float>(x[i * kP + j]);
       if (right) m[(o + i) * dp + o + kB + j] = 0.0f;
     }

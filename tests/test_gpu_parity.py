@@ -160,6 +160,39 @@ def test_biip_forward(dout, din, wdt):
         assert rel_fro(host(back), w64) <= 1e-6, tag
 
 
+@pytest.mark.parametrize("dout,din", [(320, 384), (512, 1024)])
+def test_biip_sides_compose(dout, din):
+    """The input side (with H_X) then the output side (with H_G) on its float64 result gives the
+    two-sided call: left and right multiplications commute, each scale comes from its own H."""
+    import torch
+    kq, pipeline = _kq()
+    print(f"biip sides {dout}x{din}", flush=True)
+    rng = np.random.default_rng(dout * din)
+    w = kq_synth.f32_to_bf16_bits(rng.normal(0, 0.02, (dout, din)).astype(np.float32))
+    hx, hg = _spd(rng, din, 3.0), _spd(rng, dout, 3.0)
+    si, so = kq_synth.rot_spec(9, "ci", din), kq_synth.rot_spec(9, "co", dout)
+    ri, ro = pipeline.upload_rot(si.signs, si.q, DEV), pipeline.upload_rot(so.signs, so.q, DEV)
+    f64 = torch.float64
+    wd = bits_to_dev(w)
+    hx1, hg1 = to_dev(hx.astype(np.float32)), to_dev(hg.astype(np.float32))
+    w2 = torch.empty((dout, din), dtype=f64, device=DEV)
+    sx, sg = torch.empty(din, dtype=f64, device=DEV), torch.empty(dout, dtype=f64, device=DEV)
+    kq.biip_rotate(wd, w2, hx1, hg1, ri.rot, ro.rot, pipeline.ALL_SIDES, sx, sg)
+    hx2, hg2 = to_dev(hx.astype(np.float32)), to_dev(hg.astype(np.float32))
+    w1 = torch.empty((dout, din), dtype=f64, device=DEV)
+    w3 = torch.empty((dout, din), dtype=f64, device=DEV)
+    sx2, sg2 = torch.empty(din, dtype=f64, device=DEV), torch.empty(dout, dtype=f64, device=DEV)
+    unused_x, unused_g = torch.empty(din, dtype=f64, device=DEV), torch.empty(dout, dtype=f64, device=DEV)
+    kq.biip_rotate(wd, w1, hx2, None, ri.rot, None, kq.KQ_BIIP_INPUT | kq.KQ_BIIP_SCALE, sx2, unused_g)
+    kq.biip_rotate(w1, w3, None, hg2, None, ro.rot, kq.KQ_BIIP_OUTPUT | kq.KQ_BIIP_SCALE, unused_x, sg2)
+    np.testing.assert_array_equal(host(sx2), host(sx))
+    np.testing.assert_array_equal(host(sg2), host(sg))
+    np.testing.assert_array_equal(host(unused_g), np.ones(dout))  # a side without its flag has s = 1
+    assert rel_fro(host(w3), host(w2)) <= 1e-6
+    assert rel_fro(host(hx2), host(hx1)) <= 1e-6
+    assert rel_fro(host(hg2), host(hg1)) <= 1e-6
+
+
 # ---------------------------------------------------------------------------
 # step 3: damped Cholesky factor of the inverse
 # ---------------------------------------------------------------------------

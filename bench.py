@@ -14,6 +14,11 @@ Workload: LLaMA-2-7B q_proj shapes (W 4096 x 4096 bf16; X and G 262144 x 4096
 bf16, 128 sequences of 2048 tokens), 2-bit, group 128, block 128, damping
 0.01, seeded synthetic inputs.
 
+Schedule: the Cholesky factor needs only H_X'' (the input side of BiIP), so
+by default it runs on one stream while the H_G covariance and the output side
+of BiIP run on a second stream that is kept off some CUs, which stay free for
+the latency-bound factor steps; `--serial` puts every stage on one stream.
+
 value = weights quantised per second, end to end including the covariance
 accumulation. The roofline object covers the dominant kernel, the bf16 MFMA
 SYRK (syrk_partial): algorithmic flops N d (d + 1) per covariance over the
@@ -38,6 +43,10 @@ def parse_args():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--bits", type=int, default=2, choices=(2, 4))
+    p.add_argument("--serial", action="store_true",
+                   help="run every stage on one stream (per-stage profiles) instead of the two-stream schedule")
+    p.add_argument("--reserve-cus", type=int, default=64,
+                   help="CUs the second stream leaves to the Cholesky factor (0: no CU mask)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's covariance sample")
     p.add_argument("--cpu-rows", type=int, default=64, help="weight rows in the oracle's sweep sample")
@@ -47,6 +56,32 @@ def parse_args():
                    help="no run: turn two rocprofv3 --pmc runs of '--copy-calibration' (FETCH_SIZE, then "
                         "WRITE_SIZE) into the per-launch HBM bytes of the roofline kernel")
     return p.parse_args()
+
+
+def side_stream(dev, reserve: int):
+    """Second stream at default priority; with reserve > 0 its kernels are kept off the last
+    `reserve` CUs of the mask (hipExtStreamCreateWithCUMask), which stay free for the
+    latency-bound Cholesky steps. (Masks with a hole in every 32-bit word are refused.)"""
+    import ctypes
+    import torch
+    if reserve <= 0:
+        return torch.cuda.Stream(device=dev)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    bits = [1] * n_cu
+    for i in range(n_cu - reserve, n_cu):
+        bits[i] = 0
+    words = [0] * ((n_cu + 31) // 32)
+    for i, b in enumerate(bits):
+        words[i // 32] |= b << (i % 32)
+    # the HIP runtime torch itself loaded (a second copy of the runtime would not know its device state)
+    own = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    hip = ctypes.CDLL(own if os.path.exists(own) else "libamdhip64.so")
+    handle = ctypes.c_void_p()
+    arr = (ctypes.c_uint32 * len(words))(*words)
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(len(words)), arr)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+    return torch.cuda.ExternalStream(handle.value, device=dev)
 
 
 def log(msg: str) -> None:
@@ -191,6 +226,9 @@ def main() -> int:
     from post_quantization_04_amd import pipeline
 
     dev = torch.device("cuda:0")
+    torch.zeros(1, device=dev)
+    # created before anything else takes a hardware queue: a CU-masked stream needs its own
+    side = None if args.serial else side_stream(dev, args.reserve_cus)
     cfg = kq_synth.config(2)
     sub = cfg.subs[0]
     dout, din, n_tok = sub.dout, sub.din, cfg.n_tokens
@@ -231,8 +269,17 @@ def main() -> int:
     ws_obs = scratch(kq.workspace_size(kq.KQ_OP_OBS, dout, din, cfg.block))
     flags = pipeline.ALL_SIDES
     stages = ["cov_x", "cov_g", "score_alloc", "biip", "cholesky", "obs"]
+    # two-stream schedule: the Cholesky factor needs only H_X'' (input side), so it runs next
+    # to the G covariance; the output side of BiIP follows on the second stream
+    w1 = torch.empty((dout, din), dtype=f64, device=dev)
+    score_x = torch.empty(1, dtype=f64, device=dev)
+    score_g = torch.empty(1, dtype=f64, device=dev)
+    s_unused_x = torch.empty(din, dtype=f64, device=dev)
+    s_unused_g = torch.empty(dout, dtype=f64, device=dev)
+    in_flags = kq.KQ_BIIP_INPUT | kq.KQ_BIIP_SCALE
+    out_flags = kq.KQ_BIIP_OUTPUT | kq.KQ_BIIP_SCALE
 
-    def step(ev=None):
+    def step_serial(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
@@ -251,6 +298,57 @@ def main() -> int:
         kq.obs_quantize(w2, hx, bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
         mark(6)
 
+    # the lead stream is not the null stream: the CU-masked side stream is a blocking stream,
+    # which the null stream would wait for
+    lead = torch.cuda.Stream(device=dev)
+
+    def step_overlap(ev=None):
+        with torch.cuda.stream(lead):
+            overlap_body(ev)
+
+    def overlap_body(ev):
+        # ev: events 0..6 on the lead stream, 7..11 on the side stream
+        main = torch.cuda.current_stream()
+        def mark(i, st):
+            if ev is not None:
+                ev[i].record(st)
+        mark(0, main)
+        kq.accumulate_cov(xd, hx, 1.0 / n_tok, 0.0, ws=ws_cov)
+        e_cov = torch.cuda.Event()
+        e_cov.record(main)  # the G covariance reuses this workspace
+        mark(1, main)
+        kq.sensitivity(hx, None, score_x, kq.KQ_SCORE_HX_ONLY)  # tr(H_X) of the raw covariance
+        mark(2, main)
+        kq.biip_rotate(wd, w1, hx, None, ri.rot, None, in_flags, s_x, s_unused_g, ws=ws_biip)
+        mark(3, main)
+        e_in = torch.cuda.Event()
+        e_in.record(main)
+        kq.cholesky_inv(hx, cfg.damp, info, ws=ws_chol)
+        mark(4, main)
+        with torch.cuda.stream(side):
+            side.wait_event(e_cov)
+            mark(7, side)
+            kq.accumulate_cov(gd, hg, 1.0 / n_tok, 0.0, ws=ws_cov)
+            mark(8, side)
+            kq.sensitivity(hg, None, score_g, kq.KQ_SCORE_HX_ONLY)  # tr(H_G) of the raw covariance
+            mark(9, side)
+            side.wait_event(e_in)
+            mark(10, side)
+            kq.biip_rotate(w1, w2, None, hg, None, ro.rot, out_flags, s_unused_x, s_g, ws=ws_biip)
+            mark(11, side)
+            e_out = torch.cuda.Event()
+            e_out.record(side)
+        main.wait_event(e_out)
+        # score = tr(H_G) tr(H_X): the same float64 product the combined call forms
+        sc = float(score_x.item()) * float(score_g.item())
+        bits = kq.allocate_bits([sc], [dout * din], [args.bits], args.bits * 1000)[0]
+        mark(5, main)
+        kq.obs_quantize(w2, hx, bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
+        mark(6, main)
+
+    step = step_serial if args.serial else step_overlap
+
+    torch.cuda.synchronize()  # inputs were uploaded on the null stream
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -259,7 +357,7 @@ def main() -> int:
         raise RuntimeError(f"Cholesky reported info = {int(info.item())}")
 
     log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(args.steps)]
     kq.timing_enable("syrk_partial")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -269,9 +367,27 @@ def main() -> int:
     wall = time.perf_counter() - t0
     launches, syrk_ms = kq.timing_query("syrk_partial")
     kq.timing_enable(None)
+    unshared = None
+    if not args.serial:
+        # the same kernel with the GPU to itself (the H_X launch of the schedule), three launches
+        kq.timing_enable("syrk_partial")
+        for _ in range(3):
+            kq.accumulate_cov(xd, hx, 1.0 / n_tok, 0.0, ws=ws_cov)
+        torch.cuda.synchronize()
+        n_u, ms_u = kq.timing_query("syrk_partial")
+        kq.timing_enable(None)
+        unshared = ms_u / max(n_u, 1)
 
     ms_step = wall * 1e3 / args.steps
-    stage_ms = {s: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, s in enumerate(stages)}
+    def span(a, b):
+        return sum(ev[a].elapsed_time(ev[b]) for ev in events) / args.steps
+    if args.serial:
+        stage_ms = {s: span(i, i + 1) for i, s in enumerate(stages)}
+    else:
+        # per-stage durations on the stream each ran on; cov_g and the BiIP output side
+        # overlap the Cholesky factor, so the stages add up to more than the step
+        stage_ms = {"cov_x": span(0, 1), "cov_g": span(7, 8), "score_alloc": span(1, 2) + span(8, 9),
+                    "biip": span(2, 3) + span(10, 11), "cholesky": span(3, 4), "obs": span(5, 6)}
     flops_cov = n_tok * din * (din + 1) + n_tok * dout * (dout + 1)
     t_accum = (stage_ms["cov_x"] + stage_ms["cov_g"]) / 1e3
     t_quant = sum(stage_ms[s] for s in ("score_alloc", "biip", "cholesky", "obs")) / 1e3
@@ -316,9 +432,19 @@ def main() -> int:
             "algorithmic_bytes": 2 * n_tok * din + 4 * din * din,
             "launches": launches,
             "avg_launch_ms": round(syrk_ms / max(launches, 1), 4),
+            "note": ("average over every launch of the timed region: the H_G launches run on the CU-masked "
+                     "second stream next to the Cholesky factor" if not args.serial else "one stream"),
         },
         "cpu_baseline": None,
     }
+    result["schedule"] = ("one stream" if args.serial else
+                          f"two streams: H_X covariance, BiIP input side and Cholesky factor on one; H_G covariance "
+                          f"and BiIP output side on the other, kept off {args.reserve_cus} CUs")
+    if unshared is not None:
+        ach = flops_cov / 2 / (unshared / 1e3) / 1e12 if unshared > 0 else 0.0
+        result["roofline"]["unshared"] = {"avg_launch_ms": round(unshared, 4), "achieved": round(ach, 2),
+                                          "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                                          "note": "3 launches on the H_X input after the timed region, GPU to itself"}
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -81,7 +81,20 @@ def side_stream(dev, reserve: int):
     rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(len(words)), arr)
     if rc != 0:
         raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+    _OWNED_STREAMS.append((hip, handle))
     return torch.cuda.ExternalStream(handle.value, device=dev)
+
+
+_OWNED_STREAMS = []
+
+
+def release_streams() -> None:
+    """Destroys the streams side_stream created (after the device is idle)."""
+    import torch
+    torch.cuda.synchronize()
+    while _OWNED_STREAMS:
+        hip, handle = _OWNED_STREAMS.pop()
+        hip.hipStreamDestroy(handle)
 
 
 def log(msg: str) -> None:
@@ -377,6 +390,7 @@ def main() -> int:
         n_u, ms_u = kq.timing_query("syrk_partial")
         kq.timing_enable(None)
         unshared = ms_u / max(n_u, 1)
+    release_streams()
 
     ms_step = wall * 1e3 / args.steps
     def span(a, b):

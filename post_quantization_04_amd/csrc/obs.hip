@@ -280,10 +280,12 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
 // extent is a multiple of 32; rows past dout read as zero and are not written.
 constexpr int kTK = 16;  // k chunk
 
+// Row pitch TM + 16 (TN + 16) doubles: the four k rows one MFMA operand read
+// touches fall on disjoint bank halves.
 template <int TM, int TN>
 struct TileLds {
-  double as[2][kTK][TM + 1];
-  double bs[2][kTK][TN + 1];
+  double as[2][kTK][TM + 16];
+  double bs[2][kTK][TN + 16];
 };
 
 template <int B, int TM, int TN, int WR, int WC>
@@ -293,39 +295,40 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
   static_assert(WR * WC == 4 && TM % (16 * WR) == 0 && TN % (16 * WC) == 0, "tile shape");
   constexpr int BM = TM / WR / 16, BN = TN / WC / 16;  // 16 x 16 blocks per wave
   constexpr int DA = TM / 16, DB = TN / 16;            // doubles of E, floats of R per thread per chunk
-  static_assert(DA % 2 == 0 && DB % 2 == 0, "vector loads");
+  static_assert(DA % 2 == 0 && (kTK * TN) % 256 == 0, "chunk shape");
   const int mv = static_cast<int>(dout - i0 < TM ? dout - i0 : TM);
   const int nv = static_cast<int>(din - j0 < TN ? din - j0 : TN);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = wave / WC, wj = wave % WC;
-  // this thread's loads: E row ar, k offset ak (DA doubles); R row bk, columns bc .. bc + DB - 1
+  // this thread's loads: E row ar, k offset ak (DA doubles); R elements tid + 256 q of the
+  // kTK x TN chunk (row (tid + 256 q) / TN, column (tid + 256 q) % TN): consecutive lanes,
+  // consecutive columns, in global memory and in LDS
   const int ar = tid / (kTK / DA), ak = (tid % (kTK / DA)) * DA;
-  const int bk = tid / (TN / DB), bc = (tid % (TN / DB)) * DB;
+  constexpr int NR = kTK * TN / 256;
+  const int bc = tid % TN, bk0 = tid / TN;
+  constexpr int BKS = 256 / TN;  // R rows between a thread's elements
   const bool a_ok = ar < mv, b_ok = bc < nv;
   const double* ap = e + (i0 + (a_ok ? ar : 0)) * B + ak;
-  const float* bp = r + (k0 + bk) * din + j0 + (b_ok ? bc : 0);
-  double2 va[DA / 2];
-  float2 vb[DB / 2];
-  auto load = [&](int kc) {
+  const float* bp = r + (k0 + bk0) * din + j0 + (b_ok ? bc : 0);
+  // two register sets: the chunk two ahead loads while one is multiplied and one waits
+  double2 va[2][DA / 2];
+  float vb[2][NR];
+  auto load = [&](int set, int kc) {
 #pragma unroll
     for (int q = 0; q < DA / 2; ++q)
-      va[q] = a_ok ? *reinterpret_cast<const double2*>(ap + kc + 2 * q) : double2{0.0, 0.0};
+      va[set][q] = a_ok ? *reinterpret_cast<const double2*>(ap + kc + 2 * q) : double2{0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < DB / 2; ++q)
-      vb[q] = b_ok ? *reinterpret_cast<const float2*>(bp + int64_t(kc) * din + 2 * q) : make_float2(0.f, 0.f);
+    for (int q = 0; q < NR; ++q) vb[set][q] = b_ok ? bp[int64_t(kc + q * BKS) * din] : 0.0f;
   };
-  auto store = [&](int buf) {
+  auto store = [&](int set, int buf) {
 #pragma unroll
     for (int q = 0; q < DA / 2; ++q) {
-      sm.as[buf][ak + 2 * q][ar] = -va[q].x;
-      sm.as[buf][ak + 2 * q + 1][ar] = -va[q].y;
+      sm.as[buf][ak + 2 * q][ar] = -va[set][q].x;
+      sm.as[buf][ak + 2 * q + 1][ar] = -va[set][q].y;
     }
 #pragma unroll
-    for (int q = 0; q < DB / 2; ++q) {
-      sm.bs[buf][bk][bc + 2 * q] = vb[q].x;
-      sm.bs[buf][bk][bc + 2 * q + 1] = vb[q].y;
-    }
+    for (int q = 0; q < NR; ++q) sm.bs[buf][bk0 + q * BKS][bc] = vb[set][q];
   };
   // D[i][j] of a 16 x 16 float64 block: lane l, register q -> i = 4 q + l / 16, j = l % 16
   // (measured on gfx950; the operands are A[i][k] at lane i + 16 k and B[k][j] at lane j + 16 k)
@@ -344,13 +347,14 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
       }
     }
   constexpr int nchunk = B / kTK;
-  load(0);
-  store(0);
+  load(0, 0);
+  if (nchunk > 1) load(1, kTK);
+  store(0, 0);
   __syncthreads();
 #pragma unroll
   for (int ch = 0; ch < nchunk; ++ch) {
     const int buf = ch & 1;
-    if (ch + 1 < nchunk) load((ch + 1) * kTK);
+    if (ch + 2 < nchunk) load(ch & 1, (ch + 2) * kTK);  // set ch & 1 was stored to LDS before this chunk
 #pragma unroll
     for (int kk = 0; kk < kTK / 4; ++kk) {
       const int kr = 4 * kk + il;
@@ -365,7 +369,7 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
         for (int y = 0; y < BN; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
-    if (ch + 1 < nchunk) store(buf ^ 1);
+    if (ch + 1 < nchunk) store((ch + 1) & 1, buf ^ 1);
     __syncthreads();
   }
 #pragma unroll

@@ -2,34 +2,34 @@
 //
 // A is [rows, d]: tokens by channels, channels contiguous. The contraction
 // runs over tokens, so each MFMA operand needs consecutive tokens of one
-// channel per lane. Panels of 32 tokens x 256 channels are copied straight
-// from global memory into LDS in their natural token-major layout
-// (global_load_lds_dwordx4, no register staging), and the MFMA fragments are
-// read with the gfx950 transposing LDS load ds_read_b64_tr_b16: in each group
-// of 16 lanes, four lanes per token supply 16 consecutive channels and lane j
-// receives channel j at the four tokens. Two such loads give the eight tokens
-// of a v_mfma_f32_32x32x16_bf16 operand. The 16-byte chunks of each 512-byte
-// token row are XOR-swizzled with the token index so that both the DMA writes
-// and the transposing reads run at the LDS bank minimum.
+// channel per lane. Panels of 32 tokens x 256 channels are staged in LDS in
+// their natural token-major layout and the MFMA fragments are read with the
+// gfx950 transposing LDS load ds_read_b64_tr_b16: in each group of 16 lanes,
+// four lanes per token supply 16 consecutive channels and lane j receives
+// channel j at the four tokens. Two such loads give the eight tokens of a
+// v_mfma_f32_32x32x16_bf16 operand. The 16-byte chunks of each 512-byte token
+// row are XOR-swizzled with the token index so that both the LDS writes and
+// the transposing reads run at the LDS bank minimum.
 //
-// Pipeline: four 32 KB stage buffers (both panels of 32 tokens; a diagonal
-// tile loads its one panel twice) form a ring in LDS. Loads run three stages
-// ahead (two stages in flight when a stage is awaited; a deeper ring measured
-// no faster). Each buffer is its own __shared__ object and the ring is
-// unrolled, so the compiler can tell the buffer being read from the ones
-// being filled and does not drain the DMA queue before each LDS read. Before
-// the one barrier per stage, each wave waits (vmcnt) only for its own loads
-// of the next stage. Fragments are double buffered in registers: the reads of
-// the next k-step are interleaved with the MFMAs of the current one, and the
-// first reads of the next stage are issued right after the barrier, in the
-// middle of the last k-step, together with the refill of the buffer just
-// consumed.
+// Staging: each lane loads its 16-byte chunks of a stage (both panels) into
+// registers with buffer loads, three stages ahead, and writes them to LDS with
+// ds_write_b128; three LDS stage buffers rotate with the three register sets.
+// The buffer resource of a stage ends at the slice's last token, so rows past
+// it (a partial last stage) load as zeros with no extra code. Measured against
+// copying global -> LDS directly (global_load_lds_dwordx4) on the 262144 x
+// 4096 covariance: 3.93 vs 4.37 ms per launch, exact same sums.
 //
-// A final partial stage is loaded from the last 32 tokens of the slice and
-// the rows already counted by the previous stage are zeroed in LDS; the stage
-// count is padded to whole rings with zeroed stages (a full 8192-token slice
-// is exactly 64 rings). Rows that are not 16-byte aligned, or fewer than 32
-// rows in all, take a plain register-staged kernel.
+// Schedule of one stage (one barrier): first half, the 16 MFMAs of the
+// stage's first 16-token k-step with the 16 transposing reads of its second
+// k-step and the second half of the next stage's LDS writes; barrier; second
+// half, the 16 MFMAs of the second k-step with the reads of the next stage's
+// first k-step, the first half of the stage after next's writes and the loads
+// refilling the register set just written. One MFMA per LDS read throughout,
+// one LDS write per four MFMAs, so the LDS traffic is even over the stage.
+//
+// Diagonal tiles (I = J) load their one panel once and read both operands from
+// it; the wave whose 128 x 128 block lies above the diagonal only helps stage
+// the panel (that block is never read).
 //
 // Work item = (lower-triangle 256 x 256 output tile, token slice of 8192
 // rows). Each workgroup sums one slice in float32 MFMA accumulators (bf16
@@ -53,45 +53,34 @@ namespace {
 
 constexpr int kT = 256;          // output tile edge (channels)
 constexpr int kKT = 32;          // tokens per LDS stage
-constexpr int kNB = 4;           // stage buffers in the ring (2..8)
-// tokens per float32 partial sum: whole rings, at most 8192 tokens
-constexpr int kSlice = 8192 / (kNB * kKT) * (kNB * kKT);
+constexpr int kNS = 3;           // register sets = LDS stage buffers = unroll period
+constexpr int kSlice = 8192;     // tokens per float32 partial sum
 constexpr int kThreads = 256;    // 4 waves in a 2 x 2 grid, 128 x 128 outputs each
 constexpr int kPanelUnits = kT * kKT * 2 / 16;  // 16-byte units per LDS panel (1024)
 constexpr int kPanelBytes = kPanelUnits * 16;
-constexpr int kUnitsPerLane = kPanelUnits / kThreads;  // DMA loads per lane per panel (4)
+constexpr int kUnitsPerLane = kPanelUnits / kThreads;  // 16-byte loads per lane per panel (4)
 constexpr int kTargetItems = 8192;  // work items per launch before slices are split into groups
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using Rsrc = __amdgpu_buffer_rsrc_t;
 
 #define KQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-#define KQ_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
 
-// The ring: one __shared__ object per stage buffer, panel I then panel J
-// (only the first kNB are referenced, and only those are allocated).
-[[maybe_unused]] __shared__ uint4 ring0[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring1[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring2[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring3[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring4[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring5[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring6[2 * kPanelUnits];
-[[maybe_unused]] __shared__ uint4 ring7[2 * kPanelUnits];
-static_assert(kNB >= 2 && kNB <= 8 && kNB * 2 * kPanelUnits * 16 <= 160 * 1024, "ring must fit in LDS");
+// The three stage buffers (panel I, then panel J), each its own __shared__
+// object so the compiler can tell the buffer being read from the ones being
+// written.
+__shared__ uint4 stage0[2 * kPanelUnits];
+__shared__ uint4 stage1[2 * kPanelUnits];
+__shared__ uint4 stage2[2 * kPanelUnits];
 
 template <int K>
-__device__ __forceinline__ uint4* ring() {
-  static_assert(K >= 0 && K < kNB, "ring index");
-  if constexpr (K == 0) return ring0;
-  else if constexpr (K == 1) return ring1;
-  else if constexpr (K == 2) return ring2;
-  else if constexpr (K == 3) return ring3;
-  else if constexpr (K == 4) return ring4;
-  else if constexpr (K == 5) return ring5;
-  else if constexpr (K == 6) return ring6;
-  else return ring7;
+__device__ __forceinline__ uint4* stage_buf() {
+  if constexpr (K % 3 == 0) return stage0;
+  else if constexpr (K % 3 == 1) return stage1;
+  else return stage2;
 }
 
 // 16-byte slot of (token t, channel chunk cc) in a panel stage: 32 chunks per
@@ -133,28 +122,31 @@ struct Frags {
   bf16x8 a[4], b[4];
 };
 
+// Reads in the order the MFMAs need them: row block 0's operand and the four
+// column blocks first.
 __device__ __forceinline__ void read_frags(const char* buf, int kk, const int32_t (&oa)[4], const int32_t (&ob)[4],
                                            Frags& f) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x) f.a[x] = frag_at(buf + oa[x] + kk * 8192);
+  f.a[0] = frag_at(buf + oa[0] + kk * 8192);
 #pragma unroll
   for (int y = 0; y < 4; ++y) f.b[y] = frag_at(buf + ob[y] + kk * 8192);
+#pragma unroll
+  for (int x = 1; x < 4; ++x) f.a[x] = frag_at(buf + oa[x] + kk * 8192);
 }
 
-// MFMAs of row blocks x0 .. x1 - 1 against all 4 column blocks.
-__device__ __forceinline__ void mfma_rows(const Frags& f, int x0, int x1, f32x16 (&acc)[4][4]) {
+// MFMAs of one k-step: 4 row blocks x 4 column blocks.
+__device__ __forceinline__ void mfma_all(const Frags& f, f32x16 (&acc)[4][4]) {
 #pragma unroll
-  for (int x = x0; x < x1; ++x)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y)
       acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
-// Per-lane byte offsets (from a stage origin a + t0 * lda) of the chunks this
-// lane copies into a panel: load i of wave w fills slot w * 256 + i * 64 +
+// Per-lane byte offsets (from a stage's first token row) of the chunks this
+// lane stages from a panel: load i of wave w fills slot w * 256 + i * 64 +
 // lane, whose chunk is the un-swizzled position. Chunks past channel d re-read
 // the row's last 8 channels (their outputs are discarded).
-__device__ __forceinline__ void dma_offsets(int64_t lda, int64_t d, int64_t c0, uint32_t (&off)[kUnitsPerLane]) {
+__device__ __forceinline__ void chunk_offsets(int64_t lda, int64_t d, int64_t c0, uint32_t (&off)[kUnitsPerLane]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < kUnitsPerLane; ++i) {
@@ -167,25 +159,19 @@ __device__ __forceinline__ void dma_offsets(int64_t lda, int64_t d, int64_t c0, 
   }
 }
 
-// Issues the DMA copies of one stage (both panels) into ring buffer K.
-template <int K>
-__device__ __forceinline__ void dma_stage(const char* origin, const uint32_t (&da)[kUnitsPerLane],
-                                          const uint32_t (&db)[kUnitsPerLane], int wave) {
-  uint4* dst = ring<K>() + wave * (kUnitsPerLane * 64);
-#pragma unroll
-  for (int i = 0; i < kUnitsPerLane; ++i)
-    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(origin + da[i]), KQ_LDS(dst + i * 64), 16, 0, 0);
-#pragma unroll
-  for (int i = 0; i < kUnitsPerLane; ++i)
-    __builtin_amdgcn_global_load_lds(KQ_GLOBAL(origin + db[i]), KQ_LDS(dst + kPanelUnits + i * 64), 16, 0, 0);
-}
-
 // Workgroup barrier without the full memory drain of __syncthreads (which
 // would also wait for the loads of the stages still in flight).
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Uniform per-workgroup state of the ring kernel.
-struct Ring {
+// One stage of both panels (one panel for a diagonal tile) in registers:
+// panel I units 0..3, then panel J units 0..3.
+struct RegStage {
+  uint4 v[2 * kUnitsPerLane];
+};
+
+// Uniform per-workgroup state of the pipeline. DIAG: I = J, one panel.
+template <bool DIAG>
+struct Pipe {
   const char* a;        // A as bytes
   int64_t lda2;         // row pitch in bytes
   int64_t tok_begin, tok_end;
@@ -194,86 +180,96 @@ struct Ring {
   uint32_t da[kUnitsPerLane], db[kUnitsPerLane];
   int32_t oa[4], ob[4];
 
-  // First token copied for stage q: a partial last stage is shifted back to
-  // end at tok_end, and stages past the end (which pad the count to whole
-  // rings and keep the number of copies in flight constant) repeat the last
-  // stage and are zeroed once landed.
-  __device__ __forceinline__ int64_t origin_token(int q) const {
-    const int qq = q < nstage ? q : nstage - 1;
-    const int64_t t0 = tok_begin + int64_t(qq) * kKT;
-    return t0 + kKT <= tok_end ? t0 : tok_end - kKT;
-  }
-  template <int K>
-  __device__ __forceinline__ void issue(int q) const {
-    dma_stage<K>(a + origin_token(q) * lda2, da, db, wave);
-  }
-  // Makes stage q (in ring buffer K) visible to all waves, with the copies of
-  // the kNB - 2 following stages still in flight. The rows of a partial stage
-  // that precede its first token, and all rows of a stage past the end, are
-  // zeroed by the lanes that copied them.
-  template <int K>
-  __device__ __forceinline__ void land(int q) const {
-    // s_waitcnt vmcnt((kNB - 2) stages x 8 copies) lgkmcnt(0): fields
-    // vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8], vmcnt[5:4] at [15:14]
-    constexpr int vm = (kNB - 2) * 2 * kUnitsPerLane;
-    static_assert(vm < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | 0x70);
-    const int dup = q < nstage ? static_cast<int>(tok_begin + int64_t(q) * kKT - origin_token(q)) : kKT;
-    const int lane = threadIdx.x & 63;
-    uint4* dst = ring<K>() + wave * (kUnitsPerLane * 64);
+  // Stage q's 32 token rows through a buffer resource that ends at tok_end:
+  // rows at or past it (a partial last stage, the stages loaded past the end
+  // of the slice) read as 0.
+  __device__ __forceinline__ void load(int q, RegStage& r) const {
+    const int64_t t0 = tok_begin + int64_t(q) * kKT;
+    int64_t left = tok_end - t0;
+    left = left < 0 ? 0 : (left > kKT ? kKT : left);
+    const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a + t0 * lda2), static_cast<short>(0),
+                                                      static_cast<int>(left * lda2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < kUnitsPerLane; ++i) {
-      if (((wave * (kUnitsPerLane * 64) + i * 64 + lane) >> 5) < dup) {
-        dst[i * 64 + lane] = make_uint4(0, 0, 0, 0);
-        dst[kPanelUnits + i * 64 + lane] = make_uint4(0, 0, 0, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, da[i], 0, 0);
+      r.v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    if constexpr (!DIAG) {
+#pragma unroll
+      for (int i = 0; i < kUnitsPerLane; ++i) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, db[i], 0, 0);
+        r.v[kUnitsPerLane + i] = make_uint4(x[0], x[1], x[2], x[3]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-    barrier();
+  }
+  // Half P (units 2P, 2P + 1) of the stage in r into stage buffer K.
+  template <int K, int P>
+  __device__ __forceinline__ void store(const RegStage& r) const {
+    const int lane = threadIdx.x & 63;
+    uint4* dst = stage_buf<K>() + wave * (kUnitsPerLane * 64);
+#pragma unroll
+    for (int i = 2 * P; i < 2 * P + 2; ++i) {
+      dst[i * 64 + lane] = r.v[i];
+      if constexpr (!DIAG) dst[kPanelUnits + i * 64 + lane] = r.v[kUnitsPerLane + i];
+    }
   }
 };
 
-// One stage of the ring kernel: stage s in buffer K, its first k-step's
-// fragments already in f0. Straight-line code: the refill, the barrier and
-// the next stage's first reads run even past the last stage (on zeroed
-// copies), so that the MFMA sequence has no branches.
-template <int K>
-__device__ __forceinline__ void ring_step(const Ring& r, int s, Frags& f0, Frags& f1, f32x16 (&acc)[4][4]) {
-  constexpr int KN = (K + 1) % kNB;
-  read_frags(reinterpret_cast<const char*>(ring<K>()), 1, r.oa, r.ob, f1);
-  mfma_rows(f0, 0, 4, acc);
+// Instruction interleave of one half stage: 16 x (MFMA, LDS read), with an
+// LDS write (and, in the second half, two global loads) every 4 MFMAs (every
+// 8 for a diagonal tile).
+template <int G, bool DIAG, bool LOADS>
+__device__ __forceinline__ void interleave() {
+  // one LDS write per group: 4 writes per half stage (2 for one panel)
+  constexpr int kGroups = DIAG ? 2 : 4;
+  constexpr int kPer = 16 / kGroups;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  mfma_rows(f1, 0, 2, acc);
-  // keep the wait and barrier after all MFMAs that precede them
-  __builtin_amdgcn_sched_barrier(0);
-  r.land<KN>(s + 1);
-  __builtin_amdgcn_sched_barrier(0);
-  // every wave is past its reads of stage s: refill its buffer with stage s + kNB
-  r.issue<K>(s + kNB);
-  read_frags(reinterpret_cast<const char*>(ring<KN>()), 0, r.oa, r.ob, f0);
-  mfma_rows(f1, 2, 4, acc);
+  for (int i = 0; i < kGroups; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, G);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, G);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, G);  // LDS write
+    if constexpr (LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 2, G);  // global load
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    for (int j = 1; j < kPer; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, G);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, G);
+    }
   }
 }
 
-// The kNB stages of one trip around the ring.
-template <int... K>
-__device__ __forceinline__ void ring_round(const Ring& r, int s, Frags& f0, Frags& f1, f32x16 (&acc)[4][4],
-                                           std::integer_sequence<int, K...>) {
-  (ring_step<K>(r, s + K, f0, f1, acc), ...);
+// One stage: stage s in buffer K % 3, its first k-step's fragments in f0.
+// IDLE: the wave above the diagonal of a diagonal tile, which stages data but
+// computes nothing.
+template <int K, bool DIAG, bool IDLE>
+__device__ __forceinline__ void stage_step(const Pipe<DIAG>& p, int s, RegStage (&regs)[kNS], Frags& f0, Frags& f1,
+                                           f32x16 (&acc)[4][4]) {
+  if constexpr (!IDLE) {
+    read_frags(reinterpret_cast<const char*>(stage_buf<K>()), 1, p.oa, p.ob, f1);
+    mfma_all(f0, acc);
+  }
+  p.template store<K + 1, 1>(regs[(K + 1) % kNS]);
+  if constexpr (!IDLE) interleave<0, DIAG, false>();
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's writes of stage s + 1 and reads of stage s are done
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  // stage s + 1 is fully written (register set (K + 1) % 3 is free again)
+  p.load(s + 1 + kNS, regs[(K + 1) % kNS]);
+  if constexpr (!IDLE) {
+    read_frags(reinterpret_cast<const char*>(stage_buf<K + 1>()), 0, p.oa, p.ob, f0);
+    mfma_all(f1, acc);
+  }
+  // buffer (K + 2) % 3 held stage s - 1, whose reads all finished before the barrier
+  p.template store<K + 2, 0>(regs[(K + 2) % kNS]);
+  if constexpr (!IDLE) interleave<1, DIAG, true>();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int... K>
-__device__ __forceinline__ void issue_first(const Ring& r, std::integer_sequence<int, K...>) {
-  (r.issue<K>(K), ...);
+template <bool DIAG, bool IDLE, int... K>
+__device__ __forceinline__ void stage_round(const Pipe<DIAG>& p, int s, RegStage (&regs)[kNS], Frags& f0, Frags& f1,
+                                            f32x16 (&acc)[4][4], std::integer_sequence<int, K...>) {
+  (stage_step<K, DIAG, IDLE>(p, s + K, regs, f0, f1, acc), ...);
 }
 
 // Writes a wave's 128 x 128 float32 accumulators into the partial tile.
@@ -291,6 +287,57 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[4][4], float* __re
         const int j = wj * 128 + y * 32 + (lane & 31);
         out[i * kT + j] = acc[x][y][r];
       }
+}
+
+// The slice loop of one work item.
+template <bool DIAG, bool IDLE>
+__device__ __forceinline__ void slice_sum(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t tok_begin,
+                                          int64_t tok_end, int I, int J, float* __restrict__ out) {
+  Pipe<DIAG> p;
+  p.a = reinterpret_cast<const char*>(a);
+  p.lda2 = lda * 2;
+  p.tok_begin = tok_begin;
+  p.tok_end = tok_end;
+  p.nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
+  p.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wi = p.wave >> 1, wj = p.wave & 1;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    p.oa[x] = tr_offset(wi * 128 + x * 32);
+    p.ob[x] = tr_offset(wj * 128 + x * 32) + (DIAG ? 0 : kPanelBytes);
+  }
+  chunk_offsets(lda, d, int64_t(I) * kT, p.da);
+  chunk_offsets(lda, d, int64_t(J) * kT, p.db);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
+
+  // prologue: stages 0, 1, 2 in register sets 0, 1, 2; stage 0 and the first
+  // half of stage 1 written; set 0 refilled with stage 3
+  RegStage regs[kNS];
+  p.load(0, regs[0]);
+  p.load(1, regs[1]);
+  p.load(2, regs[2]);
+  p.template store<0, 0>(regs[0]);
+  p.template store<0, 1>(regs[0]);
+  p.template store<1, 0>(regs[1]);
+  p.load(kNS, regs[0]);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  barrier();
+  Frags f0, f1;
+  if constexpr (!IDLE) read_frags(reinterpret_cast<const char*>(stage_buf<0>()), 0, p.oa, p.ob, f0);
+  int s = 0;
+  for (; s + kNS <= p.nstage; s += kNS)
+    stage_round<DIAG, IDLE>(p, s, regs, f0, f1, acc, std::make_integer_sequence<int, kNS>{});
+  // the one or two stages left (uniform branches)
+  if (s < p.nstage) stage_step<0, DIAG, IDLE>(p, s, regs, f0, f1, acc);
+  if (s + 1 < p.nstage) stage_step<1, DIAG, IDLE>(p, s + 1, regs, f0, f1, acc);
+  // no load may still be writing this wave's registers when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (!IDLE) store_acc(acc, out);
 }
 
 // Work item of blockIdx.x; workgroups are dispatched round robin over the
@@ -325,8 +372,8 @@ __global__ void tile_order_kernel(int nt, int* __restrict__ order) {
         for (int j = bj; j < bj + 8 && j <= i; ++j) order[r++] = i * (i + 1) / 2 + j;
 }
 
-// Ring kernel: needs 16-byte aligned rows (lda, d multiples of 8, A aligned)
-// and rows >= 32.
+// Pipelined kernel: needs 16-byte aligned rows (lda, d multiples of 8, A
+// aligned) and 32 rows of A addressable with 32-bit byte offsets.
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
     const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
     int nsl, int gsz, const int* __restrict__ order, float* __restrict__ part) {
@@ -334,40 +381,16 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
   if (!work_item(ntiles, nsl, gsz, order, sl, tile)) return;
   int I, J;
   tri(tile, I, J);
-  Ring r;
-  r.a = reinterpret_cast<const char*>(a);
-  r.lda2 = lda * 2;
-  r.tok_begin = int64_t(slice0 + sl) * kSlice;
-  r.tok_end = r.tok_begin + kSlice < rows ? r.tok_begin + kSlice : rows;
-  r.nstage = static_cast<int>((r.tok_end - r.tok_begin + kKT - 1) / kKT);
-  r.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int wi = r.wave >> 1, wj = r.wave & 1;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    r.oa[x] = tr_offset(wi * 128 + x * 32);
-    r.ob[x] = tr_offset(wj * 128 + x * 32) + kPanelBytes;
-  }
-  dma_offsets(lda, d, int64_t(I) * kT, r.da);
-  dma_offsets(lda, d, int64_t(J) * kT, r.db);
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
-
-  // prologue: stages 0 .. kNB - 1 issued, stage 0 landed, its first fragments read
-  issue_first(r, std::make_integer_sequence<int, kNB - 1>{});
-  r.land<0>(0);
-  r.issue<kNB - 1>(kNB - 1);
-  Frags f0, f1;
-  read_frags(reinterpret_cast<const char*>(ring<0>()), 0, r.oa, r.ob, f0);
-
-  // whole rings only: stages past nstage are zero and add nothing
-  for (int s = 0; s < r.nstage; s += kNB) ring_round(r, s, f0, f1, acc, std::make_integer_sequence<int, kNB>{});
-  // no copy may still be writing this workgroup's LDS when it exits
-  __builtin_amdgcn_s_waitcnt(0);
-  store_acc(acc, part + (int64_t(sl) * ntiles + tile) * (kT * kT));
+  const int64_t tok_begin = int64_t(slice0 + sl) * kSlice;
+  const int64_t tok_end = tok_begin + kSlice < rows ? tok_begin + kSlice : rows;
+  float* out = part + (int64_t(sl) * ntiles + tile) * (kT * kT);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (I != J)
+    slice_sum<false, false>(a, lda, d, tok_begin, tok_end, I, J, out);
+  else if (wave == 1)  // block (rows 0..127, columns 128..255): above the diagonal
+    slice_sum<true, true>(a, lda, d, tok_begin, tok_end, I, J, out);
+  else
+    slice_sum<true, false>(a, lda, d, tok_begin, tok_end, I, J, out);
 }
 
 // Register-staged copy of one panel stage with zero fill for tokens >=
@@ -388,8 +411,8 @@ __device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, 
   }
 }
 
-// Fallback for unaligned rows or fewer than 32 rows: two register-staged
-// buffers, one full barrier per stage.
+// Fallback for rows that are not 16-byte aligned: element loads with zero
+// fill, two LDS buffers, one full barrier per stage.
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial_regs(
     const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
     int nsl, int gsz, const int* __restrict__ order, float* __restrict__ part) {
@@ -425,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial_regs(
 #pragma unroll
     for (int kk = 0; kk < kKT / 16; ++kk) {
       read_frags(reinterpret_cast<const char*>(buf), kk, oa, ob, f);
-      mfma_rows(f, 0, 4, acc);
+      mfma_all(f, acc);
     }
   }
   store_acc(acc, part + (int64_t(sl) * ntiles + tile) * (kT * kT));
@@ -569,11 +592,10 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   float* part = static_cast<float*>(ws);
   double* acc = reinterpret_cast<double*>(static_cast<char*>(ws) + p.part_bytes);
   int* order = reinterpret_cast<int*>(static_cast<char*>(ws) + p.part_bytes + p.acc_bytes);
-  // The DMA ring copies whole 16-byte chunks of aligned rows, addresses a
-  // stage with 32-bit byte offsets, and shifts a partial last stage back
-  // inside A (needs 32 rows).
-  const bool ring_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
-                       rows >= kKT && int64_t(kKT) * lda * 2 < (int64_t(1) << 31);
+  // The pipelined kernel loads whole 16-byte chunks of aligned rows and
+  // addresses a stage with 32-bit byte offsets.
+  const bool pipe_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
+                       int64_t(kKT) * lda * 2 < (int64_t(1) << 31);
   {
     LaunchTimer timer("tile_order_kernel", st);
     hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(64), 0, st, p.nt, order);
@@ -586,10 +608,10 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
     // whole slices per XCD when there are enough of them, else tile groups
     const int gsz = nsl >= kXcds ? 0 : (p.ntiles + kXcds - 1) / kXcds;
     const int per_xcd = gsz == 0 ? p.ntiles * ((nsl + kXcds - 1) / kXcds) : gsz * nsl;
-    const char* kname = ring_ok ? "syrk_partial" : "syrk_partial_regs";
+    const char* kname = pipe_ok ? "syrk_partial" : "syrk_partial_regs";
     {
       LaunchTimer timer(kname, st);
-      hipLaunchKernelGGL(ring_ok ? syrk_partial : syrk_partial_regs, dim3(static_cast<unsigned>(per_xcd * kXcds)),
+      hipLaunchKernelGGL(pipe_ok ? syrk_partial : syrk_partial_regs, dim3(static_cast<unsigned>(per_xcd * kXcds)),
                          dim3(kThreads), 0, st, a, lda, d, rows, p.ntiles, s0, nsl, gsz, order, part);
     }
     kq_status s = check_launch(kname);

@@ -6,19 +6,24 @@
 //   1. damping: delta = damp * mean(diag H) in float64;
 //   2. reversal copy A = J H J + delta I into scratch, padded to a multiple of
 //      64 with an identity block;
-//   3. blocked right-looking Cholesky of A with 64 x 64 blocks, one launch
-//      per step: the diagonal role brings block column kb up to date with the
-//      previous panel (float64 MFMA), factors and inverts the diagonal block
-//      in float64 in LDS (every workgroup of the role does this itself), and
-//      each workgroup multiplies one 64-row block of the panel by the inverse;
-//      in the same launch the update role applies the previous panel's
-//      rank-64 update to the block columns beyond kb in 128 x 128 tiles on
-//      float32 MFMA (v_mfma_f32_32x32x2f32);
-//   4. M = L^-1 by recursive doubling: diagonal blocks are already inverted;
-//      at each level, neighbouring blocks (B1, B2) merge with
-//      M21 = -M22 (L21 M11), two batched 128 x 128-tile MFMA products that
-//      skip the zero triangles of M11 and M22;
-//   5. R = J M J written over H (strict lower triangle zeroed).
+//   3. blocked right-looking Cholesky of A with 64 x 64 blocks, and one step
+//      behind it M = L^-1 by blocked forward substitution; one launch per
+//      step kb = 0 .. nb (the last one only finishes M):
+//      * the diagonal role brings block column kb up to date with the
+//        previous panel (float64 MFMA), factors and inverts the diagonal
+//        block in float64 in LDS (every workgroup of the role does this
+//        itself); workgroup 0 stores M_kk = L_kk^-1 and each other one
+//        multiplies one 64-row block of the panel by L_kk^-T;
+//      * the row role forms row j = kb - 1 of M, one 64 x 64 block per
+//        workgroup, from the stored M_jj:
+//          M[j, c] = -M_jj (S[j, c] + L[j, j-1] M[j-1, c]),   c < j,
+//        where S[i, c] = sum over i' < i - 1 of L[i, i'] M[i', c] has been
+//        accumulated in M's lower blocks by the earlier launches;
+//      * the update role applies the previous panel, A[i, j'] -=
+//        L[i, kb-1] L[j', kb-1]^T to the block columns beyond kb, and adds
+//        S[i, c] += L[i, kb-2] M[kb-2, c] to the rows from kb on, in
+//        128 x 128 tiles on float32 MFMA (v_mfma_f32_32x32x2f32);
+//   4. R = J M J written over H (strict lower triangle zeroed).
 // A pivot that is not positive and finite stops the chain: `info` takes the
 // original index + 1 and every later kernel returns at once.
 #include "kq_internal.h"
@@ -204,9 +209,10 @@ __global__ __launch_bounds__(256) void damp_kernel(const float* __restrict__ h, 
   }
 }
 
-// A[i][j] = H[d-1-i][d-1-j] + delta [i == j]; identity outside d.
+// A[i][j] = H[d-1-i][d-1-j] + delta [i == j]; identity outside d. The
+// lower triangle of M (the running sums S of the substitution) starts at 0.
 __global__ void reverse_kernel(const float* __restrict__ h, int64_t d, int64_t dp, const double* __restrict__ delta,
-                               float* __restrict__ a) {
+                               float* __restrict__ a, float* __restrict__ m) {
   const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t i = blockIdx.y;
   if (j >= dp) return;
@@ -218,6 +224,7 @@ __global__ void reverse_kernel(const float* __restrict__ h, int64_t d, int64_t d
     v = (i == j) ? 1.0f : 0.0f;
   }
   a[i * dp + j] = v;
+  if (j <= i) m[i * dp + j] = 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -252,6 +259,17 @@ __device__ __forceinline__ f64x4 mm16f(const float* a, const double* b, f64x4 ac
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(a[r * kP + 4 * kk + c]), b[r * kP + 4 * kk + c],
+                                               acc, 0, 0, 0);
+  return acc;
+}
+
+// acc += A16 * B16 with A16 float64 (pitch kP) and B16 float32 in LDS (pitch kP floats, [k][j]).
+__device__ __forceinline__ f64x4 mm16df(const double* a, const float* b, f64x4 acc) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[r * kP + 4 * kk + c], static_cast<double>(b[(4 * kk + c) * kP + r]),
                                                acc, 0, 0, 0);
   return acc;
 }
@@ -370,8 +388,9 @@ __device__ int base16(double* l, double* x, int o) {
 }
 
 // Shared memory of the diagonal role: the diagonal block, its inverse, the
-// previous panel's rows of this block, and this workgroup's panel block with
-// its previous-panel rows (float32).
+// previous panel's rows of this block, and this workgroup's operand block with
+// its second operand (float32): a panel block and its previous-panel rows, or
+// a block S[kb, c] and the block M[kb-1, c].
 struct DiagLds {
   double l[kB * kP];
   double x[kB * kP];
@@ -513,16 +532,13 @@ __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict_
     if (s < t) store16(x + 16 * t * kP + 16 * s, mv, -1.0);
     __syncthreads();
   }
-  if (!panel) {
-    // L_kk^-1 into M, zeros into the M block to its right (read as the zero
-    // upper triangle by the 128-wide merge tiles). L_kk itself stays out of A:
-    // no later kernel reads a diagonal block of L, and every workgroup of this
-    // launch reads A_kk from A, possibly after this one has finished.
-    const bool right = o + kB < dp;
+  if (b == 0) {
+    // L_kk^-1 into M. L_kk itself stays out of A: no later kernel reads a
+    // diagonal block of L, and every workgroup of this launch reads A_kk from
+    // A, possibly after this one has finished.
     for (int e = tid; e < kB * kB; e += 256) {
       const int i = e >> 6, j = e & 63;
       m[(o + i) * dp + o + j] = static_cast<float>(x[i * kP + j]);
-      if (right) m[(o + i) * dp + o + kB + j] = 0.0f;
     }
     return;
   }
@@ -546,63 +562,98 @@ __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict_
   }
 }
 
-// Update role of step kb >= 1, tile u: A[i, j] -= L[i, kb-1] L[j, kb-1]^T for
-// block columns kb + 1 <= j <= i (128 x 128 tiles; a diagonal tile also
-// rewrites the upper half of its 64 x 64 diagonal blocks, which is never read).
-// Block column kb receives the same update in the diagonal role.
-__device__ void update_role(GemmLds& sm, float* __restrict__ a, int64_t dp, int kb, int u) {
-  int I, J;
-  tri(u, I, J);
-  const int64_t op = int64_t(kb - 1) * kB, c0 = int64_t(kb + 1) * kB;
-  const int64_t ri = c0 + int64_t(I) * kG, rj = c0 + int64_t(J) * kG;
-  const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
-  const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
-  gemm128<true>(sm, a + ri * dp + op, dp, a + rj * dp + op, dp, a + ri * dp + rj, dp, mv, nv, 0, kB, -1.0f, 1.0f);
+// Row role: block c < j of row j >= 1 of M = L^-1,
+//   M[j, c] = -M_jj (S[j, c] + L[j, j-1] M[j-1, c]),
+// in float64 MFMA from float32 operands; M_jj, L[j, j-1] and M[j-1, c] were
+// stored by earlier launches, S[j, c] is complete (its last term is the one
+// added here).
+__device__ void row_role(DiagLds& sm, const float* __restrict__ a, float* __restrict__ m, int64_t dp, int j, int c) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t o = int64_t(j) * kB, op = o - kB, c0 = int64_t(c) * kB;
+  float sv[16], lv[16], xv[16], mv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, i = e >> 6, jj = e & 63;
+    sv[q] = m[(o + i) * dp + c0 + jj];   // S[j, c]
+    lv[q] = a[(o + i) * dp + op + jj];   // L[j, j-1]
+    xv[q] = m[(op + i) * dp + c0 + jj];  // M[j-1, c]
+    mv[q] = m[(o + i) * dp + o + jj];    // M_jj
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q, i = e >> 6, jj = e & 63;
+    sm.pb[i * kP + jj] = static_cast<double>(sv[q]);
+    sm.lp[i * kP + jj] = static_cast<double>(lv[q]);
+    sm.lb[i * kP + jj] = xv[q];
+    sm.x[i * kP + jj] = static_cast<double>(mv[q]);
+  }
+  __syncthreads();
+  // P = S + L[j, j-1] M[j-1, c]: wave w owns tile row w
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f64x4 acc = load16(sm.pb + 16 * wave * kP + 16 * q);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mm16df(sm.lp + 16 * wave * kP + 16 * ks, sm.lb + 16 * ks * kP + 16 * q, acc);
+    store16(sm.l + 16 * wave * kP + 16 * q, acc, 1.0);
+  }
+  __syncthreads();
+  // M[j, c] = -M_jj P (M_jj lower: tile row w needs tile rows u <= w of P)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f64x4 acc = f64x4{};
+    for (int u = 0; u <= wave; ++u) acc = mm16<false>(sm.x + 16 * wave * kP + 16 * u, sm.l + 16 * u * kP + 16 * q, acc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = 16 * wave + 4 * w + (lane >> 4), jj = 16 * q + (lane & 15);
+      m[(o + i) * dp + c0 + jj] = static_cast<float>(-acc[w]);
+    }
+  }
 }
 
-// Step kb of the blocked factorization: workgroups [0, n_diag) take the
-// diagonal role, the rest the update role of the previous step's panel. The
-// two roles write disjoint block columns (kb, and kb + 1 onwards), so one
-// launch per step suffices.
+// Update role of step kb >= 1, tile u. Tiles u < n_trail: A[i, j] -=
+// L[i, kb-1] L[j, kb-1]^T for block columns kb + 1 <= j <= i (128 x 128
+// tiles; a diagonal tile also rewrites the upper half of its 64 x 64 diagonal
+// blocks, which is never read); block column kb receives the same update in
+// the diagonal role. Tiles u >= n_trail (kb >= 2): S[i, c] += L[i, kb-2]
+// M[kb-2, c] for row blocks i >= kb and column blocks c <= kb - 2; row kb - 1
+// takes this term in the row role.
+__device__ void update_role(GemmLds& sm, float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb, int u,
+                            int n_trail) {
+  const int64_t op = int64_t(kb - 1) * kB, c0 = int64_t(kb + 1) * kB;
+  if (u < n_trail) {
+    int I, J;
+    tri(u, I, J);
+    const int64_t ri = c0 + int64_t(I) * kG, rj = c0 + int64_t(J) * kG;
+    const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
+    const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
+    gemm128<true>(sm, a + ri * dp + op, dp, a + rj * dp + op, dp, a + ri * dp + rj, dp, mv, nv, 0, kB, -1.0f, 1.0f);
+    return;
+  }
+  u -= n_trail;
+  const int ncol = kb / 2;  // 128-wide tiles over columns [0, 64 (kb - 1))
+  const int64_t o2 = int64_t(kb - 2) * kB;
+  const int64_t ri = int64_t(kb) * kB + int64_t(u / ncol) * kG, cj = int64_t(u % ncol) * kG;
+  const int64_t cend = int64_t(kb - 1) * kB;
+  const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
+  const int nv = static_cast<int>(cend - cj < kG ? cend - cj : kG);
+  gemm128<false>(sm, a + ri * dp + o2, dp, m + o2 * dp + cj, dp, m + ri * dp + cj, dp, mv, nv, 0, kB, 1.0f, 1.0f);
+}
+
+// Step kb of the blocked factorization and substitution: workgroups
+// [0, n_diag) take the diagonal role, the next n_row the row role (row kb - 1
+// of M), the rest the update role. The roles write disjoint blocks (block
+// column kb of A and diagonal block kb of M; row kb - 1 of M; the columns
+// beyond kb of A and the rows from kb on of M) and read none that another
+// role of the launch writes, so one launch per step suffices.
 __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb,
-                                                   int64_t d, int n_diag, int32_t* __restrict__ info) {
+                                                   int64_t d, int n_diag, int n_row, int n_trail,
+                                                   int32_t* __restrict__ info) {
   __shared__ StepLds sm;
   if (*info) return;
-  if (static_cast<int>(blockIdx.x) < n_diag) diag_role(sm.dg, a, m, dp, kb, d, info, blockIdx.x);
-  else update_role(sm.gm, a, dp, kb, blockIdx.x - n_diag);
-}
-
-// Merge level with block size s: pair p joins B1 = [2ps, 2ps+s) and B2 = [2ps+s, min(2ps+2s, dp)).
-// stage 0: T[B2, B1] = L[B2, B1] M[B1, B1]      (M11 lower: k >= column tile start)
-// stage 1: M[B2, B1] = -M[B2, B2] T[B2, B1]     (M22 lower: k < row tile end)
-// 128 x 128 output tiles; a tile reaches at most into the 64 x 64 block just
-// above a diagonal block of M, which the diagonal step zeroes.
-template <int kStage>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ a, float* __restrict__ m,
-                                                    float* __restrict__ t, int64_t dp, int64_t s, int tiles_side,
-                                                    const int32_t* __restrict__ info) {
-  __shared__ GemmLds sm;
-  if (*info) return;
-  const int tiles_pair = tiles_side * tiles_side;
-  const int64_t p = blockIdx.x / tiles_pair;
-  const int tp = blockIdx.x % tiles_pair;
-  const int ti = tp / tiles_side, tj = tp % tiles_side;
-  const int64_t b1 = 2 * p * s, b2 = b1 + s;
-  if (b2 >= dp) return;
-  const int64_t n2 = (b2 + s <= dp) ? s : dp - b2;
-  const int64_t i0 = int64_t(ti) * kG, j0 = int64_t(tj) * kG;
-  if (i0 >= n2) return;
-  const int mv = static_cast<int>(n2 - i0 < kG ? n2 - i0 : kG);
-  const int nv = static_cast<int>(s - j0 < kG ? s - j0 : kG);
-  if (kStage == 0) {
-    // rows of B2, columns of B1, k over B1 from j0
-    gemm128<false>(sm, a + (b2 + i0) * dp + b1, dp, m + b1 * dp + b1 + j0, dp, t + (b2 + i0) * dp + b1 + j0, dp,
-                   mv, nv, static_cast<int>(j0), static_cast<int>(s), 1.0f, 0.0f);
-  } else {
-    const int kend = static_cast<int>(i0 + kG < n2 ? i0 + kG : n2);
-    gemm128<false>(sm, m + (b2 + i0) * dp + b2, dp, t + b2 * dp + b1 + j0, dp, m + (b2 + i0) * dp + b1 + j0, dp,
-                   mv, nv, 0, kend, -1.0f, 0.0f);
-  }
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < n_diag) diag_role(sm.dg, a, m, dp, kb, d, info, b);
+  else if (b < n_diag + n_row) row_role(sm.dg, a, m, dp, kb - 1, b - n_diag);
+  else update_role(sm.gm, a, m, dp, kb, b - n_diag - n_row, n_trail);
 }
 
 // R[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -615,7 +666,7 @@ __global__ void output_kernel(const float* __restrict__ m, int64_t d, int64_t dp
 
 struct Layout {
   int64_t dp;
-  size_t a_off, m_off, t_off, delta_off, total;
+  size_t a_off, m_off, delta_off, total;
 };
 
 Layout layout(int64_t d) {
@@ -624,9 +675,8 @@ Layout layout(int64_t d) {
   const size_t mat = align_up(size_t(l.dp) * l.dp * sizeof(float), 256);
   l.a_off = 0;
   l.m_off = mat;
-  l.t_off = 2 * mat;
-  l.delta_off = 3 * mat;
-  l.total = 3 * mat + 256;
+  l.delta_off = 2 * mat;
+  l.total = 2 * mat + 256;
   return l;
 }
 
@@ -639,7 +689,6 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
   char* base = static_cast<char*>(ws);
   float* a = reinterpret_cast<float*>(base + L.a_off);
   float* m = reinterpret_cast<float*>(base + L.m_off);
-  float* t = reinterpret_cast<float*>(base + L.t_off);
   double* delta = reinterpret_cast<double*>(base + L.delta_off);
   const int64_t dp = L.dp;
   const int nb = static_cast<int>(dp / kB);
@@ -650,39 +699,30 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, st, h, d, damp, delta, info);
   }
   if ((r = check_launch("damp_kernel")) != KQ_OK) return r;
-  // M is never read above its diagonal 64 x 64 blocks, so it needs no clearing.
+  // M is never read above its diagonal 64 x 64 blocks; its lower triangle is cleared here.
   {
     LaunchTimer timer("reverse_kernel", st);
     hipLaunchKernelGGL(reverse_kernel, dim3(static_cast<unsigned>((dp + 255) / 256), static_cast<unsigned>(dp)),
-                       dim3(256), 0, st, h, d, dp, delta, a);
+                       dim3(256), 0, st, h, d, dp, delta, a, m);
   }
   if ((r = check_launch("reverse_kernel")) != KQ_OK) return r;
 
-  for (int kb = 0; kb < nb; ++kb) {
+  for (int kb = 0; kb <= nb; ++kb) {
     const int rest = nb - kb - 1;
-    const int ntu = (kb >= 1) ? (rest + 1) / 2 : 0;  // 128-wide tiles over block columns kb + 1 ..
-    const unsigned grid = static_cast<unsigned>(1 + rest + ntu * (ntu + 1) / 2);
+    const int n_diag = kb < nb ? 1 + rest : 0;
+    const int n_row = kb >= 2 ? kb - 1 : 0;  // blocks c < j of row j = kb - 1 of M
+    const int ntu = (kb >= 1 && kb < nb) ? (rest + 1) / 2 : 0;  // 128-wide tiles over block columns kb + 1 ..
+    const int n_trail = ntu * (ntu + 1) / 2;
+    // rows kb .. of M (128-wide) x columns below 64 (kb - 1)
+    const int n_sub = (kb >= 2 && kb < nb) ? ((nb - kb + 1) / 2) * (kb / 2) : 0;
+    const int grid = n_diag + n_row + n_trail + n_sub;
+    if (grid == 0) continue;
     {
       LaunchTimer timer("step_kernel", st);
-      hipLaunchKernelGGL(step_kernel, dim3(grid), dim3(256), 0, st, a, m, dp, kb, d, 1 + rest, info);
+      hipLaunchKernelGGL(step_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a, m, dp, kb, d, n_diag,
+                         n_row, n_trail, info);
     }
     if ((r = check_launch("step_kernel")) != KQ_OK) return r;
-  }
-
-  for (int64_t s = kB; s < dp; s *= 2) {
-    const int64_t pairs = (dp + 2 * s - 1) / (2 * s);
-    const int tiles_side = static_cast<int>((s + kG - 1) / kG);
-    const unsigned grid = static_cast<unsigned>(pairs * tiles_side * tiles_side);
-    {
-      LaunchTimer timer("merge_kernel", st);
-      hipLaunchKernelGGL(merge_kernel<0>, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, info);
-    }
-    if ((r = check_launch("merge_kernel")) != KQ_OK) return r;
-    {
-      LaunchTimer timer("merge_kernel", st);
-      hipLaunchKernelGGL(merge_kernel<1>, dim3(grid), dim3(256), 0, st, a, m, t, dp, s, tiles_side, info);
-    }
-    if ((r = check_launch("merge_kernel")) != KQ_OK) return r;
   }
 
   {

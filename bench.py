@@ -45,7 +45,7 @@ def parse_args():
     p.add_argument("--bits", type=int, default=2, choices=(2, 4))
     p.add_argument("--serial", action="store_true",
                    help="run every stage on one stream (per-stage profiles) instead of the two-stream schedule")
-    p.add_argument("--reserve-cus", type=int, default=64,
+    p.add_argument("--reserve-cus", type=int, default=80,
                    help="CUs the second stream leaves to the Cholesky factor (0: no CU mask)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's covariance sample")
@@ -61,7 +61,8 @@ def parse_args():
 def side_stream(dev, reserve: int):
     """Second stream at default priority; with reserve > 0 its kernels are kept off the last
     `reserve` CUs of the mask (hipExtStreamCreateWithCUMask), which stay free for the
-    latency-bound Cholesky steps. (Masks with a hole in every 32-bit word are refused.)"""
+    latency-bound Cholesky steps. Mask bit i is a CU of XCD i mod 8, so the reserved CUs are
+    spread evenly over the XCDs; a mask that leaves an XCD no CU is refused."""
     import ctypes
     import torch
     if reserve <= 0:

@@ -15,9 +15,10 @@ bf16, 128 sequences of 2048 tokens), 2-bit, group 128, block 128, damping
 0.01, seeded synthetic inputs.
 
 Schedule: the Cholesky factor needs only H_X'' (the input side of BiIP), so
-by default it runs on one stream while the H_G covariance and the output side
-of BiIP run on a second stream that is kept off some CUs, which stay free for
-the latency-bound factor steps; `--serial` puts every stage on one stream.
+by default it runs on one stream while the H_G covariance runs on a second
+stream that is kept off some CUs, which stay free for the latency-bound factor
+steps; the output side of BiIP and the sweep follow on the first stream with
+every CU. `--serial` puts every stage on one stream.
 
 value = weights quantised per second, end to end including the covariance
 accumulation. The roofline object covers the dominant kernel, the bf16 MFMA
@@ -321,7 +322,7 @@ def main() -> int:
             overlap_body(ev)
 
     def overlap_body(ev):
-        # ev: events 0..6 on the lead stream, 7..11 on the side stream
+        # ev: events 0..6 and 9..11 on the lead stream, 7..8 on the side stream
         main = torch.cuda.current_stream()
         def mark(i, st):
             if ev is not None:
@@ -331,28 +332,26 @@ def main() -> int:
         e_cov = torch.cuda.Event()
         e_cov.record(main)  # the G covariance reuses this workspace
         mark(1, main)
-        kq.sensitivity(hx, None, score_x, kq.KQ_SCORE_HX_ONLY)  # tr(H_X) of the raw covariance
-        mark(2, main)
-        kq.biip_rotate(wd, w1, hx, None, ri.rot, None, in_flags, s_x, s_unused_g, ws=ws_biip)
-        mark(3, main)
-        e_in = torch.cuda.Event()
-        e_in.record(main)
-        kq.cholesky_inv(hx, cfg.damp, info, ws=ws_chol)
-        mark(4, main)
         with torch.cuda.stream(side):
             side.wait_event(e_cov)
             mark(7, side)
             kq.accumulate_cov(gd, hg, 1.0 / n_tok, 0.0, ws=ws_cov)
             mark(8, side)
-            kq.sensitivity(hg, None, score_g, kq.KQ_SCORE_HX_ONLY)  # tr(H_G) of the raw covariance
-            mark(9, side)
-            side.wait_event(e_in)
-            mark(10, side)
-            kq.biip_rotate(w1, w2, None, hg, None, ro.rot, out_flags, s_unused_x, s_g, ws=ws_biip)
-            mark(11, side)
-            e_out = torch.cuda.Event()
-            e_out.record(side)
-        main.wait_event(e_out)
+            e_g = torch.cuda.Event()
+            e_g.record(side)
+        kq.sensitivity(hx, None, score_x, kq.KQ_SCORE_HX_ONLY)  # tr(H_X) of the raw covariance
+        mark(2, main)
+        kq.biip_rotate(wd, w1, hx, None, ri.rot, None, in_flags, s_x, s_unused_g, ws=ws_biip)
+        mark(3, main)
+        kq.cholesky_inv(hx, cfg.damp, info, ws=ws_chol)
+        mark(4, main)
+        # the rest runs on the lead stream, which has every CU
+        main.wait_event(e_g)
+        mark(9, main)
+        kq.sensitivity(hg, None, score_g, kq.KQ_SCORE_HX_ONLY)  # tr(H_G) of the raw covariance
+        mark(10, main)
+        kq.biip_rotate(w1, w2, None, hg, None, ro.rot, out_flags, s_unused_x, s_g, ws=ws_biip)
+        mark(11, main)
         # score = tr(H_G) tr(H_X): the same float64 product the combined call forms
         sc = float(score_x.item()) * float(score_g.item())
         bits = kq.allocate_bits([sc], [dout * din], [args.bits], args.bits * 1000)[0]
@@ -399,9 +398,9 @@ def main() -> int:
     if args.serial:
         stage_ms = {s: span(i, i + 1) for i, s in enumerate(stages)}
     else:
-        # per-stage durations on the stream each ran on; cov_g and the BiIP output side
-        # overlap the Cholesky factor, so the stages add up to more than the step
-        stage_ms = {"cov_x": span(0, 1), "cov_g": span(7, 8), "score_alloc": span(1, 2) + span(8, 9),
+        # per-stage durations on the stream each ran on; cov_g overlaps the BiIP input side
+        # and the Cholesky factor, so the stages add up to more than the step
+        stage_ms = {"cov_x": span(0, 1), "cov_g": span(7, 8), "score_alloc": span(1, 2) + span(9, 10),
                     "biip": span(2, 3) + span(10, 11), "cholesky": span(3, 4), "obs": span(5, 6)}
     flops_cov = n_tok * din * (din + 1) + n_tok * dout * (dout + 1)
     t_accum = (stage_ms["cov_x"] + stage_ms["cov_g"]) / 1e3
@@ -453,8 +452,8 @@ def main() -> int:
         "cpu_baseline": None,
     }
     result["schedule"] = ("one stream" if args.serial else
-                          f"two streams: H_X covariance, BiIP input side and Cholesky factor on one; H_G covariance "
-                          f"and BiIP output side on the other, kept off {args.reserve_cus} CUs")
+                          f"two streams: H_X covariance, BiIP input side, Cholesky factor, BiIP output side and "
+                          f"sweep on one; H_G covariance on the other, kept off {args.reserve_cus} CUs")
     if unshared is not None:
         ach = flops_cov / 2 / (unshared / 1e3) / 1e12 if unshared > 0 else 0.0
         result["roofline"]["unshared"] = {"avg_launch_ms": round(unshared, 4), "achieved": round(ach, 2),

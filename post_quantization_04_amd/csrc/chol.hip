@@ -107,6 +107,28 @@ __device__ __forceinline__ void gemm128(GemmLds& sm, const float* a, int64_t lda
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  // D of a 32 x 32 block: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+  // Blocks are wholly valid or not. With beta != 0 the C block is read before the k loop, so
+  // its latency hides behind the products.
+  const bool rows_ok[2] = {wi * 64 < m_valid, wi * 64 + 32 < m_valid};
+  const bool cols_ok[2] = {wj * 64 < n_valid, wj * 64 + 32 < n_valid};
+  float* cp[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+      cp[x][y] = c + int64_t(wi * 64 + x * 32 + 4 * (lane >> 5)) * ldc + wj * 64 + y * 32 + (lane & 31);
+  f32x16 old[2][2];
+  if (beta != 0.0f) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) old[x][y][r] = cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc];
+        }
+  }
   const int nchunk = (k1 - k0) / kGK;
   float4 va[2], vb[2];
   auto load = [&](int kc) {
@@ -143,26 +165,7 @@ __device__ __forceinline__ void gemm128(GemmLds& sm, const float* a, int64_t lda
     if (ch + 1 < nchunk) store(buf ^ 1);
     __syncthreads();
   }
-  // D of a 32 x 32 block: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-  // Blocks are wholly valid or not; the C reads of all blocks are issued before any use.
-  const bool rows_ok[2] = {wi * 64 < m_valid, wi * 64 + 32 < m_valid};
-  const bool cols_ok[2] = {wj * 64 < n_valid, wj * 64 + 32 < n_valid};
-  float* cp[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-      cp[x][y] = c + int64_t(wi * 64 + x * 32 + 4 * (lane >> 5)) * ldc + wj * 64 + y * 32 + (lane & 31);
   if (beta != 0.0f) {
-    f32x16 old[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y)
-        if (rows_ok[x] && cols_ok[y]) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) old[x][y][r] = cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc];
-        }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll

@@ -5,8 +5,9 @@
 //     - sweep (16 rows per workgroup): 16 lanes own one row; lane l keeps
 //       columns l, l + 16, ... of the block in registers (B / 16 values).
 //       First (k > 0) the registers receive the previous block's errors of
-//       the same rows, W[r, c0:c0+B] -= E_{k-1}[r] R[c0-B:c0, c0:c0+B]; the
-//       workgroup wrote those errors itself one launch earlier. For
+//       the same rows, W[r, c0:c0+B] -= E_{k-1}[r] R[c0-B:c0, c0:c0+B], one
+//       16-row product on float64 MFMA; the workgroup wrote those errors
+//       itself one launch earlier. For
 //       column j the owning lane quantises, forms the scaled error
 //       e = (w - w^) / R_jj and the error is broadcast to the row's 16 lanes
 //       with one DPP row_newbcast; every lane then removes e * R[j][k] from
@@ -135,32 +136,49 @@ __device__ __forceinline__ void group_start(const double (&x)[EPL], int eo, int 
   }
 }
 
-// rl[j][l * EPL + e] = R[row0 + j][col0 + l + 16 e] for the B x B block (upper: entries on
-// and below the diagonal stored as 0, rinv[j] = 1 / R[row0 + j][col0 + j]). Every thread
-// issues all of its 16-byte loads before writing LDS.
-template <int B, bool UPPER>
-__device__ __forceinline__ void stage_r(float (&rl)[B][B], double* rinv, const float* __restrict__ r, int64_t din,
-                                        int64_t row0, int64_t col0) {
-  constexpr int EPL = B / 16, V = B / 4, N = B * V / kSweepThreads;
+// A B x B block of R in registers: this thread's 16-byte pieces of it.
+template <int B>
+struct RBlock {
+  static constexpr int V = B / 4, N = B * V / kSweepThreads;
   static_assert(N >= 1 && B * V % kSweepThreads == 0, "block shape");
-  const int tid = threadIdx.x;
   float4 v[N];
+};
+
+// Issues the loads of R[row0 .. row0 + B, col0 .. col0 + B] into rb.
+template <int B>
+__device__ __forceinline__ void load_r(RBlock<B>& rb, const float* __restrict__ r, int64_t din, int64_t row0,
+                                       int64_t col0) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int q = 0; q < N; ++q) {
-    const int idx = tid + q * kSweepThreads, j = idx / V, k4 = (idx % V) * 4;
-    v[q] = *reinterpret_cast<const float4*>(r + (row0 + j) * din + col0 + k4);
+  for (int q = 0; q < RBlock<B>::N; ++q) {
+    const int idx = tid + q * kSweepThreads, j = idx / RBlock<B>::V, k4 = (idx % RBlock<B>::V) * 4;
+    rb.v[q] = *reinterpret_cast<const float4*>(r + (row0 + j) * din + col0 + k4);
   }
+}
+
+// rl[j][l * EPL + e] = R[row0 + j][col0 + l + 16 e] for the block in rb (upper: entries on
+// and below the diagonal stored as 0).
+template <int B, bool UPPER>
+__device__ __forceinline__ void store_r(const RBlock<B>& rb, float (&rl)[B][B]) {
+  constexpr int EPL = B / 16;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int q = 0; q < N; ++q) {
-    const int idx = tid + q * kSweepThreads, j = idx / V, k4 = (idx % V) * 4;
-    const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+  for (int q = 0; q < RBlock<B>::N; ++q) {
+    const int idx = tid + q * kSweepThreads, j = idx / RBlock<B>::V, k4 = (idx % RBlock<B>::V) * 4;
+    const float f[4] = {rb.v[q].x, rb.v[q].y, rb.v[q].z, rb.v[q].w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int k = k4 + t;
       rl[j][(k & 15) * EPL + (k >> 4)] = (!UPPER || k > j) ? f[t] : 0.0f;
-      if (UPPER && k == j) rinv[j] = 1.0 / static_cast<double>(f[t]);
     }
   }
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses only: global loads
+// issued before it stay in flight (__syncthreads would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Sweep of block [c0, c0 + B) for rows [16 wg, 16 wg + 16); writes the scaled
@@ -189,31 +207,65 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   double x[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) x[e] = valid ? w[row * din + c0 + l16 + 16 * e] : 0.0;
+  // the block's own R block is loaded now and staged after the previous block's update,
+  // so its loads overlap that update
+  RBlock<B> rdiag;
+  // 1 / R_jj of the block, one division per thread j < B
+  const float rjj = tid < B ? r[(c0 + tid) * din + c0 + tid] : 1.0f;
   if (c0 > 0) {
-    // previous block's errors of these rows: x -= E_prev[row] R[c0-B:c0, c0:c0+B],
-    // R staged in the sweep's LDS layout (all entries)
-    stage_r<B, false>(rl, nullptr, r, din, c0 - B, c0);
-    __syncthreads();
-    // E_prev[row][j] is loaded once by lane j / EPL of the row (slot j % EPL) and broadcast
-    double ev[EPL];
-    const double* ep = e_prev + (valid ? row : 0) * B + l16 * EPL;
+    // previous block's errors of these rows: x -= E_prev R[c0-B:c0, c0:c0+B] for the
+    // workgroup's 16 rows, as a 16 x B x B product on float64 MFMA (v_mfma_f64_16x16x4f64)
+    // with R staged in the sweep's LDS layout (all entries)
+    RBlock<B> rnear;
+    load_r<B>(rnear, r, din, c0 - B, c0);
+    load_r<B>(rdiag, r, din, c0, c0);
+    // A operand of k-step kk: lane i + 16 c holds E_prev[row i of the workgroup][4 kk + c]
+    constexpr int KS = B / 4, NT = B / 16, TPW = (NT + 3) / 4;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t erow = int64_t(wg) * kRowsPerWg + (lane & 15);
+    const double* ep = e_prev + (erow < dout ? erow : 0) * B + (lane >> 4);
+    double ea[KS];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) ev[i] = ep[i];
-    const int lane0 = (tid & 63) & ~15;  // first lane of this row's 16 in the wave
-#pragma unroll 1
-    for (int src = 0; src < 16; ++src) {
+    for (int kk = 0; kk < KS; ++kk) ea[kk] = ep[4 * kk];
+    store_r<B, false>(rnear, rl);
+    lds_barrier();
+    // 16-column tiles: wave w takes tiles w, w + 4, ...; B operand of k-step kk for tile t:
+    // lane j + 16 c holds R[c0 - B + 4 kk + c][c0 + 16 t + j] = rl[4 kk + c][j EPL + t]
+    f64x4 acc[TPW];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const double eb = __shfl(ev[i], lane0 + src, 64);
-        const float* rr = &rl[src * EPL + i][l16 * EPL];
+    for (int u = 0; u < TPW; ++u) acc[u] = f64x4{};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = fma(-eb, static_cast<double>(rr[e]), x[e]);
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int t = wave + 4 * u;
+        if (t < NT)
+          acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+              ea[kk], static_cast<double>(rl[4 * kk + (lane >> 4)][(lane & 15) * EPL + t]), acc[u], 0, 0, 0);
+      }
+    lds_barrier();  // every wave is done reading the previous block's R
+    // the product, row 4 q + lane / 16 and column 16 t + lane % 16 in register q, goes through
+    // LDS (over the R block just read) into the sweep layout
+    double (*prod)[B] = reinterpret_cast<double (*)[B]>(&rl[0][0]);
+    static_assert(kRowsPerWg * B * sizeof(double) <= sizeof(rl), "product fits over the R block");
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave + 4 * u;
+      if (t < NT) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) prod[4 * q + (lane >> 4)][16 * t + (lane & 15)] = acc[u][q];
       }
     }
-    __syncthreads();
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] -= prod[tid >> 4][l16 + 16 * e];
+    lds_barrier();  // the product is read before the block's own R overwrites it
+  } else {
+    load_r<B>(rdiag, r, din, c0, c0);
   }
-  stage_r<B, true>(rl, rinv, r, din, c0, c0);
-  __syncthreads();
+  store_r<B, true>(rdiag, rl);
+  if (tid < B) rinv[tid] = 1.0 / static_cast<double>(rjj);
+  lds_barrier();
   double s = 1.0, z = 0.0;
   if (group == 0 && valid) {
     s = static_cast<double>(scales[row]);

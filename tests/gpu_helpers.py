@@ -46,7 +46,8 @@ def rel_fro(got: np.ndarray, want: np.ndarray) -> float:
     return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
 
 
-def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_frac=1e-4, label=""):
+def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_frac=1e-4, scale_rtol=1e-5,
+                label=""):
     """Code parity: replay the oracle's sweep on (w2, r), adopting the kernel's
     code or zero only where the rounding argument is within ``window`` of a
     midpoint and the kernel chose the neighbouring value. Every other entry must
@@ -57,5 +58,5 @@ def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_fr
     np.testing.assert_array_equal(res.codes, codes, err_msg=label)
     np.testing.assert_array_equal(res.zeros, zeros, err_msg=label)
     assert res.adopted_codes <= max(1, max_frac * n), f"{label}: {res.adopted_codes} tie-window codes of {n}"
-    np.testing.assert_allclose(scales, res.scales.astype(np.float32), rtol=1e-5, err_msg=label)
+    np.testing.assert_allclose(scales, res.scales.astype(np.float32), rtol=scale_rtol, err_msg=label)
     return res

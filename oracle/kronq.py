@@ -46,6 +46,7 @@ __all__ = [
     "rotation_rows", "rotate_rows", "unrotate_rows", "biip_scales", "biip_forward",
     "biip_inverse", "damped", "chol_inv_upper", "grid", "obs_quantize", "obs_quantize_blocked",
     "obq_reference", "rtn_quantize", "kron_loss", "allocate_bits", "quantize_layer",
+    "container_bits", "pack_codes", "unpack_codes", "dequantize", "decode_matvec",
     "ObsResult", "INFEASIBLE",
 ]
 
@@ -493,6 +494,70 @@ def allocate_bits(scores: Sequence[float], n_params: Sequence[int], choices: Seq
                 bits[i] = c
                 break
     return bits
+
+
+# ---------------------------------------------------------------------------
+# after the path: packed codes and the decode matvec  ([KQ-news]: the
+# quantized weights ship as packed int4 / int2 with a fused dequantization +
+# BiIP matvec for single-token decode; [KQ-art] Q&A: at inference each layer
+# applies the two Hadamard transforms, O(d log d) each)
+# ---------------------------------------------------------------------------
+def container_bits(bits: int) -> int:
+    """Bits a code occupies in a packed word: 2 for 2-bit codes, 4 for 3- and 4-bit codes,
+    8 above (a reading: the pages name int2 and int4 containers only)."""
+    if not 2 <= bits <= 8:
+        raise ValueError("bits must be in [2, 8]")
+    return 2 if bits == 2 else (4 if bits <= 4 else 8)
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[rows, cols] codes -> [rows, cols * c / 32] uint32 words; word k of a row holds codes
+    k * 32 / c + t at bits [c t, c t + c) (c = container_bits(bits))."""
+    c = container_bits(bits)
+    per = 32 // c
+    codes = np.asarray(codes, np.uint64)
+    rows, cols = codes.shape
+    if cols % per:
+        raise ValueError("columns must be a multiple of the codes per word")
+    if np.any(codes >= (1 << bits)):
+        raise ValueError("code out of range")
+    blocks = codes.reshape(rows, cols // per, per)
+    words = np.zeros((rows, cols // per), np.uint64)
+    for t in range(per):
+        words |= blocks[:, :, t] << np.uint64(c * t)
+    return words.astype(np.uint32)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, cols: int) -> np.ndarray:
+    """Inverse of ``pack_codes``."""
+    c = container_bits(bits)
+    per = 32 // c
+    words = np.asarray(packed, np.uint64)
+    rows = words.shape[0]
+    out = np.zeros((rows, cols // per, per), np.uint64)
+    for t in range(per):
+        out[:, :, t] = (words >> np.uint64(c * t)) & np.uint64((1 << c) - 1)
+    return out.reshape(rows, cols).astype(np.uint8)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int) -> np.ndarray:
+    """W^''[i][j] = scale[i][g] (code_ij - zero[i][g]), g = j / group (one grid per row for group 0),
+    with the scales as stored (float32)."""
+    codes = np.asarray(codes, np.float64)
+    rows, cols = codes.shape
+    gi = (np.arange(cols) // group) if group else np.zeros(cols, np.int64)
+    sc = np.asarray(scales, np.float32).astype(np.float64).reshape(rows, -1)
+    ze = np.asarray(zeros, np.float64).reshape(rows, -1)
+    return sc[:, gi] * (codes - ze[:, gi])
+
+
+def decode_matvec(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int, s_x: np.ndarray,
+                  s_g: np.ndarray, rot_in: kq_synth.RotSpec, rot_out: kq_synth.RotSpec, x: np.ndarray, *,
+                  inp: bool = True, out: bool = True) -> np.ndarray:
+    """y = W^ x for every row x of ``x`` ([tokens, din] -> [tokens, dout]), with the layer's
+    quantized weight in original coordinates, W^ = S_G^-1 U_G^T W^'' U_X S_X^-1."""
+    w_hat = biip_inverse(dequantize(codes, scales, zeros, group), rot_in, rot_out, s_x, s_g, inp=inp, out=out)
+    return np.asarray(x, np.float64) @ w_hat.T
 
 
 # ---------------------------------------------------------------------------

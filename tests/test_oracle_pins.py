@@ -420,3 +420,80 @@ def test_p12_config5_shape():
         bits = oracle.allocate_bits(scores, n, cfg.alloc_choices, cfg.alloc_target_millibits)
         assert sum(b * k for b, k in zip(bits, n)) <= 3 * sum(n)
         assert set(bits) <= {2, 3, 4}
+
+
+# --------------------------------------------------------------------------
+# P13: packed codes and the decode matvec (the step after the path)
+# --------------------------------------------------------------------------
+def test_p13_pack_layout_by_hand():
+    # 2-bit: code t of a word sits at bits 2t; 4-bit and 3-bit codes in nibbles; 8-bit in bytes
+    c = np.zeros((1, 16), np.uint8)
+    c[0, 0] = 1
+    assert oracle.pack_codes(c, 2).tolist() == [[0x00000001]]
+    c = np.zeros((1, 16), np.uint8)
+    c[0, 15] = 3
+    assert oracle.pack_codes(c, 2).tolist() == [[0xC0000000]]
+    c = np.array([[3, 2, 1, 0, 0, 1, 2, 3, 3, 3, 0, 0, 1, 1, 2, 2]], np.uint8)
+    assert oracle.pack_codes(c, 2).tolist() == [[0xA50FE41B]]
+    c = np.array([[0xA, 0x5, 0, 0, 0, 0, 0, 0xF]], np.uint8)
+    assert oracle.pack_codes(c, 4).tolist() == [[0xF000005A]]
+    assert oracle.pack_codes(np.array([[7, 0, 5, 1, 0, 0, 0, 0]], np.uint8), 3).tolist() == [[0x00001507]]
+    assert oracle.pack_codes(np.array([[0x12, 0x34, 0x56, 0xFF]], np.uint8), 8).tolist() == [[0xFF563412]]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_p13_pack_round_trip(bits):
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(7, 64), dtype=np.uint8)
+    packed = oracle.pack_codes(codes, bits)
+    assert packed.dtype == np.uint32 and packed.shape == (7, 64 * oracle.container_bits(bits) // 32)
+    np.testing.assert_array_equal(oracle.unpack_codes(packed, bits, 64), codes)
+
+
+def _dense_u(spec):
+    # U = (Q_m kron H_p / sqrt(p)) diag(sigma), H_p from the textbook routine, built densely
+    hp = scipy.linalg.hadamard(spec.p) / np.sqrt(spec.p)
+    return np.kron(spec.q, hp) @ np.diag(spec.signs.astype(np.float64))
+
+
+@pytest.mark.parametrize("dout,din,group", [(24, 40, 8), (48, 24, 0), (12, 64, 16)])
+def test_p13_decode_matvec_against_dense(dout, din, group):
+    """y = S_G^-1 U_G^T W^'' U_X S_X^-1 x with every matrix written out densely and the
+    dequantization done entry by entry."""
+    rng = np.random.default_rng(dout + din)
+    bits = 3
+    codes = rng.integers(0, 8, size=(dout, din), dtype=np.uint8)
+    ng = din // group if group else 1
+    scales = rng.uniform(0.01, 0.1, size=(dout, ng)).astype(np.float32)
+    zeros = rng.integers(0, 8, size=(dout, ng), dtype=np.uint8)
+    s_x, s_g = rng.uniform(0.5, 2.0, din), rng.uniform(0.5, 2.0, dout)
+    ri, ro = kq_synth.rot_spec(3, "di", din), kq_synth.rot_spec(3, "do", dout)
+    x = rng.standard_normal((3, din))
+    wq = np.zeros((dout, din))
+    for i in range(dout):
+        for j in range(din):
+            g = j // group if group else 0
+            wq[i, j] = float(scales[i, g]) * (int(codes[i, j]) - int(zeros[i, g]))
+    w_hat = np.diag(1 / s_g) @ _dense_u(ro).T @ wq @ _dense_u(ri) @ np.diag(1 / s_x)
+    want = x @ w_hat.T
+    got = oracle.decode_matvec(oracle.unpack_codes(oracle.pack_codes(codes, bits), bits, din), scales, zeros,
+                               group, s_x, s_g, ri, ro, x)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # without rotations and scales it is the plain dequantized matvec
+    plain = oracle.decode_matvec(codes, scales, zeros, group, np.ones(din), np.ones(dout), ri, ro, x,
+                                 inp=False, out=False)
+    np.testing.assert_allclose(plain, x @ wq.T, rtol=1e-12, atol=1e-12)
+
+
+def test_p13_decode_inverts_the_quantized_layer():
+    """Decoding the oracle's quantized layer applies exactly its un-rotated weight W^."""
+    rng = np.random.default_rng(5)
+    dout, din = 32, 48
+    w = rng.normal(0, 0.02, (dout, din))
+    hx, hg = _spd(rng, din, 1.0), _spd(rng, dout, 1.0)
+    ri, ro = kq_synth.rot_spec(4, "qi", din), kq_synth.rot_spec(4, "qo", dout)
+    out = oracle.quantize_layer(w, hx, hg, ri, ro, bits=2, group=16, damp=0.01)
+    res = out["obs"]
+    x = rng.standard_normal((2, din))
+    y = oracle.decode_matvec(res.codes, res.scales, res.zeros, 16, out["s_x"], out["s_g"], ri, ro, x)
+    np.testing.assert_allclose(y, x @ out["w_hat"].T, rtol=1e-10, atol=1e-13)

@@ -53,6 +53,8 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=64, help="weight rows in the oracle's sweep sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, copy 1 GiB device-to-device (a reference kernel for HBM byte counters)")
+    p.add_argument("--decode", action="store_true",
+                   help="instead of the quantization step: the packed-code decode matvec (one JSON line)")
     p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                    help="no run: turn two rocprofv3 --pmc runs of '--copy-calibration' (FETCH_SIZE, then "
                         "WRITE_SIZE) into the per-launch HBM bytes of the roofline kernel")
@@ -223,6 +225,127 @@ def stored_traffic():
         return None
 
 
+# LLaMA-2-7B linear layers of one decoder block: (name, dout, din)
+DECODE_LAYERS = [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096), ("o_proj", 4096, 4096),
+                 ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008)]
+DECODE_BLOCKS = 32
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_bench(args) -> int:
+    """Single-token decode through packed W2 layers: y = S_G^-1 U_G^T W^'' U_X S_X^-1 x per layer.
+
+    Synthetic packed codes (uniform random 2-bit fields), group-128 scales and zero points, random
+    diagonal scales and seeded rotation specs, for the 224 linear layers of LLaMA-2-7B (32 blocks x
+    q, k, v, o, gate, up, down). One step = one token through all 224 layers (the linear layers only:
+    no attention, norms or activations). The roofline covers the decode kernel on the 4096 x 4096
+    layer: weight bytes (packed codes + scales + zero points) per call over its duration."""
+    import numpy as np
+    import torch
+
+    import kq_synth
+    import post_quantization_04_amd as kq
+    from post_quantization_04_amd import pipeline
+
+    dev = torch.device("cuda:0")
+    torch.zeros(1, device=dev)
+    bits, group = 2, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2026)
+    rots = {n: pipeline.upload_rot(*(lambda sp: (sp.signs, sp.q))(kq_synth.rot_spec(77, f"dec{n}", n)), dev)
+            for n in sorted({d for _, o, i in DECODE_LAYERS for d in (o, i)})}
+    layers = []
+    for blk in range(DECODE_BLOCKS):
+        for name, dout, din in DECODE_LAYERS:
+            packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (dout, din * 2 // 32), dtype=torch.int32, device=dev,
+                                   generator=gen)
+            scales = torch.rand((dout, din // group), device=dev, generator=gen) * 0.04 + 0.005
+            zeros = torch.randint(0, 4, (dout, din // group), dtype=torch.uint8, device=dev, generator=gen)
+            s_x = torch.rand(din, dtype=torch.float64, device=dev, generator=gen) + 0.5
+            s_g = torch.rand(dout, dtype=torch.float64, device=dev, generator=gen) + 0.5
+            layers.append((name, dout, din, packed, scales, zeros, s_x, s_g))
+    xs = {n: torch.randn((1, n), device=dev, generator=gen) for n in (4096, 11008)}
+    ys = {n: torch.empty((1, n), device=dev) for n in (4096, 11008)}
+    wss = {n: kq.decode_workspace(n, 1, dev) for n in (4096, 11008)}
+    weight_bytes = sum(p.numel() * 4 + sc.numel() * 4 + z.numel() for _, _, _, p, sc, z, _, _ in layers)
+
+    def layer_call(L):
+        name, dout, din, packed, scales, zeros, s_x, s_g = L
+        kq.decode_matvec(packed, scales, zeros, bits, group, s_x, s_g, rots[din].rot, rots[dout].rot, xs[din],
+                         ys[dout], ws=wss[dout])
+
+    def token():
+        for L in layers:
+            layer_call(L)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup + 1):
+        token()
+    torch.cuda.synchronize()
+    # one layer, many calls: the roofline kernel
+    q = layers[0]
+    kq.timing_enable("decode_kernel")
+    for _ in range(200):
+        layer_call(q)
+    n_q, ms_q = kq.timing_query("decode_kernel")
+    kq.timing_enable(None)
+    q_bytes = q[3].numel() * 4 + q[4].numel() * 4 + q[5].numel()
+    q_us = ms_q / n_q * 1e3
+    # whole token, eager launches
+    steps = max(args.steps, 5) * 4
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        token()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / steps
+    # whole token captured once as a HIP graph and replayed
+    ref = ys[4096].clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        token()  # warm the capture stream
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            token()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(ys[4096], ref))
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / steps
+    ms_tok = min(ms_eager, ms_graph)
+    achieved = q_bytes / (q_us * 1e-6) / 1e9
+    result = {
+        "metric": "W2 decode: tokens per second through the 224 packed linear layers of LLaMA-2-7B",
+        "value": round(1e3 / ms_tok, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_tok, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u2/f32", "data": "synthetic",
+        "config": {"workload": "LLaMA-2-7B linear layers (32 x q, k, v, o 4096x4096; gate, up 11008x4096; "
+                               "down 4096x11008), W2 group 128, batch 1, BiIP both sides",
+                   "weight_bytes_per_token": weight_bytes},
+        "ms_per_token_eager": round(ms_eager, 4), "ms_per_token_graph": round(ms_graph, 4),
+        "graph_replay_matches_eager": replay_ok,
+        "stack_gbs": round(weight_bytes / (ms_tok * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": q_bytes, "avg_launch_us": round(q_us, 3),
+                     "note": "4096 x 4096 layer, one token: packed codes + float32 scales + uint8 zero points"},
+    }
+    log(f"decode: {ms_eager:.3f} ms/token eager, {ms_graph:.3f} ms/token graph; 4096^2 layer {q_us:.2f} us "
+        f"({achieved:.0f} GB/s)")
+    print(json.dumps(result))
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.traffic_summary:
@@ -232,6 +355,8 @@ def main() -> int:
         print(json.dumps({"error": "this build measures one GPU; the path's multi-GPU sharding is design only, "
                                    "so --gpus must be 1"}))
         return 2
+    if args.decode:
+        return decode_bench(args)
 
     import numpy as np
     import torch

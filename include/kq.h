@@ -59,10 +59,11 @@ enum {
 enum { KQ_SCORE_KRONQ = 0, KQ_SCORE_HX_ONLY = 1 };
 
 /* kq_workspace_size operations. */
-enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS = 3 };
+enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS = 3, KQ_OP_DECODE = 4 };
 
 #define KQ_MAX_ODD 63         /* largest odd factor m of a rotated dimension */
 #define KQ_MAX_ROT_DIM 32768  /* largest rotated dimension n = m * 2^k */
+#define KQ_DECODE_MAX_TOKENS 4  /* tokens per kq_decode_matvec call */
 
 /*
  * Rotation of one side: U = (Q_m kron H_p / sqrt(p)) diag(sigma), n = m * p,
@@ -105,6 +106,7 @@ kq_status kq_timing_query(const char* name, int64_t* launches, double* total_ms)
  *   KQ_OP_BIIP:           d0 = dout, d1 = din
  *   KQ_OP_CHOLESKY:       d0 = d
  *   KQ_OP_OBS:            d0 = dout, d1 = din, d2 = block
+ *   KQ_OP_DECODE:         d0 = dout, d1 = tokens
  * Returns (size_t)-1 for invalid sizes.
  */
 size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
@@ -247,6 +249,50 @@ kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, 
                           int32_t group, int32_t block, uint8_t* codes, float* scales,
                           uint8_t* zeros, double* preround, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * kq_pack_codes -- codes of a quantized weight into 32-bit words
+ *
+ * The deployment path of [KQ-news] ships the quantized weight as packed int4 /
+ * int2 codes. Container width c = 2 for 2-bit codes, 4 for 3- and 4-bit codes,
+ * 8 for 5..8 bits; code j of a row goes to word j / (32 / c) of that row at
+ * bit offset c (j mod 32 / c).
+ *   codes   device uint8 [rows, cols], each < 2^bits (higher bits are not masked)
+ *   packed  device uint32 [rows, cols * c / 32], written
+ * cols must be a multiple of 32 / c (KQ_EINVAL otherwise).
+ */
+kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
+                        uint32_t* packed, void* stream);
+
+/*
+ * kq_decode_matvec -- y = W^ x with the quantized layer in original coordinates
+ *
+ * W^ = S_G^-1 U_G^T W^'' U_X S_X^-1 with W^''[i][j] = scale[i][g] (code_ij - zero[i][g]),
+ * g = j / group: the fused dequantization + BiIP matvec of the deployment
+ * path ([KQ-news]); at inference each layer applies the two Hadamard
+ * transforms, O(d log d) each ([KQ-art] Q&A). The input side is applied to x
+ * in every workgroup of the matvec launch and rows are dequantized from the
+ * packed codes as they stream in; a second one-workgroup launch applies the
+ * output side (only when rot_out is given).
+ *   packed   device uint32 [dout, din * c / 32] from kq_pack_codes
+ *   scales   device float32 [dout, din / group] (group 0: [dout, 1]), as kq_obs_quantize wrote them
+ *   zeros    device uint8, same shape
+ *   bits     2..8; group 0 or a multiple of 16 dividing din; din a multiple of 16
+ *   s_x, s_g device float64 [din], [dout] diagonal scales; NULL means 1
+ *   rot_in, rot_out  HOST pointers to the rotation specs; NULL means U = I on that side
+ *   x        device float32 [tokens, din], y device float32 [tokens, dout] (written)
+ *   tokens   1..KQ_DECODE_MAX_TOKENS; din * tokens <= 16384 and, with rot_out,
+ *            dout * tokens <= 36928 (the output side holds its tokens and the odd
+ *            factor in 160 KB of LDS); KQ_EUNSUPPORTED otherwise
+ *   ws       kq_workspace_size(KQ_OP_DECODE, dout, tokens, 0) bytes (the matvec
+ *            result before the output side); calls sharing it must not overlap
+ * Arithmetic is float32 (scales and rotation factors read as stored).
+ */
+kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const uint8_t* zeros,
+                           int64_t dout, int64_t din, int32_t bits, int32_t group,
+                           const double* s_x, const double* s_g, const kq_rot* rot_in,
+                           const kq_rot* rot_out, const float* x, int64_t tokens, float* y,
+                           void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

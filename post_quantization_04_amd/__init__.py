@@ -18,15 +18,18 @@ __all__ = [
     "KQError", "KQ_OK", "KQ_EINVAL", "KQ_ENOTPD", "KQ_EINFEASIBLE", "KQ_EDEVICE", "KQ_EUNSUPPORTED",
     "KQ_BF16", "KQ_F32", "KQ_F64", "KQ_BIIP_INPUT", "KQ_BIIP_OUTPUT", "KQ_BIIP_SCALE", "KQ_BIIP_INVERSE",
     "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
+    "KQ_OP_DECODE", "KQ_DECODE_MAX_TOKENS",
     "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
-    "biip_rotate", "cholesky_inv", "obs_quantize", "Rot", "timing_enable", "timing_query",
+    "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_workspace", "Rot",
+    "timing_enable", "timing_query",
 ]
 
 KQ_OK, KQ_EINVAL, KQ_ENOTPD, KQ_EINFEASIBLE, KQ_EDEVICE, KQ_EUNSUPPORTED = range(6)
 KQ_BF16, KQ_F32, KQ_F64 = 0, 1, 2
 KQ_BIIP_INPUT, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_BIIP_INVERSE = 1, 2, 4, 8
 KQ_SCORE_KRONQ, KQ_SCORE_HX_ONLY = 0, 1
-KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS = 0, 1, 2, 3
+KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS, KQ_OP_DECODE = 0, 1, 2, 3, 4
+KQ_DECODE_MAX_TOKENS = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -80,8 +83,11 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(Rot), _U32, _VP, _VP, _VP, _SZ, _VP]
     L.kq_cholesky_inv.argtypes = [_VP, _I64, _F32, _VP, _VP, _SZ, _VP]
     L.kq_obs_quantize.argtypes = [_VP, _VP, _I64, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]
+    L.kq_pack_codes.argtypes = [_VP, _I64, _I64, _I32, _VP, _VP]
+    L.kq_decode_matvec.argtypes = [_VP, _VP, _VP, _I64, _I64, _I32, _I32, _VP, _VP, ctypes.POINTER(Rot),
+                                   ctypes.POINTER(Rot), _VP, _I64, _VP, _VP, _SZ, _VP]
     for name in ("kq_accumulate_cov", "kq_sensitivity", "kq_allocate_bits", "kq_biip_rotate",
-                 "kq_cholesky_inv", "kq_obs_quantize"):
+                 "kq_cholesky_inv", "kq_obs_quantize", "kq_pack_codes", "kq_decode_matvec"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -228,3 +234,49 @@ def obs_quantize(w, r, bits: int, group: int, block: int, codes, scales, zeros, 
     _check(lib().kq_obs_quantize(_ptr(w), _ptr(r), dout, din, bits, group, block, _ptr(codes), _ptr(scales),
                                  _ptr(zeros), _ptr(preround), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)), "kq_obs_quantize")
+
+
+def pack_codes(codes, bits: int, packed, *, stream=None) -> None:
+    """packed (uint32-sized int32 [rows, cols * c / 32]) <- codes (uint8 [rows, cols]); c = 2, 4 or 8."""
+    import torch
+    _need(codes.dtype == torch.uint8 and codes.is_contiguous() and packed.dtype == torch.int32
+          and packed.is_contiguous(), "pack_codes: dtypes or layout")
+    rows, cols = codes.shape
+    c = 2 if bits == 2 else (4 if bits <= 4 else 8)
+    _need(tuple(packed.shape) == (rows, cols * c // 32), "pack_codes: packed must be [rows, cols * c / 32]")
+    _check(lib().kq_pack_codes(_ptr(codes), rows, cols, bits, _ptr(packed), _stream(stream)), "kq_pack_codes")
+
+
+def decode_workspace(dout: int, tokens: int, device):
+    """A workspace for decode_matvec."""
+    import torch
+    return torch.empty(workspace_size(KQ_OP_DECODE, dout, tokens), dtype=torch.uint8, device=device)
+
+
+def decode_matvec(packed, scales, zeros, bits: int, group: int, s_x, s_g, rot_in: Optional[Rot],
+                  rot_out: Optional[Rot], x, y, *, ws=None, stream=None) -> None:
+    """y (float32 [tokens, dout]) <- S_G^-1 U_G^T W^'' U_X S_X^-1 x for x (float32 [tokens, din])."""
+    import torch
+    _need(packed.dtype == torch.int32 and scales.dtype == torch.float32 and zeros.dtype == torch.uint8
+          and x.dtype == torch.float32 and y.dtype == torch.float32 and x.is_contiguous() and y.is_contiguous(),
+          "decode_matvec: dtypes or layout")
+    _need(s_x is None or s_x.dtype == torch.float64, "decode_matvec: s_x must be float64")
+    _need(s_g is None or s_g.dtype == torch.float64, "decode_matvec: s_g must be float64")
+    tokens, din = x.shape
+    dout = y.shape[1]
+    c = 2 if bits == 2 else (4 if bits <= 4 else 8)
+    ngroups = din // group if group else 1
+    _need(y.shape[0] == tokens, "decode_matvec: x and y hold different token counts")
+    _need(tuple(packed.shape) == (dout, din * c // 32), "decode_matvec: packed must be [dout, din * c / 32]")
+    _need(tuple(scales.shape) == (dout, ngroups) and tuple(zeros.shape) == (dout, ngroups),
+          "decode_matvec: scales and zeros must be [dout, din / group]")
+    _need(scales.is_contiguous() and zeros.is_contiguous() and packed.is_contiguous(),
+          "decode_matvec: packed, scales and zeros must be contiguous")
+    _need(s_x is None or s_x.numel() == din, "decode_matvec: s_x must hold din entries")
+    _need(s_g is None or s_g.numel() == dout, "decode_matvec: s_g must hold dout entries")
+    if ws is None:
+        ws = decode_workspace(dout, tokens, x.device)
+    _check(lib().kq_decode_matvec(_ptr(packed), _ptr(scales), _ptr(zeros), dout, din, bits, group, _ptr(s_x),
+                                  _ptr(s_g), None if rot_in is None else ctypes.byref(rot_in),
+                                  None if rot_out is None else ctypes.byref(rot_out), _ptr(x), tokens, _ptr(y),
+                                  _ptr(ws), ws.numel(), _stream(stream)), "kq_decode_matvec")

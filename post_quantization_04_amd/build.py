@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ["kq_api.hip", "timing.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip"]
+SOURCES = ["kq_api.hip", "timing.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 
 

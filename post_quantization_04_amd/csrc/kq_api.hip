@@ -104,6 +104,9 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2) {
     case KQ_OP_OBS:
       if (d0 < 1 || d1 < 1 || d2 < 1 || d1 > kMaxDim) return bad;
       return kq::obs_workspace(d0, d1, static_cast<int>(d2));
+    case KQ_OP_DECODE:
+      if (d0 < 1 || d0 > KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_DECODE_MAX_TOKENS) return bad;
+      return kq::decode_workspace(d0, d1);
     default:
       return bad;
   }
@@ -214,6 +217,43 @@ kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, 
     return fail(KQ_EUNSUPPORTED, "kq_obs_quantize: block %d (supported: 32, 64, 128)", block);
   if (!ws_ok(ws, ws_bytes, kq::obs_workspace(dout, din, block))) return KQ_EINVAL;
   return kq::obs_run(w, r, dout, din, bits, group, block, codes, scales, zeros, preround, ws, kq::as_stream(stream));
+}
+
+kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* packed,
+                        void* stream) {
+  if (!codes || !packed) return fail(KQ_EINVAL, "kq_pack_codes: NULL pointer");
+  if (bits < 2 || bits > 8) return fail(KQ_EINVAL, "kq_pack_codes: bits = %d outside [2, 8]", bits);
+  const int per = 32 / kq::container_bits(bits);
+  if (rows < 0 || cols < 0 || cols % per != 0)
+    return fail(KQ_EINVAL, "kq_pack_codes: %lld columns are not a multiple of %d codes per word", (long long)cols, per);
+  return kq::pack_run(codes, rows, cols, bits, packed, kq::as_stream(stream));
+}
+
+kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout,
+                           int64_t din, int32_t bits, int32_t group, const double* s_x, const double* s_g,
+                           const kq_rot* rot_in, const kq_rot* rot_out, const float* x, int64_t tokens, float* y,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (!packed || !scales || !zeros || !x || !y) return fail(KQ_EINVAL, "kq_decode_matvec: NULL pointer");
+  if (bits < 2 || bits > 8) return fail(KQ_EINVAL, "kq_decode_matvec: bits = %d outside [2, 8]", bits);
+  if (dout < 1 || din < 1 || dout > KQ_MAX_ROT_DIM || din > KQ_MAX_ROT_DIM || din % 16 != 0)
+    return fail(KQ_EINVAL, "kq_decode_matvec: shape %lld x %lld (din must be a multiple of 16, both <= %d)",
+                (long long)dout, (long long)din, KQ_MAX_ROT_DIM);
+  if (group < 0 || (group > 0 && (group % 16 != 0 || din % group != 0)))
+    return fail(KQ_EINVAL, "kq_decode_matvec: group %d must be 0 or a multiple of 16 dividing din", group);
+  if (tokens < 1 || tokens > KQ_DECODE_MAX_TOKENS)
+    return fail(KQ_EINVAL, "kq_decode_matvec: tokens = %lld outside [1, %d]", (long long)tokens,
+                KQ_DECODE_MAX_TOKENS);
+  if (rot_in && !rot_ok(rot_in, din, "input")) return KQ_EINVAL;
+  if (rot_out && !rot_ok(rot_out, dout, "output")) return KQ_EINVAL;
+  if (kq::decode_cpl(din, tokens) == 0)
+    return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: din %lld with %lld tokens (needs din * tokens <= 16384)",
+                (long long)din, (long long)tokens);
+  if (kq::decode_lds_bytes(dout, din, tokens, rot_in && rot_in->m > 1, rot_out != nullptr) > 160 * 1024)
+    return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: %lld tokens of a %lld x %lld layer exceed LDS", (long long)tokens,
+                (long long)dout, (long long)din);
+  if (!ws_ok(ws, ws_bytes, kq::decode_workspace(dout, tokens))) return KQ_EINVAL;
+  return kq::decode_run(packed, scales, zeros, dout, din, bits, group, s_x, s_g, rot_in, rot_out, x, tokens, y, ws,
+                        kq::as_stream(stream));
 }
 
 }  // extern "C"

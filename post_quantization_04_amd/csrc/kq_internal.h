@@ -67,4 +67,14 @@ kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits
                   uint8_t* codes, float* scales, uint8_t* zeros, double* preround, void* ws,
                   hipStream_t st);
 
+// packed codes and the decode matvec (decode.hip)
+int container_bits(int bits);
+int decode_cpl(int64_t din, int64_t tokens);
+size_t decode_workspace(int64_t dout, int64_t tokens);
+size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_mix, bool out_rot);
+kq_status pack_run(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* packed, hipStream_t st);
+kq_status decode_run(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout, int64_t din,
+                     int bits, int group, const double* s_x, const double* s_g, const kq_rot* rot_in,
+                     const kq_rot* rot_out, const float* x, int64_t tokens, float* y, void* ws, hipStream_t st);
+
 }  // namespace kq

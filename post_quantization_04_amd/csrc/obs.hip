@@ -346,7 +346,7 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
                                           int64_t i0, int64_t j0) {
   static_assert(WR * WC == 4 && TM % (16 * WR) == 0 && TN % (16 * WC) == 0, "tile shape");
   constexpr int BM = TM / WR / 16, BN = TN / WC / 16;  // 16 x 16 blocks per wave
-  constexpr int DA = TM / 16, DB = TN / 16;            // doubles of E, floats of R per thread per chunk
+  constexpr int DA = TM / 16;                          // doubles of E per thread per chunk
   static_assert(DA % 2 == 0 && (kTK * TN) % 256 == 0, "chunk shape");
   const int mv = static_cast<int>(dout - i0 < TM ? dout - i0 : TM);
   const int nv = static_cast<int>(din - j0 < TN ? din - j0 : TN);

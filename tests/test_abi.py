@@ -104,6 +104,34 @@ def test_cholesky_and_score_validation(L):
     assert L.kq_sensitivity(FAKE, 8, FAKE, 8, 5, FAKE, None) == kq.KQ_EINVAL
 
 
+def test_pack_and_decode_validation(L):
+    assert L.kq_pack_codes(FAKE, 4, 64, 1, FAKE, None) == kq.KQ_EINVAL
+    assert L.kq_pack_codes(FAKE, 4, 60, 2, FAKE, None) == kq.KQ_EINVAL   # 16 2-bit codes per word
+    assert L.kq_pack_codes(FAKE, 4, 36, 3, FAKE, None) == kq.KQ_EINVAL   # 8 4-bit containers per word
+    assert L.kq_pack_codes(FAKE, 0, 64, 2, FAKE, None) == kq.KQ_OK       # nothing to pack
+    big = 1 << 30
+
+    def call(dout=4096, din=4096, bits=2, group=128, tokens=1, rin=None, rout=None, ws=big):
+        return L.kq_decode_matvec(FAKE, FAKE, FAKE, dout, din, bits, group, None, None,
+                                  None if rin is None else ctypes.byref(rin),
+                                  None if rout is None else ctypes.byref(rout), FAKE, tokens, FAKE, FAKE, ws, None)
+    assert call(bits=1) == kq.KQ_EINVAL
+    assert call(din=4100) == kq.KQ_EINVAL                  # din not a multiple of 16
+    assert call(group=48) == kq.KQ_EINVAL                  # 48 does not divide 4096
+    assert call(group=8, din=64) == kq.KQ_EINVAL
+    assert call(tokens=0) == kq.KQ_EINVAL
+    assert call(tokens=kq.KQ_DECODE_MAX_TOKENS + 1) == kq.KQ_EINVAL
+    assert call(din=8192, tokens=3) == kq.KQ_EUNSUPPORTED  # din * tokens > 16384
+    out = kq.Rot(n=16384, m=1, log2p=14, signs=0x1000, q=0x1000)
+    assert call(dout=16384, tokens=4, rout=out) == kq.KQ_EUNSUPPORTED  # output side exceeds LDS
+    assert b"LDS" in L.kq_last_error()
+    wrong = kq.Rot(n=4096, m=1, log2p=12, signs=0x1000, q=0x1000)
+    assert call(dout=16384, rout=wrong) == kq.KQ_EINVAL   # spec for another dimension
+    need = L.kq_workspace_size(kq.KQ_OP_DECODE, 4096, 2, 0)
+    assert need >= 2 * 4096 * 4
+    assert call(tokens=2, ws=need - 1) == kq.KQ_EINVAL
+
+
 def test_workspace_sizes(L):
     inv = ctypes.c_size_t(-1).value
     assert L.kq_workspace_size(99, 1, 1, 1) == inv

@@ -1,0 +1,119 @@
+"""GPU parity of the packed codes and the decode matvec against the CPU oracle."""
+import numpy as np
+import pytest
+
+import kq_synth
+import oracle
+from gpu_helpers import DEV, host, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _kq():
+    import post_quantization_04_amd as kq
+    from post_quantization_04_amd import pipeline
+    return kq, pipeline
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6])
+def test_pack_codes(bits):
+    import torch
+    kq, _ = _kq()
+    rng = np.random.default_rng(bits)
+    rows, cols = 37, 16 * 24
+    codes = rng.integers(0, 1 << bits, size=(rows, cols), dtype=np.uint8)
+    c = oracle.container_bits(bits)
+    out = torch.zeros((rows, cols * c // 32), dtype=torch.int32, device=DEV)
+    kq.pack_codes(to_dev(codes), bits, out)
+    np.testing.assert_array_equal(host(out).view(np.uint32), oracle.pack_codes(codes, bits))
+
+
+def _layer(rng, dout, din, bits, group):
+    ng = din // group if group else 1
+    codes = rng.integers(0, 1 << bits, size=(dout, din), dtype=np.uint8)
+    scales = rng.uniform(0.005, 0.05, size=(dout, ng)).astype(np.float32)
+    zeros = rng.integers(0, 1 << bits, size=(dout, ng), dtype=np.uint8)
+    return codes, scales, zeros
+
+
+def _decode(kq, pipeline, codes, scales, zeros, bits, group, s_x, s_g, ri, ro, x, inp=True, out=True):
+    import torch
+    dout, din = codes.shape
+    c = oracle.container_bits(bits)
+    packed = torch.zeros((dout, din * c // 32), dtype=torch.int32, device=DEV)
+    kq.pack_codes(to_dev(codes), bits, packed)
+    dri = pipeline.upload_rot(ri.signs, ri.q, DEV) if inp else None
+    dro = pipeline.upload_rot(ro.signs, ro.q, DEV) if out else None
+    y = torch.empty((x.shape[0], dout), dtype=torch.float32, device=DEV)
+    kq.decode_matvec(packed, to_dev(scales), to_dev(zeros), bits, group,
+                     None if s_x is None else to_dev(s_x), None if s_g is None else to_dev(s_g),
+                     dri.rot if inp else None, dro.rot if out else None, to_dev(x.astype(np.float32)), y)
+    return host(y)
+
+
+# shapes: m = 1 and odd factors on either side (7 x 512, 11 x 256), ragged last workgroup of
+# rows, per-row grids, 1..4 tokens, the LLaMA-2-7B q_proj layer at full size
+DECODE_CASES = [
+    (256, 512, 2, 128, 1), (4096, 4096, 2, 128, 1), (96, 320, 4, 64, 2), (200, 448, 3, 0, 3),
+    (448, 1024, 2, 128, 4), (160, 2048, 8, 32, 1), (384, 3584, 2, 128, 1), (2816, 1024, 4, 128, 2),
+]
+
+
+@pytest.mark.parametrize("dout,din,bits,group,tokens", DECODE_CASES)
+def test_decode_matvec(dout, din, bits, group, tokens):
+    kq, pipeline = _kq()
+    print(f"decode {dout}x{din} bits={bits} group={group} tokens={tokens}", flush=True)
+    rng = np.random.default_rng(dout * 7 + din)
+    codes, scales, zeros = _layer(rng, dout, din, bits, group)
+    s_x, s_g = rng.uniform(0.3, 3.0, din), rng.uniform(0.3, 3.0, dout)
+    ri, ro = kq_synth.rot_spec(11, "dx", din), kq_synth.rot_spec(11, "dg", dout)
+    x = rng.standard_normal((tokens, din))
+    want = oracle.decode_matvec(codes, scales, zeros, group, s_x, s_g, ri, ro, x.astype(np.float32))
+    got = _decode(kq, pipeline, codes, scales, zeros, bits, group, s_x, s_g, ri, ro, x)
+    # float32 transforms and sums: log2(n) roundings per transform and sqrt(din)-scaled
+    # accumulation error, both far below 1e-5 of the output norm
+    assert rel_fro(got, want) <= 2e-5
+
+
+@pytest.mark.parametrize("inp,out", [(False, False), (True, False), (False, True)])
+def test_decode_matvec_sides(inp, out):
+    kq, pipeline = _kq()
+    rng = np.random.default_rng(3)
+    dout, din, bits, group = 192, 640, 2, 64
+    codes, scales, zeros = _layer(rng, dout, din, bits, group)
+    ri, ro = kq_synth.rot_spec(2, "sx", din), kq_synth.rot_spec(2, "sg", dout)
+    x = rng.standard_normal((2, din))
+    ones_x, ones_g = np.ones(din), np.ones(dout)
+    want = oracle.decode_matvec(codes, scales, zeros, group, ones_x, ones_g, ri, ro, x.astype(np.float32),
+                                inp=inp, out=out)
+    got = _decode(kq, pipeline, codes, scales, zeros, bits, group, None, None, ri, ro, x, inp=inp, out=out)
+    assert rel_fro(got, want) <= 2e-5
+
+
+def test_decode_quantized_layer_and_repeat_calls():
+    """The codes of a layer quantized on the GPU, decoded twice with one workspace, against
+    the oracle's W^ x."""
+    import torch
+    kq, pipeline = _kq()
+    from test_gpu_parity import _run_layer, _workload
+    wl = _workload(2, 12000, {"q_proj": (256, 512)})
+    got = _run_layer(wl, "q_proj", "attn_in", bits=2)
+    cfg = wl.cfg
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((1, 512))
+    si, so = wl.rot_in("attn_in"), wl.rot_out("q_proj")
+    w64 = wl.weight_f64("q_proj")
+    hx, hg = oracle.covariance([wl.x("attn_in")]), oracle.covariance([wl.g("q_proj")])
+    _, _, _, s_x, s_g = oracle.biip_forward(w64, hx, hg, si, so)
+    want = oracle.decode_matvec(got["codes"], got["scales"], got["zeros"], cfg.group, s_x, s_g, si, so,
+                                x.astype(np.float32))
+    packed = torch.zeros((256, 512 // 16), dtype=torch.int32, device=DEV)
+    kq.pack_codes(to_dev(got["codes"]), 2, packed)
+    dri, dro = pipeline.upload_rot(si.signs, si.q, DEV), pipeline.upload_rot(so.signs, so.q, DEV)
+    ws = kq.decode_workspace(256, 1, DEV)
+    for _ in range(2):
+        y = torch.empty((1, 256), dtype=torch.float32, device=DEV)
+        kq.decode_matvec(packed, to_dev(got["scales"]), to_dev(got["zeros"]), 2, cfg.group, to_dev(s_x),
+                         to_dev(s_g), dri.rot, dro.rot, to_dev(x.astype(np.float32)), y, ws=ws)
+        # s_x, s_g from the oracle's float64 diagonal: within 1e-6 of the GPU's own
+        assert rel_fro(host(y), want) <= 2e-5

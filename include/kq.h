@@ -106,7 +106,7 @@ kq_status kq_timing_query(const char* name, int64_t* launches, double* total_ms)
  *   KQ_OP_BIIP:           d0 = dout, d1 = din
  *   KQ_OP_CHOLESKY:       d0 = d
  *   KQ_OP_OBS:            d0 = dout, d1 = din, d2 = block
- *   KQ_OP_DECODE:         d0 = dout, d1 = tokens
+ *   KQ_OP_DECODE:         d0 = dout, d1 = din, d2 = tokens
  * Returns (size_t)-1 for invalid sizes.
  */
 size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
@@ -270,10 +270,12 @@ kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_
  * W^ = S_G^-1 U_G^T W^'' U_X S_X^-1 with W^''[i][j] = scale[i][g] (code_ij - zero[i][g]),
  * g = j / group: the fused dequantization + BiIP matvec of the deployment
  * path ([KQ-news]); at inference each layer applies the two Hadamard
- * transforms, O(d log d) each ([KQ-art] Q&A). The input side is applied to x
- * in every workgroup of the matvec launch and rows are dequantized from the
- * packed codes as they stream in; a second one-workgroup launch applies the
- * output side (only when rot_out is given).
+ * transforms, O(d log d) each ([KQ-art] Q&A). The input side (when rot_in or
+ * s_x is given) runs either inside every workgroup of the matvec launch, in LDS
+ * while its first rows of packed codes are in flight (no odd factor, at most one
+ * workgroup per CU), or as a one-workgroup launch before it; the matvec
+ * dequantizes rows as they stream in; a one-workgroup launch after it applies
+ * the output side (when rot_out is given; s_g alone is applied by the matvec).
  *   packed   device uint32 [dout, din * c / 32] from kq_pack_codes
  *   scales   device float32 [dout, din / group] (group 0: [dout, 1]), as kq_obs_quantize wrote them
  *   zeros    device uint8, same shape
@@ -284,8 +286,9 @@ kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_
  *   tokens   1..KQ_DECODE_MAX_TOKENS; din * tokens <= 16384 and, with rot_out,
  *            dout * tokens <= 36928 (the output side holds its tokens and the odd
  *            factor in 160 KB of LDS); KQ_EUNSUPPORTED otherwise
- *   ws       kq_workspace_size(KQ_OP_DECODE, dout, tokens, 0) bytes (the matvec
- *            result before the output side); calls sharing it must not overlap
+ *   ws       kq_workspace_size(KQ_OP_DECODE, dout, din, tokens) bytes (the matvec
+ *            result before the output side, x with the input side applied when
+ *            that runs as its own launch); calls sharing it must not overlap
  * Arithmetic is float32 (scales and rotation factors read as stored).
  */
 kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const uint8_t* zeros,

@@ -247,10 +247,10 @@ def pack_codes(codes, bits: int, packed, *, stream=None) -> None:
     _check(lib().kq_pack_codes(_ptr(codes), rows, cols, bits, _ptr(packed), _stream(stream)), "kq_pack_codes")
 
 
-def decode_workspace(dout: int, tokens: int, device):
+def decode_workspace(dout: int, din: int, tokens: int, device):
     """A workspace for decode_matvec."""
     import torch
-    return torch.empty(workspace_size(KQ_OP_DECODE, dout, tokens), dtype=torch.uint8, device=device)
+    return torch.empty(workspace_size(KQ_OP_DECODE, dout, din, tokens), dtype=torch.uint8, device=device)
 
 
 def decode_matvec(packed, scales, zeros, bits: int, group: int, s_x, s_g, rot_in: Optional[Rot],
@@ -275,7 +275,7 @@ def decode_matvec(packed, scales, zeros, bits: int, group: int, s_x, s_g, rot_in
     _need(s_x is None or s_x.numel() == din, "decode_matvec: s_x must hold din entries")
     _need(s_g is None or s_g.numel() == dout, "decode_matvec: s_g must hold dout entries")
     if ws is None:
-        ws = decode_workspace(dout, tokens, x.device)
+        ws = decode_workspace(dout, din, tokens, x.device)
     _check(lib().kq_decode_matvec(_ptr(packed), _ptr(scales), _ptr(zeros), dout, din, bits, group, _ptr(s_x),
                                   _ptr(s_g), None if rot_in is None else ctypes.byref(rot_in),
                                   None if rot_out is None else ctypes.byref(rot_out), _ptr(x), tokens, _ptr(y),

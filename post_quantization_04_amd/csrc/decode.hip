@@ -10,20 +10,24 @@
 // Packing: code j of a row sits in word j / (32 / c) at bits c (j mod 32 / c),
 // with c = 2 for 2-bit codes, 4 for 3- and 4-bit codes, 8 above.
 //
-// Per layer and token batch (T <= 4 tokens):
-//   1. every workgroup forms x1 = U_X S_X^-1 x in LDS (signs and scales on
-//      load, fast Walsh-Hadamard transform per 2^k chunk in radix-16 register
-//      passes, odd-factor mix across the m chunks) and keeps the entries its
-//      lanes need in registers;
-//   2. 16 rows per workgroup: the four waves split each row's packed words
-//      (lane l of wave w reads word 64 w + l + 256 i), dequantize on the fly,
-//      y1[row] = sum_g s_g (sum_j q_j x1_j - z_g sum_j x1_j), one 32-bit load
-//      per word and row, the loads of all 16 rows in flight at once for
-//      rows of up to 256 words;
-//   3. a second, one-workgroup launch applies the output side to y1:
-//      transform per chunk, transposed odd mix, signs, 1 / s_g. (A fused
-//      last-workgroup variant needed a device-scope fence in every workgroup,
-//      which cost more than the launch.)
+// Per layer and token batch (T <= 4 tokens), three launches on one stream:
+//   1. input side, one 1024-thread workgroup: x1 = U_X S_X^-1 x (signs and
+//      scales on load, fast Walsh-Hadamard transform per 2^k chunk in radix-16
+//      register passes, odd-factor mix across the m chunks) into the workspace;
+//      skipped when there is neither a rotation nor a scale on that side;
+//   2. the matvec, 16 rows per 256-thread workgroup: every lane loads the x1
+//      entries of its words straight into registers, then the four waves split
+//      each row's packed words (lane l of wave w reads word 64 w + l + 256 i),
+//      dequantize on the fly, y1[row] = sum_g s_g (sum_j q_j x1_j - z_g sum_j x1_j),
+//      one 32-bit load per word and row, the loads of up to 16 rows in flight;
+//   3. output side, one 1024-thread workgroup: transform per chunk, transposed
+//      odd mix, signs, 1 / s_g (only with an output rotation; a scale alone is
+//      applied by the matvec).
+// The side transforms run once per call rather than once per matvec workgroup,
+// and each issues every global load of its first batch before its first wait:
+// the data are small and the cost is round trips, not bytes. (A fused
+// last-workgroup output side needed a device-scope fence in every workgroup,
+// which cost more than the launch.)
 // Everything is float32; the float64 diagonal scales and rotation factors are
 // rounded to float32 on load.
 #include "kq_internal.h"
@@ -31,9 +35,10 @@
 namespace kq {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // matvec workgroup
+constexpr int kSideThreads = 1024;  // side-transform workgroup
 constexpr int kRowsPerWg = 16;
-constexpr int kBatch = 8;  // vector entries per thread whose loads are issued together
+constexpr int kQPitch = 64;         // LDS row pitch of a staged odd factor (e >> 6, e & 63 rely on it)
 
 __global__ void pack_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t cols, int c,
                             uint32_t* __restrict__ packed) {
@@ -62,20 +67,21 @@ struct DecodeArgs {
   const uint8_t* zeros;
   int64_t dout, din;
   int group, ngroups;
-  Side in, out;
-  const float* x;   // [T, din]
-  float* y;         // [T, dout]
-  float* y1;        // scratch [T, dout]
+  const float* x;     // [T, din]: x itself (fused input side) or x1 (separate or no input side)
+  Side in;            // the input side, for the fused form
+  float* y;           // [T, dout] final output (no output rotation) ...
+  float* y1;          // ... or the matvec result before the output side
+  const double* s_g;  // applied by the matvec when there is no output rotation
 };
 
 // One pass of the fast Walsh-Hadamard transform over index bits [o, o + R) of every token's
 // n entries (pitch n): a thread owns the 2^R entries of one group (indices that differ only in
 // those bits) and does the R butterfly stages in registers.
-template <int T, int R>
+template <int T, int R, int NT>
 __device__ void fwht_pass(float* v, int n, int o) {
   constexpr int L = 1 << R;
   const int groups = n >> R, stride = 1 << o;
-  for (int e = threadIdx.x; e < T * groups; e += kThreads) {
+  for (int e = threadIdx.x; e < T * groups; e += NT) {
     const int t = e / groups, gidx = e - t * groups;
     const int base = ((gidx >> o) << (o + R)) | (gidx & (stride - 1));
     float* row = v + t * n + base;
@@ -98,118 +104,228 @@ __device__ void fwht_pass(float* v, int n, int o) {
 }
 
 // H_p (unnormalised) on every chunk of p = 2^log2p entries of each token's n = m p entries.
-template <int T>
+template <int T, int NT>
 __device__ void fwht_lds(float* v, int n, int log2p) {
   for (int o = 0; o < log2p; o += 4) {
     switch (log2p - o) {
-      case 1: fwht_pass<T, 1>(v, n, o); break;
-      case 2: fwht_pass<T, 2>(v, n, o); break;
-      case 3: fwht_pass<T, 3>(v, n, o); break;
-      default: fwht_pass<T, 4>(v, n, o); break;
+      case 1: fwht_pass<T, 1, NT>(v, n, o); break;
+      case 2: fwht_pass<T, 2, NT>(v, n, o); break;
+      case 3: fwht_pass<T, 3, NT>(v, n, o); break;
+      default: fwht_pass<T, 4, NT>(v, n, o); break;
     }
   }
 }
 
-// Odd-factor mix across the m chunks of p (column b of the m x p view of each token's
-// vector): out[a] = sum_a' W[a][a'] v[a'] with W = Q (TRANS: Q^T), times `post`
-// (1 / sqrt(p)). W is staged in LDS as float32 with qs[a' * 64 + a] = W[a][a'] post; a
-// thread forms the m outputs of one column 16 at a time, reading the 16 weights of each
-// input as four workgroup-uniform float4s. OOP: the outputs go to dst (same layout as v)
-// as they are formed; otherwise they go back to v once all of the column's are formed.
-constexpr int kQPitch = 64;  // (e >> 6 and e & 63 below rely on it)
-template <int T, bool TRANS, bool OOP>
-__device__ void mix_lds(float* v, float* dst, int n, int m, int log2p, const double* __restrict__ q, float* qs,
-                        float post) {
-  // batches of kBatch entries per thread, every load issued before the stores
-  for (int base = 0; base < m * kQPitch; base += kBatch * kThreads) {
-    float qb[kBatch];
+// 16 outputs of column b of token t from the m inputs at row[a2 p]: acc[k] = sum_a2 qs[a2 64 + g0 + k] in_a2,
+// the 16 weights of an input read as four float4s (workgroup-uniform when the 64 lanes of a
+// wave share g0).
+__device__ __forceinline__ void mix16(const float* row, int p, int m, const float* qs, int g0, float* acc) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int e = base + k * kThreads + static_cast<int>(threadIdx.x);
-      const int a2 = e >> 6, a = e & (kQPitch - 1);
-      qb[k] = (e < m * kQPitch && a < m) ? static_cast<float>(TRANS ? q[a2 * m + a] : q[a * m + a2]) * post : 0.0f;
-    }
+  for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+  for (int a2 = 0; a2 < m; ++a2) {
+    const float x = row[a2 * p];
+    const float4* w = reinterpret_cast<const float4*>(qs + a2 * kQPitch + g0);
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int e = base + k * kThreads + static_cast<int>(threadIdx.x);
-      if (e < m * kQPitch) qs[e] = qb[k];
+    for (int c = 0; c < 4; ++c) {
+      const float4 wc = w[c];
+      acc[4 * c] = fmaf(wc.x, x, acc[4 * c]);
+      acc[4 * c + 1] = fmaf(wc.y, x, acc[4 * c + 1]);
+      acc[4 * c + 2] = fmaf(wc.z, x, acc[4 * c + 2]);
+      acc[4 * c + 3] = fmaf(wc.w, x, acc[4 * c + 3]);
     }
   }
-  __syncthreads();
+}
+
+// Odd-factor mix across the m chunks of p, in place (column b of the m x p view of each token's
+// vector): out[a] = sum_a' W[a][a'] v[a'], with qs[a' * 64 + a] = W[a][a'] already staged.
+// Work items are (column, group of 16 outputs); a round takes whole columns, one item per
+// thread, all reads before a barrier and all writes after it.
+template <int T, int NT>
+__device__ void mix_lds(float* v, int n, int m, int log2p, const float* qs) {
   const int p = 1 << log2p;
-  if constexpr (OOP) {
-    for (int e = threadIdx.x; e < T * p; e += kThreads) {
-      const int t = e >> log2p, b = e & (p - 1);
-      const float* row = v + t * n + b;
-      float* out = dst + t * n + b;
-      for (int ag = 0; ag < m; ag += 16) {
-        float acc[16];
+  const int cols = T * p, groups = (m + 15) >> 4;
+  const int cpr = NT / groups;                 // whole columns per round
+  const int gi = threadIdx.x / cpr;            // this thread's output group
+  const int cr = threadIdx.x - gi * cpr;       // and column within the round
+  for (int c0 = 0; c0 < cols; c0 += cpr) {
+    const int c = c0 + cr;
+    const bool act = gi < groups && c < cols;
+    float* row = v + (c >> log2p) * n + (c & (p - 1));
+    float acc[16];
+    if (act) mix16(row, p, m, qs, 16 * gi, acc);
+    __syncthreads();
+    if (act) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-        for (int a2 = 0; a2 < m; ++a2) {
-          const float x = row[a2 * p];
-          const float4* w = reinterpret_cast<const float4*>(qs + a2 * kQPitch + ag);
+      for (int k = 0; k < 16; ++k)
+        if (16 * gi + k < m) row[(16 * gi + k) * p] = acc[k];
+    }
+    __syncthreads();
+  }
+}
+
+// Stand-ins for an absent sign vector, scale vector or odd factor, so that the side kernel's
+// loads never sit under a condition.
+__device__ double kUnitScale = 1.0;
+__device__ int8_t kPlusSign = 1;
+
+// One side of the rotation applied in LDS by the NT threads of a workgroup, for T tokens of n
+// entries:
+//   input side (OUT false):  (Q (x) H_p / sqrt p) diag(sigma) S^-1 src
+//   output side (OUT true):  S^-1 diag(sigma) (Q^T (x) H_p / sqrt p) src
+// (sd.on false: the scale alone). issue() requests the values, signs and scales of the first
+// P * NT entries and the odd factor, all before the first wait; transform() stores them to LDS
+// (the input side with sign and scale applied), streams any further entries, stages Q (times
+// 1 / sqrt p) and runs the transform. On return lds[t n + i] times `tail` is the input side's
+// result; the output side's entry i is lds[t n + i] * fo[k] for i = k NT + tid (first batch)
+// and out_factor(i) beyond.
+//
+// Loads take clamped indices and are unconditional (entries past the end are never stored):
+// a load under a per-lane condition becomes a branch whose result the compiler waits for
+// before the next one, which would serialize the round trips.
+template <int T, int NT, int P, bool OUT>
+struct SideStage {
+  static constexpr int kQPer = (KQ_MAX_ODD * kQPitch + NT - 1) / NT;
+  const float* src;
+  int n, nl, m;
+  bool on, mixed;
+  int log2p;
+  const int8_t* sgp;
+  int sgi;
+  const double* svp;
+  int svi;
+  const double* qp;
+  float post, tail;
+  float val[P][T];
+  int sg[P];
+  double sv[P];
+  double qv[kQPer];
+  float fo[P];
+
+  __device__ __forceinline__ void issue(const float* src_, int n_, const Side& sd) {
+    const int tid = threadIdx.x;
+    src = src_;
+    n = n_;
+    nl = n - 1;
+    m = sd.m;
+    on = sd.on != 0;
+    mixed = on && m > 1;
+    log2p = sd.log2p;
+    sgp = on ? sd.signs : &kPlusSign;
+    sgi = on ? 1 : 0;
+    svp = sd.s ? sd.s : &kUnitScale;
+    svi = sd.s ? 1 : 0;
+    qp = sd.q ? sd.q : &kUnitScale;  // m = 1 without a rotation
+    post = on ? 1.0f / sqrtf(static_cast<float>(1 << log2p)) : 1.0f;
+    tail = (on && !mixed) ? post : 1.0f;  // 1 / sqrt(p) when not folded into Q
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float4 wc = w[c];
-            acc[4 * c] = fmaf(wc.x, x, acc[4 * c]);
-            acc[4 * c + 1] = fmaf(wc.y, x, acc[4 * c + 1]);
-            acc[4 * c + 2] = fmaf(wc.z, x, acc[4 * c + 2]);
-            acc[4 * c + 3] = fmaf(wc.w, x, acc[4 * c + 3]);
-          }
+    for (int k = 0; k < P; ++k) {
+      const int ic = min(k * NT + tid, nl);
+#pragma unroll
+      for (int t = 0; t < T; ++t) val[k][t] = src[t * n + ic];
+    }
+    const int ml = m - 1;
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int e = k * NT + tid;
+      const int a2 = min(e >> 6, ml), a = min(e & (kQPitch - 1), ml);
+      qv[k] = OUT ? qp[a2 * m + a] : qp[a * m + a2];
+    }
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int ic = min(k * NT + tid, nl);
+      sg[k] = sgp[ic * sgi];
+      sv[k] = svp[ic * svi];
+    }
+  }
+
+  __device__ __forceinline__ float out_factor(int i) const {
+    const int ic = min(i, nl);
+    return (sgp[ic * sgi] < 0 ? -tail : tail) / static_cast<float>(svp[ic * svi]);
+  }
+
+  __device__ __forceinline__ void transform(float* lds, float* qs) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int i = k * NT + tid;
+      const float sgn = sg[k] < 0 ? -1.0f : 1.0f;
+      fo[k] = OUT ? sgn * tail / static_cast<float>(sv[k]) : tail;
+      if (i < n) {
+        const float f = OUT ? 1.0f : sgn / static_cast<float>(sv[k]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) lds[t * n + i] = val[k][t] * f;
+      }
+    }
+    // entries past the first batch, one batch at a time
+    for (int base = P * NT; base < n; base += P * NT) {
+      float f[P];
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        const int ic = min(base + k * NT + tid, nl);
+#pragma unroll
+        for (int t = 0; t < T; ++t) val[k][t] = src[t * n + ic];
+        const float sgn = sgp[ic * sgi] < 0 ? -1.0f : 1.0f;
+        f[k] = OUT ? 1.0f : sgn / static_cast<float>(svp[ic * svi]);
+      }
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        const int i = base + k * NT + tid;
+        if (i < n) {
+#pragma unroll
+          for (int t = 0; t < T; ++t) lds[t * n + i] = val[k][t] * f[k];
         }
+      }
+    }
+    if (mixed) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (ag + k < m) out[(ag + k) * p] = acc[k];
+      for (int k = 0; k < kQPer; ++k) {
+        const int e = k * NT + tid;
+        if (e < m * kQPitch) qs[e] = (e & (kQPitch - 1)) < m ? static_cast<float>(qv[k]) * post : 0.0f;
       }
     }
     __syncthreads();
-    return;
-  }
-  for (int e = threadIdx.x; e < T * p; e += kThreads) {
-    const int t = e >> log2p, b = e & (p - 1);
-    float* row = v + t * n + b;
-    // the group loop is unrolled, so every index into res is a constant (registers only); the
-    // column's inputs stay in LDS until all its outputs are formed
-    constexpr int kGroups = (KQ_MAX_ODD + 15) / 16;
-    float res[kGroups][16];
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) res[gi][k] = 0.0f;
-      if (16 * gi < m) {
-        for (int a2 = 0; a2 < m; ++a2) {
-          const float x = row[a2 * p];
-          const float4* w = reinterpret_cast<const float4*>(qs + a2 * kQPitch + 16 * gi);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float4 wc = w[c];
-            res[gi][4 * c] = fmaf(wc.x, x, res[gi][4 * c]);
-            res[gi][4 * c + 1] = fmaf(wc.y, x, res[gi][4 * c + 1]);
-            res[gi][4 * c + 2] = fmaf(wc.z, x, res[gi][4 * c + 2]);
-            res[gi][4 * c + 3] = fmaf(wc.w, x, res[gi][4 * c + 3]);
-          }
-        }
-      }
+    if (on) {
+      fwht_lds<T, NT>(lds, n, log2p);
+      if (mixed) mix_lds<T, NT>(lds, n, m, log2p, qs);
     }
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi)
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (16 * gi + k < m) row[(16 * gi + k) * p] = res[gi][k];
   }
-  __syncthreads();
+};
+
+// Floats of LDS a side transform of T x n entries uses: the entries, then Q at a 16-byte boundary.
+__host__ __device__ constexpr int side_lds_floats(int n, int tokens) {
+  return ((tokens * n + 3) & ~3) + KQ_MAX_ODD * kQPitch;
+}
+
+// One side for T tokens of n entries in one 1024-thread workgroup: dst = S^-1 U^T src (output
+// side) or U S^-1 src (input side, when it is not fused into the matvec).
+template <int T, bool OUT>
+__global__ __launch_bounds__(kSideThreads) void side_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                           int n, Side sd) {
+  extern __shared__ float lds[];
+  constexpr int P = 16 / T;
+  SideStage<T, kSideThreads, P, OUT> st;
+  st.issue(src, n, sd);
+  st.transform(lds, lds + side_lds_floats(n, T) - KQ_MAX_ODD * kQPitch);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const int i = k * kSideThreads + tid;
+    if (i < n) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) dst[t * n + i] = lds[t * n + i] * st.fo[k];
+    }
+  }
+  for (int i = P * kSideThreads + tid; i < n; i += kSideThreads) {
+    const float f = OUT ? st.out_factor(i) : st.tail;
+#pragma unroll
+    for (int t = 0; t < T; ++t) dst[t * n + i] = lds[t * n + i] * f;
+  }
 }
 
 // Code k (k < 32 / C) of a packed word with C-bit containers, as a float.
 template <int C>
 __device__ __forceinline__ float code_at(uint32_t w, int k) {
   return static_cast<float>((w >> (C * k)) & ((1u << C) - 1u));
-}
-
-// Floats at the front of the matvec kernel's LDS: the T x1 vectors, later the row partials.
-__host__ __device__ constexpr int main_vec_floats(int din, int tokens) {
-  return tokens * din > kRowsPerWg * 4 * tokens ? tokens * din : kRowsPerWg * 4 * tokens;
 }
 
 // Sum over the 64 lanes of a wave, returned uniform: DPP adds inside each row of 16 lanes
@@ -227,99 +343,112 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // C: container bits; CPL: codes per lane per row (din <= 256 CPL), held in registers with
-// their x1 values; T: tokens (CPL T <= 64).
-template <int C, int CPL, int T>
+// their x1 values; T: tokens (CPL T <= 64); IN: the input side is fused (applied in LDS by
+// every workgroup), else x holds x1 already.
+template <int C, int CPL, int T, bool IN>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
-  extern __shared__ float lds[];
+  extern __shared__ float lds[];  // the input side's vectors and odd factor, when it runs
+  __shared__ float part[kRowsPerWg * 4 * T];
   constexpr int PER = 32 / C;          // codes per word
   constexpr int NW = CPL / PER;        // words per lane per row
-  constexpr int U = NW == 1 ? 16 : (NW == 2 ? 8 : (NW == 4 ? 2 : 1));  // rows in flight
-  static_assert(NW >= 1 && CPL % PER == 0, "codes per lane");
+  constexpr int U = NW <= 16 ? 16 / NW : 1;  // rows in flight: 16 words per lane
+  static_assert(NW >= 1 && CPL % PER == 0 && PER % 4 == 0, "codes per lane");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t din = g.din, dout = g.dout;
   const int64_t wpr = din / PER;  // words per row
+  const int din32 = static_cast<int>(din);
 
-  // the first rows' codes, scales and zero points do not depend on x: their loads go first
+  // Every load is unconditional, at a clamped index: a load under a per-lane condition becomes
+  // a branch whose result the compiler waits for before the next one. Lanes past the end of a
+  // row get x1 = 0 (so their words add nothing), and rows past dout are never stored.
+  const int wl = static_cast<int>(wpr) - 1;
+  int kw[NW], gcol[NW];
+  bool kv[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int k = 64 * wave + lane + 256 * i;
+    kv[i] = k <= wl;
+    kw[i] = min(k, wl);
+    gcol[i] = g.group ? (kw[i] * PER) / g.group : 0;
+  }
   const int64_t r0 = int64_t(blockIdx.x) * kRowsPerWg;
-  uint32_t wd[U][NW];
-  float sc[U][NW], ze[U][NW];
+  uint32_t wd[U][NW], zr[U][NW];
+  float sc[U][NW];
   auto load_rows = [&](int rb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = r0 + rb + u;
-      const bool rv = row < dout;
+      const int64_t row = min(r0 + rb + u, dout - 1);
+      const uint32_t* prow = g.packed + row * wpr;
+      const float* srow = g.scales + row * g.ngroups;
+      const uint8_t* zrow = g.zeros + row * g.ngroups;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const int64_t k = 64 * wave + lane + 256 * i;
-        const bool ok = rv && k < wpr;
-        wd[u][i] = ok ? g.packed[row * wpr + k] : 0u;
-        const int64_t gi = g.group ? (k * PER) / g.group : 0;
-        sc[u][i] = ok ? g.scales[row * g.ngroups + gi] : 0.0f;
-        ze[u][i] = ok ? static_cast<float>(g.zeros[row * g.ngroups + gi]) : 0.0f;
+        wd[u][i] = prow[kw[i]];
+        sc[u][i] = srow[gcol[i]];
+        zr[u][i] = zrow[gcol[i]];
       }
     }
   };
-  load_rows(0);
 
-  // 1. x1 = U_X S_X^-1 x, in LDS [T][din]; Q of a mixed side staged after the vectors, the
-  // mixed vectors after Q
-  const int din32 = static_cast<int>(din);
-  float* qs = lds + main_vec_floats(din32, T);
-  float* mixed = qs + KQ_MAX_ODD * kQPitch;
-  const float post_in = g.in.on ? 1.0f / sqrtf(static_cast<float>(1 << g.in.log2p)) : 1.0f;
-  // batches of kBatch entries per thread: every load of a batch is issued before its stores
-  for (int base = 0; base < din32; base += kBatch * kThreads) {
-    float xb[kBatch][T], fb[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int j = base + k * kThreads + tid;
-      const bool ok = j < din32;
-      const float sg = (ok && g.in.on && g.in.signs[j] < 0) ? -1.0f : 1.0f;
-      fb[k] = (ok && g.in.s) ? sg / static_cast<float>(g.in.s[j]) : sg;
-#pragma unroll
-      for (int t = 0; t < T; ++t) xb[k][t] = ok ? g.x[t * din + j] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int j = base + k * kThreads + tid;
-      if (j < din32) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) lds[t * din32 + j] = xb[k][t] * fb[k];
-      }
-    }
-  }
-  __syncthreads();
-  const float* x1 = lds;
-  if (g.in.on) {
-    fwht_lds<T>(lds, din32, g.in.log2p);
-    if (g.in.m > 1) {
-      mix_lds<T, false, true>(lds, mixed, din32, g.in.m, g.in.log2p, g.in.q, qs, post_in);
-      x1 = mixed;
-    }
-  }
-  const float xscale = (g.in.on && g.in.m == 1) ? post_in : 1.0f;
-  // this lane's words: k = 64 wave + lane + 256 i
+  // x1 = U_X S_X^-1 x for this lane's words k = 64 wave + lane + 256 i (PER consecutive entries
+  // each). Fused input side: its loads first, then the first rows' (so that waiting for the
+  // former leaves the latter in flight), then the transform in LDS, which every workgroup
+  // repeats. Otherwise straight from x1, 16-byte aligned.
   float xv[NW][PER][T];
+  if constexpr (IN) {
+    SideStage<T, kThreads, 16 / T, false> st;
+    st.issue(g.x, din32, g.in);
+    load_rows(0);
+    st.transform(lds, lds + side_lds_floats(din32, T) - KQ_MAX_ODD * kQPitch);
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4* src = reinterpret_cast<const float4*>(lds + t * din32 + kw[i] * PER);
+#pragma unroll
+        for (int c4 = 0; c4 < PER / 4; ++c4) {
+          const float4 v = src[c4];
+          xv[i][4 * c4][t] = v.x * st.tail;
+          xv[i][4 * c4 + 1][t] = v.y * st.tail;
+          xv[i][4 * c4 + 2][t] = v.z * st.tail;
+          xv[i][4 * c4 + 3][t] = v.w * st.tail;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4* src = reinterpret_cast<const float4*>(g.x + t * din + int64_t(kw[i]) * PER);
+#pragma unroll
+        for (int c4 = 0; c4 < PER / 4; ++c4) {
+          const float4 v = src[c4];
+          xv[i][4 * c4][t] = v.x;
+          xv[i][4 * c4 + 1][t] = v.y;
+          xv[i][4 * c4 + 2][t] = v.z;
+          xv[i][4 * c4 + 3][t] = v.w;
+        }
+      }
+    load_rows(0);
+  }
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int c = 0; c < PER; ++c)
+#pragma unroll
+      for (int t = 0; t < T; ++t) xv[i][c][t] = kv[i] ? xv[i][c][t] : 0.0f;
   float xs[NW][T];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int64_t k = 64 * wave + lane + 256 * i;
+  for (int i = 0; i < NW; ++i)
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float sum = 0.0f;
 #pragma unroll
-      for (int c = 0; c < PER; ++c) {
-        const float v = k < wpr ? x1[t * din32 + static_cast<int>(k) * PER + c] * xscale : 0.0f;
-        xv[i][c][t] = v;
-        sum += v;
-      }
+      for (int c = 0; c < PER; ++c) sum += xv[i][c][t];
       xs[i][t] = sum;
     }
-  }
-  __syncthreads();  // LDS is reused for the row partials below
 
-  // 2. rows r0 .. r0 + 15: partial sums per wave, U rows at a time
-  float* part = lds;  // [kRowsPerWg][4][T]
+  // rows r0 .. r0 + 15: partial sums per wave, U rows at a time
   for (int rb = 0; rb < kRowsPerWg; rb += U) {
     if (rb > 0) load_rows(rb);
 #pragma unroll
@@ -334,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
           float dot = 0.0f;
 #pragma unroll
           for (int c = 0; c < PER; ++c) dot = fmaf(code_at<C>(wd[u][i], c), xv[i][c][t], dot);
-          acc[t] = fmaf(sc[u][i], fmaf(-ze[u][i], xs[i][t], dot), acc[t]);
+          acc[t] = fmaf(sc[u][i], fmaf(-static_cast<float>(zr[u][i]), xs[i][t], dot), acc[t]);
         }
       }
 #pragma unroll
@@ -345,75 +474,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
     }
   }
   __syncthreads();
-  const bool rotate_out = g.out.on != 0;
   for (int e = tid; e < kRowsPerWg * T; e += kThreads) {
     const int rr = e / T, t = e % T;
     const int64_t row = r0 + rr;
     if (row >= dout) continue;
     const float* pp = part + rr * 4 * T + t;
     const float v = (pp[0] + pp[T]) + (pp[2 * T] + pp[3 * T]);
-    if (rotate_out) {
+    if (g.y1) {
       g.y1[t * dout + row] = v;
     } else {
-      g.y[t * dout + row] = g.out.s ? v / static_cast<float>(g.out.s[row]) : v;
+      g.y[t * dout + row] = g.s_g ? v / static_cast<float>(g.s_g[row]) : v;
     }
   }
 }
 
-// Output side, one workgroup for all tokens: y = S_G^-1 U_G^T y1 (transform per chunk,
-// transposed odd mix, signs, 1 / s_g).
-template <int T>
-__global__ __launch_bounds__(kThreads) void decode_out_kernel(DecodeArgs g) {
-  extern __shared__ float lds[];
-  const int tid = threadIdx.x;
-  const int dout32 = static_cast<int>(g.dout);
-  float* qs = lds + T * dout32;
-  for (int base = 0; base < T * dout32; base += kBatch * kThreads) {
-    float vb[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int e = base + k * kThreads + tid;
-      vb[k] = e < T * dout32 ? g.y1[e] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int e = base + k * kThreads + tid;
-      if (e < T * dout32) lds[e] = vb[k];
-    }
-  }
-  __syncthreads();
-  const float post_out = 1.0f / sqrtf(static_cast<float>(1 << g.out.log2p));
-  fwht_lds<T>(lds, dout32, g.out.log2p);
-  if (g.out.m > 1) mix_lds<T, true, false>(lds, nullptr, dout32, g.out.m, g.out.log2p, g.out.q, qs, post_out);
-  const float yscale = g.out.m > 1 ? 1.0f : post_out;
-  for (int base = 0; base < dout32; base += kBatch * kThreads) {
-    float fb[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = base + k * kThreads + tid;
-      const bool ok = i < dout32;
-      const float sg = (ok && g.out.signs[i] < 0) ? -yscale : yscale;
-      fb[k] = (ok && g.out.s) ? sg / static_cast<float>(g.out.s[i]) : sg;
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = base + k * kThreads + tid;
-      if (i < dout32) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) g.y[t * g.dout + i] = lds[t * dout32 + i] * fb[k];
-      }
-    }
-  }
-}
-
-size_t main_lds_bytes(int64_t din, int64_t tokens, bool in_mix) {
-  const int64_t f = main_vec_floats(static_cast<int>(din), static_cast<int>(tokens)) + KQ_MAX_ODD * kQPitch +
-                    (in_mix ? tokens * din : 0);
-  return size_t(f) * sizeof(float);
-}
-
-size_t out_lds_bytes(int64_t dout, int64_t tokens) {
-  return size_t(tokens * dout + KQ_MAX_ODD * kQPitch) * sizeof(float);
+size_t side_lds_bytes(int64_t n, int64_t tokens) {
+  return size_t(side_lds_floats(static_cast<int>(n), static_cast<int>(tokens))) * sizeof(float);
 }
 
 bool allow_lds(const void* fn, size_t bytes) {
@@ -421,45 +497,65 @@ bool allow_lds(const void* fn, size_t bytes) {
          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes)) == hipSuccess;
 }
 
+template <int T, bool OUT>
+kq_status launch_side(const float* src, float* dst, int n, const Side& sd, hipStream_t st) {
+  const size_t lds = side_lds_bytes(n, T);
+  const char* name = OUT ? "decode_out_kernel" : "decode_in_kernel";
+  if (!allow_lds(reinterpret_cast<const void*>(&side_kernel<T, OUT>), lds))
+    return fail(KQ_EDEVICE, "%s: %zu bytes of LDS refused", name, lds);
+  {
+    LaunchTimer timer(name, st);
+    hipLaunchKernelGGL((side_kernel<T, OUT>), dim3(1), dim3(kSideThreads), lds, st, src, dst, n, sd);
+  }
+  return check_launch(name);
+}
+
+// in_mode: 0 no input side, 1 fused into the matvec, 2 separate launch into x1.
 template <int C, int CPL, int T>
-kq_status launch(const DecodeArgs& a, hipStream_t st) {
+kq_status launch(DecodeArgs a, int in_mode, float* x1, const Side* out, hipStream_t st) {
+  kq_status s = KQ_OK;
+  if (in_mode == 2) {
+    if ((s = launch_side<T, false>(a.x, x1, static_cast<int>(a.din), a.in, st)) != KQ_OK) return s;
+    a.x = x1;
+  }
   const unsigned grid = static_cast<unsigned>((a.dout + kRowsPerWg - 1) / kRowsPerWg);
-  const size_t lds_main = main_lds_bytes(a.din, T, a.in.on && a.in.m > 1);
-  if (!allow_lds(reinterpret_cast<const void*>(&decode_kernel<C, CPL, T>), lds_main))
-    return fail(KQ_EDEVICE, "decode_kernel: %zu bytes of LDS refused", lds_main);
+  const size_t lds = in_mode == 1 ? side_lds_bytes(a.din, T) : 0;
+  const void* fn = in_mode == 1 ? reinterpret_cast<const void*>(&decode_kernel<C, CPL, T, true>)
+                                : reinterpret_cast<const void*>(&decode_kernel<C, CPL, T, false>);
+  if (!allow_lds(fn, lds)) return fail(KQ_EDEVICE, "decode_kernel: %zu bytes of LDS refused", lds);
   {
     LaunchTimer timer("decode_kernel", st);
-    hipLaunchKernelGGL((decode_kernel<C, CPL, T>), dim3(grid), dim3(kThreads), lds_main, st, a);
+    if (in_mode == 1)
+      hipLaunchKernelGGL((decode_kernel<C, CPL, T, true>), dim3(grid), dim3(kThreads), lds, st, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<C, CPL, T, false>), dim3(grid), dim3(kThreads), 0, st, a);
   }
-  kq_status s = check_launch("decode_kernel");
-  if (s != KQ_OK || !a.out.on) return s;
-  const size_t lds_out = out_lds_bytes(a.dout, T);
-  if (!allow_lds(reinterpret_cast<const void*>(&decode_out_kernel<T>), lds_out))
-    return fail(KQ_EDEVICE, "decode_out_kernel: %zu bytes of LDS refused", lds_out);
-  {
-    LaunchTimer timer("decode_out_kernel", st);
-    hipLaunchKernelGGL((decode_out_kernel<T>), dim3(1), dim3(kThreads), lds_out, st, a);
-  }
-  return check_launch("decode_out_kernel");
+  if ((s = check_launch("decode_kernel")) != KQ_OK || !out) return s;
+  return launch_side<T, true>(a.y1, a.y, static_cast<int>(a.dout), *out, st);
 }
 
 template <int C>
-kq_status launch_t(const DecodeArgs& a, int cpl, int tokens, hipStream_t st) {
+kq_status launch_t(const DecodeArgs& a, int in_mode, float* x1, const Side* out, int cpl, int tokens,
+                   hipStream_t st) {
   if (cpl == 16) {
     switch (tokens) {
-      case 1: return launch<C, 16, 1>(a, st);
-      case 2: return launch<C, 16, 2>(a, st);
-      case 3: return launch<C, 16, 3>(a, st);
-      default: return launch<C, 16, 4>(a, st);
+      case 1: return launch<C, 16, 1>(a, in_mode, x1, out, st);
+      case 2: return launch<C, 16, 2>(a, in_mode, x1, out, st);
+      case 3: return launch<C, 16, 3>(a, in_mode, x1, out, st);
+      default: return launch<C, 16, 4>(a, in_mode, x1, out, st);
     }
   }
-  if (cpl == 32) return tokens == 1 ? launch<C, 32, 1>(a, st) : launch<C, 32, 2>(a, st);
-  return launch<C, 64, 1>(a, st);
+  if (cpl == 32)
+    return tokens == 1 ? launch<C, 32, 1>(a, in_mode, x1, out, st) : launch<C, 32, 2>(a, in_mode, x1, out, st);
+  return launch<C, 64, 1>(a, in_mode, x1, out, st);
 }
+
+size_t y1_bytes(int64_t dout, int64_t tokens) { return align_up(size_t(tokens) * dout * sizeof(float), 256); }
 
 Side make_side(const kq_rot* r, const double* s) {
   Side sd{};
   sd.on = r != nullptr;
+  sd.m = 1;
   if (r) {
     sd.m = r->m;
     sd.log2p = r->log2p;
@@ -474,11 +570,13 @@ Side make_side(const kq_rot* r, const double* s) {
 
 int container_bits(int bits) { return bits == 2 ? 2 : (bits <= 4 ? 4 : 8); }
 
-size_t decode_workspace(int64_t dout, int64_t tokens) { return align_up(size_t(tokens) * dout * sizeof(float), 256); }
+size_t decode_workspace(int64_t dout, int64_t din, int64_t tokens) {
+  return y1_bytes(dout, tokens) + align_up(size_t(tokens) * din * sizeof(float), 256);
+}
 
-size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_mix, bool out_rot) {
-  const size_t a = main_lds_bytes(din, tokens, in_mix);
-  const size_t b = out_rot ? out_lds_bytes(dout, tokens) : 0;
+size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_side, bool out_rot) {
+  const size_t a = in_side ? side_lds_bytes(din, tokens) : 0;
+  const size_t b = out_rot ? side_lds_bytes(dout, tokens) : 0;
   return a > b ? a : b;
 }
 
@@ -513,17 +611,27 @@ kq_status decode_run(const uint32_t* packed, const float* scales, const uint8_t*
   a.din = din;
   a.group = group;
   a.ngroups = group ? static_cast<int>(din / group) : 1;
-  a.in = make_side(rot_in, s_x);
-  a.out = make_side(rot_out, s_g);
   a.x = x;
+  a.in = make_side(rot_in, s_x);
   a.y = y;
-  a.y1 = static_cast<float*>(ws);
+  a.y1 = rot_out ? static_cast<float*>(ws) : nullptr;
+  a.s_g = s_g;
+  float* x1 = reinterpret_cast<float*>(static_cast<char*>(ws) + y1_bytes(dout, tokens));
+  // The input side runs inside the matvec when it is a plain transform (no odd factor) and the
+  // grid is at most one workgroup per CU (each workgroup repeats it: more would queue the
+  // copies behind each other); otherwise as its own one-workgroup launch. The direct path reads
+  // x as float4s, so an unaligned x with no input side goes through that launch too.
+  const bool need_in = rot_in || s_x || (reinterpret_cast<uintptr_t>(x) & 15) != 0;
+  const int64_t grid = (dout + kRowsPerWg - 1) / kRowsPerWg;
+  const int in_mode = !need_in ? 0 : (a.in.m == 1 && grid <= kCus ? 1 : 2);
+  const Side out = make_side(rot_out, s_g);
   const int t = static_cast<int>(tokens);
   const int cpl = decode_cpl(din, tokens);
+  const Side* pout = rot_out ? &out : nullptr;
   switch (container_bits(bits)) {
-    case 2: return launch_t<2>(a, cpl, t, st);
-    case 4: return launch_t<4>(a, cpl, t, st);
-    default: return launch_t<8>(a, cpl, t, st);
+    case 2: return launch_t<2>(a, in_mode, x1, pout, cpl, t, st);
+    case 4: return launch_t<4>(a, in_mode, x1, pout, cpl, t, st);
+    default: return launch_t<8>(a, in_mode, x1, pout, cpl, t, st);
   }
 }
 

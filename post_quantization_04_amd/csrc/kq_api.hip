@@ -105,8 +105,9 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2) {
       if (d0 < 1 || d1 < 1 || d2 < 1 || d1 > kMaxDim) return bad;
       return kq::obs_workspace(d0, d1, static_cast<int>(d2));
     case KQ_OP_DECODE:
-      if (d0 < 1 || d0 > KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_DECODE_MAX_TOKENS) return bad;
-      return kq::decode_workspace(d0, d1);
+      if (d0 < 1 || d0 > KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_MAX_ROT_DIM || d2 < 1 || d2 > KQ_DECODE_MAX_TOKENS)
+        return bad;
+      return kq::decode_workspace(d0, d1, d2);
     default:
       return bad;
   }
@@ -248,10 +249,10 @@ kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const ui
   if (kq::decode_cpl(din, tokens) == 0)
     return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: din %lld with %lld tokens (needs din * tokens <= 16384)",
                 (long long)din, (long long)tokens);
-  if (kq::decode_lds_bytes(dout, din, tokens, rot_in && rot_in->m > 1, rot_out != nullptr) > 160 * 1024)
+  if (kq::decode_lds_bytes(dout, din, tokens, rot_in || s_x, rot_out != nullptr) > 160 * 1024)
     return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: %lld tokens of a %lld x %lld layer exceed LDS", (long long)tokens,
                 (long long)dout, (long long)din);
-  if (!ws_ok(ws, ws_bytes, kq::decode_workspace(dout, tokens))) return KQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, kq::decode_workspace(dout, din, tokens))) return KQ_EINVAL;
   return kq::decode_run(packed, scales, zeros, dout, din, bits, group, s_x, s_g, rot_in, rot_out, x, tokens, y, ws,
                         kq::as_stream(stream));
 }

@@ -37,6 +37,8 @@ class LaunchTimer {
 
 // Number of XCDs on MI355X; workgroups are dispatched to them round robin.
 constexpr int kXcds = 8;
+// Compute units on MI355X (32 per XCD).
+constexpr int kCus = 256;
 
 // ---------------------------------------------------------------------------
 // module launchers (arguments already validated by the API layer)
@@ -70,8 +72,8 @@ kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits
 // packed codes and the decode matvec (decode.hip)
 int container_bits(int bits);
 int decode_cpl(int64_t din, int64_t tokens);
-size_t decode_workspace(int64_t dout, int64_t tokens);
-size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_mix, bool out_rot);
+size_t decode_workspace(int64_t dout, int64_t din, int64_t tokens);
+size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_side, bool out_rot);
 kq_status pack_run(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* packed, hipStream_t st);
 kq_status decode_run(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout, int64_t din,
                      int bits, int group, const double* s_x, const double* s_g, const kq_rot* rot_in,

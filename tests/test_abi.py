@@ -127,8 +127,9 @@ def test_pack_and_decode_validation(L):
     assert b"LDS" in L.kq_last_error()
     wrong = kq.Rot(n=4096, m=1, log2p=12, signs=0x1000, q=0x1000)
     assert call(dout=16384, rout=wrong) == kq.KQ_EINVAL   # spec for another dimension
-    need = L.kq_workspace_size(kq.KQ_OP_DECODE, 4096, 2, 0)
-    assert need >= 2 * 4096 * 4
+    need = L.kq_workspace_size(kq.KQ_OP_DECODE, 4096, 4096, 2)
+    assert need >= 2 * 2 * 4096 * 4
+    assert L.kq_workspace_size(kq.KQ_OP_DECODE, 4096, 4096, 0) == ctypes.c_size_t(-1).value
     assert call(tokens=2, ws=need - 1) == kq.KQ_EINVAL
 
 

@@ -52,10 +52,14 @@ def _decode(kq, pipeline, codes, scales, zeros, bits, group, s_x, s_g, ri, ro, x
 
 
 # shapes: m = 1 and odd factors on either side (7 x 512, 11 x 256), ragged last workgroup of
-# rows, per-row grids, 1..4 tokens, the LLaMA-2-7B q_proj layer at full size
+# rows, per-row grids, 1..4 tokens, an odd output width with no power-of-two part (63 = 63 x 1,
+# three tokens: 189 floats before the staged odd factor), the LLaMA-2-7B q_proj layer at full
+# size. The input side runs fused into the matvec (m = 1 on the input, at most 256 workgroups)
+# or as its own launch (an odd factor on the input, or 4224 rows = 264 workgroups).
 DECODE_CASES = [
     (256, 512, 2, 128, 1), (4096, 4096, 2, 128, 1), (96, 320, 4, 64, 2), (200, 448, 3, 0, 3),
     (448, 1024, 2, 128, 4), (160, 2048, 8, 32, 1), (384, 3584, 2, 128, 1), (2816, 1024, 4, 128, 2),
+    (63, 512, 2, 128, 3), (4224, 256, 2, 64, 2),
 ]
 
 
@@ -90,6 +94,47 @@ def test_decode_matvec_sides(inp, out):
     assert rel_fro(got, want) <= 2e-5
 
 
+@pytest.mark.parametrize("inp,out", [(False, False), (True, False), (False, True)])
+def test_decode_matvec_scales_without_rotation(inp, out):
+    """Diagonal scales on both sides with a rotation on at most one: the scale of a side with no
+    rotation is still applied (input side by the side transform, output side by the matvec)."""
+    kq, pipeline = _kq()
+    rng = np.random.default_rng(5)
+    dout, din, bits, group = 320, 768, 4, 128
+    codes, scales, zeros = _layer(rng, dout, din, bits, group)
+    s_x, s_g = rng.uniform(0.3, 3.0, din), rng.uniform(0.3, 3.0, dout)
+    ri, ro = kq_synth.rot_spec(4, "tx", din), kq_synth.rot_spec(4, "tg", dout)
+    x = rng.standard_normal((3, din))
+    want = oracle.decode_matvec(codes, scales, zeros, group, s_x, s_g, ri, ro, x.astype(np.float32),
+                                inp=inp, out=out)
+    got = _decode(kq, pipeline, codes, scales, zeros, bits, group, s_x, s_g, ri, ro, x, inp=inp, out=out)
+    assert rel_fro(got, want) <= 2e-5
+
+
+def test_decode_matvec_unaligned_input_view():
+    """x as a view 4 bytes into its buffer, no input side: the direct path's vector loads need
+    16-byte alignment, so such an input goes through the (identity) input-side launch."""
+    import torch
+    kq, pipeline = _kq()
+    rng = np.random.default_rng(6)
+    dout, din, bits, group = 128, 256, 2, 64
+    codes, scales, zeros = _layer(rng, dout, din, bits, group)
+    ro = kq_synth.rot_spec(5, "ug", dout)
+    x = rng.standard_normal((1, din)).astype(np.float32)
+    want = oracle.decode_matvec(codes, scales, zeros, group, np.ones(din), np.ones(dout), ro, ro, x,
+                                inp=False, out=True)
+    buf = torch.zeros(din + 1, dtype=torch.float32, device=DEV)
+    buf[1:] = to_dev(x[0])
+    xv = buf[1:].view(1, din)
+    assert xv.data_ptr() % 16 != 0
+    packed = torch.zeros((dout, din // 16), dtype=torch.int32, device=DEV)
+    kq.pack_codes(to_dev(codes), bits, packed)
+    dro = pipeline.upload_rot(ro.signs, ro.q, DEV)
+    y = torch.empty((1, dout), dtype=torch.float32, device=DEV)
+    kq.decode_matvec(packed, to_dev(scales), to_dev(zeros), bits, group, None, None, None, dro.rot, xv, y)
+    assert rel_fro(host(y), want) <= 2e-5
+
+
 def test_decode_quantized_layer_and_repeat_calls():
     """The codes of a layer quantized on the GPU, decoded twice with one workspace, against
     the oracle's W^ x."""
@@ -110,7 +155,7 @@ def test_decode_quantized_layer_and_repeat_calls():
     packed = torch.zeros((256, 512 // 16), dtype=torch.int32, device=DEV)
     kq.pack_codes(to_dev(got["codes"]), 2, packed)
     dri, dro = pipeline.upload_rot(si.signs, si.q, DEV), pipeline.upload_rot(so.signs, so.q, DEV)
-    ws = kq.decode_workspace(256, 1, DEV)
+    ws = kq.decode_workspace(256, 512, 1, DEV)
     for _ in range(2):
         y = torch.empty((1, 256), dtype=torch.float32, device=DEV)
         kq.decode_matvec(packed, to_dev(got["scales"]), to_dev(got["zeros"]), 2, cfg.group, to_dev(s_x),

@@ -141,7 +141,7 @@ def rotation_rows(spec: kq_synth.RotSpec, rows: Sequence[int]) -> np.ndarray:
 
 def rotate_rows(v: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
     """Apply x -> U x to every row of v (returns v U^T), via the Kronecker reshape."""
-    v = np.asarray(v, np.float64)
+    v = np.ascontiguousarray(v, np.float64)  # a transposed view makes numpy's batched products crawl
     k, n = v.shape
     if n != spec.n:
         raise ValueError("rotation size mismatch")
@@ -154,7 +154,7 @@ def rotate_rows(v: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
 
 def unrotate_rows(v: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
     """Apply x -> U^T x to every row of v (returns v U)."""
-    v = np.asarray(v, np.float64)
+    v = np.ascontiguousarray(v, np.float64)
     k, n = v.shape
     if n != spec.n:
         raise ValueError("rotation size mismatch")

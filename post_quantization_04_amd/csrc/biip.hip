@@ -260,6 +260,11 @@ struct RowFw {
 
 __device__ __forceinline__ int lpad(int e) { return e + (e >> 4); }
 
+// Stands in for an absent per-column factor: indexed with stride 0, so that the factor's load
+// never sits under a condition (a conditional load compiles to a branch whose result is waited
+// for at once, which serializes the loads of a group).
+__device__ double kUnitFactor = 1.0;
+
 template <typename Src>
 __device__ __forceinline__ void load16(const Src* p, double v[16]);
 template <>
@@ -340,14 +345,19 @@ __global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict_
   const Src* s = src + row * lds;
   Dst* o = dst + row * ldd;
   const double rowf = rf.rowf ? rf.rowf[row] : 1.0;
+  const double* colf = rf.colf ? rf.colf : &kUnitFactor;
+  const int cstep = rf.colf ? 1 : 0;
   for (int g = threadIdx.x; g < ng; g += kFwThreads) {
     const int e0 = g << 4;
     double v[16];
     load16<Src>(s + e0, v);
     if (!rf.inverse) {
       const uint32_t neg = neg_mask16(rf.signs + e0);
+      double cf[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = flip(v[i] * (rf.colf ? rowf * rf.colf[e0 + i] : rowf), neg, i);
+      for (int i = 0; i < 16; ++i) cf[i] = colf[(e0 + i) * cstep];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = flip(v[i] * (rowf * cf[i]), neg, i);
     }
     bfly16(v, 0);
 #pragma unroll
@@ -380,14 +390,18 @@ __global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict_
         for (int i = 0; i < 16; ++i) b0[i * lstep] = static_cast<T>(v[i]);
       } else {
         const uint32_t vo = uint32_t(e0) * uint32_t(sizeof(Dst));
+        if (rf.inverse) {
+          double f[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          double x = v[i] * rf.out_scale;
-          if (rf.inverse) {
+          for (int i = 0; i < 16; ++i) {
             const int e = e0 + (i << wlo);
-            x *= static_cast<double>(rf.signs[e]) * (rf.colf ? rowf * rf.colf[e] : rowf);
+            f[i] = static_cast<double>(rf.signs[e]) * (rowf * colf[e * cstep]);
           }
-          bstore<Dst>(ro, vo, i * gstep, x);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bstore<Dst>(ro, vo, i * gstep, v[i] * rf.out_scale * f[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bstore<Dst>(ro, vo, i * gstep, v[i] * rf.out_scale);
         }
       }
     }

@@ -474,49 +474,62 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
   const int rb = threadIdx.x >> 4;            // rows rb, rb + 16, rb + 32, rb + 48
   const int64_t tile_off = int64_t(tile) * kT * kT;
   const int64_t slice_stride = int64_t(ntiles) * kT * kT;
+  // the four rows' loads of four slices at a time are all in flight together (16 per thread);
+  // each entry still sums its slices four at a time, in order
+  const int64_t e0 = int64_t(si * 64 + rb) * kT + sj * 64 + cq;  // row rb; row rb + 16 k is + 16 k kT
+  double sum[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sum[k][c] = 0.0;
+  if (!first) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sum[k][c] = acc[tile_off + e0 + 16 * k * kT + c];
+  }
+  const float* pp = part + tile_off + e0;
+  int q = 0;
+  for (; q + 4 <= nsl; q += 4) {
+    float4 v[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[k][u] = *reinterpret_cast<const float4*>(pp + 16 * k * kT + (q + u) * slice_stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sum[k][0] += (double(v[k][0].x) + double(v[k][1].x)) + (double(v[k][2].x) + double(v[k][3].x));
+      sum[k][1] += (double(v[k][0].y) + double(v[k][1].y)) + (double(v[k][2].y) + double(v[k][3].y));
+      sum[k][2] += (double(v[k][0].z) + double(v[k][1].z)) + (double(v[k][2].z) + double(v[k][3].z));
+      sum[k][3] += (double(v[k][0].w) + double(v[k][1].w)) + (double(v[k][2].w) + double(v[k][3].w));
+    }
+  }
+  for (; q < nsl; ++q) {
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const float4*>(pp + 16 * k * kT + q * slice_stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sum[k][0] += v[k].x;
+      sum[k][1] += v[k].y;
+      sum[k][2] += v[k].z;
+      sum[k][3] += v[k].w;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int il = rb + 16 * k;
-    const int64_t e = int64_t(si * 64 + il) * kT + sj * 64 + cq;
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    if (!first) {
-      s0 = acc[tile_off + e];
-      s1 = acc[tile_off + e + 1];
-      s2 = acc[tile_off + e + 2];
-      s3 = acc[tile_off + e + 3];
-    }
-    const float* pp = part + tile_off + e;
-    int q = 0;
-    for (; q + 4 <= nsl; q += 4) {
-      const float4 v0 = *reinterpret_cast<const float4*>(pp + (q + 0) * slice_stride);
-      const float4 v1 = *reinterpret_cast<const float4*>(pp + (q + 1) * slice_stride);
-      const float4 v2 = *reinterpret_cast<const float4*>(pp + (q + 2) * slice_stride);
-      const float4 v3 = *reinterpret_cast<const float4*>(pp + (q + 3) * slice_stride);
-      s0 += (double(v0.x) + double(v1.x)) + (double(v2.x) + double(v3.x));
-      s1 += (double(v0.y) + double(v1.y)) + (double(v2.y) + double(v3.y));
-      s2 += (double(v0.z) + double(v1.z)) + (double(v2.z) + double(v3.z));
-      s3 += (double(v0.w) + double(v1.w)) + (double(v2.w) + double(v3.w));
-    }
-    for (; q < nsl; ++q) {
-      const float4 v = *reinterpret_cast<const float4*>(pp + q * slice_stride);
-      s0 += v.x;
-      s1 += v.y;
-      s2 += v.z;
-      s3 += v.w;
-    }
     if (!last) {
-      acc[tile_off + e] = s0;
-      acc[tile_off + e + 1] = s1;
-      acc[tile_off + e + 2] = s2;
-      acc[tile_off + e + 3] = s3;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[tile_off + e0 + 16 * k * kT + c] = sum[k][c];
       continue;
     }
-    const double sv[4] = {s0, s1, s2, s3};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int jl = cq + c;
       const int64_t gi = r0 + il, gj = c0 + jl;
-      double v = static_cast<double>(alpha) * sv[c];
+      double v = static_cast<double>(alpha) * sum[k][c];
       if (beta != 0.0f && gi < d && gj < d && (!dsub || il >= jl))
         v += static_cast<double>(beta) * static_cast<double>(h[gi * d + gj]);
       tr[il][jl] = static_cast<float>(v);

@@ -284,7 +284,7 @@ kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_
  *   rot_in, rot_out  HOST pointers to the rotation specs; NULL means U = I on that side
  *   x        device float32 [tokens, din], y device float32 [tokens, dout] (written)
  *   tokens   1..KQ_DECODE_MAX_TOKENS; din * tokens <= 16384 and, with rot_out,
- *            dout * tokens <= 36928 (the output side holds its tokens and the odd
+ *            dout * tokens <= 36864 (the output side holds its tokens and the odd
  *            factor in 160 KB of LDS); KQ_EUNSUPPORTED otherwise
  *   ws       kq_workspace_size(KQ_OP_DECODE, dout, din, tokens) bytes (the matvec
  *            result before the output side, x with the input side applied when

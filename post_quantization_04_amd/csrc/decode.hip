@@ -39,6 +39,9 @@ constexpr int kThreads = 256;       // matvec workgroup
 constexpr int kSideThreads = 1024;  // side-transform workgroup
 constexpr int kRowsPerWg = 16;
 constexpr int kQPitch = 64;         // LDS row pitch of a staged odd factor (e >> 6, e & 63 rely on it)
+constexpr int kQFloats = 64 * kQPitch;  // staged odd factor: 64 rows (m <= 63, rows padded to 4)
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __global__ void pack_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t cols, int c,
                             uint32_t* __restrict__ packed) {
@@ -103,10 +106,11 @@ __device__ void fwht_pass(float* v, int n, int o) {
   __syncthreads();
 }
 
-// H_p (unnormalised) on every chunk of p = 2^log2p entries of each token's n = m p entries.
+// H_p (unnormalised) on every chunk of p = 2^log2p entries of each token's n = m p entries,
+// index bits [o0, log2p) (the bits below o0 already transformed).
 template <int T, int NT>
-__device__ void fwht_lds(float* v, int n, int log2p) {
-  for (int o = 0; o < log2p; o += 4) {
+__device__ void fwht_lds(float* v, int n, int log2p, int o0 = 0) {
+  for (int o = o0; o < log2p; o += 4) {
     switch (log2p - o) {
       case 1: fwht_pass<T, 1, NT>(v, n, o); break;
       case 2: fwht_pass<T, 2, NT>(v, n, o); break;
@@ -116,48 +120,54 @@ __device__ void fwht_lds(float* v, int n, int log2p) {
   }
 }
 
-// 16 outputs of column b of token t from the m inputs at row[a2 p]: acc[k] = sum_a2 qs[a2 64 + g0 + k] in_a2,
-// the 16 weights of an input read as four float4s (workgroup-uniform when the 64 lanes of a
-// wave share g0).
-__device__ __forceinline__ void mix16(const float* row, int p, int m, const float* qs, int g0, float* acc) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-  for (int a2 = 0; a2 < m; ++a2) {
-    const float x = row[a2 * p];
-    const float4* w = reinterpret_cast<const float4*>(qs + a2 * kQPitch + g0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 wc = w[c];
-      acc[4 * c] = fmaf(wc.x, x, acc[4 * c]);
-      acc[4 * c + 1] = fmaf(wc.y, x, acc[4 * c + 1]);
-      acc[4 * c + 2] = fmaf(wc.z, x, acc[4 * c + 2]);
-      acc[4 * c + 3] = fmaf(wc.w, x, acc[4 * c + 3]);
-    }
-  }
-}
-
-// Odd-factor mix across the m chunks of p, in place (column b of the m x p view of each token's
-// vector): out[a] = sum_a' W[a][a'] v[a'], with qs[a' * 64 + a] = W[a][a'] already staged.
-// Work items are (column, group of 16 outputs); a round takes whole columns, one item per
-// thread, all reads before a barrier and all writes after it.
+// Odd-factor mix across the m chunks of p, in place: for every token t and column b of the
+// m x p view of its vector, out[a] = sum_a' W[a][a'] v[a' p + b], with qs[a' * 64 + a] =
+// W[a][a'] staged (zero for a or a' >= m, up to a' < 4 ceil(m / 4)). A matrix product
+// OUT = W V with V the m x (T p) matrix of the columns, on float32 MFMA (16 x 16 x 4): a wave
+// takes one block of 16 columns and forms all ceil(m / 16) row tiles of it; every wave reads
+// its inputs before a barrier and writes after it, in rounds of whole column blocks.
 template <int T, int NT>
-__device__ void mix_lds(float* v, int n, int m, int log2p, const float* qs) {
+__device__ void mix_mfma(float* v, int n, int m, int log2p, const float* qs) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kMaxTiles = (KQ_MAX_ODD + 15) / 16;
   const int p = 1 << log2p;
-  const int cols = T * p, groups = (m + 15) >> 4;
-  const int cpr = NT / groups;                 // whole columns per round
-  const int gi = threadIdx.x / cpr;            // this thread's output group
-  const int cr = threadIdx.x - gi * cpr;       // and column within the round
-  for (int c0 = 0; c0 < cols; c0 += cpr) {
-    const int c = c0 + cr;
-    const bool act = gi < groups && c < cols;
-    float* row = v + (c >> log2p) * n + (c & (p - 1));
-    float acc[16];
-    if (act) mix16(row, p, m, qs, 16 * gi, acc);
-    __syncthreads();
-    if (act) {
+  const int cols = T * p;
+  const int mt = (m + 15) >> 4, kt = (m + 3) >> 2;
+  const int nt = (cols + 15) >> 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lk = lane >> 4;
+  for (int r0 = 0; r0 < nt; r0 += kWaves) {
+    const int ni = r0 + wave;
+    const int c = 16 * ni + li;                 // this lane's column (B operand and output)
+    const bool cv = ni < nt && c < cols;
+    float* col = v + (c >> log2p) * n + (c & (p - 1));
+    floatx4 acc[kMaxTiles];
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (16 * gi + k < m) row[(16 * gi + k) * p] = acc[k];
+    for (int mi = 0; mi < kMaxTiles; ++mi) acc[mi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (ni < nt) {
+      for (int kk = 0; kk < kt; ++kk) {
+        const int a2 = 4 * kk + lk;             // input chunk of this lane's B entry
+        const float b = (cv && a2 < m) ? col[a2 * p] : 0.0f;
+#pragma unroll
+        for (int mi = 0; mi < kMaxTiles; ++mi) {
+          if (mi < mt) {
+            const float a = qs[a2 * kQPitch + 16 * mi + li];  // W[16 mi + li][a2]
+            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[mi], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (cv) {
+      // lane holds column li, rows 4 lk + j of each 16-row tile
+#pragma unroll
+      for (int mi = 0; mi < kMaxTiles; ++mi) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int a = 16 * mi + 4 * lk + j;
+          if (mi < mt && a < m) col[a * p] = acc[mi][j];
+        }
+      }
     }
     __syncthreads();
   }
@@ -167,6 +177,9 @@ __device__ void mix_lds(float* v, int n, int m, int log2p, const float* qs) {
 // loads never sit under a condition.
 __device__ double kUnitScale = 1.0;
 __device__ int8_t kPlusSign = 1;
+__device__ __align__(16) double kUnitScales[16] = {1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0,
+                                                   1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0};
+__device__ __align__(16) int8_t kPlusSigns[16] = {1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1};
 
 // One side of the rotation applied in LDS by the NT threads of a workgroup, for T tokens of n
 // entries:
@@ -184,7 +197,7 @@ __device__ int8_t kPlusSign = 1;
 // before the next one, which would serialize the round trips.
 template <int T, int NT, int P, bool OUT>
 struct SideStage {
-  static constexpr int kQPer = (KQ_MAX_ODD * kQPitch + NT - 1) / NT;
+  static constexpr int kQPer = (kQFloats + NT - 1) / NT;
   const float* src;
   int n, nl, m;
   bool on, mixed;
@@ -277,35 +290,224 @@ struct SideStage {
       }
     }
     if (mixed) {
+      // rows a' < 4 ceil(m / 4) (the product's K extent), zero outside the m x m factor
+      const int rows = (m + 3) & ~3;
 #pragma unroll
       for (int k = 0; k < kQPer; ++k) {
         const int e = k * NT + tid;
-        if (e < m * kQPitch) qs[e] = (e & (kQPitch - 1)) < m ? static_cast<float>(qv[k]) * post : 0.0f;
+        const int a2 = e >> 6, a = e & (kQPitch - 1);
+        if (a2 < rows) qs[e] = (a < m && a2 < m) ? static_cast<float>(qv[k]) * post : 0.0f;
       }
     }
     __syncthreads();
     if (on) {
       fwht_lds<T, NT>(lds, n, log2p);
-      if (mixed) mix_lds<T, NT>(lds, n, m, log2p, qs);
+      if (mixed) mix_mfma<T, NT>(lds, n, m, log2p, qs);
+    }
+  }
+};
+
+// The same side with 16 consecutive entries per thread (a group), for n % 16 == 0 and 16-byte
+// aligned values, signs and scales: a group's values, signs and scales arrive as 16-byte loads
+// (a quarter of the instructions of one entry per load), and the first four butterfly stages
+// (index bits 0..3, inside every chunk since 16 divides p) run in registers before the group
+// goes to LDS, so the LDS passes start at bit 4. Group g = tid is requested by issue(); on
+// return from transform() the output side's factors of that group are in fo[].
+template <int T, int NT, bool OUT>
+struct SideStageV {
+  static constexpr int kQPer = (kQFloats + NT - 1) / NT;
+  const float* src;
+  int n, ng, m, log2p;
+  bool on, mixed;
+  const int8_t* sgp;
+  int sgi;
+  const double* svp;
+  int svi;
+  const double* qp;
+  float post, tail;
+  float val[T][16];
+  uint4 sgw;
+  double sv[16];
+  double qv[kQPer];
+  float fo[16];
+
+  __device__ __forceinline__ void load_group(int g) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float4* p = reinterpret_cast<const float4*>(src + t * n + 16 * g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 f = p[c];
+        val[t][4 * c] = f.x;
+        val[t][4 * c + 1] = f.y;
+        val[t][4 * c + 2] = f.z;
+        val[t][4 * c + 3] = f.w;
+      }
+    }
+    sgw = *reinterpret_cast<const uint4*>(sgp + 16 * g * sgi);
+    const double2* sp = reinterpret_cast<const double2*>(svp + 16 * g * svi);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const double2 d = sp[c];
+      sv[2 * c] = d.x;
+      sv[2 * c + 1] = d.y;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const float* src_, int n_, const Side& sd) {
+    const int tid = threadIdx.x;
+    src = src_;
+    n = n_;
+    ng = n >> 4;
+    m = sd.m;
+    on = sd.on != 0;
+    mixed = on && m > 1;
+    log2p = sd.log2p;
+    sgp = on ? sd.signs : kPlusSigns;
+    sgi = on ? 1 : 0;
+    svp = sd.s ? sd.s : kUnitScales;
+    svi = sd.s ? 1 : 0;
+    qp = sd.q ? sd.q : &kUnitScale;
+    post = on ? 1.0f / sqrtf(static_cast<float>(1 << log2p)) : 1.0f;
+    tail = (on && !mixed) ? post : 1.0f;
+    load_group(min(tid, ng - 1));
+    const int ml = m - 1;
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int e = k * NT + tid;
+      const int a2 = min(e >> 6, ml), a = min(e & (kQPitch - 1), ml);
+      qv[k] = OUT ? qp[a2 * m + a] : qp[a * m + a2];
+    }
+  }
+
+  // Signs and scales of the loaded group: applied to the values (input side) or kept as the
+  // output factors (output side, first group only); then the group's four in-register
+  // butterfly stages.
+  template <bool KEEP>
+  __device__ __forceinline__ void process_group() {
+    const uint32_t w[4] = {sgw.x, sgw.y, sgw.z, sgw.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sgn = ((w[j >> 2] >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
+      if (OUT) {
+        if (KEEP) fo[j] = sgn * tail / static_cast<float>(sv[j]);
+      } else {
+        const float f = sgn / static_cast<float>(sv[j]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) val[t][j] *= f;
+      }
+    }
+    if (on) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if ((j & h) == 0) {
+              const float x = val[t][j], y = val[t][j + h];
+              val[t][j] = x + y;
+              val[t][j + h] = x - y;
+            }
+    }
+  }
+
+  __device__ __forceinline__ void store_group(float* lds, int g) const {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float4* p = reinterpret_cast<float4*>(lds + t * n + 16 * g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        p[c] = make_float4(val[t][4 * c], val[t][4 * c + 1], val[t][4 * c + 2], val[t][4 * c + 3]);
+    }
+  }
+
+  __device__ __forceinline__ void transform(float* lds, float* qs) {
+    const int tid = threadIdx.x;
+    process_group<true>();
+    if (tid < ng) store_group(lds, tid);
+    // groups past the first NT, one at a time
+    for (int g = tid + NT; g < ng; g += NT) {
+      load_group(g);
+      process_group<false>();
+      store_group(lds, g);
+    }
+    if (mixed) {
+      const int rows = (m + 3) & ~3;
+#pragma unroll
+      for (int k = 0; k < kQPer; ++k) {
+        const int e = k * NT + tid;
+        const int a2 = e >> 6, a = e & (kQPitch - 1);
+        if (a2 < rows) qs[e] = (a < m && a2 < m) ? static_cast<float>(qv[k]) * post : 0.0f;
+      }
+    }
+    __syncthreads();
+    if (on) {
+      fwht_lds<T, NT>(lds, n, log2p, 4);
+      if (mixed) mix_mfma<T, NT>(lds, n, m, log2p, qs);
+    }
+  }
+
+  // Output factor of group g past the first NT (its signs and scales read again).
+  __device__ __forceinline__ void out_factors(int g, float f[16]) const {
+    const uint4 u = *reinterpret_cast<const uint4*>(sgp + 16 * g * sgi);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const double2* sp = reinterpret_cast<const double2*>(svp + 16 * g * svi);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const double2 d = sp[c];
+      f[2 * c] = static_cast<float>(d.x);
+      f[2 * c + 1] = static_cast<float>(d.y);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sgn = ((w[j >> 2] >> (8 * (j & 3) + 7)) & 1u) ? -1.0f : 1.0f;
+      f[j] = OUT ? sgn * tail / f[j] : tail;
     }
   }
 };
 
 // Floats of LDS a side transform of T x n entries uses: the entries, then Q at a 16-byte boundary.
 __host__ __device__ constexpr int side_lds_floats(int n, int tokens) {
-  return ((tokens * n + 3) & ~3) + KQ_MAX_ODD * kQPitch;
+  return ((tokens * n + 3) & ~3) + kQFloats;
 }
 
 // One side for T tokens of n entries in one 1024-thread workgroup: dst = S^-1 U^T src (output
-// side) or U S^-1 src (input side, when it is not fused into the matvec).
-template <int T, bool OUT>
+// side) or U S^-1 src (input side, when it is not fused into the matvec). VEC: the grouped form
+// (n % 16 == 0, every operand 16-byte aligned).
+template <int T, bool OUT, bool VEC>
 __global__ __launch_bounds__(kSideThreads) void side_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                            int n, Side sd) {
   extern __shared__ float lds[];
+  if constexpr (VEC) {
+    SideStageV<T, kSideThreads, OUT> st;
+    st.issue(src, n, sd);
+    st.transform(lds, lds + side_lds_floats(n, T) - kQFloats);
+    for (int g = threadIdx.x; g < st.ng; g += kSideThreads) {
+      float f[16];
+      if (g == static_cast<int>(threadIdx.x)) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) f[j] = OUT ? st.fo[j] : st.tail;
+      } else {
+        st.out_factors(g, f);
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4* lp = reinterpret_cast<const float4*>(lds + t * n + 16 * g);
+        float4* dp = reinterpret_cast<float4*>(dst + t * n + 16 * g);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4 v = lp[c];
+          dp[c] = make_float4(v.x * f[4 * c], v.y * f[4 * c + 1], v.z * f[4 * c + 2], v.w * f[4 * c + 3]);
+        }
+      }
+    }
+    return;
+  }
   constexpr int P = 16 / T;
   SideStage<T, kSideThreads, P, OUT> st;
   st.issue(src, n, sd);
-  st.transform(lds, lds + side_lds_floats(n, T) - KQ_MAX_ODD * kQPitch);
+  st.transform(lds, lds + side_lds_floats(n, T) - kQFloats);
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
@@ -396,10 +598,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
   // repeats. Otherwise straight from x1, 16-byte aligned.
   float xv[NW][PER][T];
   if constexpr (IN) {
-    SideStage<T, kThreads, 16 / T, false> st;
+    SideStageV<T, kThreads, false> st;
     st.issue(g.x, din32, g.in);
     load_rows(0);
-    st.transform(lds, lds + side_lds_floats(din32, T) - KQ_MAX_ODD * kQPitch);
+    st.transform(lds, lds + side_lds_floats(din32, T) - kQFloats);
 #pragma unroll
     for (int i = 0; i < NW; ++i)
 #pragma unroll
@@ -497,15 +699,32 @@ bool allow_lds(const void* fn, size_t bytes) {
          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes)) == hipSuccess;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// The grouped side form applies: whole groups of 16 and every operand 16-byte aligned.
+bool side_vec_ok(const float* src, const float* dst, int64_t n, const Side& sd) {
+  return n % 16 == 0 && aligned16(src) && (dst == nullptr || aligned16(dst)) && (!sd.on || aligned16(sd.signs)) &&
+         (sd.s == nullptr || aligned16(sd.s));
+}
+
 template <int T, bool OUT>
 kq_status launch_side(const float* src, float* dst, int n, const Side& sd, hipStream_t st) {
   const size_t lds = side_lds_bytes(n, T);
   const char* name = OUT ? "decode_out_kernel" : "decode_in_kernel";
-  if (!allow_lds(reinterpret_cast<const void*>(&side_kernel<T, OUT>), lds))
-    return fail(KQ_EDEVICE, "%s: %zu bytes of LDS refused", name, lds);
+  // (the grouped output side holds 16 T values, 16 factors and 16 scales per thread: up to
+  // two tokens within the 1024-thread register budget)
+  constexpr bool kVecForm = !OUT || T <= 2;
+  const bool vec = kVecForm && side_vec_ok(src, dst, n, sd);
+  constexpr auto vec_kernel = side_kernel<T, OUT, kVecForm>;  // the scalar form when not allowed
+  const void* fn = vec ? reinterpret_cast<const void*>(vec_kernel)
+                       : reinterpret_cast<const void*>(&side_kernel<T, OUT, false>);
+  if (!allow_lds(fn, lds)) return fail(KQ_EDEVICE, "%s: %zu bytes of LDS refused", name, lds);
   {
     LaunchTimer timer(name, st);
-    hipLaunchKernelGGL((side_kernel<T, OUT>), dim3(1), dim3(kSideThreads), lds, st, src, dst, n, sd);
+    if (vec)
+      hipLaunchKernelGGL(vec_kernel, dim3(1), dim3(kSideThreads), lds, st, src, dst, n, sd);
+    else
+      hipLaunchKernelGGL((side_kernel<T, OUT, false>), dim3(1), dim3(kSideThreads), lds, st, src, dst, n, sd);
   }
   return check_launch(name);
 }
@@ -617,13 +836,15 @@ kq_status decode_run(const uint32_t* packed, const float* scales, const uint8_t*
   a.y1 = rot_out ? static_cast<float*>(ws) : nullptr;
   a.s_g = s_g;
   float* x1 = reinterpret_cast<float*>(static_cast<char*>(ws) + y1_bytes(dout, tokens));
-  // The input side runs inside the matvec when it is a plain transform (no odd factor) and the
-  // grid is at most one workgroup per CU (each workgroup repeats it: more would queue the
-  // copies behind each other); otherwise as its own one-workgroup launch. The direct path reads
-  // x as float4s, so an unaligned x with no input side goes through that launch too.
-  const bool need_in = rot_in || s_x || (reinterpret_cast<uintptr_t>(x) & 15) != 0;
+  // The input side runs inside the matvec (in the grouped form) when it is a plain transform (no
+  // odd factor), the grid is at most one workgroup per CU (each workgroup repeats it: more would
+  // queue the copies behind each other) and its operands are 16-byte aligned; otherwise as its
+  // own one-workgroup launch. The direct path reads x as float4s, so an unaligned x with no input
+  // side goes through that launch too.
+  const bool need_in = rot_in || s_x || !aligned16(x);
   const int64_t grid = (dout + kRowsPerWg - 1) / kRowsPerWg;
-  const int in_mode = !need_in ? 0 : (a.in.m == 1 && grid <= kCus ? 1 : 2);
+  const bool fuse = a.in.m == 1 && grid <= kCus && side_vec_ok(x, nullptr, din, a.in);
+  const int in_mode = !need_in ? 0 : (fuse ? 1 : 2);
   const Side out = make_side(rot_out, s_g);
   const int t = static_cast<int>(tokens);
   const int cpl = decode_cpl(din, tokens);

@@ -55,11 +55,14 @@ def _decode(kq, pipeline, codes, scales, zeros, bits, group, s_x, s_g, ri, ro, x
 # rows, per-row grids, 1..4 tokens, an odd output width with no power-of-two part (63 = 63 x 1,
 # three tokens: 189 floats before the staged odd factor), the LLaMA-2-7B q_proj layer at full
 # size. The input side runs fused into the matvec (m = 1 on the input, at most 256 workgroups)
-# or as its own launch (an odd factor on the input, or 4224 rows = 264 workgroups).
+# or as its own launch (an odd factor on the input, or 4224 rows = 264 workgroups). A side of
+# whole groups of 16 with aligned operands takes the grouped form (16-byte loads, the first four
+# butterfly stages in registers); 200 and 63 wide sides and three or four tokens on the output
+# side take the one-entry-per-load form.
 DECODE_CASES = [
     (256, 512, 2, 128, 1), (4096, 4096, 2, 128, 1), (96, 320, 4, 64, 2), (200, 448, 3, 0, 3),
     (448, 1024, 2, 128, 4), (160, 2048, 8, 32, 1), (384, 3584, 2, 128, 1), (2816, 1024, 4, 128, 2),
-    (63, 512, 2, 128, 3), (4224, 256, 2, 64, 2),
+    (63, 512, 2, 128, 3), (4224, 256, 2, 64, 2), (200, 448, 2, 64, 1),
 ]
 
 

@@ -10,26 +10,27 @@
 // Packing: code j of a row sits in word j / (32 / c) at bits c (j mod 32 / c),
 // with c = 2 for 2-bit codes, 4 for 3- and 4-bit codes, 8 above.
 //
-// Per layer and token batch (T <= 4 tokens), three launches on one stream:
-//   1. input side, one 1024-thread workgroup: x1 = U_X S_X^-1 x (signs and
-//      scales on load, fast Walsh-Hadamard transform per 2^k chunk in radix-16
-//      register passes, odd-factor mix across the m chunks) into the workspace;
+// Per layer and token batch (T <= 4 tokens), up to three launches on one stream:
+//   1. input side, x1 = U_X S_X^-1 x (signs and scales on load, fast Walsh-Hadamard
+//      transform per 2^k chunk in radix-16 register passes, odd-factor mix across the m
+//      chunks on float32 MFMA): applied in LDS by every workgroup of the matvec while its
+//      first rows are in flight when it has no odd factor and the grid is at most one
+//      workgroup per CU, else as a one-workgroup (1024-thread) launch into the workspace;
 //      skipped when there is neither a rotation nor a scale on that side;
-//   2. the matvec, 16 rows per 256-thread workgroup: every lane loads the x1
-//      entries of its words straight into registers, then the four waves split
-//      each row's packed words (lane l of wave w reads word 64 w + l + 256 i),
-//      dequantize on the fly, y1[row] = sum_g s_g (sum_j q_j x1_j - z_g sum_j x1_j),
-//      one 32-bit load per word and row, the loads of up to 16 rows in flight;
-//   3. output side, one 1024-thread workgroup: transform per chunk, transposed
-//      odd mix, signs, 1 / s_g (only with an output rotation; a scale alone is
-//      applied by the matvec).
-// The side transforms run once per call rather than once per matvec workgroup,
-// and each issues every global load of its first batch before its first wait:
-// the data are small and the cost is round trips, not bytes. (A fused
-// last-workgroup output side needed a device-scope fence in every workgroup,
-// which cost more than the launch.)
-// Everything is float32; the float64 diagonal scales and rotation factors are
-// rounded to float32 on load.
+//   2. the matvec, 16 rows per 256-thread workgroup: every lane holds the x1 entries of
+//      its words in registers, the four waves split each row's packed words (lane l of
+//      wave w reads word 64 w + l + 256 i), dequantize on the fly,
+//      y1[row] = sum_g s_g (sum_j q_j x1_j - z_g sum_j x1_j), one 32-bit load per word
+//      and row, the loads of up to 16 rows in flight;
+//   3. output side, one 1024-thread workgroup: transform per chunk, transposed odd mix,
+//      signs, 1 / s_g (only with an output rotation; a scale alone is applied by the
+//      matvec).
+// A side transform's data are small and its cost is round trips, not bytes: every global
+// load of its first batch is issued before its first wait, and sides of whole groups of 16
+// with aligned operands use 16-byte loads. (A fused last-workgroup output side needed a
+// device-scope fence in every workgroup, which cost more than the launch.)
+// Everything is float32; the float64 diagonal scales and rotation factors are rounded to
+// float32 on load.
 #include "kq_internal.h"
 
 namespace kq {

@@ -366,21 +366,23 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
   // two register sets: the chunk two ahead loads while one is multiplied and one waits
   double2 va[2][DA / 2];
   float vb[2][NR];
+  // The loads are unconditional (ap and bp are clamped into the tile) and the out-of-range
+  // operands are zeroed when stored to LDS: a load under a per-lane condition compiles to a
+  // branch, and the wait for a prefetched chunk then also waits for every later load.
   auto load = [&](int set, int kc) {
 #pragma unroll
-    for (int q = 0; q < DA / 2; ++q)
-      va[set][q] = a_ok ? *reinterpret_cast<const double2*>(ap + kc + 2 * q) : double2{0.0, 0.0};
+    for (int q = 0; q < DA / 2; ++q) va[set][q] = *reinterpret_cast<const double2*>(ap + kc + 2 * q);
 #pragma unroll
-    for (int q = 0; q < NR; ++q) vb[set][q] = b_ok ? bp[int64_t(kc + q * BKS) * din] : 0.0f;
+    for (int q = 0; q < NR; ++q) vb[set][q] = bp[int64_t(kc + q * BKS) * din];
   };
   auto store = [&](int set, int buf) {
 #pragma unroll
     for (int q = 0; q < DA / 2; ++q) {
-      sm.as[buf][ak + 2 * q][ar] = -va[set][q].x;
-      sm.as[buf][ak + 2 * q + 1][ar] = -va[set][q].y;
+      sm.as[buf][ak + 2 * q][ar] = a_ok ? -va[set][q].x : 0.0;
+      sm.as[buf][ak + 2 * q + 1][ar] = a_ok ? -va[set][q].y : 0.0;
     }
 #pragma unroll
-    for (int q = 0; q < NR; ++q) sm.bs[buf][bk0 + q * BKS][bc] = vb[set][q];
+    for (int q = 0; q < NR; ++q) sm.bs[buf][bk0 + q * BKS][bc] = b_ok ? vb[set][q] : 0.0f;
   };
   // D[i][j] of a 16 x 16 float64 block: lane l, register q -> i = 4 q + l / 16, j = l % 16
   // (measured on gfx950; the operands are A[i][k] at lane i + 16 k and B[k][j] at lane j + 16 k)

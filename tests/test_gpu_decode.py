@@ -82,6 +82,24 @@ def test_decode_matvec(dout, din, bits, group, tokens):
     assert rel_fro(got, want) <= 2e-5
 
 
+@pytest.mark.parametrize("dout,din", [(11008, 4096), (4096, 11008)])
+def test_decode_matvec_llama2_7b_mlp_full_size(dout, din):
+    """The gate/up and down layers of the decode bench at full size, in the launch configuration
+    the bench times: gate/up run the input side as its own launch (688 workgroups) and the output
+    side with the odd factor 43; down runs the input side with the odd factor and 256 workgroups."""
+    kq, pipeline = _kq()
+    print(f"decode full size {dout}x{din}", flush=True)
+    rng = np.random.default_rng(dout + 3 * din)
+    codes, scales, zeros = _layer(rng, dout, din, 2, 128)
+    s_x, s_g = rng.uniform(0.3, 3.0, din), rng.uniform(0.3, 3.0, dout)
+    ri, ro = kq_synth.rot_spec(77, f"dec{din}", din), kq_synth.rot_spec(77, f"dec{dout}", dout)
+    assert {ri.m, ro.m} == {1, 43}
+    x = rng.standard_normal((1, din))
+    want = oracle.decode_matvec(codes, scales, zeros, 128, s_x, s_g, ri, ro, x.astype(np.float32))
+    got = _decode(kq, pipeline, codes, scales, zeros, 2, 128, s_x, s_g, ri, ro, x)
+    assert rel_fro(got, want) <= 2e-5
+
+
 @pytest.mark.parametrize("inp,out", [(False, False), (True, False), (False, True)])
 def test_decode_matvec_sides(inp, out):
     kq, pipeline = _kq()

@@ -154,7 +154,7 @@ def test_fullsize_down_proj_covariance_slice_groups():
     """28672 channels (6328 tiles): four token slices, summed over two launches through the float64 workspace."""
     import torch
     kq, pipeline = _kq()
-    n_tok = 3 * 8192 + 100
+    n_tok = 3 * 16384 + 100  # four slices of 16384 tokens, the last one ragged
     cfg = kq_synth.scaled(kq_synth.config(4), n_tokens=n_tok, dims={})
     wl = kq_synth.Workload(cfg)
     x = wl.x("down_in")

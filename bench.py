@@ -36,6 +36,8 @@ import sys
 import time
 
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3   # MI355X float32 (vector and matrix)
+FP64_PEAK_TFLOPS = 78.6    # MI355X float64 MFMA
 
 
 def parse_args():
@@ -577,6 +579,30 @@ def main() -> int:
                      "second stream next to the Cholesky factor" if not args.serial else "one stream"),
         },
         "cpu_baseline": None,
+    }
+    # every step's fraction of its own roof (the dominant kernel's is `roofline` above)
+    biip_bytes = dout * din * (2 + 8) + 8 * din * din + 8 * dout * dout  # W bf16 in, float64 out; H in place
+    obs_flops = dout * din * (din - cfg.block)  # lazy-batch trailing products over all blocks
+    chol_flops = 2 * din ** 3 / 3              # factor and triangular inverse
+    def step_roof(bound, amount, ms, peak, unit, scale, note):
+        ach = amount / (ms / 1e3) / scale if ms > 0 else 0.0
+        return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "ms": round(ms, 4), "note": note}
+    result["step_rooflines"] = {
+        "biip": step_roof("hbm", biip_bytes, stage_ms["biip"], HBM_PEAK_GBS, "GB/s", 1e9,
+                          f"{biip_bytes} algorithmic bytes (W bf16 read, float64 W'' write, H_X and H_G float32 "
+                          f"read and write); the input side runs next to the H_G covariance"),
+        "obs_trailing": step_roof("mfma", obs_flops, stage_ms["obs"], FP64_PEAK_TFLOPS, "TFLOP/s", 1e12,
+                                  f"dout din (din - B) = {obs_flops} flop of float64 trailing products over the "
+                                  f"whole sweep time (the in-block sweep included)"),
+        **({} if args.serial else {"biip_output_side": step_roof(
+            "hbm", dout * din * 16 + 8 * dout * dout, span(10, 11), HBM_PEAK_GBS, "GB/s", 1e9,
+            "output side alone, with the GPU to itself: float64 W read and write, H_G float32 read and write "
+            "(three passes over each matrix, so about three times these bytes move)")}),
+        "cholesky": step_roof("mfma", chol_flops, stage_ms["cholesky"], FP32_PEAK_TFLOPS, "TFLOP/s", 1e12,
+                              "2 d^3 / 3 flop (factor and inverse) against the float32 roof; runs on the 80 CUs "
+                              "left to it next to the H_G covariance" if not args.serial else
+                              "2 d^3 / 3 flop (factor and inverse) against the float32 roof"),
     }
     result["schedule"] = ("one stream" if args.serial else
                           f"two streams: H_X covariance, BiIP input side, Cholesky factor, BiIP output side and "

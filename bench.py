@@ -57,6 +57,8 @@ def parse_args():
                    help="after timing, copy 1 GiB device-to-device (a reference kernel for HBM byte counters)")
     p.add_argument("--decode", action="store_true",
                    help="instead of the quantization step: the packed-code decode matvec (one JSON line)")
+    p.add_argument("--decode-per-layer", action="store_true",
+                   help="with --decode: one kq_decode_matvec call per layer instead of one group call per shared input")
     p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                    help="no run: turn two rocprofv3 --pmc runs of '--copy-calibration' (FETCH_SIZE, then "
                         "WRITE_SIZE) into the per-launch HBM bytes of the roofline kernel")
@@ -230,6 +232,8 @@ def stored_traffic():
 # LLaMA-2-7B linear layers of one decoder block: (name, dout, din)
 DECODE_LAYERS = [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096), ("o_proj", 4096, 4096),
                  ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008)]
+# layers of a block that read the same input (and so share the input side): (din, [layer indices])
+DECODE_GROUPS = [(4096, [0, 1, 2]), (4096, [3]), (4096, [4, 5]), (11008, [6])]
 DECODE_BLOCKS = 32
 HBM_PEAK_GBS = 8000.0
 
@@ -240,8 +244,10 @@ def decode_bench(args) -> int:
     Synthetic packed codes (uniform random 2-bit fields), group-128 scales and zero points, random
     diagonal scales and seeded rotation specs, for the 224 linear layers of LLaMA-2-7B (32 blocks x
     q, k, v, o, gate, up, down). One step = one token through all 224 layers (the linear layers only:
-    no attention, norms or activations). The roofline covers the matvec kernel inside the stack: the
-    average weight bytes (packed codes + scales + zero points) per launch over its average duration."""
+    no attention, norms or activations); layers that read the same input (q/k/v, gate/up) go through
+    one group call, which shares the input side. The roofline covers the matvec kernel inside the
+    stack: the average weight bytes (packed codes + scales + zero points) per launch over its average
+    duration."""
     import numpy as np
     import torch
 
@@ -256,29 +262,46 @@ def decode_bench(args) -> int:
     gen.manual_seed(2026)
     rots = {n: pipeline.upload_rot(*(lambda sp: (sp.signs, sp.q))(kq_synth.rot_spec(77, f"dec{n}", n)), dev)
             for n in sorted({d for _, o, i in DECODE_LAYERS for d in (o, i)})}
-    layers = []
+    # per block and input group: one s_x (the input side's scale comes from the shared H_X), and per
+    # layer its packed codes, scales, zero points, s_g and output buffer
+    groups = []
     for blk in range(DECODE_BLOCKS):
-        for name, dout, din in DECODE_LAYERS:
-            packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (dout, din * 2 // 32), dtype=torch.int32, device=dev,
-                                   generator=gen)
-            scales = torch.rand((dout, din // group), device=dev, generator=gen) * 0.04 + 0.005
-            zeros = torch.randint(0, 4, (dout, din // group), dtype=torch.uint8, device=dev, generator=gen)
+        for din, members in DECODE_GROUPS:
             s_x = torch.rand(din, dtype=torch.float64, device=dev, generator=gen) + 0.5
-            s_g = torch.rand(dout, dtype=torch.float64, device=dev, generator=gen) + 0.5
-            layers.append((name, dout, din, packed, scales, zeros, s_x, s_g))
+            mem = []
+            for li in members:
+                name, dout, _ = DECODE_LAYERS[li]
+                packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (dout, din * 2 // 32), dtype=torch.int32,
+                                       device=dev, generator=gen)
+                scales = torch.rand((dout, din // group), device=dev, generator=gen) * 0.04 + 0.005
+                zeros = torch.randint(0, 4, (dout, din // group), dtype=torch.uint8, device=dev, generator=gen)
+                s_g = torch.rand(dout, dtype=torch.float64, device=dev, generator=gen) + 0.5
+                y = torch.empty((1, dout), device=dev)
+                mem.append((packed, scales, zeros, s_g, rots[dout].rot, y))
+            groups.append((din, s_x, mem))
     xs = {n: torch.randn((1, n), device=dev, generator=gen) for n in (4096, 11008)}
-    ys = {n: torch.empty((1, n), device=dev) for n in (4096, 11008)}
-    wss = {(o, i): kq.decode_workspace(o, i, 1, dev) for _, o, i in DECODE_LAYERS}
-    weight_bytes = sum(p.numel() * 4 + sc.numel() * 4 + z.numel() for _, _, _, p, sc, z, _, _ in layers)
+    wss = {}
+    for din, _, mem in groups:
+        key = (din, tuple(m[5].shape[1] for m in mem))
+        if key not in wss:
+            wss[key] = kq.decode_workspace(sum(key[1]), din, 1, dev)
+    n_layers = sum(len(m) for _, _, m in groups)
+    weight_bytes = sum(p.numel() * 4 + sc.numel() * 4 + z.numel() for _, _, mem in groups
+                       for p, sc, z, _, _, _ in mem)
 
-    def layer_call(L):
-        name, dout, din, packed, scales, zeros, s_x, s_g = L
-        kq.decode_matvec(packed, scales, zeros, bits, group, s_x, s_g, rots[din].rot, rots[dout].rot, xs[din],
-                         ys[dout], ws=wss[(dout, din)])
+    def group_call(G):
+        din, s_x, mem = G
+        ws = wss[(din, tuple(m[5].shape[1] for m in mem))]
+        if args.decode_per_layer:
+            for packed, scales, zeros, s_g, rot_out, y in mem:
+                kq.decode_matvec(packed, scales, zeros, bits, group, s_x, s_g, rots[din].rot, rot_out, xs[din], y,
+                                 ws=ws)
+        else:
+            kq.decode_matvec_group(mem, bits, group, s_x, rots[din].rot, xs[din], ws=ws)
 
     def token():
-        for L in layers:
-            layer_call(L)
+        for G in groups:
+            group_call(G)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup + 1):
@@ -291,7 +314,7 @@ def decode_bench(args) -> int:
         token()
     n_q, ms_q = kq.timing_query("decode_kernel")
     kq.timing_enable(None)
-    q_bytes = weight_bytes / len(layers)  # average algorithmic bytes per launch
+    q_bytes = weight_bytes * 3 / n_q  # average algorithmic bytes per matvec launch
     q_us = ms_q / n_q * 1e3
     # whole token, eager launches
     steps = max(args.steps, 5) * 4
@@ -304,7 +327,8 @@ def decode_bench(args) -> int:
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / steps
     # whole token captured once as a HIP graph and replayed
-    ref = ys[4096].clone()
+    outs = [m[5] for _, _, mem in groups for m in mem]
+    ref = [y.clone() for y in outs]
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream(device=dev)
     cap.wait_stream(torch.cuda.current_stream())
@@ -316,7 +340,7 @@ def decode_bench(args) -> int:
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
-    replay_ok = bool(torch.equal(ys[4096], ref))
+    replay_ok = all(bool(torch.equal(y, r)) for y, r in zip(outs, ref))
     torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
@@ -333,7 +357,9 @@ def decode_bench(args) -> int:
         "dtype": "u2/f32", "data": "synthetic",
         "config": {"workload": "LLaMA-2-7B linear layers (32 x q, k, v, o 4096x4096; gate, up 11008x4096; "
                                "down 4096x11008), W2 group 128, batch 1, BiIP both sides",
-                   "weight_bytes_per_token": weight_bytes},
+                   "weight_bytes_per_token": weight_bytes,
+                   "calls": ("one kq_decode_matvec per layer" if args.decode_per_layer else
+                             "one kq_decode_matvec_group per shared input: q/k/v, o, gate/up, down")},
         "ms_per_token_eager": round(ms_eager, 4), "ms_per_token_graph": round(ms_graph, 4),
         "graph_replay_matches_eager": replay_ok,
         "stack_gbs": round(weight_bytes / (ms_tok * 1e-3) / 1e9, 1),
@@ -341,7 +367,7 @@ def decode_bench(args) -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes": round(q_bytes), "avg_launch_us": round(q_us, 3),
                      "launches": n_q,
-                     "note": "matvec launches of whole tokens (weights cold), averaged over the 224 layers: "
+                     "note": "matvec launches of whole tokens (weights cold), averaged over the launches: "
                              "algorithmic bytes = packed codes + float32 scales + uint8 zero points"},
     }
     log(f"decode: {ms_eager:.3f} ms/token eager, {ms_graph:.3f} ms/token graph; matvec launch {q_us:.2f} us "

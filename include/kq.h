@@ -64,6 +64,7 @@ enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS =
 #define KQ_MAX_ODD 63         /* largest odd factor m of a rotated dimension */
 #define KQ_MAX_ROT_DIM 32768  /* largest rotated dimension n = m * 2^k */
 #define KQ_DECODE_MAX_TOKENS 4  /* tokens per kq_decode_matvec call */
+#define KQ_DECODE_MAX_LAYERS 4  /* layers per kq_decode_matvec_group call */
 
 /*
  * Rotation of one side: U = (Q_m kron H_p / sqrt(p)) diag(sigma), n = m * p,
@@ -106,7 +107,7 @@ kq_status kq_timing_query(const char* name, int64_t* launches, double* total_ms)
  *   KQ_OP_BIIP:           d0 = dout, d1 = din
  *   KQ_OP_CHOLESKY:       d0 = d
  *   KQ_OP_OBS:            d0 = dout, d1 = din, d2 = block
- *   KQ_OP_DECODE:         d0 = dout, d1 = din, d2 = tokens
+ *   KQ_OP_DECODE:         d0 = dout (kq_decode_matvec_group: the layers' total), d1 = din, d2 = tokens
  * Returns (size_t)-1 for invalid sizes.
  */
 size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
@@ -296,6 +297,35 @@ kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const ui
                            const double* s_x, const double* s_g, const kq_rot* rot_in,
                            const kq_rot* rot_out, const float* x, int64_t tokens, float* y,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* One layer of kq_decode_matvec_group: the per-layer arguments of kq_decode_matvec. */
+typedef struct {
+  const uint32_t* packed;  /* device uint32 [dout, din * c / 32] */
+  const float* scales;     /* device float32 [dout, din / group] */
+  const uint8_t* zeros;    /* device uint8, same shape */
+  int64_t dout;
+  const double* s_g;       /* device float64 [dout] or NULL */
+  const kq_rot* rot_out;   /* HOST pointer or NULL */
+  float* y;                /* device float32 [tokens, dout], written */
+} kq_decode_layer;
+
+/*
+ * kq_decode_matvec_group -- kq_decode_matvec for up to KQ_DECODE_MAX_LAYERS
+ * layers that read the same input x with the same input side (a transformer
+ * block's q, k and v, or gate and up: the input side is keyed by the input,
+ * [KQ-art] 三). The input side is applied once, one matvec launch covers every
+ * layer's rows, and one launch applies the output sides, a workgroup per layer
+ * that has one. Each layer's result equals what kq_decode_matvec returns for it.
+ *   layers   HOST array of n_layers (1..KQ_DECODE_MAX_LAYERS) layer descriptions;
+ *            each is checked as kq_decode_matvec checks its arguments
+ *   din, bits, group, s_x, rot_in, x, tokens  shared, as in kq_decode_matvec
+ *   ws       kq_workspace_size(KQ_OP_DECODE, sum of the layers' dout, din, tokens)
+ *            bytes; calls sharing it must not overlap
+ */
+kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers, int64_t din,
+                                 int32_t bits, int32_t group, const double* s_x,
+                                 const kq_rot* rot_in, const float* x, int64_t tokens,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,9 +18,10 @@ __all__ = [
     "KQError", "KQ_OK", "KQ_EINVAL", "KQ_ENOTPD", "KQ_EINFEASIBLE", "KQ_EDEVICE", "KQ_EUNSUPPORTED",
     "KQ_BF16", "KQ_F32", "KQ_F64", "KQ_BIIP_INPUT", "KQ_BIIP_OUTPUT", "KQ_BIIP_SCALE", "KQ_BIIP_INVERSE",
     "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
-    "KQ_OP_DECODE", "KQ_DECODE_MAX_TOKENS",
+    "KQ_OP_DECODE", "KQ_DECODE_MAX_TOKENS", "KQ_DECODE_MAX_LAYERS",
     "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
-    "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_workspace", "Rot",
+    "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_matvec_group", "decode_workspace", "Rot",
+    "DecodeLayer",
     "timing_enable", "timing_query",
 ]
 
@@ -30,6 +31,7 @@ KQ_BIIP_INPUT, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_BIIP_INVERSE = 1, 2, 4, 8
 KQ_SCORE_KRONQ, KQ_SCORE_HX_ONLY = 0, 1
 KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS, KQ_OP_DECODE = 0, 1, 2, 3, 4
 KQ_DECODE_MAX_TOKENS = 4
+KQ_DECODE_MAX_LAYERS = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -49,6 +51,14 @@ class Rot(ctypes.Structure):
 
     _fields_ = [("n", ctypes.c_int64), ("m", ctypes.c_int32), ("log2p", ctypes.c_int32),
                 ("signs", ctypes.c_void_p), ("q", ctypes.c_void_p)]
+
+
+class DecodeLayer(ctypes.Structure):
+    """kq_decode_layer: one layer of a decode group (device pointers; rot_out a host pointer)."""
+
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("dout", ctypes.c_int64), ("s_g", ctypes.c_void_p), ("rot_out", ctypes.POINTER(Rot)),
+                ("y", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -86,8 +96,11 @@ def lib() -> ctypes.CDLL:
     L.kq_pack_codes.argtypes = [_VP, _I64, _I64, _I32, _VP, _VP]
     L.kq_decode_matvec.argtypes = [_VP, _VP, _VP, _I64, _I64, _I32, _I32, _VP, _VP, ctypes.POINTER(Rot),
                                    ctypes.POINTER(Rot), _VP, _I64, _VP, _VP, _SZ, _VP]
+    L.kq_decode_matvec_group.argtypes = [ctypes.POINTER(DecodeLayer), _I32, _I64, _I32, _I32, _VP,
+                                         ctypes.POINTER(Rot), _VP, _I64, _VP, _SZ, _VP]
     for name in ("kq_accumulate_cov", "kq_sensitivity", "kq_allocate_bits", "kq_biip_rotate",
-                 "kq_cholesky_inv", "kq_obs_quantize", "kq_pack_codes", "kq_decode_matvec"):
+                 "kq_cholesky_inv", "kq_obs_quantize", "kq_pack_codes", "kq_decode_matvec",
+                 "kq_decode_matvec_group"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -253,16 +266,12 @@ def decode_workspace(dout: int, din: int, tokens: int, device):
     return torch.empty(workspace_size(KQ_OP_DECODE, dout, din, tokens), dtype=torch.uint8, device=device)
 
 
-def decode_matvec(packed, scales, zeros, bits: int, group: int, s_x, s_g, rot_in: Optional[Rot],
-                  rot_out: Optional[Rot], x, y, *, ws=None, stream=None) -> None:
-    """y (float32 [tokens, dout]) <- S_G^-1 U_G^T W^'' U_X S_X^-1 x for x (float32 [tokens, din])."""
+def _check_decode_layer(packed, scales, zeros, bits: int, group: int, din: int, s_g, y, tokens: int) -> int:
+    """Shape and dtype checks of one layer's tensors; returns its dout."""
     import torch
     _need(packed.dtype == torch.int32 and scales.dtype == torch.float32 and zeros.dtype == torch.uint8
-          and x.dtype == torch.float32 and y.dtype == torch.float32 and x.is_contiguous() and y.is_contiguous(),
-          "decode_matvec: dtypes or layout")
-    _need(s_x is None or s_x.dtype == torch.float64, "decode_matvec: s_x must be float64")
+          and y.dtype == torch.float32 and y.is_contiguous(), "decode_matvec: dtypes or layout")
     _need(s_g is None or s_g.dtype == torch.float64, "decode_matvec: s_g must be float64")
-    tokens, din = x.shape
     dout = y.shape[1]
     c = 2 if bits == 2 else (4 if bits <= 4 else 8)
     ngroups = din // group if group else 1
@@ -272,11 +281,48 @@ def decode_matvec(packed, scales, zeros, bits: int, group: int, s_x, s_g, rot_in
           "decode_matvec: scales and zeros must be [dout, din / group]")
     _need(scales.is_contiguous() and zeros.is_contiguous() and packed.is_contiguous(),
           "decode_matvec: packed, scales and zeros must be contiguous")
-    _need(s_x is None or s_x.numel() == din, "decode_matvec: s_x must hold din entries")
     _need(s_g is None or s_g.numel() == dout, "decode_matvec: s_g must hold dout entries")
+    return dout
+
+
+def decode_matvec(packed, scales, zeros, bits: int, group: int, s_x, s_g, rot_in: Optional[Rot],
+                  rot_out: Optional[Rot], x, y, *, ws=None, stream=None) -> None:
+    """y (float32 [tokens, dout]) <- S_G^-1 U_G^T W^'' U_X S_X^-1 x for x (float32 [tokens, din])."""
+    import torch
+    _need(x.dtype == torch.float32 and x.is_contiguous(), "decode_matvec: x must be contiguous float32")
+    _need(s_x is None or s_x.dtype == torch.float64, "decode_matvec: s_x must be float64")
+    tokens, din = x.shape
+    dout = _check_decode_layer(packed, scales, zeros, bits, group, din, s_g, y, tokens)
+    _need(s_x is None or s_x.numel() == din, "decode_matvec: s_x must hold din entries")
     if ws is None:
         ws = decode_workspace(dout, din, tokens, x.device)
     _check(lib().kq_decode_matvec(_ptr(packed), _ptr(scales), _ptr(zeros), dout, din, bits, group, _ptr(s_x),
                                   _ptr(s_g), None if rot_in is None else ctypes.byref(rot_in),
                                   None if rot_out is None else ctypes.byref(rot_out), _ptr(x), tokens, _ptr(y),
                                   _ptr(ws), ws.numel(), _stream(stream)), "kq_decode_matvec")
+
+
+def decode_matvec_group(layers, bits: int, group: int, s_x, rot_in: Optional[Rot], x, *, ws=None,
+                        stream=None) -> None:
+    """decode_matvec for up to KQ_DECODE_MAX_LAYERS layers reading the same x with the same input
+    side. layers: sequence of (packed, scales, zeros, s_g, rot_out, y) per layer."""
+    import torch
+    _need(x.dtype == torch.float32 and x.is_contiguous(), "decode_matvec: x must be contiguous float32")
+    _need(s_x is None or (s_x.dtype == torch.float64 and s_x.numel() == x.shape[1]),
+          "decode_matvec: s_x must be float64 with din entries")
+    _need(1 <= len(layers) <= KQ_DECODE_MAX_LAYERS, "decode_matvec_group: 1 to KQ_DECODE_MAX_LAYERS layers")
+    tokens, din = x.shape
+    arr = (DecodeLayer * len(layers))()
+    keep = []
+    total = 0
+    for i, (packed, scales, zeros, s_g, rot_out, y) in enumerate(layers):
+        dout = _check_decode_layer(packed, scales, zeros, bits, group, din, s_g, y, tokens)
+        total += dout
+        arr[i] = DecodeLayer(_ptr(packed), _ptr(scales), _ptr(zeros), dout, _ptr(s_g),
+                             None if rot_out is None else ctypes.pointer(rot_out), _ptr(y))
+        keep.append(rot_out)
+    if ws is None:
+        ws = decode_workspace(total, din, tokens, x.device)
+    _check(lib().kq_decode_matvec_group(arr, len(layers), din, bits, group, _ptr(s_x),
+                                        None if rot_in is None else ctypes.byref(rot_in), _ptr(x), tokens,
+                                        _ptr(ws), ws.numel(), _stream(stream)), "kq_decode_matvec_group")

@@ -65,17 +65,44 @@ struct Side {
   const double* s;   // diagonal scale, NULL: 1
 };
 
-struct DecodeArgs {
+// One layer of a group that shares its input (q, k and v; gate and up).
+struct Layer {
   const uint32_t* packed;
   const float* scales;
   const uint8_t* zeros;
-  int64_t dout, din;
-  int group, ngroups;
-  const float* x;     // [T, din]: x itself (fused input side) or x1 (separate or no input side)
-  Side in;            // the input side, for the fused form
+  int64_t dout;
   float* y;           // [T, dout] final output (no output rotation) ...
   float* y1;          // ... or the matvec result before the output side
   const double* s_g;  // applied by the matvec when there is no output rotation
+  int wg0;            // first matvec workgroup of this layer
+};
+
+struct DecodeArgs {
+  Layer layer[KQ_DECODE_MAX_LAYERS];
+  int n_layers;
+  int64_t din;
+  int group, ngroups;
+  const float* x;     // [T, din]: x itself (fused input side) or x1 (separate or no input side)
+  Side in;            // the input side, for the fused form
+};
+
+// Layer l of a kernel argument, read with constant indices only (a dynamic index into a
+// by-value kernel argument makes the compiler copy it to scratch memory).
+template <typename A, typename E>
+__device__ __forceinline__ E pick(const A (&a)[KQ_DECODE_MAX_LAYERS], int l, E A::*f) {
+  E v = a[0].*f;
+#pragma unroll
+  for (int k = 1; k < KQ_DECODE_MAX_LAYERS; ++k)
+    if (l == k) v = a[k].*f;
+  return v;
+}
+
+// Output sides of a group, one workgroup per layer that has one.
+struct OutArgs {
+  const float* src[KQ_DECODE_MAX_LAYERS];
+  float* dst[KQ_DECODE_MAX_LAYERS];
+  int n[KQ_DECODE_MAX_LAYERS];
+  Side sd[KQ_DECODE_MAX_LAYERS];
 };
 
 // One pass of the fast Walsh-Hadamard transform over index bits [o, o + R) of every token's
@@ -473,13 +500,26 @@ __host__ __device__ constexpr int side_lds_floats(int n, int tokens) {
   return ((tokens * n + 3) & ~3) + kQFloats;
 }
 
-// One side for T tokens of n entries in one 1024-thread workgroup: dst = S^-1 U^T src (output
-// side) or U S^-1 src (input side, when it is not fused into the matvec). VEC: the grouped form
-// (n % 16 == 0, every operand 16-byte aligned).
+// One side for T tokens of n entries per 1024-thread workgroup: dst = S^-1 U^T src (output
+// side, one workgroup per layer of a group) or U S^-1 src (input side, when it is not fused into
+// the matvec; one workgroup). VEC: the grouped form (n % 16 == 0, every operand 16-byte aligned).
 template <int T, bool OUT, bool VEC>
-__global__ __launch_bounds__(kSideThreads) void side_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                           int n, Side sd) {
+__global__ __launch_bounds__(kSideThreads) void side_kernel(OutArgs oa) {
   extern __shared__ float lds[];
+  // workgroup l takes entry l (every member read with a constant index, then selected)
+  const int l = blockIdx.x;
+  const float* src = oa.src[0];
+  float* dst = oa.dst[0];
+  int n = oa.n[0];
+  Side sd = oa.sd[0];
+#pragma unroll
+  for (int k = 1; k < KQ_DECODE_MAX_LAYERS; ++k)
+    if (l == k) {
+      src = oa.src[k];
+      dst = oa.dst[k];
+      n = oa.n[k];
+      sd = oa.sd[k];
+    }
   if constexpr (VEC) {
     SideStageV<T, kSideThreads, OUT> st;
     st.issue(src, n, sd);
@@ -557,7 +597,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
   constexpr int U = NW <= 16 ? 16 / NW : 1;  // rows in flight: 16 words per lane
   static_assert(NW >= 1 && CPL % PER == 0 && PER % 4 == 0, "codes per lane");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t din = g.din, dout = g.dout;
+  // this workgroup's layer: the last one whose first workgroup it has reached
+  int li = 0;
+#pragma unroll
+  for (int l = 1; l < KQ_DECODE_MAX_LAYERS; ++l)
+    if (l < g.n_layers && static_cast<int>(blockIdx.x) >= pick(g.layer, l, &Layer::wg0)) li = l;
+  const uint32_t* packed = pick(g.layer, li, &Layer::packed);
+  const float* scales = pick(g.layer, li, &Layer::scales);
+  const uint8_t* zeros = pick(g.layer, li, &Layer::zeros);
+  const int64_t dout = pick(g.layer, li, &Layer::dout);
+  const int64_t din = g.din;
   const int64_t wpr = din / PER;  // words per row
   const int din32 = static_cast<int>(din);
 
@@ -574,16 +623,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
     kw[i] = min(k, wl);
     gcol[i] = g.group ? (kw[i] * PER) / g.group : 0;
   }
-  const int64_t r0 = int64_t(blockIdx.x) * kRowsPerWg;
+  const int64_t r0 = int64_t(static_cast<int>(blockIdx.x) - pick(g.layer, li, &Layer::wg0)) * kRowsPerWg;
   uint32_t wd[U][NW], zr[U][NW];
   float sc[U][NW];
   auto load_rows = [&](int rb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = min(r0 + rb + u, dout - 1);
-      const uint32_t* prow = g.packed + row * wpr;
-      const float* srow = g.scales + row * g.ngroups;
-      const uint8_t* zrow = g.zeros + row * g.ngroups;
+      const uint32_t* prow = packed + row * wpr;
+      const float* srow = scales + row * g.ngroups;
+      const uint8_t* zrow = zeros + row * g.ngroups;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
         wd[u][i] = prow[kw[i]];
@@ -683,10 +732,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs g) {
     if (row >= dout) continue;
     const float* pp = part + rr * 4 * T + t;
     const float v = (pp[0] + pp[T]) + (pp[2 * T] + pp[3 * T]);
-    if (g.y1) {
-      g.y1[t * dout + row] = v;
+    float* y1 = pick(g.layer, li, &Layer::y1);
+    if (y1) {
+      y1[t * dout + row] = v;
     } else {
-      g.y[t * dout + row] = g.s_g ? v / static_cast<float>(g.s_g[row]) : v;
+      const double* s_g = pick(g.layer, li, &Layer::s_g);
+      pick(g.layer, li, &Layer::y)[t * dout + row] = s_g ? v / static_cast<float>(s_g[row]) : v;
     }
   }
 }
@@ -708,14 +759,22 @@ bool side_vec_ok(const float* src, const float* dst, int64_t n, const Side& sd) 
          (sd.s == nullptr || aligned16(sd.s));
 }
 
+// Side launch over `count` entries of oa (one workgroup each). The grouped form is used when
+// every entry allows it.
 template <int T, bool OUT>
-kq_status launch_side(const float* src, float* dst, int n, const Side& sd, hipStream_t st) {
-  const size_t lds = side_lds_bytes(n, T);
+kq_status launch_side(const OutArgs& oa, int count, hipStream_t st) {
+  int nmax = 0;
+  bool vec = true;
+  for (int l = 0; l < count; ++l) {
+    nmax = oa.n[l] > nmax ? oa.n[l] : nmax;
+    vec = vec && side_vec_ok(oa.src[l], oa.dst[l], oa.n[l], oa.sd[l]);
+  }
+  const size_t lds = side_lds_bytes(nmax, T);
   const char* name = OUT ? "decode_out_kernel" : "decode_in_kernel";
   // (the grouped output side holds 16 T values, 16 factors and 16 scales per thread: up to
   // two tokens within the 1024-thread register budget)
   constexpr bool kVecForm = !OUT || T <= 2;
-  const bool vec = kVecForm && side_vec_ok(src, dst, n, sd);
+  vec = vec && kVecForm;
   constexpr auto vec_kernel = side_kernel<T, OUT, kVecForm>;  // the scalar form when not allowed
   const void* fn = vec ? reinterpret_cast<const void*>(vec_kernel)
                        : reinterpret_cast<const void*>(&side_kernel<T, OUT, false>);
@@ -723,22 +782,28 @@ kq_status launch_side(const float* src, float* dst, int n, const Side& sd, hipSt
   {
     LaunchTimer timer(name, st);
     if (vec)
-      hipLaunchKernelGGL(vec_kernel, dim3(1), dim3(kSideThreads), lds, st, src, dst, n, sd);
+      hipLaunchKernelGGL(vec_kernel, dim3(count), dim3(kSideThreads), lds, st, oa);
     else
-      hipLaunchKernelGGL((side_kernel<T, OUT, false>), dim3(1), dim3(kSideThreads), lds, st, src, dst, n, sd);
+      hipLaunchKernelGGL((side_kernel<T, OUT, false>), dim3(count), dim3(kSideThreads), lds, st, oa);
   }
   return check_launch(name);
 }
 
 // in_mode: 0 no input side, 1 fused into the matvec, 2 separate launch into x1.
 template <int C, int CPL, int T>
-kq_status launch(DecodeArgs a, int in_mode, float* x1, const Side* out, hipStream_t st) {
+kq_status launch(DecodeArgs a, int in_mode, float* x1, const OutArgs& out, int n_out, hipStream_t st) {
   kq_status s = KQ_OK;
   if (in_mode == 2) {
-    if ((s = launch_side<T, false>(a.x, x1, static_cast<int>(a.din), a.in, st)) != KQ_OK) return s;
+    OutArgs ia{};
+    ia.src[0] = a.x;
+    ia.dst[0] = x1;
+    ia.n[0] = static_cast<int>(a.din);
+    ia.sd[0] = a.in;
+    if ((s = launch_side<T, false>(ia, 1, st)) != KQ_OK) return s;
     a.x = x1;
   }
-  const unsigned grid = static_cast<unsigned>((a.dout + kRowsPerWg - 1) / kRowsPerWg);
+  const Layer& last = a.layer[a.n_layers - 1];
+  const unsigned grid = static_cast<unsigned>(last.wg0 + (last.dout + kRowsPerWg - 1) / kRowsPerWg);
   const size_t lds = in_mode == 1 ? side_lds_bytes(a.din, T) : 0;
   const void* fn = in_mode == 1 ? reinterpret_cast<const void*>(&decode_kernel<C, CPL, T, true>)
                                 : reinterpret_cast<const void*>(&decode_kernel<C, CPL, T, false>);
@@ -750,24 +815,25 @@ kq_status launch(DecodeArgs a, int in_mode, float* x1, const Side* out, hipStrea
     else
       hipLaunchKernelGGL((decode_kernel<C, CPL, T, false>), dim3(grid), dim3(kThreads), 0, st, a);
   }
-  if ((s = check_launch("decode_kernel")) != KQ_OK || !out) return s;
-  return launch_side<T, true>(a.y1, a.y, static_cast<int>(a.dout), *out, st);
+  if ((s = check_launch("decode_kernel")) != KQ_OK || n_out == 0) return s;
+  return launch_side<T, true>(out, n_out, st);
 }
 
 template <int C>
-kq_status launch_t(const DecodeArgs& a, int in_mode, float* x1, const Side* out, int cpl, int tokens,
-                   hipStream_t st) {
+kq_status launch_t(const DecodeArgs& a, int in_mode, float* x1, const OutArgs& out, int n_out, int cpl,
+                   int tokens, hipStream_t st) {
   if (cpl == 16) {
     switch (tokens) {
-      case 1: return launch<C, 16, 1>(a, in_mode, x1, out, st);
-      case 2: return launch<C, 16, 2>(a, in_mode, x1, out, st);
-      case 3: return launch<C, 16, 3>(a, in_mode, x1, out, st);
-      default: return launch<C, 16, 4>(a, in_mode, x1, out, st);
+      case 1: return launch<C, 16, 1>(a, in_mode, x1, out, n_out, st);
+      case 2: return launch<C, 16, 2>(a, in_mode, x1, out, n_out, st);
+      case 3: return launch<C, 16, 3>(a, in_mode, x1, out, n_out, st);
+      default: return launch<C, 16, 4>(a, in_mode, x1, out, n_out, st);
     }
   }
   if (cpl == 32)
-    return tokens == 1 ? launch<C, 32, 1>(a, in_mode, x1, out, st) : launch<C, 32, 2>(a, in_mode, x1, out, st);
-  return launch<C, 64, 1>(a, in_mode, x1, out, st);
+    return tokens == 1 ? launch<C, 32, 1>(a, in_mode, x1, out, n_out, st)
+                       : launch<C, 32, 2>(a, in_mode, x1, out, n_out, st);
+  return launch<C, 64, 1>(a, in_mode, x1, out, n_out, st);
 }
 
 size_t y1_bytes(int64_t dout, int64_t tokens) { return align_up(size_t(tokens) * dout * sizeof(float), 256); }
@@ -790,8 +856,10 @@ Side make_side(const kq_rot* r, const double* s) {
 
 int container_bits(int bits) { return bits == 2 ? 2 : (bits <= 4 ? 4 : 8); }
 
+// dout: the layers' total rows. Each layer's matvec result starts on a 256-byte boundary (the
+// padding is covered by one 256-byte slot per layer), then x1.
 size_t decode_workspace(int64_t dout, int64_t din, int64_t tokens) {
-  return y1_bytes(dout, tokens) + align_up(size_t(tokens) * din * sizeof(float), 256);
+  return y1_bytes(dout, tokens) + KQ_DECODE_MAX_LAYERS * 256 + align_up(size_t(tokens) * din * sizeof(float), 256);
 }
 
 size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_side, bool out_rot) {
@@ -820,40 +888,58 @@ kq_status pack_run(const uint8_t* codes, int64_t rows, int64_t cols, int bits, u
   return check_launch("pack_kernel");
 }
 
-kq_status decode_run(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout, int64_t din,
-                     int bits, int group, const double* s_x, const double* s_g, const kq_rot* rot_in,
-                     const kq_rot* rot_out, const float* x, int64_t tokens, float* y, void* ws, hipStream_t st) {
+kq_status decode_run(const kq_decode_layer* layers, int n_layers, int64_t din, int bits, int group,
+                     const double* s_x, const kq_rot* rot_in, const float* x, int64_t tokens, void* ws,
+                     hipStream_t st) {
   DecodeArgs a{};
-  a.packed = packed;
-  a.scales = scales;
-  a.zeros = zeros;
-  a.dout = dout;
+  OutArgs out{};
+  int n_out = 0, wg = 0;
+  int64_t total = 0;
+  char* wp = static_cast<char*>(ws);
+  for (int l = 0; l < n_layers; ++l) {
+    const kq_decode_layer& L = layers[l];
+    Layer& d = a.layer[l];
+    d.packed = L.packed;
+    d.scales = L.scales;
+    d.zeros = L.zeros;
+    d.dout = L.dout;
+    d.y = L.y;
+    d.s_g = L.s_g;
+    d.wg0 = wg;
+    d.y1 = nullptr;
+    if (L.rot_out) {
+      d.y1 = reinterpret_cast<float*>(wp);
+      wp += y1_bytes(L.dout, tokens);
+      out.src[n_out] = d.y1;
+      out.dst[n_out] = L.y;
+      out.n[n_out] = static_cast<int>(L.dout);
+      out.sd[n_out] = make_side(L.rot_out, L.s_g);
+      ++n_out;
+    }
+    wg += static_cast<int>((L.dout + kRowsPerWg - 1) / kRowsPerWg);
+    total += L.dout;
+  }
+  a.n_layers = n_layers;
   a.din = din;
   a.group = group;
   a.ngroups = group ? static_cast<int>(din / group) : 1;
   a.x = x;
   a.in = make_side(rot_in, s_x);
-  a.y = y;
-  a.y1 = rot_out ? static_cast<float*>(ws) : nullptr;
-  a.s_g = s_g;
-  float* x1 = reinterpret_cast<float*>(static_cast<char*>(ws) + y1_bytes(dout, tokens));
+  float* x1 = reinterpret_cast<float*>(static_cast<char*>(ws) + y1_bytes(total, tokens) + KQ_DECODE_MAX_LAYERS * 256);
   // The input side runs inside the matvec (in the grouped form) when it is a plain transform (no
   // odd factor), the grid is at most one workgroup per CU (each workgroup repeats it: more would
   // queue the copies behind each other) and its operands are 16-byte aligned; otherwise as its
   // own one-workgroup launch. The direct path reads x as float4s, so an unaligned x with no input
   // side goes through that launch too.
   const bool need_in = rot_in || s_x || !aligned16(x);
-  const int64_t grid = (dout + kRowsPerWg - 1) / kRowsPerWg;
-  const bool fuse = a.in.m == 1 && grid <= kCus && side_vec_ok(x, nullptr, din, a.in);
+  const bool fuse = a.in.m == 1 && wg <= kCus && side_vec_ok(x, nullptr, din, a.in);
   const int in_mode = !need_in ? 0 : (fuse ? 1 : 2);
-  const Side out = make_side(rot_out, s_g);
   const int t = static_cast<int>(tokens);
   const int cpl = decode_cpl(din, tokens);
-  const Side* pout = rot_out ? &out : nullptr;
   switch (container_bits(bits)) {
-    case 2: return launch_t<2>(a, in_mode, x1, pout, cpl, t, st);
-    case 4: return launch_t<4>(a, in_mode, x1, pout, cpl, t, st);
-    default: return launch_t<8>(a, in_mode, x1, pout, cpl, t, st);
+    case 2: return launch_t<2>(a, in_mode, x1, out, n_out, cpl, t, st);
+    case 4: return launch_t<4>(a, in_mode, x1, out, n_out, cpl, t, st);
+    default: return launch_t<8>(a, in_mode, x1, out, n_out, cpl, t, st);
   }
 }
 

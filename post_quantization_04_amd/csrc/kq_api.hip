@@ -105,7 +105,8 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2) {
       if (d0 < 1 || d1 < 1 || d2 < 1 || d1 > kMaxDim) return bad;
       return kq::obs_workspace(d0, d1, static_cast<int>(d2));
     case KQ_OP_DECODE:
-      if (d0 < 1 || d0 > KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_MAX_ROT_DIM || d2 < 1 || d2 > KQ_DECODE_MAX_TOKENS)
+      if (d0 < 1 || d0 > int64_t(KQ_DECODE_MAX_LAYERS) * KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_MAX_ROT_DIM || d2 < 1 ||
+          d2 > KQ_DECODE_MAX_TOKENS)
         return bad;
       return kq::decode_workspace(d0, d1, d2);
     default:
@@ -230,31 +231,49 @@ kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_
   return kq::pack_run(codes, rows, cols, bits, packed, kq::as_stream(stream));
 }
 
-kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout,
-                           int64_t din, int32_t bits, int32_t group, const double* s_x, const double* s_g,
-                           const kq_rot* rot_in, const kq_rot* rot_out, const float* x, int64_t tokens, float* y,
-                           void* ws, size_t ws_bytes, void* stream) {
-  if (!packed || !scales || !zeros || !x || !y) return fail(KQ_EINVAL, "kq_decode_matvec: NULL pointer");
+kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers, int64_t din, int32_t bits,
+                                 int32_t group, const double* s_x, const kq_rot* rot_in, const float* x,
+                                 int64_t tokens, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || !x) return fail(KQ_EINVAL, "kq_decode_matvec: NULL pointer");
+  if (n_layers < 1 || n_layers > KQ_DECODE_MAX_LAYERS)
+    return fail(KQ_EINVAL, "kq_decode_matvec_group: %d layers outside [1, %d]", n_layers, KQ_DECODE_MAX_LAYERS);
   if (bits < 2 || bits > 8) return fail(KQ_EINVAL, "kq_decode_matvec: bits = %d outside [2, 8]", bits);
-  if (dout < 1 || din < 1 || dout > KQ_MAX_ROT_DIM || din > KQ_MAX_ROT_DIM || din % 16 != 0)
-    return fail(KQ_EINVAL, "kq_decode_matvec: shape %lld x %lld (din must be a multiple of 16, both <= %d)",
-                (long long)dout, (long long)din, KQ_MAX_ROT_DIM);
+  if (din < 1 || din > KQ_MAX_ROT_DIM || din % 16 != 0)
+    return fail(KQ_EINVAL, "kq_decode_matvec: din %lld (a multiple of 16, at most %d)", (long long)din,
+                KQ_MAX_ROT_DIM);
   if (group < 0 || (group > 0 && (group % 16 != 0 || din % group != 0)))
     return fail(KQ_EINVAL, "kq_decode_matvec: group %d must be 0 or a multiple of 16 dividing din", group);
   if (tokens < 1 || tokens > KQ_DECODE_MAX_TOKENS)
     return fail(KQ_EINVAL, "kq_decode_matvec: tokens = %lld outside [1, %d]", (long long)tokens,
                 KQ_DECODE_MAX_TOKENS);
   if (rot_in && !rot_ok(rot_in, din, "input")) return KQ_EINVAL;
-  if (rot_out && !rot_ok(rot_out, dout, "output")) return KQ_EINVAL;
   if (kq::decode_cpl(din, tokens) == 0)
     return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: din %lld with %lld tokens (needs din * tokens <= 16384)",
                 (long long)din, (long long)tokens);
-  if (kq::decode_lds_bytes(dout, din, tokens, rot_in || s_x, rot_out != nullptr) > 160 * 1024)
-    return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: %lld tokens of a %lld x %lld layer exceed LDS", (long long)tokens,
-                (long long)dout, (long long)din);
-  if (!ws_ok(ws, ws_bytes, kq::decode_workspace(dout, din, tokens))) return KQ_EINVAL;
-  return kq::decode_run(packed, scales, zeros, dout, din, bits, group, s_x, s_g, rot_in, rot_out, x, tokens, y, ws,
-                        kq::as_stream(stream));
+  int64_t total = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const kq_decode_layer& L = layers[l];
+    if (!L.packed || !L.scales || !L.zeros || !L.y)
+      return fail(KQ_EINVAL, "kq_decode_matvec: NULL pointer in layer %d", l);
+    if (L.dout < 1 || L.dout > KQ_MAX_ROT_DIM)
+      return fail(KQ_EINVAL, "kq_decode_matvec: layer %d has dout %lld outside [1, %d]", l, (long long)L.dout,
+                  KQ_MAX_ROT_DIM);
+    if (L.rot_out && !rot_ok(L.rot_out, L.dout, "output")) return KQ_EINVAL;
+    if (kq::decode_lds_bytes(L.dout, din, tokens, rot_in || s_x, L.rot_out != nullptr) > 160 * 1024)
+      return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: %lld tokens of a %lld x %lld layer exceed LDS",
+                  (long long)tokens, (long long)L.dout, (long long)din);
+    total += L.dout;
+  }
+  if (!ws_ok(ws, ws_bytes, kq::decode_workspace(total, din, tokens))) return KQ_EINVAL;
+  return kq::decode_run(layers, n_layers, din, bits, group, s_x, rot_in, x, tokens, ws, kq::as_stream(stream));
+}
+
+kq_status kq_decode_matvec(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout,
+                           int64_t din, int32_t bits, int32_t group, const double* s_x, const double* s_g,
+                           const kq_rot* rot_in, const kq_rot* rot_out, const float* x, int64_t tokens, float* y,
+                           void* ws, size_t ws_bytes, void* stream) {
+  const kq_decode_layer layer{packed, scales, zeros, dout, s_g, rot_out, y};
+  return kq_decode_matvec_group(&layer, 1, din, bits, group, s_x, rot_in, x, tokens, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

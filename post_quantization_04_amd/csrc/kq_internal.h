@@ -75,8 +75,8 @@ int decode_cpl(int64_t din, int64_t tokens);
 size_t decode_workspace(int64_t dout, int64_t din, int64_t tokens);
 size_t decode_lds_bytes(int64_t dout, int64_t din, int64_t tokens, bool in_side, bool out_rot);
 kq_status pack_run(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* packed, hipStream_t st);
-kq_status decode_run(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t dout, int64_t din,
-                     int bits, int group, const double* s_x, const double* s_g, const kq_rot* rot_in,
-                     const kq_rot* rot_out, const float* x, int64_t tokens, float* y, void* ws, hipStream_t st);
+kq_status decode_run(const kq_decode_layer* layers, int n_layers, int64_t din, int bits, int group,
+                     const double* s_x, const kq_rot* rot_in, const float* x, int64_t tokens, void* ws,
+                     hipStream_t st);
 
 }  // namespace kq

@@ -133,6 +133,30 @@ def test_pack_and_decode_validation(L):
     assert call(tokens=2, ws=need - 1) == kq.KQ_EINVAL
 
 
+def test_decode_group_validation(L):
+    big = 1 << 30
+    rot = kq.Rot(n=256, m=1, log2p=8, signs=0x1000, q=0x1000)
+    wrong = kq.Rot(n=512, m=1, log2p=9, signs=0x1000, q=0x1000)
+
+    def layer(dout=256, rot_out=None, packed=0x1000):
+        return kq.DecodeLayer(packed, 0x1000, 0x1000, dout, None,
+                              None if rot_out is None else ctypes.pointer(rot_out), 0x1000)
+
+    def call(layers, n=None, ws=big, din=512):
+        arr = (kq.DecodeLayer * max(1, len(layers)))(*layers)
+        return L.kq_decode_matvec_group(arr, len(layers) if n is None else n, din, 2, 128, None, None, FAKE, 1,
+                                        FAKE, ws, None)
+    assert call([layer()], n=0) == kq.KQ_EINVAL
+    assert call([layer()] * 5) == kq.KQ_EINVAL                      # more than KQ_DECODE_MAX_LAYERS
+    assert call([layer(), layer(packed=None)]) == kq.KQ_EINVAL      # NULL codes in layer 1
+    assert b"layer 1" in L.kq_last_error()
+    assert call([layer(), layer(dout=0)]) == kq.KQ_EINVAL
+    assert call([layer(rot_out=wrong)]) == kq.KQ_EINVAL             # spec for another dimension
+    need = L.kq_workspace_size(kq.KQ_OP_DECODE, 3 * 256, 512, 1)
+    assert need >= 3 * 256 * 4 + 512 * 4
+    assert call([layer(rot_out=rot)] * 3, ws=need - 1) == kq.KQ_EINVAL
+
+
 def test_workspace_sizes(L):
     inv = ctypes.c_size_t(-1).value
     assert L.kq_workspace_size(99, 1, 1, 1) == inv

@@ -100,6 +100,67 @@ def test_decode_matvec_llama2_7b_mlp_full_size(dout, din):
     assert rel_fro(got, want) <= 2e-5
 
 
+def _group_case(rng, douts, din, bits, group, tokens, no_out=()):
+    """Layers sharing x and the input side; layer l in no_out has a diagonal scale but no output rotation."""
+    s_x = rng.uniform(0.3, 3.0, din)
+    ri = kq_synth.rot_spec(21, f"gx{din}", din)
+    x = rng.standard_normal((tokens, din))
+    layers = []
+    for l, dout in enumerate(douts):
+        codes, scales, zeros = _layer(rng, dout, din, bits, group)
+        ro = kq_synth.rot_spec(21, f"g{l}_{dout}", dout)
+        layers.append((codes, scales, zeros, rng.uniform(0.3, 3.0, dout), None if l in no_out else ro))
+    return s_x, ri, x, layers
+
+
+def _run_group(kq, pipeline, s_x, ri, x, layers, bits, group):
+    import torch
+    dev_layers, keep = [], []
+    for codes, scales, zeros, s_g, ro in layers:
+        dout, din = codes.shape
+        c = oracle.container_bits(bits)
+        packed = torch.zeros((dout, din * c // 32), dtype=torch.int32, device=DEV)
+        kq.pack_codes(to_dev(codes), bits, packed)
+        dro = pipeline.upload_rot(ro.signs, ro.q, DEV) if ro is not None else None
+        keep.append(dro)
+        y = torch.empty((x.shape[0], dout), dtype=torch.float32, device=DEV)
+        dev_layers.append((packed, to_dev(scales), to_dev(zeros), to_dev(s_g), None if dro is None else dro.rot, y))
+    dri = pipeline.upload_rot(ri.signs, ri.q, DEV)
+    kq.decode_matvec_group(dev_layers, bits, group, to_dev(s_x), dri.rot, to_dev(x.astype(np.float32)))
+    return [host(L[5]) for L in dev_layers]
+
+
+# groups of layers sharing an input: q/k/v-like widths (odd factors 5 and 7 on the output side,
+# one layer with a scale but no output rotation) with the input side fused (64 workgroups), and
+# 288 workgroups (input side as its own launch), one and two tokens
+GROUP_CASES = [((320, 256, 448), 512, 2, 128, 1, (1,)), ((320, 256, 448), 512, 4, 64, 2, ()),
+               ((2048, 2560), 1024, 2, 128, 1, ()), ((96, 200, 64, 128), 256, 3, 0, 2, (2,))]
+
+
+@pytest.mark.parametrize("douts,din,bits,group,tokens,no_out", GROUP_CASES)
+def test_decode_matvec_group(douts, din, bits, group, tokens, no_out):
+    kq, pipeline = _kq()
+    print(f"decode group {douts} x {din} bits={bits} group={group} tokens={tokens}", flush=True)
+    rng = np.random.default_rng(sum(douts) + din)
+    s_x, ri, x, layers = _group_case(rng, douts, din, bits, group, tokens, no_out)
+    got = _run_group(kq, pipeline, s_x, ri, x, layers, bits, group)
+    for (codes, scales, zeros, s_g, ro), y in zip(layers, got):
+        want = oracle.decode_matvec(codes, scales, zeros, group, s_x, s_g, ri, ro if ro is not None else ri,
+                                    x.astype(np.float32), out=ro is not None)
+        assert rel_fro(y, want) <= 2e-5
+
+
+def test_decode_matvec_group_llama2_7b_gate_up_full_size():
+    """gate and up of LLaMA-2-7B as the decode bench runs them: one group sharing the input side."""
+    kq, pipeline = _kq()
+    rng = np.random.default_rng(11008)
+    s_x, ri, x, layers = _group_case(rng, (11008, 11008), 4096, 2, 128, 1)
+    got = _run_group(kq, pipeline, s_x, ri, x, layers, 2, 128)
+    for (codes, scales, zeros, s_g, ro), y in zip(layers, got):
+        want = oracle.decode_matvec(codes, scales, zeros, 128, s_x, s_g, ri, ro, x.astype(np.float32))
+        assert rel_fro(y, want) <= 2e-5
+
+
 @pytest.mark.parametrize("inp,out", [(False, False), (True, False), (False, True)])
 def test_decode_matvec_sides(inp, out):
     kq, pipeline = _kq()

@@ -150,11 +150,12 @@ __device__ void fwht_lds(float* v, int n, int log2p, int o0 = 0) {
 
 // Odd-factor mix across the m chunks of p, in place: for every token t and column b of the
 // m x p view of its vector, out[a] = sum_a' W[a][a'] v[a' p + b], with qs[a' * 64 + a] =
-// W[a][a'] staged (zero for a or a' >= m, up to a' < 4 ceil(m / 4)). A matrix product
+// W[a][a'] staged for all 64 x 64 entries (zero for a or a' >= m). A matrix product
 // OUT = W V with V the m x (T p) matrix of the columns, on float32 MFMA (16 x 16 x 4): a wave
-// takes one block of 16 columns and forms all ceil(m / 16) row tiles of it; every wave reads
-// its inputs before a barrier and writes after it, in rounds of whole column blocks.
-template <int T, int NT>
+// takes one block of 16 columns and forms its four 16-row tiles (rows past m have zero weights,
+// and only rows below m are stored); every wave reads its inputs before a barrier and writes
+// after it, in rounds of whole column blocks.
+template <int T, int NT, int KU>
 __device__ void mix_mfma(float* v, int n, int m, int log2p, const float* qs) {
   constexpr int kWaves = NT / 64;
   constexpr int kMaxTiles = (KQ_MAX_ODD + 15) / 16;
@@ -173,16 +174,23 @@ __device__ void mix_mfma(float* v, int n, int m, int log2p, const float* qs) {
 #pragma unroll
     for (int mi = 0; mi < kMaxTiles; ++mi) acc[mi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     if (ni < nt) {
-      for (int kk = 0; kk < kt; ++kk) {
-        const int a2 = 4 * kk + lk;             // input chunk of this lane's B entry
-        const float b = (cv && a2 < m) ? col[a2 * p] : 0.0f;
+      // all kMaxTiles row tiles every step (rows past m have zero weights): no branch in the
+      // loop, so the operand reads of the next steps are issued before the MFMAs wait on them
+      // (KU K steps per iteration, written out: the staged weights are zero up to row 63)
+      for (int k0 = 0; k0 < kt; k0 += KU) {
+        float b[KU], a[KU][kMaxTiles];
 #pragma unroll
-        for (int mi = 0; mi < kMaxTiles; ++mi) {
-          if (mi < mt) {
-            const float a = qs[a2 * kQPitch + 16 * mi + li];  // W[16 mi + li][a2]
-            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[mi], 0, 0, 0);
-          }
+        for (int u = 0; u < KU; ++u) {
+          const int a2 = 4 * (k0 + u) + lk;     // input chunk of this lane's B entry
+          b[u] = (cv && a2 < m) ? col[min(a2, m - 1) * p] : 0.0f;
+#pragma unroll
+          for (int mi = 0; mi < kMaxTiles; ++mi) a[u][mi] = qs[a2 * kQPitch + 16 * mi + li];  // W[16 mi + li][a2]
         }
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int mi = 0; mi < kMaxTiles; ++mi)
+            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][mi], b[u], acc[mi], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -318,19 +326,18 @@ struct SideStage {
       }
     }
     if (mixed) {
-      // rows a' < 4 ceil(m / 4) (the product's K extent), zero outside the m x m factor
-      const int rows = (m + 3) & ~3;
+      // all 64 rows (the product's K steps run in fours), zero outside the m x m factor
 #pragma unroll
       for (int k = 0; k < kQPer; ++k) {
         const int e = k * NT + tid;
         const int a2 = e >> 6, a = e & (kQPitch - 1);
-        if (a2 < rows) qs[e] = (a < m && a2 < m) ? static_cast<float>(qv[k]) * post : 0.0f;
+        if (e < kQFloats) qs[e] = (a < m && a2 < m) ? static_cast<float>(qv[k]) * post : 0.0f;
       }
     }
     __syncthreads();
     if (on) {
       fwht_lds<T, NT>(lds, n, log2p);
-      if (mixed) mix_mfma<T, NT>(lds, n, m, log2p, qs);
+      if (mixed) mix_mfma<T, NT, (OUT && T >= 2) ? 2 : 4>(lds, n, m, log2p, qs);
     }
   }
 };
@@ -461,18 +468,17 @@ struct SideStageV {
       store_group(lds, g);
     }
     if (mixed) {
-      const int rows = (m + 3) & ~3;
 #pragma unroll
       for (int k = 0; k < kQPer; ++k) {
         const int e = k * NT + tid;
         const int a2 = e >> 6, a = e & (kQPitch - 1);
-        if (a2 < rows) qs[e] = (a < m && a2 < m) ? static_cast<float>(qv[k]) * post : 0.0f;
+        if (e < kQFloats) qs[e] = (a < m && a2 < m) ? static_cast<float>(qv[k]) * post : 0.0f;
       }
     }
     __syncthreads();
     if (on) {
       fwht_lds<T, NT>(lds, n, log2p, 4);
-      if (mixed) mix_mfma<T, NT>(lds, n, m, log2p, qs);
+      if (mixed) mix_mfma<T, NT, (OUT && T >= 2) ? 2 : 4>(lds, n, m, log2p, qs);
     }
   }
 

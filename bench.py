@@ -444,6 +444,7 @@ def main() -> int:
     w1 = torch.empty((dout, din), dtype=f64, device=dev)
     score_x = torch.empty(1, dtype=f64, device=dev)
     score_g = torch.empty(1, dtype=f64, device=dev)
+    score_host = torch.empty(2, dtype=f64, pin_memory=True)
     s_unused_x = torch.empty(din, dtype=f64, device=dev)
     s_unused_g = torch.empty(dout, dtype=f64, device=dev)
     in_flags = kq.KQ_BIIP_INPUT | kq.KQ_BIIP_SCALE
@@ -507,12 +508,22 @@ def main() -> int:
         mark(10, main)
         kq.biip_rotate(w1, w2, None, hg, None, ro.rot, out_flags, s_unused_x, s_g, ws=ws_biip)
         mark(11, main)
-        # score = tr(H_G) tr(H_X): the same float64 product the combined call forms
-        sc = float(score_x.item()) * float(score_g.item())
-        bits = kq.allocate_bits([sc], [dout * din], [args.bits], args.bits * 1000)[0]
+        # The traces go to the host without stopping the stream. One layer at one bit width leaves
+        # the allocation no choice, so the sweep is enqueued at that width and the allocation (a host
+        # routine, on score = tr(H_G) tr(H_X), the float64 product the combined call forms) runs
+        # while the sweep does, and is checked.
+        score_host[0:1].copy_(score_x, non_blocking=True)
+        score_host[1:2].copy_(score_g, non_blocking=True)
+        e_sc = torch.cuda.Event()
+        e_sc.record(main)
         mark(5, main)
-        kq.obs_quantize(w2, hx, bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
+        kq.obs_quantize(w2, hx, args.bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
         mark(6, main)
+        e_sc.synchronize()
+        sc = float(score_host[0]) * float(score_host[1])
+        bits = kq.allocate_bits([sc], [dout * din], [args.bits], args.bits * 1000)[0]
+        if bits != args.bits:
+            raise RuntimeError(f"allocation gave {bits} bits for the one layer, expected {args.bits}")
 
     step = step_serial if args.serial else step_overlap
 

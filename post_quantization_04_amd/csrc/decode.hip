@@ -10,21 +10,23 @@
 // Packing: code j of a row sits in word j / (32 / c) at bits c (j mod 32 / c),
 // with c = 2 for 2-bit codes, 4 for 3- and 4-bit codes, 8 above.
 //
-// Per layer and token batch (T <= 4 tokens), up to three launches on one stream:
+// Per call (one layer, or up to four layers that read the same input and share its input
+// side: a block's q, k and v, or gate and up) and token batch (T <= 4 tokens), up to three
+// launches on one stream:
 //   1. input side, x1 = U_X S_X^-1 x (signs and scales on load, fast Walsh-Hadamard
 //      transform per 2^k chunk in radix-16 register passes, odd-factor mix across the m
 //      chunks on float32 MFMA): applied in LDS by every workgroup of the matvec while its
 //      first rows are in flight when it has no odd factor and the grid is at most one
 //      workgroup per CU, else as a one-workgroup (1024-thread) launch into the workspace;
 //      skipped when there is neither a rotation nor a scale on that side;
-//   2. the matvec, 16 rows per 256-thread workgroup: every lane holds the x1 entries of
-//      its words in registers, the four waves split each row's packed words (lane l of
+//   2. the matvec over every layer's rows, 16 rows per 256-thread workgroup: every lane holds
+//      the x1 entries of its words in registers, the four waves split each row's packed words (lane l of
 //      wave w reads word 64 w + l + 256 i), dequantize on the fly,
 //      y1[row] = sum_g s_g (sum_j q_j x1_j - z_g sum_j x1_j), one 32-bit load per word
 //      and row, the loads of up to 16 rows in flight;
-//   3. output side, one 1024-thread workgroup: transform per chunk, transposed odd mix,
-//      signs, 1 / s_g (only with an output rotation; a scale alone is applied by the
-//      matvec).
+//   3. output sides, one 1024-thread workgroup per layer that has an output rotation:
+//      transform per chunk, transposed odd mix, signs, 1 / s_g (a scale alone is applied by
+//      the matvec).
 // A side transform's data are small and its cost is round trips, not bytes: every global
 // load of its first batch is issued before its first wait, and sides of whole groups of 16
 // with aligned operands use 16-byte loads. (A fused last-workgroup output side needed a

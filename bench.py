@@ -57,6 +57,8 @@ def parse_args():
                    help="after timing, copy 1 GiB device-to-device (a reference kernel for HBM byte counters)")
     p.add_argument("--decode", action="store_true",
                    help="instead of the quantization step: the packed-code decode matvec (one JSON line)")
+    p.add_argument("--capture", action="store_true",
+                   help="calibration capture of one LLaMA-2-7B block (forward + one backward) and its covariances")
     p.add_argument("--decode-per-layer", action="store_true",
                    help="with --decode: one kq_decode_matvec call per layer instead of one group call per shared input")
     p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
@@ -238,6 +240,59 @@ DECODE_BLOCKS = 32
 HBM_PEAK_GBS = 8000.0
 
 
+def capture_bench(args) -> int:
+    """Calibration capture for one LLaMA-2-7B decoder block with seeded random weights: forward
+    over 128 sequences of 2048 seeded token states, one backward pass from a seeded linear loss,
+    every linear layer's input (per input group) and output gradient kept in bf16; then H_X of
+    the four input groups and H_G of the seven layers through the covariance kernel. The block
+    is float32 torch (the step before the path); the covariances are the library's."""
+    import torch
+
+    import post_quantization_04_amd as kq  # noqa: F401
+    from post_quantization_04_amd import capture as cap, pipeline
+
+    dev = torch.device("cuda:0")
+    torch.zeros(1, device=dev)
+    shape, n_seq, seq = cap.LLAMA2_7B, 128, 2048
+    small = cap.BlockShape(d=512, heads=4, d_ff=1024)
+    cap.capture(small, n_seq=2, seq=256, seed=1, device=dev)  # warm the torch kernels
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    c = cap.capture(shape, n_seq=n_seq, seq=seq, seed=2026, device=dev, micro_batch=4)
+    torch.cuda.synchronize()
+    t_capture = time.perf_counter() - t0
+    tensors = list(c.x.items()) + list(c.g.items())
+    flops = sum(t.shape[0] * t.shape[1] * (t.shape[1] + 1) for _, t in tensors)
+    hs = {name: torch.empty((t.shape[1], t.shape[1]), dtype=torch.float32, device=dev) for name, t in tensors}
+    for name, t in tensors:  # warm-up of the covariance path at these widths
+        pipeline.covariance(t[:16384].view(torch.int16), out=hs[name])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for name, t in tensors:
+        pipeline.covariance(t.view(torch.int16), out=hs[name])
+    torch.cuda.synchronize()
+    t_cov = time.perf_counter() - t0
+    n = c.tokens
+    total = t_capture + t_cov
+    log(f"capture: {n} tokens in {t_capture:.2f} s; {len(tensors)} covariances in {t_cov * 1e3:.1f} ms "
+        f"({flops / t_cov / 1e12:.0f} TFLOP/s)")
+    result = {
+        "metric": "calibration capture: tokens/s through one LLaMA-2-7B block (forward + one backward, X and G "
+                  "kept) and the covariances of all its linear layers",
+        "value": round(n / total, 1), "unit": "tokens/s", "n_gpus": 1, "steps": 1, "warmup": 1,
+        "ms_per_step": round(total * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 block / bf16 X, G / f32 H", "data": "synthetic",
+        "config": {"workload": "LLaMA-2-7B decoder block (d 4096, 32 heads, d_ff 11008), seeded random weights, "
+                               "128 x 2048 seeded token states, micro-batches of 4 sequences",
+                   "tokens": n},
+        "capture_s": round(t_capture, 3), "covariance_ms": round(t_cov * 1e3, 2),
+        "covariance_tflops": round(flops / t_cov / 1e12, 1),
+        "covariances": {name: list(t.shape) for name, t in tensors},
+    }
+    print(json.dumps(result))
+    return 0
+
+
 def decode_bench(args) -> int:
     """Single-token decode through packed W2 layers: y = S_G^-1 U_G^T W^'' U_X S_X^-1 x per layer.
 
@@ -387,6 +442,8 @@ def main() -> int:
         return 2
     if args.decode:
         return decode_bench(args)
+    if args.capture:
+        return capture_bench(args)
 
     import numpy as np
     import torch

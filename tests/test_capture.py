@@ -1,0 +1,55 @@
+"""Calibration capture (X and G of a random-weight decoder block) on the CPU: shapes, the shared
+inputs of q/k/v and gate/up, and pins the block's own structure fixes."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from post_quantization_04_amd import capture as cap  # noqa: E402
+
+SHAPE = cap.BlockShape(d=64, heads=4, d_ff=96)
+
+
+def test_shapes_and_shared_inputs():
+    c = cap.capture(SHAPE, n_seq=3, seq=16, seed=1, micro_batch=2)
+    assert c.tokens == 48
+    assert set(c.x) == {"attn_in", "o_in", "mlp_in", "down_in"}
+    for name, (dout, din) in SHAPE.dims.items():
+        assert tuple(c.g[name].shape) == (48, dout) and c.g[name].dtype == torch.bfloat16
+        assert tuple(c.x[cap.GROUP_OF[name]].shape) == (48, din)
+        assert torch.isfinite(c.g[name].float()).all()
+
+
+def test_attention_input_is_the_normalised_state():
+    # q, k and v read RMSNorm(h) with unit weights: recompute it from the seeded inputs
+    c = cap.capture(SHAPE, n_seq=2, seq=8, seed=4)
+    h = cap.token_states(2, 8, SHAPE.d, 4, "cpu", torch.float64).reshape(-1, SHAPE.d)
+    want = h / torch.sqrt((h * h).mean(-1, keepdim=True) + 1e-5)
+    np.testing.assert_allclose(c.x["attn_in"].double().numpy(), want.numpy(), rtol=2 ** -7, atol=1e-6)
+
+
+def test_down_proj_gradient_is_the_loss_direction():
+    # out = h2 + down(...) and L = sum(out * R) / N, so dL/d(down output) = R / N exactly
+    n_seq, seq = 2, 8
+    c = cap.capture(SHAPE, n_seq=n_seq, seq=seq, seed=7, micro_batch=1)
+    r = cap.loss_direction(n_seq, seq, SHAPE.d, 7, "cpu", torch.float32).reshape(-1, SHAPE.d)
+    want = (r / (n_seq * seq)).to(torch.bfloat16)
+    assert torch.equal(c.g["down_proj"], want)
+
+
+def test_gate_gradient_matches_a_finite_difference():
+    # perturb the gate output at one (token, channel) in a float64 block and difference the loss
+    n_seq, seq, seed = 1, 6, 9
+    c = cap.capture(SHAPE, n_seq=n_seq, seq=seq, seed=seed, dtype=torch.float64)
+    w = cap._block_weights(SHAPE, seed, "cpu", torch.float64)
+    h = cap.token_states(n_seq, seq, SHAPE.d, seed, "cpu", torch.float64)
+    r = cap.loss_direction(n_seq, seq, SHAPE.d, seed, "cpu", torch.float64)
+    tok, ch, eps = 4, 17, 1e-6
+
+    def loss(delta):
+        def hook(name, x, y):
+            if name == "gate_proj":
+                y.view(-1, y.shape[-1])[tok, ch] += delta
+        return float((cap.block_forward(h, w, SHAPE, hook) * r).sum() / (n_seq * seq))
+    fd = (loss(eps) - loss(-eps)) / (2 * eps)
+    assert c.g["gate_proj"][tok, ch].double().item() == pytest.approx(fd, rel=2 ** -7, abs=1e-9)

@@ -50,7 +50,8 @@ class Captured:
     tokens: int = 0
 
 
-def _block_weights(shape: BlockShape, seed: int, device, dtype):
+def block_weights(shape: BlockShape, seed: int, device, dtype):
+    """Seeded N(0, 0.02²) weights [dout, din] of every linear layer."""
     import torch
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
@@ -116,7 +117,7 @@ def capture(shape: BlockShape, n_seq: int, seq: int, *, seed: int = 0, device="c
     micro-batches of sequences; returns X and G of every linear layer as bfloat16 [N, .]."""
     import torch
     dtype = torch.float32 if dtype is None else dtype
-    w = _block_weights(shape, seed, device, dtype) if weights is None else weights
+    w = block_weights(shape, seed, device, dtype) if weights is None else weights
     n = n_seq * seq
     out = Captured(tokens=n)
     for name in LAYERS:

@@ -41,7 +41,7 @@ def test_gate_gradient_matches_a_finite_difference():
     # perturb the gate output at one (token, channel) in a float64 block and difference the loss
     n_seq, seq, seed = 1, 6, 9
     c = cap.capture(SHAPE, n_seq=n_seq, seq=seq, seed=seed, dtype=torch.float64)
-    w = cap._block_weights(SHAPE, seed, "cpu", torch.float64)
+    w = cap.block_weights(SHAPE, seed, "cpu", torch.float64)
     h = cap.token_states(n_seq, seq, SHAPE.d, seed, "cpu", torch.float64)
     r = cap.loss_direction(n_seq, seq, SHAPE.d, seed, "cpu", torch.float64)
     tok, ch, eps = 4, 17, 1e-6

@@ -577,6 +577,10 @@ Plan plan(int64_t rows, int64_t d) {
   int g = (kTargetItems + p.ntiles - 1) / p.ntiles;
   if (g < 1) g = 1;
   if (g > p.nslices) g = p.nslices;
+  // A launch of whole slices hands them to the XCDs one per XCD per round, so a group of
+  // 8 < g < 16 slices would run a second round on g - 8 XCDs while the rest idle: groups
+  // above 8 slices are cut to a multiple of 8 (the remainder forms a group of its own).
+  if (g > kXcds) g -= g % kXcds;
   p.group = g;
   p.ngroups = p.nslices ? (p.nslices + g - 1) / g : 0;
   p.part_bytes = align_up(size_t(g) * p.ntiles * kT * kT * sizeof(float), 256);

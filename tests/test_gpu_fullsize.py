@@ -170,6 +170,27 @@ def test_fullsize_down_proj_covariance_slice_groups():
     np.testing.assert_allclose(np.diag(host(h)).astype(np.float64), _diag(x), rtol=2e-6)
 
 
+def test_fullsize_wide_covariance_whole_slice_groups():
+    """11008 channels (946 tiles; LLaMA-2-7B's MLP width), 8 token slices and a ragged ninth: one
+    launch of 8 whole slices, one per XCD, then the ragged slice in tile groups, summed through
+    the float64 workspace."""
+    import torch
+    kq, pipeline = _kq()
+    n_tok = 8 * 16384 + 5000
+    cfg = kq_synth.scaled(kq_synth.config(2), n_tokens=n_tok, dims={"q_proj": (64, 11008)})
+    x = kq_synth.Workload(cfg).x("attn_in")
+    d = x.shape[1]
+    assert d == 11008
+    print(f"wide covariance: {n_tok} x {d}", flush=True)
+    h = torch.empty((d, d), dtype=torch.float32, device=DEV)
+    xd = bits_to_dev(x)
+    kq.accumulate_cov(xd, h, 1.0 / n_tok, 0.0)
+    torch.cuda.synchronize()
+    del xd
+    _check_sampled_cov(x, h, _channels(d, 96, 5), "H_X 11008")
+    np.testing.assert_allclose(np.diag(host(h)).astype(np.float64), _diag(x), rtol=2e-6)
+
+
 def test_fullsize_mlp_biip_odd_factors():
     """gate_proj 13824 x 5120: output side 27 x 512, input side 5 x 1024, both transformed in full."""
     import torch

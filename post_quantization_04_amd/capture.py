@@ -111,10 +111,20 @@ def loss_direction(n_seq: int, seq: int, d: int, seed: int, device, dtype):
     return torch.randn((n_seq, seq, d), generator=gen).to(device=device, dtype=dtype)
 
 
+def block_inputs(shape: BlockShape, n_seq: int, seq: int, seed: int, device, dtype=None):
+    """(token states, loss direction R) [n_seq, seq, d] for ``capture``, drawn on the host."""
+    import torch
+    dtype = torch.float32 if dtype is None else dtype
+    return (token_states(n_seq, seq, shape.d, seed, device, dtype),
+            loss_direction(n_seq, seq, shape.d, seed, device, dtype))
+
+
 def capture(shape: BlockShape, n_seq: int, seq: int, *, seed: int = 0, device="cpu", dtype=None,
-            micro_batch: Optional[int] = None, weights=None) -> Captured:
+            micro_batch: Optional[int] = None, weights=None, inputs=None) -> Captured:
     """Forward and one backward pass of the block over n_seq sequences of `seq` tokens, in
-    micro-batches of sequences; returns X and G of every linear layer as bfloat16 [N, .]."""
+    micro-batches of sequences; returns X and G of every linear layer as bfloat16 [N, .].
+    ``weights`` and ``inputs`` (from ``block_weights`` / ``block_inputs``) default to the
+    seeded draws of ``seed``."""
     import torch
     dtype = torch.float32 if dtype is None else dtype
     w = block_weights(shape, seed, device, dtype) if weights is None else weights
@@ -127,8 +137,7 @@ def capture(shape: BlockShape, n_seq: int, seq: int, *, seed: int = 0, device="c
             out.x[grp] = torch.empty((n, din), dtype=torch.bfloat16, device=device)
         out.g[name] = torch.empty((n, dout), dtype=torch.bfloat16, device=device)
     mb = n_seq if micro_batch is None else micro_batch
-    h_all = token_states(n_seq, seq, shape.d, seed, device, dtype)
-    r_all = loss_direction(n_seq, seq, shape.d, seed, device, dtype)
+    h_all, r_all = block_inputs(shape, n_seq, seq, seed, device, dtype) if inputs is None else inputs
     for s0 in range(0, n_seq, mb):
         s1 = min(n_seq, s0 + mb)
         rows = slice(s0 * seq, s1 * seq)

@@ -164,6 +164,15 @@ def test_workspace_sizes(L):
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 0, 64, 0) == 0
     # float32 partials of all lower-triangle 256 x 256 tiles of one slice group
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8192, 512, 0) >= 3 * 256 * 256 * 4
+    # 11008 channels = 946 tiles: about 8192 tile-slice items per launch would put all 9 token
+    # slices in one launch; groups above 8 are cut to 8 (one whole slice per XCD), so the partials hold 8
+    # slices and a float64 sum of every tile carries the total across the two launches
+    tile = 256 * 256
+    want = 8 * 946 * tile * 4 + 946 * tile * 8 + ((946 * 4 + 255) // 256) * 256
+    assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8 * 16384 + 5000, 11008, 0) == want
+    # 4096 channels over 16 slices: one launch, no float64 sums
+    want = 16 * 136 * tile * 4 + ((136 * 4 + 255) // 256) * 256
+    assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 16 * 16384, 4096, 0) == want
     assert L.kq_workspace_size(kq.KQ_OP_OBS, 100, 256, 128) >= 100 * 128 * 8
     assert L.kq_workspace_size(kq.KQ_OP_CHOLESKY, 100, 0, 0) >= 2 * 128 * 128 * 4
 

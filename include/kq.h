@@ -125,7 +125,7 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
  *   rows   number of token rows, >= 0 (0: H <- beta * H)
  *   h      device float32 [d, d]; read only when beta != 0; both triangles written
  *   ws     scratch of kq_workspace_size(KQ_OP_ACCUMULATE_COV, rows, d, 0) bytes
- * bf16 products are exact; sums run in float32 within token slices of 8192
+ * bf16 products are exact; sums run in float32 within token slices of 16384
  * rows and in float64 across slices; the result is rounded once to float32.
  */
 kq_status kq_accumulate_cov(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha,
@@ -150,15 +150,18 @@ kq_status kq_sensitivity(const float* h_x, int64_t din, const float* h_g, int64_
  *
  * [KQ-art] 六: the most sensitive sub-layers are upgraded first at a fixed
  * average bit count. Rule: budget = floor(target_millibits * sum(n) / 1000)
- * bits, in 64-bit integers; every sub-layer starts at min(choices); visiting
- * sub-layers by score (highest first, ties by lower index), each is raised to
- * the largest choice that keeps sum(n_l * b_l) within the budget.
+ * bits, in exact 128-bit integer arithmetic (sum(n) up to 2^56); every
+ * sub-layer starts at min(choices); visiting sub-layers by score (highest
+ * first, ties by lower index), each is raised to the largest choice that keeps
+ * sum(n_l * b_l) within the budget.
  *   score       host float64 [n_layers]
  *   n_params    host int64 [n_layers], each > 0
  *   choices     host int32 [n_choices], each in [2, 8]
  *   bits_out    host int32 [n_layers], written on KQ_OK
- * Returns KQ_EINFEASIBLE when min(choices) * sum(n) exceeds the budget.
- * Runs entirely on the host and needs no device.
+ * Returns KQ_EINFEASIBLE when min(choices) * sum(n) exceeds the budget and
+ * KQ_EINVAL when a score is NaN or infinite (a non-finite covariance, e.g. from
+ * a NaN in X, cannot rank a sub-layer). Runs entirely on the host and needs no
+ * device.
  */
 kq_status kq_allocate_bits(const double* score, const int64_t* n_params, int32_t n_layers,
                            const int32_t* choices, int32_t n_choices, int64_t target_millibits,

@@ -472,12 +472,15 @@ def allocate_bits(scores: Sequence[float], n_params: Sequence[int], choices: Seq
     first, ties by lower index), each is raised to the largest choice that
     keeps sum(n_l * b_l) within the budget. [KQ-art] 六 upgrades the most
     sensitive class first at a fixed average bit count; the exact greedy rule
-    is a reading. Returns the list of bits, or INFEASIBLE.
+    is a reading. A score that is NaN or infinite has no place in the order and
+    is an error (ValueError). Returns the list of bits, or INFEASIBLE.
     """
     n = [int(v) for v in n_params]
     ch = sorted(set(int(c) for c in choices))
     if not n or not ch:
         raise ValueError("empty allocation problem")
+    if not all(np.isfinite(float(v)) for v in scores):
+        raise ValueError("a sensitivity score is not finite (NaN or infinite covariance)")
     total = sum(n)
     budget = (int(target_millibits) * total) // 1000
     bits = [ch[0]] * len(n)

@@ -2,6 +2,7 @@
 //
 // Every check here runs on the host before anything is enqueued, so invalid
 // calls fail the same way with or without a GPU present.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -137,6 +138,10 @@ kq_status kq_allocate_bits(const double* score, const int64_t* n_params, int32_t
   if (!score || !n_params || !choices || !bits_out) return fail(KQ_EINVAL, "kq_allocate_bits: NULL pointer");
   if (n_layers < 1 || n_choices < 1) return fail(KQ_EINVAL, "kq_allocate_bits: empty problem");
   if (target_millibits < 0) return fail(KQ_EINVAL, "kq_allocate_bits: negative target");
+  // a NaN score would make the order below undefined (no strict weak ordering), an infinite
+  // one means an overflowed covariance: neither can rank a sub-layer
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (!std::isfinite(score[l])) return fail(KQ_EINVAL, "kq_allocate_bits: score[%d] is not finite", l);
   std::vector<int32_t> ch(choices, choices + n_choices);
   for (int32_t c : ch)
     if (c < 2 || c > 8) return fail(KQ_EINVAL, "kq_allocate_bits: choice %d outside [2, 8]", c);

@@ -51,12 +51,17 @@ def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_fr
     """Code parity: replay the oracle's sweep on (w2, r), adopting the kernel's
     code or zero only where the rounding argument is within ``window`` of a
     midpoint and the kernel chose the neighbouring value. Every other entry must
-    agree exactly; adopted entries must stay under ``max_frac`` of all codes."""
+    agree exactly. Adopted codes may be at most ``max_frac`` of all codes and
+    adopted zero points at most ``max_frac`` of all zero points (rounded down:
+    no adoption at all below 1 / max_frac entries)."""
     res = oracle.obs_quantize(w2, r, bits, group, adopt_codes=codes, adopt_zeros=zeros, window=window)
-    n = codes.size
+    n, nz = codes.size, zeros.size
+    print(f"{label}: {res.adopted_codes} tie-window codes of {n}, {res.adopted_zeros} zero points of {nz}",
+          flush=True)
     assert res.mismatches == 0, f"{label}: {res.mismatches} codes/zeros differ outside the tie window"
     np.testing.assert_array_equal(res.codes, codes, err_msg=label)
     np.testing.assert_array_equal(res.zeros, zeros, err_msg=label)
-    assert res.adopted_codes <= max(1, max_frac * n), f"{label}: {res.adopted_codes} tie-window codes of {n}"
+    assert res.adopted_codes <= int(max_frac * n), f"{label}: {res.adopted_codes} tie-window codes of {n}"
+    assert res.adopted_zeros <= int(max_frac * nz), f"{label}: {res.adopted_zeros} tie-window zeros of {nz}"
     np.testing.assert_allclose(scales, res.scales.astype(np.float32), rtol=scale_rtol, err_msg=label)
     return res

@@ -497,3 +497,121 @@ def test_p13_decode_inverts_the_quantized_layer():
     x = rng.standard_normal((2, din))
     y = oracle.decode_matvec(res.codes, res.scales, res.zeros, 16, out["s_x"], out["s_g"], ri, ro, x)
     np.testing.assert_allclose(y, x @ out["w_hat"].T, rtol=1e-10, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Teacher-forced replay of the code-parity protocol. Codes may differ only
+# where the rounding argument t = w / s lies within 1e-5 of a midpoint, by one
+# code; the replay adopts such a code so that the tie-break does not cascade.
+# These pins plant flips in a sweep whose t values are set by construction.
+# --------------------------------------------------------------------------
+def _forced_sweep(w, r, bits, codes_at=None, zero_at=None):
+    """Plain column loop (one grid per row from w) with chosen codes and zero points forced:
+    the side of the comparison that took a different, legal tie-break."""
+    w = np.array(w, np.float64, copy=True)
+    dout, din = w.shape
+    maxq = (1 << bits) - 1
+    s, z = oracle.grid(w.min(axis=1), w.max(axis=1), bits)
+    for i, zi in (zero_at or {}).items():
+        z[i] = zi
+    codes = np.zeros((dout, din), np.uint8)
+    for j in range(din):
+        q = np.clip(np.rint(w[:, j] / s) + z, 0, maxq)
+        for (i, jj), c in (codes_at or {}).items():
+            if jj == j:
+                q[i] = c
+        e = (w[:, j] - s * (q - z)) / r[j, j]
+        codes[:, j] = q
+        w[:, j + 1:] -= np.outer(e, r[j, j + 1:])
+    return codes, z.astype(np.uint8)
+
+
+def _replay_case():
+    """A 6 x 24 two-bit sweep with one entry's t placed 3e-6 above a midpoint."""
+    rng = np.random.default_rng(2718)
+    dout, din, bits = 6, 24, 2
+    r = oracle.chol_inv_upper(_spd(rng, din, spread=1.0), 0.01)
+    w = rng.normal(0.0, 0.02, (dout, din))
+    i = 2
+    s0, z0 = oracle.grid(w.min(axis=1), w.max(axis=1), bits)
+    t = oracle.obs_quantize(w, r, bits, 0).t
+    for j in range(4, din - 4):  # the first entry whose move to the midpoint leaves its row's grid alone
+        target = np.floor(t[i, j]) + 0.5 + 3e-6
+        w1 = w.copy()
+        w1[i, j] += (target - t[i, j]) * s0[i]  # earlier columns are unchanged, so is the feedback into (i, j)
+        s1, z1 = oracle.grid(w1.min(axis=1), w1.max(axis=1), bits)
+        if np.array_equal(s0, s1) and np.array_equal(z0, z1):
+            break
+    else:
+        raise AssertionError("no entry of the row can be placed at a midpoint")
+    w = w1
+    base = oracle.obs_quantize(w, r, bits, 0)
+    assert abs(base.t[i, j] - target) < 1e-11
+    return w, r, bits, (i, j), base
+
+
+def test_replay_adopts_a_neighbour_inside_the_window():
+    w, r, bits, (i, j), base = _replay_case()
+    own = int(base.codes[i, j])
+    forced, _ = _forced_sweep(w, r, bits, codes_at={(i, j): own - 1})
+    # the other side's tie-break changes later codes of the same row (the cascade the replay prevents)
+    assert np.any(forced[i, j + 1:] != base.codes[i, j + 1:])
+    rep = oracle.obs_quantize(w, r, bits, 0, adopt_codes=forced, adopt_zeros=base.zeros)
+    assert (rep.mismatches, rep.adopted_codes, rep.adopted_zeros) == (0, 1, 0)
+    np.testing.assert_array_equal(rep.codes, forced)
+    # without a window the same codes are a mismatch
+    strict = oracle.obs_quantize(w, r, bits, 0, adopt_codes=forced, adopt_zeros=base.zeros, window=0.0)
+    assert strict.mismatches >= 1 and strict.adopted_codes == 0
+    # a window that does not reach t (3e-6 from the midpoint) rejects it as well
+    narrow = oracle.obs_quantize(w, r, bits, 0, adopt_codes=forced, adopt_zeros=base.zeros, window=2e-6)
+    assert narrow.mismatches >= 1
+
+
+def test_replay_rejects_a_flip_outside_the_window():
+    w, r, bits, (i, j), base = _replay_case()
+    frac = base.t - np.floor(base.t)
+    far = np.argwhere(np.abs(frac - 0.5) > 0.1)
+    i2, j2 = (int(v) for v in far[len(far) // 2])
+    other = base.codes.copy()
+    c = int(other[i2, j2])
+    other[i2, j2] = c - 1 if c > 0 else c + 1
+    rep = oracle.obs_quantize(w, r, bits, 0, adopt_codes=other, adopt_zeros=base.zeros)
+    assert (rep.mismatches, rep.adopted_codes) == (1, 0)
+    np.testing.assert_array_equal(rep.codes, base.codes)
+
+
+def test_replay_rejects_a_two_step_flip_inside_the_window():
+    w, r, bits, (i, j), base = _replay_case()
+    own, maxq = int(base.codes[i, j]), (1 << bits) - 1
+    other = base.codes.copy()
+    other[i, j] = own - 2 if own >= 2 else own + 1  # neither floor(t) + z nor floor(t) + 1 + z
+    assert other[i, j] <= maxq
+    rep = oracle.obs_quantize(w, r, bits, 0, adopt_codes=other, adopt_zeros=base.zeros)
+    assert (rep.mismatches, rep.adopted_codes) == (1, 0)
+
+
+def test_replay_adopts_a_zero_point_inside_the_window():
+    w, r, bits, _, base = _replay_case()
+    i3 = 4
+    s0 = 2.0 ** -7                               # exact in float32: the stored scale is s0 itself
+    xmin = -(1.5 + 3e-6) * s0                    # -xmin / s lies 3e-6 above the midpoint 1.5
+    xmax = xmin + 3 * s0
+    rng = np.random.default_rng(5)
+    w[i3] = rng.uniform(xmin, xmax, w.shape[1])
+    w[i3, 0], w[i3, 1] = xmin, xmax
+    s, z = oracle.grid(w.min(axis=1), w.max(axis=1), bits)
+    assert s[i3] == s0 and z[i3] == 2
+    plain = oracle.obs_quantize(w, r, bits, 0)
+    forced, fz = _forced_sweep(w, r, bits, zero_at={i3: 1})
+    assert fz[i3] == 1 and np.any(forced[i3] != plain.codes[i3])
+    rep = oracle.obs_quantize(w, r, bits, 0, adopt_codes=forced, adopt_zeros=fz[:, None])
+    assert (rep.mismatches, rep.adopted_zeros) == (0, 1)
+    np.testing.assert_array_equal(rep.codes, forced)
+    np.testing.assert_array_equal(rep.zeros[:, 0], fz)
+    # the same zero flip on a row whose -xmin / s is far from a midpoint is a mismatch
+    u = -np.minimum(w.min(axis=1), 0.0) / s
+    far = [k for k in range(w.shape[0]) if abs(u[k] - np.floor(u[k]) - 0.5) > 0.1]
+    zz = plain.zeros.copy()
+    zz[far[0], 0] = zz[far[0], 0] - 1 if zz[far[0], 0] > 0 else zz[far[0], 0] + 1
+    rep2 = oracle.obs_quantize(w, r, bits, 0, adopt_codes=plain.codes, adopt_zeros=zz)
+    assert (rep2.mismatches, rep2.adopted_zeros) == (1, 0)

@@ -65,6 +65,7 @@ enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS =
 #define KQ_MAX_ROT_DIM 32768  /* largest rotated dimension n = m * 2^k */
 #define KQ_DECODE_MAX_TOKENS 4  /* tokens per kq_decode_matvec call */
 #define KQ_DECODE_MAX_LAYERS 4  /* layers per kq_decode_matvec_group call */
+#define KQ_DECODE_NOALLOC_SCRATCH 2228224  /* bytes of the fixed scratch of kq_decode_matvec_group_noalloc */
 
 /*
  * Rotation of one side: U = (Q_m kron H_p / sqrt(p)) diag(sigma), n = m * p,
@@ -329,6 +330,29 @@ kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers
                                  int32_t bits, int32_t group, const double* s_x,
                                  const kq_rot* rot_in, const float* x, int64_t tokens,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kq_decode_matvec_group_noalloc -- kq_decode_matvec_group without a workspace argument
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, checks and result as kq_decode_matvec_group, except that the
+ * scratch space lives in a fixed device array inside the library
+ * (KQ_DECODE_NOALLOC_SCRATCH bytes, 2.125 MiB, one copy per GPU the library
+ * runs on, held until the process ends). It covers the workspace of every call
+ * that kq_decode_matvec_group accepts; a larger need returns KQ_EUNSUPPORTED.
+ * The call allocates nothing: its first call on a device resolves the array's
+ * device address (hipGetSymbolAddress) and keeps it.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (no entry needs to start at zero: every scratch value is
+ * written before it is read within a call). Calls that overlap on one GPU
+ * (concurrent streams, or host threads) race on it; calls on one stream are
+ * ordered and safe.
+ */
+kq_status kq_decode_matvec_group_noalloc(const kq_decode_layer* layers, int32_t n_layers, int64_t din,
+                                         int32_t bits, int32_t group, const double* s_x,
+                                         const kq_rot* rot_in, const float* x, int64_t tokens,
+                                         void* stream);
 
 #ifdef __cplusplus
 }

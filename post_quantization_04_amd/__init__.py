@@ -20,7 +20,8 @@ __all__ = [
     "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
     "KQ_OP_DECODE", "KQ_DECODE_MAX_TOKENS", "KQ_DECODE_MAX_LAYERS",
     "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
-    "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_matvec_group", "decode_workspace", "Rot",
+    "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_matvec_group",
+    "decode_matvec_group_noalloc", "decode_workspace", "Rot", "KQ_DECODE_NOALLOC_SCRATCH",
     "DecodeLayer",
     "timing_enable", "timing_query",
 ]
@@ -32,6 +33,7 @@ KQ_SCORE_KRONQ, KQ_SCORE_HX_ONLY = 0, 1
 KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS, KQ_OP_DECODE = 0, 1, 2, 3, 4
 KQ_DECODE_MAX_TOKENS = 4
 KQ_DECODE_MAX_LAYERS = 4
+KQ_DECODE_NOALLOC_SCRATCH = 2228224
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -98,9 +100,11 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(Rot), _VP, _I64, _VP, _VP, _SZ, _VP]
     L.kq_decode_matvec_group.argtypes = [ctypes.POINTER(DecodeLayer), _I32, _I64, _I32, _I32, _VP,
                                          ctypes.POINTER(Rot), _VP, _I64, _VP, _SZ, _VP]
+    L.kq_decode_matvec_group_noalloc.argtypes = [ctypes.POINTER(DecodeLayer), _I32, _I64, _I32, _I32, _VP,
+                                                 ctypes.POINTER(Rot), _VP, _I64, _VP]
     for name in ("kq_accumulate_cov", "kq_sensitivity", "kq_allocate_bits", "kq_biip_rotate",
                  "kq_cholesky_inv", "kq_obs_quantize", "kq_pack_codes", "kq_decode_matvec",
-                 "kq_decode_matvec_group"):
+                 "kq_decode_matvec_group", "kq_decode_matvec_group_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -326,3 +330,25 @@ def decode_matvec_group(layers, bits: int, group: int, s_x, rot_in: Optional[Rot
     _check(lib().kq_decode_matvec_group(arr, len(layers), din, bits, group, _ptr(s_x),
                                         None if rot_in is None else ctypes.byref(rot_in), _ptr(x), tokens,
                                         _ptr(ws), ws.numel(), _stream(stream)), "kq_decode_matvec_group")
+
+
+def decode_matvec_group_noalloc(layers, bits: int, group: int, s_x, rot_in: Optional[Rot], x, *,
+                                stream=None) -> None:
+    """decode_matvec_group without a workspace: the library's fixed device scratch array is used
+    (no allocation by the library or by this binding). Calls that overlap on one GPU race on it."""
+    import torch
+    _need(x.dtype == torch.float32 and x.is_contiguous(), "decode_matvec: x must be contiguous float32")
+    _need(s_x is None or (s_x.dtype == torch.float64 and s_x.numel() == x.shape[1]),
+          "decode_matvec: s_x must be float64 with din entries")
+    _need(1 <= len(layers) <= KQ_DECODE_MAX_LAYERS, "decode_matvec_group: 1 to KQ_DECODE_MAX_LAYERS layers")
+    tokens, din = x.shape
+    arr = (DecodeLayer * len(layers))()
+    keep = []
+    for i, (packed, scales, zeros, s_g, rot_out, y) in enumerate(layers):
+        dout = _check_decode_layer(packed, scales, zeros, bits, group, din, s_g, y, tokens)
+        arr[i] = DecodeLayer(_ptr(packed), _ptr(scales), _ptr(zeros), dout, _ptr(s_g),
+                             None if rot_out is None else ctypes.pointer(rot_out), _ptr(y))
+        keep.append(rot_out)
+    _check(lib().kq_decode_matvec_group_noalloc(arr, len(layers), din, bits, group, _ptr(s_x),
+                                                None if rot_in is None else ctypes.byref(rot_in), _ptr(x), tokens,
+                                                _stream(stream)), "kq_decode_matvec_group_noalloc")

@@ -33,6 +33,8 @@
 // device-scope fence in every workgroup, which cost more than the launch.)
 // Everything is float32; the float64 diagonal scales and rotation factors are rounded to
 // float32 on load.
+#include <mutex>
+
 #include "kq_internal.h"
 
 namespace kq {
@@ -894,6 +896,40 @@ kq_status pack_run(const uint8_t* codes, int64_t rows, int64_t cols, int bits, u
                        cols, c, packed);
   }
   return check_launch("pack_kernel");
+}
+
+// Scratch of kq_decode_matvec_group_noalloc: a fixed array of device memory, one copy per GPU,
+// held until the process ends. Host code never hands `scratch` itself to a kernel (in host code
+// the name stands in for the symbol, not for a device address): its address on the current
+// device comes from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) char scratch[KQ_DECODE_NOALLOC_SCRATCH];
+
+// The largest workspace a valid call can ask for: matvec results of KQ_DECODE_MAX_LAYERS layers
+// of KQ_MAX_ROT_DIM rows, their alignment slots, and x1 (din * tokens <= 16384 floats).
+static_assert(size_t(KQ_DECODE_MAX_TOKENS) * KQ_DECODE_MAX_LAYERS * KQ_MAX_ROT_DIM * sizeof(float) +
+                      KQ_DECODE_MAX_LAYERS * 256 + 16384 * sizeof(float) <=
+                  size_t(KQ_DECODE_NOALLOC_SCRATCH),
+              "the fixed decode scratch holds every valid call's workspace");
+
+constexpr int kMaxDevices = 64;
+
+kq_status decode_static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return fail(KQ_EDEVICE, "decode scratch: hipGetDevice: %s", hipGetErrorString(de));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KQ_EUNSUPPORTED, "decode scratch: device %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KQ_EDEVICE, "decode scratch: hipGetSymbolAddress on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return KQ_OK;
 }
 
 kq_status decode_run(const kq_decode_layer* layers, int n_layers, int64_t din, int bits, int group,

@@ -236,9 +236,13 @@ kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_
   return kq::pack_run(codes, rows, cols, bits, packed, kq::as_stream(stream));
 }
 
-kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers, int64_t din, int32_t bits,
-                                 int32_t group, const double* s_x, const kq_rot* rot_in, const float* x,
-                                 int64_t tokens, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the decode entry points; on success `total` holds the layers' rows.
+kq_status decode_check(const kq_decode_layer* layers, int32_t n_layers, int64_t din, int32_t bits, int32_t group,
+                       const double* s_x, const kq_rot* rot_in, const float* x, int64_t tokens, int64_t& total) {
   if (!layers || !x) return fail(KQ_EINVAL, "kq_decode_matvec: NULL pointer");
   if (n_layers < 1 || n_layers > KQ_DECODE_MAX_LAYERS)
     return fail(KQ_EINVAL, "kq_decode_matvec_group: %d layers outside [1, %d]", n_layers, KQ_DECODE_MAX_LAYERS);
@@ -255,7 +259,7 @@ kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers
   if (kq::decode_cpl(din, tokens) == 0)
     return fail(KQ_EUNSUPPORTED, "kq_decode_matvec: din %lld with %lld tokens (needs din * tokens <= 16384)",
                 (long long)din, (long long)tokens);
-  int64_t total = 0;
+  total = 0;
   for (int l = 0; l < n_layers; ++l) {
     const kq_decode_layer& L = layers[l];
     if (!L.packed || !L.scales || !L.zeros || !L.y)
@@ -269,7 +273,36 @@ kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers
                   (long long)tokens, (long long)L.dout, (long long)din);
     total += L.dout;
   }
+  return KQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kq_status kq_decode_matvec_group(const kq_decode_layer* layers, int32_t n_layers, int64_t din, int32_t bits,
+                                 int32_t group, const double* s_x, const kq_rot* rot_in, const float* x,
+                                 int64_t tokens, void* ws, size_t ws_bytes, void* stream) {
+  int64_t total = 0;
+  const kq_status st = decode_check(layers, n_layers, din, bits, group, s_x, rot_in, x, tokens, total);
+  if (st != KQ_OK) return st;
   if (!ws_ok(ws, ws_bytes, kq::decode_workspace(total, din, tokens))) return KQ_EINVAL;
+  return kq::decode_run(layers, n_layers, din, bits, group, s_x, rot_in, x, tokens, ws, kq::as_stream(stream));
+}
+
+kq_status kq_decode_matvec_group_noalloc(const kq_decode_layer* layers, int32_t n_layers, int64_t din, int32_t bits,
+                                         int32_t group, const double* s_x, const kq_rot* rot_in, const float* x,
+                                         int64_t tokens, void* stream) {
+  int64_t total = 0;
+  const kq_status st = decode_check(layers, n_layers, din, bits, group, s_x, rot_in, x, tokens, total);
+  if (st != KQ_OK) return st;
+  const size_t need = kq::decode_workspace(total, din, tokens);
+  if (need > size_t(KQ_DECODE_NOALLOC_SCRATCH))
+    return fail(KQ_EUNSUPPORTED, "kq_decode_matvec_group_noalloc: needs %zu bytes of scratch, the fixed array holds %d",
+                need, KQ_DECODE_NOALLOC_SCRATCH);
+  void* ws = nullptr;
+  const kq_status sst = kq::decode_static_scratch(&ws);
+  if (sst != KQ_OK) return sst;
   return kq::decode_run(layers, n_layers, din, bits, group, s_x, rot_in, x, tokens, ws, kq::as_stream(stream));
 }
 

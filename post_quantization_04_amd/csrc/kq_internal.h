@@ -78,5 +78,8 @@ kq_status pack_run(const uint8_t* codes, int64_t rows, int64_t cols, int bits, u
 kq_status decode_run(const kq_decode_layer* layers, int n_layers, int64_t din, int bits, int group,
                      const double* s_x, const kq_rot* rot_in, const float* x, int64_t tokens, void* ws,
                      hipStream_t st);
+// Device address of the decode module's fixed scratch array on the current device (looked up
+// once per device and kept); KQ_EDEVICE if the runtime cannot resolve it.
+kq_status decode_static_scratch(void** ptr);
 
 }  // namespace kq

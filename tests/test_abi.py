@@ -157,6 +157,20 @@ def test_decode_group_validation(L):
     assert call([layer(rot_out=rot)] * 3, ws=need - 1) == kq.KQ_EINVAL
 
 
+def test_decode_noalloc_validation(L):
+    """The no-allocation decode call checks its arguments on the host, as the workspace form does,
+    before it touches the device (no GPU here)."""
+    arr = (kq.DecodeLayer * 1)()
+    x = ctypes.c_void_p(16)  # never dereferenced: every case fails its checks first
+    assert L.kq_decode_matvec_group_noalloc(arr, 1, 512, 2, 128, None, None, x, 5, None) == kq.KQ_EINVAL
+    assert L.kq_decode_matvec_group_noalloc(arr, 0, 512, 2, 128, None, None, x, 1, None) == kq.KQ_EINVAL
+    assert L.kq_decode_matvec_group_noalloc(arr, 1, 512, 9, 128, None, None, x, 1, None) == kq.KQ_EINVAL
+    assert L.kq_decode_matvec_group_noalloc(arr, 1, 520, 2, 0, None, None, x, 1, None) == kq.KQ_EINVAL
+    # layer with NULL packed codes
+    assert L.kq_decode_matvec_group_noalloc(arr, 1, 512, 2, 128, None, None, x, 1, None) == kq.KQ_EINVAL
+    assert "NULL pointer in layer 0" in L.kq_last_error().decode()
+
+
 def test_workspace_sizes(L):
     inv = ctypes.c_size_t(-1).value
     assert L.kq_workspace_size(99, 1, 1, 1) == inv

@@ -59,7 +59,8 @@ enum {
 enum { KQ_SCORE_KRONQ = 0, KQ_SCORE_HX_ONLY = 1 };
 
 /* kq_workspace_size operations. */
-enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS = 3, KQ_OP_DECODE = 4 };
+enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS = 3, KQ_OP_DECODE = 4,
+       KQ_OP_LOSS = 5 };
 
 #define KQ_MAX_ODD 63         /* largest odd factor m of a rotated dimension */
 #define KQ_MAX_ROT_DIM 32768  /* largest rotated dimension n = m * 2^k */
@@ -109,6 +110,7 @@ kq_status kq_timing_query(const char* name, int64_t* launches, double* total_ms)
  *   KQ_OP_CHOLESKY:       d0 = d
  *   KQ_OP_OBS:            d0 = dout, d1 = din, d2 = block
  *   KQ_OP_DECODE:         d0 = dout (kq_decode_matvec_group: the layers' total), d1 = din, d2 = tokens
+ *   KQ_OP_LOSS:           d0 = dout, d1 = din
  * Returns (size_t)-1 for invalid sizes.
  */
 size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
@@ -254,6 +256,26 @@ kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, 
                           int32_t group, int32_t block, uint8_t* codes, float* scales,
                           uint8_t* zeros, double* preround, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * kq_kron_loss -- loss = tr(dW H_X dW^T H_G), dW = W^ - W
+ *
+ * The layer loss under the Kronecker-factored Hessian H_X kron H_G: the
+ * quadratic form vec(dW)^T (H_X kron H_G) vec(dW) with the column-major vec
+ * ([KQ-en] Abstract; [KQ-news]). For validation of a quantized layer (in the
+ * original frame with the raw covariances, or in the rotated frame with W'',
+ * H_X'' and H_G'': BiIP preserves it).
+ *   w_hat    device float64 [dout, din]
+ *   w        device [dout, din] of type w_dtype (KQ_BF16, KQ_F32 or KQ_F64)
+ *   h_x      device float32 [din, din], h_g device float32 [dout, dout] (full symmetric)
+ *   loss     device float64 [1], written
+ *   ws       scratch of kq_workspace_size(KQ_OP_LOSS, dout, din, 0) bytes
+ * Float64 arithmetic (float64 MFMA) on the stored values; every sum runs in a
+ * fixed order, so the result is the same on every run.
+ */
+kq_status kq_kron_loss(const double* w_hat, const void* w, int32_t w_dtype, int64_t dout, int64_t din,
+                       const float* h_x, const float* h_g, double* loss, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /*
  * kq_pack_codes -- codes of a quantized weight into 32-bit words

@@ -358,12 +358,15 @@ def obs_quantize(w2: np.ndarray, r: np.ndarray, bits: int, group: int, *, adopt_
     return out
 
 
-def obs_quantize_blocked(w2: np.ndarray, r: np.ndarray, bits: int, group: int, block: int) -> ObsResult:
+def obs_quantize_blocked(w2: np.ndarray, r: np.ndarray, bits: int, group: int, block: int, *, adopt_codes=None,
+                         adopt_zeros=None, window: float = 1e-5) -> ObsResult:
     """The same sweep with lazy batching: in-block feedback column by column, then
     one trailing product W[:, end:] -= E R[blk, end:] per block of ``block`` columns.
 
     Equal to ``obs_quantize`` in exact arithmetic when every group lies inside one
-    block (block % group == 0) or group == 0.
+    block (block % group == 0) or group == 0. ``adopt_codes`` / ``adopt_zeros`` run
+    the same teacher-forced replay as in ``obs_quantize``; the blocked form keeps
+    the replay affordable for rows thousands of columns long.
     """
     w = as_f64(w2).copy()
     r = np.asarray(r, np.float64)
@@ -377,25 +380,32 @@ def obs_quantize_blocked(w2: np.ndarray, r: np.ndarray, bits: int, group: int, b
     zeros = np.zeros((dout, ng), np.uint8)
     what = np.zeros((dout, din))
     tt = np.zeros((dout, din))
+    adopt = None if adopt_codes is None else _Adopt(adopt_codes, adopt_zeros, window)
     if not group:
-        s, z = grid(w.min(axis=1), w.max(axis=1), bits)
+        s, z = _params(w, bits, adopt, 0)
         scales[:, 0], zeros[:, 0] = s, z
     for b0 in range(0, din, block):
         b1 = b0 + block
         e_blk = np.zeros((dout, block))
         for j in range(b0, b1):
             if group and j % group == 0:
-                s, z = grid(w[:, j:j + group].min(axis=1), w[:, j:j + group].max(axis=1), bits)
+                s, z = _params(w[:, j:j + group], bits, adopt, j // group)
                 scales[:, j // group], zeros[:, j // group] = s, z
             t = w[:, j] / s
             q = np.clip(np.rint(t) + z, 0, maxq)
+            if adopt is not None:
+                q, n = adopt.pick(q, adopt.codes[:, j], t, z, maxq)
+                adopt.codes_n += n
             wq = s * (q - z)
             codes[:, j], what[:, j], tt[:, j] = q, wq, t
             e = (w[:, j] - wq) / r[j, j]
             e_blk[:, j - b0] = e
             w[:, j + 1:b1] -= np.outer(e, r[j, j + 1:b1])
         w[:, b1:] -= e_blk @ r[b0:b1, b1:]
-    return ObsResult(codes, scales, zeros, what, tt)
+    out = ObsResult(codes, scales, zeros, what, tt)
+    if adopt is not None:
+        out.adopted_codes, out.adopted_zeros, out.mismatches = adopt.codes_n, adopt.zeros_n, adopt.bad
+    return out
 
 
 def obq_reference(w2: np.ndarray, h_damped: np.ndarray, bits: int, group: int) -> ObsResult:

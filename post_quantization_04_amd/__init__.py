@@ -18,10 +18,10 @@ __all__ = [
     "KQError", "KQ_OK", "KQ_EINVAL", "KQ_ENOTPD", "KQ_EINFEASIBLE", "KQ_EDEVICE", "KQ_EUNSUPPORTED",
     "KQ_BF16", "KQ_F32", "KQ_F64", "KQ_BIIP_INPUT", "KQ_BIIP_OUTPUT", "KQ_BIIP_SCALE", "KQ_BIIP_INVERSE",
     "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
-    "KQ_OP_DECODE", "KQ_DECODE_MAX_TOKENS", "KQ_DECODE_MAX_LAYERS",
+    "KQ_OP_DECODE", "KQ_OP_LOSS", "KQ_DECODE_MAX_TOKENS", "KQ_DECODE_MAX_LAYERS",
     "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
     "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_matvec_group",
-    "decode_matvec_group_noalloc", "decode_workspace", "Rot", "KQ_DECODE_NOALLOC_SCRATCH",
+    "decode_matvec_group_noalloc", "decode_workspace", "kron_loss", "Rot", "KQ_DECODE_NOALLOC_SCRATCH",
     "DecodeLayer",
     "timing_enable", "timing_query",
 ]
@@ -30,7 +30,7 @@ KQ_OK, KQ_EINVAL, KQ_ENOTPD, KQ_EINFEASIBLE, KQ_EDEVICE, KQ_EUNSUPPORTED = range
 KQ_BF16, KQ_F32, KQ_F64 = 0, 1, 2
 KQ_BIIP_INPUT, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_BIIP_INVERSE = 1, 2, 4, 8
 KQ_SCORE_KRONQ, KQ_SCORE_HX_ONLY = 0, 1
-KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS, KQ_OP_DECODE = 0, 1, 2, 3, 4
+KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS, KQ_OP_DECODE, KQ_OP_LOSS = 0, 1, 2, 3, 4, 5
 KQ_DECODE_MAX_TOKENS = 4
 KQ_DECODE_MAX_LAYERS = 4
 KQ_DECODE_NOALLOC_SCRATCH = 2228224
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
     L.kq_cholesky_inv.argtypes = [_VP, _I64, _F32, _VP, _VP, _SZ, _VP]
     L.kq_obs_quantize.argtypes = [_VP, _VP, _I64, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.kq_pack_codes.argtypes = [_VP, _I64, _I64, _I32, _VP, _VP]
+    L.kq_kron_loss.argtypes = [_VP, _VP, _I32, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP]
     L.kq_decode_matvec.argtypes = [_VP, _VP, _VP, _I64, _I64, _I32, _I32, _VP, _VP, ctypes.POINTER(Rot),
                                    ctypes.POINTER(Rot), _VP, _I64, _VP, _VP, _SZ, _VP]
     L.kq_decode_matvec_group.argtypes = [ctypes.POINTER(DecodeLayer), _I32, _I64, _I32, _I32, _VP,
@@ -104,7 +105,7 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(Rot), _VP, _I64, _VP]
     for name in ("kq_accumulate_cov", "kq_sensitivity", "kq_allocate_bits", "kq_biip_rotate",
                  "kq_cholesky_inv", "kq_obs_quantize", "kq_pack_codes", "kq_decode_matvec",
-                 "kq_decode_matvec_group", "kq_decode_matvec_group_noalloc"):
+                 "kq_decode_matvec_group", "kq_decode_matvec_group_noalloc", "kq_kron_loss"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -251,6 +252,26 @@ def obs_quantize(w, r, bits: int, group: int, block: int, codes, scales, zeros, 
     _check(lib().kq_obs_quantize(_ptr(w), _ptr(r), dout, din, bits, group, block, _ptr(codes), _ptr(scales),
                                  _ptr(zeros), _ptr(preround), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)), "kq_obs_quantize")
+
+
+def kron_loss(w_hat, w, h_x, h_g, loss, *, ws=None, stream=None) -> None:
+    """loss[0] <- tr((w_hat - w) h_x (w_hat - w)^T h_g); w_hat float64 [dout, din], w bf16 bits / float32 /
+    float64, h_x / h_g float32, loss a float64 device tensor of one element."""
+    import torch
+    dtypes = {torch.bfloat16: KQ_BF16, torch.int16: KQ_BF16, torch.uint16: KQ_BF16,
+              torch.float32: KQ_F32, torch.float64: KQ_F64}
+    _need(w_hat.dtype == torch.float64 and w_hat.is_contiguous() and w.dtype in dtypes and w.is_contiguous(),
+          "kron_loss: w_hat / w dtype or layout")
+    _need(tuple(w.shape) == tuple(w_hat.shape), "kron_loss: w and w_hat differ in shape")
+    dout, din = w_hat.shape
+    _need(h_x.dtype == torch.float32 and h_g.dtype == torch.float32 and h_x.is_contiguous() and h_g.is_contiguous()
+          and tuple(h_x.shape) == (din, din) and tuple(h_g.shape) == (dout, dout), "kron_loss: covariances")
+    _need(loss.dtype == torch.float64 and loss.numel() >= 1, "kron_loss: loss must be float64")
+    need = workspace_size(KQ_OP_LOSS, dout, din)
+    if ws is None:
+        ws = _scratch(need, w_hat.device)
+    _check(lib().kq_kron_loss(_ptr(w_hat), _ptr(w), dtypes[w.dtype], dout, din, _ptr(h_x), _ptr(h_g), _ptr(loss),
+                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "kq_kron_loss")
 
 
 def pack_codes(codes, bits: int, packed, *, stream=None) -> None:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
 SOURCES = ["kq_api.hip", "timing.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip",
-           "decode.hip"]
+           "decode.hip", "loss.hip"]
 ARCH = "gfx950"
 
 

@@ -105,6 +105,9 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2) {
     case KQ_OP_OBS:
       if (d0 < 1 || d1 < 1 || d2 < 1 || d1 > kMaxDim) return bad;
       return kq::obs_workspace(d0, d1, static_cast<int>(d2));
+    case KQ_OP_LOSS:
+      if (d0 < 1 || d1 < 1 || d0 > kMaxDim || d1 > kMaxDim) return bad;
+      return kq::loss_workspace(d0, d1);
     case KQ_OP_DECODE:
       if (d0 < 1 || d0 > int64_t(KQ_DECODE_MAX_LAYERS) * KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_MAX_ROT_DIM || d2 < 1 ||
           d2 > KQ_DECODE_MAX_TOKENS)
@@ -224,6 +227,17 @@ kq_status kq_obs_quantize(double* w, const float* r, int64_t dout, int64_t din, 
     return fail(KQ_EUNSUPPORTED, "kq_obs_quantize: block %d (supported: 32, 64, 128)", block);
   if (!ws_ok(ws, ws_bytes, kq::obs_workspace(dout, din, block))) return KQ_EINVAL;
   return kq::obs_run(w, r, dout, din, bits, group, block, codes, scales, zeros, preround, ws, kq::as_stream(stream));
+}
+
+kq_status kq_kron_loss(const double* w_hat, const void* w, int32_t w_dtype, int64_t dout, int64_t din,
+                       const float* h_x, const float* h_g, double* loss, void* ws, size_t ws_bytes, void* stream) {
+  if (!w_hat || !w || !h_x || !h_g || !loss) return fail(KQ_EINVAL, "kq_kron_loss: NULL pointer");
+  if (dout < 1 || din < 1 || dout > kMaxDim || din > kMaxDim)
+    return fail(KQ_EINVAL, "kq_kron_loss: shape %lld x %lld", (long long)dout, (long long)din);
+  if (w_dtype != KQ_BF16 && w_dtype != KQ_F32 && w_dtype != KQ_F64)
+    return fail(KQ_EINVAL, "kq_kron_loss: w_dtype %d", w_dtype);
+  if (!ws_ok(ws, ws_bytes, kq::loss_workspace(dout, din))) return KQ_EINVAL;
+  return kq::loss_run(w_hat, w, w_dtype, dout, din, h_x, h_g, loss, ws, kq::as_stream(stream));
 }
 
 kq_status kq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* packed,

@@ -69,6 +69,11 @@ kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits
                   uint8_t* codes, float* scales, uint8_t* zeros, double* preround, void* ws,
                   hipStream_t st);
 
+// Kronecker layer loss (loss.hip)
+size_t loss_workspace(int64_t dout, int64_t din);
+kq_status loss_run(const double* w_hat, const void* w, int w_dtype, int64_t dout, int64_t din, const float* h_x,
+                   const float* h_g, double* loss, void* ws, hipStream_t st);
+
 // packed codes and the decode matvec (decode.hip)
 int container_bits(int bits);
 int decode_cpl(int64_t din, int64_t tokens);

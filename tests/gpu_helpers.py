@@ -47,14 +47,19 @@ def rel_fro(got: np.ndarray, want: np.ndarray) -> float:
 
 
 def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_frac=1e-4, scale_rtol=1e-5,
-                label=""):
+                label="", block=None):
     """Code parity: replay the oracle's sweep on (w2, r), adopting the kernel's
     code or zero only where the rounding argument is within ``window`` of a
     midpoint and the kernel chose the neighbouring value. Every other entry must
-    agree exactly. Adopted codes may be at most ``max_frac`` of all codes and
+    agree exactly (``block``: the oracle's lazy-batched sweep, equal to the
+    column-by-column one). Adopted codes may be at most ``max_frac`` of all codes and
     adopted zero points at most ``max_frac`` of all zero points (rounded down:
     no adoption at all below 1 / max_frac entries)."""
-    res = oracle.obs_quantize(w2, r, bits, group, adopt_codes=codes, adopt_zeros=zeros, window=window)
+    if block:  # lazy-batched replay (equal to the column-by-column one; affordable for long rows)
+        res = oracle.obs_quantize_blocked(w2, r, bits, group, block, adopt_codes=codes, adopt_zeros=zeros,
+                                          window=window)
+    else:
+        res = oracle.obs_quantize(w2, r, bits, group, adopt_codes=codes, adopt_zeros=zeros, window=window)
     n, nz = codes.size, zeros.size
     print(f"{label}: {res.adopted_codes} tie-window codes of {n}, {res.adopted_zeros} zero points of {nz}",
           flush=True)

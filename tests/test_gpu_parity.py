@@ -283,8 +283,11 @@ def _run_layer(wl, sub, group_key, flags=None, bits=None):
     out = pipeline.quantize_layer(wd, hxd, hgd, ri, ro, bits=bits, group=cfg.group, block=cfg.block,
                                   damp=cfg.damp, flags=flags)
     torch.cuda.synchronize()
+    loss = torch.empty(1, dtype=torch.float64, device=DEV)
+    kq.kron_loss(out.w_hat, wd, hxd, hgd, loss)  # the raw covariances: quantize_layer worked on copies
     return dict(hx=host(hxd), hg=host(hgd), score=score, codes=host(out.codes), scales=host(out.scales),
-                zeros=host(out.zeros), r=host(out.hx2), w_hat=host(out.w_hat), bits=bits)
+                zeros=host(out.zeros), r=host(out.hx2), w_hat=host(out.w_hat), bits=bits,
+                loss=float(loss.item()))
 
 
 def _check_layer(wl, sub, group_key, got, flags=(True, True, True), scale_rtol=1e-5):
@@ -305,6 +308,8 @@ def _check_layer(wl, sub, group_key, got, flags=(True, True, True), scale_rtol=1
     want_loss = oracle.kron_loss(w_hat - w64, hx, hg)
     got_loss = oracle.kron_loss(got["w_hat"] - w64, hx, hg)
     assert got_loss == pytest.approx(want_loss, rel=1e-3)
+    # the GPU's own loss kernel on the GPU's covariances and W^
+    assert got["loss"] == pytest.approx(want_loss, rel=1e-3)
     return res, want_loss
 
 
@@ -372,3 +377,75 @@ def test_block_allocation_config5_scaled():
     n = [s.dout * s.din for s in cfg.subs]
     plan = kq.allocate_bits(gpu_scores, n, cfg.alloc_choices, cfg.alloc_target_millibits)
     assert plan == oracle.allocate_bits(ora_scores, n, cfg.alloc_choices, cfg.alloc_target_millibits)
+
+
+# ---------------------------------------------------------------------------
+# validation: the Kronecker loss kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dout,din,wdt", [(64, 128, "f32"), (100, 200, "bf16"), (257, 130, "f64"), (1, 1, "f32"),
+                                          (384, 1000, "bf16"), (63, 65, "f64")])
+def test_kron_loss(dout, din, wdt):
+    """tr(dW H_X dW^T H_G) against the oracle on the same stored values (several 64 x 64 tiles, ragged
+    edges, every weight type); run twice, bit-identical (fixed-order sums)."""
+    import torch
+    kq, _ = _kq()
+    rng = np.random.default_rng(dout * 1000 + din)
+    hx = _spd(rng, din, 2.0).astype(np.float32)
+    hg = _spd(rng, dout, 2.0).astype(np.float32)
+    w = rng.normal(0, 0.02, (dout, din))
+    w_hat = w + rng.normal(0, 0.005, (dout, din))
+    if wdt == "bf16":
+        wb = kq_synth.f32_to_bf16_bits(w.astype(np.float32))
+        wd, w_eff = bits_to_dev(wb), kq_synth.bf16_bits_to_f64(wb)
+    elif wdt == "f32":
+        wd, w_eff = to_dev(w.astype(np.float32)), w.astype(np.float32).astype(np.float64)
+    else:
+        wd, w_eff = to_dev(w), w
+    want = oracle.kron_loss(w_hat - w_eff, hx.astype(np.float64), hg.astype(np.float64))
+    loss = torch.empty(2, dtype=torch.float64, device=DEV)
+    for i in range(2):
+        kq.kron_loss(to_dev(w_hat), wd, to_dev(hx), to_dev(hg), loss[i:i + 1])
+    got = host(loss)
+    print(f"kron_loss {dout}x{din} {wdt}: {got[0]:.15g} (oracle {want:.15g})", flush=True)
+    assert got[0] == got[1]
+    assert got[0] == pytest.approx(want, rel=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# failure reporting and determinism
+# ---------------------------------------------------------------------------
+def test_nan_in_x_is_reported_not_quantized():
+    """A NaN in the calibration activations reaches the covariance, the score and the factor: the
+    score is not finite, the allocation refuses it (KQ_EINVAL) and the Cholesky factor reports a bad
+    pivot (info != 0), so the layer path raises instead of producing codes."""
+    import torch
+    kq, pipeline = _kq()
+    wl = _workload(2, 3000, {"q_proj": (128, 256)})
+    x = wl.x("attn_in").copy()
+    x[1234, 77] = 0x7FC0  # bf16 quiet NaN
+    hxd = pipeline.covariance(bits_to_dev(x))
+    hgd = pipeline.covariance(bits_to_dev(wl.g("q_proj")))
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(hxd[77]).all()) and not bool(torch.isnan(hxd[76, :76]).any())
+    score = pipeline.score(hxd, hgd)
+    assert not np.isfinite(score)
+    with pytest.raises(kq.KQError) as e:
+        kq.allocate_bits([score, 1.0], [128 * 256, 128 * 256], [2, 3, 4], 3000)
+    assert e.value.status == kq.KQ_EINVAL
+    si, so = wl.rot_in("attn_in"), wl.rot_out("q_proj")
+    ri, ro = pipeline.upload_rot(si.signs, si.q, DEV), pipeline.upload_rot(so.signs, so.q, DEV)
+    with pytest.raises(kq.KQError) as e:
+        pipeline.quantize_layer(bits_to_dev(wl.weight("q_proj")), hxd, hgd, ri, ro, bits=2, group=128, block=128,
+                                damp=0.01)
+    assert e.value.status == kq.KQ_ENOTPD
+
+
+def test_layer_runs_twice_bit_identical():
+    """The whole layer path twice on the same inputs: covariances, R, codes, scales, zero points, W^ and
+    the loss are bit-identical (every reduction has a fixed order)."""
+    wl = _workload(2, 20000, {"q_proj": (256, 512)})
+    a = _run_layer(wl, "q_proj", "attn_in", bits=2)
+    b = _run_layer(wl, "q_proj", "attn_in", bits=2)
+    for k in ("hx", "hg", "r", "codes", "scales", "zeros", "w_hat"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    assert a["score"] == b["score"] and a["loss"] == b["loss"]

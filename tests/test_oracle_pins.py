@@ -615,3 +615,31 @@ def test_replay_adopts_a_zero_point_inside_the_window():
     zz[far[0], 0] = zz[far[0], 0] - 1 if zz[far[0], 0] > 0 else zz[far[0], 0] + 1
     rep2 = oracle.obs_quantize(w, r, bits, 0, adopt_codes=plain.codes, adopt_zeros=zz)
     assert (rep2.mismatches, rep2.adopted_zeros) == (1, 0)
+
+
+def test_replay_blocked_equals_unblocked():
+    """The blocked sweep's replay (used where rows are thousands of columns long) adopts the same
+    tie-window codes and zero points, and rejects the same flips, as the unblocked one (P8 with
+    the replay switched on)."""
+    w, r, bits, (i, j), base = _replay_case()
+    own = int(base.codes[i, j])
+    forced, _ = _forced_sweep(w, r, bits, codes_at={(i, j): own - 1})
+    for block in (8, 12, 24):
+        a = oracle.obs_quantize(w, r, bits, 0, adopt_codes=forced, adopt_zeros=base.zeros)
+        b = oracle.obs_quantize_blocked(w, r, bits, 0, block, adopt_codes=forced, adopt_zeros=base.zeros)
+        assert (b.mismatches, b.adopted_codes, b.adopted_zeros) == (a.mismatches, a.adopted_codes, a.adopted_zeros)
+        np.testing.assert_array_equal(a.codes, b.codes)
+        np.testing.assert_allclose(b.t, a.t, rtol=0, atol=1e-9)
+        other = base.codes.copy()
+        other[0, 3] = (other[0, 3] + 1) % (1 << bits)
+        if abs(base.t[0, 3] - np.floor(base.t[0, 3]) - 0.5) > 1e-3:
+            c = oracle.obs_quantize_blocked(w, r, bits, 0, block, adopt_codes=other, adopt_zeros=base.zeros)
+            assert c.mismatches == 1
+    # with groups that start inside blocks
+    rng = np.random.default_rng(3)
+    w2 = rng.normal(0, 0.02, (10, 64))
+    r2 = oracle.chol_inv_upper(_spd(rng, 64, 1.0), 0.01)
+    plain = oracle.obs_quantize(w2, r2, 3, 16)
+    blk = oracle.obs_quantize_blocked(w2, r2, 3, 16, 32, adopt_codes=plain.codes, adopt_zeros=plain.zeros)
+    assert (blk.mismatches, blk.adopted_codes) == (0, 0)
+    np.testing.assert_array_equal(blk.codes, plain.codes)

@@ -1,31 +1,37 @@
 #!/usr/bin/env python3
 """Throughput of the KronQ per-layer quantization path on one MI355X.
 
-One step is one pass of the whole path over one layer whose inputs are
-already resident in HBM:
-  1. H_X = X^T X / N and H_G = G^T G / N (bf16-MFMA symmetric rank-k updates
-     over all N tokens),
-  2. the trace score tr(H_G) tr(H_X) and the bit allocation from it,
+One step is one pass of the whole path over every layer of a workload whose
+inputs are already resident in HBM:
+  1. H_X = X^T X / N of every input group and H_G = G^T G / N of every layer
+     (bf16-MFMA symmetric rank-k updates over all N tokens),
+  2. the trace scores tr(H_G) tr(H_X) and the bit allocation from them,
   3. BiIP (diagonal rescale + randomised Hadamard rotation on both sides of W,
      with H_X and H_G transformed alongside),
   4. the damped Cholesky factor of H_X''^-1,
   5. the column-wise OBS sweep with its lazy-batch trailing products.
-Workload: LLaMA-2-7B q_proj shapes (W 4096 x 4096 bf16; X and G 262144 x 4096
-bf16, 128 sequences of 2048 tokens), 2-bit, group 128, block 128, damping
-0.01, seeded synthetic inputs.
+Default workload (--config 4): the LLaMA-3-70B down_proj (W 8192 x 28672 bf16
+with input-column outliers, column-norm CV 9.2; X 262144 x 28672 and G
+262144 x 8192 bf16), 2-bit, group 128, block 128, damping 0.01: the largest
+workload that fits one GPU. --config 1, 2, 3 and 5 run the 64 x 128 linear
+layer, the LLaMA-2-7B q_proj (--bits 2 or 4), the LLaMA-2-13B MLP (gate, up,
+down at 3 bits) and the LLaMA-3-8B block (seven layers, bits from the
+allocation over {2, 3, 4} at 3.0 average bits). Seeded synthetic inputs.
 
-Schedule: the Cholesky factor needs only H_X'' (the input side of BiIP), so
-by default it runs on one stream while the H_G covariance runs on a second
-stream that is kept off some CUs, which stay free for the latency-bound factor
-steps; the output side of BiIP and the sweep follow on the first stream with
-every CU. `--serial` puts every stage on one stream.
+Schedule: for one layer the Cholesky factor needs only H_X'' (the input side
+of BiIP), so it runs on one stream while the H_G covariance runs on a second
+stream kept off some CUs; the output side of BiIP and the sweep follow with
+every CU. Several layers (or --serial) run on one stream: all covariances,
+the scores and the allocation (the sweeps' widths depend on it), then per
+layer BiIP, the factor and the sweep.
 
 value = weights quantised per second, end to end including the covariance
-accumulation. The roofline object covers the dominant kernel, the bf16 MFMA
-SYRK (syrk_partial): algorithmic flops N d (d + 1) per covariance over the
-summed durations of its launches, timed with HIP events that the library
-records around each launch on its stream. The CPU baseline is the float64
-oracle timed on a bounded sample of the same workload on this host.
+accumulation. The roofline object covers the kernel with the most time in the
+step (bf16-MFMA SYRK, float32-MFMA Cholesky steps or float64-MFMA sweep
+steps): its algorithmic flops per launch over its average launch duration,
+timed with HIP events that the library records around each launch on its
+stream during the timed steps. The CPU baseline is the float64 oracle timed
+on a bounded sample of the same workload on this host, scaled to one step.
 """
 from __future__ import annotations
 
@@ -35,9 +41,7 @@ import os
 import sys
 import time
 
-BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3   # MI355X float32 (vector and matrix)
-FP64_PEAK_TFLOPS = 78.6    # MI355X float64 MFMA
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 
 
 def parse_args():
@@ -45,14 +49,15 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--bits", type=int, default=2, choices=(2, 4))
+    p.add_argument("--config", type=int, default=4, choices=(1, 2, 3, 4, 5),
+                   help="workload: 1 linear 64x128, 2 LLaMA-2-7B q_proj, 3 LLaMA-2-13B MLP, 4 LLaMA-3-70B down_proj "
+                        "(default), 5 LLaMA-3-8B block")
+    p.add_argument("--bits", type=int, default=2, choices=(2, 4), help="bit width of the LLaMA-2-7B q_proj (--config 2)")
     p.add_argument("--serial", action="store_true",
                    help="run every stage on one stream (per-stage profiles) instead of the two-stream schedule")
     p.add_argument("--reserve-cus", type=int, default=80,
                    help="CUs the second stream leaves to the Cholesky factor (0: no CU mask)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
-    p.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's covariance sample")
-    p.add_argument("--cpu-rows", type=int, default=64, help="weight rows in the oracle's sweep sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, copy 1 GiB device-to-device (a reference kernel for HBM byte counters)")
     p.add_argument("--decode", action="store_true",
@@ -61,9 +66,10 @@ def parse_args():
                    help="calibration capture of one LLaMA-2-7B block (forward + one backward) and its covariances")
     p.add_argument("--decode-per-layer", action="store_true",
                    help="with --decode: one kq_decode_matvec call per layer instead of one group call per shared input")
-    p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+    p.add_argument("--traffic-summary", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
                    help="no run: turn two rocprofv3 --pmc runs of '--copy-calibration' (FETCH_SIZE, then "
-                        "WRITE_SIZE) into the per-launch HBM bytes of the roofline kernel")
+                        "WRITE_SIZE) into the per-launch HBM bytes of KERNEL, written to "
+                        "profiles/KERNEL_WORKLOAD_hbm_traffic.json")
     return p.parse_args()
 
 
@@ -122,48 +128,103 @@ def cpu_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(wl, cfg, sub, bits, tokens, rows):
-    """The float64 oracle on a bounded sample, scaled to one full layer."""
+def cpu_baseline(wl, cfg, bits_plan):
+    """The float64 oracle, as it stands, on a bounded sample of the workload, scaled to one whole step.
+
+    Per step of the workload the oracle would: form every covariance over all tokens, score and
+    allocate, run BiIP, the Cholesky factor of the inverse and the column sweep of every layer. The
+    sample times each piece on a slice whose cost scales in a known way: covariances on a token slice
+    (cost linear in tokens), BiIP on a layer shrunk by a factor (cost in the bytes of W, H_X and H_G),
+    the factor at width <= 4096 (cost d^3), the sweep on a few rows (cost linear in rows). The sample
+    takes 10-30 s of host time."""
     import numpy as np
+
+    import kq_synth
     import oracle
 
+    def biip_work(dout, din):
+        # the oracle rotates with the dense Hadamard matrix: k rows of n = m p cost k n (p + m)
+        (mi, ki), (mo, ko) = kq_synth.split_odd(din), kq_synth.split_odd(dout)
+        ci, co = (1 << ki) + mi, (1 << ko) + mo
+        return dout * din * (ci + co) + 2 * din * din * ci + 2 * dout * dout * co
+
+    t_total, notes = 0.0, []
     n_tok = cfg.n_tokens
+    tok = min(n_tok, 2048)
+    # covariances: every X group and every G on `tok` tokens, scaled to n_tok
     t0 = time.perf_counter()
-    hx = oracle.covariance([wl.x("attn_in")[:tokens]])
-    hg = oracle.covariance([wl.g(sub.name)[:tokens]])
-    t_cov = (time.perf_counter() - t0) * (n_tok / tokens)
-    t0 = time.perf_counter()
-    s = oracle.sensitivity(hx, hg)
-    oracle.allocate_bits([s], [sub.dout * sub.din], [bits], bits * 1000)
-    t_score = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    w2, hx2, _, _, _ = oracle.biip_forward(wl.weight_f64(sub.name), hx, hg, wl.rot_in("attn_in"),
-                                           wl.rot_out(sub.name))
-    t_biip = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    r = oracle.chol_inv_upper(hx2, cfg.damp)
-    t_chol = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.obs_quantize(w2[:rows], r, bits, cfg.group)
-    t_obs = (time.perf_counter() - t0) * (sub.dout / rows)
-    total = t_cov + t_score + t_biip + t_chol + t_obs
+    for grp in cfg.x_groups:
+        oracle.covariance([wl.x_chunk(grp, 0)[:tok]])
+    for s in cfg.subs:
+        oracle.covariance([wl.g_chunk(s.name, 0)[:tok]])
+    t = (time.perf_counter() - t0) * (n_tok / tok)
+    t_total += t
+    notes.append(f"covariances on {tok} of {n_tok} tokens (x{n_tok / tok:g}) {t:.1f} s")
+    t_biip = t_chol = t_obs = 0.0
+    chol_seen = {}
+    for li, s in enumerate(cfg.subs):
+        # BiIP on a layer shrunk by f on each side (bytes scale by f^2)
+        f = 1
+        while s.dout // (2 * f) >= 512 and s.din // (2 * f) >= 512 and (s.dout // (2 * f)) % 2 == 0 \
+                and (s.din // (2 * f)) % 2 == 0:
+            f *= 2
+        do, di = s.dout // f, s.din // f
+        rng = np.random.default_rng(li)
+        hx = np.eye(di) + 0.01
+        hg = np.eye(do) + 0.01
+        w = rng.normal(0, 0.02, (do, di))
+        si, so = kq_synth.rot_spec(99, f"cpu{di}", di), kq_synth.rot_spec(99, f"cpuo{do}", do)
+        t0 = time.perf_counter()
+        w2, hx2, _, _, _ = oracle.biip_forward(w, hx, hg, si, so)
+        tb = (time.perf_counter() - t0) * (biip_work(s.dout, s.din) / biip_work(do, di))
+        t_biip += tb
+        # the factor: at min(din, 4096), scaled by d^3; once per input group of equal width
+        dc = min(s.din, 4096)
+        if dc not in chol_seen:
+            h = np.eye(dc) + rng.standard_normal((dc, dc)) * 1e-3
+            h = h @ h.T
+            t0 = time.perf_counter()
+            oracle.chol_inv_upper(h, cfg.damp)
+            chol_seen[dc] = time.perf_counter() - t0
+        t_chol += chol_seen[dc] * (s.din / dc) ** 3
+        # the sweep on 4 rows of the full width (an identity factor costs the same as any other)
+        rows = 4
+        r = np.eye(s.din)
+        t0 = time.perf_counter()
+        oracle.obs_quantize_blocked(rng.normal(0, 0.02, (rows, s.din)), r, bits_plan[li], cfg.group, cfg.block)
+        t_obs += (time.perf_counter() - t0) * (s.dout / rows)
+        del r
+    t_total += t_biip + t_chol + t_obs
+    notes.append(f"BiIP on layers shrunk to >= 512 per side (x the oracle's rotation work) {t_biip:.1f} s")
+    notes.append(f"Cholesky factor of the inverse at width <= 4096 (x d^3) {t_chol:.1f} s")
+    notes.append(f"column sweep on 4 rows (x rows) {t_obs:.1f} s")
+    weights = sum(s.dout * s.din for s in cfg.subs)
     return {
-        "value": round(sub.dout * sub.din / total / 1e6, 4),
+        "value": round(weights / t_total / 1e6, 5),
         "unit": "Mweights/s",
         "cores": cpu_threads(),
         "kind": "oracle",
-        "sample": (f"float64 oracle: covariances over {tokens} of {n_tok} tokens (x{n_tok / tokens:g}), "
-                   f"OBS sweep on {rows} of {sub.dout} rows (x{sub.dout / rows:g}), BiIP, Cholesky and score "
-                   f"at full size; seconds per layer {total:.1f}"),
-        "seconds_per_layer": round(total, 2),
+        "sample": "float64 oracle, scaled to one step: " + "; ".join(notes) + f"; total {t_total:.1f} s per step",
+        "seconds_per_step": round(t_total, 2),
     }
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-ROOFLINE_KERNEL = "syrk_partial"
-ROOFLINE_SOURCE = os.path.join(ROOT, "post_quantization_04_amd", "csrc", "syrk.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_partial_llama2-7b_q_proj_hbm_traffic.json")
 COPY_BYTES = 1 << 30
+# kernel -> (source file, peak, unit, bound)
+KERNELS = {
+    "syrk_partial": ("syrk.hip", 2500.0, "TFLOP/s", "mfma"),
+    "chol_step_kernel": ("chol.hip", 157.3, "TFLOP/s", "mfma"),
+    "obs_step_kernel": ("obs.hip", 78.6, "TFLOP/s", "mfma"),
+}
+
+
+def kernel_source(kernel: str) -> str:
+    return os.path.join(ROOT, "post_quantization_04_amd", "csrc", KERNELS[kernel][0])
+
+
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
 
 
 def source_hash(path: str) -> str:
@@ -191,19 +252,20 @@ def pmc_dispatches(run_dir: str, counter: str):
     return [(k, names[k], vals[k]) for k in sorted(vals)]
 
 
-def traffic_summary(fetch_dir: str, write_dir: str, out_json: str) -> int:
-    """HBM bytes per launch of the roofline kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by what the same counter reads for the final 1 GiB device-to-device copy."""
-    out = {"kernel": ROOFLINE_KERNEL, "source": os.path.relpath(ROOFLINE_SOURCE, ROOT),
-           "source_sha256": source_hash(ROOFLINE_SOURCE), "copy_bytes": COPY_BYTES}
+def traffic_summary(kernel: str, workload: str, fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per launch of `kernel`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
+    the same counter reads for the final 1 GiB device-to-device copy of a '--copy-calibration' run."""
+    src = kernel_source(kernel)
+    out = {"kernel": kernel, "workload": workload, "source": os.path.relpath(src, ROOT),
+           "source_sha256": source_hash(src), "copy_bytes": COPY_BYTES}
     for key, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = pmc_dispatches(run_dir, counter)
         copy = rows[-1]  # the calibration copy is the last dispatch of the run
-        if "syrk" in copy[1] or copy[2] <= 0:
+        if kernel in copy[1] or copy[2] <= 0:
             raise RuntimeError(f"{counter}: last dispatch {copy[1]!r} is not the calibration copy")
-        mine = [v for _, n, v in rows if f"::{ROOFLINE_KERNEL}(" in n or n.startswith(f"{ROOFLINE_KERNEL}(")]
+        mine = [v for _, n, v in rows if f"{kernel}(" in n or f"{kernel}<" in n]
         if not mine:
-            raise RuntimeError(f"{counter}: no {ROOFLINE_KERNEL} dispatch")
+            raise RuntimeError(f"{counter}: no {kernel} dispatch")
         scale = COPY_BYTES / (copy[2] * 1024.0)
         out[f"{key}_kib_per_launch"] = sum(mine) / len(mine)
         out[f"{key}_launches"] = len(mine)
@@ -211,20 +273,21 @@ def traffic_summary(fetch_dir: str, write_dir: str, out_json: str) -> int:
         out[f"{key}_scale"] = scale
         out[f"{key}_bytes_per_launch"] = out[f"{key}_kib_per_launch"] * 1024.0 * scale
     out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
-    with open(out_json, "w") as f:
+    path = traffic_file(kernel, workload)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
     return 0
 
 
-def stored_traffic():
-    """Per-launch HBM bytes of the roofline kernel from the committed counter summary, or None when the
-    summary is missing or was taken on a different version of the kernel's source."""
+def stored_traffic(kernel: str, workload: str):
+    """Per-launch HBM bytes of `kernel` from the committed counter summary, or None when the summary is
+    missing or was taken on a different version of the kernel's source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel, workload)) as f:
             rec = json.load(f)
-        if rec.get("source_sha256") != source_hash(ROOFLINE_SOURCE):
+        if rec.get("source_sha256") != source_hash(kernel_source(kernel)):
             return None
         return int(round(rec["traffic_bytes_per_launch"]))
     except (OSError, ValueError, KeyError):
@@ -237,7 +300,6 @@ DECODE_LAYERS = [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096
 # layers of a block that read the same input (and so share the input side): (din, [layer indices])
 DECODE_GROUPS = [(4096, [0, 1, 2]), (4096, [3]), (4096, [4, 5]), (11008, [6])]
 DECODE_BLOCKS = 32
-HBM_PEAK_GBS = 8000.0
 
 
 def capture_bench(args) -> int:
@@ -435,20 +497,15 @@ def decode_bench(args) -> int:
     return 0
 
 
-def main() -> int:
-    args = parse_args()
-    if args.traffic_summary:
-        return traffic_summary(*args.traffic_summary)
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU; the path's multi-GPU sharding is design only, "
-                                   "so --gpus must be 1"}))
-        return 2
-    if args.decode:
-        return decode_bench(args)
-    if args.capture:
-        return capture_bench(args)
+WORKLOAD_TAG = {1: "linear64x128", 2: "llama2-7b_q_proj", 3: "llama2-13b_mlp", 4: "llama3-70b_down_proj",
+                5: "llama3-8b_block"}
+TIMED_KERNELS = ("syrk_partial", "chol_step_kernel", "obs_step_kernel", "row_fwht", "col_fwht", "col_mix")
 
+
+def quant_bench(args) -> int:
+    """One step = the whole path over every layer of the workload: covariances of every input group
+    and every output gradient, scores and the bit allocation, then BiIP, the Cholesky factor of the
+    damped inverse and the column sweep of every layer. Inputs are resident in HBM before timing."""
     import numpy as np
     import torch
 
@@ -458,185 +515,224 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.zeros(1, device=dev)
+    cfg = kq_synth.config(args.config)
+    single = len(cfg.subs) == 1
+    overlap = single and not args.serial
     # created before anything else takes a hardware queue: a CU-masked stream needs its own
-    side = None if args.serial else side_stream(dev, args.reserve_cus)
-    cfg = kq_synth.config(2)
-    sub = cfg.subs[0]
-    dout, din, n_tok = sub.dout, sub.din, cfg.n_tokens
+    side = side_stream(dev, args.reserve_cus) if overlap else None
     wl = kq_synth.Workload(cfg)
-
+    n_tok = cfg.n_tokens
     log(f"libkq {kq.version()}; generating {cfg.name} inputs")
     t0 = time.perf_counter()
-    x = wl.x("attn_in")
-    g = wl.g(sub.name)
-    w = wl.weight(sub.name)
-    si, so = wl.rot_in("attn_in"), wl.rot_out(sub.name)
-    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
-    xd = torch.from_numpy(x.view(np.int16)).to(dev)
-    gd = torch.from_numpy(g.view(np.int16)).to(dev)
-    wd = torch.from_numpy(w.view(np.int16)).to(dev)
-    ri, ro = pipeline.upload_rot(si.signs, si.q, dev), pipeline.upload_rot(so.signs, so.q, dev)
-
     f32, f64 = torch.float32, torch.float64
-    hx = torch.empty((din, din), dtype=f32, device=dev)
-    hg = torch.empty((dout, dout), dtype=f32, device=dev)
-    score = torch.empty(1, dtype=f64, device=dev)
-    w2 = torch.empty((dout, din), dtype=f64, device=dev)
-    s_x = torch.empty(din, dtype=f64, device=dev)
-    s_g = torch.empty(dout, dtype=f64, device=dev)
-    info = torch.zeros(1, dtype=torch.int32, device=dev)
-    codes = torch.empty((dout, din), dtype=torch.uint8, device=dev)
-    ng = din // cfg.group
-    scales = torch.empty((dout, ng), dtype=f32, device=dev)
-    zeros = torch.empty((dout, ng), dtype=torch.uint8, device=dev)
+
+    def bits_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    xs = {}
+    for grp in cfg.x_groups:
+        xs[grp] = bits_dev(wl.x(grp))
+        wl.drop("x", grp)
+    gs, ws_, rots_in, rots_out = {}, {}, {}, {}
+    for s in cfg.subs:
+        gs[s.name] = bits_dev(wl.g(s.name))
+        wl.drop("g", s.name)
+        w = wl.weight(s.name)
+        ws_[s.name] = bits_dev(w) if w.dtype == np.uint16 else torch.from_numpy(w).to(dev)
+        so = wl.rot_out(s.name)
+        rots_out[s.name] = pipeline.upload_rot(so.signs, so.q, dev)
+    for grp in cfg.x_groups:
+        si = wl.rot_in(grp)
+        rots_in[grp] = pipeline.upload_rot(si.signs, si.q, dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM after {time.perf_counter() - t0:.1f} s")
 
     def scratch(n):
         return torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
 
-    ws_cov = scratch(max(kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, din),
-                         kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, dout)))
-    ws_biip = scratch(kq.workspace_size(kq.KQ_OP_BIIP, dout, din))
-    ws_chol = scratch(kq.workspace_size(kq.KQ_OP_CHOLESKY, din))
-    ws_obs = scratch(kq.workspace_size(kq.KQ_OP_OBS, dout, din, cfg.block))
-    flags = pipeline.ALL_SIDES
-    stages = ["cov_x", "cov_g", "score_alloc", "biip", "cholesky", "obs"]
-    # two-stream schedule: the Cholesky factor needs only H_X'' (input side), so it runs next
-    # to the G covariance; the output side of BiIP follows on the second stream
-    w1 = torch.empty((dout, din), dtype=f64, device=dev)
-    score_x = torch.empty(1, dtype=f64, device=dev)
-    score_g = torch.empty(1, dtype=f64, device=dev)
-    score_host = torch.empty(2, dtype=f64, pin_memory=True)
-    s_unused_x = torch.empty(din, dtype=f64, device=dev)
-    s_unused_g = torch.empty(dout, dtype=f64, device=dev)
-    in_flags = kq.KQ_BIIP_INPUT | kq.KQ_BIIP_SCALE
-    out_flags = kq.KQ_BIIP_OUTPUT | kq.KQ_BIIP_SCALE
+    widths_all = list(cfg.x_groups.values()) + [s.dout for s in cfg.subs]
+    ws_cov = scratch(max(kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, d) for d in widths_all))
+    ws_biip = scratch(max(kq.workspace_size(kq.KQ_OP_BIIP, s.dout, s.din) for s in cfg.subs))
+    ws_chol = scratch(max(kq.workspace_size(kq.KQ_OP_CHOLESKY, s.din) for s in cfg.subs))
+    ws_obs = scratch(max(kq.workspace_size(kq.KQ_OP_OBS, s.dout, s.din, cfg.block) for s in cfg.subs))
+    hx_raw = {grp: torch.empty((d, d), dtype=f32, device=dev) for grp, d in cfg.x_groups.items()}
+    hg = {s.name: torch.empty((s.dout, s.dout), dtype=f32, device=dev) for s in cfg.subs}
+    lay = {}
+    for s in cfg.subs:
+        ng = s.din // cfg.group if cfg.group else 1
+        lay[s.name] = dict(
+            hx=torch.empty((s.din, s.din), dtype=f32, device=dev),
+            w1=torch.empty((s.dout, s.din), dtype=f64, device=dev),
+            w2=torch.empty((s.dout, s.din), dtype=f64, device=dev),
+            s_x=torch.empty(s.din, dtype=f64, device=dev), s_g=torch.empty(s.dout, dtype=f64, device=dev),
+            s_u=torch.empty(max(s.din, s.dout), dtype=f64, device=dev),
+            codes=torch.empty((s.dout, s.din), dtype=torch.uint8, device=dev),
+            scales=torch.empty((s.dout, ng), dtype=f32, device=dev),
+            zeros=torch.empty((s.dout, ng), dtype=torch.uint8, device=dev),
+            info=torch.zeros(1, dtype=torch.int32, device=dev))
+    score_dev = torch.empty(2 * len(cfg.subs), dtype=f64, device=dev)
+    score_host = torch.empty(2 * len(cfg.subs), dtype=f64, pin_memory=True)
+    n_params = [s.dout * s.din for s in cfg.subs]
+    if cfg.alloc_choices:
+        choices, target = list(cfg.alloc_choices), cfg.alloc_target_millibits
+    else:  # one width for every layer (the 7B q_proj at --bits): the allocation has one choice
+        width = args.bits if cfg.id == 2 else cfg.subs[0].bits
+        choices, target = [width], width * 1000
+    in_flags, out_flags = kq.KQ_BIIP_INPUT | kq.KQ_BIIP_SCALE, kq.KQ_BIIP_OUTPUT | kq.KQ_BIIP_SCALE
+    plan_box = {}
 
-    def step_serial(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-        mark(0)
-        kq.accumulate_cov(xd, hx, 1.0 / n_tok, 0.0, ws=ws_cov)
-        mark(1)
-        kq.accumulate_cov(gd, hg, 1.0 / n_tok, 0.0, ws=ws_cov)
-        mark(2)
-        kq.sensitivity(hx, hg, score)
-        bits = kq.allocate_bits([float(score.item())], [dout * din], [args.bits], args.bits * 1000)[0]
-        mark(3)
-        kq.biip_rotate(wd, w2, hx, hg, ri.rot, ro.rot, flags, s_x, s_g, ws=ws_biip)
-        mark(4)
-        kq.cholesky_inv(hx, cfg.damp, info, ws=ws_chol)
-        mark(5)
-        kq.obs_quantize(w2, hx, bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
-        mark(6)
+    def allocate(scores):
+        return kq.allocate_bits(scores, n_params, choices, target)
 
-    # the lead stream is not the null stream: the CU-masked side stream is a blocking stream,
-    # which the null stream would wait for
-    lead = torch.cuda.Stream(device=dev)
+    def mark(ev, key, st=None):
+        if ev is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(st if st is not None else torch.cuda.current_stream())
+            ev.setdefault(key, []).append(e)
 
-    def step_overlap(ev=None):
-        with torch.cuda.stream(lead):
-            overlap_body(ev)
+    lead = torch.cuda.Stream(device=dev)  # not the null stream: the CU-masked stream is a blocking stream
 
-    def overlap_body(ev):
-        # ev: events 0..6 and 9..11 on the lead stream, 7..8 on the side stream
+    def step_overlap(ev):
+        # one layer: the Cholesky factor needs only H_X'' (input side of BiIP), so it runs next to
+        # the H_G covariance, which goes to a second stream kept off `reserve` CUs; the output side of
+        # BiIP and the sweep follow on the lead stream with every CU. Left and right rotations commute.
+        s = cfg.subs[0]
+        L = lay[s.name]
+        grp = s.x_group
         main = torch.cuda.current_stream()
-        def mark(i, st):
-            if ev is not None:
-                ev[i].record(st)
-        mark(0, main)
-        kq.accumulate_cov(xd, hx, 1.0 / n_tok, 0.0, ws=ws_cov)
+        mark(ev, "cov_x0", main)
+        kq.accumulate_cov(xs[grp], L["hx"], 1.0 / n_tok, 0.0, ws=ws_cov)
+        mark(ev, "cov_x1", main)
         e_cov = torch.cuda.Event()
-        e_cov.record(main)  # the G covariance reuses this workspace
-        mark(1, main)
+        e_cov.record(main)  # the G covariance reuses the covariance workspace
         with torch.cuda.stream(side):
             side.wait_event(e_cov)
-            mark(7, side)
-            kq.accumulate_cov(gd, hg, 1.0 / n_tok, 0.0, ws=ws_cov)
-            mark(8, side)
+            mark(ev, "cov_g0", side)
+            kq.accumulate_cov(gs[s.name], hg[s.name], 1.0 / n_tok, 0.0, ws=ws_cov)
+            mark(ev, "cov_g1", side)
             e_g = torch.cuda.Event()
             e_g.record(side)
-        kq.sensitivity(hx, None, score_x, kq.KQ_SCORE_HX_ONLY)  # tr(H_X) of the raw covariance
-        mark(2, main)
-        kq.biip_rotate(wd, w1, hx, None, ri.rot, None, in_flags, s_x, s_unused_g, ws=ws_biip)
-        mark(3, main)
-        kq.cholesky_inv(hx, cfg.damp, info, ws=ws_chol)
-        mark(4, main)
-        # the rest runs on the lead stream, which has every CU
+        mark(ev, "score0", main)
+        kq.sensitivity(L["hx"], None, score_dev[0:1], kq.KQ_SCORE_HX_ONLY)  # tr(H_X), raw
+        mark(ev, "score1", main)
+        mark(ev, "biip0", main)
+        kq.biip_rotate(ws_[s.name], L["w1"], L["hx"], None, rots_in[grp].rot, None, in_flags, L["s_x"], L["s_u"],
+                       ws=ws_biip)
+        mark(ev, "biip1", main)
+        mark(ev, "chol0", main)
+        kq.cholesky_inv(L["hx"], cfg.damp, L["info"], ws=ws_chol)
+        mark(ev, "chol1", main)
         main.wait_event(e_g)
-        mark(9, main)
-        kq.sensitivity(hg, None, score_g, kq.KQ_SCORE_HX_ONLY)  # tr(H_G) of the raw covariance
-        mark(10, main)
-        kq.biip_rotate(w1, w2, None, hg, None, ro.rot, out_flags, s_unused_x, s_g, ws=ws_biip)
-        mark(11, main)
-        # The traces go to the host without stopping the stream. One layer at one bit width leaves
-        # the allocation no choice, so the sweep is enqueued at that width and the allocation (a host
-        # routine, on score = tr(H_G) tr(H_X), the float64 product the combined call forms) runs
-        # while the sweep does, and is checked.
-        score_host[0:1].copy_(score_x, non_blocking=True)
-        score_host[1:2].copy_(score_g, non_blocking=True)
+        mark(ev, "score0", main)
+        kq.sensitivity(hg[s.name], None, score_dev[1:2], kq.KQ_SCORE_HX_ONLY)  # tr(H_G), raw
+        mark(ev, "score1", main)
+        mark(ev, "biip0", main)
+        kq.biip_rotate(L["w1"], L["w2"], None, hg[s.name], None, rots_out[s.name].rot, out_flags, L["s_u"], L["s_g"],
+                       ws=ws_biip)
+        mark(ev, "biip1", main)
+        # the traces reach the host by an asynchronous copy; one layer leaves the allocation one
+        # choice, so the sweep is enqueued at that width and the allocation (host, on the float64
+        # product tr(H_G) tr(H_X)) runs while the sweep does, and is checked
+        score_host[0:2].copy_(score_dev[0:2], non_blocking=True)
         e_sc = torch.cuda.Event()
         e_sc.record(main)
-        mark(5, main)
-        kq.obs_quantize(w2, hx, args.bits, cfg.group, cfg.block, codes, scales, zeros, ws=ws_obs)
-        mark(6, main)
+        bits = choices[0]
+        mark(ev, "obs0", main)
+        kq.obs_quantize(L["w2"], L["hx"], bits, cfg.group, cfg.block, L["codes"], L["scales"], L["zeros"], ws=ws_obs)
+        mark(ev, "obs1", main)
         e_sc.synchronize()
-        sc = float(score_host[0]) * float(score_host[1])
-        bits = kq.allocate_bits([sc], [dout * din], [args.bits], args.bits * 1000)[0]
-        if bits != args.bits:
-            raise RuntimeError(f"allocation gave {bits} bits for the one layer, expected {args.bits}")
+        plan_box["plan"] = allocate([float(score_host[0]) * float(score_host[1])])
 
-    step = step_serial if args.serial else step_overlap
+    def step_serial(ev):
+        main = torch.cuda.current_stream()
+        for grp in cfg.x_groups:
+            mark(ev, "cov_x0", main)
+            kq.accumulate_cov(xs[grp], hx_raw[grp], 1.0 / n_tok, 0.0, ws=ws_cov)
+            mark(ev, "cov_x1", main)
+        for s in cfg.subs:
+            mark(ev, "cov_g0", main)
+            kq.accumulate_cov(gs[s.name], hg[s.name], 1.0 / n_tok, 0.0, ws=ws_cov)
+            mark(ev, "cov_g1", main)
+        mark(ev, "score0", main)
+        for i, s in enumerate(cfg.subs):
+            kq.sensitivity(hx_raw[s.x_group], hg[s.name], score_dev[i:i + 1], kq.KQ_SCORE_KRONQ)
+        score_host[:len(cfg.subs)].copy_(score_dev[:len(cfg.subs)], non_blocking=True)
+        main.synchronize()  # the widths of the sweeps depend on the scores
+        plan = allocate([float(v) for v in score_host[:len(cfg.subs)]])
+        plan_box["plan"] = plan
+        mark(ev, "score1", main)
+        for i, s in enumerate(cfg.subs):
+            L = lay[s.name]
+            L["hx"].copy_(hx_raw[s.x_group])  # the factor works in place; the raw H_X serves every layer
+            mark(ev, "biip0", main)
+            kq.biip_rotate(ws_[s.name], L["w2"], L["hx"], hg[s.name], rots_in[s.x_group].rot, rots_out[s.name].rot,
+                           pipeline.ALL_SIDES, L["s_x"], L["s_g"], ws=ws_biip)
+            mark(ev, "biip1", main)
+            mark(ev, "chol0", main)
+            kq.cholesky_inv(L["hx"], cfg.damp, L["info"], ws=ws_chol)
+            mark(ev, "chol1", main)
+            mark(ev, "obs0", main)
+            kq.obs_quantize(L["w2"], L["hx"], plan[i], cfg.group, cfg.block, L["codes"], L["scales"], L["zeros"],
+                            ws=ws_obs)
+            mark(ev, "obs1", main)
 
-    torch.cuda.synchronize()  # inputs were uploaded on the null stream
+    def step(ev=None):
+        with torch.cuda.stream(lead):
+            (step_overlap if overlap else step_serial)(ev)
+
+    torch.cuda.synchronize()
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if int(info.item()) != 0:
-        raise RuntimeError(f"Cholesky reported info = {int(info.item())}")
+    bad = {s.name: int(lay[s.name]["info"].item()) for s in cfg.subs if int(lay[s.name]["info"].item())}
+    if bad:
+        raise RuntimeError(f"Cholesky factor reported info {bad}")
 
     log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(args.steps)]
-    kq.timing_enable("syrk_partial")
+    evs = [dict() for _ in range(args.steps)]
+    kq.timing_enable("|".join(TIMED_KERNELS))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launches, syrk_ms = kq.timing_query("syrk_partial")
+    kt = {k: kq.timing_query(k) for k in TIMED_KERNELS}
     kq.timing_enable(None)
-    unshared = None
-    if not args.serial:
-        # the same kernel with the GPU to itself (the H_X launch of the schedule), three launches
-        kq.timing_enable("syrk_partial")
-        for _ in range(3):
-            kq.accumulate_cov(xd, hx, 1.0 / n_tok, 0.0, ws=ws_cov)
-        torch.cuda.synchronize()
-        n_u, ms_u = kq.timing_query("syrk_partial")
-        kq.timing_enable(None)
-        unshared = ms_u / max(n_u, 1)
     release_streams()
+    plan = plan_box["plan"]
 
     ms_step = wall * 1e3 / args.steps
-    def span(a, b):
-        return sum(ev[a].elapsed_time(ev[b]) for ev in events) / args.steps
-    if args.serial:
-        stage_ms = {s: span(i, i + 1) for i, s in enumerate(stages)}
-    else:
-        # per-stage durations on the stream each ran on; cov_g overlaps the BiIP input side
-        # and the Cholesky factor, so the stages add up to more than the step
-        stage_ms = {"cov_x": span(0, 1), "cov_g": span(7, 8), "score_alloc": span(1, 2) + span(9, 10),
-                    "biip": span(2, 3) + span(10, 11), "cholesky": span(3, 4), "obs": span(5, 6)}
-    flops_cov = n_tok * din * (din + 1) + n_tok * dout * (dout + 1)
+    def span(stage):
+        tot = 0.0
+        for ev in evs:
+            for a, b in zip(ev.get(stage + "0", []), ev.get(stage + "1", [])):
+                tot += a.elapsed_time(b)
+        return tot / args.steps
+    stage_ms = {"cov_x": span("cov_x"), "cov_g": span("cov_g"), "score_alloc": span("score"), "biip": span("biip"),
+                "cholesky": span("chol"), "obs": span("obs")}
+    weights = sum(n_params)
+    # algorithmic work per step
+    cov_flops = sum(n_tok * d * (d + 1) for d in cfg.x_groups.values()) + sum(n_tok * s.dout * (s.dout + 1)
+                                                                             for s in cfg.subs)
+    chol_flops = sum(2 * s.din ** 3 / 3 for s in cfg.subs)
+    obs_flops = sum(s.dout * s.din * (s.din - 1) for s in cfg.subs)
+    biip_bytes = sum(s.dout * s.din * ((2 if cfg.w_dtype == "bf16" else 4) + 8) + 8 * s.din ** 2 + 8 * s.dout ** 2
+                     for s in cfg.subs)
+    work = {"syrk_partial": cov_flops, "chol_step_kernel": chol_flops, "obs_step_kernel": obs_flops}
     t_accum = (stage_ms["cov_x"] + stage_ms["cov_g"]) / 1e3
-    t_quant = sum(stage_ms[s] for s in ("score_alloc", "biip", "cholesky", "obs")) / 1e3
-    syrk_tflops = flops_cov * args.steps / (syrk_ms / 1e3) / 1e12 if syrk_ms > 0 else 0.0
-    value = dout * din / (ms_step / 1e3) / 1e6
+    t_quant = sum(stage_ms[k] for k in ("score_alloc", "biip", "cholesky", "obs")) / 1e3
+    value = weights / (ms_step / 1e3) / 1e6
     log(f"{ms_step:.2f} ms/step; stages {json.dumps({k: round(v, 3) for k, v in stage_ms.items()})}")
-    log(f"syrk_partial: {launches} launches, {syrk_ms / max(launches, 1):.3f} ms avg, {syrk_tflops:.1f} TFLOP/s")
-
+    for k, (n, ms) in kt.items():
+        if n:
+            log(f"  {k}: {n} launches, {ms / args.steps:.3f} ms per step")
+    dominant = max(work, key=lambda k: kt[k][1])
+    n_l, ms_l = kt[dominant]
+    src, peak, unit, bound = KERNELS[dominant]
+    achieved = work[dominant] * args.steps / (ms_l / 1e3) / 1e12
+    tag = WORKLOAD_TAG[cfg.id]
     result = {
         "metric": "layer quantize throughput (Mweights/s) + H_X/H_G accumulate TFLOP/s",
         "value": round(value, 3),
@@ -651,78 +747,90 @@ def main() -> int:
         "dtype": "bf16/f32/f64",
         "data": "synthetic",
         "config": {
-            "workload": (f"{cfg.name}: W {dout}x{din} bf16, X and G {n_tok}x{din} bf16, W{args.bits} "
-                         f"group {cfg.group} block {cfg.block} damp {cfg.damp}, BiIP both sides"),
-            "bits": args.bits,
+            "workload": (f"{cfg.name}: " + ", ".join(f"{s.name} {s.dout}x{s.din}" for s in cfg.subs) +
+                         f" ({cfg.w_dtype}); {n_tok} tokens of X and G (bf16); group {cfg.group}, block {cfg.block}, "
+                         f"damp {cfg.damp}, BiIP both sides"),
+            "bits": dict(zip([s.name for s in cfg.subs], plan)),
             "tokens": n_tok,
-            "weights": dout * din,
+            "weights": weights,
         },
-        "accumulate_tflops": round(flops_cov / t_accum / 1e12, 2),
-        "quantize_mweights_per_s": round(dout * din / t_quant / 1e6, 2),
-        "seconds_per_layer": round(ms_step / 1e3, 5),
+        "accumulate_tflops": round(cov_flops / t_accum / 1e12, 2) if t_accum > 0 else None,
+        "quantize_mweights_per_s": round(weights / t_quant / 1e6, 2) if t_quant > 0 else None,
+        "seconds_per_step": round(ms_step / 1e3, 5),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "kernel_ms_per_step": {k: round(ms / args.steps, 4) for k, (n, ms) in kt.items() if n},
         "roofline": {
-            "kernel": "syrk_partial",
-            "bound": "mfma",
-            "achieved": round(syrk_tflops, 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(syrk_tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": stored_traffic(),
+            "kernel": dominant,
+            "bound": bound,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": stored_traffic(dominant, tag),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes": 2 * n_tok * din + 4 * din * din,
-            "launches": launches,
-            "avg_launch_ms": round(syrk_ms / max(launches, 1), 4),
-            "note": ("average over every launch of the timed region: the H_G launches run on the CU-masked "
-                     "second stream next to the Cholesky factor" if not args.serial else "one stream"),
+            "algorithmic_flops_per_launch": round(work[dominant] * args.steps / max(n_l, 1)),
+            "launches": n_l,
+            "avg_launch_ms": round(ms_l / max(n_l, 1), 4),
+            "note": (f"the kernel with the most time in the step; algorithmic flops "
+                     + {"syrk_partial": "N d (d + 1) per covariance",
+                        "chol_step_kernel": "2 d^3 / 3 per factor (factor and inverse), float32 MFMA trailing updates",
+                        "obs_step_kernel": "dout din (din - 1) per layer (in-block sweep and lazy-batch updates)"}[dominant]
+                     + "; launch durations from HIP events the library records on each launch's stream"),
         },
         "cpu_baseline": None,
     }
-    # every step's fraction of its own roof (the dominant kernel's is `roofline` above)
-    biip_bytes = dout * din * (2 + 8) + 8 * din * din + 8 * dout * dout  # W bf16 in, float64 out; H in place
-    obs_flops = dout * din * (din - cfg.block)  # lazy-batch trailing products over all blocks
-    chol_flops = 2 * din ** 3 / 3              # factor and triangular inverse
-    def step_roof(bound, amount, ms, peak, unit, scale, note):
+
+    def roof(bound, amount, ms, peak, unit, scale, note):
         ach = amount / (ms / 1e3) / scale if ms > 0 else 0.0
-        return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "ms": round(ms, 4), "note": note}
+        return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                "ms": round(ms, 4), "note": note}
+
+    kms = {k: ms / args.steps for k, (n, ms) in kt.items()}
     result["step_rooflines"] = {
-        "biip": step_roof("hbm", biip_bytes, stage_ms["biip"], HBM_PEAK_GBS, "GB/s", 1e9,
-                          f"{biip_bytes} algorithmic bytes (W bf16 read, float64 W'' write, H_X and H_G float32 "
-                          f"read and write); the input side runs next to the H_G covariance"),
-        "obs_trailing": step_roof("mfma", obs_flops, stage_ms["obs"], FP64_PEAK_TFLOPS, "TFLOP/s", 1e12,
-                                  f"dout din (din - B) = {obs_flops} flop of float64 trailing products over the "
-                                  f"whole sweep time (the in-block sweep included)"),
-        **({} if args.serial else {"biip_output_side": step_roof(
-            "hbm", dout * din * 16 + 8 * dout * dout, span(10, 11), HBM_PEAK_GBS, "GB/s", 1e9,
-            "output side alone, with the GPU to itself: float64 W read and write, H_G float32 read and write "
-            "(three passes over each matrix, so about three times these bytes move)")}),
-        "cholesky": step_roof("mfma", chol_flops, stage_ms["cholesky"], FP32_PEAK_TFLOPS, "TFLOP/s", 1e12,
-                              "2 d^3 / 3 flop (factor and inverse) against the float32 roof; runs on the 80 CUs "
-                              "left to it next to the H_G covariance" if not args.serial else
-                              "2 d^3 / 3 flop (factor and inverse) against the float32 roof"),
+        "covariance": roof("mfma", cov_flops, kms["syrk_partial"], 2500.0, "TFLOP/s", 1e12,
+                           "syrk_partial launches: N d (d + 1) flop per covariance"),
+        "biip": roof("hbm", biip_bytes, stage_ms["biip"], HBM_PEAK_GBS, "GB/s", 1e9,
+                     "whole BiIP stage: W read, float64 W'' write, H_X and H_G float32 read and write"),
+        "cholesky": roof("mfma", chol_flops, kms["chol_step_kernel"], 157.3, "TFLOP/s", 1e12,
+                         "chol_step_kernel launches: 2 d^3 / 3 flop per factor, against the float32 roof"),
+        "obs": roof("mfma", obs_flops, kms["obs_step_kernel"], 78.6, "TFLOP/s", 1e12,
+                    "obs_step_kernel launches: dout din (din - 1) flop per layer, against the float64 roof"),
     }
-    result["schedule"] = ("one stream" if args.serial else
-                          f"two streams: H_X covariance, BiIP input side, Cholesky factor, BiIP output side and "
-                          f"sweep on one; H_G covariance on the other, kept off {args.reserve_cus} CUs")
-    if unshared is not None:
-        ach = flops_cov / 2 / (unshared / 1e3) / 1e12 if unshared > 0 else 0.0
-        result["roofline"]["unshared"] = {"avg_launch_ms": round(unshared, 4), "achieved": round(ach, 2),
-                                          "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                                          "note": "3 launches on the H_X input after the timed region, GPU to itself"}
+    result["schedule"] = ("two streams: H_X covariance, BiIP input side, Cholesky factor, BiIP output side and "
+                          f"sweep on one; H_G covariance on the other, kept off {args.reserve_cus} CUs" if overlap else
+                          "one stream: every covariance, the scores and the allocation, then per layer BiIP, "
+                          "Cholesky factor and sweep")
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
+        src_t = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst_t = torch.empty_like(src_t)
+        src_t.fill_(1)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        dst_t.copy_(src_t)
         torch.cuda.synchronize()
-        del src, dst
+        del src_t, dst_t
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(wl, cfg, sub, args.bits, args.cpu_tokens, args.cpu_rows)
+        del xs, gs
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(wl, cfg, plan)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def main() -> int:
+    args = parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU; the path's multi-GPU sharding is design only, "
+                                   "so --gpus must be 1"}))
+        return 2
+    if args.decode:
+        return decode_bench(args)
+    if args.capture:
+        return capture_bench(args)
+    return quant_bench(args)
 
 
 if __name__ == "__main__":

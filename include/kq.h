@@ -94,7 +94,8 @@ const char* kq_last_error(void);
 /*
  * Kernel timing (diagnostics, host calls). kq_timing_enable(filter) clears the
  * record and, while enabled, brackets every launch of a kernel whose name
- * contains `filter` ("" = all kernels) with HIP events on that launch's
+ * contains `filter` ("" = all kernels; "a|b" = names containing a or b) with
+ * HIP events on that launch's
  * stream; NULL disables. kq_timing_query(name, ...) waits for the recorded
  * events of kernels whose name contains `name` and returns the number of
  * launches and their summed duration in milliseconds. Not thread safe

@@ -648,7 +648,7 @@ __device__ void update_role(GemmLds& sm, float* __restrict__ a, float* __restric
 // column kb of A and diagonal block kb of M; row kb - 1 of M; the columns
 // beyond kb of A and the rows from kb on of M) and read none that another
 // role of the launch writes, so one launch per step suffices.
-__global__ __launch_bounds__(256) void step_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb,
+__global__ __launch_bounds__(256) void chol_step_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb,
                                                    int64_t d, int n_diag, int n_row, int n_trail,
                                                    int32_t* __restrict__ info) {
   __shared__ StepLds sm;
@@ -721,11 +721,11 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
     const int grid = n_diag + n_row + n_trail + n_sub;
     if (grid == 0) continue;
     {
-      LaunchTimer timer("step_kernel", st);
-      hipLaunchKernelGGL(step_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a, m, dp, kb, d, n_diag,
+      LaunchTimer timer("chol_step_kernel", st);
+      hipLaunchKernelGGL(chol_step_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a, m, dp, kb, d, n_diag,
                          n_row, n_trail, info);
     }
-    if ((r = check_launch("step_kernel")) != KQ_OK) return r;
+    if ((r = check_launch("chol_step_kernel")) != KQ_OK) return r;
   }
 
   {

@@ -454,7 +454,7 @@ union StepLds {
 
 // Two waves per SIMD: a sweep workgroup and a far-update workgroup share each CU.
 template <int B, bool SG>
-__global__ __launch_bounds__(256, 2) void step_kernel(double* __restrict__ w, const float* __restrict__ r,
+__global__ __launch_bounds__(256, 2) void obs_step_kernel(double* __restrict__ w, const float* __restrict__ r,
                                                    int64_t dout, int64_t din, int64_t c0, int bits, int group,
                                                    uint8_t* __restrict__ codes, float* __restrict__ scales,
                                                    uint8_t* __restrict__ zeros, double* __restrict__ preround,
@@ -484,13 +484,13 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
     const int64_t rest = din - c0 - B;  // columns beyond this block
     const int far_cols = (k > 0 && rest > 0) ? static_cast<int>((rest + kFT - 1) / kFT) : 0;
     {
-      LaunchTimer timer("step_kernel", st);
+      LaunchTimer timer("obs_step_kernel", st);
       const bool small_group = group > 0 && group < 16;  // groups that start inside a 16-column slice
-      auto kern = small_group ? step_kernel<B, true> : step_kernel<B, false>;
+      auto kern = small_group ? obs_step_kernel<B, true> : obs_step_kernel<B, false>;
       hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_sweep + far_cols * far_rows)), dim3(256), 0, st, w, r, dout,
                          din, c0, bits, group, codes, scales, zeros, preround, e_prev, ebuf[k & 1], n_sweep, far_cols);
     }
-    if ((s = check_launch("step_kernel")) != KQ_OK) return s;
+    if ((s = check_launch("obs_step_kernel")) != KQ_OK) return s;
   }
   return KQ_OK;
 }

@@ -18,7 +18,7 @@ struct Record {
 struct State {
   std::mutex mu;
   bool on = false;
-  std::string filter;
+  std::vector<std::string> filters;  // alternatives; a launch is timed if its name contains any
   std::vector<Record> records;
   std::vector<hipEvent_t> pool;
 };
@@ -52,7 +52,10 @@ void recycle(State& s) {
 LaunchTimer::LaunchTimer(const char* name, hipStream_t st) : name_(name), st_(st) {
   State& s = state();
   std::lock_guard<std::mutex> lock(s.mu);
-  if (!s.on || std::strstr(name, s.filter.c_str()) == nullptr) return;
+  if (!s.on) return;
+  bool hit = false;
+  for (const std::string& f : s.filters) hit = hit || std::strstr(name, f.c_str()) != nullptr;
+  if (!hit) return;
   begin_ = take_event(s);
   if (begin_ && hipEventRecord(begin_, st_) != hipSuccess) begin_ = nullptr;
 }
@@ -79,7 +82,13 @@ kq_status kq_timing_enable(const char* filter) {
   std::lock_guard<std::mutex> lock(s.mu);
   kq::recycle(s);
   s.on = filter != nullptr;
-  s.filter = filter ? filter : "";
+  s.filters.clear();
+  if (filter) {
+    std::string all(filter);
+    size_t b = 0;
+    for (size_t e; (e = all.find('|', b)) != std::string::npos; b = e + 1) s.filters.push_back(all.substr(b, e - b));
+    s.filters.push_back(all.substr(b));
+  }
   return KQ_OK;
 }
 

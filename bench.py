@@ -214,9 +214,27 @@ COPY_BYTES = 1 << 30
 # kernel -> (source file, peak, unit, bound)
 KERNELS = {
     "syrk_partial": ("syrk.hip", 2500.0, "TFLOP/s", "mfma"),
+    "chol_far_kernel": ("chol.hip", 157.3, "TFLOP/s", "mfma"),
     "chol_step_kernel": ("chol.hip", 157.3, "TFLOP/s", "mfma"),
     "obs_step_kernel": ("obs.hip", 78.6, "TFLOP/s", "mfma"),
 }
+
+
+def chol_far_flops(d: int, b: int = 64, sp: int = 4) -> int:
+    """Algorithmic flops of the Cholesky factor's far launches (rank-256 updates after each super-panel
+    of sp 64-blocks): the lower triangle of the trailing block of A, and the substitution sums for
+    the rows beyond the super-panel over the nonzero part of M (columns up to each k)."""
+    nb = -(-d // b)
+    total = 0
+    for s0 in range(0, nb, sp):
+        s1 = min(s0 + sp, nb)
+        if s1 >= nb:
+            break
+        nrem = nb - s1                       # trailing blocks
+        total += 2 * b ** 3 * (s1 - s0) * nrem * (nrem + 1) // 2
+        for k in range(max(s0 - 1, 0), s1 - 1):  # row blocks beyond s1 x column blocks c <= k
+            total += 2 * b ** 3 * nrem * (k + 1)
+    return total
 
 
 def kernel_source(kernel: str) -> str:
@@ -499,7 +517,8 @@ def decode_bench(args) -> int:
 
 WORKLOAD_TAG = {1: "linear64x128", 2: "llama2-7b_q_proj", 3: "llama2-13b_mlp", 4: "llama3-70b_down_proj",
                 5: "llama3-8b_block"}
-TIMED_KERNELS = ("syrk_partial", "chol_step_kernel", "obs_step_kernel", "row_fwht", "col_fwht", "col_mix")
+TIMED_KERNELS = ("syrk_partial", "chol_far_kernel", "chol_step_kernel", "obs_step_kernel", "row_fwht", "col_fwht",
+                 "col_mix")
 
 
 def quant_bench(args) -> int:
@@ -720,7 +739,9 @@ def quant_bench(args) -> int:
     obs_flops = sum(s.dout * s.din * (s.din - 1) for s in cfg.subs)
     biip_bytes = sum(s.dout * s.din * ((2 if cfg.w_dtype == "bf16" else 4) + 8) + 8 * s.din ** 2 + 8 * s.dout ** 2
                      for s in cfg.subs)
-    work = {"syrk_partial": cov_flops, "chol_step_kernel": chol_flops, "obs_step_kernel": obs_flops}
+    far_flops = sum(chol_far_flops(s.din) for s in cfg.subs)
+    work = {"syrk_partial": cov_flops, "chol_far_kernel": far_flops, "chol_step_kernel": chol_flops - far_flops,
+            "obs_step_kernel": obs_flops}
     t_accum = (stage_ms["cov_x"] + stage_ms["cov_g"]) / 1e3
     t_quant = sum(stage_ms[k] for k in ("score_alloc", "biip", "cholesky", "obs")) / 1e3
     value = weights / (ms_step / 1e3) / 1e6
@@ -773,7 +794,10 @@ def quant_bench(args) -> int:
             "avg_launch_ms": round(ms_l / max(n_l, 1), 4),
             "note": (f"the kernel with the most time in the step; algorithmic flops "
                      + {"syrk_partial": "N d (d + 1) per covariance",
-                        "chol_step_kernel": "2 d^3 / 3 per factor (factor and inverse), float32 MFMA trailing updates",
+                        "chol_far_kernel": "of the rank-256 updates after each 256-column super-panel (lower "
+                                           "triangle of the trailing matrix and the substitution sums over the "
+                                           "nonzero part of L^-1), float32 MFMA",
+                        "chol_step_kernel": "2 d^3 / 3 per factor less the far launches' share, float32 MFMA",
                         "obs_step_kernel": "dout din (din - 1) per layer (in-block sweep and lazy-batch updates)"}[dominant]
                      + "; launch durations from HIP events the library records on each launch's stream"),
         },
@@ -791,8 +815,9 @@ def quant_bench(args) -> int:
                            "syrk_partial launches: N d (d + 1) flop per covariance"),
         "biip": roof("hbm", biip_bytes, stage_ms["biip"], HBM_PEAK_GBS, "GB/s", 1e9,
                      "whole BiIP stage: W read, float64 W'' write, H_X and H_G float32 read and write"),
-        "cholesky": roof("mfma", chol_flops, kms["chol_step_kernel"], 157.3, "TFLOP/s", 1e12,
-                         "chol_step_kernel launches: 2 d^3 / 3 flop per factor, against the float32 roof"),
+        "cholesky": roof("mfma", chol_flops, kms["chol_step_kernel"] + kms["chol_far_kernel"], 157.3, "TFLOP/s",
+                         1e12, "chol_step_kernel and chol_far_kernel launches: 2 d^3 / 3 flop per factor, against "
+                               "the float32 roof"),
         "obs": roof("mfma", obs_flops, kms["obs_step_kernel"], 78.6, "TFLOP/s", 1e12,
                     "obs_step_kernel launches: dout din (din - 1) flop per layer, against the float64 roof"),
     }

@@ -5,24 +5,35 @@
 // chain is:
 //   1. damping: delta = damp * mean(diag H) in float64;
 //   2. reversal copy A = J H J + delta I into scratch, padded to a multiple of
-//      64 with an identity block;
+//      64 with an identity block; M (which becomes L^-1) starts at zero;
 //   3. blocked right-looking Cholesky of A with 64 x 64 blocks, and one step
-//      behind it M = L^-1 by blocked forward substitution; one launch per
-//      step kb = 0 .. nb (the last one only finishes M):
+//      behind it M = L^-1 by blocked forward substitution, in two levels:
+//      super-panels of kSP = 4 blocks (256 columns). One launch per step
+//      kb = 0 .. nb (the last one only finishes M):
 //      * the diagonal role brings block column kb up to date with the
-//        previous panel (float64 MFMA), factors and inverts the diagonal
-//        block in float64 in LDS (every workgroup of the role does this
-//        itself); workgroup 0 stores M_kk = L_kk^-1 and each other one
-//        multiplies one 64-row block of the panel by L_kk^-T;
+//        previous panel (float64 MFMA) when that panel belongs to the same
+//        super-panel, factors and inverts the diagonal block in float64 in LDS
+//        (every workgroup of the role does this itself); workgroup 0 stores
+//        M_kk = L_kk^-1 and each other one multiplies one 64-row block of the
+//        panel by L_kk^-T;
 //      * the row role forms row j = kb - 1 of M, one 64 x 64 block per
 //        workgroup, from the stored M_jj:
 //          M[j, c] = -M_jj (S[j, c] + L[j, j-1] M[j-1, c]),   c < j,
 //        where S[i, c] = sum over i' < i - 1 of L[i, i'] M[i', c] has been
 //        accumulated in M's lower blocks by the earlier launches;
-//      * the update role applies the previous panel, A[i, j'] -=
-//        L[i, kb-1] L[j', kb-1]^T to the block columns beyond kb, and adds
-//        S[i, c] += L[i, kb-2] M[kb-2, c] to the rows from kb on, in
-//        128 x 128 tiles on float32 MFMA (v_mfma_f32_32x32x2f32);
+//      * the update role applies the previous panel (rank 64) only inside the
+//        current super-panel: A[i, j'] -= L[i, kb-1] L[j', kb-1]^T for block
+//        columns kb + 1 .. to the super-panel's end (every row below), and
+//        S[i, c] += L[i, kb-2] M[kb-2, c] for the super-panel's rows from kb;
+//      after the last step of a super-panel [s0, s1) one more launch applies
+//      the whole super-panel at once (rank 256) to everything beyond it:
+//        A[i, j] -= L[i, s0:s1] L[j, s0:s1]^T            for s1 <= j <= i,
+//        S[i, c] += L[i, s0-1:s1-1] M[s0-1:s1-1, c]       for i >= s1
+//      (the substitution runs one block behind the factor, so its panel is the
+//      super-panel shifted by one block). Each element of the trailing matrix
+//      is read and written once per super-panel instead of once per block, a
+//      quarter of the HBM traffic of the one-level form; all products are
+//      128 x 128 tiles on float32 MFMA (v_mfma_f32_32x32x2f32);
 //   4. R = J M J written over H (strict lower triangle zeroed).
 // A pivot that is not positive and finite stops the chain: `info` takes the
 // original index + 1 and every later kernel returns at once.
@@ -32,6 +43,7 @@ namespace kq {
 namespace {
 
 constexpr int kB = 64;  // block edge
+constexpr int kSP = 4;  // blocks per super-panel
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -212,8 +224,9 @@ __global__ __launch_bounds__(256) void damp_kernel(const float* __restrict__ h, 
   }
 }
 
-// A[i][j] = H[d-1-i][d-1-j] + delta [i == j]; identity outside d. The
-// lower triangle of M (the running sums S of the substitution) starts at 0.
+// A[i][j] = H[d-1-i][d-1-j] + delta [i == j]; identity outside d. M starts at
+// 0: its lower blocks hold the running sums S of the substitution, and the
+// blocks above its diagonal stay 0 (the far substitution update reads them).
 __global__ void reverse_kernel(const float* __restrict__ h, int64_t d, int64_t dp, const double* __restrict__ delta,
                                float* __restrict__ a, float* __restrict__ m) {
   const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -227,7 +240,7 @@ __global__ void reverse_kernel(const float* __restrict__ h, int64_t d, int64_t d
     v = (i == j) ? 1.0f : 0.0f;
   }
   a[i * dp + j] = v;
-  if (j <= i) m[i * dp + j] = 0.0f;
+  m[i * dp + j] = 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -425,7 +438,9 @@ __device__ void diag_role(DiagLds& sm, float* __restrict__ a, float* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t o = int64_t(kb) * kB, op = o - kB;
   const int64_t r0 = o + int64_t(b) * kB;
-  const bool panel = b > 0, prev = kb > 0;
+  // the previous panel's update is deferred to here only inside a super-panel; at a super-panel's
+  // first block the far launch before this one has applied it
+  const bool panel = b > 0, prev = (kb % kSP) != 0;
   // this thread's 16 elements e = tid + 256 q of the diagonal block, its previous-panel
   // rows, the panel block and its previous-panel rows: every load is issued before the
   // first LDS write, so the inputs written by the previous launch arrive in one round trip
@@ -613,31 +628,31 @@ __device__ void row_role(DiagLds& sm, const float* __restrict__ a, float* __rest
   }
 }
 
-// Update role of step kb >= 1, tile u. Tiles u < n_trail: A[i, j] -=
-// L[i, kb-1] L[j, kb-1]^T for block columns kb + 1 <= j <= i (128 x 128
-// tiles; a diagonal tile also rewrites the upper half of its 64 x 64 diagonal
-// blocks, which is never read); block column kb receives the same update in
-// the diagonal role. Tiles u >= n_trail (kb >= 2): S[i, c] += L[i, kb-2]
-// M[kb-2, c] for row blocks i >= kb and column blocks c <= kb - 2; row kb - 1
-// takes this term in the row role.
-__device__ void update_role(GemmLds& sm, float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb, int u,
-                            int n_trail) {
-  const int64_t op = int64_t(kb - 1) * kB, c0 = int64_t(kb + 1) * kB;
-  if (u < n_trail) {
-    int I, J;
-    tri(u, I, J);
-    const int64_t ri = c0 + int64_t(I) * kG, rj = c0 + int64_t(J) * kG;
+// Update role of step kb, tile u, inside super-panel [s0, s1) (block indices).
+// Tiles u < n_a (kb > s0): A[i, j] -= L[i, kb-1] L[j, kb-1]^T for block
+// columns kb + 1 <= j < s1 and every row from kb + 1 on (a strip of at most 128
+// columns; a tile that crosses the diagonal also rewrites part of A's upper
+// triangle, which is never read); block column kb receives the same update in
+// the diagonal role. Tiles u >= n_a (kb > s0, kb >= 2): S[i, c] += L[i, kb-2]
+// M[kb-2, c] for row blocks kb <= i < s1 and column blocks c <= kb - 2; row kb -
+// 1 takes this term in the row role, rows from s1 on in the far launch.
+__device__ void update_role(GemmLds& sm, float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb, int s1,
+                            int u, int n_a) {
+  if (u < n_a) {
+    const int64_t c0 = int64_t(kb + 1) * kB;
+    const int64_t ri = c0 + int64_t(u) * kG;
     const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
-    const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
-    gemm128<true>(sm, a + ri * dp + op, dp, a + rj * dp + op, dp, a + ri * dp + rj, dp, mv, nv, 0, kB, -1.0f, 1.0f);
+    const int nv = (s1 - kb - 1) * kB;  // 64 or 128
+    const int64_t op = int64_t(kb - 1) * kB;
+    gemm128<true>(sm, a + ri * dp + op, dp, a + c0 * dp + op, dp, a + ri * dp + c0, dp, mv, nv, 0, kB, -1.0f, 1.0f);
     return;
   }
-  u -= n_trail;
+  u -= n_a;
   const int ncol = kb / 2;  // 128-wide tiles over columns [0, 64 (kb - 1))
   const int64_t o2 = int64_t(kb - 2) * kB;
   const int64_t ri = int64_t(kb) * kB + int64_t(u / ncol) * kG, cj = int64_t(u % ncol) * kG;
-  const int64_t cend = int64_t(kb - 1) * kB;
-  const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
+  const int64_t rend = int64_t(s1) * kB, cend = int64_t(kb - 1) * kB;
+  const int mv = static_cast<int>(rend - ri < kG ? rend - ri : kG);
   const int nv = static_cast<int>(cend - cj < kG ? cend - cj : kG);
   gemm128<false>(sm, a + ri * dp + o2, dp, m + o2 * dp + cj, dp, m + ri * dp + cj, dp, mv, nv, 0, kB, 1.0f, 1.0f);
 }
@@ -645,18 +660,55 @@ __device__ void update_role(GemmLds& sm, float* __restrict__ a, float* __restric
 // Step kb of the blocked factorization and substitution: workgroups
 // [0, n_diag) take the diagonal role, the next n_row the row role (row kb - 1
 // of M), the rest the update role. The roles write disjoint blocks (block
-// column kb of A and diagonal block kb of M; row kb - 1 of M; the columns
-// beyond kb of A and the rows from kb on of M) and read none that another
-// role of the launch writes, so one launch per step suffices.
+// column kb of A and diagonal block kb of M; row kb - 1 of M; the super-panel's
+// columns beyond kb of A and its rows from kb on of M) and read none that
+// another role of the launch writes, so one launch per step suffices.
 __global__ __launch_bounds__(256) void chol_step_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int kb,
-                                                   int64_t d, int n_diag, int n_row, int n_trail,
-                                                   int32_t* __restrict__ info) {
+                                                        int64_t d, int s1, int n_diag, int n_row, int n_a,
+                                                        int32_t* __restrict__ info) {
   __shared__ StepLds sm;
   if (*info) return;
   const int b = static_cast<int>(blockIdx.x);
   if (b < n_diag) diag_role(sm.dg, a, m, dp, kb, d, info, b);
   else if (b < n_diag + n_row) row_role(sm.dg, a, m, dp, kb - 1, b - n_diag);
-  else update_role(sm.gm, a, m, dp, kb, b - n_diag - n_row, n_trail);
+  else update_role(sm.gm, a, m, dp, kb, s1, b - n_diag - n_row, n_a);
+}
+
+// Rank-256 update of everything beyond super-panel [s0, s1): tiles u < n_a
+// take the lower triangle of A's trailing block (128 x 128 tiles from block
+// s1 on), A[i, j] -= L[i, s0:s1] L[j, s0:s1]^T; the others take S[i, c] +=
+// L[i, k0:k1] M[k0:k1, c] for rows from block s1 on and column blocks below
+// s1 - 1, with k0 = max(s0 - 1, 0) and k1 = s1 - 1 (the substitution's panel,
+// one block behind; M is zero above its diagonal blocks, so columns beyond a
+// row's diagonal add nothing). The two roles write disjoint blocks and read
+// none that the other writes.
+__global__ __launch_bounds__(256) void chol_far_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int s0,
+                                                       int s1, int n_a, int32_t* __restrict__ info) {
+  __shared__ GemmLds sm;
+  if (*info) return;
+  const int u = static_cast<int>(blockIdx.x);
+  const int64_t r0 = int64_t(s1) * kB;
+  if (u < n_a) {
+    int I, J;
+    tri(u, I, J);
+    const int64_t ri = r0 + int64_t(I) * kG, rj = r0 + int64_t(J) * kG;
+    const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
+    const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
+    const int64_t k0 = int64_t(s0) * kB;
+    gemm128<true>(sm, a + ri * dp + k0, dp, a + rj * dp + k0, dp, a + ri * dp + rj, dp, mv, nv, 0,
+                  (s1 - s0) * kB, -1.0f, 1.0f);
+    return;
+  }
+  const int v = u - n_a;
+  const int64_t cend = int64_t(s1 - 1) * kB;
+  const int ncol = static_cast<int>((cend + kG - 1) / kG);
+  const int64_t ri = r0 + int64_t(v / ncol) * kG, cj = int64_t(v % ncol) * kG;
+  const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
+  const int nv = static_cast<int>(cend - cj < kG ? cend - cj : kG);
+  const int kb0 = s0 > 0 ? s0 - 1 : 0;
+  const int64_t k0 = int64_t(kb0) * kB;
+  gemm128<false>(sm, a + ri * dp + k0, dp, m + k0 * dp + cj, dp, m + ri * dp + cj, dp, mv, nv, 0,
+                 (s1 - 1 - kb0) * kB, 1.0f, 1.0f);
 }
 
 // R[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -712,20 +764,37 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
 
   for (int kb = 0; kb <= nb; ++kb) {
     const int rest = nb - kb - 1;
+    const int s0 = kb / kSP * kSP;
+    const int s1 = s0 + kSP < nb ? s0 + kSP : nb;
+    const bool inner = kb > s0 && kb < nb;  // the previous panel belongs to this super-panel
     const int n_diag = kb < nb ? 1 + rest : 0;
     const int n_row = kb >= 2 ? kb - 1 : 0;  // blocks c < j of row j = kb - 1 of M
-    const int ntu = (kb >= 1 && kb < nb) ? (rest + 1) / 2 : 0;  // 128-wide tiles over block columns kb + 1 ..
-    const int n_trail = ntu * (ntu + 1) / 2;
-    // rows kb .. of M (128-wide) x columns below 64 (kb - 1)
-    const int n_sub = (kb >= 2 && kb < nb) ? ((nb - kb + 1) / 2) * (kb / 2) : 0;
-    const int grid = n_diag + n_row + n_trail + n_sub;
-    if (grid == 0) continue;
-    {
-      LaunchTimer timer("chol_step_kernel", st);
-      hipLaunchKernelGGL(chol_step_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a, m, dp, kb, d, n_diag,
-                         n_row, n_trail, info);
+    // strip of A: block columns kb + 1 .. s1 - 1 (at most 128 wide), 128-row tiles from block kb + 1
+    const int n_a = (inner && kb + 1 < s1) ? static_cast<int>((dp - int64_t(kb + 1) * kB + kG - 1) / kG) : 0;
+    // S rows kb .. s1 - 1 (128-row tiles) x 128-wide column tiles below 64 (kb - 1)
+    const int n_s = (inner && kb >= 2) ? ((s1 - kb) * kB + kG - 1) / kG * (kb / 2) : 0;
+    const int grid = n_diag + n_row + n_a + n_s;
+    if (grid > 0) {
+      {
+        LaunchTimer timer("chol_step_kernel", st);
+        hipLaunchKernelGGL(chol_step_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a, m, dp, kb, d, s1,
+                           n_diag, n_row, n_a, info);
+      }
+      if ((r = check_launch("chol_step_kernel")) != KQ_OK) return r;
     }
-    if ((r = check_launch("chol_step_kernel")) != KQ_OK) return r;
+    if (kb + 1 == s1 && s1 < nb) {
+      // the super-panel [s0, s1) is factored (and M one block behind it): apply it beyond s1
+      const int64_t nrem = dp - int64_t(s1) * kB;
+      const int ntu = static_cast<int>((nrem + kG - 1) / kG);
+      const int fa = ntu * (ntu + 1) / 2;
+      const int fs = ntu * static_cast<int>((int64_t(s1 - 1) * kB + kG - 1) / kG);
+      {
+        LaunchTimer timer("chol_far_kernel", st);
+        hipLaunchKernelGGL(chol_far_kernel, dim3(static_cast<unsigned>(fa + fs)), dim3(256), 0, st, a, m, dp, s0, s1,
+                           fa, info);
+      }
+      if ((r = check_launch("chol_far_kernel")) != KQ_OK) return r;
+    }
   }
 
   {

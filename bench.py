@@ -18,12 +18,12 @@ layer, the LLaMA-2-7B q_proj (--bits 2 or 4), the LLaMA-2-13B MLP (gate, up,
 down at 3 bits) and the LLaMA-3-8B block (seven layers, bits from the
 allocation over {2, 3, 4} at 3.0 average bits). Seeded synthetic inputs.
 
-Schedule: for one layer the Cholesky factor needs only H_X'' (the input side
-of BiIP), so it runs on one stream while the H_G covariance runs on a second
-stream kept off some CUs; the output side of BiIP and the sweep follow with
-every CU. Several layers (or --serial) run on one stream: all covariances,
-the scores and the allocation (the sweeps' widths depend on it), then per
-layer BiIP, the factor and the sweep.
+Schedule: for one layer with at most 8192 inputs the Cholesky factor needs
+only H_X'' (the input side of BiIP), so it runs on one stream while the H_G
+covariance runs on a second stream kept off some CUs; the output side of BiIP
+and the sweep follow with every CU. Wider layers, several layers (or --serial)
+run on one stream: all covariances, the scores and the allocation (the
+sweeps' widths depend on it), then per layer BiIP, the factor and the sweep.
 
 value = weights quantised per second, end to end including the covariance
 accumulation. The roofline object covers the kernel with the most time in the
@@ -536,7 +536,9 @@ def quant_bench(args) -> int:
     torch.zeros(1, device=dev)
     cfg = kq_synth.config(args.config)
     single = len(cfg.subs) == 1
-    overlap = single and not args.serial
+    # two streams pay where the factor is latency-bound (its 64-wide steps leave CUs idle next to the
+    # G covariance); at 28672 inputs the factor's rank-256 launches fill the GPU and one stream is as fast
+    overlap = single and not args.serial and cfg.subs[0].din <= 8192
     # created before anything else takes a hardware queue: a CU-masked stream needs its own
     side = side_stream(dev, args.reserve_cus) if overlap else None
     wl = kq_synth.Workload(cfg)
@@ -613,8 +615,9 @@ def quant_bench(args) -> int:
 
     def step_overlap(ev):
         # one layer: the Cholesky factor needs only H_X'' (input side of BiIP), so it runs next to
-        # the H_G covariance, which goes to a second stream kept off `reserve` CUs; the output side of
-        # BiIP and the sweep follow on the lead stream with every CU. Left and right rotations commute.
+        # the H_G covariance, which goes to a second stream kept off `reserve` CUs once the input side
+        # is done; the output side of BiIP and the sweep follow on the lead stream with every CU. Left
+        # and right rotations commute.
         s = cfg.subs[0]
         L = lay[s.name]
         grp = s.x_group
@@ -622,15 +625,6 @@ def quant_bench(args) -> int:
         mark(ev, "cov_x0", main)
         kq.accumulate_cov(xs[grp], L["hx"], 1.0 / n_tok, 0.0, ws=ws_cov)
         mark(ev, "cov_x1", main)
-        e_cov = torch.cuda.Event()
-        e_cov.record(main)  # the G covariance reuses the covariance workspace
-        with torch.cuda.stream(side):
-            side.wait_event(e_cov)
-            mark(ev, "cov_g0", side)
-            kq.accumulate_cov(gs[s.name], hg[s.name], 1.0 / n_tok, 0.0, ws=ws_cov)
-            mark(ev, "cov_g1", side)
-            e_g = torch.cuda.Event()
-            e_g.record(side)
         mark(ev, "score0", main)
         kq.sensitivity(L["hx"], None, score_dev[0:1], kq.KQ_SCORE_HX_ONLY)  # tr(H_X), raw
         mark(ev, "score1", main)
@@ -638,6 +632,17 @@ def quant_bench(args) -> int:
         kq.biip_rotate(ws_[s.name], L["w1"], L["hx"], None, rots_in[grp].rot, None, in_flags, L["s_x"], L["s_u"],
                        ws=ws_biip)
         mark(ev, "biip1", main)
+        # the G covariance starts once the input side (which the factor waits for) is done, so it
+        # shares the GPU with the factor instead; it reuses the covariance workspace
+        e_in = torch.cuda.Event()
+        e_in.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(e_in)
+            mark(ev, "cov_g0", side)
+            kq.accumulate_cov(gs[s.name], hg[s.name], 1.0 / n_tok, 0.0, ws=ws_cov)
+            mark(ev, "cov_g1", side)
+            e_g = torch.cuda.Event()
+            e_g.record(side)
         mark(ev, "chol0", main)
         kq.cholesky_inv(L["hx"], cfg.damp, L["info"], ws=ws_chol)
         mark(ev, "chol1", main)
@@ -822,7 +827,8 @@ def quant_bench(args) -> int:
                     "obs_step_kernel launches: dout din (din - 1) flop per layer, against the float64 roof"),
     }
     result["schedule"] = ("two streams: H_X covariance, BiIP input side, Cholesky factor, BiIP output side and "
-                          f"sweep on one; H_G covariance on the other, kept off {args.reserve_cus} CUs" if overlap else
+                          f"sweep on one; H_G covariance on the other from the end of the input side, kept off "
+                          f"{args.reserve_cus} CUs" if overlap else
                           "one stream: every covariance, the scores and the allocation, then per layer BiIP, "
                           "Cholesky factor and sweep")
     if args.copy_calibration:

@@ -32,7 +32,8 @@ namespace kq {
 namespace {
 
 constexpr int kRowThreads = 512;   // rot_rows (general row kernel)
-constexpr int kFwThreads = 256;    // row_fwht
+constexpr int kFwThreads = 256;    // row_fwht, rows whose staging leaves room for several workgroups per CU
+constexpr int kFwThreadsWide = 1024;  // row_fwht, rows staged in more than half of the LDS (one workgroup per CU)
 constexpr int kColThreads = 256;
 constexpr size_t kRowLdsF64 = 64 * 1024;  // row_fwht keeps float64 in LDS up to this size
 constexpr size_t kLdsBudget = 160 * 1024;  // bytes of LDS a pass may use (all of a gfx950 CU)
@@ -334,8 +335,8 @@ __device__ __forceinline__ void bfly16(double v[16], int first) {
   }
 }
 
-template <typename T, typename Src, typename Dst, int MB>
-__global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict__ src, int64_t lds, int64_t n,
+template <typename T, typename Src, typename Dst, int MB, int NT>
+__global__ __launch_bounds__(NT, NT == kFwThreads ? 6 : 1) void row_fwht(const Src* __restrict__ src, int64_t lds, int64_t n,
                                                        Dst* __restrict__ dst, int64_t ldd, RowFw rf) {
   extern __shared__ double smem[];
   T* buf = reinterpret_cast<T*>(smem);
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict_
   const double rowf = rf.rowf ? rf.rowf[row] : 1.0;
   const double* colf = rf.colf ? rf.colf : &kUnitFactor;
   const int cstep = rf.colf ? 1 : 0;
-  for (int g = threadIdx.x; g < ng; g += kFwThreads) {
+  for (int g = threadIdx.x; g < ng; g += NT) {
     const int e0 = g << 4;
     double v[16];
     load16<Src>(s + e0, v);
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict_
   __syncthreads();
   if (MB > 1 && rf.m > 1) {
     const int p = 1 << k;
-    for (int b = threadIdx.x; b < p; b += kFwThreads)
+    for (int b = threadIdx.x; b < p; b += NT)
       mix_column<T, MB>(buf + lpad(b), p + (p >> 4), rf.m, rf.q, rf.transpose);
     __syncthreads();
   }
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kFwThreads, 6) void row_fwht(const Src* __restrict_
     const int first = lo - wlo;
     const int lstep = (1 << wlo) + (1 << (wlo - 4));
     const uint32_t gstep = uint32_t(sizeof(Dst)) << wlo;
-    for (int g = threadIdx.x; g < ng; g += kFwThreads) {
+    for (int g = threadIdx.x; g < ng; g += NT) {
       const int a = g >> kg, idx = g & ((1 << kg) - 1);
       const int e0 = (a << k) + (idx & ((1 << wlo) - 1)) + ((idx >> wlo) << (wlo + 4));
       T* b0 = buf + lpad(e0);
@@ -715,13 +716,16 @@ kq_status launch_rows_t(const Src* src, int64_t lds, int64_t rows, int64_t n, Ds
 template <typename T, typename Src, typename Dst, int MB>
 kq_status launch_fw_mb(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, const RowFw& rf,
                        size_t lds_bytes, hipStream_t st) {
-  auto kern = row_fwht<T, Src, Dst, MB>;
+  // a row staged in more than half of the LDS leaves one workgroup per CU: it gets 16 waves, so that
+  // the CU still has enough loads in flight (4 waves stalled on them at 28672-long rows)
+  const bool wide = lds_bytes > kLdsBudget / 2;
+  auto kern = wide ? row_fwht<T, Src, Dst, MB, kFwThreadsWide> : row_fwht<T, Src, Dst, MB, kFwThreads>;
   kq_status r = allow_lds(kern, "row_fwht");
   if (r != KQ_OK) return r;
   {
     LaunchTimer timer("row_fwht", st);
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kFwThreads), lds_bytes, st, src, lds, n, dst,
-                       ldd, rf);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(wide ? kFwThreadsWide : kFwThreads), lds_bytes, st,
+                       src, lds, n, dst, ldd, rf);
   }
   return check_launch("row_fwht");
 }

@@ -32,8 +32,10 @@
 //      (the substitution runs one block behind the factor, so its panel is the
 //      super-panel shifted by one block). Each element of the trailing matrix
 //      is read and written once per super-panel instead of once per block, a
-//      quarter of the HBM traffic of the one-level form; all products are
-//      128 x 128 tiles on float32 MFMA (v_mfma_f32_32x32x2f32);
+//      quarter of the HBM traffic of the one-level form. Products are 128 x 128
+//      tiles: float32 MFMA (v_mfma_f32_32x32x2f32) inside a super-panel, and
+//      for the rank-256 launches bfloat16 MFMA on an exact three-piece split of
+//      each float32 operand (float32-level products at 2.7x the float32 rate);
 //   4. R = J M J written over H (strict lower triangle zeroed).
 // A pivot that is not positive and finite stops the chain: `info` takes the
 // original index + 1 and every later kernel returns at once.
@@ -174,6 +176,145 @@ __device__ __forceinline__ void gemm128(GemmLds& sm, const float* a, int64_t lda
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
+    if (ch + 1 < nchunk) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (beta != 0.0f) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc] = alpha * acc[x][y][r] + beta * old[x][y][r];
+        }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc] = alpha * acc[x][y][r];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same 128 x 128 tile product with float32 operands on bfloat16 MFMA
+// (v_mfma_f32_32x32x16_bf16, 16x the float32 MFMA rate): each operand x is
+// split exactly into three round-to-nearest bfloat16 pieces, x = hi + mid + lo
+// (8 + 8 + 8 significant bits), and the product takes the six piece products
+// whose weight is at least 2^-16 of hi * hi: hi*hi, hi*mid, mid*hi, hi*lo,
+// mid*mid, lo*hi. Each piece product is exact in float32 and accumulates in
+// the MFMA's float32 accumulator, so the result carries float32-level
+// rounding (the dropped terms are below 2^-24 relative). Staging as in gemm128
+// (float32 chunks of 16 k, k-major in LDS); a lane's operand of one k-step is
+// 8 consecutive k of one row (lanes 0-31: k 0..7, lanes 32-63: k 8..15).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct Split3 {
+  bf16x8 hi, mid, lo;
+};
+
+__device__ __forceinline__ Split3 split3(const float (&v)[8]) {
+  Split3 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(v[e]);
+    const float r1 = v[e] - static_cast<float>(h);   // exact: below half a bfloat16 ulp of v
+    const __bf16 m = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(m);     // exact, at most 8 significant bits
+    s.hi[e] = h;
+    s.mid[e] = m;
+    s.lo[e] = static_cast<__bf16>(r2);               // exact
+  }
+  return s;
+}
+
+__device__ __forceinline__ f32x16 mfma_split(const Split3& a, const Split3& b, f32x16 acc) {
+  // smallest terms first
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.lo, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b.mid, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b.lo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b.mid, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  return acc;
+}
+
+template <bool TB>
+__device__ __forceinline__ void gemm128_split(GemmLds& sm, const float* a, int64_t lda, const float* b, int64_t ldb,
+                                              float* c, int64_t ldc, int m_valid, int n_valid, int k0, int k1,
+                                              float alpha, float beta) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  const bool rows_ok[2] = {wi * 64 < m_valid, wi * 64 + 32 < m_valid};
+  const bool cols_ok[2] = {wj * 64 < n_valid, wj * 64 + 32 < n_valid};
+  float* cp[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+      cp[x][y] = c + int64_t(wi * 64 + x * 32 + 4 * (lane >> 5)) * ldc + wj * 64 + y * 32 + (lane & 31);
+  f32x16 old[2][2];
+  if (beta != 0.0f) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        if (rows_ok[x] && cols_ok[y]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) old[x][y][r] = cp[x][y][int64_t(8 * (r >> 2) + (r & 3)) * ldc];
+        }
+  }
+  const int nchunk = (k1 - k0) / kGK;
+  float4 va[2], vb[2];
+  auto load = [&](int kc) {
+    load_rows(a, lda, m_valid, kc, va);
+    if (TB) load_rows(b, ldb, n_valid, kc, vb);
+    else load_cols(b, ldb, n_valid, kc, vb);
+  };
+  auto store = [&](int buf) {
+    store_rows(sm.a[buf], va);
+    if (TB) store_rows(sm.b[buf], vb);
+    else store_cols(sm.b[buf], vb);
+  };
+  if (nchunk > 0) {
+    load(k0);
+    store(0);
+  }
+  __syncthreads();
+  const int kb = 8 * (lane >> 5), ln = lane & 31;
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunk) load(k0 + (ch + 1) * kGK);
+    Split3 fa[2], fb[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sm.a[buf][kb + e][wi * 64 + x * 32 + ln];
+      fa[x] = split3(v);
+    }
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sm.b[buf][kb + e][wj * 64 + y * 32 + ln];
+      fb[y] = split3(v);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = mfma_split(fa[x], fb[y], acc[x][y]);
     if (ch + 1 < nchunk) store(buf ^ 1);
     __syncthreads();
   }
@@ -695,7 +836,7 @@ __global__ __launch_bounds__(256) void chol_far_kernel(float* __restrict__ a, fl
     const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
     const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
     const int64_t k0 = int64_t(s0) * kB;
-    gemm128<true>(sm, a + ri * dp + k0, dp, a + rj * dp + k0, dp, a + ri * dp + rj, dp, mv, nv, 0,
+    gemm128_split<true>(sm, a + ri * dp + k0, dp, a + rj * dp + k0, dp, a + ri * dp + rj, dp, mv, nv, 0,
                   (s1 - s0) * kB, -1.0f, 1.0f);
     return;
   }
@@ -707,7 +848,7 @@ __global__ __launch_bounds__(256) void chol_far_kernel(float* __restrict__ a, fl
   const int nv = static_cast<int>(cend - cj < kG ? cend - cj : kG);
   const int kb0 = s0 > 0 ? s0 - 1 : 0;
   const int64_t k0 = int64_t(kb0) * kB;
-  gemm128<false>(sm, a + ri * dp + k0, dp, m + k0 * dp + cj, dp, m + ri * dp + cj, dp, mv, nv, 0,
+  gemm128_split<false>(sm, a + ri * dp + k0, dp, m + k0 * dp + cj, dp, m + ri * dp + cj, dp, mv, nv, 0,
                  (s1 - 1 - kb0) * kB, 1.0f, 1.0f);
 }
 

@@ -46,6 +46,16 @@ def rel_fro(got: np.ndarray, want: np.ndarray) -> float:
     return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
 
 
+def scale_tolerance(r_err: float) -> float:
+    """Relative tolerance of the group scales given the factor's relative Frobenius error.
+
+    A group's scale comes from the error-fed weights of its columns; the feedback is the
+    earlier columns' errors times rows of R, so the scale carries R's relative error (up to a
+    factor near one). 1e-5 where R is within 3.3e-6, three times R's error beyond that (in
+    the worst-conditioned layers: the float32 factor of a float32 H_X'' at condition ~1e4)."""
+    return max(1e-5, 3.0 * r_err)
+
+
 def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_frac=1e-4, scale_rtol=1e-5,
                 label="", block=None):
     """Code parity: replay the oracle's sweep on (w2, r), adopting the kernel's

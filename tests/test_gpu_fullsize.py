@@ -129,7 +129,7 @@ def test_fullsize_q_proj_chain():
     r = host(hxd)
     e_r = rel_fro(r, r_ref)
     print(f"Cholesky: R {e_r:.2e} relative Frobenius", flush=True)
-    assert e_r <= 1e-4 and e_r <= 2e-5
+    assert e_r <= 1e-4 and e_r <= 1e-5  # measured 3.5e-6
 
     ng = din // cfg.group
     codes = torch.empty((dout, din), dtype=torch.uint8, device=DEV)

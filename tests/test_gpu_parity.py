@@ -12,7 +12,7 @@ import pytest
 
 import kq_synth
 import oracle
-from gpu_helpers import DEV, bits_to_dev, check_codes, host, rel_fro, require_gpu, to_dev
+from gpu_helpers import DEV, bits_to_dev, check_codes, host, rel_fro, require_gpu, scale_tolerance, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -290,7 +290,7 @@ def _run_layer(wl, sub, group_key, flags=None, bits=None):
                 loss=float(loss.item()))
 
 
-def _check_layer(wl, sub, group_key, got, flags=(True, True, True), scale_rtol=1e-5):
+def _check_layer(wl, sub, group_key, got, flags=(True, True, True)):
     cfg = wl.cfg
     inp, out, scale = flags
     x, g = wl.x(group_key), wl.g(sub)
@@ -301,9 +301,11 @@ def _check_layer(wl, sub, group_key, got, flags=(True, True, True), scale_rtol=1
     w2, hx2, _, sx, sg = oracle.biip_forward(w64, hx, hg, wl.rot_in(group_key), wl.rot_out(sub), inp=inp, out=out,
                                              scale=scale)
     r = oracle.chol_inv_upper(hx2, cfg.damp)
-    assert rel_fro(got["r"], r) <= 1e-4
+    e_r = rel_fro(got["r"], r)
+    print(f"{sub}: R {e_r:.2e} relative Frobenius", flush=True)
+    assert e_r <= 1e-4
     res = check_codes(got["codes"], got["zeros"], got["scales"], w2, r, got["bits"], cfg.group, label=sub,
-                      scale_rtol=scale_rtol)
+                      scale_rtol=scale_tolerance(e_r))
     w_hat = oracle.biip_inverse(res.what, wl.rot_in(group_key), wl.rot_out(sub), sx, sg, inp=inp, out=out)
     want_loss = oracle.kron_loss(w_hat - w64, hx, hg)
     got_loss = oracle.kron_loss(got["w_hat"] - w64, hx, hg)
@@ -341,11 +343,10 @@ def test_layer_ablation_modes(inp, out, scale):
     wl = _workload(2, 12000, {"q_proj": (256, 384)})
     flags = (kq.KQ_BIIP_INPUT * inp) | (kq.KQ_BIIP_OUTPUT * out) | (kq.KQ_BIIP_SCALE * scale)
     got = _run_layer(wl, "q_proj", "attn_in", flags=flags, bits=2)
-    # Without the diagonal rescale H_X'' keeps the inputs' lognormal channel spread, and the
-    # float32 factor's relative error (bounded by the R tolerance, 1e-4) reaches the group
-    # ranges of the error-fed weights: the scales are held to that bound instead of 1e-5.
-    _check_layer(wl, "q_proj", "attn_in", got, flags=(bool(inp), bool(out), bool(scale)),
-                 scale_rtol=1e-5 if (scale or not inp) else 1e-4)
+    # Without the diagonal rescale H_X'' keeps the inputs' lognormal channel spread (condition
+    # ~1e4 after damping): the scales are held to three times the factor's measured error
+    # (scale_tolerance), 1.4e-5 measured against a 1e-5 floor.
+    _check_layer(wl, "q_proj", "attn_in", got, flags=(bool(inp), bool(out), bool(scale)))
 
 
 def test_layer_config4_scaled_outliers():

@@ -23,6 +23,8 @@
 // Float64 keeps the rounding argument w / s of every entry within about
 // 1e-6 grid units of the float64 oracle across thousands of columns, where a
 // float32 sweep drifts past 1e-5.
+#include <type_traits>
+
 #include "kq_internal.h"
 
 namespace kq {
@@ -181,15 +183,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// Sweep of block [c0, c0 + B) for rows [16 wg, 16 wg + 16); writes the scaled
-// errors of the block to e_out [dout, B]. Groups are powers of two dividing B:
+// Sweep of block [c0, c0 + B) for rows [16 wg, 16 wg + 16). First the errors of
+// the nq blocks before it that no earlier launch applied to it (nq = 1 inside a
+// super-block, kSB at its first block) are applied: e_prev holds them for
+// columns c0 - nq B .. c0, rows of pitch pe. Then the sweep; the block's scaled
+// errors go to e_out (rows of pitch pe). Groups are powers of two dividing B:
 // with SG false (no group, or group >= 16) a group can start only at a
 // 16-column slice, so the grid code sits outside the unrolled column loop.
-template <int B, bool SG>
+template <int B, bool SG, bool TL>
 __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, const float* __restrict__ r,
                            int64_t dout, int64_t din, int64_t c0, int bits, int group, uint8_t* __restrict__ codes,
                            float* __restrict__ scales, uint8_t* __restrict__ zeros, double* __restrict__ preround,
-                           const double* __restrict__ e_prev, double* __restrict__ e_out) {
+                           const double* __restrict__ e_prev, int nq, double* __restrict__ e_out, int pe) {
   constexpr int EPL = B / 16;
   auto& rl = sm.rl;
   auto& rinv = sm.rinv;
@@ -213,37 +218,46 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   // 1 / R_jj of the block, one division per thread j < B
   const float rjj = tid < B ? r[(c0 + tid) * din + c0 + tid] : 1.0f;
   if (c0 > 0) {
-    // previous block's errors of these rows: x -= E_prev R[c0-B:c0, c0:c0+B] for the
-    // workgroup's 16 rows, as a 16 x B x B product on float64 MFMA (v_mfma_f64_16x16x4f64)
-    // with R staged in the sweep's LDS layout (all entries)
-    RBlock<B> rnear;
-    load_r<B>(rnear, r, din, c0 - B, c0);
-    load_r<B>(rdiag, r, din, c0, c0);
-    // A operand of k-step kk: lane i + 16 c holds E_prev[row i of the workgroup][4 kk + c]
+    // earlier blocks' errors of these rows: x -= E_prev R[c0-nq B:c0, c0:c0+B] for the
+    // workgroup's 16 rows, as a 16 x (nq B) x B product on float64 MFMA (v_mfma_f64_16x16x4f64),
+    // one B x B block of R at a time, staged in the sweep's LDS layout (all entries)
     constexpr int KS = B / 4, NT = B / 16, TPW = (NT + 3) / 4;
     const int lane = tid & 63, wave = tid >> 6;
     const int64_t erow = int64_t(wg) * kRowsPerWg + (lane & 15);
-    const double* ep = e_prev + (erow < dout ? erow : 0) * B + (lane >> 4);
-    double ea[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) ea[kk] = ep[4 * kk];
-    store_r<B, false>(rnear, rl);
-    lds_barrier();
-    // 16-column tiles: wave w takes tiles w, w + 4, ...; B operand of k-step kk for tile t:
-    // lane j + 16 c holds R[c0 - B + 4 kk + c][c0 + 16 t + j] = rl[4 kk + c][j EPL + t]
     f64x4 acc[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) acc[u] = f64x4{};
+    const int nqb = TL ? nq : 1;  // one-level: always the previous block only
+    // one earlier block q of R; the last one also loads the block's own R (peeled, so that
+    // block is live only there and the runtime loop over the others holds one R block)
+    auto near = [&](int q, auto last) {
+      RBlock<B> rnear;
+      load_r<B>(rnear, r, din, c0 - int64_t(nqb - q) * B, c0);
+      if constexpr (decltype(last)::value) load_r<B>(rdiag, r, din, c0, c0);
+      // A operand of k-step kk: lane i + 16 c holds E_prev[row i of the workgroup][q B + 4 kk + c]
+      const double* ep = e_prev + (erow < dout ? erow : 0) * pe + q * B + (lane >> 4);
+      double ea[KS];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+      for (int kk = 0; kk < KS; ++kk) ea[kk] = ep[4 * kk];
+      if (q > 0) lds_barrier();  // every wave is done reading the previous R block
+      store_r<B, false>(rnear, rl);
+      lds_barrier();
+      // 16-column tiles: wave w takes tiles w, w + 4, ...; B operand of k-step kk for tile t:
+      // lane j + 16 c holds R[c0 - (nq - q) B + 4 kk + c][c0 + 16 t + j] = rl[4 kk + c][j EPL + t]
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const int t = wave + 4 * u;
-        if (t < NT)
-          acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-              ea[kk], static_cast<double>(rl[4 * kk + (lane >> 4)][(lane & 15) * EPL + t]), acc[u], 0, 0, 0);
-      }
-    lds_barrier();  // every wave is done reading the previous block's R
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int t = wave + 4 * u;
+          if (t < NT)
+            acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                ea[kk], static_cast<double>(rl[4 * kk + (lane >> 4)][(lane & 15) * EPL + t]), acc[u], 0, 0, 0);
+        }
+    };
+    if constexpr (TL)
+      for (int q = 0; q + 1 < nqb; ++q) near(q, std::false_type{});
+    near(nqb - 1, std::true_type{});
+    lds_barrier();  // every wave is done reading the last R block
     // the product, row 4 q + lane / 16 and column 16 t + lane % 16 in register q, goes through
     // LDS (over the R block just read) into the sweep layout
     double (*prod)[B] = reinterpret_cast<double (*)[B]>(&rl[0][0]);
@@ -311,7 +325,7 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
       w[row * din + col] = x[eo];
       codes[row * din + col] = static_cast<uint8_t>(qcur);
       if (preround) preround[row * din + col] = tcur;
-      e_out[row * B + l16 + 16 * eo] = ecur;
+      e_out[row * pe + l16 + 16 * eo] = ecur;
     }
 #pragma unroll
     for (int e = eo + 1; e < EPL; ++e)
@@ -321,15 +335,16 @@ __device__ void sweep_role(SweepLds<B>& sm, int wg, double* __restrict__ w, cons
   }
 }
 
-// Tile of W[rows, cols] -= E R[k0 .. k0 + B, cols] on float64 MFMA
+// Tile of W[rows, cols] -= E R[k0 .. k0 + K, cols] on float64 MFMA
 // (v_mfma_f64_16x16x4f64): TM x TN output tile at (i0, j0), 4 waves in a
 // WR x WC grid, each a grid of 16 x 16 blocks. The accumulators start as the
 // W tile (read at entry, under the first chunk's loads) and -E goes into LDS,
 // so the MFMAs produce W - E R directly and the exit only stores. k advances
 // in chunks of 16 through two LDS buffers held k-major ([k][row], [k][column]);
 // the next chunk is loaded into registers (R converted to float64 on its way
-// into LDS) while the current one is multiplied. E is [dout, B]; the column
-// extent is a multiple of 32; rows past dout read as zero and are not written.
+// into LDS) while the current one is multiplied. E rows have pitch pe; columns
+// run to col_end (a multiple of 32); rows past dout read as zero and are not
+// written.
 constexpr int kTK = 16;  // k chunk
 
 // Row pitch TM + 16 (TN + 16) doubles: the four k rows one MFMA operand read
@@ -340,16 +355,16 @@ struct TileLds {
   double bs[2][kTK][TN + 16];
 };
 
-template <int B, int TM, int TN, int WR, int WC>
+template <int K, int TM, int TN, int WR, int WC>
 __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restrict__ w, const float* __restrict__ r,
-                                          const double* __restrict__ e, int64_t dout, int64_t din, int64_t k0,
-                                          int64_t i0, int64_t j0) {
+                                          const double* __restrict__ e, int64_t pe, int64_t dout, int64_t din,
+                                          int64_t col_end, int64_t k0, int64_t i0, int64_t j0) {
   static_assert(WR * WC == 4 && TM % (16 * WR) == 0 && TN % (16 * WC) == 0, "tile shape");
   constexpr int BM = TM / WR / 16, BN = TN / WC / 16;  // 16 x 16 blocks per wave
   constexpr int DA = TM / 16;                          // doubles of E per thread per chunk
   static_assert(DA % 2 == 0 && (kTK * TN) % 256 == 0, "chunk shape");
   const int mv = static_cast<int>(dout - i0 < TM ? dout - i0 : TM);
-  const int nv = static_cast<int>(din - j0 < TN ? din - j0 : TN);
+  const int nv = static_cast<int>(col_end - j0 < TN ? col_end - j0 : TN);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = wave / WC, wj = wave % WC;
@@ -361,7 +376,7 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
   const int bc = tid % TN, bk0 = tid / TN;
   constexpr int BKS = 256 / TN;  // R rows between a thread's elements
   const bool a_ok = ar < mv, b_ok = bc < nv;
-  const double* ap = e + (i0 + (a_ok ? ar : 0)) * B + ak;
+  const double* ap = e + (i0 + (a_ok ? ar : 0)) * pe + ak;
   const float* bp = r + (k0 + bk0) * din + j0 + (b_ok ? bc : 0);
   // two register sets: the chunk two ahead loads while one is multiplied and one waits
   double2 va[2][DA / 2];
@@ -400,7 +415,7 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
         acc[x][y][q] = wr[j < nv ? j : 0];
       }
     }
-  constexpr int nchunk = B / kTK;
+  constexpr int nchunk = K / kTK;
   load(0, 0);
   if (nchunk > 1) load(1, kTK);
   store(0, 0);
@@ -439,12 +454,25 @@ __device__ __forceinline__ void tile_role(TileLds<TM, TN>& sm, double* __restric
     }
 }
 
-// One step of the sweep: workgroups [0, n_sweep) sweep block [c0, c0 + B)
-// (errors to e_cur), the others apply the previous block's errors e_prev to
-// every column from c0 + B on in 128 x 128 tiles. The two roles touch
-// disjoint columns, so the latency-bound sweep and the MFMA-bound update
-// share the GPU.
+// One step of the sweep, two-level: blocks of B columns are grouped in
+// super-blocks of sb blocks (sb = kSB where the float64 W'' is larger than the
+// Infinity Cache; sb = 1, every launch updating every later column, where it
+// fits: there the far updates hit the cache and the three launches of a
+// super-block with little far work would leave the sweep's latency exposed). Workgroups [0, n_sweep) apply the errors no earlier
+// launch applied to block [c0, c0 + B) and sweep it (errors to e_out); the others
+// apply earlier errors to columns beyond the block, in 128 x 128 tiles:
+//   * inside a super-block: the previous block's errors (rank B) to the rest of
+//     the super-block, [c0 + B, super-block end);
+//   * at a super-block's first block: the whole previous super-block's errors
+//     (rank sb B) to every column from c0 + B on.
+// So the columns right of a super-block are read and written once per super-block
+// instead of once per block; each block still receives every earlier error before
+// its sweep (the previous super-block's in its own launch at a super-block start,
+// the earlier blocks of its own super-block through the far updates of the
+// launches between). The roles touch disjoint columns, so the latency-bound sweep
+// shares the GPU with the MFMA-bound update.
 constexpr int kFT = 128;  // far tile edge
+constexpr int kSB = 4;    // blocks per super-block
 
 template <int B>
 union StepLds {
@@ -453,42 +481,75 @@ union StepLds {
 };
 
 // Two waves per SIMD: a sweep workgroup and a far-update workgroup share each CU.
-template <int B, bool SG>
+// TL: two-level (super-blocks); the one-level kernel carries only the rank-B far tile.
+template <int B, bool SG, bool TL>
 __global__ __launch_bounds__(256, 2) void obs_step_kernel(double* __restrict__ w, const float* __restrict__ r,
                                                    int64_t dout, int64_t din, int64_t c0, int bits, int group,
                                                    uint8_t* __restrict__ codes, float* __restrict__ scales,
                                                    uint8_t* __restrict__ zeros, double* __restrict__ preround,
-                                                   const double* __restrict__ e_prev, double* __restrict__ e_cur,
-                                                   int n_sweep, int far_cols) {
+                                                   const double* __restrict__ e_near, int nq,
+                                                   double* __restrict__ e_out, int pe, const double* __restrict__ e_far,
+                                                   int kfar, int64_t far_end, int n_sweep, int far_cols) {
   __shared__ StepLds<B> sm;
   const int b = blockIdx.x;
   if (b < n_sweep) {
-    sweep_role<B, SG>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_prev, e_cur);
+    sweep_role<B, SG, TL>(sm.sw, b, w, r, dout, din, c0, bits, group, codes, scales, zeros, preround, e_near, nq,
+                          e_out, pe);
     return;
   }
   const int t = b - n_sweep;
-  const int64_t c1 = c0 + B;
-  tile_role<B, kFT, kFT, 2, 2>(sm.tl, w, r, e_prev, dout, din, c0 - B, int64_t(t / far_cols) * kFT,
-                               c1 + int64_t(t % far_cols) * kFT);
+  const int64_t i0 = int64_t(t / far_cols) * kFT, j0 = c0 + B + int64_t(t % far_cols) * kFT;
+  if constexpr (TL) {
+    if (kfar == kSB) {
+      tile_role<kSB * B, kFT, kFT, 2, 2>(sm.tl, w, r, e_far, pe, dout, din, far_end, c0 - kSB * B, i0, j0);
+      return;
+    }
+  }
+  tile_role<B, kFT, kFT, 2, 2>(sm.tl, w, r, e_far, pe, dout, din, far_end, c0 - B, i0, j0);
 }
+
+// Super-block size: kSB where the float64 W'' (dout x din) exceeds the 256 MB Infinity Cache.
+inline int super_blocks(int64_t dout, int64_t din) { return dout * din * 8 > (int64_t(256) << 20) ? kSB : 1; }
 
 template <int B>
 kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int bits, int group, uint8_t* codes,
                      float* scales, uint8_t* zeros, double* preround, double* e, hipStream_t st) {
   const int n_sweep = static_cast<int>((dout + kRowsPerWg - 1) / kRowsPerWg);
   const int far_rows = static_cast<int>((dout + kFT - 1) / kFT);
-  double* ebuf[2] = {e, e + dout * B};
+  // errors of two consecutive super-blocks, rows of nsb B
+  const int nsb = super_blocks(dout, din);
+  const int pe = nsb * B;
+  double* ebuf[2] = {e, e + dout * pe};
   kq_status s;
   for (int64_t c0 = 0, k = 0; c0 < din; c0 += B, ++k) {
-    double* e_prev = ebuf[(k + 1) & 1];
-    const int64_t rest = din - c0 - B;  // columns beyond this block
-    const int far_cols = (k > 0 && rest > 0) ? static_cast<int>((rest + kFT - 1) / kFT) : 0;
+    const int64_t sb = k / nsb, j = k % nsb;
+    double* e_cur = ebuf[sb & 1];
+    const double* e_near = nullptr;
+    const double* e_far = nullptr;
+    int nq = 0, kfar = 1;
+    int64_t far_end = c0 + B;
+    if (k > 0 && j == 0) {  // super-block start: the whole previous super-block
+      e_near = ebuf[(sb + 1) & 1];
+      nq = nsb;
+      e_far = e_near;
+      kfar = nsb;
+      far_end = din;
+    } else if (j > 0) {      // inside a super-block: the previous block, to the rest of the super-block
+      e_near = e_cur + (j - 1) * B;
+      nq = 1;
+      e_far = e_near;
+      kfar = 1;
+      far_end = (sb + 1) * nsb * B < din ? (sb + 1) * nsb * B : din;
+    }
+    const int far_cols = far_end > c0 + B ? static_cast<int>((far_end - c0 - B + kFT - 1) / kFT) : 0;
     {
       LaunchTimer timer("obs_step_kernel", st);
       const bool small_group = group > 0 && group < 16;  // groups that start inside a 16-column slice
-      auto kern = small_group ? obs_step_kernel<B, true> : obs_step_kernel<B, false>;
-      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_sweep + far_cols * far_rows)), dim3(256), 0, st, w, r, dout,
-                         din, c0, bits, group, codes, scales, zeros, preround, e_prev, ebuf[k & 1], n_sweep, far_cols);
+      auto kern = nsb > 1 ? (small_group ? obs_step_kernel<B, true, true> : obs_step_kernel<B, false, true>)
+                          : (small_group ? obs_step_kernel<B, true, false> : obs_step_kernel<B, false, false>);
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_sweep + far_cols * far_rows)), dim3(256), 0, st, w, r,
+                         dout, din, c0, bits, group, codes, scales, zeros, preround, e_near, nq, e_cur + j * B, pe,
+                         e_far, kfar, far_end, n_sweep, far_cols);
     }
     if ((s = check_launch("obs_step_kernel")) != KQ_OK) return s;
   }
@@ -499,7 +560,7 @@ kq_status run_blocks(double* w, const float* r, int64_t dout, int64_t din, int b
 
 size_t obs_workspace(int64_t dout, int64_t din, int block) {
   (void)din;
-  return align_up(2 * size_t(dout) * block * sizeof(double), 256);  // errors of two consecutive blocks
+  return align_up(2 * size_t(dout) * kSB * block * sizeof(double), 256);  // errors of two consecutive super-blocks
 }
 
 kq_status obs_run(double* w, const float* r, int64_t dout, int64_t din, int bits, int group, int block,

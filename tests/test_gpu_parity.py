@@ -450,3 +450,32 @@ def test_layer_runs_twice_bit_identical():
     for k in ("hx", "hg", "r", "codes", "scales", "zeros", "w_hat"):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     assert a["score"] == b["score"] and a["loss"] == b["loss"]
+
+
+@pytest.mark.parametrize("din,block,group,bits", [(4096, 128, 128, 2), (4064, 32, 16, 4), (4032, 64, 64, 3),
+                                                  (4096, 32, 0, 2)])
+def test_obs_two_level(din, block, group, bits):
+    """The sweep's two-level form (super-blocks of 4 blocks, taken where the float64 W'' exceeds
+    256 MB: 8448 rows here) against the oracle's replay on sampled rows: every block size, small
+    groups, a per-row grid and a partial last super-block (4064 = 31.75 super-blocks of 128)."""
+    import torch
+    kq, _ = _kq()
+    dout = 8448
+    assert dout * din * 8 > 256 << 20
+    print(f"two-level obs {dout}x{din} block={block} group={group} bits={bits}", flush=True)
+    rng = np.random.default_rng(din + block + group)
+    r = oracle.chol_inv_upper(_spd(rng, din, 1.5), 0.01).astype(np.float32)
+    w2 = rng.normal(0.0, 0.02, (dout, din))
+    wd = to_dev(w2)
+    ng = din // group if group else 1
+    codes = torch.empty((dout, din), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((dout, ng), dtype=torch.float32, device=DEV)
+    zeros = torch.empty((dout, ng), dtype=torch.uint8, device=DEV)
+    kq.obs_quantize(wd, to_dev(r), bits, group, block, codes, scales, zeros)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 15, 16, dout - 1], rng.choice(dout, 60, replace=False)]))
+    check_codes(host(codes)[rows], host(zeros)[rows], host(scales)[rows], w2[rows], r.astype(np.float64), bits, group,
+                label=f"two-level b{bits} g{group} B{block}", block=block)
+    gi = (torch.arange(din, device=DEV) // group) if group else torch.zeros(din, dtype=torch.long, device=DEV)
+    deq = scales.double()[:, gi] * (codes.double() - zeros.double()[:, gi])
+    assert torch.equal(deq, wd), "W^'' is not s (code - zero) everywhere"

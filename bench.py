@@ -32,6 +32,11 @@ steps): its algorithmic flops per launch over its average launch duration,
 timed with HIP events that the library records around each launch on its
 stream during the timed steps. The CPU baseline is the float64 oracle timed
 on a bounded sample of the same workload on this host, scaled to one step.
+
+--peaks measures the machine instead: sustained bf16, float32 and float64
+MFMA rates (random and constant operands, with the shader clock they ran at)
+and a device-to-device copy, as context for the published peaks the rooflines
+are priced against.
 """
 from __future__ import annotations
 
@@ -66,6 +71,8 @@ def parse_args():
                    help="calibration capture of one LLaMA-2-7B block (forward + one backward) and its covariances")
     p.add_argument("--decode-per-layer", action="store_true",
                    help="with --decode: one kq_decode_matvec call per layer instead of one group call per shared input")
+    p.add_argument("--peaks", action="store_true",
+                   help="instead of the quantization step: sustained MFMA rates and HBM copy bandwidth")
     p.add_argument("--traffic-summary", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
                    help="no run: turn two rocprofv3 --pmc runs of '--copy-calibration' (FETCH_SIZE, then "
                         "WRITE_SIZE) into the per-launch HBM bytes of KERNEL, written to "
@@ -848,6 +855,94 @@ def quant_bench(args) -> int:
     return 0
 
 
+PEAK_PROBES = [  # (kind, name, published dense peak TFLOP/s, wave-rounds per launch)
+    (0, "bf16 MFMA, random operands", 2500.0, 60000),
+    (1, "bf16 MFMA, constant operands", 2500.0, 60000),
+    (2, "float32 MFMA, random operands", 157.3, 30000),
+    (3, "float32 MFMA, constant operands", 157.3, 30000),
+    (4, "float64 MFMA, random operands", 78.6, 30000),
+    (5, "float64 MFMA, constant operands", 78.6, 30000),
+]
+
+
+def peaks_bench(args) -> int:
+    """Sustained MFMA rates (each probe launched `warmup` + `steps` times, ~50 ms per launch; the
+    median of the timed launches) and a 4 GiB device-to-device copy, one JSON line."""
+    import ctypes
+    import statistics
+    import torch
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "post_quantization_04_amd", "libkq_peaks.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m post_quantization_04_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.kqp_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kqp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.kqp_flops_per_round.restype = ctypes.c_double
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    blocks = lib.kqp_mfma_blocks()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    probes = {}
+    for kind, name, peak, iters in PEAK_PROBES:
+        runs = []
+        for rep in range(args.warmup + args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            if lib.kqp_mfma(kind, iters, out.data_ptr(), clk.data_ptr(), ctypes.c_void_p(st.cuda_stream)) != 0:
+                raise RuntimeError(f"probe {name} failed to launch")
+            e1.record(st)
+            e1.synchronize()
+            if rep < args.warmup:
+                continue
+            ms = e0.elapsed_time(e1)
+            c = clk.tolist()
+            mhz = 100.0 * (c[2] - c[0]) / (c[3] - c[1]) if c[3] > c[1] else None
+            flops = lib.kqp_flops_per_round(kind) * iters * blocks * 4
+            runs.append((flops / ms / 1e9, mhz, ms))
+        tf = statistics.median(r[0] for r in runs)
+        mhz = statistics.median(r[1] for r in runs if r[1] is not None)
+        probes[name] = {"tflops": round(tf, 1), "frac_of_published": round(tf / peak, 3),
+                        "shader_clock_mhz": round(mhz), "ms_per_launch": round(statistics.median(r[2] for r in runs), 2)}
+        log(f"{name}: {tf:.1f} TFLOP/s ({tf / peak:.1%} of {peak}), {mhz:.0f} MHz")
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    copies = []
+    for rep in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        if lib.kqp_copy(src.data_ptr(), dst.data_ptr(), nbytes, ctypes.c_void_p(st.cuda_stream)) != 0:
+            raise RuntimeError("copy probe failed to launch")
+        e1.record(st)
+        e1.synchronize()
+        if rep >= args.warmup:
+            copies.append(2 * nbytes / e0.elapsed_time(e1) / 1e6)
+    if not torch.equal(src, dst):
+        raise RuntimeError("copy probe: destination differs from source")
+    gbs = statistics.median(copies)
+    log(f"copy: {gbs:.0f} GB/s read + write ({gbs / HBM_PEAK_GBS:.1%} of {HBM_PEAK_GBS:.0f})")
+    runtime = []
+    for rep in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        dst.copy_(src)
+        e1.record(st)
+        e1.synchronize()
+        if rep >= args.warmup:
+            runtime.append(2 * nbytes / e0.elapsed_time(e1) / 1e6)
+    rt = statistics.median(runtime)
+    log(f"runtime device copy (torch copy_): {rt:.0f} GB/s read + write")
+    print(json.dumps({"metric": "peak_probes", "device": torch.cuda.get_device_name(dev),
+                      "launches_timed": args.steps, "mfma": probes,
+                      "copy": {"gb_per_s": round(gbs, 1), "bytes_per_launch": 2 * nbytes,
+                               "frac_of_published": round(gbs / HBM_PEAK_GBS, 3)},
+                      "runtime_copy": {"gb_per_s": round(rt, 1), "bytes_per_launch": 2 * nbytes,
+                                       "frac_of_published": round(rt / HBM_PEAK_GBS, 3)}}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     if args.traffic_summary:
@@ -859,6 +954,8 @@ def main() -> int:
         return 2
     if args.decode:
         return decode_bench(args)
+    if args.peaks:
+        return peaks_bench(args)
     if args.capture:
         return capture_bench(args)
     return quant_bench(args)

@@ -1,8 +1,10 @@
 """Build libkq.so for gfx950 in-tree: ``python -m post_quantization_04_amd.build``.
 
 Each HIP source is compiled to an object under ``_build/`` (in parallel) and
-linked into ``post_quantization_04_amd/libkq.so`` with hipcc. Packed float32
-instructions are disabled for all device code.
+linked into ``post_quantization_04_amd/libkq.so`` with hipcc. The peak probes
+(``csrc/peaks.hip``, not part of the quantization path) go into
+``post_quantization_04_amd/libkq_peaks.so``. Packed float32 instructions are
+disabled for all device code.
 """
 from __future__ import annotations
 
@@ -18,6 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
+PEAKS_LIB = os.path.join(HERE, "libkq_peaks.so")
 SOURCES = ["kq_api.hip", "timing.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip",
            "decode.hip", "loss.hip"]
 ARCH = "gfx950"
@@ -50,17 +53,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every HIP source and link libkq.so. Returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libkq.so failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{res.stderr}")
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every HIP source and link libkq.so and libkq_peaks.so. Returns libkq.so's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + ["peaks.hip"]
+    with concurrent.futures.ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAKS_LIB)
     return LIB
 
 

@@ -29,6 +29,29 @@ def declared_symbols():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kq_\w+)\s*\(", text, re.M)))
 
 
+def test_peak_probes_export_their_header():
+    """libkq_peaks.so (the machine probes behind bench.py --peaks) exports what kq_peaks.h declares."""
+    path = os.path.join(ROOT, "post_quantization_04_amd", "libkq_peaks.so")
+    if not os.path.exists(path):
+        pytest.skip("libkq_peaks.so not built")
+    text = open(os.path.join(ROOT, "include", "kq_peaks.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kqp_\w+)\s*\(", text, re.M)))
+    assert names == ["kqp_copy", "kqp_flops_per_round", "kqp_mfma", "kqp_mfma_blocks"]
+    P = ctypes.CDLL(path)
+    for name in names:
+        assert hasattr(P, name), name
+    P.kqp_flops_per_round.restype = ctypes.c_double
+    assert P.kqp_flops_per_round(0) == 16 * 32 * 32 * 16 * 2
+    assert P.kqp_flops_per_round(4) == 16 * 16 * 16 * 4 * 2
+    assert P.kqp_flops_per_round(9) == 0.0
+    # argument checks come before any launch
+    P.kqp_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.kqp_mfma(0, 0, FAKE, FAKE, None) == -1
+    assert P.kqp_mfma(0, 10, None, FAKE, None) == -1
+    P.kqp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert P.kqp_copy(FAKE, FAKE, 1000, None) == -1
+
+
 def test_header_declares_the_six_entry_points():
     syms = declared_symbols()
     for name in ("kq_accumulate_cov", "kq_biip_rotate", "kq_cholesky_inv", "kq_obs_quantize",
@@ -180,12 +203,14 @@ def test_workspace_sizes(L):
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8192, 512, 0) >= 3 * 256 * 256 * 4
     # 11008 channels = 946 tiles: about 8192 tile-slice items per launch would put all 9 token
     # slices in one launch; groups above 8 are cut to 8 (one whole slice per XCD), so the partials hold 8
-    # slices and a float64 sum of every tile carries the total across the two launches
+    # slices and a float64 sum of every tile carries the total across the two launches; the tile
+    # orders are the 256 slots of each 16 x 16 super-block (6 of them at 43 tile rows) and the
+    # blocked list of all tiles
     tile = 256 * 256
-    want = 8 * 946 * tile * 4 + 946 * tile * 8 + ((946 * 4 + 255) // 256) * 256
+    want = 8 * 946 * tile * 4 + 946 * tile * 8 + (((6 * 256 + 946) * 4 + 255) // 256) * 256
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8 * 16384 + 5000, 11008, 0) == want
     # 4096 channels over 16 slices: one launch, no float64 sums
-    want = 16 * 136 * tile * 4 + ((136 * 4 + 255) // 256) * 256
+    want = 16 * 136 * tile * 4 + (((256 + 136) * 4 + 255) // 256) * 256
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 16 * 16384, 4096, 0) == want
     assert L.kq_workspace_size(kq.KQ_OP_OBS, 100, 256, 128) >= 100 * 128 * 8
     assert L.kq_workspace_size(kq.KQ_OP_CHOLESKY, 100, 0, 0) >= 2 * 128 * 128 * 4

@@ -117,7 +117,8 @@ def _spd(rng, n, spread):
     return ((d[:, None] * (a @ a.T) * d[None, :]) / (2 * n)).astype(np.float32).astype(np.float64)
 
 
-BIIP_SHAPES = [(64, 128), (320, 384), (200, 448), (96, 1024)]
+# odd factors 1, 3, 5, 7, 25 (in registers) and 33, 45, 63 (on LDS tiles)
+BIIP_SHAPES = [(64, 128), (320, 384), (200, 448), (96, 1024), (360, 1008), (66, 1056)]
 
 
 @pytest.mark.parametrize("dout,din", BIIP_SHAPES)

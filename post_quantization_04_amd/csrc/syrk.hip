@@ -657,12 +657,12 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   // addresses a stage with 32-bit byte offsets.
   const bool pipe_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
                        int64_t(kKT) * lda * 2 < (int64_t(1) << 31);
-  // the orders the launches below use: blocked where a launch holds at least 8 slices
+  // whole slices per XCD (blocked order) where a launch holds at least 8 slices, else super-blocks
+  // shared by the XCDs; the tile orders are built for the launches below by the same rule
+  auto slices_of = [&](int g) { return (g * p.group + p.group <= p.nslices) ? p.group : p.nslices - g * p.group; };
+  auto superblocks_of = [&](int nsl) { return nsl >= kXcds ? 0 : p.nsb; };
   bool need_blocked = false, need_sb = false;
-  for (int g = 0; g < p.ngroups; ++g) {
-    const int nsl = (g * p.group + p.group <= p.nslices) ? p.group : p.nslices - g * p.group;
-    (nsl >= kXcds ? need_blocked : need_sb) = true;
-  }
+  for (int g = 0; g < p.ngroups; ++g) (superblocks_of(slices_of(g)) == 0 ? need_blocked : need_sb) = true;
   if (need_sb) {
     {
       LaunchTimer timer("superblock_order_kernel", st);
@@ -681,9 +681,8 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   }
   for (int g = 0; g < p.ngroups; ++g) {
     const int s0 = g * p.group;
-    const int nsl = (s0 + p.group <= p.nslices) ? p.group : p.nslices - s0;
-    // whole slices per XCD when there are enough of them, else super-blocks shared by the XCDs
-    const int nsb = nsl >= kXcds ? 0 : p.nsb;
+    const int nsl = slices_of(g);
+    const int nsb = superblocks_of(nsl);
     const int per_xcd = nsb == 0 ? p.ntiles * ((nsl + kXcds - 1) / kXcds) : nsb * 32 * nsl;
     const int* ord = nsb == 0 ? order + size_t(p.nsb) * 256 : order;
     const char* kname = pipe_ok ? "syrk_partial" : "syrk_partial_regs";

@@ -60,6 +60,8 @@ def parse_args():
     p.add_argument("--bits", type=int, default=2, choices=(2, 4), help="bit width of the LLaMA-2-7B q_proj (--config 2)")
     p.add_argument("--serial", action="store_true",
                    help="run every stage on one stream (per-stage profiles) instead of the two-stream schedule")
+    p.add_argument("--overlap", action="store_true",
+                   help="one layer: use the two-stream schedule at any width (by default only up to 8192 inputs)")
     p.add_argument("--reserve-cus", type=int, default=80,
                    help="CUs the second stream leaves to the Cholesky factor (0: no CU mask)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
@@ -545,7 +547,7 @@ def quant_bench(args) -> int:
     single = len(cfg.subs) == 1
     # two streams pay where the factor is latency-bound (its 64-wide steps leave CUs idle next to the
     # G covariance); at 28672 inputs the factor's rank-256 launches fill the GPU and one stream is as fast
-    overlap = single and not args.serial and cfg.subs[0].din <= 8192
+    overlap = single and not args.serial and (cfg.subs[0].din <= 8192 or args.overlap)
     # created before anything else takes a hardware queue: a CU-masked stream needs its own
     side = side_stream(dev, args.reserve_cus) if overlap else None
     wl = kq_synth.Workload(cfg)

@@ -31,6 +31,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 CHUNK_TOKENS = 8192
+DRIFT = 0.1  # input drift of the full-precision model, in units of the channel scale
 
 
 # ---------------------------------------------------------------------------
@@ -243,12 +244,22 @@ class Workload:
         raise ValueError(cfg.g_scale)
 
     # -- token-major bf16 matrices ----------------------------------------
-    def _chunk(self, kind: str, key: str, c: int, d: int, scales: np.ndarray) -> np.ndarray:
+    def _chunk_f32(self, kind: str, key: str, c: int, d: int, scales: np.ndarray) -> np.ndarray:
         rows = self.cfg.chunk_rows(c)
         rng = stream(self.cfg.id, kind + ":" + key, c, d)
         a = rng.standard_normal((rows, d), dtype=np.float32)
         a *= scales[None, :]
-        return f32_to_bf16_bits(a)
+        return a
+
+    def _chunk(self, kind: str, key: str, c: int, d: int, scales: np.ndarray) -> np.ndarray:
+        if kind == "xt":
+            # full-precision inputs: the same draws as "x" plus a seeded drift of DRIFT x the
+            # channel scale, rounded to bf16 on their own
+            a = self._chunk_f32("x", key, c, d, scales)
+            rng = stream(self.cfg.id, "xdrift:" + key, c, d)
+            a += DRIFT * rng.standard_normal(a.shape, dtype=np.float32) * scales[None, :]
+            return f32_to_bf16_bits(a)
+        return f32_to_bf16_bits(self._chunk_f32(kind, key, c, d, scales))
 
     def x_chunk(self, group: str, c: int) -> np.ndarray:
         return self._chunk("x", group, c, self.cfg.x_groups[group], self.x_scales(group))
@@ -278,6 +289,13 @@ class Workload:
     def g(self, sub: str) -> np.ndarray:
         """All output gradients of one sub-layer, [n_tokens, dout] bf16 bits."""
         return self._full("g", sub, self.cfg.sub(sub).dout, self.g_scales(sub))
+
+    def xt(self, group: str) -> np.ndarray:
+        """Full-precision-model inputs of one input group for the asymmetric (GPTAQ) objective,
+        [n_tokens, din] bf16 bits: x(group)'s values before rounding plus a seeded drift of
+        DRIFT x the channel scale. x(group) stands for the inputs the partly quantised model
+        sees."""
+        return self._full("xt", group, self.cfg.x_groups[group], self.x_scales(group))
 
     def drop(self, kind: str, key: str) -> None:
         self._cache.pop((kind, key), None)

@@ -16,7 +16,8 @@ Sources (cited by page title and section):
   [KQ-news] "KronQ: Kronecker Hessians break GPTQ's 2-bit wall", aimodeling.com news item.
   [KQ-art]  wmrh.cn popular article on KronQ: sections 二 (the Kronecker split),
             三 (BiIP and the trace score), 四 (H_G cancels from the column update),
-            六 (mixed precision), 七 (cost), 八 (ablations, diagonal scaling), Q&A.
+            六 (mixed precision), 七 (cost), 八 (ablations, diagonal scaling, the
+            GPTAQ base quantizer), Q&A.
 
 Readings where the pages are silent (each also listed in the design notes):
   * s_j = H_jj^(1/4) per side, 1 where H_jj <= 0 (the pages name only "the
@@ -30,6 +31,9 @@ Readings where the pages are silent (each also listed in the design notes):
     reaches the group's first column; per-row grids come from W'' before the sweep.
   * bit allocation: greedy by score (descending, ties by index) under an
     integer, parameter-weighted budget. Parity against the pages: unpinned.
+  * GPTAQ (row f2): every column's input drift (w_q dx_q) compensated by least squares on
+    the later columns' inputs, then GPTQ's sweep. Parity against the pages: unpinned (no
+    formula there).
 """
 from __future__ import annotations
 
@@ -47,7 +51,8 @@ __all__ = [
     "biip_inverse", "damped", "chol_inv_upper", "grid", "obs_quantize", "obs_quantize_blocked",
     "obq_reference", "rtn_quantize", "kron_loss", "allocate_bits", "quantize_layer",
     "container_bits", "pack_codes", "unpack_codes", "dequantize", "decode_matvec",
-    "ObsResult", "INFEASIBLE",
+    "ObsResult", "INFEASIBLE", "cross_covariance", "gptaq_target", "gptaq_quantize", "biip_transform",
+    "quantize_layer_gptaq", "gptaq_drift_map",
 ]
 
 
@@ -206,6 +211,13 @@ def biip_forward(w: np.ndarray, h_x: np.ndarray, h_g: np.ndarray, rot_in: kq_syn
         w1 = rotate_rows(w1.T, rot_out).T
         hg1 = _two_sided(hg1, rot_out)
     return w1, hx1, hg1, s_x, s_g
+
+
+def biip_transform(m: np.ndarray, s: np.ndarray, spec: kq_synth.RotSpec) -> np.ndarray:
+    """U S^-1 M S^-1 U^T for any square M (the input-side map of H_X, applied with given scales):
+    a second-moment matrix of the layer's inputs in the basis the sweep works in."""
+    s = np.asarray(s, np.float64)
+    return _two_sided(np.asarray(m, np.float64) / s[:, None] / s[None, :], spec)
 
 
 def biip_inverse(w2: np.ndarray, rot_in: kq_synth.RotSpec, rot_out: kq_synth.RotSpec,
@@ -440,6 +452,72 @@ def obq_reference(w2: np.ndarray, h_damped: np.ndarray, bits: int, group: int) -
         w[:, j + 1:] -= np.outer(err / hinv[j, j], hinv[j, j + 1:])
         hinv = hinv - np.outer(hinv[:, j], hinv[j, :]) / hinv[j, j]
     return ObsResult(codes, scales, zeros, what, tt)
+
+
+# ---------------------------------------------------------------------------
+# row f2: the GPTAQ base quantizer, asymmetric calibration ([KQ-art] 四, 八)
+# ---------------------------------------------------------------------------
+# The pages say KronQ's column update is GPTAQ's and that GPTAQ adds an input-drift
+# correction to GPTQ ([KQ-art] 四, 八); they do not state its formula. Reading taken here,
+# in two stages. X are the inputs the partly quantized model feeds the layer, Xt those of
+# the full-precision model, dX = Xt - X, H = X^T X / N, D = dX^T X / N and H~ = H + lam
+# mean(diag H) I (GPTQ's damping).
+#   1. Drift correction: column q of the layer loses w_q dx_q of output against the
+#      full-precision layer; the later columns take its least-squares compensation on their
+#      own inputs X_{>q} (damping as ridge rows), delta H~_{>q,>q} = w_q D_{q,>q}. The
+#      compensations do not depend on the rounding, so all of them are applied first:
+#      W' = W (I + P), row q of P = D_{q,>q} H~_{>q,>q}^-1 (strictly upper triangular).
+#   2. GPTQ's column sweep on W' with the same H~.
+# Without drift (D = 0) this is GPTQ. Parity against the pages: unpinned (no formula there);
+# pinned against the definition of the compensation.
+def cross_covariance(a_chunks: Iterable[np.ndarray], b_chunks: Iterable[np.ndarray]) -> np.ndarray:
+    """C = A^T B / N in float64 for token-major A, B (bf16 bits or floats) over the same tokens."""
+    acc, n = None, 0
+    for a, b in zip(a_chunks, b_chunks):
+        fa, fb = as_f64(a), as_f64(b)
+        part = fa.T @ fb
+        acc = part if acc is None else acc + part
+        n += fa.shape[0]
+    return acc / n
+
+
+def gptaq_drift_map(h: np.ndarray, d: np.ndarray, lam: float) -> np.ndarray:
+    """P, strictly upper triangular: row q = D_{q,>q} H~_{>q,>q}^-1, one solve per row."""
+    ht = damped(h, lam)
+    dd = np.asarray(d, np.float64)
+    n = ht.shape[0]
+    p = np.zeros((n, n))
+    for q in range(n - 1):
+        p[q, q + 1:] = np.linalg.solve(ht[q + 1:, q + 1:], dd[q, q + 1:])
+    return p
+
+
+def gptaq_target(w2: np.ndarray, h: np.ndarray, d: np.ndarray, lam: float) -> np.ndarray:
+    """Stage 1: W' = W (I + P), every column's drift compensated on the later columns."""
+    w = as_f64(w2)
+    return w + w @ gptaq_drift_map(h, d, lam)
+
+
+def gptaq_quantize(w2: np.ndarray, h: np.ndarray, d: np.ndarray, lam: float, bits: int, group: int,
+                   **replay) -> ObsResult:
+    """Stages 1 and 2: GPTQ's sweep (``obs_quantize``) of W' with the factor of H~^-1."""
+    return obs_quantize(gptaq_target(w2, h, d, lam), chol_inv_upper(h, lam), bits, group, **replay)
+
+
+def quantize_layer_gptaq(w, h_x, d_x, h_g, rot_in, rot_out, *, bits: int, group: int, damp: float,
+                         **replay) -> Dict[str, object]:
+    """Row f2 on one layer: BiIP as in ``quantize_layer`` (scales from H_X and H_G), D'' = the
+    input-side map of D = dX^T X / N with the same scales and rotation (the second moments of
+    the rotated inputs), then the two GPTAQ stages on W'' with H_X'' and D''."""
+    w64 = as_f64(w)
+    w2, hx2, hg2, s_x, s_g = biip_forward(w64, h_x, h_g, rot_in, rot_out)
+    d2 = biip_transform(d_x, s_x, rot_in)
+    target = gptaq_target(w2, hx2, d2, damp)
+    r = chol_inv_upper(hx2, damp)
+    res = obs_quantize(target, r, bits, group, **replay)
+    w_hat = biip_inverse(res.what, rot_in, rot_out, s_x, s_g)
+    return {"w2": w2, "hx2": hx2, "d2": d2, "s_x": s_x, "s_g": s_g, "target": target, "r": r, "obs": res,
+            "w_hat": w_hat}
 
 
 def rtn_quantize(w2: np.ndarray, bits: int, group: int) -> ObsResult:

@@ -60,7 +60,7 @@ enum { KQ_SCORE_KRONQ = 0, KQ_SCORE_HX_ONLY = 1 };
 
 /* kq_workspace_size operations. */
 enum { KQ_OP_ACCUMULATE_COV = 0, KQ_OP_BIIP = 1, KQ_OP_CHOLESKY = 2, KQ_OP_OBS = 3, KQ_OP_DECODE = 4,
-       KQ_OP_LOSS = 5 };
+       KQ_OP_LOSS = 5, KQ_OP_XCOV = 6, KQ_OP_GPTAQ = 7 };
 
 #define KQ_MAX_ODD 63         /* largest odd factor m of a rotated dimension */
 #define KQ_MAX_ROT_DIM 32768  /* largest rotated dimension n = m * 2^k */
@@ -112,6 +112,9 @@ kq_status kq_timing_query(const char* name, int64_t* launches, double* total_ms)
  *   KQ_OP_OBS:            d0 = dout, d1 = din, d2 = block
  *   KQ_OP_DECODE:         d0 = dout (kq_decode_matvec_group: the layers' total), d1 = din, d2 = tokens
  *   KQ_OP_LOSS:           d0 = dout, d1 = din
+ *   KQ_OP_XCOV:           d0 = rows, d1 = d
+ *   KQ_OP_GPTAQ:          d0 = dout, d1 = din
+ *   (kq_biip_transform of an n x n matrix uses KQ_OP_BIIP with d0 = d1 = n)
  * Returns (size_t)-1 for invalid sizes.
  */
 size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
@@ -134,6 +137,62 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
  */
 kq_status kq_accumulate_cov(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha,
                             float beta, float* h, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kq_accumulate_xcov -- C <- alpha * A^T B + beta * C_in   (cross second moment)
+ *
+ * Row f2, the GPTAQ base quantizer: KronQ's column update is GPTAQ's, which
+ * corrects GPTQ for the drift between the inputs of the full-precision layer
+ * and those of the partly quantized model ([KQ-art] 四, 八; the pages give no
+ * formula). With A = Xt (full-precision inputs), B = X (quantized-model
+ * inputs, the same tokens), alpha = 1/N, beta = -1 and C_in = H_X from
+ * kq_accumulate_cov of X, it forms the drift moment D = (Xt - X)^T X / N.
+ *   a, b   device, bf16 bit patterns, [rows, d] with row pitches lda, ldb (>= d)
+ *   rows   number of token rows, >= 0 (0: C <- beta * C_in)
+ *   c_in   device float32 [d, d]; read only when beta != 0 (then not NULL); may equal c
+ *   c      device float32 [d, d]; every entry written
+ *   ws     scratch of kq_workspace_size(KQ_OP_XCOV, rows, d, 0) bytes
+ * Arithmetic as kq_accumulate_cov (exact bf16 products, float32 within token
+ * slices of 16384 rows, float64 across slices), over every 256 x 256 tile of
+ * the square; alpha * A^T B is rounded to float32 before beta * C_in is added
+ * (and the sum rounded again), so identical inputs with C_in from
+ * kq_accumulate_cov and beta = -1 give exactly zero.
+ */
+kq_status kq_accumulate_xcov(const uint16_t* a, const uint16_t* b, int64_t rows, int64_t d, int64_t lda,
+                             int64_t ldb, float alpha, float beta, const float* c_in, float* c, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * kq_biip_transform -- M <- U S^-1 M S^-1 U^T   (the input-side map of BiIP)
+ *
+ * The map kq_biip_rotate applies to H_X, for another second moment of the same
+ * inputs (row f2: the drift moment D), with the scales of that forward call.
+ *   m      device float32 [n, n], in place (need not be symmetric)
+ *   rot    HOST pointer to the input-side rotation spec (its n must match)
+ *   s      device float64 [n]: the s_x of the forward call; NULL means 1
+ *   ws     scratch of kq_workspace_size(KQ_OP_BIIP, n, n, 0) bytes
+ * Precision as kq_biip_rotate (float64 on chip, float32 between passes).
+ */
+kq_status kq_biip_transform(float* m, int64_t n, const kq_rot* rot, const double* s, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * kq_gptaq_target -- W <- W + W triu(D R^T, 1) R   (GPTAQ's drift correction)
+ *
+ * Row f2. Reading of GPTAQ taken ([KQ-art] 四, 八): each column q's drift
+ * w_q dx_q is compensated by least squares on the later columns' inputs
+ * (GPTQ's damping as ridge), which moves them by w_q D_{q,>q} H~_{>q,>q}^-1;
+ * with R^T R = H~^-1 the trailing inverse is R_{>q,>q}^T R_{>q,>q}, so all of
+ * them together are W P, P = triu(D R^T, 1) R. GPTQ's sweep (kq_obs_quantize
+ * with the same R) then runs on the result. Without drift (D = 0) W is unchanged.
+ *   w      device float64 [dout, din], in place (W'' of kq_biip_rotate)
+ *   d2     device float32 [din, din]: D'' (kq_accumulate_xcov, then kq_biip_transform)
+ *   r      device float32 [din, din]: R of kq_cholesky_inv on H_X'' (upper, zero below)
+ *   ws     scratch of kq_workspace_size(KQ_OP_GPTAQ, dout, din, 0) bytes
+ * Three float64 MFMA products with fixed summation order (deterministic).
+ */
+kq_status kq_gptaq_target(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * kq_sensitivity -- score = tr(H_G) * tr(H_X), or tr(H_X) alone

@@ -31,7 +31,10 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 CHUNK_TOKENS = 8192
-DRIFT = 0.1  # input drift of the full-precision model, in units of the channel scale
+# drift of the full-precision model's inputs against the partly quantized model's: a per-channel
+# gain 1 + N(0, DRIFT_GAIN) and independent noise of DRIFT_NOISE x the channel scale
+DRIFT_GAIN = 0.1
+DRIFT_NOISE = 0.05
 
 
 # ---------------------------------------------------------------------------
@@ -253,11 +256,14 @@ class Workload:
 
     def _chunk(self, kind: str, key: str, c: int, d: int, scales: np.ndarray) -> np.ndarray:
         if kind == "xt":
-            # full-precision inputs: the same draws as "x" plus a seeded drift of DRIFT x the
-            # channel scale, rounded to bf16 on their own
+            # full-precision inputs: the same draws as "x" with a seeded per-channel gain
+            # (1 + g_j, g ~ N(0, DRIFT_GAIN)) and independent noise of DRIFT_NOISE x the channel
+            # scale, rounded to bf16 on their own
             a = self._chunk_f32("x", key, c, d, scales)
+            gain = 1.0 + DRIFT_GAIN * stream(self.cfg.id, "xgain:" + key, d).standard_normal(d)
             rng = stream(self.cfg.id, "xdrift:" + key, c, d)
-            a += DRIFT * rng.standard_normal(a.shape, dtype=np.float32) * scales[None, :]
+            a = a * gain.astype(np.float32)[None, :]
+            a += DRIFT_NOISE * rng.standard_normal(a.shape, dtype=np.float32) * scales[None, :]
             return f32_to_bf16_bits(a)
         return f32_to_bf16_bits(self._chunk_f32(kind, key, c, d, scales))
 
@@ -292,9 +298,9 @@ class Workload:
 
     def xt(self, group: str) -> np.ndarray:
         """Full-precision-model inputs of one input group for the asymmetric (GPTAQ) objective,
-        [n_tokens, din] bf16 bits: x(group)'s values before rounding plus a seeded drift of
-        DRIFT x the channel scale. x(group) stands for the inputs the partly quantised model
-        sees."""
+        [n_tokens, din] bf16 bits: x(group)'s values before rounding with a seeded per-channel
+        gain drift (DRIFT_GAIN) and noise (DRIFT_NOISE x the channel scale). x(group) stands
+        for the inputs the partly quantised model sees."""
         return self._full("xt", group, self.cfg.x_groups[group], self.x_scales(group))
 
     def drop(self, kind: str, key: str) -> None:

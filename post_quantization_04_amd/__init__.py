@@ -18,11 +18,11 @@ __all__ = [
     "KQError", "KQ_OK", "KQ_EINVAL", "KQ_ENOTPD", "KQ_EINFEASIBLE", "KQ_EDEVICE", "KQ_EUNSUPPORTED",
     "KQ_BF16", "KQ_F32", "KQ_F64", "KQ_BIIP_INPUT", "KQ_BIIP_OUTPUT", "KQ_BIIP_SCALE", "KQ_BIIP_INVERSE",
     "KQ_SCORE_KRONQ", "KQ_SCORE_HX_ONLY", "KQ_OP_ACCUMULATE_COV", "KQ_OP_BIIP", "KQ_OP_CHOLESKY", "KQ_OP_OBS",
-    "KQ_OP_DECODE", "KQ_OP_LOSS", "KQ_DECODE_MAX_TOKENS", "KQ_DECODE_MAX_LAYERS",
+    "KQ_OP_DECODE", "KQ_OP_LOSS", "KQ_OP_XCOV", "KQ_OP_GPTAQ", "KQ_DECODE_MAX_TOKENS", "KQ_DECODE_MAX_LAYERS",
     "lib", "lib_path", "version", "workspace_size", "accumulate_cov", "sensitivity", "allocate_bits",
     "biip_rotate", "cholesky_inv", "obs_quantize", "pack_codes", "decode_matvec", "decode_matvec_group",
     "decode_matvec_group_noalloc", "decode_workspace", "kron_loss", "Rot", "KQ_DECODE_NOALLOC_SCRATCH",
-    "DecodeLayer",
+    "DecodeLayer", "accumulate_xcov", "biip_transform", "gptaq_target",
     "timing_enable", "timing_query",
 ]
 
@@ -31,6 +31,7 @@ KQ_BF16, KQ_F32, KQ_F64 = 0, 1, 2
 KQ_BIIP_INPUT, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_BIIP_INVERSE = 1, 2, 4, 8
 KQ_SCORE_KRONQ, KQ_SCORE_HX_ONLY = 0, 1
 KQ_OP_ACCUMULATE_COV, KQ_OP_BIIP, KQ_OP_CHOLESKY, KQ_OP_OBS, KQ_OP_DECODE, KQ_OP_LOSS = 0, 1, 2, 3, 4, 5
+KQ_OP_XCOV, KQ_OP_GPTAQ = 6, 7
 KQ_DECODE_MAX_TOKENS = 4
 KQ_DECODE_MAX_LAYERS = 4
 KQ_DECODE_NOALLOC_SCRATCH = 2228224
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.kq_workspace_size.restype = _SZ
     L.kq_workspace_size.argtypes = [_I32, _I64, _I64, _I64]
     L.kq_accumulate_cov.argtypes = [_VP, _I64, _I64, _I64, _F32, _F32, _VP, _VP, _SZ, _VP]
+    L.kq_accumulate_xcov.argtypes = [_VP, _VP, _I64, _I64, _I64, _I64, _F32, _F32, _VP, _VP, _VP, _SZ, _VP]
+    L.kq_biip_transform.argtypes = [_VP, _I64, ctypes.POINTER(Rot), _VP, _VP, _SZ, _VP]
+    L.kq_gptaq_target.argtypes = [_VP, _VP, _VP, _I64, _I64, _VP, _SZ, _VP]
     L.kq_sensitivity.argtypes = [_VP, _I64, _VP, _I64, _I32, _VP, _VP]
     L.kq_allocate_bits.argtypes = [_VP, _VP, _I32, _VP, _I32, _I64, _VP]
     L.kq_biip_rotate.argtypes = [_VP, _I32, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(Rot),
@@ -105,7 +109,8 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(Rot), _VP, _I64, _VP]
     for name in ("kq_accumulate_cov", "kq_sensitivity", "kq_allocate_bits", "kq_biip_rotate",
                  "kq_cholesky_inv", "kq_obs_quantize", "kq_pack_codes", "kq_decode_matvec",
-                 "kq_decode_matvec_group", "kq_decode_matvec_group_noalloc", "kq_kron_loss"):
+                 "kq_decode_matvec_group", "kq_decode_matvec_group_noalloc", "kq_kron_loss",
+                 "kq_accumulate_xcov", "kq_biip_transform", "kq_gptaq_target"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -176,6 +181,56 @@ def accumulate_cov(a, h, alpha: float, beta: float, *, ws=None, stream=None) -> 
         ws = _scratch(need, h.device)
     _check(lib().kq_accumulate_cov(_ptr(a), rows, d, a.stride(0), alpha, beta, _ptr(h), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)), "kq_accumulate_cov")
+
+
+def accumulate_xcov(a, b, c, alpha: float, beta: float, c_in=None, *, ws=None, stream=None) -> None:
+    """c <- alpha * a^T b + beta * c_in (c_in defaults to c); a, b: [rows, d] bf16 (or int16/uint16 bits)
+    over the same tokens, c / c_in: [d, d] float32."""
+    import torch
+    _need(a.dim() == 2 and b.shape == a.shape and c.dim() == 2 and c.shape[0] == c.shape[1] == a.shape[1],
+          "accumulate_xcov: shapes")
+    bits = (torch.bfloat16, torch.int16, torch.uint16)
+    _need(a.dtype in bits and b.dtype in bits and c.dtype == torch.float32, "accumulate_xcov: dtypes")
+    _need(a.stride(1) == 1 and b.stride(1) == 1 and c.is_contiguous(), "accumulate_xcov: layout")
+    if c_in is None:
+        c_in = c
+    _need(c_in.shape == c.shape and c_in.dtype == torch.float32 and c_in.is_contiguous(), "accumulate_xcov: c_in")
+    rows, d = a.shape
+    need = workspace_size(KQ_OP_XCOV, rows, d)
+    if ws is None:
+        ws = _scratch(need, c.device)
+    _check(lib().kq_accumulate_xcov(_ptr(a), _ptr(b), rows, d, a.stride(0), b.stride(0), alpha, beta, _ptr(c_in),
+                                    _ptr(c), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "kq_accumulate_xcov")
+
+
+def biip_transform(m, rot: Rot, s=None, *, ws=None, stream=None) -> None:
+    """m <- U S^-1 m S^-1 U^T in place (the input-side map of BiIP); m: [n, n] float32, s: [n] float64 or None."""
+    import torch
+    _need(m.dim() == 2 and m.shape[0] == m.shape[1] and m.dtype == torch.float32 and m.is_contiguous(),
+          "biip_transform: m must be a contiguous square float32 matrix")
+    _need(s is None or (s.dtype == torch.float64 and s.numel() == m.shape[0]), "biip_transform: s")
+    n = m.shape[0]
+    need = workspace_size(KQ_OP_BIIP, n, n)
+    if ws is None:
+        ws = _scratch(need, m.device)
+    _check(lib().kq_biip_transform(_ptr(m), n, ctypes.byref(rot), _ptr(s), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(stream)), "kq_biip_transform")
+
+
+def gptaq_target(w, d2, r, *, ws=None, stream=None) -> None:
+    """w <- w + w triu(d2 r^T, 1) r in place; w: [dout, din] float64, d2 and r: [din, din] float32."""
+    import torch
+    _need(w.dim() == 2 and w.dtype == torch.float64 and w.is_contiguous(), "gptaq_target: w")
+    din = w.shape[1]
+    for m, name in ((d2, "d2"), (r, "r")):
+        _need(m.shape == (din, din) and m.dtype == torch.float32 and m.is_contiguous(), f"gptaq_target: {name}")
+    dout = w.shape[0]
+    need = workspace_size(KQ_OP_GPTAQ, dout, din)
+    if ws is None:
+        ws = _scratch(need, w.device)
+    _check(lib().kq_gptaq_target(_ptr(w), _ptr(d2), _ptr(r), dout, din, _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)), "kq_gptaq_target")
 
 
 def sensitivity(h_x, h_g, score, mode: int = KQ_SCORE_KRONQ, *, stream=None) -> None:

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
 PEAKS_LIB = os.path.join(HERE, "libkq_peaks.so")
 SOURCES = ["kq_api.hip", "timing.hip", "syrk.hip", "score.hip", "biip.hip", "chol.hip", "obs.hip",
-           "decode.hip", "loss.hip"]
+           "decode.hip", "loss.hip", "gptaq.hip"]
 ARCH = "gfx950"
 
 

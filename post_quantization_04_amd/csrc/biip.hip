@@ -928,8 +928,9 @@ int64_t mid_pitch(int64_t n) {
   return r % 1024 == 0 ? r + 64 : r;
 }
 
-// U S^-1 M S^-1 U^T of a symmetric d x d float32 matrix, in place, through a float32 scratch copy:
-// column passes (with both scales) h -> tmp, then the row pass tmp -> h.
+// U S^-1 M S^-1 U^T of a d x d float32 matrix, in place, through a float32 scratch copy:
+// column passes (with both scales) h -> tmp, then the row pass tmp -> h. M need not be
+// symmetric.
 kq_status two_sided(float* h, int64_t d, const Rot& rot, const double* inv_s, float* tmp, double* fac,
                     const double* ones, hipStream_t st) {
   const int64_t pm = mid_pitch(d);
@@ -1060,6 +1061,31 @@ kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double
   if (inp && (r = two_sided(h_x, din, ri, inv_x, tmp, fac, ones, st)) != KQ_OK) return r;
   if (out && (r = two_sided(h_g, dout, ro, inv_g, tmp, fac, ones, st)) != KQ_OK) return r;
   return KQ_OK;
+}
+
+// M <- U S^-1 M S^-1 U^T for any square float32 M with given scales (the input-side map of
+// H_X applied to another second-moment matrix of the same inputs), in place; workspace as
+// for BiIP of an n x n weight.
+kq_status biip_transform_run(float* m, int64_t n, const kq_rot* rot, const double* s, void* ws, hipStream_t st) {
+  char* p = static_cast<char*>(ws);
+  float* tmp = reinterpret_cast<float*>(p);
+  p += biip_tmp_bytes(n, n);
+  double* inv = reinterpret_cast<double*>(p);
+  p += 2 * biip_vec_bytes(n);
+  double* fac = reinterpret_cast<double*>(p);
+  p += biip_vec_bytes(4 * n);
+  double* ones = reinterpret_cast<double*>(p);
+  kq_status r;
+  {
+    LaunchTimer timer("ones_kernel", st);
+    hipLaunchKernelGGL(ones_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, ones, n);
+    if (s)
+      hipLaunchKernelGGL(recip_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, s, n, inv);
+    else
+      hipLaunchKernelGGL(ones_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, inv, n);
+  }
+  if ((r = check_launch("ones_kernel")) != KQ_OK) return r;
+  return two_sided(m, n, make_rot(rot, true, false), inv, tmp, fac, ones, st);
 }
 
 }  // namespace kq

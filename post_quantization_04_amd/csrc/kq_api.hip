@@ -108,6 +108,12 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2) {
     case KQ_OP_LOSS:
       if (d0 < 1 || d1 < 1 || d0 > kMaxDim || d1 > kMaxDim) return bad;
       return kq::loss_workspace(d0, d1);
+    case KQ_OP_XCOV:
+      if (d0 < 0 || d1 < 1 || d1 > kMaxDim) return bad;
+      return kq::xcov_workspace(d0, d1);
+    case KQ_OP_GPTAQ:
+      if (d0 < 1 || d1 < 1 || d0 > kMaxDim || d1 > kMaxDim) return bad;
+      return kq::gptaq_workspace(d0, d1);
     case KQ_OP_DECODE:
       if (d0 < 1 || d0 > int64_t(KQ_DECODE_MAX_LAYERS) * KQ_MAX_ROT_DIM || d1 < 1 || d1 > KQ_MAX_ROT_DIM || d2 < 1 ||
           d2 > KQ_DECODE_MAX_TOKENS)
@@ -126,6 +132,38 @@ kq_status kq_accumulate_cov(const uint16_t* a, int64_t rows, int64_t d, int64_t 
   if (!h || (rows > 0 && !a)) return fail(KQ_EINVAL, "kq_accumulate_cov: NULL pointer");
   if (!ws_ok(ws, ws_bytes, kq::syrk_workspace(rows, d))) return KQ_EINVAL;
   return kq::syrk_run(a, rows, d, lda, alpha, beta, h, ws, kq::as_stream(stream));
+}
+
+kq_status kq_accumulate_xcov(const uint16_t* a, const uint16_t* b, int64_t rows, int64_t d, int64_t lda,
+                             int64_t ldb, float alpha, float beta, const float* c_in, float* c, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (rows < 0 || d < 1 || d > kMaxDim) return fail(KQ_EINVAL, "kq_accumulate_xcov: bad shape rows=%lld d=%lld",
+                                                    (long long)rows, (long long)d);
+  if (lda < d || ldb < d)
+    return fail(KQ_EINVAL, "kq_accumulate_xcov: row pitches %lld, %lld < d %lld", (long long)lda, (long long)ldb,
+                (long long)d);
+  if (!c || (rows > 0 && (!a || !b))) return fail(KQ_EINVAL, "kq_accumulate_xcov: NULL pointer");
+  if (beta != 0.0f && !c_in) return fail(KQ_EINVAL, "kq_accumulate_xcov: beta != 0 needs c_in");
+  if (!ws_ok(ws, ws_bytes, kq::xcov_workspace(rows, d))) return KQ_EINVAL;
+  return kq::xcov_run(a, b, rows, d, lda, ldb, alpha, beta, c_in, c, ws, kq::as_stream(stream));
+}
+
+kq_status kq_biip_transform(float* m, int64_t n, const kq_rot* rot, const double* s, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (n < 1 || n > KQ_MAX_ROT_DIM) return fail(KQ_EINVAL, "kq_biip_transform: n = %lld", (long long)n);
+  if (!m) return fail(KQ_EINVAL, "kq_biip_transform: NULL pointer");
+  if (!rot_ok(rot, n, "input")) return KQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, kq::biip_workspace(n, n))) return KQ_EINVAL;
+  return kq::biip_transform_run(m, n, rot, s, ws, kq::as_stream(stream));
+}
+
+kq_status kq_gptaq_target(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (dout < 1 || din < 1 || dout > kMaxDim || din > kMaxDim)
+    return fail(KQ_EINVAL, "kq_gptaq_target: shape %lld x %lld", (long long)dout, (long long)din);
+  if (!w || !d2 || !r) return fail(KQ_EINVAL, "kq_gptaq_target: NULL pointer");
+  if (!ws_ok(ws, ws_bytes, kq::gptaq_workspace(dout, din))) return KQ_EINVAL;
+  return kq::gptaq_target_run(w, d2, r, dout, din, ws, kq::as_stream(stream));
 }
 
 kq_status kq_sensitivity(const float* h_x, int64_t din, const float* h_g, int64_t dout, int32_t mode,

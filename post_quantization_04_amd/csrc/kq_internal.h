@@ -48,6 +48,14 @@ constexpr int kCus = 256;
 size_t syrk_workspace(int64_t rows, int64_t d);
 kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha, float beta,
                    float* h, void* ws, hipStream_t st);
+size_t xcov_workspace(int64_t rows, int64_t d);
+kq_status xcov_run(const uint16_t* a, const uint16_t* b, int64_t rows, int64_t d, int64_t lda, int64_t ldb,
+                   float alpha, float beta, const float* c_in, float* c, void* ws, hipStream_t st);
+
+// GPTAQ drift correction (gptaq.hip)
+size_t gptaq_workspace(int64_t dout, int64_t din);
+kq_status gptaq_target_run(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
+                           hipStream_t st);
 
 // trace score (score.hip)
 kq_status score_run(const float* h_x, int64_t din, const float* h_g, int64_t dout, int mode,
@@ -58,6 +66,7 @@ size_t biip_workspace(int64_t dout, int64_t din);
 kq_status biip_run(const void* w, int w_dtype, int64_t dout, int64_t din, double* w_out, float* h_x,
                    float* h_g, const kq_rot* rot_in, const kq_rot* rot_out, uint32_t flags,
                    double* s_x, double* s_g, void* ws, hipStream_t st);
+kq_status biip_transform_run(float* m, int64_t n, const kq_rot* rot, const double* s, void* ws, hipStream_t st);
 
 // damped Cholesky factor of the inverse (chol.hip)
 size_t chol_workspace(int64_t d);

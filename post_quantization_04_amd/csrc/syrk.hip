@@ -102,6 +102,17 @@ __device__ __forceinline__ void tri(int t, int& I, int& J) {
   J = t - i * (i + 1) / 2;
 }
 
+// Tile t of the square (CROSS: all nt x nt tiles, t = I nt + J) or of the lower triangle.
+template <bool CROSS>
+__device__ __forceinline__ void tile_ij(int t, int nt, int& I, int& J) {
+  if constexpr (CROSS) {
+    I = t / nt;
+    J = t % nt;
+  } else {
+    tri(t, I, J);
+  }
+}
+
 // Byte offset (inside a panel) of this lane's first transposing read for the
 // operand block starting at channel ch0; k-step kk adds 8192 bytes, the second
 // read of a pair (+4 tokens) adds 2048.
@@ -175,11 +186,14 @@ struct RegStage {
   uint4 v[2 * kUnitsPerLane];
 };
 
-// Uniform per-workgroup state of the pipeline. DIAG: I = J, one panel.
-template <bool DIAG>
+// Uniform per-workgroup state of the pipeline. DIAG: I = J, one panel. CROSS:
+// panel J comes from a second matrix B (row pitch ldb2 bytes).
+template <bool DIAG, bool CROSS = false>
 struct Pipe {
   const char* a;        // A as bytes
   int64_t lda2;         // row pitch in bytes
+  const char* b;        // B as bytes (CROSS)
+  int64_t ldb2;
   int64_t tok_begin, tok_end;
   int nstage;
   int wave;
@@ -201,9 +215,13 @@ struct Pipe {
       r.v[i] = make_uint4(x[0], x[1], x[2], x[3]);
     }
     if constexpr (!DIAG) {
+      Rsrc rb = rs;
+      if constexpr (CROSS)
+        rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b + t0 * ldb2), static_cast<short>(0),
+                                               static_cast<int>(left * ldb2), 0x00020000);
 #pragma unroll
       for (int i = 0; i < kUnitsPerLane; ++i) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, db[i], 0, 0);
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rb, db[i], 0, 0);
         r.v[kUnitsPerLane + i] = make_uint4(x[0], x[1], x[2], x[3]);
       }
     }
@@ -246,8 +264,8 @@ __device__ __forceinline__ void interleave() {
 // One stage: stage s in buffer K % 3, its first k-step's fragments in f0.
 // IDLE: the wave above the diagonal of a diagonal tile, which stages data but
 // computes nothing.
-template <int K, bool DIAG, bool IDLE>
-__device__ __forceinline__ void stage_step(const Pipe<DIAG>& p, int s, RegStage (&regs)[kNS], Frags& f0, Frags& f1,
+template <int K, bool DIAG, bool IDLE, typename PIPE>
+__device__ __forceinline__ void stage_step(const PIPE& p, int s, RegStage (&regs)[kNS], Frags& f0, Frags& f1,
                                            f32x16 (&acc)[4][4]) {
   if constexpr (!IDLE) {
     read_frags(reinterpret_cast<const char*>(stage_buf<K>()), 1, p.oa, p.ob, f1);
@@ -272,8 +290,8 @@ __device__ __forceinline__ void stage_step(const Pipe<DIAG>& p, int s, RegStage 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool DIAG, bool IDLE, int... K>
-__device__ __forceinline__ void stage_round(const Pipe<DIAG>& p, int s, RegStage (&regs)[kNS], Frags& f0, Frags& f1,
+template <bool DIAG, bool IDLE, typename PIPE, int... K>
+__device__ __forceinline__ void stage_round(const PIPE& p, int s, RegStage (&regs)[kNS], Frags& f0, Frags& f1,
                                             f32x16 (&acc)[4][4], std::integer_sequence<int, K...>) {
   (stage_step<K, DIAG, IDLE>(p, s + K, regs, f0, f1, acc), ...);
 }
@@ -296,12 +314,15 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[4][4], float* __re
 }
 
 // The slice loop of one work item.
-template <bool DIAG, bool IDLE>
-__device__ __forceinline__ void slice_sum(const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t tok_begin,
-                                          int64_t tok_end, int I, int J, float* __restrict__ out) {
-  Pipe<DIAG> p;
+template <bool DIAG, bool IDLE, bool CROSS>
+__device__ __forceinline__ void slice_sum(const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ b,
+                                          int64_t ldb, int64_t d, int64_t tok_begin, int64_t tok_end, int I, int J,
+                                          float* __restrict__ out) {
+  Pipe<DIAG, CROSS> p;
   p.a = reinterpret_cast<const char*>(a);
   p.lda2 = lda * 2;
+  p.b = reinterpret_cast<const char*>(b);
+  p.ldb2 = ldb * 2;
   p.tok_begin = tok_begin;
   p.tok_end = tok_end;
   p.nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
@@ -313,7 +334,7 @@ __device__ __forceinline__ void slice_sum(const uint16_t* __restrict__ a, int64_
     p.ob[x] = tr_offset(wj * 128 + x * 32) + (DIAG ? 0 : kPanelBytes);
   }
   chunk_offsets(lda, d, int64_t(I) * kT, p.da);
-  chunk_offsets(lda, d, int64_t(J) * kT, p.db);
+  chunk_offsets(CROSS ? ldb : lda, d, int64_t(J) * kT, p.db);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -377,14 +398,22 @@ __device__ __forceinline__ bool work_item(int ntiles, int nsl, int nsb, const in
 // gets sub-block x; a partial one (on the diagonal or at the edge) deals its
 // n tiles out in that order, ceil(n / 8) per XCD (the q-th tile to slot
 // 32 (q / per) + q % per, q from a prefix count). Empty slots hold -1.
+// CROSS: super-blocks cover the whole square, b = bi side + bj, and tile (i, j) is i nt + j.
+template <bool CROSS>
 __global__ __launch_bounds__(256) void superblock_order_kernel(int nt, int* __restrict__ slots) {
   __shared__ int cnt[256];
   int bi, bj;
-  tri(static_cast<int>(blockIdx.x), bi, bj);
+  if constexpr (CROSS) {
+    const int side = (nt + 15) / 16;
+    bi = static_cast<int>(blockIdx.x) / side;
+    bj = static_cast<int>(blockIdx.x) % side;
+  } else {
+    tri(static_cast<int>(blockIdx.x), bi, bj);
+  }
   const int t = static_cast<int>(threadIdx.x);
   const int x = t >> 5, k = t & 31;
   const int i = 16 * bi + 4 * (x >> 1) + (k >> 3), j = 16 * bj + 8 * (x & 1) + (k & 7);
-  const int valid = (i < nt && j <= i) ? 1 : 0;
+  const int valid = (i < nt && j < nt && (CROSS || j <= i)) ? 1 : 0;
   int* out = slots + size_t(blockIdx.x) * 256;
   out[t] = -1;
   // inclusive prefix count of the valid positions
@@ -398,41 +427,46 @@ __global__ __launch_bounds__(256) void superblock_order_kernel(int nt, int* __re
   }
   const int n = cnt[255], q = cnt[t] - valid;
   const int per = n == 256 ? 32 : (n + 7) / 8;
-  if (valid) out[(q / per) * 32 + q % per] = i * (i + 1) / 2 + j;
+  if (valid) out[(q / per) * 32 + q % per] = CROSS ? i * nt + j : i * (i + 1) / 2 + j;
 }
 
 // Every lower-triangle tile in blocks of 4 tile rows x 8 tile columns,
 // row-major inside a block (32 consecutive items share about 12 channel
 // panels). One thread; used by launches of at least 8 slices, where H has at
 // most about a thousand tiles.
+// CROSS: every tile of the square, the same blocks.
+template <bool CROSS>
 __global__ void blocked_order_kernel(int nt, int* __restrict__ order) {
   if (blockIdx.x != 0 || threadIdx.x != 0) return;
   int r = 0;
   for (int bi = 0; bi < nt; bi += 4)
-    for (int bj = 0; bj <= bi + 3 && bj < nt; bj += 8)
+    for (int bj = 0; bj < nt && (CROSS || bj <= bi + 3); bj += 8)
       for (int i = bi; i < bi + 4 && i < nt; ++i)
-        for (int j = bj; j < bj + 8 && j <= i; ++j) order[r++] = i * (i + 1) / 2 + j;
+        for (int j = bj; j < bj + 8 && j < nt && (CROSS || j <= i); ++j) order[r++] = CROSS ? i * nt + j : i * (i + 1) / 2 + j;
 }
 
 // Pipelined kernel: needs 16-byte aligned rows (lda, d multiples of 8, A
-// aligned) and 32 rows of A addressable with 32-bit byte offsets.
+// aligned; CROSS: the same of B) and 32 rows addressable with 32-bit byte
+// offsets. CROSS: partial sums of A^T B over every tile of the square.
+template <bool CROSS>
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial(
-    const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
-    int nsl, int nsb, const int* __restrict__ order, float* __restrict__ part) {
+    const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ b, int64_t ldb, int64_t d,
+    int64_t rows, int nt, int ntiles, int slice0, int nsl, int nsb, const int* __restrict__ order,
+    float* __restrict__ part) {
   int sl, tile;
   if (!work_item(ntiles, nsl, nsb, order, sl, tile)) return;
   int I, J;
-  tri(tile, I, J);
+  tile_ij<CROSS>(tile, nt, I, J);
   const int64_t tok_begin = int64_t(slice0 + sl) * kSlice;
   const int64_t tok_end = tok_begin + kSlice < rows ? tok_begin + kSlice : rows;
   float* out = part + (int64_t(sl) * ntiles + tile) * (kT * kT);
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  if (I != J)
-    slice_sum<false, false>(a, lda, d, tok_begin, tok_end, I, J, out);
+  if (CROSS || I != J)
+    slice_sum<false, false, CROSS>(a, lda, b, ldb, d, tok_begin, tok_end, I, J, out);
   else if (wave == 1)  // block (rows 0..127, columns 128..255): above the diagonal
-    slice_sum<true, true>(a, lda, d, tok_begin, tok_end, I, J, out);
+    slice_sum<true, true, false>(a, lda, a, lda, d, tok_begin, tok_end, I, J, out);
   else
-    slice_sum<true, false>(a, lda, d, tok_begin, tok_end, I, J, out);
+    slice_sum<true, false, false>(a, lda, a, lda, d, tok_begin, tok_end, I, J, out);
 }
 
 // Register-staged copy of one panel stage with zero fill for tokens >=
@@ -455,15 +489,17 @@ __device__ __forceinline__ void load_stage_regs(const uint16_t* __restrict__ a, 
 
 // Fallback for rows that are not 16-byte aligned: element loads with zero
 // fill, two LDS buffers, one full barrier per stage.
+template <bool CROSS>
 __global__ __launch_bounds__(kThreads, 1) void syrk_partial_regs(
-    const uint16_t* __restrict__ a, int64_t lda, int64_t d, int64_t rows, int ntiles, int slice0,
-    int nsl, int nsb, const int* __restrict__ order, float* __restrict__ part) {
+    const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ b, int64_t ldb, int64_t d,
+    int64_t rows, int nt, int ntiles, int slice0, int nsl, int nsb, const int* __restrict__ order,
+    float* __restrict__ part) {
   __shared__ uint4 lds[2][2 * kPanelUnits];
   int sl, tile;
   if (!work_item(ntiles, nsl, nsb, order, sl, tile)) return;
   int I, J;
-  tri(tile, I, J);
-  const bool two = (I != J);
+  tile_ij<CROSS>(tile, nt, I, J);
+  const bool two = CROSS || (I != J);
   const int64_t tok_begin = int64_t(slice0 + sl) * kSlice;
   const int64_t tok_end = tok_begin + kSlice < rows ? tok_begin + kSlice : rows;
   const int nstage = static_cast<int>((tok_end - tok_begin + kKT - 1) / kKT);
@@ -484,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial_regs(
     uint4* buf = lds[s & 1];
     const int64_t t0 = tok_begin + int64_t(s) * kKT;
     load_stage_regs(a, lda, d, int64_t(I) * kT, t0, tok_end, buf);
-    if (two) load_stage_regs(a, lda, d, int64_t(J) * kT, t0, tok_end, buf + kPanelUnits);
+    if (two) load_stage_regs(CROSS ? b : a, CROSS ? ldb : lda, d, int64_t(J) * kT, t0, tok_end, buf + kPanelUnits);
     __syncthreads();
     Frags f;
 #pragma unroll
@@ -497,20 +533,22 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_partial_regs(
 }
 
 // Sums the float32 partials of a tile in float64; at the last slice group
-// writes H = alpha * S + beta * H to both triangles. One workgroup per 64 x 64
+// writes H = alpha * S + beta * C_in to both triangles (CROSS: C = alpha * S +
+// beta * C_in over the tile only; c_in may be h). One workgroup per 64 x 64
 // sub-block; a thread owns 4 columns x 4 rows (16-byte loads), slices summed
 // four at a time.
-__global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ part, int nsl, int ntiles,
+template <bool CROSS>
+__global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ part, int nsl, int nt, int ntiles,
                                                    int64_t d, double* __restrict__ acc, int first,
-                                                   int last, float alpha, float beta,
-                                                   float* __restrict__ h) {
+                                                   int last, float alpha, float beta, const float* c_in,
+                                                   float* h) {
   __shared__ float tr[64][65];
   const int tile = blockIdx.x >> 4;
   const int si = (blockIdx.x >> 2) & 3, sj = blockIdx.x & 3;
   int I, J;
-  tri(tile, I, J);
-  const bool dsub = (I == J) && (si == sj);  // sub-block on the diagonal of H
-  if (I == J && sj > si) return;              // mirror of another sub-block
+  tile_ij<CROSS>(tile, nt, I, J);
+  const bool dsub = !CROSS && (I == J) && (si == sj);  // sub-block on the diagonal of H
+  if (!CROSS && I == J && sj > si) return;              // mirror of another sub-block
   const int64_t r0 = int64_t(I) * kT + si * 64, c0 = int64_t(J) * kT + sj * 64;
   const int cq = (threadIdx.x & 15) * 4;      // first of this thread's 4 columns
   const int rb = threadIdx.x >> 4;            // rows rb, rb + 16, rb + 32, rb + 48
@@ -572,11 +610,19 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
       const int jl = cq + c;
       const int64_t gi = r0 + il, gj = c0 + jl;
       double v = static_cast<double>(alpha) * sum[k][c];
+      // CROSS rounds alpha * S to float32 first, so C_in = the same moment gives exactly 0
+      if constexpr (CROSS) v = static_cast<double>(static_cast<float>(v));
       if (beta != 0.0f && gi < d && gj < d && (!dsub || il >= jl))
-        v += static_cast<double>(beta) * static_cast<double>(h[gi * d + gj]);
-      tr[il][jl] = static_cast<float>(v);
+        v += static_cast<double>(beta) * static_cast<double>(c_in[gi * d + gj]);
+      if constexpr (CROSS) {
+        // each entry belongs to this tile alone: read (above) and written by the same thread
+        if (gi < d && gj < d) h[gi * d + gj] = static_cast<float>(v);
+      } else {
+        tr[il][jl] = static_cast<float>(v);
+      }
     }
   }
+  if constexpr (CROSS) return;
   if (!last) return;
   __syncthreads();
   const int jl = threadIdx.x & 63;
@@ -598,9 +644,10 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
   }
 }
 
-__global__ void scale_kernel(float* __restrict__ h, int64_t n, float beta) {
+// out = beta * in (0 when beta is 0); in may be out.
+__global__ void scale_kernel(const float* in, float* out, int64_t n, float beta) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) h[i] = (beta == 0.0f) ? 0.0f : beta * h[i];
+  if (i < n) out[i] = (beta == 0.0f) ? 0.0f : beta * in[i];
 }
 
 struct Plan {
@@ -608,10 +655,11 @@ struct Plan {
   size_t part_bytes, acc_bytes, order_bytes;
 };
 
-Plan plan(int64_t rows, int64_t d) {
+// CROSS: every tile of the square and super-blocks over the square.
+Plan plan(int64_t rows, int64_t d, bool cross) {
   Plan p{};
   p.nt = static_cast<int>((d + kT - 1) / kT);
-  p.ntiles = p.nt * (p.nt + 1) / 2;
+  p.ntiles = cross ? p.nt * p.nt : p.nt * (p.nt + 1) / 2;
   p.nslices = static_cast<int>((rows + kSlice - 1) / kSlice);
   int g = (kTargetItems + p.ntiles - 1) / p.ntiles;
   if (g < 1) g = 1;
@@ -625,38 +673,43 @@ Plan plan(int64_t rows, int64_t d) {
   p.part_bytes = align_up(size_t(g) * p.ntiles * kT * kT * sizeof(float), 256);
   p.acc_bytes = p.ngroups > 1 ? align_up(size_t(p.ntiles) * kT * kT * sizeof(double), 256) : 0;
   const int side = (p.nt + 15) / 16;
-  p.nsb = side * (side + 1) / 2;  // 16 x 16 super-blocks of the lower triangle
+  p.nsb = cross ? side * side : side * (side + 1) / 2;  // 16 x 16 super-blocks
   p.order_bytes = align_up((size_t(p.nsb) * 256 + p.ntiles) * sizeof(int), 256);
   return p;
 }
 
-}  // namespace
-
-size_t syrk_workspace(int64_t rows, int64_t d) {
+size_t workspace(int64_t rows, int64_t d, bool cross) {
   if (rows <= 0) return 0;
-  const Plan p = plan(rows, d);
+  const Plan p = plan(rows, d, cross);
   return p.part_bytes + p.acc_bytes + p.order_bytes;
 }
 
-kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha, float beta,
-                   float* h, void* ws, hipStream_t st) {
+// C = alpha * A^T B + beta * C_in (CROSS), or H = alpha * A^T A + beta * H (b = a, c_in = h).
+template <bool CROSS>
+kq_status cov_run(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, int64_t rows, int64_t d,
+                  float alpha, float beta, const float* c_in, float* h, void* ws, hipStream_t st) {
+  const char* kpart = CROSS ? "xcov_partial" : "syrk_partial";
+  const char* kregs = CROSS ? "xcov_partial_regs" : "syrk_partial_regs";
+  const char* kred = CROSS ? "xcov_reduce" : "syrk_reduce";
   if (rows == 0) {
     const int64_t n = d * d;
     {
       LaunchTimer timer("scale_kernel", st);
-      hipLaunchKernelGGL(scale_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, h, n,
-                         beta);
+      hipLaunchKernelGGL(scale_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                         beta == 0.0f ? h : c_in, h, n, beta);
     }
     return check_launch("scale_kernel");
   }
-  const Plan p = plan(rows, d);
+  const Plan p = plan(rows, d, CROSS);
   float* part = static_cast<float*>(ws);
   double* acc = reinterpret_cast<double*>(static_cast<char*>(ws) + p.part_bytes);
   int* order = reinterpret_cast<int*>(static_cast<char*>(ws) + p.part_bytes + p.acc_bytes);
   // The pipelined kernel loads whole 16-byte chunks of aligned rows and
   // addresses a stage with 32-bit byte offsets.
-  const bool pipe_ok = (lda % 8 == 0) && (d % 8 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
-                       int64_t(kKT) * lda * 2 < (int64_t(1) << 31);
+  auto aligned = [&](const uint16_t* m, int64_t ld) {
+    return (ld % 8 == 0) && (reinterpret_cast<uintptr_t>(m) % 16 == 0) && int64_t(kKT) * ld * 2 < (int64_t(1) << 31);
+  };
+  const bool pipe_ok = (d % 8 == 0) && aligned(a, lda) && (!CROSS || aligned(b, ldb));
   // whole slices per XCD (blocked order) where a launch holds at least 8 slices, else super-blocks
   // shared by the XCDs; the tile orders are built for the launches below by the same rule
   auto slices_of = [&](int g) { return (g * p.group + p.group <= p.nslices) ? p.group : p.nslices - g * p.group; };
@@ -666,7 +719,8 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   if (need_sb) {
     {
       LaunchTimer timer("superblock_order_kernel", st);
-      hipLaunchKernelGGL(superblock_order_kernel, dim3(static_cast<unsigned>(p.nsb)), dim3(256), 0, st, p.nt, order);
+      hipLaunchKernelGGL(superblock_order_kernel<CROSS>, dim3(static_cast<unsigned>(p.nsb)), dim3(256), 0, st, p.nt,
+                         order);
     }
     const kq_status s0 = check_launch("superblock_order_kernel");
     if (s0 != KQ_OK) return s0;
@@ -674,7 +728,7 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
   if (need_blocked) {
     {
       LaunchTimer timer("blocked_order_kernel", st);
-      hipLaunchKernelGGL(blocked_order_kernel, dim3(1), dim3(64), 0, st, p.nt, order + size_t(p.nsb) * 256);
+      hipLaunchKernelGGL(blocked_order_kernel<CROSS>, dim3(1), dim3(64), 0, st, p.nt, order + size_t(p.nsb) * 256);
     }
     const kq_status s0 = check_launch("blocked_order_kernel");
     if (s0 != KQ_OK) return s0;
@@ -685,23 +739,39 @@ kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, floa
     const int nsb = superblocks_of(nsl);
     const int per_xcd = nsb == 0 ? p.ntiles * ((nsl + kXcds - 1) / kXcds) : nsb * 32 * nsl;
     const int* ord = nsb == 0 ? order + size_t(p.nsb) * 256 : order;
-    const char* kname = pipe_ok ? "syrk_partial" : "syrk_partial_regs";
+    const char* kname = pipe_ok ? kpart : kregs;
     {
       LaunchTimer timer(kname, st);
-      hipLaunchKernelGGL(pipe_ok ? syrk_partial : syrk_partial_regs, dim3(static_cast<unsigned>(per_xcd * kXcds)),
-                         dim3(kThreads), 0, st, a, lda, d, rows, p.ntiles, s0, nsl, nsb, ord, part);
+      hipLaunchKernelGGL(pipe_ok ? syrk_partial<CROSS> : syrk_partial_regs<CROSS>,
+                         dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a, lda, b, ldb, d, rows,
+                         p.nt, p.ntiles, s0, nsl, nsb, ord, part);
     }
     kq_status s = check_launch(kname);
     if (s != KQ_OK) return s;
     {
-      LaunchTimer timer("syrk_reduce", st);
-      hipLaunchKernelGGL(syrk_reduce, dim3(static_cast<unsigned>(p.ntiles * 16)), dim3(256), 0, st, part, nsl,
-                         p.ntiles, d, acc, g == 0 ? 1 : 0, g == p.ngroups - 1 ? 1 : 0, alpha, beta, h);
+      LaunchTimer timer(kred, st);
+      hipLaunchKernelGGL(syrk_reduce<CROSS>, dim3(static_cast<unsigned>(p.ntiles * 16)), dim3(256), 0, st, part, nsl,
+                         p.nt, p.ntiles, d, acc, g == 0 ? 1 : 0, g == p.ngroups - 1 ? 1 : 0, alpha, beta, c_in, h);
     }
-    s = check_launch("syrk_reduce");
+    s = check_launch(kred);
     if (s != KQ_OK) return s;
   }
   return KQ_OK;
+}
+
+}  // namespace
+
+size_t syrk_workspace(int64_t rows, int64_t d) { return workspace(rows, d, false); }
+size_t xcov_workspace(int64_t rows, int64_t d) { return workspace(rows, d, true); }
+
+kq_status syrk_run(const uint16_t* a, int64_t rows, int64_t d, int64_t lda, float alpha, float beta,
+                   float* h, void* ws, hipStream_t st) {
+  return cov_run<false>(a, lda, a, lda, rows, d, alpha, beta, h, h, ws, st);
+}
+
+kq_status xcov_run(const uint16_t* a, const uint16_t* b, int64_t rows, int64_t d, int64_t lda, int64_t ldb,
+                   float alpha, float beta, const float* c_in, float* c, void* ws, hipStream_t st) {
+  return cov_run<true>(a, lda, b, ldb, rows, d, alpha, beta, c_in, c, ws, st);
 }
 
 }  // namespace kq

@@ -13,8 +13,8 @@ from typing import Optional
 import numpy as np
 
 from . import (KQ_BIIP_INPUT, KQ_BIIP_INVERSE, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_SCORE_KRONQ, KQError,
-               KQ_ENOTPD, Rot, accumulate_cov, biip_rotate, cholesky_inv, make_rot, obs_quantize,
-               sensitivity)
+               KQ_ENOTPD, Rot, accumulate_cov, accumulate_xcov, biip_rotate, biip_transform, cholesky_inv,
+               gptaq_target, make_rot, obs_quantize, sensitivity)
 
 ALL_SIDES = KQ_BIIP_INPUT | KQ_BIIP_OUTPUT | KQ_BIIP_SCALE
 
@@ -47,6 +47,16 @@ def covariance(a, *, out=None, chunk_rows: Optional[int] = None, stream=None):
     return h
 
 
+def drift_moment(xt, x, h_x, *, out=None, stream=None):
+    """D = (Xt - X)^T X / N from the full-precision inputs Xt and the quantized-model inputs X
+    (bf16 [N, d], the same tokens) and H_X = X^T X / N: one cross-moment call with beta = -1."""
+    import torch
+    n, d = x.shape
+    dm = torch.empty((d, d), dtype=torch.float32, device=x.device) if out is None else out
+    accumulate_xcov(xt, x, dm, 1.0 / n, -1.0, c_in=h_x, stream=stream)
+    return dm
+
+
 @dataclass
 class LayerOut:
     w2: object          # rotated weight W'' (float64), overwritten by the dequantised W^''
@@ -62,11 +72,13 @@ class LayerOut:
 
 def quantize_layer(w, h_x, h_g, rot_in: DeviceRot, rot_out: DeviceRot, *, bits: int, group: int, block: int,
                    damp: float, flags: int = ALL_SIDES, keep_inputs: bool = True, unrotate: bool = True,
-                   check_info: bool = True, preround=None, stream=None) -> LayerOut:
+                   check_info: bool = True, preround=None, d_x=None, stream=None) -> LayerOut:
     """BiIP -> damped Cholesky factor of the inverse -> OBS sweep (-> un-rotation).
 
     ``h_x`` / ``h_g`` are the raw covariances; with ``keep_inputs`` they are
-    copied first (the library transforms them in place)."""
+    copied first (the library transforms them in place). ``d_x`` (the drift moment of
+    ``drift_moment``) selects the GPTAQ base quantizer: D'' by the input-side map, then the
+    drift correction of W'' before the sweep."""
     import torch
     dev = w.device
     dout, din = w.shape
@@ -80,12 +92,20 @@ def quantize_layer(w, h_x, h_g, rot_in: DeviceRot, rot_out: DeviceRot, *, bits: 
     biip_rotate(w, w2, hx, hg, rot_in.rot if flags & KQ_BIIP_INPUT else None,
                 rot_out.rot if flags & KQ_BIIP_OUTPUT else None, flags, s_x, s_g, stream=stream)
     del hg  # H_G'' is not needed by anything after BiIP
+    d2 = None
+    if d_x is not None:
+        d2 = d_x.clone() if keep_inputs else d_x
+        if flags & KQ_BIIP_INPUT:
+            biip_transform(d2, rot_in.rot, s_x, stream=stream)
     info = torch.zeros(1, dtype=torch.int32, device=dev)
     cholesky_inv(hx, damp, info, stream=stream)
     if check_info:
         bad = int(info.item())
         if bad:
             raise KQError(KQ_ENOTPD, f"damped H_X'' is not positive definite at index {bad - 1}")
+    if d2 is not None:
+        gptaq_target(w2, d2, hx, stream=stream)
+        del d2
     ng = din // group if group else 1
     codes = torch.empty((dout, din), dtype=torch.uint8, device=dev)
     scales = torch.empty((dout, ng), dtype=torch.float32, device=dev)

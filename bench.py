@@ -60,6 +60,9 @@ def parse_args():
     p.add_argument("--bits", type=int, default=2, choices=(2, 4), help="bit width of the LLaMA-2-7B q_proj (--config 2)")
     p.add_argument("--serial", action="store_true",
                    help="run every stage on one stream (per-stage profiles) instead of the two-stream schedule")
+    p.add_argument("--gptaq", action="store_true",
+                   help="row f2: the GPTAQ base quantizer in the step (drift moment of full-precision inputs of the "
+                        "same shape, its input-side map and the drift correction of W'' before the sweep)")
     p.add_argument("--overlap", action="store_true",
                    help="one layer: use the two-stream schedule at any width (by default only up to 8192 inputs)")
     p.add_argument("--reserve-cus", type=int, default=80,
@@ -223,6 +226,10 @@ COPY_BYTES = 1 << 30
 # kernel -> (source file, peak, unit, bound)
 KERNELS = {
     "syrk_partial": ("syrk.hip", 2500.0, "TFLOP/s", "mfma"),
+    "xcov_partial": ("syrk.hip", 2500.0, "TFLOP/s", "mfma"),
+    "gptaq_drift_kernel": ("gptaq.hip", 78.6, "TFLOP/s", "mfma"),
+    "gptaq_weight_kernel": ("gptaq.hip", 78.6, "TFLOP/s", "mfma"),
+    "gptaq_update_kernel": ("gptaq.hip", 78.6, "TFLOP/s", "mfma"),
     "chol_far_kernel": ("chol.hip", 157.3, "TFLOP/s", "mfma"),
     "chol_step_kernel": ("chol.hip", 157.3, "TFLOP/s", "mfma"),
     "obs_step_kernel": ("obs.hip", 78.6, "TFLOP/s", "mfma"),
@@ -528,6 +535,7 @@ WORKLOAD_TAG = {1: "linear64x128", 2: "llama2-7b_q_proj", 3: "llama2-13b_mlp", 4
                 5: "llama3-8b_block"}
 TIMED_KERNELS = ("syrk_partial", "chol_far_kernel", "chol_step_kernel", "obs_step_kernel", "row_fwht", "col_fwht",
                  "col_mix")
+GPTAQ_KERNELS = ("xcov_partial", "gptaq_drift_kernel", "gptaq_weight_kernel", "gptaq_update_kernel")
 
 
 def quant_bench(args) -> int:
@@ -547,7 +555,7 @@ def quant_bench(args) -> int:
     single = len(cfg.subs) == 1
     # two streams pay where the factor is latency-bound (its 64-wide steps leave CUs idle next to the
     # G covariance); at 28672 inputs the factor's rank-256 launches fill the GPU and one stream is as fast
-    overlap = single and not args.serial and (cfg.subs[0].din <= 8192 or args.overlap)
+    overlap = single and not args.serial and not args.gptaq and (cfg.subs[0].din <= 8192 or args.overlap)
     # created before anything else takes a hardware queue: a CU-masked stream needs its own
     side = side_stream(dev, args.reserve_cus) if overlap else None
     wl = kq_synth.Workload(cfg)
@@ -560,9 +568,13 @@ def quant_bench(args) -> int:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
     xs = {}
+    xts = {}
     for grp in cfg.x_groups:
         xs[grp] = bits_dev(wl.x(grp))
         wl.drop("x", grp)
+        if args.gptaq:  # full-precision inputs (gain drift and noise on the same draws)
+            xts[grp] = bits_dev(wl.xt(grp))
+            wl.drop("xt", grp)
     gs, ws_, rots_in, rots_out = {}, {}, {}, {}
     for s in cfg.subs:
         gs[s.name] = bits_dev(wl.g(s.name))
@@ -582,10 +594,16 @@ def quant_bench(args) -> int:
 
     widths_all = list(cfg.x_groups.values()) + [s.dout for s in cfg.subs]
     ws_cov = scratch(max(kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, d) for d in widths_all))
-    ws_biip = scratch(max(kq.workspace_size(kq.KQ_OP_BIIP, s.dout, s.din) for s in cfg.subs))
+    ws_biip = scratch(max(max(kq.workspace_size(kq.KQ_OP_BIIP, s.dout, s.din),
+                              kq.workspace_size(kq.KQ_OP_BIIP, s.din, s.din) if args.gptaq else 0)
+                          for s in cfg.subs))
     ws_chol = scratch(max(kq.workspace_size(kq.KQ_OP_CHOLESKY, s.din) for s in cfg.subs))
     ws_obs = scratch(max(kq.workspace_size(kq.KQ_OP_OBS, s.dout, s.din, cfg.block) for s in cfg.subs))
     hx_raw = {grp: torch.empty((d, d), dtype=f32, device=dev) for grp, d in cfg.x_groups.items()}
+    if args.gptaq:
+        ws_xcov = scratch(max(kq.workspace_size(kq.KQ_OP_XCOV, n_tok, d) for d in cfg.x_groups.values()))
+        ws_gptaq = scratch(max(kq.workspace_size(kq.KQ_OP_GPTAQ, s.dout, s.din) for s in cfg.subs))
+        dm = {grp: torch.empty((d, d), dtype=f32, device=dev) for grp, d in cfg.x_groups.items()}
     hg = {s.name: torch.empty((s.dout, s.dout), dtype=f32, device=dev) for s in cfg.subs}
     lay = {}
     for s in cfg.subs:
@@ -599,7 +617,8 @@ def quant_bench(args) -> int:
             codes=torch.empty((s.dout, s.din), dtype=torch.uint8, device=dev),
             scales=torch.empty((s.dout, ng), dtype=f32, device=dev),
             zeros=torch.empty((s.dout, ng), dtype=torch.uint8, device=dev),
-            info=torch.zeros(1, dtype=torch.int32, device=dev))
+            info=torch.zeros(1, dtype=torch.int32, device=dev),
+            d2=torch.empty((s.din, s.din), dtype=f32, device=dev) if args.gptaq else None)
     score_dev = torch.empty(2 * len(cfg.subs), dtype=f64, device=dev)
     score_host = torch.empty(2 * len(cfg.subs), dtype=f64, pin_memory=True)
     n_params = [s.dout * s.din for s in cfg.subs]
@@ -682,6 +701,10 @@ def quant_bench(args) -> int:
             mark(ev, "cov_x0", main)
             kq.accumulate_cov(xs[grp], hx_raw[grp], 1.0 / n_tok, 0.0, ws=ws_cov)
             mark(ev, "cov_x1", main)
+            if args.gptaq:  # drift moment D = Xt^T X / N - H_X
+                mark(ev, "drift0", main)
+                kq.accumulate_xcov(xts[grp], xs[grp], dm[grp], 1.0 / n_tok, -1.0, c_in=hx_raw[grp], ws=ws_xcov)
+                mark(ev, "drift1", main)
         for s in cfg.subs:
             mark(ev, "cov_g0", main)
             kq.accumulate_cov(gs[s.name], hg[s.name], 1.0 / n_tok, 0.0, ws=ws_cov)
@@ -701,9 +724,18 @@ def quant_bench(args) -> int:
             kq.biip_rotate(ws_[s.name], L["w2"], L["hx"], hg[s.name], rots_in[s.x_group].rot, rots_out[s.name].rot,
                            pipeline.ALL_SIDES, L["s_x"], L["s_g"], ws=ws_biip)
             mark(ev, "biip1", main)
+            if args.gptaq:
+                mark(ev, "gptaq0", main)
+                L["d2"].copy_(dm[s.x_group])
+                kq.biip_transform(L["d2"], rots_in[s.x_group].rot, L["s_x"], ws=ws_biip)
+                mark(ev, "gptaq1", main)
             mark(ev, "chol0", main)
             kq.cholesky_inv(L["hx"], cfg.damp, L["info"], ws=ws_chol)
             mark(ev, "chol1", main)
+            if args.gptaq:
+                mark(ev, "gptaq0", main)
+                kq.gptaq_target(L["w2"], L["d2"], L["hx"], ws=ws_gptaq)
+                mark(ev, "gptaq1", main)
             mark(ev, "obs0", main)
             kq.obs_quantize(L["w2"], L["hx"], plan[i], cfg.group, cfg.block, L["codes"], L["scales"], L["zeros"],
                             ws=ws_obs)
@@ -724,14 +756,15 @@ def quant_bench(args) -> int:
 
     log(f"timing {args.steps} steps")
     evs = [dict() for _ in range(args.steps)]
-    kq.timing_enable("|".join(TIMED_KERNELS))
+    timed = TIMED_KERNELS + (GPTAQ_KERNELS if args.gptaq else ())
+    kq.timing_enable("|".join(timed))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kt = {k: kq.timing_query(k) for k in TIMED_KERNELS}
+    kt = {k: kq.timing_query(k) for k in timed}
     kq.timing_enable(None)
     release_streams()
     plan = plan_box["plan"]
@@ -745,6 +778,9 @@ def quant_bench(args) -> int:
         return tot / args.steps
     stage_ms = {"cov_x": span("cov_x"), "cov_g": span("cov_g"), "score_alloc": span("score"), "biip": span("biip"),
                 "cholesky": span("chol"), "obs": span("obs")}
+    if args.gptaq:
+        stage_ms["drift_moment"] = span("drift")
+        stage_ms["gptaq_correction"] = span("gptaq")
     weights = sum(n_params)
     # algorithmic work per step
     cov_flops = sum(n_tok * d * (d + 1) for d in cfg.x_groups.values()) + sum(n_tok * s.dout * (s.dout + 1)
@@ -756,8 +792,15 @@ def quant_bench(args) -> int:
     far_flops = sum(chol_far_flops(s.din) for s in cfg.subs)
     work = {"syrk_partial": cov_flops, "chol_far_kernel": far_flops, "chol_step_kernel": chol_flops - far_flops,
             "obs_step_kernel": obs_flops}
+    if args.gptaq:
+        # cross moment: every entry of the square; the correction's three products skip their triangles
+        work["xcov_partial"] = sum(2 * n_tok * d * d for d in cfg.x_groups.values())
+        work["gptaq_drift_kernel"] = sum(s.din ** 3 / 3 for s in cfg.subs)
+        work["gptaq_weight_kernel"] = sum(s.dout * s.din ** 2 for s in cfg.subs)
+        work["gptaq_update_kernel"] = sum(s.dout * s.din ** 2 for s in cfg.subs)
     t_accum = (stage_ms["cov_x"] + stage_ms["cov_g"]) / 1e3
-    t_quant = sum(stage_ms[k] for k in ("score_alloc", "biip", "cholesky", "obs")) / 1e3
+    t_quant = sum(stage_ms[k] for k in ("score_alloc", "biip", "cholesky", "obs", "gptaq_correction")
+                  if k in stage_ms) / 1e3
     value = weights / (ms_step / 1e3) / 1e6
     log(f"{ms_step:.2f} ms/step; stages {json.dumps({k: round(v, 3) for k, v in stage_ms.items()})}")
     for k, (n, ms) in kt.items():
@@ -784,7 +827,9 @@ def quant_bench(args) -> int:
         "config": {
             "workload": (f"{cfg.name}: " + ", ".join(f"{s.name} {s.dout}x{s.din}" for s in cfg.subs) +
                          f" ({cfg.w_dtype}); {n_tok} tokens of X and G (bf16); group {cfg.group}, block {cfg.block}, "
-                         f"damp {cfg.damp}, BiIP both sides"),
+                         f"damp {cfg.damp}, BiIP both sides" +
+                         (", GPTAQ base quantizer (drift moment of full-precision inputs Xt of the same shape, "
+                          "drift correction of W'' before the sweep)" if args.gptaq else "")),
             "bits": dict(zip([s.name for s in cfg.subs], plan)),
             "tokens": n_tok,
             "weights": weights,
@@ -812,7 +857,11 @@ def quant_bench(args) -> int:
                                            "triangle of the trailing matrix and the substitution sums over the "
                                            "nonzero part of L^-1), float32 MFMA",
                         "chol_step_kernel": "2 d^3 / 3 per factor less the far launches' share, float32 MFMA",
-                        "obs_step_kernel": "dout din (din - 1) per layer (in-block sweep and lazy-batch updates)"}[dominant]
+                        "obs_step_kernel": "dout din (din - 1) per layer (in-block sweep and lazy-batch updates)",
+                        "xcov_partial": "2 N d^2 per cross moment (every entry of the square)",
+                        "gptaq_drift_kernel": "din^3 / 3 per layer (the strict upper triangle of D R^T), float64 MFMA",
+                        "gptaq_weight_kernel": "dout din^2 per layer (W times the strictly upper Y), float64 MFMA",
+                        "gptaq_update_kernel": "dout din^2 per layer (Z times the upper R), float64 MFMA"}[dominant]
                      + "; launch durations from HIP events the library records on each launch's stream"),
         },
         "cpu_baseline": None,
@@ -835,6 +884,14 @@ def quant_bench(args) -> int:
         "obs": roof("mfma", obs_flops, kms["obs_step_kernel"], 78.6, "TFLOP/s", 1e12,
                     "obs_step_kernel launches: dout din (din - 1) flop per layer, against the float64 roof"),
     }
+    if args.gptaq:
+        g_flops = work["gptaq_drift_kernel"] + work["gptaq_weight_kernel"] + work["gptaq_update_kernel"]
+        result["step_rooflines"]["drift_moment"] = roof(
+            "mfma", work["xcov_partial"], kms["xcov_partial"], 2500.0, "TFLOP/s", 1e12,
+            "xcov_partial launches: 2 N d^2 flop per cross moment (every entry of the square)")
+        result["step_rooflines"]["gptaq_correction"] = roof(
+            "mfma", g_flops, kms["gptaq_drift_kernel"] + kms["gptaq_weight_kernel"] + kms["gptaq_update_kernel"],
+            78.6, "TFLOP/s", 1e12, "the three float64 products: din^3 / 3 + 2 dout din^2 flop per layer")
     result["schedule"] = ("two streams: H_X covariance, BiIP input side, Cholesky factor, BiIP output side and "
                           f"sweep on one; H_G covariance on the other from the end of the input side, kept off "
                           f"{args.reserve_cus} CUs" if overlap else
@@ -848,7 +905,7 @@ def quant_bench(args) -> int:
         dst_t.copy_(src_t)
         torch.cuda.synchronize()
         del src_t, dst_t
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.gptaq:  # the timed oracle sample models the GPTQ path
         log("timing the float64 oracle on a bounded sample")
         del xs, gs
         torch.cuda.empty_cache()

@@ -593,7 +593,12 @@ def quant_bench(args) -> int:
         return torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
 
     widths_all = list(cfg.x_groups.values()) + [s.dout for s in cfg.subs]
-    ws_cov = scratch(max(kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, d) for d in widths_all))
+    # the covariances and (with --gptaq) the cross moments run one after another on one stream and
+    # share one workspace
+    cov_bytes = max(kq.workspace_size(kq.KQ_OP_ACCUMULATE_COV, n_tok, d) for d in widths_all)
+    if args.gptaq:
+        cov_bytes = max([cov_bytes] + [kq.workspace_size(kq.KQ_OP_XCOV, n_tok, d) for d in cfg.x_groups.values()])
+    ws_cov = scratch(cov_bytes)
     ws_biip = scratch(max(max(kq.workspace_size(kq.KQ_OP_BIIP, s.dout, s.din),
                               kq.workspace_size(kq.KQ_OP_BIIP, s.din, s.din) if args.gptaq else 0)
                           for s in cfg.subs))
@@ -601,7 +606,7 @@ def quant_bench(args) -> int:
     ws_obs = scratch(max(kq.workspace_size(kq.KQ_OP_OBS, s.dout, s.din, cfg.block) for s in cfg.subs))
     hx_raw = {grp: torch.empty((d, d), dtype=f32, device=dev) for grp, d in cfg.x_groups.items()}
     if args.gptaq:
-        ws_xcov = scratch(max(kq.workspace_size(kq.KQ_OP_XCOV, n_tok, d) for d in cfg.x_groups.values()))
+        ws_xcov = ws_cov
         ws_gptaq = scratch(max(kq.workspace_size(kq.KQ_OP_GPTAQ, s.dout, s.din) for s in cfg.subs))
         dm = {grp: torch.empty((d, d), dtype=f32, device=dev) for grp, d in cfg.x_groups.items()}
     hg = {s.name: torch.empty((s.dout, s.dout), dtype=f32, device=dev) for s in cfg.subs}

@@ -132,6 +132,8 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
  *   rows   number of token rows, >= 0 (0: H <- beta * H)
  *   h      device float32 [d, d]; read only when beta != 0; both triangles written
  *   ws     scratch of kq_workspace_size(KQ_OP_ACCUMULATE_COV, rows, d, 0) bytes
+ *          (the float32 partial sums of every 16384-row slice when they fit in
+ *          64 GiB, else of one launch's slices plus a float64 running sum)
  * bf16 products are exact; sums run in float32 within token slices of 16384
  * rows and in float64 across slices; the result is rounded once to float32.
  */
@@ -156,7 +158,9 @@ kq_status kq_accumulate_cov(const uint16_t* a, int64_t rows, int64_t d, int64_t 
  * slices of 16384 rows, float64 across slices), over every 256 x 256 tile of
  * the square; alpha * A^T B is rounded to float32 before beta * C_in is added
  * (and the sum rounded again), so identical inputs with C_in from
- * kq_accumulate_cov and beta = -1 give exactly zero.
+ * kq_accumulate_cov and beta = -1 give exactly zero (both sum the same float32
+ * slice partials in slice order in float64, however the slices are split into
+ * launches).
  */
 kq_status kq_accumulate_xcov(const uint16_t* a, const uint16_t* b, int64_t rows, int64_t d, int64_t lda,
                              int64_t ldb, float alpha, float beta, const float* c_in, float* c, void* ws,

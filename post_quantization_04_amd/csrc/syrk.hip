@@ -66,6 +66,7 @@ constexpr int kPanelUnits = kT * kKT * 2 / 16;  // 16-byte units per LDS panel (
 constexpr int kPanelBytes = kPanelUnits * 16;
 constexpr int kUnitsPerLane = kPanelUnits / kThreads;  // 16-byte loads per lane per panel (4)
 constexpr int kTargetItems = 8192;  // work items per launch before slices are split into groups
+constexpr size_t kKeepAllBytes = size_t(64) << 30;  // the partials of every slice are kept below this
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -555,7 +556,8 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
   const int64_t tile_off = int64_t(tile) * kT * kT;
   const int64_t slice_stride = int64_t(ntiles) * kT * kT;
   // the four rows' loads of four slices at a time are all in flight together (16 per thread);
-  // each entry still sums its slices four at a time, in order
+  // each entry adds its slices one by one in slice order, so the float64 total does not depend
+  // on how the slices were split into launches (the running sum is stored exactly between them)
   const int64_t e0 = int64_t(si * 64 + rb) * kT + sj * 64 + cq;  // row rb; row rb + 16 k is + 16 k kT
   double sum[4][4];
 #pragma unroll
@@ -579,10 +581,13 @@ __global__ __launch_bounds__(256) void syrk_reduce(const float* __restrict__ par
         v[k][u] = *reinterpret_cast<const float4*>(pp + 16 * k * kT + (q + u) * slice_stride);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      sum[k][0] += (double(v[k][0].x) + double(v[k][1].x)) + (double(v[k][2].x) + double(v[k][3].x));
-      sum[k][1] += (double(v[k][0].y) + double(v[k][1].y)) + (double(v[k][2].y) + double(v[k][3].y));
-      sum[k][2] += (double(v[k][0].z) + double(v[k][1].z)) + (double(v[k][2].z) + double(v[k][3].z));
-      sum[k][3] += (double(v[k][0].w) + double(v[k][1].w)) + (double(v[k][2].w) + double(v[k][3].w));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sum[k][0] += v[k][u].x;
+        sum[k][1] += v[k][u].y;
+        sum[k][2] += v[k][u].z;
+        sum[k][3] += v[k][u].w;
+      }
     }
   }
   for (; q < nsl; ++q) {
@@ -652,6 +657,7 @@ __global__ void scale_kernel(const float* in, float* out, int64_t n, float beta)
 
 struct Plan {
   int nt, ntiles, nslices, group, ngroups, nsb;
+  bool keep_all;  // the partials of every slice stay until one reduce after the last launch
   size_t part_bytes, acc_bytes, order_bytes;
 };
 
@@ -670,8 +676,15 @@ Plan plan(int64_t rows, int64_t d, bool cross) {
   if (g > kXcds) g -= g % kXcds;
   p.group = g;
   p.ngroups = p.nslices ? (p.nslices + g - 1) / g : 0;
-  p.part_bytes = align_up(size_t(g) * p.ntiles * kT * kT * sizeof(float), 256);
-  p.acc_bytes = p.ngroups > 1 ? align_up(size_t(p.ntiles) * kT * kT * sizeof(double), 256) : 0;
+  // With several launches, a float64 running sum of every tile carries the total from one
+  // launch's reduce to the next: read and written once per launch. When the float32 partials of
+  // all slices fit in kKeepAllBytes they are kept instead and reduced once at the end (262144
+  // tokens at width 28672: 26.5 GB for H, one 5 ms reduce against eight of 1.6 ms; 52.6 GB for
+  // the cross moment's full square, one reduce against sixteen that each also move the sum).
+  const size_t slice_bytes = size_t(p.ntiles) * kT * kT * sizeof(float);
+  p.keep_all = p.ngroups > 1 && size_t(p.nslices) * slice_bytes <= kKeepAllBytes;
+  p.part_bytes = align_up((p.keep_all ? size_t(p.nslices) : size_t(g)) * slice_bytes, 256);
+  p.acc_bytes = (p.ngroups > 1 && !p.keep_all) ? align_up(size_t(p.ntiles) * kT * kT * sizeof(double), 256) : 0;
   const int side = (p.nt + 15) / 16;
   p.nsb = cross ? side * side : side * (side + 1) / 2;  // 16 x 16 super-blocks
   p.order_bytes = align_up((size_t(p.nsb) * 256 + p.ntiles) * sizeof(int), 256);
@@ -740,18 +753,22 @@ kq_status cov_run(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb
     const int per_xcd = nsb == 0 ? p.ntiles * ((nsl + kXcds - 1) / kXcds) : nsb * 32 * nsl;
     const int* ord = nsb == 0 ? order + size_t(p.nsb) * 256 : order;
     const char* kname = pipe_ok ? kpart : kregs;
+    float* out = p.keep_all ? part + size_t(s0) * p.ntiles * kT * kT : part;
     {
       LaunchTimer timer(kname, st);
       hipLaunchKernelGGL(pipe_ok ? syrk_partial<CROSS> : syrk_partial_regs<CROSS>,
                          dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kThreads), 0, st, a, lda, b, ldb, d, rows,
-                         p.nt, p.ntiles, s0, nsl, nsb, ord, part);
+                         p.nt, p.ntiles, s0, nsl, nsb, ord, out);
     }
     kq_status s = check_launch(kname);
     if (s != KQ_OK) return s;
+    if (p.keep_all && g + 1 < p.ngroups) continue;
     {
       LaunchTimer timer(kred, st);
-      hipLaunchKernelGGL(syrk_reduce<CROSS>, dim3(static_cast<unsigned>(p.ntiles * 16)), dim3(256), 0, st, part, nsl,
-                         p.nt, p.ntiles, d, acc, g == 0 ? 1 : 0, g == p.ngroups - 1 ? 1 : 0, alpha, beta, c_in, h);
+      // keep_all: one reduce over every slice; otherwise this launch's slices onto the running sum
+      hipLaunchKernelGGL(syrk_reduce<CROSS>, dim3(static_cast<unsigned>(p.ntiles * 16)), dim3(256), 0, st, part,
+                         p.keep_all ? p.nslices : nsl, p.nt, p.ntiles, d, acc, (p.keep_all || g == 0) ? 1 : 0,
+                         g == p.ngroups - 1 ? 1 : 0, alpha, beta, c_in, h);
     }
     s = check_launch(kred);
     if (s != KQ_OK) return s;

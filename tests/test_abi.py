@@ -202,13 +202,18 @@ def test_workspace_sizes(L):
     # float32 partials of all lower-triangle 256 x 256 tiles of one slice group
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8192, 512, 0) >= 3 * 256 * 256 * 4
     # 11008 channels = 946 tiles: about 8192 tile-slice items per launch would put all 9 token
-    # slices in one launch; groups above 8 are cut to 8 (one whole slice per XCD), so the partials hold 8
-    # slices and a float64 sum of every tile carries the total across the two launches; the tile
-    # orders are the 256 slots of each 16 x 16 super-block (6 of them at 43 tile rows) and the
-    # blocked list of all tiles
+    # slices in one launch; groups above 8 are cut to 8 (one whole slice per XCD), so two launches
+    # run, and the float32 partials of all 9 slices (2.2 GB, under the 64 GiB cap) stay for one
+    # reduce at the end; the tile orders are the 256 slots of each 16 x 16 super-block (6 of them
+    # at 43 tile rows) and the blocked list of all tiles
     tile = 256 * 256
-    want = 8 * 946 * tile * 4 + 946 * tile * 8 + (((6 * 256 + 946) * 4 + 255) // 256) * 256
+    want = 9 * 946 * tile * 4 + (((6 * 256 + 946) * 4 + 255) // 256) * 256
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8 * 16384 + 5000, 11008, 0) == want
+    # 65536 channels = 32896 tiles (8.6 GB of partials per slice): one slice per launch, and 8
+    # slices exceed the cap, so one slice's partials and a float64 sum of every tile that
+    # carries the total from launch to launch (136 super-blocks)
+    want = 32896 * tile * 4 + 32896 * tile * 8 + (((136 * 256 + 32896) * 4 + 255) // 256) * 256
+    assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8 * 16384, 65536, 0) == want
     # 4096 channels over 16 slices: one launch, no float64 sums
     want = 16 * 136 * tile * 4 + (((256 + 136) * 4 + 255) // 256) * 256
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 16 * 16384, 4096, 0) == want

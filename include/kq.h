@@ -133,7 +133,10 @@ size_t kq_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2);
  *   h      device float32 [d, d]; read only when beta != 0; both triangles written
  *   ws     scratch of kq_workspace_size(KQ_OP_ACCUMULATE_COV, rows, d, 0) bytes
  *          (the float32 partial sums of every 16384-row slice when they fit in
- *          64 GiB, else of one launch's slices plus a float64 running sum)
+ *          64 GiB, else of one launch's slices plus a float64 running sum; the
+ *          environment variable KQ_COV_KEEP_ALL_MAX_BYTES, a decimal byte count,
+ *          replaces the 64 GiB when set, for kq_workspace_size and the call
+ *          alike: keep it unchanged between the two)
  * bf16 products are exact; sums run in float32 within token slices of 16384
  * rows and in float64 across slices; the result is rounded once to float32.
  */

@@ -50,6 +50,7 @@
 // its 4 x 8 sub-block x, so the 32 panels of a super-block come from HBM about
 // once and reach the other XCDs from the Infinity Cache. At width 28672 this
 // ran 3.5 % faster than giving each XCD a contiguous eighth of the tiles.
+#include <cstdlib>
 #include <utility>
 
 #include "kq_internal.h"
@@ -661,6 +662,18 @@ struct Plan {
   size_t part_bytes, acc_bytes, order_bytes;
 };
 
+// Bytes of float32 partials up to which every slice's are kept: kKeepAllBytes, or the decimal
+// value of KQ_COV_KEEP_ALL_MAX_BYTES (a lower cap takes the running-sum path at small sizes).
+size_t keep_all_cap() {
+  const char* e = std::getenv("KQ_COV_KEEP_ALL_MAX_BYTES");
+  if (e != nullptr && *e != '\0') {
+    char* end = nullptr;
+    const unsigned long long v = std::strtoull(e, &end, 10);
+    if (end != nullptr && *end == '\0') return static_cast<size_t>(v);
+  }
+  return kKeepAllBytes;
+}
+
 // CROSS: every tile of the square and super-blocks over the square.
 Plan plan(int64_t rows, int64_t d, bool cross) {
   Plan p{};
@@ -682,7 +695,7 @@ Plan plan(int64_t rows, int64_t d, bool cross) {
   // tokens at width 28672: 26.5 GB for H, one 5 ms reduce against eight of 1.6 ms; 52.6 GB for
   // the cross moment's full square, one reduce against sixteen that each also move the sum).
   const size_t slice_bytes = size_t(p.ntiles) * kT * kT * sizeof(float);
-  p.keep_all = p.ngroups > 1 && size_t(p.nslices) * slice_bytes <= kKeepAllBytes;
+  p.keep_all = p.ngroups > 1 && size_t(p.nslices) * slice_bytes <= keep_all_cap();
   p.part_bytes = align_up((p.keep_all ? size_t(p.nslices) : size_t(g)) * slice_bytes, 256);
   p.acc_bytes = (p.ngroups > 1 && !p.keep_all) ? align_up(size_t(p.ntiles) * kT * kT * sizeof(double), 256) : 0;
   const int side = (p.nt + 15) / 16;

@@ -214,6 +214,15 @@ def test_workspace_sizes(L):
     # carries the total from launch to launch (136 super-blocks)
     want = 32896 * tile * 4 + 32896 * tile * 8 + (((136 * 256 + 32896) * 4 + 255) // 256) * 256
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8 * 16384, 65536, 0) == want
+    # a lower cap on the kept partials: one launch's 8 slices and a float64 sum of every tile that
+    # carries the total across the two launches
+    import os
+    os.environ["KQ_COV_KEEP_ALL_MAX_BYTES"] = "0"
+    try:
+        want = 8 * 946 * tile * 4 + 946 * tile * 8 + (((6 * 256 + 946) * 4 + 255) // 256) * 256
+        assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 8 * 16384 + 5000, 11008, 0) == want
+    finally:
+        del os.environ["KQ_COV_KEEP_ALL_MAX_BYTES"]
     # 4096 channels over 16 slices: one launch, no float64 sums
     want = 16 * 136 * tile * 4 + (((256 + 136) * 4 + 255) // 256) * 256
     assert L.kq_workspace_size(kq.KQ_OP_ACCUMULATE_COV, 16 * 16384, 4096, 0) == want

@@ -11,7 +11,12 @@ bench times, on outputs the float64 oracle can compute one by one.
   per-row OBS objective on those rows.
 * LLaMA-3-70B down_proj input covariance (28672 channels, 6328 tiles of
   256 x 256): enough token slices that the slices are split over several
-  launches, which sum through the float64 workspace.
+  launches; the float32 partials of all slices kept for one reduce, and (with
+  the cap on kept partials lowered) summed launch by launch through a float64
+  running sum, bit for bit the same.
+* LLaMA-3-70B down_proj drift correction of row f2 (8192 x 28672): random D''
+  and upper R, sampled rows of the corrected W'' against the formula in
+  float64 (each row needs only O(din^2) work).
 * LLaMA-2-13B MLP gate_proj BiIP (13824 x 5120): odd factors 27 and 5 of the
   randomised Hadamard transform at their real sizes; sampled rows of W'' and
   sampled entries of H_G'' from the rotation's definition, H_X'' in full.
@@ -150,9 +155,24 @@ def test_fullsize_q_proj_chain():
     np.testing.assert_allclose(obj_got, obj_want, rtol=1e-3)
 
 
-def test_fullsize_down_proj_covariance_slice_groups():
-    """28672 channels (6328 tiles): four token slices, summed over two launches through the float64 workspace."""
+def _cov_both_paths(xd, d, n_tok, monkeypatch):
+    """H from the kept partials of every slice (one reduce) and from launch-by-launch float64 sums."""
     import torch
+    kq, _ = _kq()
+    h = torch.empty((d, d), dtype=torch.float32, device=DEV)
+    kq.accumulate_cov(xd, h, 1.0 / n_tok, 0.0)
+    h_run = torch.empty((d, d), dtype=torch.float32, device=DEV)
+    with monkeypatch.context() as m:
+        m.setenv("KQ_COV_KEEP_ALL_MAX_BYTES", "0")
+        kq.accumulate_cov(xd, h_run, 1.0 / n_tok, 0.0)
+    torch.cuda.synchronize()
+    # the slices are added one by one in slice order in float64 either way
+    assert torch.equal(h, h_run), "kept partials and running sums differ"
+    return h
+
+
+def test_fullsize_down_proj_covariance_slice_groups(monkeypatch):
+    """28672 channels (6328 tiles): four token slices over two launches."""
     kq, pipeline = _kq()
     n_tok = 3 * 16384 + 100  # four slices of 16384 tokens, the last one ragged
     cfg = kq_synth.scaled(kq_synth.config(4), n_tokens=n_tok, dims={})
@@ -161,20 +181,16 @@ def test_fullsize_down_proj_covariance_slice_groups():
     d = x.shape[1]
     assert d == 28672
     print(f"full-size down_proj input covariance: {n_tok} x {d}", flush=True)
-    h = torch.empty((d, d), dtype=torch.float32, device=DEV)
     xd = bits_to_dev(x)
-    kq.accumulate_cov(xd, h, 1.0 / n_tok, 0.0)
-    torch.cuda.synchronize()
+    h = _cov_both_paths(xd, d, n_tok, monkeypatch)
     del xd
     _check_sampled_cov(x, h, _channels(d, 96, 4), "H_X down_proj")
     np.testing.assert_allclose(np.diag(host(h)).astype(np.float64), _diag(x), rtol=2e-6)
 
 
-def test_fullsize_wide_covariance_whole_slice_groups():
+def test_fullsize_wide_covariance_whole_slice_groups(monkeypatch):
     """11008 channels (946 tiles; LLaMA-2-7B's MLP width), 8 token slices and a ragged ninth: one
-    launch of 8 whole slices, one per XCD, then the ragged slice in tile groups, summed through
-    the float64 workspace."""
-    import torch
+    launch of 8 whole slices, one per XCD, then the ragged slice in tile groups."""
     kq, pipeline = _kq()
     n_tok = 8 * 16384 + 5000
     cfg = kq_synth.scaled(kq_synth.config(2), n_tokens=n_tok, dims={"q_proj": (64, 11008)})
@@ -182,13 +198,65 @@ def test_fullsize_wide_covariance_whole_slice_groups():
     d = x.shape[1]
     assert d == 11008
     print(f"wide covariance: {n_tok} x {d}", flush=True)
-    h = torch.empty((d, d), dtype=torch.float32, device=DEV)
     xd = bits_to_dev(x)
-    kq.accumulate_cov(xd, h, 1.0 / n_tok, 0.0)
-    torch.cuda.synchronize()
+    h = _cov_both_paths(xd, d, n_tok, monkeypatch)
     del xd
     _check_sampled_cov(x, h, _channels(d, 96, 5), "H_X 11008")
     np.testing.assert_allclose(np.diag(host(h)).astype(np.float64), _diag(x), rtol=2e-6)
+
+
+def _gptaq_rows(w, d2, r, rows, block=512):
+    """Rows of W + W triu(D R^T, 1) R in float64 without forming D R^T: with c_k = sum_{q<k} w[q] D[q, :],
+    (w triu(D R^T, 1))[k] = R[k, :] . c_k. Per block of k: R_b . c at the block start, plus the
+    pairs inside the block through G = R_b D_b^T (shared by all rows), then c += w_b D_b."""
+    din = d2.shape[0]
+    ws = w[rows].astype(np.float64)
+    c = np.zeros((len(rows), din))
+    z = np.zeros((len(rows), din))
+    for k0 in range(0, din, block):
+        k1 = min(k0 + block, din)
+        rb, db = r[k0:k1].astype(np.float64), d2[k0:k1].astype(np.float64)
+        g = np.tril(rb @ db.T, -1)                      # g[k, q] = R[k] . D[q] for q < k in the block
+        z[:, k0:k1] = c @ rb.T + ws[:, k0:k1] @ g.T
+        c += ws[:, k0:k1] @ db
+    out = ws.copy()
+    for k0 in range(0, din, block):
+        k1 = min(k0 + block, din)
+        out += z[:, k0:k1] @ r[k0:k1].astype(np.float64)
+    return out
+
+
+def test_fullsize_gptaq_target_down_proj():
+    """The drift correction at 8192 x 28672 (8 x 8-tile super-blocks, the launch shape the bench
+    times): random D'' and upper R (zero below the diagonal, as the factor leaves it), sampled rows
+    against the formula in float64."""
+    import torch
+    kq, _ = _kq()
+    dout, din = 8192, 28672
+    rng = np.random.default_rng(70)
+    print(f"full-size gptaq target {dout} x {din}: generating inputs", flush=True)
+    w = rng.random((dout, din)) - 0.5
+    d2 = rng.random((din, din), dtype=np.float32)
+    d2 -= np.float32(0.5)
+    d2 *= np.float32(2e-3)
+    r = rng.random((din, din), dtype=np.float32)
+    r -= np.float32(0.5)
+    r *= np.float32(2.0 / np.sqrt(din))
+    for k0 in range(0, din, 1024):  # zero below the diagonal, a block of rows at a time
+        r[k0:k0 + 1024, :k0] = 0.0
+        r[k0:k0 + 1024, k0:k0 + 1024] = np.triu(r[k0:k0 + 1024, k0:k0 + 1024])
+    wd = torch.from_numpy(w).to(DEV)
+    kq.gptaq_target(wd, to_dev(d2), to_dev(r))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 4095, 4096, 8190, 8191])
+    got = wd[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del wd
+    print("reference rows", flush=True)
+    want = _gptaq_rows(w, d2, r, rows)
+    corr = want - w[rows]
+    err = np.linalg.norm(got - want, axis=1) / np.linalg.norm(corr, axis=1)
+    print(f"gptaq target rows: max error {err.max():.2e} of the correction", flush=True)
+    assert err.max() <= 1e-11
 
 
 def test_fullsize_mlp_biip_odd_factors():

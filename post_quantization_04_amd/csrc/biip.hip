@@ -335,35 +335,44 @@ __device__ __forceinline__ void bfly16(double v[16], int first) {
   }
 }
 
-template <typename T, typename Src, typename Dst, int MB, int NT>
-__global__ __launch_bounds__(NT, NT == kFwThreads ? 6 : 1) void row_fwht(const Src* __restrict__ src, int64_t lds, int64_t n,
-                                                       Dst* __restrict__ dst, int64_t ldd, RowFw rf) {
-  extern __shared__ double smem[];
-  T* buf = reinterpret_cast<T*>(smem);
-  const int64_t row = blockIdx.x;
+// Window 0 of group e0 (16 contiguous values v, as loaded): signs and factors when they go at
+// load, the first four radix-2 stages, then the values into the row's LDS slots.
+template <typename T>
+__device__ __forceinline__ void row_stage0(T* buf, int e0, double v[16], const RowFw& rf, double rowf,
+                                           const double* colf, int cstep) {
+  if (!rf.inverse) {
+    const uint32_t neg = neg_mask16(rf.signs + e0);
+    // the factors of the 16 values are contiguous (16-byte loads from one base) or all one
+    // (cstep = 0, a uniform branch): 16 separate addresses would take 32 registers
+    double cf[16];
+    if (cstep) {
+      const double2* c2 = reinterpret_cast<const double2*>(colf + e0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double2 t = c2[i];
+        cf[2 * i] = t.x;
+        cf[2 * i + 1] = t.y;
+      }
+    } else {
+      const double c = colf[0];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cf[i] = c;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = flip(v[i] * (rowf * cf[i]), neg, i);
+  }
+  bfly16(v, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[lpad(e0 + i)] = static_cast<T>(v[i]);
+}
+
+// The rest of a row once window 0 is in LDS: the odd mix on the staged row, the windows above
+// bit 4 through LDS, and the last window's values to global memory at o.
+template <typename T, typename Dst, int MB, int NT>
+__device__ __forceinline__ void row_rest(T* buf, Dst* o, int64_t n, const RowFw& rf, double rowf,
+                                         const double* colf, int cstep) {
   const int k = rf.k, kg = k - 4;
   const int ng = static_cast<int>(n >> 4);
-  const Src* s = src + row * lds;
-  Dst* o = dst + row * ldd;
-  const double rowf = rf.rowf ? rf.rowf[row] : 1.0;
-  const double* colf = rf.colf ? rf.colf : &kUnitFactor;
-  const int cstep = rf.colf ? 1 : 0;
-  for (int g = threadIdx.x; g < ng; g += NT) {
-    const int e0 = g << 4;
-    double v[16];
-    load16<Src>(s + e0, v);
-    if (!rf.inverse) {
-      const uint32_t neg = neg_mask16(rf.signs + e0);
-      double cf[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cf[i] = colf[(e0 + i) * cstep];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = flip(v[i] * (rowf * cf[i]), neg, i);
-    }
-    bfly16(v, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) buf[lpad(e0 + i)] = static_cast<T>(v[i]);
-  }
   __syncthreads();
   if (MB > 1 && rf.m > 1) {
     const int p = 1 << k;
@@ -408,6 +417,25 @@ __global__ __launch_bounds__(NT, NT == kFwThreads ? 6 : 1) void row_fwht(const S
     }
     if (!last) __syncthreads();
   }
+}
+
+template <typename T, typename Src, typename Dst, int MB, int NT>
+__global__ __launch_bounds__(NT, NT == kFwThreads ? 6 : 1) void row_fwht(const Src* __restrict__ src, int64_t lds, int64_t n,
+                                                       Dst* __restrict__ dst, int64_t ldd, RowFw rf) {
+  extern __shared__ double smem[];
+  T* buf = reinterpret_cast<T*>(smem);
+  const int64_t row = blockIdx.x;
+  const int ng = static_cast<int>(n >> 4);
+  const Src* s = src + row * lds;
+  const double rowf = rf.rowf ? rf.rowf[row] : 1.0;
+  const double* colf = rf.colf ? rf.colf : &kUnitFactor;
+  const int cstep = rf.colf ? 1 : 0;
+  for (int g = threadIdx.x; g < ng; g += NT) {
+    double v[16];
+    load16<Src>(s + (g << 4), v);
+    row_stage0<T>(buf, g << 4, v, rf, rowf, colf, cstep);
+  }
+  row_rest<T, Dst, MB, NT>(buf, dst + row * ldd, n, rf, rowf, colf, cstep);
 }
 
 // One digit pass of the column direction on a [n_rows, n_cols] row-major
@@ -600,41 +628,60 @@ __global__ __launch_bounds__(kColThreads) void col_fwht(const Src* __restrict__ 
   }
 }
 
+// Column blocks of 256 a col_mix thread covers: four for mixes of up to 7 (28 loads in flight
+// per thread; one block each left the pass waiting on load latency), one for wider mixes.
+template <int MB>
+constexpr int mix_cols() { return MB <= 8 ? 4 : 1; }
+
 template <typename Src, typename Dst, int MB, bool OPS>
 __global__ __launch_bounds__(kColThreads) void col_mix(const Src* __restrict__ src, Dst* __restrict__ dst,
                                                        ColPass cp) {
-  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
+  constexpr int CPT = mix_cols<MB>();
+  const int64_t span = int64_t(kColThreads) * CPT;
+  const int64_t ncb = (cp.n_cols + span - 1) / span;
   const int64_t g = blockIdx.x / ncb;
-  const int64_t j0 = (blockIdx.x % ncb) * kColThreads;  // uniform
-  const uint32_t lane = threadIdx.x;
-  const int64_t j = j0 + lane;
-  if (j >= cp.n_cols) return;
+  const int64_t j0 = (blockIdx.x % ncb) * span + threadIdx.x;  // column of block 0
   const int64_t base = group_base(cp, g);
-  const Src* s0 = src + j0;
-  Dst* d0 = dst + j0;
   const int m = cp.mt;
-  const double cl = OPS ? cp.cl[j] : 1.0, cs = OPS ? cp.cs[j] : 1.0;
-  double v[MB];
+  // every slot loads (slots past m read row m - 1 again and are zeroed after; columns past the
+  // end read the last column and are not stored), so all loads are in flight together: a load
+  // under a condition compiles to a branch that waits for it
+  int64_t jc[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) jc[c] = j0 + c * kColThreads < cp.n_cols ? j0 + c * kColThreads : cp.n_cols - 1;
+  Src raw[CPT][MB];
+  double rf[MB], cl[CPT], cs[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    cl[c] = OPS ? cp.cl[jc[c]] : 1.0;
+    cs[c] = OPS ? cp.cs[jc[c]] : 1.0;
+  }
 #pragma unroll
   for (int a = 0; a < MB; ++a) {
-    const int64_t r = base + a * cp.sa;
-    v[a] = 0.0;
-    if (a < m) {
-      v[a] = load_elem<Src>(s0 + r * cp.lds + lane);
-      if (OPS) v[a] *= cp.rl[r] * cl;
-    }
+    const int64_t r = base + (a < m ? a : m - 1) * cp.sa;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) raw[c][a] = src[r * cp.lds + jc[c]];
+    rf[a] = OPS ? cp.rl[r] : 1.0;
   }
   const int qs_a = cp.transpose ? 1 : m, qs_k = cp.transpose ? m : 1;
 #pragma unroll
-  for (int a = 0; a < MB; ++a) {
-    if (a < m) {
-      const double* qa = cp.q + a * qs_a;
-      double acc = 0.0;
-      // k >= m: v[k] is zero and the Q index is clamped inside the row, so the term adds zero
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t j = j0 + c * kColThreads;
+    double v[MB];
 #pragma unroll
-      for (int k = 0; k < MB; ++k) acc = fma(qa[(k < m ? k : m - 1) * qs_k], v[k], acc);
-      const int64_t r = base + a * cp.sa;
-      store_elem<Dst>(d0 + r * cp.ldd + lane, OPS ? acc * (cp.rs[r] * cs) : acc);
+    for (int a = 0; a < MB; ++a) v[a] = a < m ? widen(raw[c][a]) * (OPS ? rf[a] * cl[c] : 1.0) : 0.0;
+    if (j >= cp.n_cols) continue;
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      if (a < m) {
+        const double* qa = cp.q + a * qs_a;
+        double acc = 0.0;
+        // k >= m: v[k] is zero and the Q index is clamped inside the row, so the term adds zero
+#pragma unroll
+        for (int k = 0; k < MB; ++k) acc = fma(qa[(k < m ? k : m - 1) * qs_k], v[k], acc);
+        const int64_t r = base + a * cp.sa;
+        store_elem<Dst>(dst + r * cp.ldd + j, OPS ? acc * (cp.rs[r] * cs[c]) : acc);
+      }
     }
   }
 }
@@ -745,14 +792,15 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // Row direction of rot on each of the rows (pitches lds, ldd elements), with
 // the diagonal factors of sc. The register-butterfly kernel takes chunks of at
-// least 256, odd factors up to 31, 16-byte aligned rows and factors on the
-// signs' side; anything else takes the LDS kernel.
+// least 256, odd factors up to 31, 16-byte aligned rows, signs and column
+// factors, and factors on the signs' side; anything else takes the LDS kernel.
 template <typename Src, typename Dst>
 kq_status launch_rows(const Src* src, int64_t lds, int64_t rows, int64_t n, Dst* dst, int64_t ldd, Rot rot,
                       Scales sc, hipStream_t st) {
   const bool side_ok = (!sc.row && !sc.col) || (sc.at_store != 0) == (rot.inverse != 0);
   const bool rows_aligned = aligned16(src) && (lds * int64_t(sizeof(Src))) % 16 == 0;
-  if (rot.signs && rot.log2p >= 8 && rot.m <= 31 && side_ok && rows_aligned && aligned16(rot.signs)) {
+  if (rot.signs && rot.log2p >= 8 && rot.m <= 31 && side_ok && rows_aligned && aligned16(rot.signs) &&
+      (!sc.col || aligned16(sc.col))) {
     const RowFw rf{rot.log2p, rot.m, rot.q, rot.inverse, rot.signs, rot.inverse, rot.out_scale, sc.row, sc.col};
     // float64 staging for float64 output while a row stays small; float32 staging (one
     // rounding per window, below the float32 output's own) keeps more rows per CU
@@ -823,7 +871,8 @@ kq_status launch_fwht(const Src* src, Dst* dst, const ColPass& cp, bool ops, hip
 
 template <typename Src, typename Dst, int MB>
 kq_status launch_mix(const Src* src, Dst* dst, const ColPass& cp, bool ops, hipStream_t st) {
-  const int64_t ncb = (cp.n_cols + kColThreads - 1) / kColThreads;
+  const int64_t span = int64_t(kColThreads) * mix_cols<MB>();
+  const int64_t ncb = (cp.n_cols + span - 1) / span;
   const dim3 grid(static_cast<unsigned>((cp.n_rows / cp.mt) * ncb));
   {
     LaunchTimer timer("col_mix", st);

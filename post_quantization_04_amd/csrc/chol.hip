@@ -245,8 +245,17 @@ __device__ __forceinline__ f32x16 mfma_split(const Split3& a, const Split3& b, f
   return acc;
 }
 
+// The LDS of the split product: per buffer and operand the hi, mid and lo bfloat16 pieces of a
+// 128 x 16 chunk as [row][k] tiles (pitch 24: eight consecutive rows on distinct banks for the
+// 16-byte reads), each value split once when stored.
+constexpr int kSplitPitch = kGK + 8;
+struct SplitLds {
+  alignas(16) __bf16 a[2][3][kG][kSplitPitch];
+  alignas(16) __bf16 b[2][3][kG][kSplitPitch];
+};
+
 template <bool TB>
-__device__ __forceinline__ void gemm128_split(GemmLds& sm, const float* a, int64_t lda, const float* b, int64_t ldb,
+__device__ __forceinline__ void gemm128_split(SplitLds& sm, const float* a, int64_t lda, const float* b, int64_t ldb,
                                               float* c, int64_t ldc, int m_valid, int n_valid, int k0, int k1,
                                               float alpha, float beta) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -276,16 +285,47 @@ __device__ __forceinline__ void gemm128_split(GemmLds& sm, const float* a, int64
         }
   }
   const int nchunk = (k1 - k0) / kGK;
-  float4 va[2], vb[2];
+  // A and (TB) B: thread t takes row t / 2 of the tile and 8 consecutive k from 8 (t % 2), two
+  // 16-byte loads; B without TB: column t % 128 and the 8 k rows from 8 (t / 128), 8 loads along
+  // the row. Rows (columns) past the valid count read row (column) 0 and are stored as zero.
+  const int t = threadIdx.x;
+  const int ar = t >> 1, ak = 8 * (t & 1);
+  const int bj = t & 127, bk = 8 * (t >> 7);
+  const bool a_in = ar < m_valid, b_in = TB ? ar < n_valid : bj < n_valid;
+  const float* arow = a + int64_t(a_in ? ar : 0) * lda + ak;
+  const float* brow = TB ? b + int64_t(b_in ? ar : 0) * ldb + ak : b + (b_in ? bj : 0);
+  float va[8], vb[8];
   auto load = [&](int kc) {
-    load_rows(a, lda, m_valid, kc, va);
-    if (TB) load_rows(b, ldb, n_valid, kc, vb);
-    else load_cols(b, ldb, n_valid, kc, vb);
+    const float4 x0 = *reinterpret_cast<const float4*>(arow + kc);
+    const float4 x1 = *reinterpret_cast<const float4*>(arow + kc + 4);
+    va[0] = x0.x; va[1] = x0.y; va[2] = x0.z; va[3] = x0.w;
+    va[4] = x1.x; va[5] = x1.y; va[6] = x1.z; va[7] = x1.w;
+    if (TB) {
+      const float4 y0 = *reinterpret_cast<const float4*>(brow + kc);
+      const float4 y1 = *reinterpret_cast<const float4*>(brow + kc + 4);
+      vb[0] = y0.x; vb[1] = y0.y; vb[2] = y0.z; vb[3] = y0.w;
+      vb[4] = y1.x; vb[5] = y1.y; vb[6] = y1.z; vb[7] = y1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vb[e] = brow[int64_t(kc + bk + e) * ldb];
+    }
   };
+  // each value split once, into the hi / mid / lo tiles the MFMAs read
   auto store = [&](int buf) {
-    store_rows(sm.a[buf], va);
-    if (TB) store_rows(sm.b[buf], vb);
-    else store_cols(sm.b[buf], vb);
+    float x[8], y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = a_in ? va[e] : 0.0f;
+      y[e] = b_in ? vb[e] : 0.0f;
+    }
+    const Split3 sa = split3(x), sb = split3(y);
+    *reinterpret_cast<bf16x8*>(&sm.a[buf][0][ar][ak]) = sa.hi;
+    *reinterpret_cast<bf16x8*>(&sm.a[buf][1][ar][ak]) = sa.mid;
+    *reinterpret_cast<bf16x8*>(&sm.a[buf][2][ar][ak]) = sa.lo;
+    const int br = TB ? ar : bj, bc = TB ? ak : bk;
+    *reinterpret_cast<bf16x8*>(&sm.b[buf][0][br][bc]) = sb.hi;
+    *reinterpret_cast<bf16x8*>(&sm.b[buf][1][br][bc]) = sb.mid;
+    *reinterpret_cast<bf16x8*>(&sm.b[buf][2][br][bc]) = sb.lo;
   };
   if (nchunk > 0) {
     load(k0);
@@ -299,17 +339,17 @@ __device__ __forceinline__ void gemm128_split(GemmLds& sm, const float* a, int64
     Split3 fa[2], fb[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sm.a[buf][kb + e][wi * 64 + x * 32 + ln];
-      fa[x] = split3(v);
+      const int r = wi * 64 + x * 32 + ln;
+      fa[x].hi = *reinterpret_cast<const bf16x8*>(&sm.a[buf][0][r][kb]);
+      fa[x].mid = *reinterpret_cast<const bf16x8*>(&sm.a[buf][1][r][kb]);
+      fa[x].lo = *reinterpret_cast<const bf16x8*>(&sm.a[buf][2][r][kb]);
     }
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sm.b[buf][kb + e][wj * 64 + y * 32 + ln];
-      fb[y] = split3(v);
+      const int r = wj * 64 + y * 32 + ln;
+      fb[y].hi = *reinterpret_cast<const bf16x8*>(&sm.b[buf][0][r][kb]);
+      fb[y].mid = *reinterpret_cast<const bf16x8*>(&sm.b[buf][1][r][kb]);
+      fb[y].lo = *reinterpret_cast<const bf16x8*>(&sm.b[buf][2][r][kb]);
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
@@ -823,15 +863,28 @@ __global__ __launch_bounds__(256) void chol_step_kernel(float* __restrict__ a, f
 // one block behind; M is zero above its diagonal blocks, so columns beyond a
 // row's diagonal add nothing). The two roles write disjoint blocks and read
 // none that the other writes.
+// Tiles run in super-blocks of kFarSB x kFarSB tiles, dealt to the XCDs in turn (workgroups are
+// dispatched to the XCDs round robin; two workgroups per CU give an XCD 64 at once, one
+// super-block): the 64 tiles running together on an XCD read 8 + 8 panel strips (128 KB each)
+// through its L2 instead of two each from beyond it. Super-blocks 0 .. n_sa - 1 cover the lower
+// triangle of the trailing A (ntu tiles a side), the rest the ntu x ncol rectangle of M.
+constexpr int kFarSB = 8;
+constexpr int kFarXcds = 8;
+
 __global__ __launch_bounds__(256) void chol_far_kernel(float* __restrict__ a, float* __restrict__ m, int64_t dp, int s0,
-                                                       int s1, int n_a, int32_t* __restrict__ info) {
-  __shared__ GemmLds sm;
+                                                       int s1, int ntu, int ncol, int n_sa, int n_sm,
+                                                       int32_t* __restrict__ info) {
+  __shared__ SplitLds sm;
   if (*info) return;
-  const int u = static_cast<int>(blockIdx.x);
+  const int xcd = static_cast<int>(blockIdx.x) % kFarXcds, local = static_cast<int>(blockIdx.x) / kFarXcds;
+  const int sb = (local / (kFarSB * kFarSB)) * kFarXcds + xcd, within = local % (kFarSB * kFarSB);
+  if (sb >= n_sa + n_sm) return;
   const int64_t r0 = int64_t(s1) * kB;
-  if (u < n_a) {
-    int I, J;
-    tri(u, I, J);
+  if (sb < n_sa) {
+    int P, Q;
+    tri(sb, P, Q);
+    const int I = P * kFarSB + within / kFarSB, J = Q * kFarSB + within % kFarSB;
+    if (I >= ntu || J > I) return;
     const int64_t ri = r0 + int64_t(I) * kG, rj = r0 + int64_t(J) * kG;
     const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
     const int nv = static_cast<int>(dp - rj < kG ? dp - rj : kG);
@@ -840,10 +893,12 @@ __global__ __launch_bounds__(256) void chol_far_kernel(float* __restrict__ a, fl
                   (s1 - s0) * kB, -1.0f, 1.0f);
     return;
   }
-  const int v = u - n_a;
+  const int v = sb - n_sa;
+  const int ncsb = (ncol + kFarSB - 1) / kFarSB;
+  const int I = (v / ncsb) * kFarSB + within / kFarSB, J = (v % ncsb) * kFarSB + within % kFarSB;
+  if (I >= ntu || J >= ncol) return;
   const int64_t cend = int64_t(s1 - 1) * kB;
-  const int ncol = static_cast<int>((cend + kG - 1) / kG);
-  const int64_t ri = r0 + int64_t(v / ncol) * kG, cj = int64_t(v % ncol) * kG;
+  const int64_t ri = r0 + int64_t(I) * kG, cj = int64_t(J) * kG;
   const int mv = static_cast<int>(dp - ri < kG ? dp - ri : kG);
   const int nv = static_cast<int>(cend - cj < kG ? cend - cj : kG);
   const int kb0 = s0 > 0 ? s0 - 1 : 0;
@@ -927,12 +982,16 @@ kq_status chol_run(float* h, int64_t d, float damp, int32_t* info, void* ws, hip
       // the super-panel [s0, s1) is factored (and M one block behind it): apply it beyond s1
       const int64_t nrem = dp - int64_t(s1) * kB;
       const int ntu = static_cast<int>((nrem + kG - 1) / kG);
-      const int fa = ntu * (ntu + 1) / 2;
-      const int fs = ntu * static_cast<int>((int64_t(s1 - 1) * kB + kG - 1) / kG);
+      const int ncol = static_cast<int>((int64_t(s1 - 1) * kB + kG - 1) / kG);
+      const int nsb = (ntu + kFarSB - 1) / kFarSB;
+      const int n_sa = nsb * (nsb + 1) / 2;
+      const int n_sm = nsb * ((ncol + kFarSB - 1) / kFarSB);
+      // every XCD runs the same number of super-block slots (the surplus workgroups return at once)
+      const int64_t blocks = int64_t((n_sa + n_sm + kFarXcds - 1) / kFarXcds) * kFarXcds * kFarSB * kFarSB;
       {
         LaunchTimer timer("chol_far_kernel", st);
-        hipLaunchKernelGGL(chol_far_kernel, dim3(static_cast<unsigned>(fa + fs)), dim3(256), 0, st, a, m, dp, s0, s1,
-                           fa, info);
+        hipLaunchKernelGGL(chol_far_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, m, dp, s0, s1,
+                           ntu, ncol, n_sa, n_sm, info);
       }
       if ((r = check_launch("chol_far_kernel")) != KQ_OK) return r;
     }

@@ -80,3 +80,24 @@ def check_codes(codes, zeros, scales, w2, r, bits, group, *, window=1e-5, max_fr
     assert res.adopted_zeros <= int(max_frac * nz), f"{label}: {res.adopted_zeros} tie-window zeros of {nz}"
     np.testing.assert_allclose(scales, res.scales.astype(np.float32), rtol=scale_rtol, err_msg=label)
     return res
+
+
+def gptaq_rows(w, d2, r, rows, block=512):
+    """Rows of W + W triu(D R^T, 1) R in float64 without forming D R^T: with c_k = sum_{q<k} w[q] D[q, :],
+    (w triu(D R^T, 1))[k] = R[k, :] . c_k. Per block of k: R_b . c at the block start, plus the
+    pairs inside the block through G = R_b D_b^T (shared by all rows), then c += w_b D_b."""
+    din = d2.shape[0]
+    ws = w[rows].astype(np.float64)
+    c = np.zeros((len(rows), din))
+    z = np.zeros((len(rows), din))
+    for k0 in range(0, din, block):
+        k1 = min(k0 + block, din)
+        rb, db = r[k0:k1].astype(np.float64), d2[k0:k1].astype(np.float64)
+        g = np.tril(rb @ db.T, -1)                      # g[k, q] = R[k] . D[q] for q < k in the block
+        z[:, k0:k1] = c @ rb.T + ws[:, k0:k1] @ g.T
+        c += ws[:, k0:k1] @ db
+    out = ws.copy()
+    for k0 in range(0, din, block):
+        k1 = min(k0 + block, din)
+        out += z[:, k0:k1] @ r[k0:k1].astype(np.float64)
+    return out

@@ -26,7 +26,7 @@ import pytest
 
 import kq_synth
 import oracle
-from gpu_helpers import DEV, bits_to_dev, check_codes, host, rel_fro, require_gpu, to_dev
+from gpu_helpers import DEV, bits_to_dev, check_codes, gptaq_rows, host, rel_fro, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -205,27 +205,6 @@ def test_fullsize_wide_covariance_whole_slice_groups(monkeypatch):
     np.testing.assert_allclose(np.diag(host(h)).astype(np.float64), _diag(x), rtol=2e-6)
 
 
-def _gptaq_rows(w, d2, r, rows, block=512):
-    """Rows of W + W triu(D R^T, 1) R in float64 without forming D R^T: with c_k = sum_{q<k} w[q] D[q, :],
-    (w triu(D R^T, 1))[k] = R[k, :] . c_k. Per block of k: R_b . c at the block start, plus the
-    pairs inside the block through G = R_b D_b^T (shared by all rows), then c += w_b D_b."""
-    din = d2.shape[0]
-    ws = w[rows].astype(np.float64)
-    c = np.zeros((len(rows), din))
-    z = np.zeros((len(rows), din))
-    for k0 in range(0, din, block):
-        k1 = min(k0 + block, din)
-        rb, db = r[k0:k1].astype(np.float64), d2[k0:k1].astype(np.float64)
-        g = np.tril(rb @ db.T, -1)                      # g[k, q] = R[k] . D[q] for q < k in the block
-        z[:, k0:k1] = c @ rb.T + ws[:, k0:k1] @ g.T
-        c += ws[:, k0:k1] @ db
-    out = ws.copy()
-    for k0 in range(0, din, block):
-        k1 = min(k0 + block, din)
-        out += z[:, k0:k1] @ r[k0:k1].astype(np.float64)
-    return out
-
-
 def test_fullsize_gptaq_target_down_proj():
     """The drift correction at 8192 x 28672 (8 x 8-tile super-blocks, the launch shape the bench
     times): random D'' and upper R (zero below the diagonal, as the factor leaves it), sampled rows
@@ -252,7 +231,7 @@ def test_fullsize_gptaq_target_down_proj():
     got = wd[torch.from_numpy(rows).to(DEV)].cpu().numpy()
     del wd
     print("reference rows", flush=True)
-    want = _gptaq_rows(w, d2, r, rows)
+    want = gptaq_rows(w, d2, r, rows)
     corr = want - w[rows]
     err = np.linalg.norm(got - want, axis=1) / np.linalg.norm(corr, axis=1)
     print(f"gptaq target rows: max error {err.max():.2e} of the correction", flush=True)

@@ -9,7 +9,7 @@ import pytest
 
 import kq_synth
 import oracle
-from gpu_helpers import DEV, bits_to_dev, check_codes, host, rel_fro, require_gpu, scale_tolerance, to_dev
+from gpu_helpers import DEV, bits_to_dev, check_codes, gptaq_rows, host, rel_fro, require_gpu, scale_tolerance, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -143,6 +143,27 @@ def test_gptaq_target(dout, din):
     want_o = oracle.gptaq_target(w2, hx2, d2.astype(np.float64), 0.01)
     assert np.linalg.norm(got - want_o) <= 1e-4 * np.linalg.norm(want_o - w2)
     assert rel_fro(got, want_o) <= 2e-6
+
+
+@pytest.mark.parametrize("dout,din", [(4096, 4096), (4096, 8192)])
+def test_gptaq_target_super_tile_edges(dout, din):
+    """Widths where the three products run in super-tiles of 2 x 2 (4096) and 4 x 4 tiles (8192):
+    random D'' and upper R, sampled rows of the corrected W against the formula in float64."""
+    import torch
+    kq, _ = _kq()
+    print(f"gptaq target {dout}x{din}", flush=True)
+    rng = np.random.default_rng(din)
+    w = rng.random((dout, din)) - 0.5
+    d2 = ((rng.random((din, din), dtype=np.float32) - np.float32(0.5)) * np.float32(2e-3)).astype(np.float32)
+    r = np.triu((rng.random((din, din), dtype=np.float32) - np.float32(0.5)) * np.float32(2.0 / np.sqrt(din)))
+    wd = torch.from_numpy(w).to(DEV)
+    kq.gptaq_target(wd, to_dev(d2), to_dev(r))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, dout // 2, dout - 2, dout - 1])
+    got = wd[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    want = gptaq_rows(w, d2, r, rows)
+    err = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want - w[rows], axis=1)
+    assert err.max() <= 1e-11, f"{err.max():.2e}"
 
 
 # ---------------------------------------------------------------------------

@@ -1013,8 +1013,8 @@ def main() -> int:
         return traffic_summary(*args.traffic_summary)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU; the path's multi-GPU sharding is design only, "
-                                   "so --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; sharding the path over several GPUs is "
+                                   "described, not implemented, so --gpus must be 1"}))
         return 2
     if args.decode:
         return decode_bench(args)

@@ -195,11 +195,15 @@ kq_status kq_biip_transform(float* m, int64_t n, const kq_rot* rot, const double
  *   w      device float64 [dout, din], in place (W'' of kq_biip_rotate)
  *   d2     device float32 [din, din]: D'' (kq_accumulate_xcov, then kq_biip_transform)
  *   r      device float32 [din, din]: R of kq_cholesky_inv on H_X'' (upper, zero below)
+ *   info   device int32 (may be NULL): set to 1 when a corrected weight is
+ *          not finite (a NaN or Inf in the drift moment, R or W reaches every
+ *          later column); the caller sets it to 0 first. W must then not go
+ *          to the sweep: its codes would be meaningless.
  *   ws     scratch of kq_workspace_size(KQ_OP_GPTAQ, dout, din, 0) bytes
  * Three float64 MFMA products with fixed summation order (deterministic).
  */
-kq_status kq_gptaq_target(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
-                          size_t ws_bytes, void* stream);
+kq_status kq_gptaq_target(double* w, const float* d2, const float* r, int64_t dout, int64_t din, int32_t* info,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * kq_sensitivity -- score = tr(H_G) * tr(H_X), or tr(H_X) alone

@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
     L.kq_accumulate_cov.argtypes = [_VP, _I64, _I64, _I64, _F32, _F32, _VP, _VP, _SZ, _VP]
     L.kq_accumulate_xcov.argtypes = [_VP, _VP, _I64, _I64, _I64, _I64, _F32, _F32, _VP, _VP, _VP, _SZ, _VP]
     L.kq_biip_transform.argtypes = [_VP, _I64, ctypes.POINTER(Rot), _VP, _VP, _SZ, _VP]
-    L.kq_gptaq_target.argtypes = [_VP, _VP, _VP, _I64, _I64, _VP, _SZ, _VP]
+    L.kq_gptaq_target.argtypes = [_VP, _VP, _VP, _I64, _I64, _VP, _VP, _SZ, _VP]
     L.kq_sensitivity.argtypes = [_VP, _I64, _VP, _I64, _I32, _VP, _VP]
     L.kq_allocate_bits.argtypes = [_VP, _VP, _I32, _VP, _I32, _I64, _VP]
     L.kq_biip_rotate.argtypes = [_VP, _I32, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(Rot),
@@ -218,8 +218,9 @@ def biip_transform(m, rot: Rot, s=None, *, ws=None, stream=None) -> None:
                                    _stream(stream)), "kq_biip_transform")
 
 
-def gptaq_target(w, d2, r, *, ws=None, stream=None) -> None:
-    """w <- w + w triu(d2 r^T, 1) r in place; w: [dout, din] float64, d2 and r: [din, din] float32."""
+def gptaq_target(w, d2, r, *, info=None, ws=None, stream=None) -> None:
+    """w <- w + w triu(d2 r^T, 1) r in place; w: [dout, din] float64, d2 and r: [din, din] float32.
+    ``info`` (optional int32 device tensor, zeroed by the caller) becomes 1 if a result is not finite."""
     import torch
     _need(w.dim() == 2 and w.dtype == torch.float64 and w.is_contiguous(), "gptaq_target: w")
     din = w.shape[1]
@@ -229,8 +230,10 @@ def gptaq_target(w, d2, r, *, ws=None, stream=None) -> None:
     need = workspace_size(KQ_OP_GPTAQ, dout, din)
     if ws is None:
         ws = _scratch(need, w.device)
-    _check(lib().kq_gptaq_target(_ptr(w), _ptr(d2), _ptr(r), dout, din, _ptr(ws), 0 if ws is None else ws.numel(),
-                                 _stream(stream)), "kq_gptaq_target")
+    if info is not None:
+        _need(info.dtype == torch.int32 and info.numel() >= 1, "gptaq_target: info must be int32")
+    _check(lib().kq_gptaq_target(_ptr(w), _ptr(d2), _ptr(r), dout, din, _ptr(info), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)), "kq_gptaq_target")
 
 
 def sensitivity(h_x, h_g, score, mode: int = KQ_SCORE_KRONQ, *, stream=None) -> None:

@@ -58,12 +58,12 @@ struct TileLds {
 // of B through that XCD's L2. The super-tiles that hold work are numbered column by column in
 // order of falling k range (the longest tiles start first) and dealt to the XCDs in turn, so
 // each XCD gets an even share of the work; with MASK only those on or above the diagonal.
-template <typename TA, typename TB, bool TRANSB, int KR, bool ACC, bool MASK>
+template <typename TA, typename TB, bool TRANSB, int KR, bool ACC, bool MASK, bool CHECK>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const TA* __restrict__ a, int64_t lda,
                                                       const TB* __restrict__ b, int64_t ldb,
                                                       double* __restrict__ out, int64_t ldo, int64_t M,
                                                       int64_t N, int64_t K, int sup, int super_i, int super_j,
-                                                      int n_super) {
+                                                      int n_super, int32_t* __restrict__ info) {
   __shared__ TileLds<TRANSB> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
@@ -188,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const TA* __restrict__ a, 
     __syncthreads();
   }
   if (nch > 0) mma(static_cast<int>((nch - 1) & 1));
+  bool bad = false;
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -200,12 +201,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const TA* __restrict__ a, 
         if (MASK && j <= i) v = 0.0;
         if (ACC) v += out[i * ldo + j];
         out[i * ldo + j] = v;
+        if (CHECK) bad = bad || !isfinite(v);
       }
+  if (CHECK && bad && info) atomicOr(info, 1);
 }
 
-template <typename TA, typename TB, bool TRANSB, int KR, bool ACC, bool MASK>
+template <typename TA, typename TB, bool TRANSB, int KR, bool ACC, bool MASK, bool CHECK = false>
 kq_status gemm(const char* name, const TA* a, int64_t lda, const TB* b, int64_t ldb, double* out, int64_t ldo,
-               int64_t M, int64_t N, int64_t K, hipStream_t st) {
+               int64_t M, int64_t N, int64_t K, hipStream_t st, int32_t* info = nullptr) {
   const int64_t ti = (M + kT - 1) / kT, tj = (N + kT - 1) / kT;
   if (ti * tj == 0) return KQ_OK;
   // the largest super-tile edge that still deals at least 16 super-tiles with work to each XCD
@@ -230,9 +233,9 @@ kq_status gemm(const char* name, const TA* a, int64_t lda, const TB* b, int64_t 
                                       (long long)N);
   {
     LaunchTimer timer(name, st);
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, TRANSB, KR, ACC, MASK>), dim3(static_cast<unsigned>(blocks)), dim3(256),
-                       0, st, a, lda, b, ldb, out, ldo, M, N, K, sup, static_cast<int>(super_i),
-                       static_cast<int>(super_j), static_cast<int>(n_super));
+    hipLaunchKernelGGL((gemm_kernel<TA, TB, TRANSB, KR, ACC, MASK, CHECK>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, st, a, lda, b, ldb, out, ldo, M, N, K, sup, static_cast<int>(super_i),
+                       static_cast<int>(super_j), static_cast<int>(n_super), info);
   }
   return check_launch(name);
 }
@@ -252,8 +255,8 @@ size_t gptaq_workspace(int64_t dout, int64_t din) {
   return l.y_bytes + l.z_bytes;
 }
 
-kq_status gptaq_target_run(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
-                           hipStream_t st) {
+kq_status gptaq_target_run(double* w, const float* d2, const float* r, int64_t dout, int64_t din, int32_t* info,
+                           void* ws, hipStream_t st) {
   const Layout l = layout(dout, din);
   double* y = static_cast<double*>(ws);
   double* z = reinterpret_cast<double*>(static_cast<char*>(ws) + l.y_bytes);
@@ -266,9 +269,9 @@ kq_status gptaq_target_run(double* w, const float* d2, const float* r, int64_t d
   s = gemm<double, double, false, K_TO_COL, false, false>("gptaq_weight_kernel", w, din, y, din, z, din, dout, din,
                                                           din, st);
   if (s != KQ_OK) return s;
-  // 3. W += Z R
-  return gemm<double, float, false, K_TO_COL, true, false>("gptaq_update_kernel", z, din, r, din, w, din, dout, din,
-                                                           din, st);
+  // 3. W += Z R; a corrected weight that is not finite sets *info
+  return gemm<double, float, false, K_TO_COL, true, false, true>("gptaq_update_kernel", z, din, r, din, w, din, dout,
+                                                                 din, din, st, info);
 }
 
 }  // namespace kq

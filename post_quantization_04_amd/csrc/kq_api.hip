@@ -157,13 +157,13 @@ kq_status kq_biip_transform(float* m, int64_t n, const kq_rot* rot, const double
   return kq::biip_transform_run(m, n, rot, s, ws, kq::as_stream(stream));
 }
 
-kq_status kq_gptaq_target(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
-                          size_t ws_bytes, void* stream) {
+kq_status kq_gptaq_target(double* w, const float* d2, const float* r, int64_t dout, int64_t din, int32_t* info,
+                          void* ws, size_t ws_bytes, void* stream) {
   if (dout < 1 || din < 1 || dout > kMaxDim || din > kMaxDim)
     return fail(KQ_EINVAL, "kq_gptaq_target: shape %lld x %lld", (long long)dout, (long long)din);
   if (!w || !d2 || !r) return fail(KQ_EINVAL, "kq_gptaq_target: NULL pointer");
   if (!ws_ok(ws, ws_bytes, kq::gptaq_workspace(dout, din))) return KQ_EINVAL;
-  return kq::gptaq_target_run(w, d2, r, dout, din, ws, kq::as_stream(stream));
+  return kq::gptaq_target_run(w, d2, r, dout, din, info, ws, kq::as_stream(stream));
 }
 
 kq_status kq_sensitivity(const float* h_x, int64_t din, const float* h_g, int64_t dout, int32_t mode,

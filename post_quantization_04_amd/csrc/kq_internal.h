@@ -54,8 +54,8 @@ kq_status xcov_run(const uint16_t* a, const uint16_t* b, int64_t rows, int64_t d
 
 // GPTAQ drift correction (gptaq.hip)
 size_t gptaq_workspace(int64_t dout, int64_t din);
-kq_status gptaq_target_run(double* w, const float* d2, const float* r, int64_t dout, int64_t din, void* ws,
-                           hipStream_t st);
+kq_status gptaq_target_run(double* w, const float* d2, const float* r, int64_t dout, int64_t din, int32_t* info,
+                           void* ws, hipStream_t st);
 
 // trace score (score.hip)
 kq_status score_run(const float* h_x, int64_t din, const float* h_g, int64_t dout, int mode,

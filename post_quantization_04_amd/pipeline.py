@@ -13,8 +13,8 @@ from typing import Optional
 import numpy as np
 
 from . import (KQ_BIIP_INPUT, KQ_BIIP_INVERSE, KQ_BIIP_OUTPUT, KQ_BIIP_SCALE, KQ_SCORE_KRONQ, KQError,
-               KQ_ENOTPD, Rot, accumulate_cov, accumulate_xcov, biip_rotate, biip_transform, cholesky_inv,
-               gptaq_target, make_rot, obs_quantize, sensitivity)
+               KQ_EINVAL, KQ_ENOTPD, Rot, accumulate_cov, accumulate_xcov, biip_rotate, biip_transform,
+               cholesky_inv, gptaq_target, make_rot, obs_quantize, sensitivity)
 
 ALL_SIDES = KQ_BIIP_INPUT | KQ_BIIP_OUTPUT | KQ_BIIP_SCALE
 
@@ -104,8 +104,12 @@ def quantize_layer(w, h_x, h_g, rot_in: DeviceRot, rot_out: DeviceRot, *, bits: 
         if bad:
             raise KQError(KQ_ENOTPD, f"damped H_X'' is not positive definite at index {bad - 1}")
     if d2 is not None:
-        gptaq_target(w2, d2, hx, stream=stream)
+        info_t = torch.zeros(1, dtype=torch.int32, device=dev)
+        gptaq_target(w2, d2, hx, info=info_t, stream=stream)
         del d2
+        if check_info and int(info_t.item()):
+            raise KQError(KQ_EINVAL, "the drift correction produced non-finite weights "
+                                     "(the drift moment holds a NaN or Inf)")
     ng = din // group if group else 1
     codes = torch.empty((dout, din), dtype=torch.uint8, device=dev)
     scales = torch.empty((dout, ng), dtype=torch.float32, device=dev)

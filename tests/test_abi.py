@@ -85,6 +85,17 @@ def test_accumulate_cov_validation(L):
     assert b"workspace" in L.kq_last_error()
 
 
+def test_gptaq_target_validation(L):
+    need = L.kq_workspace_size(kq.KQ_OP_GPTAQ, 64, 128, 0)
+    assert need > 0
+    assert L.kq_gptaq_target(FAKE, FAKE, FAKE, 0, 128, None, FAKE, need, None) == kq.KQ_EINVAL
+    assert L.kq_gptaq_target(FAKE, FAKE, FAKE, 64, -1, None, FAKE, need, None) == kq.KQ_EINVAL
+    assert L.kq_gptaq_target(None, FAKE, FAKE, 64, 128, None, FAKE, need, None) == kq.KQ_EINVAL
+    assert L.kq_gptaq_target(FAKE, FAKE, None, 64, 128, FAKE, FAKE, need, None) == kq.KQ_EINVAL
+    assert L.kq_gptaq_target(FAKE, FAKE, FAKE, 64, 128, FAKE, FAKE, need - 1, None) == kq.KQ_EINVAL
+    assert b"workspace" in L.kq_last_error()
+
+
 def test_obs_validation(L):
     def call(bits=4, group=128, block=128, din=256, ws=1 << 30):
         return L.kq_obs_quantize(FAKE, FAKE, 4, din, bits, group, block, FAKE, FAKE, FAKE, None, FAKE, ws, None)

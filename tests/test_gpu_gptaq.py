@@ -166,6 +166,28 @@ def test_gptaq_target_super_tile_edges(dout, din):
     assert err.max() <= 1e-11, f"{err.max():.2e}"
 
 
+def test_gptaq_target_flags_non_finite_results():
+    """A NaN in D'' reaches every later column of the corrected W: info becomes 1; clean inputs leave
+    it 0."""
+    import torch
+    kq, _ = _kq()
+    rng = np.random.default_rng(5)
+    dout, din = 96, 320
+    w = rng.random((dout, din)) - 0.5
+    d2 = ((rng.random((din, din)) - 0.5) * 1e-3).astype(np.float32)
+    r = np.triu(rng.random((din, din)) - 0.5).astype(np.float32)
+    info = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kq.gptaq_target(torch.from_numpy(w).to(DEV), to_dev(d2), to_dev(r), info=info)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    d2[7, 200] = np.nan
+    wd = torch.from_numpy(w).to(DEV)
+    kq.gptaq_target(wd, to_dev(d2), to_dev(r), info=info)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 1
+    assert not bool(torch.isfinite(wd).all())
+
+
 # ---------------------------------------------------------------------------
 # whole layers
 # ---------------------------------------------------------------------------
@@ -214,6 +236,26 @@ def test_layer_gptaq(bits):
                 label=f"gptaq W{bits}", scale_rtol=scale_tolerance(e_r))
     # the drift correction changes the quantization
     assert np.mean(got["codes"] != got["plain_codes"]) > 0.01
+
+
+def test_nan_in_full_precision_inputs_is_reported_not_quantized():
+    """A NaN only in Xt (the full-precision model's inputs) leaves H_X, the score and the factor
+    finite but reaches the drift moment; the drift correction flags it and the layer path raises
+    instead of sweeping non-finite weights."""
+    kq, pipeline = _kq()
+    wl = _workload(6000, 128, 256)
+    x, xt = wl.x("attn_in"), wl.xt("attn_in").copy()
+    xt[1234, 77] = 0x7FC0  # bf16 quiet NaN
+    xd = bits_to_dev(x)
+    hx = pipeline.covariance(xd)
+    hg = pipeline.covariance(bits_to_dev(wl.g("q_proj")))
+    dm = pipeline.drift_moment(bits_to_dev(xt), xd, hx)
+    ri = pipeline.upload_rot(wl.rot_in("attn_in").signs, wl.rot_in("attn_in").q, DEV)
+    ro = pipeline.upload_rot(wl.rot_out("q_proj").signs, wl.rot_out("q_proj").q, DEV)
+    with pytest.raises(kq.KQError) as e:
+        pipeline.quantize_layer(bits_to_dev(wl.weight("q_proj")), hx, hg, ri, ro, bits=2, group=128, block=128,
+                                damp=0.01, d_x=dm)
+    assert e.value.status == kq.KQ_EINVAL
 
 
 def test_layer_gptaq_without_drift_is_gptq():

@@ -39,6 +39,8 @@
 //   4. R = J M J written over H (strict lower triangle zeroed).
 // A pivot that is not positive and finite stops the chain: `info` takes the
 // original index + 1 and every later kernel returns at once.
+#include <type_traits>
+
 #include "kq_internal.h"
 
 namespace kq {
@@ -294,69 +296,96 @@ __device__ __forceinline__ void gemm128_split(SplitLds& sm, const float* a, int6
   const bool a_in = ar < m_valid, b_in = TB ? ar < n_valid : bj < n_valid;
   const float* arow = a + int64_t(a_in ? ar : 0) * lda + ak;
   const float* brow = TB ? b + int64_t(b_in ? ar : 0) * ldb + ak : b + (b_in ? bj : 0);
-  float va[8], vb[8];
-  auto load = [&](int kc) {
+  // two register sets: chunk c is loaded into set c % 2 two chunks ahead of its multiply, so its
+  // loads stay in flight across a whole chunk of MFMAs (a single set left each chunk's load
+  // latency exposed behind only the 24 MFMAs of the chunk before it)
+  float va[2][8], vb[2][8];
+  auto load = [&](auto set_c, int kc) {
+    constexpr int S = decltype(set_c)::value;
     const float4 x0 = *reinterpret_cast<const float4*>(arow + kc);
     const float4 x1 = *reinterpret_cast<const float4*>(arow + kc + 4);
-    va[0] = x0.x; va[1] = x0.y; va[2] = x0.z; va[3] = x0.w;
-    va[4] = x1.x; va[5] = x1.y; va[6] = x1.z; va[7] = x1.w;
+    va[S][0] = x0.x; va[S][1] = x0.y; va[S][2] = x0.z; va[S][3] = x0.w;
+    va[S][4] = x1.x; va[S][5] = x1.y; va[S][6] = x1.z; va[S][7] = x1.w;
     if (TB) {
       const float4 y0 = *reinterpret_cast<const float4*>(brow + kc);
       const float4 y1 = *reinterpret_cast<const float4*>(brow + kc + 4);
-      vb[0] = y0.x; vb[1] = y0.y; vb[2] = y0.z; vb[3] = y0.w;
-      vb[4] = y1.x; vb[5] = y1.y; vb[6] = y1.z; vb[7] = y1.w;
+      vb[S][0] = y0.x; vb[S][1] = y0.y; vb[S][2] = y0.z; vb[S][3] = y0.w;
+      vb[S][4] = y1.x; vb[S][5] = y1.y; vb[S][6] = y1.z; vb[S][7] = y1.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vb[e] = brow[int64_t(kc + bk + e) * ldb];
+      for (int e = 0; e < 8; ++e) vb[S][e] = brow[int64_t(kc + bk + e) * ldb];
     }
   };
-  // each value split once, into the hi / mid / lo tiles the MFMAs read
-  auto store = [&](int buf) {
+  // each value split once, into the hi / mid / lo tiles the MFMAs read; set S goes to buffer S
+  auto store = [&](auto set_c) {
+    constexpr int S = decltype(set_c)::value;
     float x[8], y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[e] = a_in ? va[e] : 0.0f;
-      y[e] = b_in ? vb[e] : 0.0f;
+      x[e] = a_in ? va[S][e] : 0.0f;
+      y[e] = b_in ? vb[S][e] : 0.0f;
     }
     const Split3 sa = split3(x), sb = split3(y);
-    *reinterpret_cast<bf16x8*>(&sm.a[buf][0][ar][ak]) = sa.hi;
-    *reinterpret_cast<bf16x8*>(&sm.a[buf][1][ar][ak]) = sa.mid;
-    *reinterpret_cast<bf16x8*>(&sm.a[buf][2][ar][ak]) = sa.lo;
+    *reinterpret_cast<bf16x8*>(&sm.a[S][0][ar][ak]) = sa.hi;
+    *reinterpret_cast<bf16x8*>(&sm.a[S][1][ar][ak]) = sa.mid;
+    *reinterpret_cast<bf16x8*>(&sm.a[S][2][ar][ak]) = sa.lo;
     const int br = TB ? ar : bj, bc = TB ? ak : bk;
-    *reinterpret_cast<bf16x8*>(&sm.b[buf][0][br][bc]) = sb.hi;
-    *reinterpret_cast<bf16x8*>(&sm.b[buf][1][br][bc]) = sb.mid;
-    *reinterpret_cast<bf16x8*>(&sm.b[buf][2][br][bc]) = sb.lo;
+    *reinterpret_cast<bf16x8*>(&sm.b[S][0][br][bc]) = sb.hi;
+    *reinterpret_cast<bf16x8*>(&sm.b[S][1][br][bc]) = sb.mid;
+    *reinterpret_cast<bf16x8*>(&sm.b[S][2][br][bc]) = sb.lo;
   };
-  if (nchunk > 0) {
-    load(k0);
-    store(0);
-  }
-  __syncthreads();
+  // waits for this wave's LDS accesses only (a full __syncthreads would also wait for the
+  // chunk loads still in flight)
+  auto lds_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  // Every chunk issues the same loads (past the last chunk they re-read it and are not used), so
+  // the wait before a split covers only the set it splits: a load under a condition would leave
+  // the compiler a path where that set's loads are the newest, and it would wait for all loads.
+  auto kc_of = [&](int c) { return k0 + (c < nchunk ? c : nchunk - 1) * kGK; };
   const int kb = 8 * (lane >> 5), ln = lane & 31;
-  for (int ch = 0; ch < nchunk; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nchunk) load(k0 + (ch + 1) * kGK);
+  // chunk c: buffer and register set c % 2; its multiply, then chunk c + 1 into the other buffer
+  auto chunk = [&](auto set_c, int c) {
+    constexpr int S = decltype(set_c)::value;
+    using Other = std::integral_constant<int, 1 - S>;
+    load(set_c, kc_of(c + 2));  // set S went to LDS before chunk c
     Split3 fa[2], fb[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int r = wi * 64 + x * 32 + ln;
-      fa[x].hi = *reinterpret_cast<const bf16x8*>(&sm.a[buf][0][r][kb]);
-      fa[x].mid = *reinterpret_cast<const bf16x8*>(&sm.a[buf][1][r][kb]);
-      fa[x].lo = *reinterpret_cast<const bf16x8*>(&sm.a[buf][2][r][kb]);
+      fa[x].hi = *reinterpret_cast<const bf16x8*>(&sm.a[S][0][r][kb]);
+      fa[x].mid = *reinterpret_cast<const bf16x8*>(&sm.a[S][1][r][kb]);
+      fa[x].lo = *reinterpret_cast<const bf16x8*>(&sm.a[S][2][r][kb]);
     }
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int r = wj * 64 + y * 32 + ln;
-      fb[y].hi = *reinterpret_cast<const bf16x8*>(&sm.b[buf][0][r][kb]);
-      fb[y].mid = *reinterpret_cast<const bf16x8*>(&sm.b[buf][1][r][kb]);
-      fb[y].lo = *reinterpret_cast<const bf16x8*>(&sm.b[buf][2][r][kb]);
+      fb[y].hi = *reinterpret_cast<const bf16x8*>(&sm.b[S][0][r][kb]);
+      fb[y].mid = *reinterpret_cast<const bf16x8*>(&sm.b[S][1][r][kb]);
+      fb[y].lo = *reinterpret_cast<const bf16x8*>(&sm.b[S][2][r][kb]);
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int y = 0; y < 2; ++y) acc[x][y] = mfma_split(fa[x], fb[y], acc[x][y]);
-    if (ch + 1 < nchunk) store(buf ^ 1);
-    __syncthreads();
+    // buffer 1 - S held chunk c - 1, whose reads finished before the last barrier
+    if (c + 1 < nchunk) store(Other{});
+    lds_sync();
+  };
+  if (nchunk > 0) {
+    load(C0{}, kc_of(0));
+    load(C1{}, kc_of(1));
+    store(C0{});
+    lds_sync();
+    int ch = 0;
+    for (; ch + 2 <= nchunk; ch += 2) {
+      chunk(C0{}, ch);
+      chunk(C1{}, ch + 1);
+    }
+    if (ch < nchunk) chunk(C0{}, ch);
   }
   if (beta != 0.0f) {
 #pragma unroll
